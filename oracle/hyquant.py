@@ -1,0 +1,494 @@
+"""HyQuant-style hybrid-precision attention: the plain CPU definitions.
+
+TEST INFRASTRUCTURE ONLY (tests, the smoke check and the benchmark's CPU
+baseline may call it; the product path never does).
+
+Sources (the pages are cited by title and section):
+  [HQ-wiki]  "HyQuant: Hybrid-Precision Quantization for LLM Attention"
+             (wiki summary): TL;DR, flowchart, "What problem it solves",
+             "Key results", "Gaps".
+  [HQ-news]  "How HyQuant uses hybrid-precision attention to cut decode
+             compute": "What hybrid-precision attention changes", "Why
+             preserve selected positions?", "What the authors tested",
+             "Memory and runtime costs".
+  [HQ-abs]   The HyQuant abstract on the ACL Anthology author page.
+
+What the method computes, in the pages' terms: a lightweight probe of the
+attention pattern finds "vertical-line" key columns that almost every query
+attends to; those columns plus a recent local window stay in high precision
+and everything else is quantized to low bit width (K4/V4 in the reported
+implementation). Prefill runs a hybrid-precision attention operator with the
+same split; decode keeps a hybrid KV cache and fuses dequantization into
+attention. The pages leave the probe statistic, the quantizer format, the
+window shape, tie-breaks and rounding unspecified; the readings used here are
+stated at each function and collected in the design doc's list of readings.
+
+Conventions: arrays are float64 copies of exact 16-bit inputs; per-(batch,
+KV head) functions take one sequence at a time; GQA maps query head h to KV
+head h // G.
+
+Parity status: every function below is pinned by the CPU tests in
+``tests/test_oracle_*.py`` (closed forms, invariants, special cases that
+reduce to textbook/library attention, brute force on tiny inputs), except the
+diagnostics at the end, which are "parity unpinned" (they measure, they do not
+define).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# 16-bit decoding
+# ---------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE fp16 bit patterns (uint16) -> exact float64 values."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_to_f64(bits)
+    if dtype == "f16":
+        return f16_to_f64(bits)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# O1: vertical-line probe (column scores)
+# ---------------------------------------------------------------------------
+
+
+def probe_column_scores(q_probe: np.ndarray, k: np.ndarray, T: int, sm_scale: float) -> np.ndarray:
+    """Column scores of the vertical-line probe for one batch element.
+
+    [HQ-wiki] TL;DR and "What problem it solves": vertical-line tokens are key
+    columns that almost every query row attends to, found from a cheap pattern
+    signal; [HQ-news] "Why preserve selected positions?": the retained set is
+    the high-score positions; [HQ-abs]: "vertical-line-aware attention-pattern
+    signals". Reading: the signal is the column sum of the row-normalised
+    causal softmax over the last R query rows, summed over the query heads of
+    a KV head (GQA):
+
+        c[g, j] = sum_{h in group g} sum_{rows r} softmax_{j' <= pos_r}(q_{h,r} . k_{g,j'} * sm_scale)[j]
+
+    q_probe: [Hq][R][D]; row r sits at position T - R + r (rows at negative
+    positions, when T < R, are ignored). k: [Hkv][>=T][D]. Returns [Hkv][T].
+    """
+    Hq, R, D = q_probe.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    r_eff = min(R, T)
+    rows = q_probe[:, R - r_eff:, :]
+    pos = np.arange(T - r_eff, T)
+    causal_out = np.arange(T)[None, :] > pos[:, None]          # [r_eff][T]
+    c = np.zeros((Hkv, T), dtype=np.float64)
+    for g in range(Hkv):
+        kg = k[g, :T, :]
+        for h in range(g * G, (g + 1) * G):
+            logits = (rows[h] @ kg.T) * sm_scale
+            logits[causal_out] = -np.inf
+            m = logits.max(axis=1, keepdims=True)
+            e = np.exp(logits - m)
+            p = e / e.sum(axis=1, keepdims=True)
+            c[g] += p.sum(axis=0)
+    return c
+
+
+# ---------------------------------------------------------------------------
+# O2: top-k selection of the retained columns
+# ---------------------------------------------------------------------------
+
+
+def keep_count(T: int, window: int, keep_num: int, keep_den: int) -> int:
+    """Number of retained columns k = min(floor(keep_num*T/keep_den), T - W).
+
+    [HQ-news] "Why preserve selected positions?" / "What the authors tested":
+    the top 5% of key positions plus a local window stay in high precision.
+    Reading: the percentage is taken over the full context T (integer floor);
+    candidates exclude the window, so the kept total is k + min(W, T).
+    """
+    n_cand = max(0, T - window)
+    return min((keep_num * T) // keep_den, n_cand)
+
+
+@dataclasses.dataclass
+class Selection:
+    idx: np.ndarray      # ascending int64 positions
+    k: int
+    tau: float           # score of the k-th ranked candidate (+inf when k == 0)
+    j_k: int             # its position (-1 when k == 0)
+
+
+def select_topk(c_g: np.ndarray, T: int, window: int, keep_num: int, keep_den: int) -> Selection:
+    """Top-k candidates by (score descending, position ascending).
+
+    Candidates are [0, T - W). Ties go to the lower position. Returns the
+    selected set in ascending order and the threshold pair (tau, j_k) of the
+    k-th ranked element, used by the append rule.
+    """
+    n_cand = max(0, T - window)
+    k = keep_count(T, window, keep_num, keep_den)
+    cand = np.arange(n_cand)
+    order = np.lexsort((cand, -c_g[:n_cand]))
+    top = order[:k]
+    if k == 0:
+        return Selection(np.zeros(0, dtype=np.int64), 0, float("inf"), -1)
+    return Selection(np.sort(top).astype(np.int64), k, float(c_g[top[-1]]), int(top[-1]))
+
+
+def ranks_above(c_d: float, d: int, tau: float, j_k: int) -> bool:
+    """(c_d, -d) ranks above (tau, -j_k) in the selection order."""
+    return (c_d > tau) or (c_d == tau and d < j_k)
+
+
+# ---------------------------------------------------------------------------
+# O3: asymmetric per-token INT4 quantizer (group 32, fp16 scale and zero)
+# ---------------------------------------------------------------------------
+
+INT4_GROUP = 32
+
+
+def int4_quantize(x: np.ndarray):
+    """Asymmetric INT4 codes per 32-channel group of each token.
+
+    [HQ-news] "What the authors tested": the non-retained K and V are stored
+    as Key-4bit / Value-4bit. Format (reading of the unspecified details):
+        mn, mx = min, max over the group; d = mx - mn (exact in fp32)
+        s = fp16_rne(fp32_rne(d / 15));  z = fp16_rne(mn)
+        code = clamp(rint_even(fp32(x - z) / fp32 s), 0, 15), or 0 when s == 0
+    The code decision is taken in fp32 (x, z, s are exact fp32 values; one
+    fp32 subtraction, one correctly rounded fp32 division, round half to
+    even). Dequantization x_hat = code*s + z is exact in float64.
+
+    x: [..., D] float64 holding exact 16-bit values. Returns
+    (codes uint8 [..., D], s float16 [..., D/32], z float16 [..., D/32]).
+    """
+    D = x.shape[-1]
+    g = x.reshape(x.shape[:-1] + (D // INT4_GROUP, INT4_GROUP))
+    mn = g.min(axis=-1)
+    mx = g.max(axis=-1)
+    d32 = (mx - mn).astype(np.float32)
+    if not np.array_equal(d32.astype(np.float64), mx - mn):
+        raise ArithmeticError("group range not exact in fp32")
+    s16 = (d32 / np.float32(15.0)).astype(np.float16)
+    z16 = mn.astype(np.float16)
+    s32 = s16.astype(np.float32)[..., None]
+    z32 = z16.astype(np.float32)[..., None]
+    diff = g.astype(np.float32) - z32
+    with np.errstate(divide="ignore", invalid="ignore"):
+        qq = diff / s32
+    codes = np.where(s32 > 0, np.clip(np.rint(qq), 0, 15), 0).astype(np.uint8)
+    return codes.reshape(x.shape), s16, z16
+
+
+def int4_dequantize(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    """x_hat = code * s + z per group (exact in float64)."""
+    D = codes.shape[-1]
+    c = codes.reshape(codes.shape[:-1] + (D // INT4_GROUP, INT4_GROUP)).astype(np.float64)
+    xh = c * s16.astype(np.float64)[..., None] + z16.astype(np.float64)[..., None]
+    return xh.reshape(codes.shape)
+
+
+def int4_pack(codes: np.ndarray) -> np.ndarray:
+    """Two codes per byte: byte i = code[2i] | code[2i+1] << 4 (canonical order)."""
+    c = codes.astype(np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def int4_unpack(packed: np.ndarray) -> np.ndarray:
+    p = packed.astype(np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0x0F
+    out[..., 1::2] = p >> 4
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O4 / O6: the hybrid KV cache of one (batch, KV head)
+# ---------------------------------------------------------------------------
+
+MODE_INT4, MODE_KEPT, MODE_WINDOW = 0, 1, 2
+
+
+@dataclasses.dataclass
+class HybridCache:
+    """Canonical (position-indexed) view of one (batch, KV head) cache.
+
+    [HQ-wiki] flowchart / "Key results" and [HQ-news] "What hybrid-precision
+    attention changes": most positions are held in low bit width, the
+    vertical-line positions and the recent window in high precision.
+    Reading: a retained token is stored only in 16-bit form (never also in
+    INT4), which is what makes the pages' "about 15% over strict 4-bit"
+    storage figure come out (see storage_ratio_vs_int4).
+    """
+    k: np.ndarray          # [T][D] exact 16-bit values (for kept/window rows)
+    v: np.ndarray
+    mode: np.ndarray       # [T] int8
+    k_codes: np.ndarray    # [T][D] uint8 (valid where mode == INT4)
+    v_codes: np.ndarray
+    k_s: np.ndarray        # [T][D/32] float16
+    k_z: np.ndarray
+    v_s: np.ndarray
+    v_z: np.ndarray
+    window: int
+    T0: int                # context length when the probe ran
+    col_scores: np.ndarray  # [T0] probe scores (used by the append rule)
+    tau: float
+    j_k: int
+
+    @property
+    def T(self) -> int:
+        return int(self.mode.shape[0])
+
+
+def build_cache(k: np.ndarray, v: np.ndarray, T: int, sel: Selection, window: int,
+                col_scores: np.ndarray) -> HybridCache:
+    """Quantize one (b, g) sequence into the hybrid cache (O4).
+
+    Kept set H = S u [T - W, T); every other position is INT4-quantized,
+    K and V alike.
+    """
+    D = k.shape[-1]
+    mode = np.full(T, MODE_INT4, dtype=np.int8)
+    mode[sel.idx] = MODE_KEPT
+    mode[max(0, T - window):T] = MODE_WINDOW
+    kk = k[:T].copy()
+    vv = v[:T].copy()
+    kc, ks, kz = int4_quantize(kk)
+    vc, vs, vz = int4_quantize(vv)
+    return HybridCache(kk, vv, mode, kc, vc, ks, kz, vs, vz, window, T,
+                       np.asarray(col_scores[:T], dtype=np.float64), sel.tau, sel.j_k)
+
+
+def cache_kv_hat(cache: HybridCache):
+    """Effective (K~, V~) seen by attention: exact on kept/window positions,
+    dequantized INT4 elsewhere."""
+    kq = int4_dequantize(cache.k_codes, cache.k_s, cache.k_z)
+    vq = int4_dequantize(cache.v_codes, cache.v_s, cache.v_z)
+    hi = (cache.mode != MODE_INT4)[:, None]
+    return np.where(hi, cache.k, kq), np.where(hi, cache.v, vq)
+
+
+def append_token(cache: HybridCache, k_new: np.ndarray, v_new: np.ndarray) -> HybridCache:
+    """One decode-time append (O6).
+
+    The new token p = T enters the window. The token that leaves the window,
+    d = T - W (when T >= W), is kept in 16-bit form when it was probed
+    (d < T0) and its probe score ranks above the k-th selected candidate (it
+    would have been selected had it been a candidate), and is quantized to
+    INT4 otherwise. Tokens generated after the probe always quantize when
+    they leave the window. Reading of "tokens leaving the window are
+    quantized unless selected".
+    """
+    T, W = cache.T, cache.window
+    D = cache.k.shape[-1]
+    k = np.vstack([cache.k, k_new.reshape(1, D)])
+    v = np.vstack([cache.v, v_new.reshape(1, D)])
+    mode = np.concatenate([cache.mode, [MODE_WINDOW]]).astype(np.int8)
+    grow = lambda a, fill: np.concatenate([a, np.full((1,) + a.shape[1:], fill, dtype=a.dtype)])
+    kc, vc = grow(cache.k_codes, 0), grow(cache.v_codes, 0)
+    ks, kz, vs, vz = (grow(a, 0) for a in (cache.k_s, cache.k_z, cache.v_s, cache.v_z))
+    T1 = T + 1
+    for d in np.nonzero((mode == MODE_WINDOW) & (np.arange(T1) < T1 - W))[0]:
+        probed = d < cache.T0
+        if probed and ranks_above(float(cache.col_scores[d]), int(d), cache.tau, cache.j_k):
+            mode[d] = MODE_KEPT
+        else:
+            mode[d] = MODE_INT4
+            c1, s1, z1 = int4_quantize(k[d:d + 1])
+            kc[d], ks[d], kz[d] = c1[0], s1[0], z1[0]
+            c2, s2, z2 = int4_quantize(v[d:d + 1])
+            vc[d], vs[d], vz[d] = c2[0], s2[0], z2[0]
+    return HybridCache(k, v, mode, kc, vc, ks, kz, vs, vz, W, cache.T0, cache.col_scores,
+                       cache.tau, cache.j_k)
+
+
+def storage_ratio_vs_int4(T: int, window: int, k: int) -> float:
+    """Non-window bits per element relative to strict 4-bit storage.
+
+    [HQ-news] "Memory and runtime costs": at 5% retention the non-window
+    cache is about 15% larger than strict 4-bit. With retained tokens held
+    only in 16 bits: (k*16 + (T - W - k)*4) / ((T - W)*4).
+    """
+    n = T - window
+    return (k * 16 + (n - k) * 4) / (n * 4)
+
+
+# ---------------------------------------------------------------------------
+# O5: decode attention over the hybrid cache
+# ---------------------------------------------------------------------------
+
+
+def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float) -> np.ndarray:
+    """Plain softmax attention of G query vectors over T keys (no mask)."""
+    logits = (q @ K.T) * sm_scale
+    m = logits.max(axis=-1, keepdims=True)
+    e = np.exp(logits - m)
+    return (e @ V) / e.sum(axis=-1, keepdims=True)
+
+
+def decode_attention(q_group: np.ndarray, cache: HybridCache, sm_scale: float) -> np.ndarray:
+    """Decode attention of the G query heads of one KV head (O5).
+
+    [HQ-wiki] TL;DR / "Key results" and [HQ-abs]: decode attends over the
+    hybrid cache with dequantization fused into attention; numerically it is
+    softmax(q K~^T * sm_scale) V~ over all T cached tokens (the current one
+    included; no mask).
+    """
+    Kh, Vh = cache_kv_hat(cache)
+    return softmax_attention(q_group, Kh, Vh, sm_scale)
+
+
+# ---------------------------------------------------------------------------
+# O7: prefill INT8 block quantization
+# ---------------------------------------------------------------------------
+
+INT8_BLOCK = 64
+
+
+def int8_block_quantize(x: np.ndarray):
+    """Symmetric INT8 per 64-token block over all channels (O7).
+
+    [HQ-news] "What hybrid-precision attention changes" / [HQ-abs]: during
+    prefill the rest of the context is processed in low precision. Format
+    (reading): per block of 64 rows of one head, s = fp32_rne(max|x| / 127);
+    code = clamp(rint_even(fp32 x / s), -127, 127), 0 when s == 0. Decisions
+    in fp32 like the kernels.
+
+    x: [T][D] float64 exact values. Returns (codes int8 [T][D], s float32 [ceil(T/64)]).
+    """
+    T, D = x.shape
+    nb = (T + INT8_BLOCK - 1) // INT8_BLOCK
+    codes = np.zeros((T, D), dtype=np.int8)
+    scales = np.zeros(nb, dtype=np.float32)
+    for b in range(nb):
+        blk = x[b * INT8_BLOCK:(b + 1) * INT8_BLOCK].astype(np.float32)
+        amax = np.float32(np.abs(blk).max()) if blk.size else np.float32(0)
+        s = np.float32(amax / np.float32(127.0))
+        scales[b] = s
+        if s > 0:
+            codes[b * INT8_BLOCK:(b + 1) * INT8_BLOCK] = np.clip(np.rint(blk / s), -127, 127).astype(np.int8)
+    return codes, scales
+
+
+# ---------------------------------------------------------------------------
+# O8: prefill hybrid-precision attention
+# ---------------------------------------------------------------------------
+
+
+def prefill_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_idx: np.ndarray,
+                           window: int, sm_scale: float, q8: np.ndarray, sq: np.ndarray,
+                           k8: np.ndarray, sk: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """Causal hybrid-precision attention for one query head, selected rows (O8).
+
+    [HQ-abs] (Prefill stage) and [HQ-news] "What hybrid-precision attention
+    changes": selected positions and the local window are computed in full
+    precision, the remaining context in low precision; [HQ-wiki] "How this
+    relates to prior wiki pages": both precision paths update one softmax.
+
+    Score of (i, j <= i):
+      j in S or i - j < W : (q_i . k_j) * sm_scale              (exact)
+      otherwise           : (Q8_i . K8_j) * sQ(i) * sK(j) * sm_scale
+    o_i = sum_j softmax_j(score) v_j with exact V.
+
+    q: [T][D], k, v: [T][D] (this head's KV head), q8/sq: this query head's
+    INT8 codes/scales, k8/sk: the KV head's; rows: query positions to compute.
+    Returns [len(rows)][D].
+    """
+    T, D = k.shape
+    in_sel = np.zeros(T, dtype=bool)
+    in_sel[sel_idx] = True
+    k8f = k8.astype(np.float64)
+    skf = sk.astype(np.float64)[np.arange(T) // INT8_BLOCK]
+    out = np.empty((len(rows), D), dtype=np.float64)
+    for n, i in enumerate(rows):
+        i = int(i)
+        j = np.arange(i + 1)
+        exact = k[:i + 1] @ q[i]
+        low = (k8f[:i + 1] @ q8[i].astype(np.float64)) * float(sq[i // INT8_BLOCK]) * skf[:i + 1]
+        use_exact = in_sel[:i + 1] | (i - j < window)
+        logits = np.where(use_exact, exact, low) * sm_scale
+        m = logits.max()
+        e = np.exp(logits - m)
+        out[n] = (e @ v[:i + 1]) / e.sum()
+    return out
+
+
+def prefill_attention_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_idx: np.ndarray,
+                            window: int, sm_scale: float, q8: np.ndarray, sq: np.ndarray,
+                            k8: np.ndarray, sk: np.ndarray, r0: int, r1: int) -> np.ndarray:
+    """Same definition as prefill_attention_rows for the contiguous rows
+    [r0, r1), written with matrix products (one fp64 GEMM per precision)."""
+    T, D = k.shape
+    rows = np.arange(r0, r1)
+    cols = np.arange(r1)
+    in_sel = np.zeros(r1, dtype=bool)
+    in_sel[sel_idx[sel_idx < r1]] = True
+    exact = q[r0:r1] @ k[:r1].T
+    low = (q8[r0:r1].astype(np.float64) @ k8[:r1].astype(np.float64).T)
+    low *= sq.astype(np.float64)[rows // INT8_BLOCK][:, None]
+    low *= sk.astype(np.float64)[cols // INT8_BLOCK][None, :]
+    diff = rows[:, None] - cols[None, :]
+    use_exact = in_sel[None, :] | (diff < window)
+    logits = np.where(use_exact, exact, low) * sm_scale
+    logits[diff < 0] = -np.inf
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    return (e @ v[:r1]) / e.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# Whole-batch drivers (numpy in, numpy out)
+# ---------------------------------------------------------------------------
+
+
+def probe_select_batch(q_probe: np.ndarray, k: np.ndarray, seq_lens, sm_scale: float,
+                       window: int, keep_num: int, keep_den: int):
+    """O1 + O2 for every (b, g). Returns (scores list[b] -> [Hkv][T_b],
+    selections list[b][g])."""
+    B = q_probe.shape[0]
+    Hkv = k.shape[1]
+    scores, sels = [], []
+    for b in range(B):
+        T = int(seq_lens[b])
+        c = probe_column_scores(q_probe[b], k[b], T, sm_scale)
+        scores.append(c)
+        sels.append([select_topk(c[g], T, window, keep_num, keep_den) for g in range(Hkv)])
+    return scores, sels
+
+
+def decode_batch(q: np.ndarray, caches, sm_scale: float) -> np.ndarray:
+    """O5 over the batch: q [B][Hq][D], caches[b][g] -> out [B][Hq][D]."""
+    B, Hq, D = q.shape
+    Hkv = len(caches[0])
+    G = Hq // Hkv
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for g in range(Hkv):
+            out[b, g * G:(g + 1) * G] = decode_attention(q[b, g * G:(g + 1) * G], caches[b][g], sm_scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Diagnostics (parity unpinned: measurements, not definitions)
+# ---------------------------------------------------------------------------
+
+
+def kept_mass_coverage(q_group: np.ndarray, K: np.ndarray, mode: np.ndarray, sm_scale: float) -> float:
+    """Fraction of the exact attention mass that falls on kept/window tokens
+    ([HQ-news] "Why preserve selected positions?" reports this for real
+    models; here it is only a synthetic analogue). parity unpinned."""
+    logits = (q_group @ K.T) * sm_scale
+    p = np.exp(logits - logits.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    return float(p[:, mode != MODE_INT4].sum(axis=-1).mean())
