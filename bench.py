@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the HyQuant-style hybrid-precision attention hot path on one
+MI355X.
+
+One step = one pass of every row of the hot path over one batch of seeded
+synthetic input:
+  decode workload (8B GQA shape: B=16, 32 Q / 8 KV heads, D=128, T=32768):
+    probe + top-k select -> quantize/pack -> append one token -> decode
+    (prep + split-K + cross-split reduce);
+  prefill workload (32 Q / 8 KV heads, causal, T=16384):
+    probe + select on the last 64 rows -> INT8 block quantization + hybrid
+    attention (skipped if the prefill operator is not built).
+Inputs are resident in HBM before timing starts. Every kernel call is
+bracketed by HIP events on the stream it is launched on (torch's current
+stream); `value` is the decode attention time per step (hq_decode_attn) in
+microseconds; the other rows are reported beside it.
+
+Prints ONE JSON line (see README of the output fields in the design doc).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0
+MFMA_I8_TOPS = 5000.0
+MFMA_F64_TFLOPS = 78.6
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only append+decode per step (profiling aid)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run a plain device copy of this size (HBM counter calibration) and exit")
+    return ap.parse_args()
+
+
+def _dev16(a, dtype, dev):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to(dev)
+
+
+class Timer:
+    """HIP-event timing of one labelled call on the current stream."""
+
+    def __init__(self):
+        self.ev = {}
+
+    def __call__(self, name, fn, *a, **kw):
+        import torch
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        r = fn(*a, **kw)
+        e.record()
+        self.ev.setdefault(name, []).append((s, e))
+        return r
+
+    def ms(self, name):
+        v = [s.elapsed_time(e) for s, e in self.ev.get(name, [])]
+        return sum(v) / len(v) if v else float("nan")
+
+    def reset(self):
+        self.ev = {}
+
+
+def decode_bytes_per_step(counts):
+    """Algorithmic HBM bytes of one decode over the cache: 160 B per INT4
+    token-head (64+64 code bytes, 2x16 meta bytes), 512 B per 16-bit token-head."""
+    T, nq, nk = counts[..., 0], counts[..., 1], counts[..., 2]
+    nring = T.clip(max=128)
+    return int((nq * 160 + (nk + nring) * 512).sum())
+
+
+def prefill_flops(T, Hq, B=1):
+    pairs = T * (T + 1) // 2
+    return 4.0 * 128 * pairs * Hq * B
+
+
+def cpu_baseline(inp, sels_gpu, budget_s=20.0):
+    """The oracle (numpy fp64) timed on this host on a bounded sample of the
+    decode workload: whole (b, g) units of one decode step, scaled to the
+    full step."""
+    import numpy as np
+    import oracle as O
+    sp = inp.spec
+    sm = 1 / math.sqrt(sp.D)
+    G = sp.Hq // sp.Hkv
+    col, sel, cnt, thr = sels_gpu
+    t_units = []
+    n = 0
+    start = time.perf_counter()
+    for b in range(sp.B):
+        for g in range(sp.Hkv):
+            if time.perf_counter() - start > budget_s:
+                break
+            T = int(inp.seq_lens[b])
+            t0 = time.perf_counter()
+            k = O.to_f64(inp.k[b, g, :T], sp.dtype)
+            v = O.to_f64(inp.v[b, g, :T], sp.dtype)
+            idx = sel[b, g, : cnt[b, g]].astype(np.int64)
+            c = O.build_cache(k, v, T, O.Selection(idx, len(idx), float(thr[b, g, 0:1].view(np.float32)[0]),
+                                                   int(thr[b, g, 1])), 128, col[b, g, :T].astype(np.float64))
+            O.decode_attention(O.to_f64(inp.q[b, g * G:(g + 1) * G], sp.dtype), c, sm)
+            t_units.append(time.perf_counter() - t0)
+            n += 1
+    per_unit = sum(t_units) / len(t_units)
+    full_us = per_unit * sp.B * sp.Hkv * 1e6
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(full_us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {sp.B * sp.Hkv} (batch, KV head) units of one 32K decode step "
+                      f"(cache build + fp64 attention), {sum(t_units):.1f} s, scaled x{sp.B * sp.Hkv / n:.1f}",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import kv_cache_amd as hq
+    from synth.inputs import CONFIGS, make_append_tokens, make_decode_inputs, make_prefill_inputs
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n}))
+        return
+
+    t_gen = time.perf_counter()
+    spec = CONFIGS["c2_decode_8b_32k"]
+    inp = make_decode_inputs(spec)
+    kn, vn, qn = make_append_tokens(spec, inp.outlier_channels, 1)
+    print(f"# generated decode inputs in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    pol = hq.Policy()
+    B, Hq, Hkv, T, D = spec.B, spec.Hq, spec.Hkv, spec.T, spec.D
+    k = _dev16(inp.k, "bf16", dev)
+    v = _dev16(inp.v, "bf16", dev)
+    qp = _dev16(inp.q_probe, "bf16", dev)
+    q = _dev16(qn[0], "bf16", dev)
+    knew, vnew = _dev16(kn[0], "bf16", dev), _dev16(vn[0], "bf16", dev)
+    lens = torch.from_numpy(inp.seq_lens).to(dev)
+    cache = hq.HybridCache(B, Hkv, T + 64, T, torch.bfloat16, dev, pol)
+
+    pf = None
+    if not args.no_prefill and not args.decode_only:
+        pspec = CONFIGS["c4_prefill_8b_16k"]
+        pin = make_prefill_inputs(pspec)
+        pf = dict(spec=pspec, q=_dev16(pin.q, "bf16", dev), k=_dev16(pin.k, "bf16", dev),
+                  v=_dev16(pin.v, "bf16", dev), lens=torch.full((1,), pspec.T, dtype=torch.int32, device=dev))
+        pf["qprobe"] = pf["q"][:, :, pspec.T - 64:].contiguous()
+        pf["out"] = torch.empty((1, pspec.Hq, pspec.T, 128), dtype=torch.float32, device=dev)
+        del pin
+        print(f"# generated prefill inputs", file=sys.stderr, flush=True)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    tm = Timer()
+    prefill_ok = pf is not None
+
+    def step():
+        nonlocal prefill_ok
+        if not args.decode_only:
+            sel4 = tm("probe_select", hq.probe_select, qp, k, lens, pol)
+            tm("quantize_kv", hq.quantize_kv, cache, k, v, lens, *sel4)
+        else:
+            sel4 = None
+        tm("append_kv", hq.append_kv, cache, knew, vnew)
+        tm("decode_attn", hq.decode_attn, cache, q, None, out)
+        if prefill_ok:
+            psel = tm("prefill_probe_select", hq.probe_select, pf["qprobe"], pf["k"], pf["lens"], pol)
+            try:
+                tm("prefill_attn", hq.prefill_attn, pf["q"], pf["k"], pf["v"], psel[1], psel[2], pol, None, pf["out"])
+            except hq.HQError as e:
+                if e.status != hq.HQ_ERR_UNSUPPORTED:
+                    raise
+                prefill_ok = False
+        return sel4
+
+    if args.decode_only:
+        sel4 = hq.probe_select(qp, k, lens, pol)
+        hq.quantize_kv(cache, k, v, lens, *sel4)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tm.reset()
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    s0.record()
+    for _ in range(args.steps):
+        sel4 = step()
+    s1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = s0.elapsed_time(s1) / args.steps
+
+    counts = cache.counts().cpu().numpy()
+    dec_ms = tm.ms("decode_attn")
+    dbytes = decode_bytes_per_step(counts)
+    res = {
+        "metric": "hybrid decode attn us/step + achieved HBM TB/s @32K; prefill TFLOP/s",
+        "value": round(dec_ms * 1e3, 2),
+        "unit": "us/step",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4+bf16 cache, fp32 accumulate",
+        "data": "synthetic (seeded; Llama-3.1-8B attention shapes, outlier K channels, planted vertical lines)",
+        "config": {"workload": "decode_8b_gqa_b16_32k (+ prefill_8b_gqa_16k causal)", "B": B, "Hq": Hq,
+                   "Hkv": Hkv, "T": T, "head_dim": D, "keep": "top-5% + 128 window", "int4_group": 32},
+        "decode_us": round(dec_ms * 1e3, 2),
+        "decode_TBps": round(dbytes / (dec_ms * 1e-3) / 1e12, 3),
+        "decode_bytes": dbytes,
+        "append_us": round(tm.ms("append_kv") * 1e3, 2),
+        "wall_s": round(wall, 3),
+    }
+    if not args.decode_only:
+        res["probe_select_ms"] = round(tm.ms("probe_select"), 3)
+        res["quantize_ms"] = round(tm.ms("quantize_kv"), 3)
+    res["roofline"] = {"bound": "hbm", "kernel": "hq_decode_attn (prep + split-K + reduce)",
+                       "achieved": round(dbytes / (dec_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                       "unit": "GB/s", "frac": round(dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                       "traffic": None}
+    if prefill_ok:
+        pms = tm.ms("prefill_attn")
+        fl = prefill_flops(pf["spec"].T, pf["spec"].Hq)
+        res["prefill_ms"] = round(pms, 3)
+        res["prefill_TFLOPs"] = round(fl / (pms * 1e-3) / 1e12, 1)
+        res["prefill_probe_select_ms"] = round(tm.ms("prefill_probe_select"), 3)
+    if not args.no_cpu_baseline:
+        sels = tuple(t.cpu().numpy() for t in (hq.probe_select(qp, k, lens, pol)))
+        res["cpu_baseline"] = cpu_baseline(inp, sels)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

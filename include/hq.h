@@ -1,0 +1,251 @@
+/* hq.h -- C ABI of libhyquant: HyQuant-style hybrid-precision attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages: "HyQuant: Hybrid-Precision Quantization for LLM
+ * Attention", TL;DR and flowchart; "How HyQuant uses hybrid-precision
+ * attention to cut decode compute", "What hybrid-precision attention
+ * changes"; the HyQuant abstract on the ACL Anthology author page):
+ * a cheap vertical-line-aware probe of the attention pattern picks the key
+ * columns that nearly every query attends to; those columns plus a recent
+ * local window stay in high precision and everything else is quantized to
+ * low bit width. Prefill runs a hybrid-precision attention operator with
+ * that split; decode keeps a hybrid KV cache and fuses dequantization into
+ * the attention kernel so dequantized values never go back to memory.
+ *
+ * The five calls below follow that statement of the problem:
+ *   hq_probe_select  -- the probe and the top-k column selection
+ *   hq_quantize_kv   -- build the hybrid cache (INT4 rest + 16-bit kept/window)
+ *   hq_append_kv     -- one decode-time token append (the window slides)
+ *   hq_decode_attn   -- decode attention with fused INT4 dequantization
+ *   hq_prefill_attn  -- the causal prefill hybrid-precision operator
+ *
+ * Conventions shared by every call
+ *   - Device pointers unless stated otherwise. All work is enqueued on
+ *     `stream` (a hipStream_t passed as void*; NULL = the null stream) and is
+ *     asynchronous; no call synchronizes, allocates device memory, frees, or
+ *     changes the current device. Buffers are owned by the caller; the *_bytes
+ *     and hq_cache_layout queries give their sizes.
+ *   - Tensors are contiguous, row-major, in the shapes written next to each
+ *     argument. 16-bit tensors use `dt` (HQ_BF16 or HQ_F16); head_dim D must
+ *     be 128; Hq must be a multiple of Hkv (grouped-query attention: query
+ *     head h reads KV head h / (Hq/Hkv)); Hq/Hkv must be 1, 2, 4 or 8.
+ *   - All device pointers must be 16-byte aligned. Outputs must not alias
+ *     inputs.
+ *   - Every argument is validated on the host before anything is launched.
+ *     On error nothing is enqueued, no output is written, the call returns a
+ *     negative status and hq_last_error() describes the problem. A failed
+ *     kernel launch returns HQ_ERR_HIP with the HIP error string.
+ *   - The library holds no global state and is safe to call from several
+ *     threads (each thread has its own hq_last_error buffer).
+ */
+#ifndef HQ_H_
+#define HQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int hq_status;
+#define HQ_OK 0
+#define HQ_ERR_INVALID_ARG (-1) /* null pointer, bad size, misalignment, bad policy */
+#define HQ_ERR_UNSUPPORTED (-2) /* D != 128, Hq % Hkv != 0, group size, dtype      */
+#define HQ_ERR_CAPACITY (-3)    /* workspace or cache capacity too small           */
+#define HQ_ERR_HIP (-4)         /* kernel launch failed                            */
+
+typedef enum { HQ_F16 = 0, HQ_BF16 = 1, HQ_F32 = 2 } hq_dtype;
+
+/* Retention policy. Pages: "How HyQuant uses hybrid-precision attention to
+ * cut decode compute", sections "Why preserve selected positions?" and "What
+ * the authors tested": the top 5% of key positions plus a local window (128
+ * tokens in the coverage analysis) stay in high precision.
+ *   keep_num/keep_den : retained fraction; k = floor(keep_num*T/keep_den),
+ *                       capped at the T - window candidates (default 5/100)
+ *   window            : recent positions always kept; multiple of 64 (128)
+ *   probe_rows        : last query rows the probe looks at (64)            */
+typedef struct {
+    int32_t keep_num;
+    int32_t keep_den;
+    int32_t window;
+    int32_t probe_rows;
+} hq_policy;
+
+/* Score and position of the k-th selected candidate (k > 0), or
+ * {+inf, -1} when nothing was selected. */
+typedef struct {
+    float tau;
+    int32_t j_k;
+} hq_thresh;
+
+/* Size in elements of the per-(batch, KV head) selected-index stride for a
+ * context of up to T tokens: max(1, floor(keep_num*T/keep_den)). */
+int32_t hq_sel_stride(int32_t T, const hq_policy* policy);
+
+/* ------------------------------------------------------------------------
+ * hq_probe_select -- vertical-line probe + top-k column selection.
+ * Pages: "HyQuant: Hybrid-Precision Quantization for LLM Attention", TL;DR
+ * and "What problem it solves" (a few key columns are attended by almost
+ * every query, found with a lightweight pattern signal, no calibration);
+ * "How HyQuant uses ...", "Why preserve selected positions?" (retain the
+ * high-score positions, top 5%).
+ * Computes, for each batch b and KV head g, with T = seq_lens[b]:
+ *   col_scores[b][g][j] = sum over the Hq/Hkv query heads of g and the last
+ *     R = min(probe_rows, T) rows r (at positions T-R..T-1) of
+ *     softmax_{j' <= pos_r}(q_r . k_j' * sm_scale)[j],  for j < T
+ *   sel_idx[b][g][0..k)  = the k candidates j in [0, T - window) with the
+ *     largest score (ties: lower j first), in ascending order; k as in
+ *     hq_policy. sel_count[b][g] = k; thresh[b][g] = the k-th one.
+ * Logits are formed exactly (fp64 accumulation of the exact products);
+ * softmax normalisers and column sums accumulate in fp64; scores are
+ * returned as fp32.
+ *   q_probe   [B][Hq][probe_rows][D] dt  row r is position T_b - probe_rows + r
+ *   k         [B][Hkv][Tmax][D]      dt
+ *   seq_lens  [B] int32, 1 <= T_b <= Tmax
+ *   col_scores[B][Hkv][Tmax] fp32 out (entries >= T_b are set to 0)
+ *   sel_idx   [B][Hkv][hq_sel_stride(Tmax)] int32 out (unused tail = -1)
+ *   sel_count [B][Hkv] int32 out;  thresh [B][Hkv] out
+ *   ws        workspace of hq_probe_ws_bytes(...) bytes                    */
+hq_status hq_probe_select(const void* q_probe, const void* k, const int32_t* seq_lens,
+                          int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32_t D,
+                          hq_dtype dt, const hq_policy* policy, float sm_scale,
+                          float* col_scores, int32_t* sel_idx, int32_t* sel_count,
+                          hq_thresh* thresh, void* ws, size_t ws_bytes, void* stream);
+size_t hq_probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32_t D,
+                         const hq_policy* policy);
+
+/* ------------------------------------------------------------------------
+ * The hybrid KV cache. Pages: "HyQuant: ...", flowchart and "Key results"
+ * (decode keeps a hybrid cache; dequantization fused into attention);
+ * "How HyQuant uses ...", "What the authors tested" (non-retained KV in
+ * Key-4bit/Value-4bit) and "Memory and runtime costs" (retention costs about
+ * 15% over strict 4-bit, i.e. retained tokens are held only in 16 bits).
+ *
+ * Per (batch b, KV head g) the cache holds
+ *   INT4 store : every position that is neither selected nor in the window,
+ *                ascending; per token and per 32-channel group of K and of
+ *                V: asymmetric codes (0..15), fp16 scale s and zero z with
+ *                x_hat = code*s + z, where s = fp16(fp32(max-min)/15),
+ *                z = fp16(min), code = clamp(rint((x - z)/s), 0, 15) in fp32.
+ *   kept store : the selected positions (and departures flagged by the append
+ *                rule), 16-bit, in insertion order.
+ *   ring       : the last `window` positions, 16-bit, slot = position % window.
+ * Storage is tiled in 64-token tiles laid out so that every 128-bit load of
+ * the decode kernel is contiguous across the wavefront:
+ *   K codes, tile byte  group*1024 + slot*16 + i : packed byte i of the
+ *       32-channel group (byte i = code[2i] | code[2i+1] << 4);
+ *   V codes, pre-paired: the 32-bit word for slots (2P, 2P+1) and channels
+ *       4Q..4Q+3 holds slot 2P's four nibbles in its low half and slot
+ *       2P+1's in its high half; it sits at (j/2)*1024 + (16u + Q/2)*16 +
+ *       ((j%2)*2 + Q%2)*4 with u = P/8, j = P%8;
+ *   16-bit K rows, chunk c (channels 8c..8c+7) of slot t at c*1024 + t*16;
+ *   16-bit V rows, chunk c of slot t at (t%16)*1024 + (16*(t/16) + c)*16.
+ * Position tags give the canonical order. The struct is filled by the caller
+ * with buffers of the sizes hq_cache_layout() returns; all counters live on
+ * the device so no call needs a device-to-host copy.                       */
+typedef struct {
+    int32_t B, Hkv, D, window;
+    int32_t cap_q;      /* INT4 slots per (b, g), multiple of 64              */
+    int32_t cap_keep;   /* kept-store slots per (b, g), multiple of 64        */
+    int32_t cap_probe;  /* probed positions per (b, g) (col_scores stride)    */
+    int32_t dt;         /* hq_dtype of the 16-bit stores (HQ_BF16 or HQ_F16)  */
+    void* k_codes;      /* [B][Hkv][cap_q/64][4096] bytes                     */
+    void* v_codes;      /* [B][Hkv][cap_q/64][4096] bytes                     */
+    void* k_meta;       /* [B][Hkv][cap_q][8] fp16: (s,z) x 4 groups          */
+    void* v_meta;       /* [B][Hkv][cap_q][8] fp16                            */
+    void* k_keep;       /* [B][Hkv][cap_keep/64][64*D] 16-bit                 */
+    void* v_keep;
+    void* k_win;        /* [B][Hkv][window/64][64*D] 16-bit                   */
+    void* v_win;
+    int32_t* q_pos;     /* [B][Hkv][cap_q] position of each INT4 slot         */
+    int32_t* keep_pos;  /* [B][Hkv][cap_keep] position of each kept slot      */
+    int32_t* counts;    /* [B][Hkv][4]: seq_len, n_q, n_keep, probe_len       */
+    float* col_scores;  /* [B][Hkv][cap_probe] probe scores kept for append   */
+    hq_thresh* thresh;  /* [B][Hkv]                                           */
+    int32_t* err_flag;  /* [1]: set nonzero by a kernel on capacity overflow  */
+} hq_cache;
+
+typedef struct {
+    int32_t cap_q, cap_keep, cap_probe;
+    size_t k_codes, v_codes, k_meta, v_meta, k_keep, v_keep, k_win, v_win;
+    size_t q_pos, keep_pos, counts, col_scores, thresh, err_flag;
+} hq_cache_sizes;
+
+/* Byte sizes of every cache buffer for contexts of up to cap_tokens tokens
+ * (prompt plus appends) whose probe covered at most cap_probe positions.   */
+hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens,
+                          int32_t cap_probe, hq_dtype dt, const hq_policy* policy,
+                          hq_cache_sizes* out);
+
+/* ------------------------------------------------------------------------
+ * hq_quantize_kv -- build the hybrid cache from a prompt's K and V.
+ * Kept set H = S u [T-W, T) with S = sel_idx[b][g][0..sel_count); every other
+ * position is INT4-quantized (K and V alike); the probe scores and threshold
+ * are copied into the cache for the append rule. Resets the cache counters.
+ *   k, v       [B][Hkv][Tmax][D] dt;  seq_lens [B] int32
+ *   sel_idx    [B][Hkv][hq_sel_stride(Tmax)] ascending; sel_count [B][Hkv]
+ *   col_scores [B][Hkv][Tmax] fp32; thresh [B][Hkv]
+ *   cache      host struct describing caller-owned buffers (Tmax <= cap_probe) */
+hq_status hq_quantize_kv(const void* k, const void* v, const int32_t* seq_lens, int32_t Tmax,
+                         const int32_t* sel_idx, const int32_t* sel_count,
+                         const float* col_scores, const hq_thresh* thresh,
+                         const hq_policy* policy, const hq_cache* cache, void* stream);
+
+/* ------------------------------------------------------------------------
+ * hq_append_kv -- append one token per (b, g) at position T = seq_len.
+ * The new token enters the ring. The token leaving the window, d = T - W
+ * (when T >= W), goes to the kept store if it was probed (d < probe_len) and
+ * its probe score ranks above the k-th selected candidate (it would have been
+ * selected had it been a candidate), and is INT4-quantized otherwise.
+ * Reading of "tokens leaving the window are quantized unless selected".
+ *   k_new, v_new [B][Hkv][D] cache->dt                                      */
+hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_new, void* stream);
+
+/* ------------------------------------------------------------------------
+ * hq_decode_attn -- one decode step of attention over the hybrid cache.
+ * Pages: "HyQuant: ...", TL;DR and "Key results" (KV dequantization fused
+ * with the attention computation); "How HyQuant uses ...", "What
+ * hybrid-precision attention changes" (no full-precision copy of the cache
+ * is ever expanded).
+ *   out[b][h] = sum_j softmax_j(q[b][h] . k~_j * sm_scale) v~_j over all
+ *   T = seq_len cached tokens of KV head h / (Hq/Hkv), with k~, v~ the 16-bit
+ *   values on kept/window positions and code*s + z elsewhere.
+ * INT4 codes are dequantized in registers; dot products accumulate in fp32;
+ * split-K partial softmax states are merged by a second kernel.
+ *   q   [B][Hq][D] cache->dt;  out [B][Hq][D] out_dt (HQ_F32 for parity)
+ *   ws  workspace of hq_decode_ws_bytes(cache, Hq) bytes                   */
+hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,
+                         void* out, hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
+size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq);
+
+/* ------------------------------------------------------------------------
+ * hq_prefill_attn -- causal hybrid-precision prefill attention.
+ * Pages: HyQuant abstract (Prefill stage: vertical-line tokens and a local
+ * sliding window in full precision, the remaining context quantized);
+ * "HyQuant: ...", "How this relates to prior wiki pages" (two precision
+ * paths updating one online-softmax state).
+ * For query row i of head h (KV head g) and key j <= i:
+ *   j in S_g or i - j < window : score = (q_i . k_j) * sm_scale   (bf16 MFMA)
+ *   otherwise : score = (Q8_i . K8_j) * sQ * sK * sm_scale          (INT8 MFMA)
+ * with symmetric INT8 per 64-token block over all channels (s = max|x|/127
+ * in fp32, code = rint(x/s)); out_i = sum_j softmax(score)_j v_j. P and V
+ * enter the PV product as fp16.
+ *   q [B][Hq][T][D], k, v [B][Hkv][T][D] dt; sel_idx/sel_count as returned
+ *   by hq_probe_select with Tmax = T; out [B][Hq][T][D] out_dt.            */
+hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,
+                          int32_t Hkv, int32_t T, int32_t D, hq_dtype dt,
+                          const hq_policy* policy, const int32_t* sel_idx,
+                          const int32_t* sel_count, float sm_scale, void* out,
+                          hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
+size_t hq_prefill_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t D,
+                           const hq_policy* policy);
+
+/* Description of the last error on the calling thread ("" if none). Valid
+ * until the next hq_* call on this thread. */
+const char* hq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HQ_H_ */

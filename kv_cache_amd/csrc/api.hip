@@ -1,0 +1,284 @@
+// Host side of libhyquant: argument validation, sizing and launches.
+// Every check runs before anything is enqueued; on error nothing is launched.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "hq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hq_status fail(hq_status code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+void clear_err() { g_err[0] = '\0'; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQ_PTR(p)                                                                           \
+    do {                                                                                     \
+        if ((p) == nullptr) return fail(HQ_ERR_INVALID_ARG, "%s: %s is null", fn, #p);        \
+        if (!aligned16(p)) return fail(HQ_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p); \
+    } while (0)
+
+hq_status check_policy(const char* fn, const hq_policy* p) {
+    if (!p) return fail(HQ_ERR_INVALID_ARG, "%s: policy is null", fn);
+    if (p->keep_den <= 0 || p->keep_num < 0 || p->keep_num > p->keep_den)
+        return fail(HQ_ERR_INVALID_ARG, "%s: retained fraction %d/%d must satisfy 0 <= num <= den, den > 0", fn,
+                    p->keep_num, p->keep_den);
+    if (p->window < 0 || p->window % hq::kTile != 0 || p->window > (1 << 20))
+        return fail(HQ_ERR_INVALID_ARG, "%s: window %d must be a non-negative multiple of 64", fn, p->window);
+    if (p->probe_rows < 1 || p->probe_rows > 256)
+        return fail(HQ_ERR_INVALID_ARG, "%s: probe_rows %d must be in [1, 256]", fn, p->probe_rows);
+    return HQ_OK;
+}
+
+hq_status check_heads(const char* fn, int32_t B, int32_t Hq, int32_t Hkv, int32_t D) {
+    if (B < 1 || Hq < 1 || Hkv < 1) return fail(HQ_ERR_INVALID_ARG, "%s: B, Hq, Hkv must be >= 1", fn);
+    if (D != hq::kD) return fail(HQ_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (only 128)", fn, D);
+    if (Hq % Hkv != 0) return fail(HQ_ERR_UNSUPPORTED, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+    const int G = Hq / Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(HQ_ERR_UNSUPPORTED, "%s: query heads per KV head %d unsupported (1, 2, 4, 8)", fn, G);
+    return HQ_OK;
+}
+
+hq_status check_dt(const char* fn, int dt) {
+    if (dt != HQ_BF16 && dt != HQ_F16) return fail(HQ_ERR_UNSUPPORTED, "%s: dtype %d unsupported (bf16, f16)", fn, dt);
+    return HQ_OK;
+}
+
+hq_status check_cache(const char* fn, const hq_cache* c) {
+    if (!c) return fail(HQ_ERR_INVALID_ARG, "%s: cache is null", fn);
+    if (c->B < 1 || c->Hkv < 1) return fail(HQ_ERR_INVALID_ARG, "%s: cache B/Hkv must be >= 1", fn);
+    if (c->D != hq::kD) return fail(HQ_ERR_UNSUPPORTED, "%s: cache head_dim %d unsupported", fn, c->D);
+    hq_status st = check_dt(fn, c->dt);
+    if (st) return st;
+    if (c->window < 0 || c->window % hq::kTile)
+        return fail(HQ_ERR_INVALID_ARG, "%s: cache window %d must be a multiple of 64", fn, c->window);
+    if (c->cap_q < hq::kTile || c->cap_q % hq::kTile || c->cap_keep < hq::kTile || c->cap_keep % hq::kTile)
+        return fail(HQ_ERR_INVALID_ARG, "%s: cache capacities must be positive multiples of 64", fn);
+    if (c->cap_probe < 1 || c->cap_probe > c->cap_q)
+        return fail(HQ_ERR_INVALID_ARG, "%s: cap_probe %d must be in [1, cap_q]", fn, c->cap_probe);
+    REQ_PTR(c->k_codes);
+    REQ_PTR(c->v_codes);
+    REQ_PTR(c->k_meta);
+    REQ_PTR(c->v_meta);
+    REQ_PTR(c->k_keep);
+    REQ_PTR(c->v_keep);
+    if (c->window > 0) {
+        REQ_PTR(c->k_win);
+        REQ_PTR(c->v_win);
+    }
+    REQ_PTR(c->q_pos);
+    REQ_PTR(c->keep_pos);
+    REQ_PTR(c->counts);
+    REQ_PTR(c->col_scores);
+    REQ_PTR(c->thresh);
+    if (c->err_flag == nullptr) return fail(HQ_ERR_INVALID_ARG, "%s: cache err_flag is null", fn);
+    return HQ_OK;
+}
+
+hq_status hip_fail(const char* fn, hipError_t e) {
+    return fail(HQ_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+}
+
+int32_t decode_tps() {
+    const char* s = std::getenv("HQ_DECODE_TPS");
+    int v = s ? std::atoi(s) : 0;
+    return v > 0 ? v : 16;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hq_last_error(void) { return g_err; }
+
+int32_t hq_sel_stride(int32_t T, const hq_policy* policy) {
+    if (!policy || policy->keep_den <= 0 || T < 0) return 1;
+    return hq::sel_stride(T, *policy);
+}
+
+hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens, int32_t cap_probe, hq_dtype dt,
+                          const hq_policy* policy, hq_cache_sizes* out) {
+    static const char* fn = "hq_cache_layout";
+    clear_err();
+    hq_status st = check_policy(fn, policy);
+    if (st) return st;
+    if (!out) return fail(HQ_ERR_INVALID_ARG, "%s: out is null", fn);
+    if (B < 1 || Hkv < 1) return fail(HQ_ERR_INVALID_ARG, "%s: B and Hkv must be >= 1", fn);
+    if (D != hq::kD) return fail(HQ_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (only 128)", fn, D);
+    if ((st = check_dt(fn, dt))) return st;
+    if (cap_tokens < 1 || cap_tokens > (1 << 26))
+        return fail(HQ_ERR_INVALID_ARG, "%s: cap_tokens %d out of range", fn, cap_tokens);
+    if (cap_probe < 1 || cap_probe > cap_tokens)
+        return fail(HQ_ERR_INVALID_ARG, "%s: cap_probe %d must be in [1, cap_tokens]", fn, cap_probe);
+    const int32_t kmax = hq::keep_count(cap_probe, *policy);
+    const int32_t w = policy->window < cap_probe ? policy->window : cap_probe;
+    out->cap_q = hq::round_up(cap_tokens, hq::kTile);
+    int32_t ck = hq::round_up(kmax + w, hq::kTile);
+    out->cap_keep = ck < hq::kTile ? hq::kTile : ck;
+    out->cap_probe = cap_probe;
+    const size_t BG = (size_t)B * Hkv;
+    out->k_codes = out->v_codes = BG * (size_t)out->cap_q / 2 * hq::kD;  // 64 B per token
+    out->k_meta = out->v_meta = BG * (size_t)out->cap_q * 16;
+    out->k_keep = out->v_keep = BG * (size_t)out->cap_keep * hq::kD * 2;
+    out->k_win = out->v_win = BG * (size_t)policy->window * hq::kD * 2;
+    out->q_pos = BG * (size_t)out->cap_q * 4;
+    out->keep_pos = BG * (size_t)out->cap_keep * 4;
+    out->counts = BG * 16;
+    out->col_scores = BG * (size_t)cap_probe * 4;
+    out->thresh = BG * sizeof(hq_thresh);
+    out->err_flag = 4;
+    return HQ_OK;
+}
+
+size_t hq_probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32_t D, const hq_policy* policy) {
+    if (!policy || B < 1 || Hq < 1 || Hkv < 1 || Tmax < 1 || D != hq::kD || Hq % Hkv) return 0;
+    return hq::probe_ws_bytes(B, Hq, Hkv, Tmax, *policy);
+}
+
+hq_status hq_probe_select(const void* q_probe, const void* k, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                          int32_t Hkv, int32_t Tmax, int32_t D, hq_dtype dt, const hq_policy* policy,
+                          float sm_scale, float* col_scores, int32_t* sel_idx, int32_t* sel_count,
+                          hq_thresh* thresh, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "hq_probe_select";
+    clear_err();
+    hq_status st;
+    if ((st = check_policy(fn, policy))) return st;
+    if ((st = check_heads(fn, B, Hq, Hkv, D))) return st;
+    if ((st = check_dt(fn, dt))) return st;
+    if (Tmax < 1 || Tmax > (1 << 24)) return fail(HQ_ERR_INVALID_ARG, "%s: Tmax %d out of range", fn, Tmax);
+    if (!(sm_scale > 0.0f) || sm_scale > 1e6f) return fail(HQ_ERR_INVALID_ARG, "%s: sm_scale must be positive", fn);
+    REQ_PTR(q_probe);
+    REQ_PTR(k);
+    REQ_PTR(seq_lens);
+    REQ_PTR(col_scores);
+    REQ_PTR(sel_idx);
+    REQ_PTR(sel_count);
+    REQ_PTR(thresh);
+    const size_t need = hq::probe_ws_bytes(B, Hq, Hkv, Tmax, *policy);
+    if (need > 0) REQ_PTR(ws);
+    if (ws_bytes < need)
+        return fail(HQ_ERR_CAPACITY, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    hipError_t e = hq::launch_probe(q_probe, k, seq_lens, B, Hq, Hkv, Tmax, dt == HQ_F16, *policy, sm_scale,
+                                    col_scores, sel_idx, sel_count, thresh, ws, (hipStream_t)stream);
+    if (e == hipErrorNotSupported) return fail(HQ_ERR_UNSUPPORTED, "%s: not available in this build", fn);
+    return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
+}
+
+hq_status hq_quantize_kv(const void* k, const void* v, const int32_t* seq_lens, int32_t Tmax, const int32_t* sel_idx,
+                         const int32_t* sel_count, const float* col_scores, const hq_thresh* thresh,
+                         const hq_policy* policy, const hq_cache* cache, void* stream) {
+    static const char* fn = "hq_quantize_kv";
+    clear_err();
+    hq_status st;
+    if ((st = check_policy(fn, policy))) return st;
+    if ((st = check_cache(fn, cache))) return st;
+    if (policy->window != cache->window)
+        return fail(HQ_ERR_INVALID_ARG, "%s: policy window %d != cache window %d", fn, policy->window, cache->window);
+    if (Tmax < 1 || Tmax > cache->cap_probe || Tmax > cache->cap_q)
+        return fail(HQ_ERR_CAPACITY, "%s: Tmax %d exceeds the cache capacity (cap_probe %d)", fn, Tmax,
+                    cache->cap_probe);
+    if (hq::keep_count(Tmax, *policy) > cache->cap_keep)
+        return fail(HQ_ERR_CAPACITY, "%s: kept store capacity %d < %d", fn, cache->cap_keep,
+                    hq::keep_count(Tmax, *policy));
+    REQ_PTR(k);
+    REQ_PTR(v);
+    REQ_PTR(seq_lens);
+    REQ_PTR(sel_idx);
+    REQ_PTR(sel_count);
+    REQ_PTR(col_scores);
+    REQ_PTR(thresh);
+    hipError_t e = hq::launch_quantize(k, v, seq_lens, Tmax, sel_idx, sel_count, hq::sel_stride(Tmax, *policy),
+                                       col_scores, thresh, *cache, (hipStream_t)stream);
+    return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
+}
+
+hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_new, void* stream) {
+    static const char* fn = "hq_append_kv";
+    clear_err();
+    hq_status st;
+    if ((st = check_cache(fn, cache))) return st;
+    REQ_PTR(k_new);
+    REQ_PTR(v_new);
+    hipError_t e = hq::launch_append(*cache, k_new, v_new, (hipStream_t)stream);
+    return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
+}
+
+size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq) {
+    if (!cache || cache->Hkv < 1 || Hq < 1 || Hq % cache->Hkv) return 0;
+    const int32_t tps = decode_tps();
+    const int32_t nsplit = (hq::decode_max_tiles(*cache) + tps - 1) / tps;
+    return hq::decode_ws_bytes(*cache, Hq, nsplit);
+}
+
+hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale, void* out,
+                         hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "hq_decode_attn";
+    clear_err();
+    hq_status st;
+    if ((st = check_cache(fn, cache))) return st;
+    if ((st = check_heads(fn, cache->B, Hq, cache->Hkv, cache->D))) return st;
+    if (out_dt != HQ_F32 && out_dt != HQ_BF16 && out_dt != HQ_F16)
+        return fail(HQ_ERR_UNSUPPORTED, "%s: out dtype %d unsupported", fn, out_dt);
+    if (!(sm_scale > 0.0f) || sm_scale > 1e6f) return fail(HQ_ERR_INVALID_ARG, "%s: sm_scale must be positive", fn);
+    REQ_PTR(q);
+    REQ_PTR(out);
+    REQ_PTR(ws);
+    hq::DecodeLaunch d;
+    d.Hq = Hq;
+    d.G = Hq / cache->Hkv;
+    d.tiles_per_split = decode_tps();
+    d.nsplit = (hq::decode_max_tiles(*cache) + d.tiles_per_split - 1) / d.tiles_per_split;
+    d.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+    d.ws = ws;
+    const size_t need = hq::decode_ws_bytes(*cache, Hq, d.nsplit);
+    if (ws_bytes < need) return fail(HQ_ERR_CAPACITY, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    hipError_t e = hq::launch_decode(*cache, q, out, out_dt, d, (hipStream_t)stream);
+    return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
+}
+
+size_t hq_prefill_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t D, const hq_policy* policy) {
+    if (!policy || B < 1 || Hq < 1 || Hkv < 1 || T < 1 || D != hq::kD || Hq % Hkv) return 0;
+    return hq::prefill_ws_bytes(B, Hq, Hkv, T, *policy);
+}
+
+hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
+                          int32_t D, hq_dtype dt, const hq_policy* policy, const int32_t* sel_idx,
+                          const int32_t* sel_count, float sm_scale, void* out, hq_dtype out_dt, void* ws,
+                          size_t ws_bytes, void* stream) {
+    static const char* fn = "hq_prefill_attn";
+    clear_err();
+    hq_status st;
+    if ((st = check_policy(fn, policy))) return st;
+    if ((st = check_heads(fn, B, Hq, Hkv, D))) return st;
+    if ((st = check_dt(fn, dt))) return st;
+    if (T < 1 || T > (1 << 22)) return fail(HQ_ERR_INVALID_ARG, "%s: T %d out of range", fn, T);
+    if (out_dt != HQ_F32 && out_dt != HQ_BF16 && out_dt != HQ_F16)
+        return fail(HQ_ERR_UNSUPPORTED, "%s: out dtype %d unsupported", fn, out_dt);
+    if (!(sm_scale > 0.0f) || sm_scale > 1e6f) return fail(HQ_ERR_INVALID_ARG, "%s: sm_scale must be positive", fn);
+    REQ_PTR(q);
+    REQ_PTR(k);
+    REQ_PTR(v);
+    REQ_PTR(sel_idx);
+    REQ_PTR(sel_count);
+    REQ_PTR(out);
+    const size_t need = hq::prefill_ws_bytes(B, Hq, Hkv, T, *policy);
+    REQ_PTR(ws);
+    if (ws_bytes < need) return fail(HQ_ERR_CAPACITY, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    hipError_t e = hq::launch_prefill(q, k, v, B, Hq, Hkv, T, dt == HQ_F16, *policy, sel_idx, sel_count,
+                                      hq::sel_stride(T, *policy), sm_scale, out, out_dt, ws, (hipStream_t)stream);
+    if (e == hipErrorNotSupported) return fail(HQ_ERR_UNSUPPORTED, "%s: not available in this build", fn);
+    return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
+}
+
+}  // extern "C"

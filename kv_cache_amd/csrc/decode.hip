@@ -1,0 +1,514 @@
+// hq_decode_attn: split-K decode attention over the hybrid KV cache (gfx950).
+//
+// HyQuant pages: "HyQuant: Hybrid-Precision Quantization for LLM
+// Attention", TL;DR and "Key results" (KV dequantization fused into the
+// decode attention so dequantized values never round-trip through memory);
+// "How HyQuant uses hybrid-precision attention to cut decode compute", "What
+// hybrid-precision attention changes" (no full-precision copy of the cache is
+// expanded first). The low-bit and 16-bit paths share one online-softmax
+// state ("HyQuant: ...", "How this relates to prior wiki pages").
+//
+// Design (MI355X, wave64, HBM-bound):
+//  * One workgroup = 4 waves = one (b, g) and a contiguous span of 64-token
+//    tiles (a split); every wave takes every 4th tile of the span. All G query
+//    heads of the KV head are processed together, so each cache byte is read
+//    once per step.
+//  * Token phase, lane = token: the lane loads its token's 64 B of K codes
+//    (4 x 128-bit, contiguous across the wave) and 16 B of K scales/zeros.
+//    Codes are turned into bf16 (or fp16) "128 + 8c" magic values with one
+//    shift + one and-or per pair and multiplied against the query with
+//    v_dot2 (exact products, fp32 accumulation); the per-group scale and
+//    zero are applied afterwards: q.k~ = s*(q/8 . (128+8c)) + (z - 16 s)*sum(q).
+//    The query pairs sit in scalar registers (uniform loads).
+//  * Online softmax per tile with a lazy rescale (only when the running max
+//    grows by more than 2^8), in log2 units with v_exp_f32.
+//  * Channel phase, lane = 8 channels x 16 tokens: the V codes are stored
+//    pre-transposed so each lane's four 128-bit loads hold exactly its
+//    channels for its tokens; p*s per token and group comes through LDS;
+//    PV accumulates in fp32 FMAs. z-terms (sum p*z) accumulate per lane in
+//    the token phase.
+//  * 16-bit tiles (kept columns, window ring) use the same loop with the
+//    16-bit rows instead of codes.
+//  * Each workgroup writes one partial (m, l, o[128]) per head; a second
+//    kernel merges the splits.
+#include "hq_internal.h"
+
+namespace hq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr float kLazy = 8.0f;  // log2-domain growth that triggers a rescale
+
+struct DecodeParams {
+    hq_cache c;
+    const uint32_t* qp;    // [B][Hkv][4][G][16]  pairs for the INT4 path (prescaled)
+    const uint32_t* qn;    // [B][Hkv][G][64]     natural pairs for the 16-bit path
+    const float* qsum;     // [B][Hkv][G][4]      per-group sum of q
+    float* part_m;         // [B][Hkv][nsplit][G]
+    float* part_l;         // [B][Hkv][nsplit][G]
+    float* part_o;         // [B][Hkv][nsplit][G][128]
+    int32_t nsplit, tps, G;
+    float scale2;          // sm_scale * log2(e)
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+template <bool F16>
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                      false);
+    else
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                               __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Four magic-biased code pairs from one dword of 8 nibbles (channels 8i+n).
+// Pair n holds channels (n, n+4). bf16: value 128 + 8c (code in bits 3..6);
+// fp16: value 1024 + 16c (code in bits 4..7).
+template <bool F16>
+__device__ inline void extract_pairs(uint32_t w, uint32_t* pr) {
+    if constexpr (F16) {
+        constexpr uint32_t M = 0x00F000F0u, C = 0x64006400u;
+        pr[0] = ((w << 4) & M) | C;
+        pr[1] = (w & M) | C;
+        pr[2] = ((w >> 4) & M) | C;
+        pr[3] = ((w >> 8) & M) | C;
+    } else {
+        constexpr uint32_t M = 0x00780078u, C = 0x43004300u;
+        pr[0] = ((w << 3) & M) | C;
+        pr[1] = ((w >> 1) & M) | C;
+        pr[2] = ((w >> 5) & M) | C;
+        pr[3] = ((w >> 9) & M) | C;
+    }
+}
+// sum over the group of q_d * (bias value): bf16 16*sum(q), fp16 64*sum(q).
+template <bool F16>
+constexpr float kBias = F16 ? 64.0f : 16.0f;
+
+__device__ inline uint32_t u4w(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__device__ inline void lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int G, bool F16>
+__global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
+    __shared__ float lds_ps[kWaves][kTile * 4 * G];       // [slot][group][head]
+    __shared__ float lds_m[kWaves][G], lds_l[kWaves][G];
+    __shared__ float lds_o[kWaves][G][kD];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int Hkv = p.c.Hkv, W = p.c.window;
+    const int bg = b * Hkv + g;
+    const int4 cnt = *reinterpret_cast<const int4*>(p.c.counts + 4 * bg);
+    const int T = cnt.x, n_q = cnt.y, n_keep = cnt.z;
+    const int nring = T < W ? T : W;
+    const int nqt = (n_q + kTile - 1) / kTile, nkt = (n_keep + kTile - 1) / kTile;
+    const int nwt = (nring + kTile - 1) / kTile;
+    const int total = nqt + nkt + nwt;
+    const int v0 = s * p.tps;
+    if (v0 >= total) return;
+    const int v1 = min(v0 + p.tps, total);
+
+    const int qt_cap = p.c.cap_q / kTile, kt_cap = p.c.cap_keep / kTile, wt_cap = W / kTile;
+    const uint32_t* qp = p.qp + (size_t)bg * 4 * G * 16;
+    const uint32_t* qn = p.qn + (size_t)bg * G * 64;
+    const float* qs = p.qsum + (size_t)bg * G * 4;
+
+    float m[G], l[G], zacc[G][4], acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zacc[h][i] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+    }
+    const int u = lane >> 4, c8 = lane & 15, gk = c8 >> 2;
+    float* ps_w = lds_ps[wave];
+
+    for (int v = v0 + wave; v < v1; v += kWaves) {
+        float lg[G];
+        bool int4_tile = v < nqt;
+        int count, tile_base_slot;
+        float vs[4], vz[4];
+        if (int4_tile) {
+            // ----------------------------- token phase, INT4 tile
+            const int tile = v;
+            tile_base_slot = tile * kTile;
+            count = n_q;
+            const bool valid = tile_base_slot + lane < n_q;
+            const uint8_t* kc = reinterpret_cast<const uint8_t*>(p.c.k_codes) +
+                                ((size_t)bg * qt_cap + tile) * kTileBytesQ;
+            const size_t slot_g = (size_t)bg * p.c.cap_q + tile_base_slot + lane;
+            uint4 kw[4];
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp)
+                kw[grp] = *reinterpret_cast<const uint4*>(kc + kcode_off(lane, grp));
+            uint4 km = reinterpret_cast<const uint4*>(p.c.k_meta)[slot_g];
+            uint4 vm = reinterpret_cast<const uint4*>(p.c.v_meta)[slot_g];
+            if (!valid) {
+                km = make_uint4(0, 0, 0, 0);
+                vm = km;
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) lg[h] = 0.f;
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const uint32_t mk = u4w(km, grp), mv = u4w(vm, grp);
+                const float sk = f16_to_f32(mk & 0xFFFFu), zk = f16_to_f32(mk >> 16);
+                vs[grp] = f16_to_f32(mv & 0xFFFFu);
+                vz[grp] = f16_to_f32(mv >> 16);
+                const float zz = zk - kBias<F16> * sk;
+                uint32_t pr[16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) extract_pairs<F16>(u4w(kw[grp], i), pr + 4 * i);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const uint32_t* qh = qp + (grp * G + h) * 16;
+                    float a = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) a = dot2<F16>(pr[e], qh[e], a);
+                    lg[h] = fmaf(sk, a, fmaf(zz, qs[h * 4 + grp], lg[h]));
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) lg[h] = valid ? lg[h] * p.scale2 : -INFINITY;
+        } else {
+            // ----------------------------- token phase, 16-bit tile
+            const bool keep = v < nqt + nkt;
+            const int tile = keep ? v - nqt : v - nqt - nkt;
+            tile_base_slot = tile * kTile;
+            count = keep ? n_keep : nring;
+            const bool valid = tile_base_slot + lane < count;
+            const uint8_t* kt = keep ? reinterpret_cast<const uint8_t*>(p.c.k_keep) +
+                                           ((size_t)bg * kt_cap + tile) * kTileBytes16
+                                     : reinterpret_cast<const uint8_t*>(p.c.k_win) +
+                                           ((size_t)bg * wt_cap + tile) * kTileBytes16;
+#pragma unroll
+            for (int h = 0; h < G; ++h) lg[h] = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const uint4 kk = *reinterpret_cast<const uint4*>(kt + k16_off(lane, c));
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const uint32_t* qh = qn + h * 64 + 4 * c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) lg[h] = dot2<F16>(u4w(kk, i), qh[i], lg[h]);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) lg[h] = valid ? lg[h] * p.scale2 : -INFINITY;
+        }
+
+        // ----------------------------- online softmax (wave-uniform update)
+        float pr_h[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float tmax = wave_max(lg[h]);
+            if (tmax > m[h] + kLazy) {
+                const float alpha = __builtin_amdgcn_exp2f(m[h] - tmax);
+                m[h] = tmax;
+                l[h] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zacc[h][i] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
+            }
+            pr_h[h] = __builtin_amdgcn_exp2f(lg[h] - m[h]);
+            l[h] += pr_h[h];
+        }
+
+        if (int4_tile) {
+            // p*s per group to LDS; z-terms accumulate here
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    ps_w[(lane * 4 + grp) * G + h] = pr_h[h] * vs[grp];
+                    zacc[h][grp] = fmaf(pr_h[h], vz[grp], zacc[h][grp]);
+                }
+            }
+            lds_fence();
+            // ----------------------------- channel phase, INT4 V
+            const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.c.v_codes) +
+                                ((size_t)bg * qt_cap + (tile_base_slot / kTile)) * kTileBytesQ;
+            uint4 vw[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) vw[kk] = *reinterpret_cast<const uint4*>(vc + kk * 1024 + lane * 16);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int sa = 16 * u + 2 * j;
+                float pa[G], pb[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    pa[h] = ps_w[(sa * 4 + gk) * G + h];
+                    pb[h] = ps_w[((sa + 1) * 4 + gk) * G + h];
+                }
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const uint32_t d = u4w(vw[j >> 1], (j & 1) * 2 + e);
+                    const uint32_t m0 = d & 0x0F0F0F0Fu, m1 = (d >> 4) & 0x0F0F0F0Fu;
+                    const float a0 = (float)(m0 & 0xFF), a2 = (float)((m0 >> 8) & 0xFF);
+                    const float b0 = (float)((m0 >> 16) & 0xFF), b2 = (float)(m0 >> 24);
+                    const float a1 = (float)(m1 & 0xFF), a3 = (float)((m1 >> 8) & 0xFF);
+                    const float b1 = (float)((m1 >> 16) & 0xFF), b3 = (float)(m1 >> 24);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        acc[h][4 * e + 0] = fmaf(pb[h], b0, fmaf(pa[h], a0, acc[h][4 * e + 0]));
+                        acc[h][4 * e + 1] = fmaf(pb[h], b1, fmaf(pa[h], a1, acc[h][4 * e + 1]));
+                        acc[h][4 * e + 2] = fmaf(pb[h], b2, fmaf(pa[h], a2, acc[h][4 * e + 2]));
+                        acc[h][4 * e + 3] = fmaf(pb[h], b3, fmaf(pa[h], a3, acc[h][4 * e + 3]));
+                    }
+                }
+            }
+            lds_fence();
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; ++h) ps_w[lane * G + h] = pr_h[h];
+            lds_fence();
+            // ----------------------------- channel phase, 16-bit V
+            const bool keep = v < nqt + nkt;
+            const int tile = tile_base_slot / kTile;
+            const uint8_t* vt = keep ? reinterpret_cast<const uint8_t*>(p.c.v_keep) +
+                                           ((size_t)bg * kt_cap + tile) * kTileBytes16
+                                     : reinterpret_cast<const uint8_t*>(p.c.v_win) +
+                                           ((size_t)bg * wt_cap + tile) * kTileBytes16;
+#pragma unroll 4
+            for (int i = 0; i < 16; ++i) {
+                const int slot = 16 * u + i;
+                const uint4 vv = *reinterpret_cast<const uint4*>(vt + i * 1024 + lane * 16);
+                if (tile_base_slot + slot < count) {
+                    float x[8];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        x[2 * w] = h16_to_f32<F16>(u4w(vv, w) & 0xFFFFu);
+                        x[2 * w + 1] = h16_to_f32<F16>(u4w(vv, w) >> 16);
+                    }
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const float pw = ps_w[slot * G + h];
+#pragma unroll
+                        for (int ch = 0; ch < 8; ++ch) acc[h][ch] = fmaf(pw, x[ch], acc[h][ch]);
+                    }
+                }
+            }
+            lds_fence();
+        }
+    }
+
+    // ----------------------------- wave epilogue
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        l[h] = wave_sum(l[h]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zacc[h][i] = wave_sum(zacc[h][i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc[h][i] += __shfl_xor(acc[h][i], 16);
+            acc[h][i] += __shfl_xor(acc[h][i], 32);
+        }
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) lds_o[wave][h][8 * lane + i] = acc[h][i] + zacc[h][lane >> 2];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            lds_m[wave][h] = m[h];
+            lds_l[wave][h] = l[h];
+        }
+    }
+    __syncthreads();
+    // ----------------------------- merge the waves, write the split partial
+    const size_t pbase = ((size_t)bg * p.nsplit + s) * G;
+    for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
+        const int h = idx / kD, d = idx % kD;
+        float M = lds_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, lds_m[w][h]);
+        float o = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = lds_m[w][h];
+            const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+            o = fmaf(f, lds_o[w][h][d], o);
+            L = fmaf(f, lds_l[w][h], L);
+        }
+        p.part_o[(pbase + h) * kD + d] = o;
+        if (d == 0) {
+            p.part_m[pbase + h] = M;
+            p.part_l[pbase + h] = L;
+        }
+    }
+}
+
+// Rearranges the query for the split kernel: INT4-path pairs (prescaled by
+// 1/8 for bf16, 1/16 for fp16, exact), natural pairs and group sums.
+template <bool F16>
+__global__ __launch_bounds__(128) void k_decode_prep(const uint16_t* q, int Hq, int G, uint32_t* qp,
+                                                     uint32_t* qn, float* qsum) {
+    const int g = blockIdx.x, b = blockIdx.y, Hkv = gridDim.x;
+    const int bg = b * Hkv + g;
+    const int t = threadIdx.x;
+    for (int h = 0; h < G; ++h) {
+        const uint16_t* qh = q + ((size_t)b * Hq + g * G + h) * kD;
+        if (t < 64) qn[((size_t)bg * G + h) * 64 + t] = (uint32_t)qh[2 * t] | ((uint32_t)qh[2 * t + 1] << 16);
+        // INT4 arrangement: entry (grp, 4i + n) = (q[32grp+8i+n], q[32grp+8i+n+4]) * 2^-3 (bf16) / 2^-4 (fp16)
+        if (t < 64) {
+            const int grp = t >> 4, e = t & 15, i = e >> 2, n = e & 3;
+            const int d0 = 32 * grp + 8 * i + n;
+            const float sc = F16 ? 0.0625f : 0.125f;
+            const float a = h16_to_f32<F16>(qh[d0]) * sc, c = h16_to_f32<F16>(qh[d0 + 4]) * sc;
+            uint32_t wa, wc;
+            if constexpr (F16) {
+                wa = f32_to_f16_bits(a);
+                wc = f32_to_f16_bits(c);
+            } else {
+                wa = __float_as_uint(a) >> 16;  // exact: power-of-two scaling of a bf16 value
+                wc = __float_as_uint(c) >> 16;
+            }
+            qp[(((size_t)bg * 4 + grp) * G + h) * 16 + e] = wa | (wc << 16);
+        }
+        if (t < 4) {
+            // group sum of the prescaled-then-rescaled values (exactly the values the
+            // pairs carry, times 8 or 16), accumulated in double
+            const float sc = F16 ? 0.0625f : 0.125f;
+            double acc = 0.0;
+            for (int d = 32 * t; d < 32 * t + 32; ++d) {
+                float a = h16_to_f32<F16>(qh[d]) * sc;
+                if constexpr (F16) a = f16_to_f32(f32_to_f16_bits(a));
+                acc += (double)a;
+            }
+            qsum[((size_t)bg * G + h) * 4 + t] = (float)(acc / sc);
+        }
+    }
+}
+
+__global__ __launch_bounds__(128) void k_decode_reduce(const hq_cache c, const float* part_m,
+                                                       const float* part_l, const float* part_o,
+                                                       int nsplit, int tps, int G, int Hq, void* out,
+                                                       int out_dt) {
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int g = h / G, hl = h % G;
+    const int bg = b * c.Hkv + g;
+    const int4 cnt = *reinterpret_cast<const int4*>(c.counts + 4 * bg);
+    const int T = cnt.x, n_q = cnt.y, n_keep = cnt.z;
+    const int nring = T < c.window ? T : c.window;
+    const int total = (n_q + kTile - 1) / kTile + (n_keep + kTile - 1) / kTile + (nring + kTile - 1) / kTile;
+    const int active = min((total + tps - 1) / tps, nsplit);
+    const size_t base = (size_t)bg * nsplit * G + hl;
+    float M = -INFINITY;
+    for (int s = 0; s < active; ++s) M = fmaxf(M, part_m[base + (size_t)s * G]);
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < active; ++s) {
+        const float ms = part_m[base + (size_t)s * G];
+        const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+        L = fmaf(f, part_l[base + (size_t)s * G], L);
+        O = fmaf(f, part_o[(base + (size_t)s * G) * kD + d], O);
+    }
+    const float r = O / L;
+    const size_t oi = ((size_t)b * Hq + h) * kD + d;
+    if (out_dt == HQ_F32)
+        static_cast<float*>(out)[oi] = r;
+    else if (out_dt == HQ_F16)
+        static_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_f16_bits(r);
+    else {
+        // bf16, round to nearest even
+        uint32_t x = __float_as_uint(r);
+        x += 0x7FFFu + ((x >> 16) & 1u);
+        static_cast<uint16_t*>(out)[oi] = (uint16_t)(x >> 16);
+    }
+}
+
+struct WsLayout {
+    size_t qp, qn, qsum, pm, pl, po, total;
+};
+inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+WsLayout ws_layout(const hq_cache& c, int32_t Hq, int32_t nsplit) {
+    const size_t BG = (size_t)c.B * c.Hkv;
+    const int G = Hq / c.Hkv;
+    WsLayout w;
+    w.qp = 0;
+    w.qn = w.qp + al(BG * 4 * G * 16 * 4);
+    w.qsum = w.qn + al(BG * G * 64 * 4);
+    w.pm = w.qsum + al(BG * G * 4 * 4);
+    w.pl = w.pm + al(BG * nsplit * G * 4);
+    w.po = w.pl + al(BG * nsplit * G * 4);
+    w.total = w.po + al(BG * nsplit * G * kD * 4);
+    return w;
+}
+
+template <int G, bool F16>
+void launch_split(const DecodeParams& p, dim3 grid, hipStream_t s) {
+    k_decode_split<G, F16><<<grid, 256, 0, s>>>(p);
+}
+
+}  // namespace
+
+int32_t decode_max_tiles(const hq_cache& c) {
+    return c.cap_q / kTile + c.cap_keep / kTile + c.window / kTile;
+}
+
+size_t decode_ws_bytes(const hq_cache& c, int32_t Hq, int32_t nsplit) {
+    return ws_layout(c, Hq, nsplit).total;
+}
+
+hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype out_dt,
+                         const DecodeLaunch& d, hipStream_t s) {
+    const WsLayout w = ws_layout(c, d.Hq, d.nsplit);
+    char* ws = static_cast<char*>(d.ws);
+    DecodeParams p;
+    p.c = c;
+    p.qp = reinterpret_cast<uint32_t*>(ws + w.qp);
+    p.qn = reinterpret_cast<uint32_t*>(ws + w.qn);
+    p.qsum = reinterpret_cast<float*>(ws + w.qsum);
+    p.part_m = reinterpret_cast<float*>(ws + w.pm);
+    p.part_l = reinterpret_cast<float*>(ws + w.pl);
+    p.part_o = reinterpret_cast<float*>(ws + w.po);
+    p.nsplit = d.nsplit;
+    p.tps = d.tiles_per_split;
+    p.G = d.G;
+    p.scale2 = d.sm_scale_log2;
+    const bool f16 = c.dt == HQ_F16;
+    dim3 pg(c.Hkv, c.B);
+    if (f16)
+        k_decode_prep<true><<<pg, 128, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
+                                               const_cast<uint32_t*>(p.qp), const_cast<uint32_t*>(p.qn),
+                                               const_cast<float*>(p.qsum));
+    else
+        k_decode_prep<false><<<pg, 128, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
+                                                const_cast<uint32_t*>(p.qp), const_cast<uint32_t*>(p.qn),
+                                                const_cast<float*>(p.qsum));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid(d.nsplit, c.Hkv, c.B);
+    switch (d.G * 2 + (f16 ? 1 : 0)) {
+        case 2: launch_split<1, false>(p, grid, s); break;
+        case 3: launch_split<1, true>(p, grid, s); break;
+        case 4: launch_split<2, false>(p, grid, s); break;
+        case 5: launch_split<2, true>(p, grid, s); break;
+        case 8: launch_split<4, false>(p, grid, s); break;
+        case 9: launch_split<4, true>(p, grid, s); break;
+        case 16: launch_split<8, false>(p, grid, s); break;
+        case 17: launch_split<8, true>(p, grid, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_decode_reduce<<<dim3(d.Hq, c.B), 128, 0, s>>>(c, p.part_m, p.part_l, p.part_o, d.nsplit,
+                                                     d.tiles_per_split, d.G, d.Hq, out, (int)out_dt);
+    return hipGetLastError();
+}
+
+}  // namespace hq

@@ -1,0 +1,132 @@
+// Internal declarations shared by the libhyquant translation units (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/hq.h"
+
+namespace hq {
+
+constexpr int kD = 128;          // head_dim (the only supported value)
+constexpr int kTile = 64;        // tokens per cache tile == wavefront size
+constexpr int kGroup = 32;       // INT4 quantization group (channels)
+constexpr int kTileBytesQ = 4096;        // packed INT4 codes of one tile (K or V)
+constexpr int kTileBytes16 = kTile * kD * 2;  // one tile of 16-bit rows
+constexpr int kInt8Block = 64;   // prefill INT8 block (tokens)
+
+// ---------------------------------------------------------------------------
+// INT4 tile layouts (per (b, g), tile of 64 slots; see hq.h for the format).
+//
+// K codes (read by the token phase, lane = slot): the 16 bytes of group k of
+// slot t are the canonical packed bytes of channels 32k..32k+31
+// (byte i = code[2i] | code[2i+1] << 4) at  k*1024 + t*16.
+__host__ __device__ inline int kcode_off(int slot, int group) { return group * 1024 + slot * 16; }
+
+// V codes (read by the channel phase, lane l = 16u + c8 owns channels
+// 8c8..8c8+7 of slots 16u..16u+15). Dword (pair P, quad Q) holds, in its low
+// 16 bits, the canonical nibbles of slot 2P, channels 4Q..4Q+3, and in its
+// high 16 bits the same channels of slot 2P+1. It lives at
+//   u = P/8, j = P%8, c8 = Q/2, e = Q%2, l = 16u + c8,
+//   byte offset = (j/2)*1024 + l*16 + ((j%2)*2 + e)*4.
+__host__ __device__ inline int vcode_off(int pair, int quad) {
+    int u = pair >> 3, j = pair & 7, c8 = quad >> 1, e = quad & 1;
+    return (j >> 1) * 1024 + (16 * u + c8) * 16 + ((j & 1) * 2 + e) * 4;
+}
+
+// 16-bit tiles. K (token phase): 16-byte chunk c (channels 8c..8c+7) of slot
+// t at c*1024 + t*16. V (channel phase): chunk c8 of slot t = 16u + i at
+// i*1024 + (16u + c8)*16.
+__host__ __device__ inline int k16_off(int slot, int chunk) { return chunk * 1024 + slot * 16; }
+__host__ __device__ inline int v16_off(int slot, int chunk) {
+    return (slot & 15) * 1024 + (16 * (slot >> 4) + chunk) * 16;
+}
+
+// Device-side counters of one (b, g).
+struct Counts {
+    int32_t seq_len, n_q, n_keep, probe_len;
+};
+
+// ---------------------------------------------------------------------------
+// Scalar conversions.
+__device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ inline float f16_to_f32(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+__device__ inline uint32_t f32_to_f16_bits(float x) {  // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <bool F16>
+__device__ inline float h16_to_f32(uint32_t bits16) {
+    if constexpr (F16) return f16_to_f32(bits16);
+    else return bf16_to_f32(bits16);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions (wave64).
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ inline double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ inline double wave_max_d(double v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = fmax(v, __shfl_xor(v, o));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Policy helpers (host and device).
+__host__ __device__ inline int32_t keep_count(int32_t T, const hq_policy& p) {
+    int32_t n_cand = T > p.window ? T - p.window : 0;
+    int64_t k = (int64_t)p.keep_num * T / p.keep_den;
+    return (int32_t)(k < n_cand ? k : n_cand);
+}
+inline int32_t sel_stride(int32_t T, const hq_policy& p) {
+    int64_t k = (int64_t)p.keep_num * T / p.keep_den;
+    return (int32_t)(k > 1 ? k : 1);
+}
+inline int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
+
+// ---------------------------------------------------------------------------
+// Launchers (each defined next to its kernels). Return hipSuccess or the
+// launch error.
+hipError_t launch_quantize(const void* k, const void* v, const int32_t* seq_lens, int32_t Tmax,
+                           const int32_t* sel_idx, const int32_t* sel_count, int32_t sel_stride,
+                           const float* col_scores, const hq_thresh* thresh, const hq_cache& c,
+                           hipStream_t s);
+hipError_t launch_append(const hq_cache& c, const void* k_new, const void* v_new, hipStream_t s);
+
+struct DecodeLaunch {
+    int32_t Hq, G, nsplit, tiles_per_split;
+    float sm_scale_log2;
+    void* ws;
+};
+hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype out_dt,
+                         const DecodeLaunch& d, hipStream_t s);
+size_t decode_ws_bytes(const hq_cache& c, int32_t Hq, int32_t nsplit);
+int32_t decode_max_tiles(const hq_cache& c);
+
+hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_lens, int32_t B,
+                        int32_t Hq, int32_t Hkv, int32_t Tmax, bool f16, const hq_policy& pol,
+                        float sm_scale, float* col_scores, int32_t* sel_idx, int32_t* sel_count,
+                        hq_thresh* thresh, void* ws, hipStream_t s);
+size_t probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_policy& pol);
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,
+                          int32_t Hkv, int32_t T, bool f16, const hq_policy& pol,
+                          const int32_t* sel_idx, const int32_t* sel_count, int32_t sel_stride,
+                          float sm_scale, void* out, hq_dtype out_dt, void* ws, hipStream_t s);
+size_t prefill_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, const hq_policy& pol);
+
+}  // namespace hq

@@ -1,0 +1,389 @@
+// hq_probe_select: vertical-line probe and top-k column selection (gfx950).
+//
+// HyQuant pages: "HyQuant: Hybrid-Precision Quantization for LLM
+// Attention", TL;DR and "What problem it solves" (a small number of key
+// columns are attended to by almost every query row; a lightweight pattern
+// signal finds them without calibration), "Gaps" (the probe must not
+// materialise the attention map); "How HyQuant uses hybrid-precision
+// attention to cut decode compute", "Why preserve selected positions?" (keep
+// the top 5% high-score positions).
+//
+// Column score c[j] = sum over the G query heads and the last R probe rows of
+// the row-normalised causal softmax. The map is never stored: pass 1
+// computes each row's max and normaliser over key chunks, a combine kernel
+// merges the chunks, pass 2 recomputes the logits and sums the normalised
+// probabilities per column.
+//
+// Precision: the selection is a ranking of scores whose top-k gap is often
+// only ~1e-5..1e-4 relative on long contexts, so the logits are formed
+// exactly (bf16/fp16 inputs converted to fp64, v_mfma_f64_16x16x4 with fp64
+// accumulation), exponentials use an fp64 polynomial, and normalisers and
+// column sums accumulate in fp64. The scores are rounded once to fp32.
+//
+// Top-k: one workgroup per (b, g); 4-pass 8-bit radix select on the fp32 bit
+// patterns (scores are >= 0, so bit order = value order) with LDS histograms,
+// then an index-ordered block-scan compaction that takes all scores above
+// the threshold and the lowest-index ties.
+#include "hq_internal.h"
+
+namespace hq {
+namespace {
+
+typedef double double4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kKeyChunk = 1024;  // keys per pass-1 workgroup
+
+// 2^x in fp64 (x finite or very negative): 2^n * e^(f ln2), |f| <= 1/2,
+// Taylor series to degree 14 (truncation < 1e-17 relative).
+__device__ inline double exp2_f64(double x) {
+    if (x < -1000.0) return 0.0;
+    const double n = rint(x);
+    const double y = (x - n) * 0.69314718055994530942;
+    double e = 1.0 / 87178291200.0;  // 1/14!
+    e = fma(e, y, 1.0 / 6227020800.0);
+    e = fma(e, y, 1.0 / 479001600.0);
+    e = fma(e, y, 1.0 / 39916800.0);
+    e = fma(e, y, 1.0 / 3628800.0);
+    e = fma(e, y, 1.0 / 362880.0);
+    e = fma(e, y, 1.0 / 40320.0);
+    e = fma(e, y, 1.0 / 5040.0);
+    e = fma(e, y, 1.0 / 720.0);
+    e = fma(e, y, 1.0 / 120.0);
+    e = fma(e, y, 1.0 / 24.0);
+    e = fma(e, y, 1.0 / 6.0);
+    e = fma(e, y, 0.5);
+    e = fma(e, y, 1.0);
+    e = fma(e, y, 1.0);
+    return ldexp(e, (int)n);
+}
+
+template <bool F16>
+__device__ inline void load32_f64(const uint16_t* src, bool ok, double* out) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 u = ok ? s4[i] : make_uint4(0, 0, 0, 0);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            out[8 * i + 2 * j] = (double)h16_to_f32<F16>(w[j] & 0xFFFFu);
+            out[8 * i + 2 * j + 1] = (double)h16_to_f32<F16>(w[j] >> 16);
+        }
+    }
+}
+
+// Exact 16 x 16 block of dot products over 128 channels. Lane l supplies row
+// (l % 16) of A and column (l % 16) of B for channels 32*(l/16) .. +31; the
+// result element i of lane l is D[4*(l/16) + i][l % 16].
+__device__ inline double4_t mfma_dot128(const double* a, const double* b) {
+    double4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc, 0, 0, 0);
+    return acc;
+}
+
+struct ProbeParams {
+    const uint16_t* q;     // [B][Hq][R][D]
+    const uint16_t* k;     // [B][Hkv][Tmax][D]
+    const int32_t* seq_lens;
+    double2* part;         // [B][Hkv][nchunk][NR] (m, l) per key chunk
+    double2* rows;         // [B][Hkv][NR] (m, 1/l)
+    float* col_scores;     // [B][Hkv][Tmax]
+    int32_t B, Hq, Hkv, Tmax, R, G, NR, nchunk;
+    double sc2;            // sm_scale * log2(e)
+};
+
+__device__ inline const uint16_t* qrow(const ProbeParams& p, int b, int g, int row) {
+    const int h = row / p.R, r = row % p.R;
+    return p.q + (((size_t)b * p.Hq + g * p.G + h) * p.R + r) * kD;
+}
+__device__ inline int row_pos(const ProbeParams& p, int T, int row) { return T - p.R + (row % p.R); }
+
+// Pass 1: per (key chunk, g, b), online max / sum of 2^x per probe row.
+template <bool F16>
+__global__ __launch_bounds__(256) void k_probe_rowstats(ProbeParams p) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int T = p.seq_lens[b];
+    const int key_lo = chunk * kKeyChunk;
+    const int bg = b * p.Hkv + g;
+    const int li = lane & 15, kq = lane >> 4;
+    const uint16_t* kbase = p.k + (size_t)bg * p.Tmax * kD;
+    const int nrt = p.NR / 16;
+    for (int rt = wave; rt < nrt; rt += 4) {
+        double m[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m[i] = -INFINITY;
+            l[i] = 0.0;
+        }
+        if (key_lo < T) {
+            double a[32];
+            load32_f64<F16>(qrow(p, b, g, rt * 16 + li) + 32 * kq, true, a);
+            int pos[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pos[i] = row_pos(p, T, rt * 16 + 4 * kq + i);
+            const int key_hi = min(key_lo + kKeyChunk, T);
+            for (int k0 = key_lo; k0 < key_hi; k0 += 16) {
+                const int key = k0 + li;
+                const bool kok = key < T;
+                double bv[32];
+                load32_f64<F16>(kbase + (size_t)(kok ? key : 0) * kD + 32 * kq, kok, bv);
+                const double4_t acc = mfma_dot128(a, bv);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (kok && pos[i] >= 0 && key <= pos[i]) {
+                        const double x = acc[i] * p.sc2;
+                        if (x > m[i]) {
+                            l[i] = l[i] * exp2_f64(m[i] - x) + 1.0;
+                            m[i] = x;
+                        } else {
+                            l[i] += exp2_f64(x - m[i]);
+                        }
+                    }
+                }
+            }
+        }
+        // merge the 16 lanes that hold the same rows (different keys)
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double m2 = __shfl_xor(m[i], off), l2 = __shfl_xor(l[i], off);
+                const double M = fmax(m[i], m2);
+                double L = 0.0;
+                if (m[i] != -INFINITY) L += l[i] * exp2_f64(m[i] - M);
+                if (m2 != -INFINITY) L += l2 * exp2_f64(m2 - M);
+                m[i] = M;
+                l[i] = L;
+            }
+        }
+        if (li == 0) {
+            double2* dst = p.part + ((size_t)bg * p.nchunk + chunk) * p.NR + rt * 16 + 4 * kq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = make_double2(m[i], l[i]);
+        }
+    }
+}
+
+// Merge the chunk statistics of every probe row: (m, 1/l).
+__global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
+    const int g = blockIdx.x, b = blockIdx.y;
+    const int bg = b * p.Hkv + g;
+    const int T = p.seq_lens[b];
+    const int nch = (T + kKeyChunk - 1) / kKeyChunk;
+    for (int row = threadIdx.x; row < p.NR; row += 256) {
+        double M = -INFINITY;
+        for (int c = 0; c < nch; ++c) M = fmax(M, p.part[((size_t)bg * p.nchunk + c) * p.NR + row].x);
+        double L = 0.0;
+        for (int c = 0; c < nch; ++c) {
+            const double2 v = p.part[((size_t)bg * p.nchunk + c) * p.NR + row];
+            if (v.x != -INFINITY) L += v.y * exp2_f64(v.x - M);
+        }
+        p.rows[(size_t)bg * p.NR + row] = make_double2(M, L > 0.0 ? 1.0 / L : 0.0);
+    }
+}
+
+// Pass 2: per (64-key block, g, b), column sums of the normalised softmax.
+template <bool F16>
+__global__ __launch_bounds__(256) void k_probe_colsum(ProbeParams p) {
+    __shared__ double2 rs[512];
+    __shared__ int rpos[512];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int T = p.seq_lens[b];
+    const int bg = b * p.Hkv + g;
+    const int li = lane & 15, kq = lane >> 4;
+    const int key = blk * 64 + wave * 16 + li;
+    if (blk * 64 >= T) {
+        if (threadIdx.x < 64 && blk * 64 + threadIdx.x < p.Tmax)
+            p.col_scores[(size_t)bg * p.Tmax + blk * 64 + threadIdx.x] = 0.0f;
+        return;
+    }
+    for (int row = threadIdx.x; row < p.NR; row += 256) {
+        rs[row] = p.rows[(size_t)bg * p.NR + row];
+        rpos[row] = row_pos(p, T, row);
+    }
+    __syncthreads();
+    const bool kok = key < T;
+    double bv[32];
+    load32_f64<F16>(p.k + ((size_t)bg * p.Tmax + (kok ? key : 0)) * kD + 32 * kq, kok, bv);
+    double colacc = 0.0;
+    const int nrt = p.NR / 16;
+    for (int rt = 0; rt < nrt; ++rt) {
+        double a[32];
+        load32_f64<F16>(qrow(p, b, g, rt * 16 + li) + 32 * kq, true, a);
+        const double4_t acc = mfma_dot128(a, bv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = rt * 16 + 4 * kq + i;
+            const int pr = rpos[row];
+            if (kok && pr >= 0 && key <= pr) {
+                const double2 st = rs[row];
+                colacc += exp2_f64(acc[i] * p.sc2 - st.x) * st.y;
+            }
+        }
+    }
+    colacc += __shfl_xor(colacc, 16);
+    colacc += __shfl_xor(colacc, 32);
+    if (kq == 0 && key < p.Tmax) p.col_scores[(size_t)bg * p.Tmax + key] = kok ? (float)colacc : 0.0f;
+}
+
+// ---------------------------------------------------------------- top-k
+
+__device__ inline uint32_t block_excl_scan(uint32_t flag, uint32_t* wsum, uint32_t& total) {
+    // 1024 threads = 16 waves
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t bal = __ballot(flag);
+    const uint32_t within = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const uint32_t c = wsum[w];
+        before += w < wave ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    total = tot;
+    return before + within;
+}
+
+__global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, const int32_t* seq_lens, int Hkv,
+                                                     int Tmax, hq_policy pol, int stride, int32_t* sel_idx,
+                                                     int32_t* sel_count, hq_thresh* thresh) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t sh_prefix, sh_mask, sh_remaining;
+    __shared__ int sh_jk;
+    const int g = blockIdx.x, b = blockIdx.y;
+    const int bg = b * Hkv + g;
+    const int tid = threadIdx.x;
+    const int T = seq_lens[b];
+    const int ncand = T > pol.window ? T - pol.window : 0;
+    const int k = keep_count(T, pol);
+    const uint32_t* xs = reinterpret_cast<const uint32_t*>(col_scores + (size_t)bg * Tmax);
+    int32_t* sel = sel_idx + (size_t)bg * stride;
+    for (int i = k + tid; i < stride; i += 1024) sel[i] = -1;
+    if (k == 0) {
+        if (tid == 0) {
+            sel_count[bg] = 0;
+            thresh[bg] = hq_thresh{INFINITY, -1};
+        }
+        return;
+    }
+    if (tid == 0) {
+        sh_prefix = 0;
+        sh_mask = 0;
+        sh_remaining = (uint32_t)k;
+        sh_jk = -1;
+    }
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+        __syncthreads();
+        const uint32_t prefix = sh_prefix, mask = sh_mask;
+        for (int j = tid; j < ncand; j += 1024) {
+            const uint32_t x = xs[j];
+            if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t cum = 0, rem = sh_remaining;
+            int bin = 255;
+            for (; bin > 0; --bin) {
+                if (cum + hist[bin] >= rem) break;
+                cum += hist[bin];
+            }
+            sh_remaining = rem - cum;
+            sh_prefix = prefix | ((uint32_t)bin << shift);
+            sh_mask = mask | (255u << shift);
+        }
+        __syncthreads();
+    }
+    const uint32_t tau = sh_prefix;
+    const uint32_t remaining = sh_remaining;  // ties to take, lowest index first (>= 1)
+    uint32_t out = 0, ties = 0;
+    for (int base = 0; base < ncand; base += 1024) {
+        const int j = base + tid;
+        const uint32_t x = j < ncand ? xs[j] : 0u;
+        const bool gt = j < ncand && x > tau;
+        const bool eq = j < ncand && x == tau;
+        uint32_t eq_tot, take_tot;
+        const uint32_t eq_rank = ties + block_excl_scan(eq ? 1u : 0u, wsum, eq_tot);
+        const bool take = gt || (eq && eq_rank < remaining);
+        const uint32_t pos = out + block_excl_scan(take ? 1u : 0u, wsum, take_tot);
+        if (take) sel[pos] = j;
+        if (eq && eq_rank == remaining - 1) sh_jk = j;
+        out += take_tot;
+        ties += eq_tot;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        sel_count[bg] = k;
+        thresh[bg] = hq_thresh{__uint_as_float(tau), sh_jk};
+    }
+}
+
+struct ProbeWs {
+    size_t part, rows, total;
+};
+inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+ProbeWs probe_ws(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_policy& pol) {
+    const int G = Hq / Hkv;
+    const size_t NR = (size_t)G * pol.probe_rows;
+    const size_t nchunk = (Tmax + kKeyChunk - 1) / kKeyChunk;
+    ProbeWs w;
+    w.part = 0;
+    w.rows = al((size_t)B * Hkv * nchunk * NR * 16);
+    w.total = w.rows + al((size_t)B * Hkv * NR * 16);
+    return w;
+}
+
+}  // namespace
+
+size_t probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_policy& pol) {
+    return probe_ws(B, Hq, Hkv, Tmax, pol).total;
+}
+
+hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                        int32_t Hkv, int32_t Tmax, bool f16, const hq_policy& pol, float sm_scale,
+                        float* col_scores, int32_t* sel_idx, int32_t* sel_count, hq_thresh* thresh, void* ws,
+                        hipStream_t s) {
+    const int G = Hq / Hkv;
+    const int NR = G * pol.probe_rows;
+    if (NR % 16 != 0 || NR > 512) return hipErrorNotSupported;
+    const ProbeWs w = probe_ws(B, Hq, Hkv, Tmax, pol);
+    ProbeParams p;
+    p.q = static_cast<const uint16_t*>(q_probe);
+    p.k = static_cast<const uint16_t*>(k);
+    p.seq_lens = seq_lens;
+    p.part = reinterpret_cast<double2*>(static_cast<char*>(ws) + w.part);
+    p.rows = reinterpret_cast<double2*>(static_cast<char*>(ws) + w.rows);
+    p.col_scores = col_scores;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Tmax = Tmax;
+    p.R = pol.probe_rows;
+    p.G = G;
+    p.NR = NR;
+    p.nchunk = (Tmax + kKeyChunk - 1) / kKeyChunk;
+    p.sc2 = (double)sm_scale * 1.4426950408889634074;
+    dim3 g1(p.nchunk, Hkv, B);
+    if (f16) k_probe_rowstats<true><<<g1, 256, 0, s>>>(p);
+    else k_probe_rowstats<false><<<g1, 256, 0, s>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_probe_rowfinal<<<dim3(Hkv, B), 256, 0, s>>>(p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dim3 g2((Tmax + 63) / 64, Hkv, B);
+    if (f16) k_probe_colsum<true><<<g2, 256, 0, s>>>(p);
+    else k_probe_colsum<false><<<g2, 256, 0, s>>>(p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_topk_select<<<dim3(Hkv, B), 1024, 0, s>>>(col_scores, seq_lens, Hkv, Tmax, pol, sel_stride(Tmax, pol),
+                                                  sel_idx, sel_count, thresh);
+    return hipGetLastError();
+}
+
+}  // namespace hq

@@ -1,0 +1,192 @@
+// hq_quantize_kv: build the hybrid KV cache of a prompt (gfx950).
+//
+// HyQuant pages: "HyQuant: Hybrid-Precision Quantization for LLM
+// Attention", flowchart (persistently attended columns and the recent local
+// window go to high precision, everything else low-bit); "How HyQuant uses
+// hybrid-precision attention to cut decode compute", "What the authors
+// tested" (Key-4bit / Value-4bit for the rest) and "Memory and runtime
+// costs" (retained tokens held only in 16 bits).
+//
+// One workgroup per destination tile of 64 slots of one (b, g): INT4 tiles
+// gather the n-th non-selected position (binary search on the selected set),
+// quantize K and V per 32-channel group (4 threads per slot) and write the
+// codes in the decode kernel's tile layouts; kept tiles copy the selected
+// rows; ring tiles copy the last `window` rows into slot = position % window.
+// Writes are full 64-slot tiles, contiguous across the workgroup.
+#include "int4_quant.h"
+
+namespace hq {
+namespace {
+
+struct QuantParams {
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* seq_lens;
+    const int32_t* sel_idx;
+    const int32_t* sel_count;
+    const float* col_scores;
+    const hq_thresh* thresh;
+    hq_cache c;
+    int32_t Tmax, sel_stride;
+};
+
+// Position of the n-th (0-based) non-selected token: n + #{i : S[i] - i <= n}.
+__device__ inline int32_t nth_unselected(const int32_t* S, int32_t k, int32_t n) {
+    int32_t lo = 0, hi = k;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (S[mid] - mid <= n) lo = mid + 1;
+        else hi = mid;
+    }
+    return n + lo;
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
+    const int tid = threadIdx.x;
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int Hkv = p.c.Hkv, W = p.c.window;
+    const int bg = b * Hkv + g;
+    const int T = p.seq_lens[b];
+    const int32_t* S = p.sel_idx + (size_t)bg * p.sel_stride;
+    int k = p.sel_count[bg];
+    const int nwin = T < W ? T : W;
+    const bool bad = k < 0 || k > p.c.cap_keep || k > p.sel_stride || k > T - nwin || T > p.Tmax || T < 1;
+    if (bad) {
+        if (tid == 0) atomicOr(p.c.err_flag, 1);
+        return;
+    }
+    const int n_q = T - k - nwin;
+    const int qt = p.c.cap_q / kTile, kt = p.c.cap_keep / kTile;
+    int tile = blockIdx.x;
+    const uint16_t* krows = p.k + (size_t)bg * p.Tmax * kD;
+    const uint16_t* vrows = p.v + (size_t)bg * p.Tmax * kD;
+
+    if (tile == 0 && tid == 0) {
+        int4 cnt = {T, n_q, k, T};
+        *reinterpret_cast<int4*>(p.c.counts + 4 * bg) = cnt;
+        p.c.thresh[bg] = p.thresh[bg];
+    }
+
+    if (tile < qt) {
+        // ---------------- INT4 tile
+        if (tid < kTile) {
+            const int j = tile * kTile + tid;
+            if (j < p.c.cap_probe)
+                p.c.col_scores[(size_t)bg * p.c.cap_probe + j] =
+                    j < T ? p.col_scores[(size_t)bg * p.Tmax + j] : 0.0f;
+        }
+        const int t = tid >> 2, grp = tid & 3;
+        const int n = tile * kTile + t;
+        const bool valid = n < n_q;
+        if (tile * kTile >= n_q) return;  // uniform: whole tile empty
+        const int pos = valid ? nth_unselected(S, k, n) : 0;
+        float x[kGroup];
+        uint32_t kp[4], vp[4], ks, kz, vs, vz;
+        {
+            const uint4* src = reinterpret_cast<const uint4*>(krows + (size_t)pos * kD + grp * kGroup);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unpack8<F16>(src[i], x + 8 * i);
+            int4_quant_group(x, kp, ks, kz);
+        }
+        {
+            const uint4* src = reinterpret_cast<const uint4*>(vrows + (size_t)pos * kD + grp * kGroup);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unpack8<F16>(src[i], x + 8 * i);
+            int4_quant_group(x, vp, vs, vz);
+        }
+        uint32_t other[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) other[i] = __shfl_xor(vp[i], 4);
+        uint32_t pw[4];
+        const bool odd = t & 1;
+        vpair_words(vp, other, odd, pw);
+        const size_t tile_base = ((size_t)bg * qt + tile) * kTileBytesQ;
+        uint8_t* kc = reinterpret_cast<uint8_t*>(p.c.k_codes) + tile_base;
+        uint8_t* vc = reinterpret_cast<uint8_t*>(p.c.v_codes) + tile_base;
+        const size_t slot_g = (size_t)bg * p.c.cap_q + n;
+        if (valid) {
+            *reinterpret_cast<uint4*>(kc + kcode_off(t, grp)) = make_uint4(kp[0], kp[1], kp[2], kp[3]);
+            reinterpret_cast<uint32_t*>(p.c.k_meta)[slot_g * 4 + grp] = ks | (kz << 16);
+            reinterpret_cast<uint32_t*>(p.c.v_meta)[slot_g * 4 + grp] = vs | (vz << 16);
+            if (grp == 0) p.c.q_pos[slot_g] = pos;
+        }
+        const bool pair_valid = (tile * kTile + (t & ~1)) < n_q;
+        if (pair_valid) {
+            const int P = t >> 1;
+            const int Q0 = 8 * grp + (odd ? 4 : 0);
+            *reinterpret_cast<uint2*>(vc + vcode_off(P, Q0)) = make_uint2(pw[0], pw[1]);
+            *reinterpret_cast<uint2*>(vc + vcode_off(P, Q0 + 2)) = make_uint2(pw[2], pw[3]);
+        }
+        return;
+    }
+    tile -= qt;
+    const int t = tid >> 2, part = tid & 3;
+    if (tile < kt) {
+        // ---------------- kept tile
+        const int i = tile * kTile + t;
+        if (tile * kTile >= k) return;
+        if (i >= k) return;
+        const int pos = S[i];
+        const size_t tb = ((size_t)bg * kt + tile) * kTileBytes16;
+        uint8_t* kd = reinterpret_cast<uint8_t*>(p.c.k_keep) + tb;
+        uint8_t* vd = reinterpret_cast<uint8_t*>(p.c.v_keep) + tb;
+        const uint4* ks = reinterpret_cast<const uint4*>(krows + (size_t)pos * kD);
+        const uint4* vs = reinterpret_cast<const uint4*>(vrows + (size_t)pos * kD);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int c = part * 4 + c4;
+            *reinterpret_cast<uint4*>(kd + k16_off(t, c)) = ks[c];
+            *reinterpret_cast<uint4*>(vd + v16_off(t, c)) = vs[c];
+        }
+        if (part == 0) p.c.keep_pos[(size_t)bg * p.c.cap_keep + i] = pos;
+        return;
+    }
+    tile -= kt;
+    {
+        // ---------------- ring tile (slot = position % W)
+        const int s = tile * kTile + t;
+        const bool valid = T >= W || s < T;
+        const int pos = T >= W ? T - 1 - ((T - 1 - s) % W) : s;
+        const size_t tb = ((size_t)bg * (W / kTile) + tile) * kTileBytes16;
+        uint8_t* kd = reinterpret_cast<uint8_t*>(p.c.k_win) + tb;
+        uint8_t* vd = reinterpret_cast<uint8_t*>(p.c.v_win) + tb;
+        const uint4* ks = reinterpret_cast<const uint4*>(krows + (size_t)(valid ? pos : 0) * kD);
+        const uint4* vs = reinterpret_cast<const uint4*>(vrows + (size_t)(valid ? pos : 0) * kD);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int c = part * 4 + c4;
+            const uint4 zero = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(kd + k16_off(t, c)) = valid ? ks[c] : zero;
+            *reinterpret_cast<uint4*>(vd + v16_off(t, c)) = valid ? vs[c] : zero;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* k, const void* v, const int32_t* seq_lens, int32_t Tmax,
+                           const int32_t* sel_idx, const int32_t* sel_count, int32_t sel_stride_,
+                           const float* col_scores, const hq_thresh* thresh, const hq_cache& c,
+                           hipStream_t s) {
+    QuantParams p;
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.seq_lens = seq_lens;
+    p.sel_idx = sel_idx;
+    p.sel_count = sel_count;
+    p.col_scores = col_scores;
+    p.thresh = thresh;
+    p.c = c;
+    p.Tmax = Tmax;
+    p.sel_stride = sel_stride_;
+    const int tiles = c.cap_q / kTile + c.cap_keep / kTile + c.window / kTile;
+    dim3 grid(tiles, c.Hkv, c.B);
+    if (c.dt == HQ_F16)
+        k_quantize<true><<<grid, 256, 0, s>>>(p);
+    else
+        k_quantize<false><<<grid, 256, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace hq

@@ -1,0 +1,191 @@
+"""GPU parity: hq_quantize_kv (bit-exact codes, scales, zeros, positions,
+16-bit rows), hq_decode_attn (attention within max-abs 2e-3, rel-L2 1e-3 of
+the fp64 oracle) and hq_append_kv (bit-exact cache evolution), all through
+the C ABI."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import small_decode_inputs
+from synth.inputs import CONFIGS, make_decode_inputs
+
+from gpu_common import (assert_attn_close, ints_to_dev, oracle_caches, oracle_selection, selection_tensors,
+                        to_dev)
+from hq_layout import read_cache
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (inputs kwargs, window, keep)
+    "bf16_g4_ragged": (dict(B=2, Hq=8, Hkv=2, T=700, ragged_min=389, seed=11), 128, (5, 100)),
+    "f16_g1": (dict(B=1, Hq=1, Hkv=1, T=1000, dtype="f16", seed=12), 128, (5, 100)),
+    "bf16_g8_ragged": (dict(B=2, Hq=16, Hkv=2, T=1500, ragged_min=1100, n_outlier=8, outlier_scale=30.0,
+                            plant_frac=0.01, seed=13), 128, (5, 100)),
+    "bf16_g2": (dict(B=3, Hq=4, Hkv=2, T=640, seed=14), 128, (5, 100)),
+    "bf16_short_T_lt_W": (dict(B=2, Hq=4, Hkv=1, T=100, probe_rows=64, seed=15), 128, (5, 100)),
+    "bf16_ratio100": (dict(B=1, Hq=4, Hkv=1, T=500, seed=16), 128, (100, 100)),
+    "bf16_window_covers": (dict(B=1, Hq=4, Hkv=1, T=900, seed=17), 1024, (5, 100)),
+    "bf16_all_int4": (dict(B=1, Hq=4, Hkv=1, T=777, seed=18), 0, (0, 100)),
+}
+
+
+def _run_quantize(inp, window, keep):
+    import torch
+    import kv_cache_amd as hq
+    sp = inp.spec
+    pol = hq.Policy(keep[0], keep[1], window, sp.probe_rows)
+    scores, sels = oracle_selection(inp, window, keep)
+    Tmax = inp.k.shape[2]
+    stride = hq.sel_stride(Tmax, pol)
+    sel, cnt, col, thr = selection_tensors(scores, sels, sp.B, sp.Hkv, Tmax, stride)
+    cache = hq.HybridCache(sp.B, sp.Hkv, Tmax + 256, Tmax, torch_dt(sp.dtype), "cuda", pol)
+    k, v = to_dev(inp.k, sp.dtype), to_dev(inp.v, sp.dtype)
+    hq.quantize_kv(cache, k, v, ints_to_dev(inp.seq_lens), sel, cnt, col, thr)
+    torch.cuda.synchronize()
+    return cache, scores, sels
+
+
+def torch_dt(dtype):
+    import torch
+    return torch.bfloat16 if dtype == "bf16" else torch.float16
+
+
+def _check_cache(cache, inp, ocaches):
+    g = read_cache(cache)
+    sp = inp.spec
+    assert g["err_flag"] == 0
+    for b in range(sp.B):
+        for h in range(sp.Hkv):
+            oc = ocaches[b][h]
+            bg = b * sp.Hkv + h
+            T = oc.T
+            qpos = np.nonzero(oc.mode == O.MODE_INT4)[0]
+            kpos = np.nonzero(oc.mode == O.MODE_KEPT)[0]
+            nq, nk = len(qpos), len(kpos)
+            assert list(g["counts"][b, h][:3]) == [T, nq, nk], (b, h)
+            assert np.array_equal(g["q_pos"][bg, :nq], qpos)
+            assert np.array_equal(np.sort(g["keep_pos"][bg, :nk]), kpos)
+            assert np.array_equal(g["k_codes"][bg, :nq], oc.k_codes[qpos]), (b, h)
+            assert np.array_equal(g["v_codes"][bg, :nq], oc.v_codes[qpos]), (b, h)
+            for name in ("k_s", "k_z", "v_s", "v_z"):
+                assert np.array_equal(g[name][bg, :nq].view(np.uint16), getattr(oc, name)[qpos].view(np.uint16)), name
+            kbits = inp.k[b, h]
+            vbits = inp.v[b, h]
+            order = g["keep_pos"][bg, :nk]
+            assert np.array_equal(g["k_keep"][bg, :nk], kbits[order])
+            assert np.array_equal(g["v_keep"][bg, :nk], vbits[order])
+            W = oc.window
+            if W:
+                wpos = np.arange(max(0, T - W), T)
+                assert np.array_equal(g["k_win"][bg, wpos % W], kbits[wpos])
+                assert np.array_equal(g["v_win"][bg, wpos % W], vbits[wpos])
+    return g
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_quantize_and_decode(name):
+    import torch
+    import kv_cache_amd as hq
+    kw, window, keep = CASES[name]
+    inp = small_decode_inputs(window=window, **kw)
+    sp = inp.spec
+    print(f"case {name}", flush=True)
+    cache, scores, sels = _run_quantize(inp, window, keep)
+    ocaches = oracle_caches(inp, sels, scores, window)
+    _check_cache(cache, inp, ocaches)
+    q = to_dev(inp.q, sp.dtype)
+    out = hq.decode_attn(cache, q).cpu().numpy()
+    torch.cuda.synchronize()
+    ref = O.decode_batch(O.to_f64(inp.q, sp.dtype), ocaches, 1 / math.sqrt(sp.D))
+    assert_attn_close(out, ref, f"decode {name}")
+    if keep == (100, 100) or window >= int(inp.seq_lens.max()):
+        # special cases: equal to exact softmax attention over the 16-bit K/V
+        G = sp.Hq // sp.Hkv
+        for b in range(sp.B):
+            T = int(inp.seq_lens[b])
+            for h in range(sp.Hkv):
+                qg = O.to_f64(inp.q[b, h * G:(h + 1) * G], sp.dtype)
+                ex = O.softmax_attention(qg, O.to_f64(inp.k[b, h, :T], sp.dtype),
+                                         O.to_f64(inp.v[b, h, :T], sp.dtype), 1 / math.sqrt(sp.D))
+                assert_attn_close(out[b, h * G:(h + 1) * G], ex, f"{name} exact-attention special case")
+
+
+def test_decode_output_dtypes_and_determinism():
+    import torch
+    import kv_cache_amd as hq
+    inp = small_decode_inputs(B=2, Hq=8, Hkv=2, T=900, seed=21)
+    cache, _, _ = _run_quantize(inp, 128, (5, 100))
+    q = to_dev(inp.q, "bf16")
+    a = hq.decode_attn(cache, q)
+    b = hq.decode_attn(cache, q)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "decode must be bitwise deterministic"
+    o16 = hq.decode_attn(cache, q, out_dtype=torch.bfloat16).float()
+    assert torch.allclose(o16, a, rtol=0, atol=float(a.abs().max()) * 2 ** -8 + 1e-6)
+
+
+def test_decode_c1_full_size():
+    """The 1-head 4K fp16 workload end to end (oracle selection)."""
+    import torch
+    import kv_cache_amd as hq
+    inp = make_decode_inputs(CONFIGS["c1_decode_4k_1head"])
+    sp = inp.spec
+    cache, scores, sels = _run_quantize(inp, 128, (5, 100))
+    ocaches = oracle_caches(inp, sels, scores, 128)
+    _check_cache(cache, inp, ocaches)
+    assert int(cache.counts()[0, 0, 2]) == 204 and int(cache.counts()[0, 0, 1]) == 4096 - 204 - 128
+    out = hq.decode_attn(cache, to_dev(inp.q, "f16")).cpu().numpy()
+    torch.cuda.synchronize()
+    ref = O.decode_batch(O.to_f64(inp.q, "f16"), ocaches, 1 / math.sqrt(128))
+    assert_attn_close(out, ref, "decode c1")
+
+
+@pytest.mark.parametrize("dtype,W,steps", [("bf16", 128, 150), ("f16", 128, 70), ("bf16", 0, 40), ("bf16", 192, 90)])
+def test_append_matches_oracle(dtype, W, steps):
+    import torch
+    import kv_cache_amd as hq
+    from synth.inputs import make_append_tokens
+    inp = small_decode_inputs(B=2, Hq=8, Hkv=2, T=600, dtype=dtype, window=W, seed=31)
+    sp = inp.spec
+    keep = (5, 100) if W else (0, 100)
+    pol = hq.Policy(keep[0], keep[1], W, sp.probe_rows)
+    scores, sels = oracle_selection(inp, W, keep)
+    # make a few window tokens outrank the k-th candidate so departures get kept
+    for b in range(sp.B):
+        for g in range(sp.Hkv):
+            T = int(inp.seq_lens[b])
+            if W and sels[b][g].k:
+                scores[b][g][T - W + 3] = 10.0
+                scores[b][g][T - W + 40] = sels[b][g].tau   # exact tie with tau, lower index?
+    Tmax = inp.k.shape[2]
+    stride = hq.sel_stride(Tmax, pol)
+    sel, cnt, col, thr = selection_tensors(scores, sels, sp.B, sp.Hkv, Tmax, stride)
+    cache = hq.HybridCache(sp.B, sp.Hkv, Tmax + steps, Tmax, torch_dt(dtype), "cuda", pol)
+    hq.quantize_kv(cache, to_dev(inp.k, dtype), to_dev(inp.v, dtype), ints_to_dev(inp.seq_lens), sel, cnt, col, thr)
+    ocaches = oracle_caches(inp, sels, scores, W)
+    kn, vn, qn = make_append_tokens(sp, inp.outlier_channels, steps)
+    kd, vd = to_dev(kn, dtype), to_dev(vn, dtype)
+    for s in range(steps):
+        hq.append_kv(cache, kd[s], vd[s])
+        for b in range(sp.B):
+            for g in range(sp.Hkv):
+                ocaches[b][g] = O.append_token(ocaches[b][g], O.to_f64(kn[s, b, g], dtype), O.to_f64(vn[s, b, g], dtype))
+    torch.cuda.synchronize()
+    # extend the inputs seen by the row checks with the appended tokens
+    k_all = np.concatenate([inp.k, np.zeros((sp.B, sp.Hkv, steps, sp.D), np.uint16)], axis=2)
+    v_all = np.concatenate([inp.v, np.zeros((sp.B, sp.Hkv, steps, sp.D), np.uint16)], axis=2)
+    for b in range(sp.B):
+        T0 = int(inp.seq_lens[b])
+        k_all[b, :, T0:T0 + steps] = kn[:, b].transpose(1, 0, 2)
+        v_all[b, :, T0:T0 + steps] = vn[:, b].transpose(1, 0, 2)
+
+    class _I:
+        pass
+    ext = _I()
+    ext.spec, ext.k, ext.v = sp, k_all, v_all
+    _check_cache(cache, ext, ocaches)
+    out = hq.decode_attn(cache, to_dev(qn[-1], dtype)).cpu().numpy()
+    ref = O.decode_batch(O.to_f64(qn[-1], dtype), ocaches, 1 / math.sqrt(sp.D))
+    assert_attn_close(out, ref, f"decode after {steps} appends")
