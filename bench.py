@@ -185,8 +185,9 @@ def main():
     def step():
         nonlocal prefill_ok
         if not args.decode_only:
-            sel4 = tm("probe_select", hq.probe_select, qp, k, lens, pol)
-            tm("quantize_kv", hq.quantize_kv, cache, k, v, lens, *sel4)
+            col, sel, cnt, thr = tm("probe_select", hq.probe_select, qp, k, lens, pol)
+            tm("quantize_kv", hq.quantize_kv, cache, k, v, lens, sel, cnt, col, thr)
+            sel4 = (col, sel, cnt, thr)
         else:
             sel4 = None
         tm("append_kv", hq.append_kv, cache, knew, vnew)
@@ -202,8 +203,8 @@ def main():
         return sel4
 
     if args.decode_only:
-        sel4 = hq.probe_select(qp, k, lens, pol)
-        hq.quantize_kv(cache, k, v, lens, *sel4)
+        col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol)
+        hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

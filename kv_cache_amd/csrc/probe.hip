@@ -74,7 +74,8 @@ __device__ inline void load32_f64(const uint16_t* src, bool ok, double* out) {
 
 // Exact 16 x 16 block of dot products over 128 channels. Lane l supplies row
 // (l % 16) of A and column (l % 16) of B for channels 32*(l/16) .. +31; the
-// result element i of lane l is D[4*(l/16) + i][l % 16].
+// result element i of lane l is D[4*i + l/16][l % 16] (rows interleave across
+// the four 16-lane groups).
 __device__ inline double4_t mfma_dot128(const double* a, const double* b) {
     double4_t acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void k_probe_rowstats(ProbeParams p) {
             load32_f64<F16>(qrow(p, b, g, rt * 16 + li) + 32 * kq, true, a);
             int pos[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pos[i] = row_pos(p, T, rt * 16 + 4 * kq + i);
+            for (int i = 0; i < 4; ++i) pos[i] = row_pos(p, T, rt * 16 + 4 * i + kq);
             const int key_hi = min(key_lo + kKeyChunk, T);
             for (int k0 = key_lo; k0 < key_hi; k0 += 16) {
                 const int key = k0 + li;
@@ -159,9 +160,9 @@ __global__ __launch_bounds__(256) void k_probe_rowstats(ProbeParams p) {
             }
         }
         if (li == 0) {
-            double2* dst = p.part + ((size_t)bg * p.nchunk + chunk) * p.NR + rt * 16 + 4 * kq;
+            double2* dst = p.part + ((size_t)bg * p.nchunk + chunk) * p.NR + rt * 16 + kq;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = make_double2(m[i], l[i]);
+            for (int i = 0; i < 4; ++i) dst[4 * i] = make_double2(m[i], l[i]);
         }
     }
 }
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(256) void k_probe_colsum(ProbeParams p) {
         const double4_t acc = mfma_dot128(a, bv);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = rt * 16 + 4 * kq + i;
+            const int row = rt * 16 + 4 * i + kq;
             const int pr = rpos[row];
             if (kok && pr >= 0 && key <= pr) {
                 const double2 st = rs[row];

@@ -128,6 +128,10 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
         if (tile * kTile >= k) return;
         if (i >= k) return;
         const int pos = S[i];
+        if (pos < 0 || pos >= T - nwin || (i > 0 && S[i - 1] >= pos)) {
+            atomicOr(p.c.err_flag, 4);  // selected positions must be ascending candidates
+            return;
+        }
         const size_t tb = ((size_t)bg * kt + tile) * kTileBytes16;
         uint8_t* kd = reinterpret_cast<uint8_t*>(p.c.k_keep) + tb;
         uint8_t* vd = reinterpret_cast<uint8_t*>(p.c.v_keep) + tb;

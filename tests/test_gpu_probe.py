@@ -1,0 +1,98 @@
+"""GPU parity of hq_probe_select: column scores against the fp64 oracle,
+the selected index sets (bit-exact, lower-index tie-break; flips allowed
+only between near-ties whose oracle scores differ by < 1e-6 relative, each
+counted and reported), and the top-k applied to the GPU's own fp32 scores
+(bit-exact)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import small_decode_inputs
+
+from gpu_common import ints_to_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NEAR_TIE = 1e-6
+
+
+def compare_selection(gpu_idx, gpu_cnt, c_or, T, W, keep):
+    """Returns the number of near-tie flips; fails on any other difference."""
+    s = O.select_topk(c_or, T, W, keep[0], keep[1])
+    assert gpu_cnt == s.k
+    a, b = set(gpu_idx.tolist()), set(s.idx.tolist())
+    only_gpu, only_or = sorted(a - b), sorted(b - a)
+    assert len(only_gpu) == len(only_or)
+    for x, y in zip(sorted(only_gpu, key=lambda j: -c_or[j]), sorted(only_or, key=lambda j: c_or[j])):
+        gap = abs(c_or[x] - c_or[y]) / max(c_or[x], c_or[y])
+        assert gap < NEAR_TIE, f"selection flip with gap {gap:.3e} (positions {x}, {y})"
+    return len(only_gpu)
+
+
+def run_probe(inp, window, keep):
+    import kv_cache_amd as hq
+    sp = inp.spec
+    pol = hq.Policy(keep[0], keep[1], window, sp.probe_rows)
+    col, sel, cnt, thr = hq.probe_select(to_dev(inp.q_probe, sp.dtype), to_dev(inp.k, sp.dtype),
+                                         ints_to_dev(inp.seq_lens), pol)
+    return tuple(t.cpu().numpy() for t in (col, sel, cnt, thr))
+
+
+def check_probe(inp, window=128, keep=(5, 100), rel_tol=1e-6, sample=None):
+    sp = inp.spec
+    col, sel, cnt, thr = run_probe(inp, window, keep)
+    sm = 1 / math.sqrt(sp.D)
+    qp = O.to_f64(inp.q_probe, sp.dtype)
+    flips, worst = 0, 0.0
+    pairs = sample or [(b, g) for b in range(sp.B) for g in range(sp.Hkv)]
+    for (b, g) in pairs:
+        T = int(inp.seq_lens[b])
+        c_or = O.probe_column_scores(qp[b, g * (sp.Hq // sp.Hkv):(g + 1) * (sp.Hq // sp.Hkv)],
+                                     O.to_f64(inp.k[b, g:g + 1], sp.dtype), T, sm)[0]
+        rel = np.abs(col[b, g, :T].astype(np.float64) - c_or) / np.maximum(c_or, 1e-300)
+        worst = max(worst, float(rel.max()))
+        assert rel.max() <= rel_tol, (b, g, float(rel.max()))
+        assert np.all(col[b, g, T:] == 0)
+        flips += compare_selection(sel[b, g, : cnt[b, g]], int(cnt[b, g]), c_or, T, window, keep)
+        # the top-k stage alone: the oracle's selection on the GPU's own fp32 scores
+        s32 = O.select_topk(col[b, g, :T].astype(np.float64), T, window, keep[0], keep[1])
+        assert np.array_equal(sel[b, g, : cnt[b, g]], s32.idx), (b, g)
+        assert np.all(sel[b, g, cnt[b, g]:] == -1)
+        assert int(thr[b, g, 1]) == s32.j_k
+        tau = float(thr[b, g, 0:1].view(np.float32)[0])
+        assert (tau == s32.tau) or (s32.k == 0 and math.isinf(tau))
+    print(f"probe: max rel err {worst:.3e}, near-tie flips {flips}", flush=True)
+    return flips
+
+
+@pytest.mark.parametrize("kw,window,keep", [
+    (dict(B=2, Hq=8, Hkv=2, T=700, ragged_min=389, seed=41), 128, (5, 100)),
+    (dict(B=1, Hq=1, Hkv=1, T=1000, dtype="f16", seed=42), 128, (5, 100)),
+    (dict(B=2, Hq=16, Hkv=2, T=2500, ragged_min=1100, n_outlier=8, outlier_scale=30.0, plant_frac=0.01,
+          seed=43), 128, (5, 100)),
+    (dict(B=2, Hq=4, Hkv=2, T=1500, seed=44), 128, (1, 100)),
+    (dict(B=1, Hq=4, Hkv=1, T=600, seed=45), 128, (100, 100)),
+    (dict(B=2, Hq=2, Hkv=1, T=40, seed=46), 128, (5, 100)),        # T < probe rows, T < window
+    (dict(B=1, Hq=8, Hkv=1, T=300, probe_rows=16, seed=47), 64, (5, 100)),
+])
+def test_probe_matches_oracle(kw, window, keep):
+    inp = small_decode_inputs(window=window, **kw)
+    check_probe(inp, window, keep)
+
+
+def test_probe_exact_ties_take_lower_index():
+    """Copies of a key row placed before every probe row give exactly equal
+    column scores; among the tied columns the selection must be a prefix in
+    position order."""
+    inp = small_decode_inputs(B=1, Hq=4, Hkv=1, T=800, seed=48)
+    inp.k[0, 0, 100:400] = inp.k[0, 0, 0]   # token 0 is a planted vertical line
+    flips = check_probe(inp, 128, (5, 100))
+    assert flips == 0
+    col, sel, cnt, thr = run_probe(inp, 128, (5, 100))
+    tied = np.array([0] + list(range(100, 400)))
+    assert np.all(col[0, 0, tied] == col[0, 0, 0])
+    chosen = sorted(set(sel[0, 0, : cnt[0, 0]].tolist()) & set(tied.tolist()))
+    assert chosen == sorted(tied.tolist())[: len(chosen)]
+    print(f"tied columns selected: {len(chosen)} of {len(tied)}")
