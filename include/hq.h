@@ -135,10 +135,10 @@ size_t hq_probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32
  * the decode kernel is contiguous across the wavefront:
  *   K codes, tile byte  group*1024 + slot*16 + i : packed byte i of the
  *       32-channel group (byte i = code[2i] | code[2i+1] << 4);
- *   V codes, pre-paired: the 32-bit word for slots (2P, 2P+1) and channels
- *       4Q..4Q+3 holds slot 2P's four nibbles in its low half and slot
- *       2P+1's in its high half; it sits at (j/2)*1024 + (16u + Q/2)*16 +
- *       ((j%2)*2 + Q%2)*4 with u = P/8, j = P%8;
+ *   V codes, pre-paired: the 32-bit word for slots (P, P+32), P < 32, and
+ *       channels 4Q..4Q+3 holds slot P's four nibbles in its low half and
+ *       slot P+32's in its high half; it sits at (j/2)*1024 + (16u + Q/2)*16
+ *       + ((j%2)*2 + Q%2)*4 with u = P/8, j = P%8;
  *   16-bit K rows, chunk c (channels 8c..8c+7) of slot t at c*1024 + t*16;
  *   16-bit V rows, chunk c of slot t at (t%16)*1024 + (16*(t/16) + c)*16.
  * Position tags give the canonical order. The struct is filled by the caller

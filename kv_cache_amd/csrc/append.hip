@@ -92,7 +92,7 @@ __global__ __launch_bounds__(64) void k_append(hq_cache c, const uint16_t* k_new
                         reinterpret_cast<uint32_t*>(c.k_meta)[slot_g * 4 + grp] = sb | (zb << 16);
                     } else {
                         uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + tb;
-                        const int P = ts >> 1, half = ts & 1;
+                        const int P = ts & 31, half = ts >> 5;  // pairs are slots (P, P + 32)
 #pragma unroll
                         for (int q = 0; q < 8; ++q) {
                             const uint16_t bits = (uint16_t)((pk[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);

@@ -8,29 +8,34 @@
 // expanded first). The low-bit and 16-bit paths share one online-softmax
 // state ("HyQuant: ...", "How this relates to prior wiki pages").
 //
-// Design (MI355X, wave64, HBM-bound):
+// Design (MI355X, wave64, HBM-bound, VALU-heavy):
 //  * One workgroup = 4 waves = one (b, g) and a contiguous span of 64-token
 //    tiles (a split); every wave takes every 4th tile of the span. All G query
 //    heads of the KV head are processed together, so each cache byte is read
 //    once per step.
 //  * Token phase, lane = token: the lane loads its token's 64 B of K codes
-//    (4 x 128-bit, contiguous across the wave) and 16 B of K scales/zeros.
-//    Codes are turned into bf16 (or fp16) "128 + 8c" magic values with one
-//    shift + one and-or per pair and multiplied against the query with
-//    v_dot2 (exact products, fp32 accumulation); the per-group scale and
-//    zero are applied afterwards: q.k~ = s*(q/8 . (128+8c)) + (z - 16 s)*sum(q).
-//    The query pairs sit in scalar registers (uniform loads).
-//  * Online softmax per tile with a lazy rescale (only when the running max
-//    grows by more than 2^8), in log2 units with v_exp_f32.
-//  * Channel phase, lane = 8 channels x 16 tokens: the V codes are stored
-//    pre-transposed so each lane's four 128-bit loads hold exactly its
-//    channels for its tokens; p*s per token and group comes through LDS;
-//    PV accumulates in fp32 FMAs. z-terms (sum p*z) accumulate per lane in
-//    the token phase.
-//  * 16-bit tiles (kept columns, window ring) use the same loop with the
-//    16-bit rows instead of codes.
-//  * Each workgroup writes one partial (m, l, o[128]) per head; a second
-//    kernel merges the splits.
+//    (4 x 128-bit, contiguous across the wave) and its K and V scales/zeros.
+//    Codes become bf16 (or fp16) "128 + 8c" magic values with one shift + one
+//    and-or per pair and meet the query in v_dot2 (exact products, fp32
+//    accumulation); the group's scale and zero are applied afterwards:
+//    q.k~ = s * (q/8 . (128 + 8c)) + (z - 16 s) * sum(q). Query pairs are
+//    uniform and live in scalar registers.
+//  * Online softmax per tile in log2 units (v_exp_f32) with a lazy rescale
+//    (only when the running max grows by more than 2^8); wave maxima use DPP
+//    and v_permlane16/32_swap, no LDS.
+//  * PV on INT4 tiles: the V codes are stored pre-paired, slot t with slot
+//    t + 32, so the weights w = p * s * 2^-E of the two tokens form one fp16
+//    pair (one v_permlane32_swap); the channel-phase lane (8 channels x 16
+//    tokens) turns each code pair into fp16 "1024 + 16c" with one and-or and
+//    accumulates with v_dot2_f32_f16 in fp32. E is a running power-of-two
+//    bound on p*s (exact rescale when it grows) so every w is <= 1 in fp16.
+//    The 1024-bias is removed exactly with the sum of the same fp16 weights;
+//    sum(p*z) accumulates in fp32 in the token phase.
+//  * 16-bit tiles (kept columns, window ring) use fp32 FMAs on the 16-bit
+//    rows.
+//  * Each workgroup writes one partial (m, l, o[128]) per head; the last
+//    workgroup of a (b, g) (device-scope atomic counter, cleared by the prep
+//    kernel) merges the splits and writes the output.
 #include "hq_internal.h"
 
 namespace hq {
@@ -47,6 +52,9 @@ struct DecodeParams {
     float* part_m;         // [B][Hkv][nsplit][G]
     float* part_l;         // [B][Hkv][nsplit][G]
     float* part_o;         // [B][Hkv][nsplit][G][128]
+    int32_t* done;         // [B][Hkv] finished-split counters
+    void* out;
+    int32_t out_dt, Hq;
     int32_t nsplit, tps, G;
     float scale2;          // sm_scale * log2(e)
 };
@@ -63,6 +71,7 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
         return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                                __builtin_bit_cast(bf16x2_t, b), c, false);
 }
+__device__ inline float dot2h(uint32_t a, uint32_t b, float c) { return dot2<true>(a, b, c); }
 
 // Four magic-biased code pairs from one dword of 8 nibbles (channels 8i+n).
 // Pair n holds channels (n, n+4). bf16: value 128 + 8c (code in bits 3..6);
@@ -83,7 +92,6 @@ __device__ inline void extract_pairs(uint32_t w, uint32_t* pr) {
         pr[3] = ((w >> 9) & M) | C;
     }
 }
-// sum over the group of q_d * (bias value): bf16 16*sum(q), fp16 64*sum(q).
 template <bool F16>
 constexpr float kBias = F16 ? 64.0f : 16.0f;
 
@@ -91,16 +99,53 @@ __device__ inline uint32_t u4w(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+template <int CTRL>
+__device__ inline float dppmov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Maximum over the 64 lanes, every lane gets it (no LDS traffic).
+__device__ inline float wave_max_fast(float v) {
+    v = fmaxf(v, dppmov<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dppmov<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dppmov<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dppmov<0x140>(v));  // row_mirror
+    auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+// Value held by lane (l + 32) % 64.
+__device__ inline float other_half(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
+}
+
 __device__ inline void lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
 }
 
+__device__ inline void store_out(void* out, int dt, size_t i, float r) {
+    if (dt == HQ_F32)
+        static_cast<float*>(out)[i] = r;
+    else if (dt == HQ_F16)
+        static_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_f16_bits(r);
+    else {
+        uint32_t x = __float_as_uint(r);
+        x += 0x7FFFu + ((x >> 16) & 1u);
+        static_cast<uint16_t*>(out)[i] = (uint16_t)(x >> 16);
+    }
+}
+
 template <int G, bool F16>
 __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
-    __shared__ float lds_ps[kWaves][kTile * 4 * G];       // [slot][group][head]
+    // fp16 weight pairs of the INT4 tile: word (pair P, group g, head h) at
+    // P*4G + ((g ^ (P/8 % 4)) * G) + h
+    __shared__ uint32_t lds_pw[kWaves][32 * 4 * G];
+    __shared__ float lds_p[kWaves][kTile * G];          // 16-bit tiles: p per token
     __shared__ float lds_m[kWaves][G], lds_l[kWaves][G];
     __shared__ float lds_o[kWaves][G][kD];
+    __shared__ int sh_last;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -115,39 +160,46 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
     const int v0 = s * p.tps;
     if (v0 >= total) return;
     const int v1 = min(v0 + p.tps, total);
+    const int active = (total + p.tps - 1) / p.tps;
 
     const int qt_cap = p.c.cap_q / kTile, kt_cap = p.c.cap_keep / kTile, wt_cap = W / kTile;
     const uint32_t* qp = p.qp + (size_t)bg * 4 * G * 16;
     const uint32_t* qn = p.qn + (size_t)bg * G * 64;
     const float* qs = p.qsum + (size_t)bg * G * 4;
 
-    float m[G], l[G], zacc[G][4], acc[G][8];
+    // token-phase state
+    float m[G], l[G], zacc[G][4], wsum[G][4];
+    // channel-phase state, in units of 2^E / 16: INT4 tiles add magic-biased
+    // sums (bias removed at the end with wsum), 16-bit tiles add p*v*16*2^-E
+    float acc[G][8];
+    int E = -1000;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         m[h] = -INFINITY;
         l[h] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zacc[h][i] = 0.f;
+        for (int i = 0; i < 4; ++i) zacc[h][i] = wsum[h][i] = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
     }
     const int u = lane >> 4, c8 = lane & 15, gk = c8 >> 2;
-    float* ps_w = lds_ps[wave];
+    uint32_t* pw_w = lds_pw[wave];
+    float* p_w = lds_p[wave];
+    const uint32_t ONES = 0x3C003C00u;  // fp16 (1, 1)
 
     for (int v = v0 + wave; v < v1; v += kWaves) {
         float lg[G];
-        bool int4_tile = v < nqt;
-        int count, tile_base_slot;
+        const bool int4_tile = v < nqt;
+        int count, tile;
         float vs[4], vz[4];
         if (int4_tile) {
             // ----------------------------- token phase, INT4 tile
-            const int tile = v;
-            tile_base_slot = tile * kTile;
+            tile = v;
             count = n_q;
-            const bool valid = tile_base_slot + lane < n_q;
+            const bool valid = tile * kTile + lane < n_q;
             const uint8_t* kc = reinterpret_cast<const uint8_t*>(p.c.k_codes) +
                                 ((size_t)bg * qt_cap + tile) * kTileBytesQ;
-            const size_t slot_g = (size_t)bg * p.c.cap_q + tile_base_slot + lane;
+            const size_t slot_g = (size_t)bg * p.c.cap_q + tile * kTile + lane;
             uint4 kw[4];
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp)
@@ -184,10 +236,9 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         } else {
             // ----------------------------- token phase, 16-bit tile
             const bool keep = v < nqt + nkt;
-            const int tile = keep ? v - nqt : v - nqt - nkt;
-            tile_base_slot = tile * kTile;
+            tile = keep ? v - nqt : v - nqt - nkt;
             count = keep ? n_keep : nring;
-            const bool valid = tile_base_slot + lane < count;
+            const bool valid = tile * kTile + lane < count;
             const uint8_t* kt = keep ? reinterpret_cast<const uint8_t*>(p.c.k_keep) +
                                            ((size_t)bg * kt_cap + tile) * kTileBytes16
                                      : reinterpret_cast<const uint8_t*>(p.c.k_win) +
@@ -212,13 +263,16 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         float pr_h[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float tmax = wave_max(lg[h]);
+            const float tmax = wave_max_fast(lg[h]);
             if (tmax > m[h] + kLazy) {
                 const float alpha = __builtin_amdgcn_exp2f(m[h] - tmax);
                 m[h] = tmax;
                 l[h] *= alpha;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) zacc[h][i] *= alpha;
+                for (int i = 0; i < 4; ++i) {
+                    zacc[h][i] *= alpha;
+                    wsum[h][i] *= alpha;
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
             }
@@ -227,56 +281,77 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         }
 
         if (int4_tile) {
-            // p*s per group to LDS; z-terms accumulate here
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
+            // running power-of-two bound 2^E >= 2^8 * max(s) so that p*s*2^-E <= 1
+            const float smax = wave_max_fast(fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])));
+            const int e_need = smax > 0.f ? (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127 + 9 : -1000;
+            if (e_need > E) {
+                const float r = E <= -1000 ? 0.f : __builtin_ldexpf(1.0f, E - e_need);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    ps_w[(lane * 4 + grp) * G + h] = pr_h[h] * vs[grp];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[h][i] *= r;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) wsum[h][i] *= r;
+                }
+                E = e_need;
+            }
+            const float f = E <= -1000 ? 1.0f : __builtin_ldexpf(1.0f, -E);
+            // fp16 weight pairs (slot lane, slot lane + 32), built by lanes 0..31
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const float sf = vs[grp] * f;
+                uint32_t words[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
                     zacc[h][grp] = fmaf(pr_h[h], vz[grp], zacc[h][grp]);
+                    const float w = pr_h[h] * sf;
+                    const float w2 = other_half(w);
+                    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+                    h2_t pk = {(_Float16)w, (_Float16)w2};
+                    words[h] = __builtin_bit_cast(uint32_t, pk);
+                    wsum[h][grp] = dot2h(words[h], ONES, wsum[h][grp]);
+                }
+                if (lane < 32) {
+                    const int P = lane;
+                    uint32_t* dst = pw_w + P * 4 * G + ((grp ^ ((P >> 3) & 3)) * G);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) dst[h] = words[h];
                 }
             }
             lds_fence();
             // ----------------------------- channel phase, INT4 V
             const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.c.v_codes) +
-                                ((size_t)bg * qt_cap + (tile_base_slot / kTile)) * kTileBytesQ;
+                                ((size_t)bg * qt_cap + tile) * kTileBytesQ;
             uint4 vw[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) vw[kk] = *reinterpret_cast<const uint4*>(vc + kk * 1024 + lane * 16);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int sa = 16 * u + 2 * j;
-                float pa[G], pb[G];
+                const int P = 8 * u + j;
+                uint32_t pw[G];
+                const uint32_t* src = pw_w + P * 4 * G + ((gk ^ u) * G);
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    pa[h] = ps_w[(sa * 4 + gk) * G + h];
-                    pb[h] = ps_w[((sa + 1) * 4 + gk) * G + h];
-                }
+                for (int h = 0; h < G; ++h) pw[h] = src[h];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const uint32_t d = u4w(vw[j >> 1], (j & 1) * 2 + e);
-                    const uint32_t m0 = d & 0x0F0F0F0Fu, m1 = (d >> 4) & 0x0F0F0F0Fu;
-                    const float a0 = (float)(m0 & 0xFF), a2 = (float)((m0 >> 8) & 0xFF);
-                    const float b0 = (float)((m0 >> 16) & 0xFF), b2 = (float)(m0 >> 24);
-                    const float a1 = (float)(m1 & 0xFF), a3 = (float)((m1 >> 8) & 0xFF);
-                    const float b1 = (float)((m1 >> 16) & 0xFF), b3 = (float)(m1 >> 24);
+                    uint32_t cp[4];
+                    extract_pairs<true>(d, cp);
 #pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        acc[h][4 * e + 0] = fmaf(pb[h], b0, fmaf(pa[h], a0, acc[h][4 * e + 0]));
-                        acc[h][4 * e + 1] = fmaf(pb[h], b1, fmaf(pa[h], a1, acc[h][4 * e + 1]));
-                        acc[h][4 * e + 2] = fmaf(pb[h], b2, fmaf(pa[h], a2, acc[h][4 * e + 2]));
-                        acc[h][4 * e + 3] = fmaf(pb[h], b3, fmaf(pa[h], a3, acc[h][4 * e + 3]));
-                    }
+                    for (int n = 0; n < 4; ++n)
+#pragma unroll
+                        for (int h = 0; h < G; ++h) acc[h][4 * e + n] = dot2h(cp[n], pw[h], acc[h][4 * e + n]);
                 }
             }
             lds_fence();
         } else {
+            if (E <= -1000) E = 0;  // no INT4 tile yet: fix the accumulator unit
+            const float k16 = __builtin_ldexpf(16.0f, -E);
 #pragma unroll
-            for (int h = 0; h < G; ++h) ps_w[lane * G + h] = pr_h[h];
+            for (int h = 0; h < G; ++h) p_w[lane * G + h] = pr_h[h] * k16;
             lds_fence();
             // ----------------------------- channel phase, 16-bit V
             const bool keep = v < nqt + nkt;
-            const int tile = tile_base_slot / kTile;
             const uint8_t* vt = keep ? reinterpret_cast<const uint8_t*>(p.c.v_keep) +
                                            ((size_t)bg * kt_cap + tile) * kTileBytes16
                                      : reinterpret_cast<const uint8_t*>(p.c.v_win) +
@@ -285,7 +360,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
             for (int i = 0; i < 16; ++i) {
                 const int slot = 16 * u + i;
                 const uint4 vv = *reinterpret_cast<const uint4*>(vt + i * 1024 + lane * 16);
-                if (tile_base_slot + slot < count) {
+                if (tile * kTile + slot < count) {
                     float x[8];
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
@@ -294,7 +369,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
                     }
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        const float pw = ps_w[slot * G + h];
+                        const float pw = p_w[slot * G + h];
 #pragma unroll
                         for (int ch = 0; ch < 8; ++ch) acc[h][ch] = fmaf(pw, x[ch], acc[h][ch]);
                     }
@@ -305,11 +380,16 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
     }
 
     // ----------------------------- wave epilogue
+    // wsum: lanes 0..31 hold the packed pairs; reduce over them only
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         l[h] = wave_sum(l[h]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zacc[h][i] = wave_sum(zacc[h][i]);
+        for (int i = 0; i < 4; ++i) {
+            zacc[h][i] = wave_sum(zacc[h][i]);
+            float ws = lane < 32 ? wsum[h][i] : 0.f;
+            wsum[h][i] = wave_sum(ws);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             acc[h][i] += __shfl_xor(acc[h][i], 16);
@@ -317,10 +397,14 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         }
     }
     if (lane < 16) {
+        const float unit = E <= -1000 ? 0.f : __builtin_ldexpf(1.0f, E - 4);  // 2^E / 16
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h) {
+            const float bias = 1024.0f * wsum[h][lane >> 2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) lds_o[wave][h][8 * lane + i] = acc[h][i] + zacc[h][lane >> 2];
+            for (int i = 0; i < 8; ++i)
+                lds_o[wave][h][8 * lane + i] = fmaf(unit, acc[h][i] - bias, zacc[h][lane >> 2]);
+        }
     }
     if (lane == 0) {
 #pragma unroll
@@ -351,24 +435,47 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
             p.part_l[pbase + h] = L;
         }
     }
+    // ----------------------------- the last split of (b, g) merges all splits
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) sh_last = atomicAdd(p.done + bg, 1) == active - 1;
+    __syncthreads();
+    if (!sh_last) return;
+    __threadfence();
+    const size_t base0 = (size_t)bg * p.nsplit * G;
+    for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
+        const int h = idx / kD, d = idx % kD;
+        float M = -INFINITY;
+        for (int sp = 0; sp < active; ++sp) M = fmaxf(M, p.part_m[base0 + sp * G + h]);
+        float L = 0.f, O = 0.f;
+        for (int sp = 0; sp < active; ++sp) {
+            const float ms = p.part_m[base0 + sp * G + h];
+            const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+            L = fmaf(f, p.part_l[base0 + sp * G + h], L);
+            O = fmaf(f, p.part_o[(base0 + sp * G + h) * kD + d], O);
+        }
+        store_out(p.out, p.out_dt, ((size_t)b * p.Hq + g * G + h) * kD + d, O / L);
+    }
 }
 
 // Rearranges the query for the split kernel: INT4-path pairs (prescaled by
-// 1/8 for bf16, 1/16 for fp16, exact), natural pairs and group sums.
+// 1/8 for bf16, 1/16 for fp16, exact), natural pairs and group sums; clears
+// the split counters of this (b, g).
 template <bool F16>
 __global__ __launch_bounds__(128) void k_decode_prep(const uint16_t* q, int Hq, int G, uint32_t* qp,
-                                                     uint32_t* qn, float* qsum) {
+                                                     uint32_t* qn, float* qsum, int32_t* done) {
     const int g = blockIdx.x, b = blockIdx.y, Hkv = gridDim.x;
     const int bg = b * Hkv + g;
     const int t = threadIdx.x;
+    if (t == 0) done[bg] = 0;
+    const float sc = F16 ? 0.0625f : 0.125f;
     for (int h = 0; h < G; ++h) {
         const uint16_t* qh = q + ((size_t)b * Hq + g * G + h) * kD;
-        if (t < 64) qn[((size_t)bg * G + h) * 64 + t] = (uint32_t)qh[2 * t] | ((uint32_t)qh[2 * t + 1] << 16);
-        // INT4 arrangement: entry (grp, 4i + n) = (q[32grp+8i+n], q[32grp+8i+n+4]) * 2^-3 (bf16) / 2^-4 (fp16)
         if (t < 64) {
+            qn[((size_t)bg * G + h) * 64 + t] = (uint32_t)qh[2 * t] | ((uint32_t)qh[2 * t + 1] << 16);
+            // INT4 arrangement: entry (grp, 4i + n) = (q[32grp+8i+n], q[32grp+8i+n+4]) * 2^-3 / 2^-4
             const int grp = t >> 4, e = t & 15, i = e >> 2, n = e & 3;
             const int d0 = 32 * grp + 8 * i + n;
-            const float sc = F16 ? 0.0625f : 0.125f;
             const float a = h16_to_f32<F16>(qh[d0]) * sc, c = h16_to_f32<F16>(qh[d0 + 4]) * sc;
             uint32_t wa, wc;
             if constexpr (F16) {
@@ -380,59 +487,18 @@ __global__ __launch_bounds__(128) void k_decode_prep(const uint16_t* q, int Hq, 
             }
             qp[(((size_t)bg * 4 + grp) * G + h) * 16 + e] = wa | (wc << 16);
         }
-        if (t < 4) {
-            // group sum of the prescaled-then-rescaled values (exactly the values the
-            // pairs carry, times 8 or 16), accumulated in double
-            const float sc = F16 ? 0.0625f : 0.125f;
-            double acc = 0.0;
-            for (int d = 32 * t; d < 32 * t + 32; ++d) {
-                float a = h16_to_f32<F16>(qh[d]) * sc;
-                if constexpr (F16) a = f16_to_f32(f32_to_f16_bits(a));
-                acc += (double)a;
-            }
-            qsum[((size_t)bg * G + h) * 4 + t] = (float)(acc / sc);
-        }
-    }
-}
-
-__global__ __launch_bounds__(128) void k_decode_reduce(const hq_cache c, const float* part_m,
-                                                       const float* part_l, const float* part_o,
-                                                       int nsplit, int tps, int G, int Hq, void* out,
-                                                       int out_dt) {
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-    const int g = h / G, hl = h % G;
-    const int bg = b * c.Hkv + g;
-    const int4 cnt = *reinterpret_cast<const int4*>(c.counts + 4 * bg);
-    const int T = cnt.x, n_q = cnt.y, n_keep = cnt.z;
-    const int nring = T < c.window ? T : c.window;
-    const int total = (n_q + kTile - 1) / kTile + (n_keep + kTile - 1) / kTile + (nring + kTile - 1) / kTile;
-    const int active = min((total + tps - 1) / tps, nsplit);
-    const size_t base = (size_t)bg * nsplit * G + hl;
-    float M = -INFINITY;
-    for (int s = 0; s < active; ++s) M = fmaxf(M, part_m[base + (size_t)s * G]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < active; ++s) {
-        const float ms = part_m[base + (size_t)s * G];
-        const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-        L = fmaf(f, part_l[base + (size_t)s * G], L);
-        O = fmaf(f, part_o[(base + (size_t)s * G) * kD + d], O);
-    }
-    const float r = O / L;
-    const size_t oi = ((size_t)b * Hq + h) * kD + d;
-    if (out_dt == HQ_F32)
-        static_cast<float*>(out)[oi] = r;
-    else if (out_dt == HQ_F16)
-        static_cast<uint16_t*>(out)[oi] = (uint16_t)f32_to_f16_bits(r);
-    else {
-        // bf16, round to nearest even
-        uint32_t x = __float_as_uint(r);
-        x += 0x7FFFu + ((x >> 16) & 1u);
-        static_cast<uint16_t*>(out)[oi] = (uint16_t)(x >> 16);
+        // group sums of exactly the values the pairs carry (rescaled), in double
+        float a = h16_to_f32<F16>(qh[t]) * sc;
+        if constexpr (F16) a = f16_to_f32(f32_to_f16_bits(a));
+        double acc = (double)a;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) acc += __shfl_xor(acc, o);
+        if ((t & 31) == 0) qsum[((size_t)bg * G + h) * 4 + (t >> 5)] = (float)(acc / sc);
     }
 }
 
 struct WsLayout {
-    size_t qp, qn, qsum, pm, pl, po, total;
+    size_t qp, qn, qsum, pm, pl, po, done, total;
 };
 inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 WsLayout ws_layout(const hq_cache& c, int32_t Hq, int32_t nsplit) {
@@ -445,7 +511,8 @@ WsLayout ws_layout(const hq_cache& c, int32_t Hq, int32_t nsplit) {
     w.pm = w.qsum + al(BG * G * 4 * 4);
     w.pl = w.pm + al(BG * nsplit * G * 4);
     w.po = w.pl + al(BG * nsplit * G * 4);
-    w.total = w.po + al(BG * nsplit * G * kD * 4);
+    w.done = w.po + al(BG * nsplit * G * kD * 4);
+    w.total = w.done + al(BG * 4);
     return w;
 }
 
@@ -476,6 +543,10 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     p.part_m = reinterpret_cast<float*>(ws + w.pm);
     p.part_l = reinterpret_cast<float*>(ws + w.pl);
     p.part_o = reinterpret_cast<float*>(ws + w.po);
+    p.done = reinterpret_cast<int32_t*>(ws + w.done);
+    p.out = out;
+    p.out_dt = (int)out_dt;
+    p.Hq = d.Hq;
     p.nsplit = d.nsplit;
     p.tps = d.tiles_per_split;
     p.G = d.G;
@@ -485,11 +556,11 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     if (f16)
         k_decode_prep<true><<<pg, 128, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
                                                const_cast<uint32_t*>(p.qp), const_cast<uint32_t*>(p.qn),
-                                               const_cast<float*>(p.qsum));
+                                               const_cast<float*>(p.qsum), p.done);
     else
         k_decode_prep<false><<<pg, 128, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
                                                 const_cast<uint32_t*>(p.qp), const_cast<uint32_t*>(p.qn),
-                                                const_cast<float*>(p.qsum));
+                                                const_cast<float*>(p.qsum), p.done);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid(d.nsplit, c.Hkv, c.B);
@@ -504,10 +575,6 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
         case 17: launch_split<8, true>(p, grid, s); break;
         default: return hipErrorInvalidValue;
     }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    k_decode_reduce<<<dim3(d.Hq, c.B), 128, 0, s>>>(c, p.part_m, p.part_l, p.part_o, d.nsplit,
-                                                     d.tiles_per_split, d.G, d.Hq, out, (int)out_dt);
     return hipGetLastError();
 }
 

@@ -24,9 +24,9 @@ constexpr int kInt8Block = 64;   // prefill INT8 block (tokens)
 __host__ __device__ inline int kcode_off(int slot, int group) { return group * 1024 + slot * 16; }
 
 // V codes (read by the channel phase, lane l = 16u + c8 owns channels
-// 8c8..8c8+7 of slots 16u..16u+15). Dword (pair P, quad Q) holds, in its low
-// 16 bits, the canonical nibbles of slot 2P, channels 4Q..4Q+3, and in its
-// high 16 bits the same channels of slot 2P+1. It lives at
+// 8c8..8c8+7 of pairs P = 8u..8u+7). Dword (pair P, quad Q), P in [0, 32),
+// holds in its low 16 bits the canonical nibbles of slot P, channels
+// 4Q..4Q+3, and in its high 16 bits the same channels of slot P+32. It lives at
 //   u = P/8, j = P%8, c8 = Q/2, e = Q%2, l = 16u + c8,
 //   byte offset = (j/2)*1024 + l*16 + ((j%2)*2 + e)*4.
 __host__ __device__ inline int vcode_off(int pair, int quad) {

@@ -62,22 +62,6 @@ __device__ inline void unpack8(const uint4& u, float* out) {
     }
 }
 
-// Pre-pair the V codes of slots (2P, 2P+1) for one 32-channel group.
-// mine/other: canonical packed words of this slot and of its partner slot.
-// Returns the 4 pair-words for quads q0..q0+3 of the group (q0 = 0 for the
-// even slot, 4 for the odd slot), low half = even slot.
-__device__ inline void vpair_words(const uint32_t (&mine)[4], const uint32_t (&other)[4],
-                                   bool odd, uint32_t (&outw)[4]) {
-    const int q0 = odd ? 4 : 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = q0 + i;
-        const uint32_t a = (mine[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
-        const uint32_t b = (other[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
-        outw[i] = odd ? (b | (a << 16)) : (a | (b << 16));
-    }
-}
-
 #pragma clang fp contract(on)
 
 }  // namespace hq

@@ -95,12 +95,10 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
             for (int i = 0; i < 4; ++i) unpack8<F16>(src[i], x + 8 * i);
             int4_quant_group(x, vp, vs, vz);
         }
-        uint32_t other[4];
+        // V pairs are slots (P, P + 32): stage the packed words in LDS
+        __shared__ uint32_t vstage[kTile][4][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) other[i] = __shfl_xor(vp[i], 4);
-        uint32_t pw[4];
-        const bool odd = t & 1;
-        vpair_words(vp, other, odd, pw);
+        for (int i = 0; i < 4; ++i) vstage[t][grp][i] = vp[i];
         const size_t tile_base = ((size_t)bg * qt + tile) * kTileBytesQ;
         uint8_t* kc = reinterpret_cast<uint8_t*>(p.c.k_codes) + tile_base;
         uint8_t* vc = reinterpret_cast<uint8_t*>(p.c.v_codes) + tile_base;
@@ -111,12 +109,21 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
             reinterpret_cast<uint32_t*>(p.c.v_meta)[slot_g * 4 + grp] = vs | (vz << 16);
             if (grp == 0) p.c.q_pos[slot_g] = pos;
         }
-        const bool pair_valid = (tile * kTile + (t & ~1)) < n_q;
-        if (pair_valid) {
-            const int P = t >> 1;
-            const int Q0 = 8 * grp + (odd ? 4 : 0);
-            *reinterpret_cast<uint2*>(vc + vcode_off(P, Q0)) = make_uint2(pw[0], pw[1]);
-            *reinterpret_cast<uint2*>(vc + vcode_off(P, Q0 + 2)) = make_uint2(pw[2], pw[3]);
+        __syncthreads();
+        {
+            const int P = tid >> 3, Q0 = (tid & 7) * 4;
+            if (tile * kTile + P < n_q) {
+                uint32_t pw[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int Q = Q0 + i, g8 = Q >> 3, q = Q & 7, w = q >> 1, h = 16 * (q & 1);
+                    const uint32_t lo = (vstage[P][g8][w] >> h) & 0xFFFFu;
+                    const uint32_t hi = (vstage[P + 32][g8][w] >> h) & 0xFFFFu;
+                    pw[i] = lo | (hi << 16);
+                }
+                *reinterpret_cast<uint2*>(vc + vcode_off(P, Q0)) = make_uint2(pw[0], pw[1]);
+                *reinterpret_cast<uint2*>(vc + vcode_off(P, Q0 + 2)) = make_uint2(pw[2], pw[3]);
+            }
         }
         return;
     }

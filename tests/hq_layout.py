@@ -31,9 +31,10 @@ def unpack_k_codes(kc: np.ndarray, BG: int, cap_q: int) -> np.ndarray:
 def unpack_v_codes(vc: np.ndarray, BG: int, cap_q: int) -> np.ndarray:
     nt = cap_q // TILE
     w = vc.view(np.uint32).reshape(BG, nt, 1024)[:, :, _VIDX]          # [BG][nt][P][Q]
-    halves = np.stack([w & 0xFFFF, w >> 16], axis=3)                  # [BG][nt][P][2][Q]
+    halves = np.stack([w & 0xFFFF, w >> 16], axis=2)                  # [BG][nt][half][P][Q]
     nib = np.stack([(halves >> (4 * n)) & 0xF for n in range(4)], axis=-1)  # [..][Q][4]
-    return nib.reshape(BG, nt, 32, 2, 128).reshape(BG, cap_q, 128).astype(np.uint8)
+    # slot = P + 32 * half
+    return nib.reshape(BG, nt, 2, 32, 128).reshape(BG, cap_q, 128).astype(np.uint8)
 
 
 def unpack_meta(meta: np.ndarray, BG: int, cap_q: int):

@@ -28,7 +28,22 @@ CASES = {
     "bf16_ratio100": (dict(B=1, Hq=4, Hkv=1, T=500, seed=16), 128, (100, 100)),
     "bf16_window_covers": (dict(B=1, Hq=4, Hkv=1, T=900, seed=17), 1024, (5, 100)),
     "bf16_all_int4": (dict(B=1, Hq=4, Hkv=1, T=777, seed=18), 0, (0, 100)),
+    # V magnitudes spanning 2^16 across the sequence: the PV weight scale grows
+    # mid-stream and many fp16 weights become tiny
+    "bf16_vscale_mix": (dict(B=2, Hq=8, Hkv=2, T=1300, seed=19), 128, (5, 100)),
+    "f16_vscale_mix": (dict(B=1, Hq=4, Hkv=1, T=1300, dtype="f16", seed=20), 128, (5, 100)),
 }
+
+
+def _vscale_mix(inp):
+    """Multiply V by powers of two that change every 200 positions (exact)."""
+    from synth import bf16_bits_from_f32, f16_bits_from_f32
+    sp = inp.spec
+    v = O.to_f64(inp.v, sp.dtype)
+    T = v.shape[2]
+    f = 2.0 ** np.array([(-8, 4, -2, 8, 0, -6, 6)[(t // 200) % 7] for t in range(T)])
+    v = (v * f[None, None, :, None]).astype(np.float32)
+    inp.v[...] = bf16_bits_from_f32(v) if sp.dtype == "bf16" else f16_bits_from_f32(v)
 
 
 def _run_quantize(inp, window, keep):
@@ -91,6 +106,8 @@ def test_quantize_and_decode(name):
     kw, window, keep = CASES[name]
     inp = small_decode_inputs(window=window, **kw)
     sp = inp.spec
+    if "vscale" in name:
+        _vscale_mix(inp)
     print(f"case {name}", flush=True)
     cache, scores, sels = _run_quantize(inp, window, keep)
     ocaches = oracle_caches(inp, sels, scores, window)
