@@ -28,14 +28,15 @@
 //    pair (one v_permlane32_swap); the channel-phase lane (8 channels x 16
 //    tokens) turns each code pair into fp16 "1024 + 16c" with one and-or and
 //    accumulates with v_dot2_f32_f16 in fp32. E is a running power-of-two
-//    bound on p*s (exact rescale when it grows) so every w is <= 1 in fp16.
+//    scale (exact rescale when it grows) keeping every w below 2^15, so the
+//    fp16 weights stay finite and normal down to p*s ~ 2^-29 of the bound.
 //    The 1024-bias is removed exactly with the sum of the same fp16 weights;
 //    sum(p*z) accumulates in fp32 in the token phase.
 //  * 16-bit tiles (kept columns, window ring) use fp32 FMAs on the 16-bit
 //    rows.
-//  * Each workgroup writes one partial (m, l, o[128]) per head; the last
-//    workgroup of a (b, g) (device-scope atomic counter, cleared by the prep
-//    kernel) merges the splits and writes the output.
+//  * Each workgroup writes one partial (m, l, o[128]) per head; a second
+//    kernel merges the splits of each (b, g) (split weights staged in LDS,
+//    coalesced partial reads).
 #include "hq_internal.h"
 
 namespace hq {
@@ -145,7 +146,6 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
     __shared__ float lds_p[kWaves][kTile * G];          // 16-bit tiles: p per token
     __shared__ float lds_m[kWaves][G], lds_l[kWaves][G];
     __shared__ float lds_o[kWaves][G][kD];
-    __shared__ int sh_last;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -160,7 +160,6 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
     const int v0 = s * p.tps;
     if (v0 >= total) return;
     const int v1 = min(v0 + p.tps, total);
-    const int active = (total + p.tps - 1) / p.tps;
 
     const int qt_cap = p.c.cap_q / kTile, kt_cap = p.c.cap_keep / kTile, wt_cap = W / kTile;
     const uint32_t* qp = p.qp + (size_t)bg * 4 * G * 16;
@@ -281,9 +280,10 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         }
 
         if (int4_tile) {
-            // running power-of-two bound 2^E >= 2^8 * max(s) so that p*s*2^-E <= 1
+            // running power-of-two scale 2^E with p*s*2^-E < 2^15 (p <= 2^8 by the lazy
+            // rescale, s < 2^(e_s+1)): fp16 weights stay finite and mostly normal
             const float smax = wave_max_fast(fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])));
-            const int e_need = smax > 0.f ? (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127 + 9 : -1000;
+            const int e_need = smax > 0.f ? (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127 - 6 : -1000;
             if (e_need > E) {
                 const float r = E <= -1000 ? 0.f : __builtin_ldexpf(1.0f, E - e_need);
 #pragma unroll
@@ -435,27 +435,6 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
             p.part_l[pbase + h] = L;
         }
     }
-    // ----------------------------- the last split of (b, g) merges all splits
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) sh_last = atomicAdd(p.done + bg, 1) == active - 1;
-    __syncthreads();
-    if (!sh_last) return;
-    __threadfence();
-    const size_t base0 = (size_t)bg * p.nsplit * G;
-    for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
-        const int h = idx / kD, d = idx % kD;
-        float M = -INFINITY;
-        for (int sp = 0; sp < active; ++sp) M = fmaxf(M, p.part_m[base0 + sp * G + h]);
-        float L = 0.f, O = 0.f;
-        for (int sp = 0; sp < active; ++sp) {
-            const float ms = p.part_m[base0 + sp * G + h];
-            const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-            L = fmaf(f, p.part_l[base0 + sp * G + h], L);
-            O = fmaf(f, p.part_o[(base0 + sp * G + h) * kD + d], O);
-        }
-        store_out(p.out, p.out_dt, ((size_t)b * p.Hq + g * G + h) * kD + d, O / L);
-    }
 }
 
 // Rearranges the query for the split kernel: INT4-path pairs (prescaled by
@@ -494,6 +473,51 @@ __global__ __launch_bounds__(128) void k_decode_prep(const uint16_t* q, int Hq, 
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) acc += __shfl_xor(acc, o);
         if ((t & 31) == 0) qsum[((size_t)bg * G + h) * 4 + (t >> 5)] = (float)(acc / sc);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_decode_reduce(const hq_cache c, const float* part_m, const float* part_l,
+                                                       const float* part_o, int nsplit, int tps, int G, int Hq,
+                                                       void* out, int out_dt) {
+    extern __shared__ float sh[];  // [nsplit][G] weights, then [G] 1/L
+    const int g = blockIdx.x, b = blockIdx.y;
+    const int bg = b * c.Hkv + g;
+    const int4 cnt = *reinterpret_cast<const int4*>(c.counts + 4 * bg);
+    const int T = cnt.x, n_q = cnt.y, n_keep = cnt.z;
+    const int nring = T < c.window ? T : c.window;
+    const int total = (n_q + kTile - 1) / kTile + (n_keep + kTile - 1) / kTile + (nring + kTile - 1) / kTile;
+    const int active = min((total + tps - 1) / tps, nsplit);
+    const size_t base = (size_t)bg * nsplit * G;
+    float* wsp = sh;
+    float* invl = sh + nsplit * G;
+    // per head: M = max over splits, weights 2^(m - M), 1/L
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
+        float M = -INFINITY;
+        for (int sp = 0; sp < active; ++sp) M = fmaxf(M, part_m[base + sp * G + h]);
+        float L = 0.f;
+        for (int sp = 0; sp < active; ++sp) {
+            const float ms = part_m[base + sp * G + h];
+            const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+            wsp[sp * G + h] = f;
+            L = fmaf(f, part_l[base + sp * G + h], L);
+        }
+        invl[h] = 1.0f / L;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
+        const int h = idx / kD;
+        const float* po = part_o + base * kD + idx;
+        float O0 = 0.f, O1 = 0.f, O2 = 0.f, O3 = 0.f;
+        int sp = 0;
+        for (; sp + 4 <= active; sp += 4) {
+            O0 = fmaf(wsp[sp * G + h], po[(size_t)sp * G * kD], O0);
+            O1 = fmaf(wsp[(sp + 1) * G + h], po[(size_t)(sp + 1) * G * kD], O1);
+            O2 = fmaf(wsp[(sp + 2) * G + h], po[(size_t)(sp + 2) * G * kD], O2);
+            O3 = fmaf(wsp[(sp + 3) * G + h], po[(size_t)(sp + 3) * G * kD], O3);
+        }
+        for (; sp < active; ++sp) O0 = fmaf(wsp[sp * G + h], po[(size_t)sp * G * kD], O0);
+        store_out(out, out_dt, ((size_t)b * Hq + g * G) * kD + idx, ((O0 + O1) + (O2 + O3)) * invl[h]);
     }
 }
 
@@ -575,6 +599,11 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
         case 17: launch_split<8, true>(p, grid, s); break;
         default: return hipErrorInvalidValue;
     }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t shb = ((size_t)d.nsplit * d.G + d.G) * sizeof(float);
+    k_decode_reduce<<<dim3(c.Hkv, c.B), 256, shb, s>>>(c, p.part_m, p.part_l, p.part_o, d.nsplit,
+                                                        d.tiles_per_split, d.G, d.Hq, out, (int)out_dt);
     return hipGetLastError();
 }
 

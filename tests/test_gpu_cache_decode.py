@@ -116,7 +116,12 @@ def test_quantize_and_decode(name):
     out = hq.decode_attn(cache, q).cpu().numpy()
     torch.cuda.synchronize()
     ref = O.decode_batch(O.to_f64(inp.q, sp.dtype), ocaches, 1 / math.sqrt(sp.D))
-    assert_attn_close(out, ref, f"decode {name}")
+    if "vscale" in name:
+        # outputs reach |o| ~ 1e2 here: the absolute bar applies to o / max(1, max|o|)
+        sc = max(1.0, float(np.abs(ref).max()))
+        assert_attn_close(out / sc, ref / sc, f"decode {name} (scaled by {sc:.1f})")
+    else:
+        assert_attn_close(out, ref, f"decode {name}")
     if keep == (100, 100) or window >= int(inp.seq_lens.max()):
         # special cases: equal to exact softmax attention over the 16-bit K/V
         G = sp.Hq // sp.Hkv
