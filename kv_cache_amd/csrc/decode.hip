@@ -53,9 +53,6 @@ struct DecodeParams {
     float* part_m;         // [B][Hkv][nsplit][G]
     float* part_l;         // [B][Hkv][nsplit][G]
     float* part_o;         // [B][Hkv][nsplit][G][128]
-    int32_t* done;         // [B][Hkv] finished-split counters
-    void* out;
-    int32_t out_dt, Hq;
     int32_t nsplit, tps, G;
     float scale2;          // sm_scale * log2(e)
 };
@@ -438,15 +435,13 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
 }
 
 // Rearranges the query for the split kernel: INT4-path pairs (prescaled by
-// 1/8 for bf16, 1/16 for fp16, exact), natural pairs and group sums; clears
-// the split counters of this (b, g).
+// 1/8 for bf16, 1/16 for fp16, exact), natural pairs and group sums.
 template <bool F16>
 __global__ __launch_bounds__(128) void k_decode_prep(const uint16_t* q, int Hq, int G, uint32_t* qp,
-                                                     uint32_t* qn, float* qsum, int32_t* done) {
+                                                     uint32_t* qn, float* qsum) {
     const int g = blockIdx.x, b = blockIdx.y, Hkv = gridDim.x;
     const int bg = b * Hkv + g;
     const int t = threadIdx.x;
-    if (t == 0) done[bg] = 0;
     const float sc = F16 ? 0.0625f : 0.125f;
     for (int h = 0; h < G; ++h) {
         const uint16_t* qh = q + ((size_t)b * Hq + g * G + h) * kD;
@@ -522,7 +517,7 @@ __global__ __launch_bounds__(256) void k_decode_reduce(const hq_cache c, const f
 }
 
 struct WsLayout {
-    size_t qp, qn, qsum, pm, pl, po, done, total;
+    size_t qp, qn, qsum, pm, pl, po, total;
 };
 inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 WsLayout ws_layout(const hq_cache& c, int32_t Hq, int32_t nsplit) {
@@ -535,8 +530,7 @@ WsLayout ws_layout(const hq_cache& c, int32_t Hq, int32_t nsplit) {
     w.pm = w.qsum + al(BG * G * 4 * 4);
     w.pl = w.pm + al(BG * nsplit * G * 4);
     w.po = w.pl + al(BG * nsplit * G * 4);
-    w.done = w.po + al(BG * nsplit * G * kD * 4);
-    w.total = w.done + al(BG * 4);
+    w.total = w.po + al(BG * nsplit * G * kD * 4);
     return w;
 }
 
@@ -567,9 +561,6 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     p.part_m = reinterpret_cast<float*>(ws + w.pm);
     p.part_l = reinterpret_cast<float*>(ws + w.pl);
     p.part_o = reinterpret_cast<float*>(ws + w.po);
-    p.done = reinterpret_cast<int32_t*>(ws + w.done);
-    p.out = out;
-    p.out_dt = (int)out_dt;
     p.Hq = d.Hq;
     p.nsplit = d.nsplit;
     p.tps = d.tiles_per_split;
@@ -580,11 +571,11 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     if (f16)
         k_decode_prep<true><<<pg, 128, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
                                                const_cast<uint32_t*>(p.qp), const_cast<uint32_t*>(p.qn),
-                                               const_cast<float*>(p.qsum), p.done);
+                                               const_cast<float*>(p.qsum));
     else
         k_decode_prep<false><<<pg, 128, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
                                                 const_cast<uint32_t*>(p.qp), const_cast<uint32_t*>(p.qn),
-                                                const_cast<float*>(p.qsum), p.done);
+                                                const_cast<float*>(p.qsum));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid(d.nsplit, c.Hkv, c.B);
