@@ -561,7 +561,6 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     p.part_m = reinterpret_cast<float*>(ws + w.pm);
     p.part_l = reinterpret_cast<float*>(ws + w.pl);
     p.part_o = reinterpret_cast<float*>(ws + w.po);
-    p.Hq = d.Hq;
     p.nsplit = d.nsplit;
     p.tps = d.tiles_per_split;
     p.G = d.G;
