@@ -26,11 +26,11 @@
 //  * PV on INT4 tiles: the V codes are stored pre-paired, slot t with slot
 //    t + 32, so the weights w = p * s * 2^-E of the two tokens form one fp16
 //    pair (one v_permlane32_swap); the channel-phase lane (8 channels x 16
-//    tokens) turns each code pair into fp16 "1024 + 16c" with one and-or and
-//    accumulates with v_dot2_f32_f16 in fp32. E is a running power-of-two
+//    tokens) turns each code pair into fp16 "1024 + c" / "64 + c" magic
+//    values with one v_bfi_b32 and accumulates with v_dot2_f32_f16 in fp32. E is a running power-of-two
 //    scale (exact rescale when it grows) keeping every w below 2^15, so the
 //    fp16 weights stay finite and normal down to p*s ~ 2^-29 of the bound.
-//    The 1024-bias is removed exactly with the sum of the same fp16 weights;
+//    The magic bias is removed exactly with the sum of the same fp16 weights;
 //    sum(p*z) accumulates in fp32 in the token phase.
 //  * 16-bit tiles (kept columns, window ring) use fp32 FMAs on the 16-bit
 //    rows.
@@ -71,24 +71,42 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
 }
 __device__ inline float dot2h(uint32_t a, uint32_t b, float c) { return dot2<true>(a, b, c); }
 
-// Four magic-biased code pairs from one dword of 8 nibbles (channels 8i+n).
-// Pair n holds channels (n, n+4). bf16: value 128 + 8c (code in bits 3..6);
-// fp16: value 1024 + 16c (code in bits 4..7).
+// (a & mask) | c for c & mask == 0, in one v_bfi_b32 with register constants
+// (a VOP3 op cannot take two literals, so the compiler would otherwise emit and + or).
+__device__ inline uint32_t bfi(uint32_t mask, uint32_t a, uint32_t c) {
+    uint32_t r;
+    asm volatile("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(c));
+    return r;
+}
+
+// Four magic-biased code pairs from one dword of 8 nibbles (channels 8i+n) for
+// the QK dot products. Pair n holds channels (n, n+4). bf16: value 128 + 8c
+// (code in bits 3..6); fp16: value 1024 + 16c (code in bits 4..7).
 template <bool F16>
-__device__ inline void extract_pairs(uint32_t w, uint32_t* pr) {
+__device__ inline void extract_pairs(uint32_t w, uint32_t* pr, uint32_t M, uint32_t C) {
     if constexpr (F16) {
-        constexpr uint32_t M = 0x00F000F0u, C = 0x64006400u;
-        pr[0] = ((w << 4) & M) | C;
-        pr[1] = (w & M) | C;
-        pr[2] = ((w >> 4) & M) | C;
-        pr[3] = ((w >> 8) & M) | C;
+        pr[0] = bfi(M, w << 4, C);
+        pr[1] = bfi(M, w, C);
+        pr[2] = bfi(M, w >> 4, C);
+        pr[3] = bfi(M, w >> 8, C);
     } else {
-        constexpr uint32_t M = 0x00780078u, C = 0x43004300u;
-        pr[0] = ((w << 3) & M) | C;
-        pr[1] = ((w >> 1) & M) | C;
-        pr[2] = ((w >> 5) & M) | C;
-        pr[3] = ((w >> 9) & M) | C;
+        pr[0] = bfi(M, w << 3, C);
+        pr[1] = bfi(M, w >> 1, C);
+        pr[2] = bfi(M, w >> 5, C);
+        pr[3] = bfi(M, w >> 9, C);
     }
+}
+// The V-code word of slots (P, P+32), channels 4Q+n: fp16 magic pairs with
+// one bfi each (and one shift for n >= 2). Even channels (code in bits 0..3)
+// read 1024 + c with magic 0x6400, odd channels (bits 4..7) read 64 + c with
+// magic 0x5400: every channel carries the code with factor 1.
+__device__ inline void extract_vpairs(uint32_t d, uint32_t* cp, uint32_t M_lo, uint32_t M_hi, uint32_t C_lo,
+                                      uint32_t C_hi) {
+    const uint32_t d8 = d >> 8;
+    cp[0] = bfi(M_lo, d, C_lo);
+    cp[1] = bfi(M_hi, d, C_hi);
+    cp[2] = bfi(M_lo, d8, C_lo);
+    cp[3] = bfi(M_hi, d8, C_hi);
 }
 template <bool F16>
 constexpr float kBias = F16 ? 64.0f : 16.0f;
@@ -112,10 +130,23 @@ __device__ inline float wave_max_fast(float v) {
     auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
-// Value held by lane (l + 32) % 64.
-__device__ inline float other_half(float v) {
+// Lanes 0..31 receive the value of lane l + 32 (lanes 32..63 get junk).
+__device__ inline float upper_half(float v) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
+    return __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ inline float dpp_add(float v) { return v + dppmov<CTRL>(v); }
+// Sum over the 64 lanes, every lane gets it (no LDS traffic).
+__device__ inline float wave_sum_fast(float v) {
+    v = dpp_add<0xB1>(v);
+    v = dpp_add<0x4E>(v);
+    v = dpp_add<0x141>(v);
+    v = dpp_add<0x140>(v);
+    auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 __device__ inline void lds_fence() {
@@ -182,6 +213,11 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
     uint32_t* pw_w = lds_pw[wave];
     float* p_w = lds_p[wave];
     const uint32_t ONES = 0x3C003C00u;  // fp16 (1, 1)
+    // extraction constants kept in VGPRs (opaque to constant folding)
+    uint32_t kM = F16 ? 0x00F000F0u : 0x00780078u, kC = F16 ? 0x64006400u : 0x43004300u;
+    uint32_t vMlo = 0x000F000Fu, vMhi = 0x00F000F0u, vClo = 0x64006400u, vChi = 0x54005400u;
+    asm volatile("" : "+v"(kM), "+v"(kC), "+v"(vMlo), "+v"(vMhi), "+v"(vClo), "+v"(vChi));
+    float s_thr = 0.f;  // 2^(E+7): a V scale at or above it needs a larger E
 
     for (int v = v0 + wave; v < v1; v += kWaves) {
         float lg[G];
@@ -217,7 +253,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
                 const float zz = zk - kBias<F16> * sk;
                 uint32_t pr[16];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) extract_pairs<F16>(u4w(kw[grp], i), pr + 4 * i);
+                for (int i = 0; i < 4; ++i) extract_pairs<F16>(u4w(kw[grp], i), pr + 4 * i, kM, kC);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     const uint32_t* qh = qp + (grp * G + h) * 16;
@@ -259,8 +295,9 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         float pr_h[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float tmax = wave_max_fast(lg[h]);
-            if (tmax > m[h] + kLazy) {
+            // lazy max: the full reduction only runs when some logit exceeds m + 2^8
+            if (__any(lg[h] > m[h] + kLazy)) {
+                const float tmax = wave_max_fast(lg[h]);
                 const float alpha = __builtin_amdgcn_exp2f(m[h] - tmax);
                 m[h] = tmax;
                 l[h] *= alpha;
@@ -279,10 +316,11 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         if (int4_tile) {
             // running power-of-two scale 2^E with p*s*2^-E < 2^15 (p <= 2^8 by the lazy
             // rescale, s < 2^(e_s+1)): fp16 weights stay finite and mostly normal
-            const float smax = wave_max_fast(fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3])));
-            const int e_need = smax > 0.f ? (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127 - 6 : -1000;
-            if (e_need > E) {
-                const float r = E <= -1000 ? 0.f : __builtin_ldexpf(1.0f, E - e_need);
+            const float s4 = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3]));
+            if (__any(s4 >= s_thr && s4 > 0.f)) {
+                const float smax = wave_max_fast(s4);
+                const int e_need = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127 - 6;
+                const float r = E <= -1000 ? 0.f : (e_need > E ? __builtin_ldexpf(1.0f, E - e_need) : 1.0f);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -290,7 +328,8 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) wsum[h][i] *= r;
                 }
-                E = e_need;
+                E = e_need > E ? e_need : E;
+                s_thr = __builtin_ldexpf(1.0f, E + 7);
             }
             const float f = E <= -1000 ? 1.0f : __builtin_ldexpf(1.0f, -E);
             // fp16 weight pairs (slot lane, slot lane + 32), built by lanes 0..31
@@ -302,7 +341,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
                 for (int h = 0; h < G; ++h) {
                     zacc[h][grp] = fmaf(pr_h[h], vz[grp], zacc[h][grp]);
                     const float w = pr_h[h] * sf;
-                    const float w2 = other_half(w);
+                    const float w2 = upper_half(w);
                     typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
                     h2_t pk = {(_Float16)w, (_Float16)w2};
                     words[h] = __builtin_bit_cast(uint32_t, pk);
@@ -333,7 +372,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
                 for (int e = 0; e < 2; ++e) {
                     const uint32_t d = u4w(vw[j >> 1], (j & 1) * 2 + e);
                     uint32_t cp[4];
-                    extract_pairs<true>(d, cp);
+                    extract_vpairs(d, cp, vMlo, vMhi, vClo, vChi);
 #pragma unroll
                     for (int n = 0; n < 4; ++n)
 #pragma unroll
@@ -343,7 +382,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
             lds_fence();
         } else {
             if (E <= -1000) E = 0;  // no INT4 tile yet: fix the accumulator unit
-            const float k16 = __builtin_ldexpf(16.0f, -E);
+            const float k16 = __builtin_ldexpf(1.0f, -E);
 #pragma unroll
             for (int h = 0; h < G; ++h) p_w[lane * G + h] = pr_h[h] * k16;
             lds_fence();
@@ -377,15 +416,17 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
     }
 
     // ----------------------------- wave epilogue
-    // wsum: lanes 0..31 hold the packed pairs; reduce over them only
+    // acc units: o = 2^E * (acc - bias * wsum) + sum(p z), bias 1024 on even
+    // and 64 on odd channels (the fp16 magic values); 16-bit tiles added
+    // p*v*2^-E directly.
+    const float unit = E <= -1000 ? 0.f : __builtin_ldexpf(1.0f, E);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        l[h] = wave_sum(l[h]);
+        l[h] = wave_sum_fast(l[h]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            zacc[h][i] = wave_sum(zacc[h][i]);
-            float ws = lane < 32 ? wsum[h][i] : 0.f;
-            wsum[h][i] = wave_sum(ws);
+            zacc[h][i] = wave_sum_fast(zacc[h][i]);
+            wsum[h][i] = unit * wave_sum_fast(lane < 32 ? wsum[h][i] : 0.f);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -394,13 +435,13 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         }
     }
     if (lane < 16) {
-        const float unit = E <= -1000 ? 0.f : __builtin_ldexpf(1.0f, E - 4);  // 2^E / 16
+        const int gq = lane >> 2;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float bias = 1024.0f * wsum[h][lane >> 2];
+            const float z_even = fmaf(-1024.0f, wsum[h][gq], zacc[h][gq]);
+            const float z_odd = fmaf(-64.0f, wsum[h][gq], zacc[h][gq]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                lds_o[wave][h][8 * lane + i] = fmaf(unit, acc[h][i] - bias, zacc[h][lane >> 2]);
+            for (int i = 0; i < 8; ++i) lds_o[wave][h][8 * lane + i] = fmaf(unit, acc[h][i], (i & 1) ? z_odd : z_even);
         }
     }
     if (lane == 0) {
@@ -474,7 +515,7 @@ __global__ __launch_bounds__(128) void k_decode_prep(const uint16_t* q, int Hq, 
 __global__ __launch_bounds__(256) void k_decode_reduce(const hq_cache c, const float* part_m, const float* part_l,
                                                        const float* part_o, int nsplit, int tps, int G, int Hq,
                                                        void* out, int out_dt) {
-    extern __shared__ float sh[];  // [nsplit][G] weights, then [G] 1/L
+    extern __shared__ float sh[];  // [nsplit][G] m -> weights, [nsplit][G] l, [G] 1/L
     const int g = blockIdx.x, b = blockIdx.y;
     const int bg = b * c.Hkv + g;
     const int4 cnt = *reinterpret_cast<const int4*>(c.counts + 4 * bg);
@@ -484,18 +525,24 @@ __global__ __launch_bounds__(256) void k_decode_reduce(const hq_cache c, const f
     const int active = min((total + tps - 1) / tps, nsplit);
     const size_t base = (size_t)bg * nsplit * G;
     float* wsp = sh;
-    float* invl = sh + nsplit * G;
+    float* lsp = sh + nsplit * G;
+    float* invl = lsp + nsplit * G;
+    for (int i = threadIdx.x; i < active * G; i += 256) {
+        wsp[i] = part_m[base + i];
+        lsp[i] = part_l[base + i];
+    }
+    __syncthreads();
     // per head: M = max over splits, weights 2^(m - M), 1/L
     if (threadIdx.x < G) {
         const int h = threadIdx.x;
         float M = -INFINITY;
-        for (int sp = 0; sp < active; ++sp) M = fmaxf(M, part_m[base + sp * G + h]);
+        for (int sp = 0; sp < active; ++sp) M = fmaxf(M, wsp[sp * G + h]);
         float L = 0.f;
         for (int sp = 0; sp < active; ++sp) {
-            const float ms = part_m[base + sp * G + h];
+            const float ms = wsp[sp * G + h];
             const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
             wsp[sp * G + h] = f;
-            L = fmaf(f, part_l[base + sp * G + h], L);
+            L = fmaf(f, lsp[sp * G + h], L);
         }
         invl[h] = 1.0f / L;
     }
@@ -591,7 +638,7 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t shb = ((size_t)d.nsplit * d.G + d.G) * sizeof(float);
+    const size_t shb = ((size_t)2 * d.nsplit * d.G + d.G) * sizeof(float);
     k_decode_reduce<<<dim3(c.Hkv, c.B), 256, shb, s>>>(c, p.part_m, p.part_l, p.part_o, d.nsplit,
                                                         d.tiles_per_split, d.G, d.Hq, out, (int)out_dt);
     return hipGetLastError();
