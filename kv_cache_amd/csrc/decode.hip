@@ -75,7 +75,7 @@ __device__ inline float dot2h(uint32_t a, uint32_t b, float c) { return dot2<tru
 // (a VOP3 op cannot take two literals, so the compiler would otherwise emit and + or).
 __device__ inline uint32_t bfi(uint32_t mask, uint32_t a, uint32_t c) {
     uint32_t r;
-    asm volatile("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(c));
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(c));
     return r;
 }
 
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
     // extraction constants kept in VGPRs (opaque to constant folding)
     uint32_t kM = F16 ? 0x00F000F0u : 0x00780078u, kC = F16 ? 0x64006400u : 0x43004300u;
     uint32_t vMlo = 0x000F000Fu, vMhi = 0x00F000F0u, vClo = 0x64006400u, vChi = 0x54005400u;
-    asm volatile("" : "+v"(kM), "+v"(kC), "+v"(vMlo), "+v"(vMhi), "+v"(vClo), "+v"(vChi));
+    asm("" : "+v"(kM), "+v"(kC), "+v"(vMlo), "+v"(vMhi), "+v"(vClo), "+v"(vChi));
     float s_thr = 0.f;  // 2^(E+7): a V scale at or above it needs a larger E
 
     for (int v = v0 + wave; v < v1; v += kWaves) {
