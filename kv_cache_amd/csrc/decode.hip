@@ -224,6 +224,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         const bool int4_tile = v < nqt;
         int count, tile;
         float vs[4], vz[4];
+        uint4 vw[4];
         if (int4_tile) {
             // ----------------------------- token phase, INT4 tile
             tile = v;
@@ -238,6 +239,12 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
                 kw[grp] = *reinterpret_cast<const uint4*>(kc + kcode_off(lane, grp));
             uint4 km = reinterpret_cast<const uint4*>(p.c.k_meta)[slot_g];
             uint4 vm = reinterpret_cast<const uint4*>(p.c.v_meta)[slot_g];
+            {   // V codes requested before QK so their latency overlaps the QK work
+                const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.c.v_codes) +
+                                    ((size_t)bg * qt_cap + tile) * kTileBytesQ;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) vw[kk] = *reinterpret_cast<const uint4*>(vc + kk * 1024 + lane * 16);
+            }
             if (!valid) {
                 km = make_uint4(0, 0, 0, 0);
                 vm = km;
@@ -356,11 +363,6 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
             }
             lds_fence();
             // ----------------------------- channel phase, INT4 V
-            const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.c.v_codes) +
-                                ((size_t)bg * qt_cap + tile) * kTileBytesQ;
-            uint4 vw[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) vw[kk] = *reinterpret_cast<const uint4*>(vc + kk * 1024 + lane * 16);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int P = 8 * u + j;
@@ -478,89 +480,90 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
 // Rearranges the query for the split kernel: INT4-path pairs (prescaled by
 // 1/8 for bf16, 1/16 for fp16, exact), natural pairs and group sums.
 template <bool F16>
-__global__ __launch_bounds__(128) void k_decode_prep(const uint16_t* q, int Hq, int G, uint32_t* qp,
-                                                     uint32_t* qn, float* qsum) {
+__global__ __launch_bounds__(1024) void k_decode_prep(const uint16_t* q, int Hq, int G, uint32_t* qp,
+                                                      uint32_t* qn, float* qsum) {
     const int g = blockIdx.x, b = blockIdx.y, Hkv = gridDim.x;
     const int bg = b * Hkv + g;
-    const int t = threadIdx.x;
+    const int h = threadIdx.x >> 7, t = threadIdx.x & 127;   // one thread per (head, channel)
     const float sc = F16 ? 0.0625f : 0.125f;
-    for (int h = 0; h < G; ++h) {
-        const uint16_t* qh = q + ((size_t)b * Hq + g * G + h) * kD;
-        if (t < 64) {
-            qn[((size_t)bg * G + h) * 64 + t] = (uint32_t)qh[2 * t] | ((uint32_t)qh[2 * t + 1] << 16);
-            // INT4 arrangement: entry (grp, 4i + n) = (q[32grp+8i+n], q[32grp+8i+n+4]) * 2^-3 / 2^-4
-            const int grp = t >> 4, e = t & 15, i = e >> 2, n = e & 3;
-            const int d0 = 32 * grp + 8 * i + n;
-            const float a = h16_to_f32<F16>(qh[d0]) * sc, c = h16_to_f32<F16>(qh[d0 + 4]) * sc;
-            uint32_t wa, wc;
-            if constexpr (F16) {
-                wa = f32_to_f16_bits(a);
-                wc = f32_to_f16_bits(c);
-            } else {
-                wa = __float_as_uint(a) >> 16;  // exact: power-of-two scaling of a bf16 value
-                wc = __float_as_uint(c) >> 16;
-            }
-            qp[(((size_t)bg * 4 + grp) * G + h) * 16 + e] = wa | (wc << 16);
+    const uint16_t* qh = q + ((size_t)b * Hq + g * G + h) * kD;
+    if (t < 64) {
+        qn[((size_t)bg * G + h) * 64 + t] = (uint32_t)qh[2 * t] | ((uint32_t)qh[2 * t + 1] << 16);
+        // INT4 arrangement: entry (grp, 4i + n) = (q[32grp+8i+n], q[32grp+8i+n+4]) * 2^-3 / 2^-4
+        const int grp = t >> 4, e = t & 15, i = e >> 2, n = e & 3;
+        const int d0 = 32 * grp + 8 * i + n;
+        const float a = h16_to_f32<F16>(qh[d0]) * sc, c = h16_to_f32<F16>(qh[d0 + 4]) * sc;
+        uint32_t wa, wc;
+        if constexpr (F16) {
+            wa = f32_to_f16_bits(a);
+            wc = f32_to_f16_bits(c);
+        } else {
+            wa = __float_as_uint(a) >> 16;  // exact: power-of-two scaling of a bf16 value
+            wc = __float_as_uint(c) >> 16;
         }
-        // group sums of exactly the values the pairs carry (rescaled), in double
-        float a = h16_to_f32<F16>(qh[t]) * sc;
-        if constexpr (F16) a = f16_to_f32(f32_to_f16_bits(a));
-        double acc = (double)a;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) acc += __shfl_xor(acc, o);
-        if ((t & 31) == 0) qsum[((size_t)bg * G + h) * 4 + (t >> 5)] = (float)(acc / sc);
+        qp[(((size_t)bg * 4 + grp) * G + h) * 16 + e] = wa | (wc << 16);
     }
+    // group sums of exactly the values the pairs carry (rescaled), in double
+    float a = h16_to_f32<F16>(qh[t]) * sc;
+    if constexpr (F16) a = f16_to_f32(f32_to_f16_bits(a));
+    double acc = (double)a;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) acc += __shfl_xor(acc, o);
+    if ((t & 31) == 0) qsum[((size_t)bg * G + h) * 4 + (t >> 5)] = (float)(acc / sc);
 }
 
-__global__ __launch_bounds__(256) void k_decode_reduce(const hq_cache c, const float* part_m, const float* part_l,
+__global__ __launch_bounds__(128) void k_decode_reduce(const hq_cache c, const float* part_m, const float* part_l,
                                                        const float* part_o, int nsplit, int tps, int G, int Hq,
                                                        void* out, int out_dt) {
-    extern __shared__ float sh[];  // [nsplit][G] m -> weights, [nsplit][G] l, [G] 1/L
-    const int g = blockIdx.x, b = blockIdx.y;
+    extern __shared__ float sh[];  // [nsplit] weights, then 1/L
+    const int gh = blockIdx.x, b = blockIdx.y;
+    const int g = gh / G, h = gh % G, d = threadIdx.x;
     const int bg = b * c.Hkv + g;
     const int4 cnt = *reinterpret_cast<const int4*>(c.counts + 4 * bg);
     const int T = cnt.x, n_q = cnt.y, n_keep = cnt.z;
     const int nring = T < c.window ? T : c.window;
     const int total = (n_q + kTile - 1) / kTile + (n_keep + kTile - 1) / kTile + (nring + kTile - 1) / kTile;
     const int active = min((total + tps - 1) / tps, nsplit);
-    const size_t base = (size_t)bg * nsplit * G;
+    const size_t base = (size_t)bg * nsplit * G + h;
     float* wsp = sh;
-    float* lsp = sh + nsplit * G;
-    float* invl = lsp + nsplit * G;
-    for (int i = threadIdx.x; i < active * G; i += 256) {
-        wsp[i] = part_m[base + i];
-        lsp[i] = part_l[base + i];
+    __shared__ float red[2];
+    // split weights 2^(m_s - M) and 1/L, one split per thread
+    float ms = -INFINITY, ls = 0.f;
+    if (d < active) {
+        ms = part_m[base + (size_t)d * G];
+        ls = part_l[base + (size_t)d * G];
     }
+    for (int i = d + 128; i < active; i += 128) {  // more than 128 splits: fold
+        const float m2 = part_m[base + (size_t)i * G];
+        if (m2 > ms) ms = m2;
+    }
+    float M = wave_max(ms);
+    if ((d & 63) == 0) red[d >> 6] = M;
     __syncthreads();
-    // per head: M = max over splits, weights 2^(m - M), 1/L
-    if (threadIdx.x < G) {
-        const int h = threadIdx.x;
-        float M = -INFINITY;
-        for (int sp = 0; sp < active; ++sp) M = fmaxf(M, wsp[sp * G + h]);
-        float L = 0.f;
-        for (int sp = 0; sp < active; ++sp) {
-            const float ms = wsp[sp * G + h];
-            const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-            wsp[sp * G + h] = f;
-            L = fmaf(f, lsp[sp * G + h], L);
-        }
-        invl[h] = 1.0f / L;
-    }
+    M = fmaxf(red[0], red[1]);
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
-        const int h = idx / kD;
-        const float* po = part_o + base * kD + idx;
-        float O0 = 0.f, O1 = 0.f, O2 = 0.f, O3 = 0.f;
-        int sp = 0;
-        for (; sp + 4 <= active; sp += 4) {
-            O0 = fmaf(wsp[sp * G + h], po[(size_t)sp * G * kD], O0);
-            O1 = fmaf(wsp[(sp + 1) * G + h], po[(size_t)(sp + 1) * G * kD], O1);
-            O2 = fmaf(wsp[(sp + 2) * G + h], po[(size_t)(sp + 2) * G * kD], O2);
-            O3 = fmaf(wsp[(sp + 3) * G + h], po[(size_t)(sp + 3) * G * kD], O3);
-        }
-        for (; sp < active; ++sp) O0 = fmaf(wsp[sp * G + h], po[(size_t)sp * G * kD], O0);
-        store_out(out, out_dt, ((size_t)b * Hq + g * G) * kD + idx, ((O0 + O1) + (O2 + O3)) * invl[h]);
+    float L = 0.f;
+    for (int i = d; i < active; i += 128) {
+        const float mi = part_m[base + (size_t)i * G];
+        const float f = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M);
+        wsp[i] = f;
+        L = fmaf(f, part_l[base + (size_t)i * G], L);
     }
+    (void)ls;
+    L = wave_sum(L);
+    if ((d & 63) == 0) red[d >> 6] = L;
+    __syncthreads();
+    const float invL = 1.0f / (red[0] + red[1]);
+    const float* po = part_o + base * kD + d;
+    float O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int sp = 0;
+    for (; sp + 8 <= active; sp += 8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) O[j] = fmaf(wsp[sp + j], po[(size_t)(sp + j) * G * kD], O[j]);
+    }
+    for (; sp < active; ++sp) O[0] = fmaf(wsp[sp], po[(size_t)sp * G * kD], O[0]);
+    const float r = (((O[0] + O[1]) + (O[2] + O[3])) + ((O[4] + O[5]) + (O[6] + O[7]))) * invL;
+    store_out(out, out_dt, ((size_t)b * Hq + g * G + h) * kD + d, r);
 }
 
 struct WsLayout {
@@ -615,11 +618,11 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     const bool f16 = c.dt == HQ_F16;
     dim3 pg(c.Hkv, c.B);
     if (f16)
-        k_decode_prep<true><<<pg, 128, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
+        k_decode_prep<true><<<pg, 128 * d.G, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
                                                const_cast<uint32_t*>(p.qp), const_cast<uint32_t*>(p.qn),
                                                const_cast<float*>(p.qsum));
     else
-        k_decode_prep<false><<<pg, 128, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
+        k_decode_prep<false><<<pg, 128 * d.G, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
                                                 const_cast<uint32_t*>(p.qp), const_cast<uint32_t*>(p.qn),
                                                 const_cast<float*>(p.qsum));
     hipError_t e = hipGetLastError();
@@ -638,9 +641,9 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t shb = ((size_t)2 * d.nsplit * d.G + d.G) * sizeof(float);
-    k_decode_reduce<<<dim3(c.Hkv, c.B), 256, shb, s>>>(c, p.part_m, p.part_l, p.part_o, d.nsplit,
-                                                        d.tiles_per_split, d.G, d.Hq, out, (int)out_dt);
+    const size_t shb = (size_t)d.nsplit * sizeof(float);
+    k_decode_reduce<<<dim3(c.Hkv * d.G, c.B), 128, shb, s>>>(c, p.part_m, p.part_l, p.part_o, d.nsplit,
+                                                              d.tiles_per_split, d.G, d.Hq, out, (int)out_dt);
     return hipGetLastError();
 }
 
