@@ -231,8 +231,24 @@ size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq);
  * with symmetric INT8 per 64-token block over all channels (s = max|x|/127
  * in fp32, code = rint(x/s)); out_i = sum_j softmax(score)_j v_j. P and V
  * enter the PV product as fp16.
- *   q [B][Hq][T][D], k, v [B][Hkv][T][D] dt; sel_idx/sel_count as returned
- *   by hq_probe_select with Tmax = T; out [B][Hq][T][D] out_dt.            */
+ *   q [B][Hq][T][D], k, v [B][Hkv][T][D] dt (values within fp16 range for
+ *   V); sel_idx [B][Hkv][hq_sel_stride(T)] int32, the first sel_count[b][g]
+ *   entries ascending, distinct and in [0, T) (as hq_probe_select returns
+ *   them for Tmax = T; any such set is accepted, including an empty one);
+ *   out [B][Hq][T][D] out_dt; ws of hq_prefill_ws_bytes() bytes, 256-byte
+ *   aligned. Entries outside the documented range are ignored, never read
+ *   out of bounds.
+ * Workspace after the call (the INT8 stage, readable for inspection), with
+ * nb = ceil(T / 64), Tp = 64 nb and A(x) = x rounded up to a multiple of 256:
+ *   offset 0                      Q8 int8 [B][Hq][Tp][D] (rows >= T are 0)
+ *   o1 = A(B Hq Tp D)             sQ fp32 [B][Hq][nb]
+ *   o2 = o1 + A(4 B Hq nb)        K8 int8 [B][Hkv][Tp][D]
+ *   o3 = o2 + A(B Hkv Tp D)       sK fp32 [B][Hkv][nb]
+ * the rest is staging (fp16 V^T blocks, selected-column masks and gathered
+ * selected K / V tiles).
+ * Errors: HQ_ERR_UNSUPPORTED for D != 128, Hq % Hkv != 0, G = Hq / Hkv not
+ * in {1, 2, 4, 8} or an unsupported dtype; HQ_ERR_CAPACITY if ws_bytes is
+ * too small; HQ_ERR_INVALID_ARG for null pointers or T outside [1, 2^22]. */
 hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,
                           int32_t Hkv, int32_t T, int32_t D, hq_dtype dt,
                           const hq_policy* policy, const int32_t* sel_idx,

@@ -275,6 +275,8 @@ hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B
     const size_t need = hq::prefill_ws_bytes(B, Hq, Hkv, T, *policy);
     REQ_PTR(ws);
     if (ws_bytes < need) return fail(HQ_ERR_CAPACITY, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    if (reinterpret_cast<uintptr_t>(ws) % 256)
+        return fail(HQ_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
     hipError_t e = hq::launch_prefill(q, k, v, B, Hq, Hkv, T, dt == HQ_F16, *policy, sel_idx, sel_count,
                                       hq::sel_stride(T, *policy), sm_scale, out, out_dt, ws, (hipStream_t)stream);
     if (e == hipErrorNotSupported) return fail(HQ_ERR_UNSUPPORTED, "%s: not available in this build", fn);

@@ -1,15 +1,585 @@
 // hq_prefill_attn: causal hybrid-precision prefill attention (gfx950).
-// (kernels pending; the entry point reports HQ_ERR_UNSUPPORTED until then)
+//
+// HyQuant pages: the HyQuant abstract (Prefill stage: the vertical-line
+// tokens and a local sliding window stay in full precision, the remaining
+// context is quantized); "How HyQuant uses hybrid-precision attention to cut
+// decode compute", "What hybrid-precision attention changes" (compute the
+// selected positions and the window in full precision, the rest in low
+// precision); "HyQuant: Hybrid-Precision Quantization for LLM Attention",
+// "How this relates to prior wiki pages" (two precision paths updating one
+// online-softmax state).
+//
+// Score of query row i and key j <= i (window W, selected set S of the KV head):
+//   j in S or i - j < W : (q_i . k_j) * sm_scale                 bf16 MFMA
+//   otherwise           : (Q8_i . K8_j) * sQ * sK * sm_scale      int8 MFMA
+// INT8 is symmetric per 64-token block over all 128 channels:
+// s = fp32(max|x| / 127), code = clamp(rint(x / s), -127, 127).
+//
+// Pre-pass (k_pf_quant_q, k_pf_quant_kv, k_pf_gather_sel): Q8/sQ, K8/sK, V
+// converted to fp16 and transposed per 64-key block (the PV operand
+// layout), a 64-bit selected-column mask per key block, and gathered tiles of
+// the selected columns (16-bit K rows and transposed fp16 V).
+//
+// Attention (k_pf_attn): one workgroup = 4 waves = 128 query rows of one head;
+// each wave owns 32 queries. S^T = K Q^T is computed with 32x32 MFMA tiles so
+// a lane holds one query column (16 keys per tile); row maxima need one
+// cross-half exchange. Key blocks of 64:
+//   * blocks entirely below the window band: int8 MFMA, selected columns
+//     dropped (p = 0);
+//   * the 4 blocks that touch the band/diagonal: int8 and bf16 MFMA, the
+//     score picked per element (band or selected -> bf16), causal mask;
+//   * gathered selected columns below the band: bf16 MFMA, no mask needed.
+// P goes to fp16 straight from the S^T registers (same key order as the V^T
+// operand) for the fp16 PV MFMA; O^T accumulates in fp32. Online softmax in
+// log2 units.
 #include "hq_internal.h"
 
 namespace hq {
+namespace {
 
-size_t prefill_ws_bytes(int32_t, int32_t, int32_t, int32_t, const hq_policy&) { return 256; }
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx16 __attribute__((ext_vector_type(16)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-hipError_t launch_prefill(const void*, const void*, const void*, int32_t, int32_t, int32_t, int32_t, bool,
-                          const hq_policy&, const int32_t*, const int32_t*, int32_t, float, void*, hq_dtype, void*,
-                          hipStream_t) {
-    return hipErrorNotSupported;
+constexpr int kBM = 128;  // query rows per workgroup
+constexpr int kBN = 64;   // keys per block
+
+struct PfLayout {
+    size_t q8, sq, k8, sk, vt, mask, ksel, vtsel, total;
+    int nblk, nsel_tiles;
+};
+inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+PfLayout pf_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, const hq_policy& pol) {
+    PfLayout w;
+    w.nblk = (T + kBN - 1) / kBN;
+    const int kmax = sel_stride(T, pol);
+    w.nsel_tiles = (kmax + kBN - 1) / kBN;
+    const size_t Tp = (size_t)w.nblk * kBN;
+    w.q8 = 0;
+    w.sq = w.q8 + al((size_t)B * Hq * Tp * kD);
+    w.k8 = w.sq + al((size_t)B * Hq * w.nblk * 4);
+    w.sk = w.k8 + al((size_t)B * Hkv * Tp * kD);
+    w.vt = w.sk + al((size_t)B * Hkv * w.nblk * 4);
+    w.mask = w.vt + al((size_t)B * Hkv * Tp * kD * 2);
+    w.ksel = w.mask + al((size_t)B * Hkv * w.nblk * 8);
+    w.vtsel = w.ksel + al((size_t)B * Hkv * w.nsel_tiles * kBN * kD * 2);
+    w.total = w.vtsel + al((size_t)B * Hkv * w.nsel_tiles * kBN * kD * 2);
+    return w;
+}
+
+__device__ inline float block_max256(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return r;
+}
+
+#pragma clang fp contract(off)
+// Symmetric INT8 of one 64 x 128 block (rows beyond T are zero); 256 threads,
+// thread t owns row t/4, channels 32*(t%4) .. +31.
+template <bool F16>
+__device__ inline void quant_block_i8(const uint16_t* src, int rows_valid, int8_t* dst, float* scale) {
+    __shared__ float red[4];
+    const int t = threadIdx.x, r = t >> 2, c0 = (t & 3) * 32;
+    float x[32];
+    if (r < rows_valid) {
+        const uint4* s4 = reinterpret_cast<const uint4*>(src + (size_t)r * kD + c0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 u = s4[i];
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[8 * i + 2 * j] = h16_to_f32<F16>(w[j] & 0xFFFFu);
+                x[8 * i + 2 * j + 1] = h16_to_f32<F16>(w[j] >> 16);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = 0.f;
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
+    am = block_max256(am, red);
+    const float s = am / 127.0f;
+    uint32_t packed[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float c = 0.f;
+            if (s > 0.f) c = fminf(fmaxf(rintf(x[4 * i + j] / s), -127.f), 127.f);
+            w |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * j);
+        }
+        packed[i] = w;
+    }
+    uint4* d4 = reinterpret_cast<uint4*>(dst + (size_t)r * kD + c0);
+    d4[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    d4[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    if (t == 0) *scale = s;
+}
+#pragma clang fp contract(on)
+
+struct PfParams {
+    const uint16_t* q;   // [B][Hq][T][D]
+    const uint16_t* k;   // [B][Hkv][T][D]
+    const uint16_t* v;
+    const int32_t* sel_idx;
+    const int32_t* sel_count;
+    int8_t* q8;          // [B][Hq][Tp][D]
+    float* sq;           // [B][Hq][nblk]
+    int8_t* k8;          // [B][Hkv][Tp][D]
+    float* sk;           // [B][Hkv][nblk]
+    uint16_t* vt;        // [B][Hkv][nblk][D][64] fp16 (V^T per key block)
+    uint64_t* mask;      // [B][Hkv][nblk] selected-column bits
+    uint16_t* ksel;      // [B][Hkv][nsel_tiles][64][D] 16-bit K rows of selected columns
+    uint16_t* vtsel;     // [B][Hkv][nsel_tiles][D][64] fp16 V^T of selected columns
+    float* out;
+    int out_dt;
+    int B, Hq, Hkv, G, T, nblk, nsel_tiles, sel_stride, W;
+    float c16;           // sm_scale * log2(e)
+};
+
+template <bool F16>
+__global__ __launch_bounds__(256) void k_pf_quant_q(PfParams p) {
+    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const size_t Tp = (size_t)p.nblk * kBN;
+    const uint16_t* src = p.q + (((size_t)b * p.Hq + h) * p.T + (size_t)blk * kBN) * kD;
+    int8_t* dst = p.q8 + (((size_t)b * p.Hq + h) * Tp + (size_t)blk * kBN) * kD;
+    quant_block_i8<F16>(src, min(kBN, p.T - blk * kBN), dst, p.sq + ((size_t)b * p.Hq + h) * p.nblk + blk);
+}
+
+// K8 + sK, V^T in fp16, and the selected-column mask of one key block.
+template <bool F16>
+__global__ __launch_bounds__(256) void k_pf_quant_kv(PfParams p) {
+    __shared__ uint16_t vs[kBN][kD + 8];
+    const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int bg = b * p.Hkv + g;
+    const size_t Tp = (size_t)p.nblk * kBN;
+    const int rows = min(kBN, p.T - blk * kBN);
+    const uint16_t* ksrc = p.k + ((size_t)bg * p.T + (size_t)blk * kBN) * kD;
+    quant_block_i8<F16>(ksrc, rows, p.k8 + ((size_t)bg * Tp + (size_t)blk * kBN) * kD, p.sk + (size_t)bg * p.nblk + blk);
+    // V -> fp16 -> transposed
+    const int t = threadIdx.x, r = t >> 2, c0 = (t & 3) * 32;
+    const uint16_t* vsrc = p.v + ((size_t)bg * p.T + (size_t)blk * kBN) * kD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (r < rows) u = reinterpret_cast<const uint4*>(vsrc + (size_t)r * kD + c0)[i];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            vs[r][c0 + 8 * i + 2 * j] = (uint16_t)f32_to_f16_bits(h16_to_f32<F16>(w[j] & 0xFFFFu));
+            vs[r][c0 + 8 * i + 2 * j + 1] = (uint16_t)f32_to_f16_bits(h16_to_f32<F16>(w[j] >> 16));
+        }
+    }
+    __syncthreads();
+    uint16_t* vdst = p.vt + ((size_t)bg * p.nblk + blk) * kD * kBN;
+    for (int e = t; e < kD * 8; e += 256) {   // (channel, 8-key segment)
+        const int ch = e >> 3, k0 = (e & 7) * 8;
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = (uint32_t)vs[k0 + 2 * j][ch] | ((uint32_t)vs[k0 + 2 * j + 1][ch] << 16);
+        *reinterpret_cast<uint4*>(vdst + (size_t)ch * kBN + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    // selected-column bits of this block
+    if (t == 0) {
+        const int32_t* S = p.sel_idx + (size_t)bg * p.sel_stride;
+        const int k = min(max(p.sel_count[bg], 0), p.sel_stride);
+        int lo = 0, hi = k;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (S[mid] < blk * kBN) lo = mid + 1;
+            else hi = mid;
+        }
+        uint64_t bits = 0;
+        for (int i = lo; i < k && S[i] < blk * kBN + kBN; ++i)
+            if (S[i] >= blk * kBN) bits |= 1ull << (S[i] - blk * kBN);
+        p.mask[(size_t)bg * p.nblk + blk] = bits;
+    }
+}
+
+// Gathered tiles of selected columns: 16-bit K rows and fp16 V^T.
+template <bool F16>
+__global__ __launch_bounds__(256) void k_pf_gather_sel(PfParams p) {
+    __shared__ uint16_t vs[kBN][kD + 8];
+    const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int bg = b * p.Hkv + g;
+    const int k = min(max(p.sel_count[bg], 0), p.sel_stride);
+    if (tile * kBN >= k) return;
+    const int32_t* S = p.sel_idx + (size_t)bg * p.sel_stride;
+    const int t = threadIdx.x, r = t >> 2, c0 = (t & 3) * 32;
+    const int i = tile * kBN + r;
+    const bool ok = i < k && S[i] >= 0 && S[i] < p.T;
+    const int pos = ok ? S[i] : 0;
+    const uint4* ks = reinterpret_cast<const uint4*>(p.k + ((size_t)bg * p.T + pos) * kD + c0);
+    const uint4* vsrc = reinterpret_cast<const uint4*>(p.v + ((size_t)bg * p.T + pos) * kD + c0);
+    uint4* kd = reinterpret_cast<uint4*>(p.ksel + (((size_t)bg * p.nsel_tiles + tile) * kBN + r) * kD + c0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 kk = ok ? ks[j] : make_uint4(0, 0, 0, 0);
+        kd[j] = kk;
+        const uint4 u = ok ? vsrc[j] : make_uint4(0, 0, 0, 0);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vs[r][c0 + 8 * j + 2 * e] = (uint16_t)f32_to_f16_bits(h16_to_f32<F16>(w[e] & 0xFFFFu));
+            vs[r][c0 + 8 * j + 2 * e + 1] = (uint16_t)f32_to_f16_bits(h16_to_f32<F16>(w[e] >> 16));
+        }
+    }
+    __syncthreads();
+    uint16_t* vdst = p.vtsel + ((size_t)bg * p.nsel_tiles + tile) * kD * kBN;
+    for (int e = t; e < kD * 8; e += 256) {
+        const int ch = e >> 3, k0 = (e & 7) * 8;
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = (uint32_t)vs[k0 + 2 * j][ch] | ((uint32_t)vs[k0 + 2 * j + 1][ch] << 16);
+        *reinterpret_cast<uint4*>(vdst + (size_t)ch * kBN + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// ---------------------------------------------------------------- attention
+
+// LDS tile strides (bytes), padded so the 32 rows read by one MFMA operand
+// fetch fall in different banks.
+constexpr int kK8Stride = kD + 16;        // int8 K rows
+constexpr int kK16Stride = 2 * kD + 16;   // 16-bit K rows
+constexpr int kVtStride = 2 * kBN + 8;    // fp16 V^T rows (one channel, 64 keys)
+
+struct Smem {
+    int8_t k8[kBN * kK8Stride];
+    uint8_t k16[kBN * kK16Stride];
+    uint8_t vt[kD * kVtStride];
+};
+
+// The key of S^T row m (m < 32) of a 32-key MFMA tile held by lane half hf in
+// register r: m = 8*(r/4) + 4*hf + r%4.
+__device__ inline int st_key(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+// Cooperative copies into LDS (256 threads).
+__device__ inline void copy_k8(Smem& sm, const int8_t* src) {  // [64][128] int8
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int e = t; e < kBN * 8; e += 256) {
+        const int r = e >> 3, c = (e & 7) * 16;
+        *reinterpret_cast<uint4*>(sm.k8 + r * kK8Stride + c) = *reinterpret_cast<const uint4*>(src + r * kD + c);
+    }
+}
+__device__ inline void copy_k16(Smem& sm, const uint16_t* src, int rows_valid) {  // [64][128] 16-bit
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int e = t; e < kBN * 16; e += 256) {
+        const int r = e >> 4, c = (e & 15) * 16;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < rows_valid) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(src) + (size_t)r * 2 * kD + c);
+        *reinterpret_cast<uint4*>(sm.k16 + r * kK16Stride + c) = v;
+    }
+}
+__device__ inline void copy_vt(Smem& sm, const uint16_t* src) {  // [128][64] fp16
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int e = t; e < kD * 8; e += 256) {
+        const int r = e >> 3, c = (e & 7) * 16;
+        *reinterpret_cast<uint4*>(sm.vt + r * kVtStride + c) =
+            *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(src) + (size_t)r * 2 * kBN + c);
+    }
+}
+
+// S^T (64 keys x 32 queries) in int8: two 32x32 tiles, K = 128 in 4 steps.
+__device__ inline void st_int8(const Smem& sm, const intx4 (&qb)[4], intx16 (&s)[2]) {
+    const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        intx16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const intx4 a = *reinterpret_cast<const intx4*>(sm.k8 + (32 * tt + m) * kK8Stride + 32 * ks + 16 * hf);
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qb[ks], acc, 0, 0, 0);
+        }
+        s[tt] = acc;
+    }
+}
+// S^T in 16-bit (bf16 or fp16 inputs), K = 128 in 8 steps.
+template <bool F16>
+__device__ inline void st_16(const uint8_t* k16, const intx4 (&qb)[8], floatx16 (&s)[2]) {
+    const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        floatx16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const intx4 a = *reinterpret_cast<const intx4*>(k16 + (32 * tt + m) * kK16Stride + 2 * (16 * ks + 8 * hf));
+            if constexpr (F16)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, qb[ks]),
+                                                             acc, 0, 0, 0);
+            else
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                              __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
+        }
+        s[tt] = acc;
+    }
+}
+
+// O^T += V^T P^T for one 64-key block. P^T step j covers S^T tile j/2,
+// registers 8*(j%2) .. +7 (keys 16*(j%2) + {4hf..4hf+3, 8+4hf..8+4hf+3} of
+// that tile); the V^T operand reads the same keys for channel 32*ct + m.
+__device__ inline void pv_block(const uint8_t* vt, const float (&p)[2][16], floatx16 (&o)[4]) {
+    const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
+    halfx8 pb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[j][e] = (_Float16)p[j >> 1][8 * (j & 1) + e];
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        const uint8_t* row = vt + (32 * ct + m) * kVtStride;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int key0 = 32 * (j >> 1) + 16 * (j & 1) + 4 * hf;
+            const uint2 lo = *reinterpret_cast<const uint2*>(row + 2 * key0);
+            const uint2 hi = *reinterpret_cast<const uint2*>(row + 2 * (key0 + 8));
+            const intx4 a = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+            o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a), pb[j], o[ct], 0, 0, 0);
+        }
+    }
+}
+
+// Online softmax update of one block: x[tt][r] are log2-domain scores
+// (-inf for masked); updates m, l (this lane's half), rescales o, returns p.
+__device__ inline void softmax_block(float (&x)[2][16], float& m, float& l, floatx16 (&o)[4]) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bm = fmaxf(bm, x[tt][r]);
+    {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+        bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    if (bm > m) {
+        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - bm);
+        m = bm;
+        l *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[tt][r] - m);
+            x[tt][r] = pv;
+            l += pv;
+        }
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256) void k_pf_attn(PfParams p) {
+    __shared__ Smem sm;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m_ = lane & 31, hf = lane >> 5;
+    // heavy (late) query blocks first
+    const int qb = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int g = h / p.G, bg = b * p.Hkv + g;
+    const int i0 = qb * kBM;
+    if (i0 >= p.T) return;
+    const int W = p.W;
+    const size_t Tp = (size_t)p.nblk * kBN;
+    // this wave's 32 queries; lane's query column
+    const int qrow0 = i0 + 32 * wave;
+    const int qi = qrow0 + m_;
+    const bool qvalid = qi < p.T;
+    // B operands: Q8 (16 B per k-step) and 16-bit Q (16 B per k-step)
+    intx4 q8b[4], q16b[8];
+    {
+        const int8_t* q8 = p.q8 + (((size_t)b * p.Hq + h) * Tp + (size_t)(qvalid ? qi : 0)) * kD;
+        const uint16_t* q16 = p.q + (((size_t)b * p.Hq + h) * p.T + (size_t)(qvalid ? qi : 0)) * kD;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) q8b[ks] = *reinterpret_cast<const intx4*>(q8 + 32 * ks + 16 * hf);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const intx4 z = {0, 0, 0, 0};
+            q16b[ks] = qvalid ? *reinterpret_cast<const intx4*>(q16 + 16 * ks + 8 * hf) : z;
+        }
+    }
+    const float sq = p.sq[((size_t)b * p.Hq + h) * p.nblk + min(qrow0 >> 6, p.nblk - 1)];
+    const float c16 = p.c16;
+    float m = -INFINITY, l = 0.f;
+    floatx16 o[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) o[ct] = floatx16{};
+
+    const int nkb = min(p.nblk, (i0 + kBM + kBN - 1) / kBN);  // key blocks with keys <= last row
+    // key blocks kb < kb_band are entirely below the window band for all rows
+    const int kb_band = max(0, (i0 - W + 1) / kBN);  // first block that may touch i - j < W
+    for (int kb = 0; kb < nkb; ++kb) {
+        const bool band = kb >= kb_band;
+        __syncthreads();
+        copy_k8(sm, p.k8 + ((size_t)bg * Tp + (size_t)kb * kBN) * kD);
+        copy_vt(sm, p.vt + ((size_t)bg * p.nblk + kb) * kD * kBN);
+        if (band) copy_k16(sm, p.k + ((size_t)bg * p.T + (size_t)kb * kBN) * kD, min(kBN, p.T - kb * kBN));
+        __syncthreads();
+        intx16 si[2];
+        st_int8(sm, q8b, si);
+        const float c8 = sq * p.sk[(size_t)bg * p.nblk + kb] * c16;
+        const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
+        float x[2][16];
+        if (!band) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * tt + st_key(r, hf);
+                    const bool sel = (selbits >> key) & 1ull;
+                    x[tt][r] = sel ? -INFINITY : (float)si[tt][r] * c8;
+                }
+        } else {
+            floatx16 sb[2];
+            st_16<F16>(sm.k16, q16b, sb);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kl = 32 * tt + st_key(r, hf);
+                    const int j = kb * kBN + kl;
+                    const bool sel = (selbits >> kl) & 1ull;
+                    const bool hi = sel || (qi - j < W);
+                    float val = hi ? sb[tt][r] * c16 : (float)si[tt][r] * c8;
+                    if (j > qi || j >= p.T || !qvalid) val = -INFINITY;
+                    x[tt][r] = val;
+                }
+        }
+        softmax_block(x, m, l, o);
+        pv_block(sm.vt, x, o);
+    }
+    // gathered selected columns strictly below the band of every row of the block
+    {
+        const int32_t* S = p.sel_idx + (size_t)bg * p.sel_stride;
+        const int k = min(max(p.sel_count[bg], 0), p.sel_stride);
+        // columns j < kb_band * 64 are below the band for all rows of this block
+        const int lim = kb_band * kBN;
+        int lo = 0, hi = k;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (S[mid] < lim) lo = mid + 1;
+            else hi = mid;
+        }
+        const int nsel = lo;
+        for (int tile = 0; tile * kBN < nsel; ++tile) {
+            __syncthreads();
+            copy_k16(sm, p.ksel + ((size_t)bg * p.nsel_tiles + tile) * kBN * kD, kBN);
+            copy_vt(sm, p.vtsel + ((size_t)bg * p.nsel_tiles + tile) * kD * kBN);
+            __syncthreads();
+            floatx16 sb[2];
+            st_16<F16>(sm.k16, q16b, sb);
+            float x[2][16];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int idx = tile * kBN + 32 * tt + st_key(r, hf);
+                    x[tt][r] = (idx < nsel && qvalid) ? sb[tt][r] * c16 : -INFINITY;
+                }
+            softmax_block(x, m, l, o);
+            pv_block(sm.vt, x, o);
+        }
+    }
+    // combine the two lane halves of each query and write
+    {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+        l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (!qvalid) return;
+    const float inv = 1.0f / l;
+    const size_t orow = (((size_t)b * p.Hq + h) * p.T + qi) * kD;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int ch = 32 * ct + 8 * r4 + 4 * hf;
+            float4 v = make_float4(o[ct][4 * r4] * inv, o[ct][4 * r4 + 1] * inv, o[ct][4 * r4 + 2] * inv,
+                                   o[ct][4 * r4 + 3] * inv);
+            if (p.out_dt == HQ_F32) {
+                *reinterpret_cast<float4*>(p.out + orow + ch) = v;
+            } else {
+                uint16_t* o16 = reinterpret_cast<uint16_t*>(p.out) + orow + ch;
+                const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (p.out_dt == HQ_F16) o16[e] = (uint16_t)f32_to_f16_bits(vv[e]);
+                    else {
+                        uint32_t xb = __float_as_uint(vv[e]);
+                        xb += 0x7FFFu + ((xb >> 16) & 1u);
+                        o16[e] = (uint16_t)(xb >> 16);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+size_t prefill_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, const hq_policy& pol) {
+    return pf_layout(B, Hq, Hkv, T, pol).total;
+}
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv,
+                          int32_t T, bool f16, const hq_policy& pol, const int32_t* sel_idx,
+                          const int32_t* sel_count, int32_t sel_stride_, float sm_scale, void* out,
+                          hq_dtype out_dt, void* ws, hipStream_t s) {
+    const PfLayout w = pf_layout(B, Hq, Hkv, T, pol);
+    char* base = static_cast<char*>(ws);
+    PfParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.sel_idx = sel_idx;
+    p.sel_count = sel_count;
+    p.q8 = reinterpret_cast<int8_t*>(base + w.q8);
+    p.sq = reinterpret_cast<float*>(base + w.sq);
+    p.k8 = reinterpret_cast<int8_t*>(base + w.k8);
+    p.sk = reinterpret_cast<float*>(base + w.sk);
+    p.vt = reinterpret_cast<uint16_t*>(base + w.vt);
+    p.mask = reinterpret_cast<uint64_t*>(base + w.mask);
+    p.ksel = reinterpret_cast<uint16_t*>(base + w.ksel);
+    p.vtsel = reinterpret_cast<uint16_t*>(base + w.vtsel);
+    p.out = static_cast<float*>(out);
+    p.out_dt = (int)out_dt;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = Hq / Hkv;
+    p.T = T;
+    p.nblk = w.nblk;
+    p.nsel_tiles = w.nsel_tiles;
+    p.sel_stride = sel_stride_;
+    p.W = pol.window;
+    p.c16 = sm_scale * 1.4426950408889634f;
+    if (f16) {
+        k_pf_quant_q<true><<<dim3(w.nblk, Hq, B), 256, 0, s>>>(p);
+        k_pf_quant_kv<true><<<dim3(w.nblk, Hkv, B), 256, 0, s>>>(p);
+        k_pf_gather_sel<true><<<dim3(w.nsel_tiles, Hkv, B), 256, 0, s>>>(p);
+        k_pf_attn<true><<<dim3((T + kBM - 1) / kBM, Hq, B), 256, 0, s>>>(p);
+    } else {
+        k_pf_quant_q<false><<<dim3(w.nblk, Hq, B), 256, 0, s>>>(p);
+        k_pf_quant_kv<false><<<dim3(w.nblk, Hkv, B), 256, 0, s>>>(p);
+        k_pf_gather_sel<false><<<dim3(w.nsel_tiles, Hkv, B), 256, 0, s>>>(p);
+        k_pf_attn<false><<<dim3((T + kBM - 1) / kBM, Hq, B), 256, 0, s>>>(p);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace hq
