@@ -94,6 +94,61 @@ def prefill_flops(T, Hq, B=1):
     return 4.0 * 128 * pairs * Hq * B
 
 
+def prefill_pair_split(T, W, sel_idx, sel_cnt, G):
+    """Causal (query, key) pairs whose score is exact (window band or selected
+    column) and INT8 (the rest), summed over query heads. A selected column j
+    adds the rows i >= j + W that the band does not already cover."""
+    import numpy as np
+    total = T * (T + 1) // 2
+    band = sum(min(i + 1, W) for i in range(T)) if W > 0 else 0
+    exact = 0
+    B, Hkv = sel_cnt.shape
+    for b in range(B):
+        for g in range(Hkv):
+            j = sel_idx[b, g, : sel_cnt[b, g]].astype(np.int64)
+            exact += G * (band + int(np.clip(T - (j + W), 0, None).sum()))
+    heads = B * Hkv * G
+    return exact, heads * total - exact
+
+
+def prefill_roofline(T, W, sel_idx, sel_cnt, G, ms):
+    """Mixed MFMA floor: INT8 QK pairs at the int8 peak, exact QK pairs and
+    every PV pair at the 16-bit peak (2 * 128 flops per pair each)."""
+    exact, low = prefill_pair_split(T, W, sel_idx, sel_cnt, G)
+    per = 2.0 * 128
+    f16_flops = per * exact + per * (exact + low)
+    i8_ops = per * low
+    floor_s = f16_flops / (MFMA_BF16_TFLOPS * 1e12) + i8_ops / (MFMA_I8_TOPS * 1e12)
+    total = f16_flops + i8_ops
+    achieved = total / (ms * 1e-3) / 1e12
+    peak = total / floor_s / 1e12
+    return {"bound": "mfma", "kernel": "hq_prefill_attn (INT8 stage + hybrid attention)",
+            "achieved": round(achieved, 1), "peak": round(peak, 1), "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "floor_us": round(floor_s * 1e6, 1), "int8_qk_pair_frac": round(low / (exact + low), 4)}
+
+
+def decode_traffic(launch_bytes_alg):
+    """HBM bytes per launch of the decode split kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, each scaled by the factor a
+    plain copy of known size gives for the same counter; None when the kernel
+    source changed after the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "decode_8b_32k_split_traffic.md")
+    src = os.path.join(ROOT, "kv_cache_amd", "csrc", "decode.hip")
+    try:
+        text = open(path).read()
+        m = re.search(r"```json\n(.*?)\n```", text, re.S)
+        rec = json.loads(m.group(1))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, AttributeError, ValueError):
+        return None
+    if rec.get("decode_hip_sha256") != sha:
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
 def cpu_baseline(inp, sels_gpu, budget_s=20.0):
     """The oracle (numpy fp64) timed on this host on a bounded sample of the
     decode workload: whole (b, g) units of one decode step, scaled to the
@@ -123,11 +178,54 @@ def cpu_baseline(inp, sels_gpu, budget_s=20.0):
             n += 1
     per_unit = sum(t_units) / len(t_units)
     full_us = per_unit * sp.B * sp.Hkv * 1e6
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(full_us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+    return {"value": round(full_us, 1), "unit": "us/step", "cores": _cpu_threads(), "kind": "oracle",
             "sample": f"{n} of {sp.B * sp.Hkv} (batch, KV head) units of one 32K decode step "
                       f"(cache build + fp64 attention), {sum(t_units):.1f} s, scaled x{sp.B * sp.Hkv / n:.1f}",
             "cpu": platform.processor() or platform.machine()}
+
+
+def _cpu_threads():
+    """Threads the oracle's numpy BLAS actually runs with."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d["num_threads"] for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def cpu_baseline_prefill(pin, sel_idx, sel_cnt, budget_s=8.0):
+    """The oracle's hybrid prefill timed on this host on sampled query rows of
+    the 16K workload (INT8 stage of the head + per-row fp64 attention),
+    scaled to all rows of all heads, in ms."""
+    import numpy as np
+    import oracle as O
+    sp = pin.spec
+    G = sp.Hq // sp.Hkv
+    sm = 1 / math.sqrt(sp.D)
+    rng = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    q = O.to_f64(pin.q[0, 0], sp.dtype)
+    k = O.to_f64(pin.k[0, 0], sp.dtype)
+    v = O.to_f64(pin.v[0, 0], sp.dtype)
+    q8, sq = O.int8_block_quantize(q)
+    k8, sk = O.int8_block_quantize(k)
+    t_quant = time.perf_counter() - t0
+    S = sel_idx[0, 0, : sel_cnt[0, 0]].astype(np.int64)
+    done, t_rows = 0, 0.0
+    while t_rows < budget_s:
+        rows = rng.integers(0, sp.T, size=16)
+        t1 = time.perf_counter()
+        O.prefill_attention_rows(q, k, v, S, 128, sm, q8, sq, k8, sk, rows)
+        t_rows += time.perf_counter() - t1
+        done += len(rows)
+    # rows are uniform over [0, T), so the mean row cost scales to all rows
+    full_s = t_rows / done * sp.T * sp.Hq + t_quant * (sp.Hq + sp.Hkv) / 2
+    return {"value": round(full_s * 1e3, 1), "unit": "ms/prefill", "cores": _cpu_threads(), "kind": "oracle",
+            "sample": f"{done} uniformly drawn query rows of head 0 of the 16K prefill "
+                      f"({t_rows:.1f} s) plus one head's INT8 stage, scaled to {sp.T} rows x {sp.Hq} heads"}
 
 
 def main():
@@ -176,7 +274,10 @@ def main():
                   v=_dev16(pin.v, "bf16", dev), lens=torch.full((1,), pspec.T, dtype=torch.int32, device=dev))
         pf["qprobe"] = pf["q"][:, :, pspec.T - 64:].contiguous()
         pf["out"] = torch.empty((1, pspec.Hq, pspec.T, 128), dtype=torch.float32, device=dev)
-        del pin
+        if args.no_cpu_baseline:
+            del pin
+        else:
+            pf["pin"] = pin
         print(f"# generated prefill inputs", file=sys.stderr, flush=True)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     tm = Timer()
@@ -249,16 +350,22 @@ def main():
     res["roofline"] = {"bound": "hbm", "kernel": "hq_decode_attn (prep + split-K + reduce)",
                        "achieved": round(dbytes / (dec_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                        "unit": "GB/s", "frac": round(dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                       "traffic": None}
+                       "traffic": decode_traffic(dbytes)}
     if prefill_ok:
         pms = tm.ms("prefill_attn")
-        fl = prefill_flops(pf["spec"].T, pf["spec"].Hq)
+        psp = pf["spec"]
+        fl = prefill_flops(psp.T, psp.Hq)
         res["prefill_ms"] = round(pms, 3)
         res["prefill_TFLOPs"] = round(fl / (pms * 1e-3) / 1e12, 1)
         res["prefill_probe_select_ms"] = round(tm.ms("prefill_probe_select"), 3)
+        psel = hq.probe_select(pf["qprobe"], pf["k"], pf["lens"], pol)
+        psel_idx, psel_cnt = psel[1].cpu().numpy(), psel[2].cpu().numpy()
+        res["prefill_roofline"] = prefill_roofline(psp.T, pol.window, psel_idx, psel_cnt, psp.Hq // psp.Hkv, pms)
     if not args.no_cpu_baseline:
         sels = tuple(t.cpu().numpy() for t in (hq.probe_select(qp, k, lens, pol)))
         res["cpu_baseline"] = cpu_baseline(inp, sels)
+        if prefill_ok and "pin" in pf:
+            res["cpu_baseline_prefill"] = cpu_baseline_prefill(pf["pin"], psel_idx, psel_cnt)
     print(json.dumps(res), flush=True)
 
 
