@@ -15,7 +15,8 @@ bracketed by HIP events on the stream it is launched on (torch's current
 stream); `value` is the decode attention time per step (hq_decode_attn) in
 microseconds; the other rows are reported beside it.
 
-Prints ONE JSON line (see README of the output fields in the design doc).
+Prints ONE JSON line: the decode time and bandwidth, the prefill time and
+TFLOP/s, a roofline object for each, and the oracle's CPU timings.
 """
 from __future__ import annotations
 

@@ -20,8 +20,8 @@ and everything else is quantized to low bit width (K4/V4 in the reported
 implementation). Prefill runs a hybrid-precision attention operator with the
 same split; decode keeps a hybrid KV cache and fuses dequantization into
 attention. The pages leave the probe statistic, the quantizer format, the
-window shape, tie-breaks and rounding unspecified; the readings used here are
-stated at each function and collected in the design doc's list of readings.
+window shape, tie-breaks and rounding unspecified; the reading used for each
+is stated at the function that depends on it.
 
 Conventions: arrays are float64 copies of exact 16-bit inputs; per-(batch,
 KV head) functions take one sequence at a time; GQA maps query head h to KV
