@@ -128,6 +128,10 @@ __device__ inline void quant_block_i8(const uint16_t* src, int rows_valid, int8_
 }
 #pragma clang fp contract(on)
 
+// Key held at position s of a 64-key V^T row: each 16-key group is stored as
+// keys 0-3, 8-11, 4-7, 12-15 (the order one lane half of the PV MFMA reads).
+__device__ constexpr int vt_key(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
+
 struct PfParams {
     const uint16_t* q;   // [B][Hq][T][D]
     const uint16_t* k;   // [B][Hkv][T][D]
@@ -138,10 +142,10 @@ struct PfParams {
     float* sq;           // [B][Hq][nblk]
     int8_t* k8;          // [B][Hkv][Tp][D]
     float* sk;           // [B][Hkv][nblk]
-    uint16_t* vt;        // [B][Hkv][nblk][D][64] fp16 (V^T per key block)
+    uint16_t* vt;        // [B][Hkv][nblk][D][64] fp16 V^T per key block, keys in vt_key order
     uint64_t* mask;      // [B][Hkv][nblk] selected-column bits
     uint16_t* ksel;      // [B][Hkv][nsel_tiles][64][D] 16-bit K rows of selected columns
-    uint16_t* vtsel;     // [B][Hkv][nsel_tiles][D][64] fp16 V^T of selected columns
+    uint16_t* vtsel;     // [B][Hkv][nsel_tiles][D][64] fp16 V^T of selected columns, vt_key order
     float* out;
     int out_dt;
     int B, Hq, Hkv, G, T, nblk, nsel_tiles, sel_stride, W;
@@ -187,7 +191,8 @@ __global__ __launch_bounds__(256) void k_pf_quant_kv(PfParams p) {
         const int ch = e >> 3, k0 = (e & 7) * 8;
         uint32_t w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = (uint32_t)vs[k0 + 2 * j][ch] | ((uint32_t)vs[k0 + 2 * j + 1][ch] << 16);
+        for (int j = 0; j < 4; ++j)
+            w[j] = (uint32_t)vs[vt_key(k0 + 2 * j)][ch] | ((uint32_t)vs[vt_key(k0 + 2 * j + 1)][ch] << 16);
         *reinterpret_cast<uint4*>(vdst + (size_t)ch * kBN + k0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
     // selected-column bits of this block
@@ -241,67 +246,84 @@ __global__ __launch_bounds__(256) void k_pf_gather_sel(PfParams p) {
         const int ch = e >> 3, k0 = (e & 7) * 8;
         uint32_t w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = (uint32_t)vs[k0 + 2 * j][ch] | ((uint32_t)vs[k0 + 2 * j + 1][ch] << 16);
+        for (int j = 0; j < 4; ++j)
+            w[j] = (uint32_t)vs[vt_key(k0 + 2 * j)][ch] | ((uint32_t)vs[vt_key(k0 + 2 * j + 1)][ch] << 16);
         *reinterpret_cast<uint4*>(vdst + (size_t)ch * kBN + k0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
 // ---------------------------------------------------------------- attention
 
-// LDS tile strides (bytes), padded so the 32 rows read by one MFMA operand
-// fetch fall in different banks.
-constexpr int kK8Stride = kD + 16;        // int8 K rows
-constexpr int kK16Stride = 2 * kD + 16;   // 16-bit K rows
-constexpr int kVtStride = 2 * kBN + 8;    // fp16 V^T rows (one channel, 64 keys)
+// LDS row strides (bytes), padded so that the 8 lanes of one 128-bit LDS
+// access phase read 8 different rows in disjoint banks.
+constexpr int kK8Stride = kD + 16;        // int8 K rows (128 B + pad)
+constexpr int kK16Stride = 2 * kD + 16;   // 16-bit K rows (256 B + pad)
+constexpr int kVtStride = 2 * kBN + 16;   // fp16 V^T rows (one channel, 64 keys)
+constexpr float kLazy = 8.0f;             // log2-domain growth that triggers a rescale
 
 struct Smem {
-    int8_t k8[kBN * kK8Stride];
+    int8_t k8[2][kBN * kK8Stride];
+    uint8_t vt[2][kD * kVtStride];
     uint8_t k16[kBN * kK16Stride];
-    uint8_t vt[kD * kVtStride];
 };
 
-// The key of S^T row m (m < 32) of a 32-key MFMA tile held by lane half hf in
-// register r: m = 8*(r/4) + 4*hf + r%4.
-__device__ inline int st_key(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+// S^T register r of lane half hf in a 32-key MFMA tile holds key
+// 8*(r/4) + 4*hf + r%4 (the 32x32 MFMA output layout, M = keys).
+__device__ constexpr int st_key(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
 // Cooperative copies into LDS (256 threads).
-__device__ inline void copy_k8(Smem& sm, const int8_t* src) {  // [64][128] int8
+__device__ inline void copy_k16(uint8_t* dst, const uint16_t* src, int rows_valid) {  // [64][128] 16-bit
     const int t = threadIdx.x;
 #pragma unroll
-    for (int e = t; e < kBN * 8; e += 256) {
-        const int r = e >> 3, c = (e & 7) * 16;
-        *reinterpret_cast<uint4*>(sm.k8 + r * kK8Stride + c) = *reinterpret_cast<const uint4*>(src + r * kD + c);
-    }
-}
-__device__ inline void copy_k16(Smem& sm, const uint16_t* src, int rows_valid) {  // [64][128] 16-bit
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int e = t; e < kBN * 16; e += 256) {
-        const int r = e >> 4, c = (e & 15) * 16;
+    for (int i = 0; i < 4; ++i) {
+        const int e = t + 256 * i, r = e >> 4, c = (e & 15) * 16;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (r < rows_valid) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(src) + (size_t)r * 2 * kD + c);
-        *reinterpret_cast<uint4*>(sm.k16 + r * kK16Stride + c) = v;
+        *reinterpret_cast<uint4*>(dst + r * kK16Stride + c) = v;
     }
 }
-__device__ inline void copy_vt(Smem& sm, const uint16_t* src) {  // [128][64] fp16
+
+// Register staging of one INT8 K block (8 KB) and one fp16 V^T block (16 KB):
+// thread t moves 16-byte chunks e = t + 256 i (row e / 8, column chunk e % 8).
+struct Stage {
+    uint4 k0, k1, v0, v1, v2, v3;
+};
+__device__ inline const uint4& ld16(const void* base, int e, int row_bytes) {
+    return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(base) + (e >> 3) * row_bytes + (e & 7) * 16);
+}
+__device__ inline void st16(void* base, int e, int row_bytes, const uint4& v) {
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(base) + (e >> 3) * row_bytes + (e & 7) * 16) = v;
+}
+__device__ inline Stage stage_load(const int8_t* k8, const uint16_t* vt) {
     const int t = threadIdx.x;
-#pragma unroll
-    for (int e = t; e < kD * 8; e += 256) {
-        const int r = e >> 3, c = (e & 7) * 16;
-        *reinterpret_cast<uint4*>(sm.vt + r * kVtStride + c) =
-            *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(src) + (size_t)r * 2 * kBN + c);
-    }
+    Stage s;
+    s.k0 = ld16(k8, t, kD);
+    s.k1 = ld16(k8, t + 256, kD);
+    s.v0 = ld16(vt, t, 2 * kBN);
+    s.v1 = ld16(vt, t + 256, 2 * kBN);
+    s.v2 = ld16(vt, t + 512, 2 * kBN);
+    s.v3 = ld16(vt, t + 768, 2 * kBN);
+    return s;
+}
+__device__ inline void stage_store(Smem& sm, int buf, const Stage& s) {
+    const int t = threadIdx.x;
+    st16(sm.k8[buf], t, kK8Stride, s.k0);
+    st16(sm.k8[buf], t + 256, kK8Stride, s.k1);
+    st16(sm.vt[buf], t, kVtStride, s.v0);
+    st16(sm.vt[buf], t + 256, kVtStride, s.v1);
+    st16(sm.vt[buf], t + 512, kVtStride, s.v2);
+    st16(sm.vt[buf], t + 768, kVtStride, s.v3);
 }
 
 // S^T (64 keys x 32 queries) in int8: two 32x32 tiles, K = 128 in 4 steps.
-__device__ inline void st_int8(const Smem& sm, const intx4 (&qb)[4], intx16 (&s)[2]) {
+__device__ inline void st_int8(const int8_t* k8, const intx4 (&qb)[4], intx16 (&s)[2]) {
     const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         intx16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const intx4 a = *reinterpret_cast<const intx4*>(sm.k8 + (32 * tt + m) * kK8Stride + 32 * ks + 16 * hf);
+            const intx4 a = *reinterpret_cast<const intx4*>(k8 + (32 * tt + m) * kK8Stride + 32 * ks + 16 * hf);
             acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qb[ks], acc, 0, 0, 0);
         }
         s[tt] = acc;
@@ -328,147 +350,158 @@ __device__ inline void st_16(const uint8_t* k16, const intx4 (&qb)[8], floatx16 
     }
 }
 
-// O^T += V^T P^T for one 64-key block. P^T step j covers S^T tile j/2,
-// registers 8*(j%2) .. +7 (keys 16*(j%2) + {4hf..4hf+3, 8+4hf..8+4hf+3} of
-// that tile); the V^T operand reads the same keys for channel 32*ct + m.
-__device__ inline void pv_block(const uint8_t* vt, const float (&p)[2][16], floatx16 (&o)[4]) {
+// O^T += V^T P^T for one 64-key block. Step j covers keys 16j..16j+15: the
+// P^T operand is registers 8*(j%2)..+7 of S^T tile j/2 (keys 16j + 4hf +
+// {0..3, 8..11}); the V^T block stores each 16-key group in the order
+// (0-3, 8-11, 4-7, 12-15) so lane half hf reads its 8 keys with one 128-bit load.
+__device__ inline void pv_block(const uint8_t* vt, const halfx8 (&pb)[4], floatx16 (&o)[4]) {
     const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
-    halfx8 pb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[j][e] = (_Float16)p[j >> 1][8 * (j & 1) + e];
-    }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-        const uint8_t* row = vt + (32 * ct + m) * kVtStride;
+        const uint8_t* row = vt + (32 * ct + m) * kVtStride + 16 * hf;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int key0 = 32 * (j >> 1) + 16 * (j & 1) + 4 * hf;
-            const uint2 lo = *reinterpret_cast<const uint2*>(row + 2 * key0);
-            const uint2 hi = *reinterpret_cast<const uint2*>(row + 2 * (key0 + 8));
-            const intx4 a = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+            const intx4 a = *reinterpret_cast<const intx4*>(row + 32 * j);
             o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a), pb[j], o[ct], 0, 0, 0);
         }
     }
 }
 
-// Online softmax update of one block: x[tt][r] are log2-domain scores
-// (-inf for masked); updates m, l (this lane's half), rescales o, returns p.
-__device__ inline void softmax_block(float (&x)[2][16], float& m, float& l, floatx16 (&o)[4]) {
-    float bm = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) bm = fmaxf(bm, x[tt][r]);
-    {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
-        bm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    if (bm > m) {
-        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - bm);
-        m = bm;
+__device__ inline float swap_max(float v) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ inline int swap_max_i(int v) {
+    auto sw = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return max((int)sw[0], (int)sw[1]);
+}
+
+// Lazy online-softmax reference: p = 2^(x - m_ref) is used as long as the
+// block maximum stays within 2^kLazy of m_ref (p < 2^8 fits fp16); when it
+// grows further the reference moves to the new maximum and l, o are rescaled
+// (a wave-uniform branch taken rarely after the first blocks).
+__device__ inline void lazy_rescale(float bm, float& m_ref, float& l, floatx16 (&o)[4]) {
+    const bool grow = bm > m_ref + kLazy;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mn = grow ? bm : m_ref;
+        const float alpha = (!grow) ? 1.0f : (m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - mn));
+        m_ref = mn;
         l *= alpha;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
     }
+}
+
+__device__ inline uint32_t pack_h2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, half2_t{(_Float16)a, (_Float16)b});
+}
+
+// p (fp32, >= 0) -> fp16 P^T operands; l += sum of the rounded values.
+__device__ inline void pack_p(const float (&p)[2][16], halfx8 (&pb)[4], float& l) {
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            w[e] = pack_h2(p[j >> 1][8 * (j & 1) + 2 * e], p[j >> 1][8 * (j & 1) + 2 * e + 1]);
+            l = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[e]), ones, l, false);
+        }
+        const intx4 v = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        pb[j] = __builtin_bit_cast(halfx8, v);
+    }
+}
+
+// Softmax step of a block given log2-domain scores x (-inf = masked).
+__device__ inline void softmax_x(float (&x)[2][16], float& m_ref, float& l, floatx16 (&o)[4], halfx8 (&pb)[4]) {
+    float bm = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pv = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[tt][r] - m);
-            x[tt][r] = pv;
-            l += pv;
+        for (int r = 0; r < 16; ++r) bm = fmaxf(bm, x[tt][r]);
+    bm = swap_max(bm);
+    lazy_rescale(bm, m_ref, l, o);
+    const float mr = m_ref == -INFINITY ? 0.0f : m_ref;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[tt][r] = __builtin_amdgcn_exp2f(x[tt][r] - mr);
+    pack_p(x, pb, l);
+}
+
+// Wave64 lane mask of the lanes whose S^T element r = 4a + b (tile tt)
+// holds a selected key: lane half 0 holds key 32tt + 8a + b, half 1 key
+// 32tt + 8a + 4 + b; `byte` = the 8 selection bits of keys 32tt + 8a ... +7.
+__device__ inline uint64_t elem_lanes(uint32_t byte, int b) {
+    return (((byte >> b) & 1u) ? 0x00000000FFFFFFFFull : 0ull) | (((byte >> (4 + b)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
+}
+
+// v = sentinel on the elements of selected keys. The tests on the selection
+// bits are scalar, so only 8-key groups that hold a selected key cost VALU
+// work (one v_cndmask per element with a scalar lane mask).
+template <typename V, typename A>
+__device__ inline void mask_selected(uint64_t selbits, A (&v)[2], V sentinel) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const uint32_t byte = (uint32_t)(selbits >> (32 * tt + 8 * a)) & 0xFFu;
+            if (byte) {
+#pragma unroll
+                for (int b4 = 0; b4 < 4; ++b4)
+                    v[tt][4 * a + b4] = __builtin_amdgcn_inverse_ballot_w64(elem_lanes(byte, b4)) ? sentinel
+                                                                                                  : v[tt][4 * a + b4];
+            }
         }
 }
 
 template <bool F16>
-__global__ __launch_bounds__(256) void k_pf_attn(PfParams p) {
+__global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
     __shared__ Smem sm;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m_ = lane & 31, hf = lane >> 5;
-    // heavy (late) query blocks first
-    const int qb = (int)gridDim.x - 1 - (int)blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int g = h / p.G, bg = b * p.Hkv + g;
+    // Workgroup order: consecutive ids cycle over (b, KV head) first, so the
+    // XCD that a workgroup lands on (id mod 8) sees one KV head's key
+    // blocks; query blocks are taken latest (heaviest) first.
+    const int nqb = (p.T + kBM - 1) / kBM;
+    const int BG = p.B * p.Hkv;
+    const int id = blockIdx.x;
+    const int bg = id % BG;
+    const int rest = id / BG;
+    const int hh = rest % p.G;
+    const int qb = nqb - 1 - rest / p.G;
+    const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const int h = g * p.G + hh;
     const int i0 = qb * kBM;
-    if (i0 >= p.T) return;
     const int W = p.W;
     const size_t Tp = (size_t)p.nblk * kBN;
-    // this wave's 32 queries; lane's query column
     const int qrow0 = i0 + 32 * wave;
     const int qi = qrow0 + m_;
     const bool qvalid = qi < p.T;
-    // B operands: Q8 (16 B per k-step) and 16-bit Q (16 B per k-step)
-    intx4 q8b[4], q16b[8];
-    {
-        const int8_t* q8 = p.q8 + (((size_t)b * p.Hq + h) * Tp + (size_t)(qvalid ? qi : 0)) * kD;
-        const uint16_t* q16 = p.q + (((size_t)b * p.Hq + h) * p.T + (size_t)(qvalid ? qi : 0)) * kD;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) q8b[ks] = *reinterpret_cast<const intx4*>(q8 + 32 * ks + 16 * hf);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const intx4 z = {0, 0, 0, 0};
-            q16b[ks] = qvalid ? *reinterpret_cast<const intx4*>(q16 + 16 * ks + 8 * hf) : z;
-        }
-    }
-    const float sq = p.sq[((size_t)b * p.Hq + h) * p.nblk + min(qrow0 >> 6, p.nblk - 1)];
     const float c16 = p.c16;
-    float m = -INFINITY, l = 0.f;
+    const float sq = p.sq[((size_t)b * p.Hq + h) * p.nblk + min(qrow0 >> 6, p.nblk - 1)];
+
+    float m_ref = -INFINITY, l = 0.f;
     floatx16 o[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) o[ct] = floatx16{};
+    halfx8 pb[4];
 
-    const int nkb = min(p.nblk, (i0 + kBM + kBN - 1) / kBN);  // key blocks with keys <= last row
-    // key blocks kb < kb_band are entirely below the window band for all rows
-    const int kb_band = max(0, (i0 - W + 1) / kBN);  // first block that may touch i - j < W
-    for (int kb = 0; kb < nkb; ++kb) {
-        const bool band = kb >= kb_band;
-        __syncthreads();
-        copy_k8(sm, p.k8 + ((size_t)bg * Tp + (size_t)kb * kBN) * kD);
-        copy_vt(sm, p.vt + ((size_t)bg * p.nblk + kb) * kD * kBN);
-        if (band) copy_k16(sm, p.k + ((size_t)bg * p.T + (size_t)kb * kBN) * kD, min(kBN, p.T - kb * kBN));
-        __syncthreads();
-        intx16 si[2];
-        st_int8(sm, q8b, si);
-        const float c8 = sq * p.sk[(size_t)bg * p.nblk + kb] * c16;
-        const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
-        float x[2][16];
-        if (!band) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 32 * tt + st_key(r, hf);
-                    const bool sel = (selbits >> key) & 1ull;
-                    x[tt][r] = sel ? -INFINITY : (float)si[tt][r] * c8;
-                }
-        } else {
-            floatx16 sb[2];
-            st_16<F16>(sm.k16, q16b, sb);
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kl = 32 * tt + st_key(r, hf);
-                    const int j = kb * kBN + kl;
-                    const bool sel = (selbits >> kl) & 1ull;
-                    const bool hi = sel || (qi - j < W);
-                    float val = hi ? sb[tt][r] * c16 : (float)si[tt][r] * c8;
-                    if (j > qi || j >= p.T || !qvalid) val = -INFINITY;
-                    x[tt][r] = val;
-                }
-        }
-        softmax_block(x, m, l, o);
-        pv_block(sm.vt, x, o);
-    }
-    // gathered selected columns strictly below the band of every row of the block
+    intx4 q8b[4];
     {
-        const int32_t* S = p.sel_idx + (size_t)bg * p.sel_stride;
+        const int8_t* q8 = p.q8 + (((size_t)b * p.Hq + h) * Tp + (size_t)(qvalid ? qi : 0)) * kD;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) q8b[ks] = *reinterpret_cast<const intx4*>(q8 + 32 * ks + 16 * hf);
+    }
+
+    const int nkb = min(p.nblk, (i0 + kBM + kBN - 1) / kBN);  // key blocks holding keys <= last row
+    const int kb_band = min(nkb, max(0, (i0 - W + 1) / kBN));  // blocks below it miss every row's band
+    const int32_t* S = p.sel_idx + (size_t)bg * p.sel_stride;
+    int nsel = 0;  // selected columns below kb_band * 64
+    {
         const int k = min(max(p.sel_count[bg], 0), p.sel_stride);
-        // columns j < kb_band * 64 are below the band for all rows of this block
         const int lim = kb_band * kBN;
         int lo = 0, hi = k;
         while (lo < hi) {
@@ -476,11 +509,57 @@ __global__ __launch_bounds__(256) void k_pf_attn(PfParams p) {
             if (S[mid] < lim) lo = mid + 1;
             else hi = mid;
         }
-        const int nsel = lo;
+        nsel = lo;
+    }
+
+    // ---- phase A: the blocks touching the window band / diagonal, and
+    // ---- phase B: gathered selected columns below the band (16-bit scores)
+    {
+        intx4 q16b[8];
+        {
+            const uint16_t* q16 = p.q + (((size_t)b * p.Hq + h) * p.T + (size_t)(qvalid ? qi : 0)) * kD;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const intx4 z = {0, 0, 0, 0};
+                q16b[ks] = qvalid ? *reinterpret_cast<const intx4*>(q16 + 16 * ks + 8 * hf) : z;
+            }
+        }
+        for (int kb = kb_band; kb < nkb; ++kb) {
+            __syncthreads();
+            stage_store(sm, 0, stage_load(p.k8 + ((size_t)bg * Tp + (size_t)kb * kBN) * kD,
+                                          p.vt + ((size_t)bg * p.nblk + kb) * kD * kBN));
+            copy_k16(sm.k16, p.k + ((size_t)bg * p.T + (size_t)kb * kBN) * kD, min(kBN, p.T - kb * kBN));
+            __syncthreads();
+            intx16 si[2];
+            st_int8(sm.k8[0], q8b, si);
+            floatx16 sb[2];
+            st_16<F16>(sm.k16, q16b, sb);
+            const float c8 = sq * p.sk[(size_t)bg * p.nblk + kb] * c16;
+            const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
+            float x[2][16];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kl = 32 * tt + st_key(r, hf);
+                    const int j = kb * kBN + kl;
+                    const bool hi = ((selbits >> kl) & 1ull) || (qi - j < W);
+                    float val = hi ? sb[tt][r] * c16 : (float)si[tt][r] * c8;
+                    if (j > qi || j >= p.T || !qvalid) val = -INFINITY;
+                    x[tt][r] = val;
+                }
+            softmax_x(x, m_ref, l, o, pb);
+            pv_block(sm.vt[0], pb, o);
+        }
         for (int tile = 0; tile * kBN < nsel; ++tile) {
             __syncthreads();
-            copy_k16(sm, p.ksel + ((size_t)bg * p.nsel_tiles + tile) * kBN * kD, kBN);
-            copy_vt(sm, p.vtsel + ((size_t)bg * p.nsel_tiles + tile) * kD * kBN);
+            copy_k16(sm.k16, p.ksel + ((size_t)bg * p.nsel_tiles + tile) * kBN * kD, kBN);
+            {
+                const int t = threadIdx.x;
+                const uint16_t* src = p.vtsel + ((size_t)bg * p.nsel_tiles + tile) * kD * kBN;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st16(sm.vt[0], t + 256 * i, kVtStride, ld16(src, t + 256 * i, 2 * kBN));
+            }
             __syncthreads();
             floatx16 sb[2];
             st_16<F16>(sm.k16, q16b, sb);
@@ -492,10 +571,52 @@ __global__ __launch_bounds__(256) void k_pf_attn(PfParams p) {
                     const int idx = tile * kBN + 32 * tt + st_key(r, hf);
                     x[tt][r] = (idx < nsel && qvalid) ? sb[tt][r] * c16 : -INFINITY;
                 }
-            softmax_block(x, m, l, o);
-            pv_block(sm.vt, x, o);
+            softmax_x(x, m_ref, l, o, pb);
+            pv_block(sm.vt[0], pb, o);
         }
     }
+
+    // ---- phase C: INT8 blocks below the band (selected columns dropped),
+    // ---- register-staged one block ahead into double-buffered LDS
+    if (kb_band > 0) {
+        const int8_t* k8base = p.k8 + (size_t)bg * Tp * kD;
+        const uint16_t* vtbase = p.vt + (size_t)bg * p.nblk * kD * kBN;
+        Stage st = stage_load(k8base, vtbase);
+        __syncthreads();
+        stage_store(sm, 0, st);
+        __syncthreads();
+        for (int kb = 0; kb < kb_band; ++kb) {
+            const int cur = kb & 1;
+            // the block after the last is a harmless reload of the last one
+            const int nx = min(kb + 1, kb_band - 1);
+            st = stage_load(k8base + (size_t)nx * kBN * kD, vtbase + (size_t)nx * kD * kBN);
+            intx16 si[2];
+            st_int8(sm.k8[cur], q8b, si);
+            const float c8 = sq * p.sk[(size_t)bg * p.nblk + kb] * c16;
+            const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
+            mask_selected(selbits, si, (int)INT_MIN);
+            int imax = INT_MIN;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) imax = max(imax, si[tt][r]);
+            imax = swap_max_i(imax);
+            const float bm = imax == INT_MIN ? -INFINITY : (float)imax * c8;
+            lazy_rescale(bm, m_ref, l, o);
+            const float nmr = m_ref == -INFINITY ? 0.0f : -m_ref;
+            float x[2][16];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[tt][r] = __builtin_amdgcn_exp2f(fmaf((float)si[tt][r], c8, nmr));
+            mask_selected(selbits, x, 0.0f);
+            pack_p(x, pb, l);
+            pv_block(sm.vt[cur], pb, o);
+            stage_store(sm, cur ^ 1, st);
+            __syncthreads();
+        }
+    }
+
     // combine the two lane halves of each query and write
     {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
@@ -509,13 +630,12 @@ __global__ __launch_bounds__(256) void k_pf_attn(PfParams p) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const int ch = 32 * ct + 8 * r4 + 4 * hf;
-            float4 v = make_float4(o[ct][4 * r4] * inv, o[ct][4 * r4 + 1] * inv, o[ct][4 * r4 + 2] * inv,
-                                   o[ct][4 * r4 + 3] * inv);
+            const float vv[4] = {o[ct][4 * r4] * inv, o[ct][4 * r4 + 1] * inv, o[ct][4 * r4 + 2] * inv,
+                                 o[ct][4 * r4 + 3] * inv};
             if (p.out_dt == HQ_F32) {
-                *reinterpret_cast<float4*>(p.out + orow + ch) = v;
+                *reinterpret_cast<float4*>(p.out + orow + ch) = make_float4(vv[0], vv[1], vv[2], vv[3]);
             } else {
                 uint16_t* o16 = reinterpret_cast<uint16_t*>(p.out) + orow + ch;
-                const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if (p.out_dt == HQ_F16) o16[e] = (uint16_t)f32_to_f16_bits(vv[e]);
@@ -572,12 +692,12 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, int32_t B
         k_pf_quant_q<true><<<dim3(w.nblk, Hq, B), 256, 0, s>>>(p);
         k_pf_quant_kv<true><<<dim3(w.nblk, Hkv, B), 256, 0, s>>>(p);
         k_pf_gather_sel<true><<<dim3(w.nsel_tiles, Hkv, B), 256, 0, s>>>(p);
-        k_pf_attn<true><<<dim3((T + kBM - 1) / kBM, Hq, B), 256, 0, s>>>(p);
+        k_pf_attn<true><<<dim3(((T + kBM - 1) / kBM) * Hq * B), 256, 0, s>>>(p);
     } else {
         k_pf_quant_q<false><<<dim3(w.nblk, Hq, B), 256, 0, s>>>(p);
         k_pf_quant_kv<false><<<dim3(w.nblk, Hkv, B), 256, 0, s>>>(p);
         k_pf_gather_sel<false><<<dim3(w.nsel_tiles, Hkv, B), 256, 0, s>>>(p);
-        k_pf_attn<false><<<dim3((T + kBM - 1) / kBM, Hq, B), 256, 0, s>>>(p);
+        k_pf_attn<false><<<dim3(((T + kBM - 1) / kBM) * Hq * B), 256, 0, s>>>(p);
     }
     return hipGetLastError();
 }
