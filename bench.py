@@ -46,6 +46,8 @@ def _args():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only append+decode per step (profiling aid)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill probe + attention per step and print its fields (profiling aid)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain device copy of this size (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -229,6 +231,35 @@ def cpu_baseline_prefill(pin, sel_idx, sel_cnt, budget_s=8.0):
                       f"({t_rows:.1f} s) plus one head's INT8 stage, scaled to {sp.T} rows x {sp.Hq} heads"}
 
 
+def prefill_only(args):
+    """Probe + hybrid prefill attention on the 16K workload only."""
+    import torch
+    import kv_cache_amd as hq
+    from synth.inputs import CONFIGS, make_prefill_inputs
+    dev = "cuda:0"
+    pspec = CONFIGS["c4_prefill_8b_16k"]
+    pin = make_prefill_inputs(pspec)
+    q, k, v = (_dev16(x, "bf16", dev) for x in (pin.q, pin.k, pin.v))
+    lens = torch.full((1,), pspec.T, dtype=torch.int32, device=dev)
+    qprobe = q[:, :, pspec.T - 64:].contiguous()
+    out = torch.empty((1, pspec.Hq, pspec.T, 128), dtype=torch.float32, device=dev)
+    pol = hq.Policy()
+    tm = Timer()
+    col, sel, cnt, thr = hq.probe_select(qprobe, k, lens, pol)
+    for _ in range(args.warmup):
+        hq.prefill_attn(q, k, v, sel, cnt, pol, None, out)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        tm("prefill_attn", hq.prefill_attn, q, k, v, sel, cnt, pol, None, out)
+    torch.cuda.synchronize()
+    pms = tm.ms("prefill_attn")
+    res = {"prefill_ms": round(pms, 3),
+           "prefill_TFLOPs": round(prefill_flops(pspec.T, pspec.Hq) / (pms * 1e-3) / 1e12, 1),
+           "prefill_roofline": prefill_roofline(pspec.T, pol.window, sel.cpu().numpy(), cnt.cpu().numpy(),
+                                                pspec.Hq // pspec.Hkv, pms)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -252,6 +283,8 @@ def main():
         print(json.dumps({"calib_copy_bytes": n}))
         return
 
+    if args.prefill_only:
+        return prefill_only(args)
     t_gen = time.perf_counter()
     spec = CONFIGS["c2_decode_8b_32k"]
     inp = make_decode_inputs(spec)

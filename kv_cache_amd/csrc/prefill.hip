@@ -283,6 +283,11 @@ __device__ inline void copy_k16(uint8_t* dst, const uint16_t* src, int rows_vali
     }
 }
 
+template <int N>
+struct IConst {
+    static constexpr int value = N;
+};
+
 // Register staging of one INT8 K block (8 KB) and one fp16 V^T block (16 KB):
 // thread t moves 16-byte chunks e = t + 256 i (row e / 8, column chunk e % 8).
 struct Stage {
@@ -348,6 +353,34 @@ __device__ inline void st_16(const uint8_t* k16, const intx4 (&qb)[8], floatx16 
         }
         s[tt] = acc;
     }
+}
+
+// One 32-key S^T tile (keys 32tt..32tt+31) of the int8 / 16-bit products.
+__device__ inline intx16 st_int8_tile(const int8_t* k8, const intx4 (&qb)[4], int tt) {
+    const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
+    intx16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const intx4 a = *reinterpret_cast<const intx4*>(k8 + (32 * tt + m) * kK8Stride + 32 * ks + 16 * hf);
+        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qb[ks], acc, 0, 0, 0);
+    }
+    return acc;
+}
+template <bool F16>
+__device__ inline floatx16 st_16_tile(const uint8_t* k16, const intx4 (&qb)[8], int tt) {
+    const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
+    floatx16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const intx4 a = *reinterpret_cast<const intx4*>(k16 + (32 * tt + m) * kK16Stride + 2 * (16 * ks + 8 * hf));
+        if constexpr (F16)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, qb[ks]),
+                                                         acc, 0, 0, 0);
+        else
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
+    }
+    return acc;
 }
 
 // O^T += V^T P^T for one 64-key block. Step j covers keys 16j..16j+15: the
@@ -530,24 +563,23 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
                                           p.vt + ((size_t)bg * p.nblk + kb) * kD * kBN));
             copy_k16(sm.k16, p.k + ((size_t)bg * p.T + (size_t)kb * kBN) * kD, min(kBN, p.T - kb * kBN));
             __syncthreads();
-            intx16 si[2];
-            st_int8(sm.k8[0], q8b, si);
-            floatx16 sb[2];
-            st_16<F16>(sm.k16, q16b, sb);
             const float c8 = sq * p.sk[(size_t)bg * p.nblk + kb] * c16;
             const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
             float x[2][16];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < 2; ++tt) {
+                const intx16 si = st_int8_tile(sm.k8[0], q8b, tt);
+                const floatx16 sb = st_16_tile<F16>(sm.k16, q16b, tt);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kl = 32 * tt + st_key(r, hf);
                     const int j = kb * kBN + kl;
                     const bool hi = ((selbits >> kl) & 1ull) || (qi - j < W);
-                    float val = hi ? sb[tt][r] * c16 : (float)si[tt][r] * c8;
+                    float val = hi ? sb[r] * c16 : (float)si[r] * c8;
                     if (j > qi || j >= p.T || !qvalid) val = -INFINITY;
                     x[tt][r] = val;
                 }
+            }
             softmax_x(x, m_ref, l, o, pb);
             pv_block(sm.vt[0], pb, o);
         }
@@ -576,44 +608,94 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
         }
     }
 
-    // ---- phase C: INT8 blocks below the band (selected columns dropped),
-    // ---- register-staged one block ahead into double-buffered LDS
+    // ---- phase C: INT8 blocks below the band (selected columns dropped).
+    // Software pipeline per wave: the QK MFMAs of block kb+1 are issued
+    // before the softmax of block kb, so the matrix cores and the VALU work
+    // of one wave overlap. LDS: K8 of block kb in K slot kb%2, V^T of block
+    // kb in V slot kb%2; iteration kb loads K8[kb+2] and V^T[kb+1] into
+    // registers (buffer loads with scalar offsets) and stores them into the
+    // slots freed by the previous iteration; one barrier per iteration.
     if (kb_band > 0) {
-        const int8_t* k8base = p.k8 + (size_t)bg * Tp * kD;
-        const uint16_t* vtbase = p.vt + (size_t)bg * p.nblk * kD * kBN;
-        Stage st = stage_load(k8base, vtbase);
+        const int t = threadIdx.x;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.k8 + (size_t)bg * Tp * kD), (short)0, kb_band * kBN * kD, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.vt + (size_t)bg * p.nblk * kD * kBN), (short)0, kb_band * kD * kBN * 2, 0x00020000);
+        const int voff = 16 * t;  // chunk t of a block; rows of K8 and V^T are both 128 bytes
+        auto ld = [&](const __amdgpu_buffer_rsrc_t& r, int soff) {
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+        };
+        __syncthreads();  // the band phases are done with LDS
+        {
+            stage_store(sm, 0, Stage{ld(rk, 0), ld(rk, 4096), ld(rv, 0), ld(rv, 4096), ld(rv, 8192), ld(rv, 12288)});
+            if (kb_band > 1) {
+                st16(sm.k8[1], t, kK8Stride, ld(rk, 8192));
+                st16(sm.k8[1], t + 256, kK8Stride, ld(rk, 8192 + 4096));
+            }
+        }
         __syncthreads();
-        stage_store(sm, 0, st);
-        __syncthreads();
-        for (int kb = 0; kb < kb_band; ++kb) {
-            const int cur = kb & 1;
-            // the block after the last is a harmless reload of the last one
-            const int nx = min(kb + 1, kb_band - 1);
-            st = stage_load(k8base + (size_t)nx * kBN * kD, vtbase + (size_t)nx * kD * kBN);
-            intx16 si[2];
-            st_int8(sm.k8[cur], q8b, si);
+        intx16 sA[2], sB[2];
+        st_int8(sm.k8[0], q8b, sA);
+        __syncthreads();  // every wave has read K slot 0 before iteration 0 refills it
+
+        auto step = [&](auto P, intx16 (&sc)[2], intx16 (&sn)[2], int kb) {
+            constexpr int cur = decltype(P)::value;
+            const int kn2 = min(kb + 2, kb_band - 1), kn1 = min(kb + 1, kb_band - 1);
+            const uint4 k0 = ld(rk, kn2 * 8192), k1 = ld(rk, kn2 * 8192 + 4096);
+            const uint4 v0 = ld(rv, kn1 * 16384), v1 = ld(rv, kn1 * 16384 + 4096);
+            const uint4 v2 = ld(rv, kn1 * 16384 + 8192), v3 = ld(rv, kn1 * 16384 + 12288);
+            if (kb + 1 < kb_band) st_int8(sm.k8[cur ^ 1], q8b, sn);
             const float c8 = sq * p.sk[(size_t)bg * p.nblk + kb] * c16;
             const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
-            mask_selected(selbits, si, (int)INT_MIN);
-            int imax = INT_MIN;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) imax = max(imax, si[tt][r]);
-            imax = swap_max_i(imax);
-            const float bm = imax == INT_MIN ? -INFINITY : (float)imax * c8;
-            lazy_rescale(bm, m_ref, l, o);
-            const float nmr = m_ref == -INFINITY ? 0.0f : -m_ref;
+            // No block maximum on the common path: p = 2^(s - m_ref) with the
+            // reference from the earlier blocks (the band and the selected
+            // columns come first, so it is normally the row maximum already).
+            // Only if some p of the block reaches 2^15 (the block sum shows
+            // it, and catches inf) is the maximum taken and the state rescaled.
             float x[2][16];
+            float lb = 0.0f;
+            {
+                const float nmr = m_ref == -INFINITY ? 0.0f : -m_ref;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) x[tt][r] = __builtin_amdgcn_exp2f(fmaf((float)si[tt][r], c8, nmr));
-            mask_selected(selbits, x, 0.0f);
-            pack_p(x, pb, l);
+                    for (int r = 0; r < 16; ++r) x[tt][r] = __builtin_amdgcn_exp2f(fmaf((float)sc[tt][r], c8, nmr));
+                mask_selected(selbits, x, 0.0f);
+                pack_p(x, pb, lb);
+            }
+            if (__builtin_amdgcn_ballot_w64(!(lb <= 32768.0f))) {
+                mask_selected(selbits, sc, (int)INT_MIN);
+                int imax = INT_MIN;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) imax = max(imax, sc[tt][r]);
+                imax = swap_max_i(imax);
+                const float bm = imax == INT_MIN ? -INFINITY : (float)imax * c8;
+                lazy_rescale(bm, m_ref, l, o);
+                const float nmr = m_ref == -INFINITY ? 0.0f : -m_ref;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        x[tt][r] = sc[tt][r] == INT_MIN ? 0.0f : __builtin_amdgcn_exp2f(fmaf((float)sc[tt][r], c8, nmr));
+                lb = 0.0f;
+                pack_p(x, pb, lb);
+            }
+            l += lb;
             pv_block(sm.vt[cur], pb, o);
-            stage_store(sm, cur ^ 1, st);
+            st16(sm.k8[cur], t, kK8Stride, k0);
+            st16(sm.k8[cur], t + 256, kK8Stride, k1);
+            st16(sm.vt[cur ^ 1], t, kVtStride, v0);
+            st16(sm.vt[cur ^ 1], t + 256, kVtStride, v1);
+            st16(sm.vt[cur ^ 1], t + 512, kVtStride, v2);
+            st16(sm.vt[cur ^ 1], t + 768, kVtStride, v3);
             __syncthreads();
+        };
+        for (int kb = 0; kb < kb_band; kb += 2) {
+            step(IConst<0>{}, sA, sB, kb);
+            if (kb + 1 >= kb_band) break;
+            step(IConst<1>{}, sB, sA, kb + 1);
         }
     }
 
