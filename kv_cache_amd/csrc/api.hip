@@ -93,7 +93,7 @@ hq_status hip_fail(const char* fn, hipError_t e) {
 int32_t decode_tps() {
     const char* s = std::getenv("HQ_DECODE_TPS");
     int v = s ? std::atoi(s) : 0;
-    return v > 0 ? v : 16;
+    return v > 0 ? v : 43;
 }
 
 }  // namespace
@@ -217,7 +217,7 @@ hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_n
 size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq) {
     if (!cache || cache->Hkv < 1 || Hq < 1 || Hq % cache->Hkv) return 0;
     const int32_t tps = decode_tps();
-    const int32_t nsplit = (hq::decode_max_tiles(*cache) + tps - 1) / tps;
+    const int32_t nsplit = hq::decode_nsplit(*cache, tps);
     return hq::decode_ws_bytes(*cache, Hq, nsplit);
 }
 
@@ -238,7 +238,7 @@ hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float
     d.Hq = Hq;
     d.G = Hq / cache->Hkv;
     d.tiles_per_split = decode_tps();
-    d.nsplit = (hq::decode_max_tiles(*cache) + d.tiles_per_split - 1) / d.tiles_per_split;
+    d.nsplit = hq::decode_nsplit(*cache, d.tiles_per_split);
     d.sm_scale_log2 = sm_scale * 1.4426950408889634f;
     d.ws = ws;
     const size_t need = hq::decode_ws_bytes(*cache, Hq, d.nsplit);

@@ -76,6 +76,8 @@ __global__ __launch_bounds__(64) void k_append(hq_cache c, const uint16_t* k_new
             if (!overflow) {
                 const int n = n_q, tile = n / kTile, ts = n % kTile;
                 const size_t tb = ((size_t)bg * (c.cap_q / kTile) + tile) * kTileBytesQ;
+                const size_t mb = ((size_t)bg * (c.cap_q / kTile) + tile) * (kTile * 16);
+                __shared__ uint32_t vwords[4][4];  // canonical V words of the departing token
                 if (lane < 8) {
                     const bool isv = lane >= 4;
                     const int grp = lane & 3;
@@ -85,21 +87,30 @@ __global__ __launch_bounds__(64) void k_append(hq_cache c, const uint16_t* k_new
                     for (int i = 0; i < 4; ++i) unpack8<F16>(src[4 * grp + i], x + 8 * i);
                     uint32_t pk[4], sb, zb;
                     int4_quant_group(x, pk, sb, zb);
-                    const size_t slot_g = (size_t)bg * c.cap_q + n;
                     if (!isv) {
-                        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(c.k_codes) + tb + kcode_off(ts, grp)) =
-                            make_uint4(pk[0], pk[1], pk[2], pk[3]);
-                        reinterpret_cast<uint32_t*>(c.k_meta)[slot_g * 4 + grp] = sb | (zb << 16);
-                    } else {
-                        uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + tb;
-                        const int P = ts & 31, half = ts >> 5;  // pairs are slots (P, P + 32)
+                        uint8_t* kc = reinterpret_cast<uint8_t*>(c.k_codes) + tb;
 #pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const uint16_t bits = (uint16_t)((pk[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
-                            *reinterpret_cast<uint16_t*>(vc + vcode_off(P, 8 * grp + q) + 2 * half) = bits;
-                        }
-                        reinterpret_cast<uint32_t*>(c.v_meta)[slot_g * 4 + grp] = sb | (zb << 16);
+                        for (int w = 0; w < 4; ++w)
+                            *reinterpret_cast<uint32_t*>(kc + kq_word(ts, kGroup * grp + 8 * w)) = to_mf_order(pk[w]);
+                        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(c.k_meta) + mb + kmeta_word(ts, grp)) =
+                            sb | (zb << 16);
+                    } else {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) vwords[grp][w] = pk[w];
+                        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(c.v_meta) + mb + vmeta_word(ts, grp)) =
+                            sb | (zb << 16);
                     }
+                }
+                __syncthreads();
+                // each V word holds 8 slots of one channel: replace this slot's nibble
+                uint8_t* vc = reinterpret_cast<uint8_t*>(c.v_codes) + tb;
+                const int sh = mf_nib(ts & 7);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int ch = lane + 64 * i;
+                    const uint32_t code = (vwords[ch >> 5][(ch >> 3) & 3] >> (4 * (ch & 7))) & 0xFu;
+                    uint32_t* wp = reinterpret_cast<uint32_t*>(vc + vq_word(ts, ch));
+                    *wp = (*wp & ~(0xFu << sh)) | (code << sh);
                 }
                 if (lane == 0) c.q_pos[(size_t)bg * c.cap_q + n] = d;
                 n_q += 1;

@@ -8,35 +8,36 @@
 // expanded first). The low-bit and 16-bit paths share one online-softmax
 // state ("HyQuant: ...", "How this relates to prior wiki pages").
 //
-// Design (MI355X, wave64, HBM-bound, VALU-heavy):
-//  * One workgroup = 4 waves = one (b, g) and a contiguous span of 64-token
-//    tiles (a split); every wave takes every 4th tile of the span. All G query
-//    heads of the KV head are processed together, so each cache byte is read
-//    once per step.
-//  * Token phase, lane = token: the lane loads its token's 64 B of K codes
-//    (4 x 128-bit, contiguous across the wave) and its K and V scales/zeros.
-//    Codes become bf16 (or fp16) "128 + 8c" magic values with one shift + one
-//    and-or per pair and meet the query in v_dot2 (exact products, fp32
-//    accumulation); the group's scale and zero are applied afterwards:
-//    q.k~ = s * (q/8 . (128 + 8c)) + (z - 16 s) * sum(q). Query pairs are
-//    uniform and live in scalar registers.
-//  * Online softmax per tile in log2 units (v_exp_f32) with a lazy rescale
-//    (only when the running max grows by more than 2^8); wave maxima use DPP
-//    and v_permlane16/32_swap, no LDS.
-//  * PV on INT4 tiles: the V codes are stored pre-paired, slot t with slot
-//    t + 32, so the weights w = p * s * 2^-E of the two tokens form one fp16
-//    pair (one v_permlane32_swap); the channel-phase lane (8 channels x 16
-//    tokens) turns each code pair into fp16 "1024 + c" / "64 + c" magic
-//    values with one v_bfi_b32 and accumulates with v_dot2_f32_f16 in fp32. E is a running power-of-two
-//    scale (exact rescale when it grows) keeping every w below 2^15, so the
-//    fp16 weights stay finite and normal down to p*s ~ 2^-29 of the bound.
-//    The magic bias is removed exactly with the sum of the same fp16 weights;
-//    sum(p*z) accumulates in fp32 in the token phase.
-//  * 16-bit tiles (kept columns, window ring) use fp32 FMAs on the 16-bit
-//    rows.
+// Design (MI355X, wave64). One workgroup = 4 waves = one (b, g) and a
+// contiguous span of 64-token tiles (a split); every wave takes every 4th
+// tile of the span. All G query heads of the KV head are processed together,
+// so each cache byte is read once per step.
+//
+// INT4 tiles run on the matrix cores: with G query heads per KV head, QK and
+// PV of a tile are small dense products, and on gfx950 a 16x16x32 fp16 MFMA
+// does the work of ~64 VALU dot2 instructions in a sixteenth of their issue
+// time even with 12 of its 16 columns idle. The codes are dequantized in
+// registers, never written back:
+//  * QK: D[4j+h][t] = sum over group j of q'_h[c] * (bias_c + code[t][c]),
+//    with A = the query (row 4j+h is head h restricted to group j, so the 16
+//    rows cover 4 groups x 4 heads and one accumulator holds the per-group
+//    partial dots) and B = the K codes turned into fp16 "1024 + c" / "64 + c"
+//    values by one and-or per register (plus one shift per word). The
+//    accumulator starts at -sum(q' * bias); the group's scale and zero are
+//    applied per (token, group) lane, the four groups are summed through an
+//    LDS transpose that lands one token per lane for the softmax. q' is the
+//    query scaled per head by a power of two into fp16 range (exact).
+//  * Online softmax per tile in log2 units with a lazy rescale (only when
+//    the running max grows by more than 2^8).
+//  * PV: D[c][h] += sum_t (bias_t + code[t][c]) * w[t][h] with A = the V
+//    codes (same extraction) and B = fp16 weights w = p * s_v * 2^-E staged
+//    through LDS. E is a running power of two keeping every w below 2^15;
+//    the bias is removed exactly with the sum of the same fp16 weights and
+//    sum(p * z_v) is accumulated in fp32 per token.
+//  * 16-bit tiles (kept columns, window ring) use v_dot2 / fp32 FMAs on the
+//    16-bit rows (they are a few percent of the tiles).
 //  * Each workgroup writes one partial (m, l, o[128]) per head; a second
-//    kernel merges the splits of each (b, g) (split weights staged in LDS,
-//    coalesced partial reads).
+//    kernel merges the splits of each (b, g).
 #include "hq_internal.h"
 
 namespace hq {
@@ -45,75 +46,57 @@ namespace {
 constexpr int kWaves = 4;
 constexpr float kLazy = 8.0f;  // log2-domain growth that triggers a rescale
 
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
 struct DecodeParams {
     hq_cache c;
-    const uint32_t* qp;    // [B][Hkv][4][G][16]  pairs for the INT4 path (prescaled)
-    const uint32_t* qn;    // [B][Hkv][G][64]     natural pairs for the 16-bit path
-    const float* qsum;     // [B][Hkv][G][4]      per-group sum of q
+    const uint32_t* qa;    // [B][Hkv][NHB][4 ks][64 lanes][4] QK A operands (fp16 pairs)
+    const float* qc;       // [B][Hkv][NHB][4 j][4 r][2] (sum q' * bias, sum q') per group
+    const float* qsc;      // [B][Hkv][8] per-head 2^-k (q' = q * 2^k)
+    const uint32_t* qn;    // [B][Hkv][G][64] natural pairs for the 16-bit path
     float* part_m;         // [B][Hkv][nsplit][G]
     float* part_l;         // [B][Hkv][nsplit][G]
     float* part_o;         // [B][Hkv][nsplit][G][128]
     int32_t nsplit, tps, G;
+    int32_t nsq, tps16;    // INT4 splits (first nsq partials), tiles per 16-bit split
     float scale2;          // sm_scale * log2(e)
 };
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 template <bool F16>
 __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
     if constexpr (F16)
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
-                                      false);
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
     else
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                               __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-__device__ inline float dot2h(uint32_t a, uint32_t b, float c) { return dot2<true>(a, b, c); }
-
-// (a & mask) | c for c & mask == 0, in one v_bfi_b32 with register constants
-// (a VOP3 op cannot take two literals, so the compiler would otherwise emit and + or).
-__device__ inline uint32_t bfi(uint32_t mask, uint32_t a, uint32_t c) {
-    uint32_t r;
-    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(c));
-    return r;
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                               false);
 }
 
-// Four magic-biased code pairs from one dword of 8 nibbles (channels 8i+n) for
-// the QK dot products. Pair n holds channels (n, n+4). bf16: value 128 + 8c
-// (code in bits 3..6); fp16: value 1024 + 16c (code in bits 4..7).
-template <bool F16>
-__device__ inline void extract_pairs(uint32_t w, uint32_t* pr, uint32_t M, uint32_t C) {
-    if constexpr (F16) {
-        pr[0] = bfi(M, w << 4, C);
-        pr[1] = bfi(M, w, C);
-        pr[2] = bfi(M, w >> 4, C);
-        pr[3] = bfi(M, w >> 8, C);
-    } else {
-        pr[0] = bfi(M, w << 3, C);
-        pr[1] = bfi(M, w >> 1, C);
-        pr[2] = bfi(M, w >> 5, C);
-        pr[3] = bfi(M, w >> 9, C);
-    }
+__device__ inline uint32_t u4w(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
+// The 8 codes of one operand word -> fp16 operand registers (elements 2k, 2k+1
+// in register k): nibbles at bits 0..3 of a half read 1024 + c (magic 0x6400),
+// at bits 4..7 read 64 + c (magic 0x5400). The masks and magics are passed in
+// VGPRs so that each register is one v_and_or_b32 (a VOP3 instruction can
+// read only one literal constant).
+struct CodeConsts {
+    uint32_t m_lo, m_hi, c_lo, c_hi;
+};
+__device__ inline CodeConsts code_consts() {
+    CodeConsts k{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+    asm("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.c_lo), "+v"(k.c_hi));
+    return k;
 }
-// The V-code word of slots (P, P+32), channels 4Q+n: fp16 magic pairs with
-// one bfi each (and one shift for n >= 2). Even channels (code in bits 0..3)
-// read 1024 + c with magic 0x6400, odd channels (bits 4..7) read 64 + c with
-// magic 0x5400: every channel carries the code with factor 1.
-__device__ inline void extract_vpairs(uint32_t d, uint32_t* cp, uint32_t M_lo, uint32_t M_hi, uint32_t C_lo,
-                                      uint32_t C_hi) {
+__device__ inline halfx8 codes_to_f16(uint32_t d, const CodeConsts& k) {
     const uint32_t d8 = d >> 8;
-    cp[0] = bfi(M_lo, d, C_lo);
-    cp[1] = bfi(M_hi, d, C_hi);
-    cp[2] = bfi(M_lo, d8, C_lo);
-    cp[3] = bfi(M_hi, d8, C_hi);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = {(d & k.m_lo) | k.c_lo, (d & k.m_hi) | k.c_hi, (d8 & k.m_lo) | k.c_lo, (d8 & k.m_hi) | k.c_hi};
+    return __builtin_bit_cast(halfx8, v);
 }
-template <bool F16>
-constexpr float kBias = F16 ? 64.0f : 16.0f;
-
-__device__ inline uint32_t u4w(const uint4& v, int i) {
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
+// Magic bias of operand element e (= slot or channel index mod 8).
+__device__ inline float elem_bias(int e) { return (e & 2) ? 64.0f : 1024.0f; }
 
 template <int CTRL>
 __device__ inline float dppmov(float v) {
@@ -129,11 +112,6 @@ __device__ inline float wave_max_fast(float v) {
     v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
     auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-}
-// Lanes 0..31 receive the value of lane l + 32 (lanes 32..63 get junk).
-__device__ inline float upper_half(float v) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[1]);
 }
 template <int CTRL>
 __device__ inline float dpp_add(float v) { return v + dppmov<CTRL>(v); }
@@ -154,6 +132,15 @@ __device__ inline void lds_fence() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// v[idx] for a lane-dependent idx < N without dynamic register indexing.
+template <int N>
+__device__ inline float pick(const float (&v)[N], int idx) {
+    float r = v[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) r = idx == i ? v[i] : r;
+    return r;
+}
+
 __device__ inline void store_out(void* out, int dt, size_t i, float r) {
     if (dt == HQ_F32)
         static_cast<float*>(out)[i] = r;
@@ -166,17 +153,38 @@ __device__ inline void store_out(void* out, int dt, size_t i, float r) {
     }
 }
 
-template <int G, bool F16>
-__global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
-    // fp16 weight pairs of the INT4 tile: word (pair P, group g, head h) at
-    // P*4G + ((g ^ (P/8 % 4)) * G) + h
-    __shared__ uint32_t lds_pw[kWaves][32 * 4 * G];
-    __shared__ float lds_p[kWaves][kTile * G];          // 16-bit tiles: p per token
-    __shared__ float lds_m[kWaves][G], lds_l[kWaves][G];
-    __shared__ float lds_o[kWaves][G][kD];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+// MODE 0: the INT4 tiles of a (b, g), split s = blockIdx.x covers tiles
+// [s*tps, (s+1)*tps); MODE 1: its 16-bit tiles (kept, then ring), split s
+// covers [s*tps16, ...) of them and writes partial nsq + s. Every workgroup
+// writes its partial (empty ones carry m = -inf).
+template <int G>
+struct SplitSmem {
+    static constexpr int NHB = (G + 3) / 4;
+    float4 y[kWaves][4 * NHB * 64];
+    __align__(16) uint16_t w[kWaves][4 * 2 * 4 * G * 8];
+    float p[kWaves][kTile * G];
+    float m[kWaves][G], l[kWaves][G];
+    float o[kWaves][G][kD];
+    uint4 qa[NHB * 4 * 64];
+};
+
+template <int G, bool F16, int MODE>
+__device__ __attribute__((always_inline)) inline void split_body(const DecodeParams& p, SplitSmem<G>& sm, int s) {
+    constexpr int NHB = (G + 3) / 4;  // 4-head blocks of the QK product
+    // per wave: QK partials y[block nb][head block][lane] (float4), the PV
+    // weights w[group][token half][token octet][head][8 slots] (fp16), the
+    // 16-bit tiles' p per token
+    auto& lds_y = sm.y;
+    auto& lds_w = sm.w;
+    auto& lds_p = sm.p;
+    auto& lds_m = sm.m;
+    auto& lds_l = sm.l;
+    auto& lds_o = sm.o;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
+    const int g = blockIdx.y, b = blockIdx.z;
     const int Hkv = p.c.Hkv, W = p.c.window;
     const int bg = b * Hkv + g;
     const int4 cnt = *reinterpret_cast<const int4*>(p.c.counts + 4 * bg);
@@ -185,103 +193,258 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
     const int nqt = (n_q + kTile - 1) / kTile, nkt = (n_keep + kTile - 1) / kTile;
     const int nwt = (nring + kTile - 1) / kTile;
     const int total = nqt + nkt + nwt;
-    const int v0 = s * p.tps;
-    if (v0 >= total) return;
-    const int v1 = min(v0 + p.tps, total);
+    const int v0 = MODE == 0 ? s * p.tps : nqt + s * p.tps16;
+    const int v1 = MODE == 0 ? min(v0 + p.tps, nqt) : min(v0 + p.tps16, total);
+    const int split_out = MODE == 0 ? s : p.nsq + s;
+    if (v0 >= v1) {  // nothing here: an empty partial
+        const size_t pb = ((size_t)bg * p.nsplit + split_out) * G;
+        for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
+            p.part_o[pb * kD + idx] = 0.f;
+            if (idx < G) {
+                p.part_m[pb + idx] = -INFINITY;
+                p.part_l[pb + idx] = 0.f;
+            }
+        }
+        return;
+    }
 
     const int qt_cap = p.c.cap_q / kTile, kt_cap = p.c.cap_keep / kTile, wt_cap = W / kTile;
-    const uint32_t* qp = p.qp + (size_t)bg * 4 * G * 16;
     const uint32_t* qn = p.qn + (size_t)bg * G * 64;
-    const float* qs = p.qsum + (size_t)bg * G * 4;
+    const float* qsc = p.qsc + (size_t)bg * 8;
 
-    // token-phase state
-    float m[G], l[G], zacc[G][4], wsum[G][4];
-    // channel-phase state, in units of 2^E / 16: INT4 tiles add magic-biased
-    // sums (bias removed at the end with wsum), 16-bit tiles add p*v*16*2^-E
-    float acc[G][8];
+    // QK A operands and the per-group constants of this lane's group j = lane/16
+    // the QK A operands live in LDS (read per use): [hb][ks][lane] x 16 bytes
+    auto& lds_qa = sm.qa;
+    for (int i = threadIdx.x; i < NHB * 4 * 64; i += 256)
+        lds_qa[i] = reinterpret_cast<const uint4*>(p.qa)[(size_t)bg * NHB * 256 + i];
+    __syncthreads();
+    floatx4 qb0[NHB];
+    float qsj[NHB][4];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+        const float* qcj = p.qc + (((size_t)bg * NHB + hb) * 4 + (lane >> 4)) * 8;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            qb0[hb][r] = -qcj[2 * r];
+            qsj[hb][r] = qcj[2 * r + 1];
+        }
+    }
+
+    // softmax state (lane = token), channel accumulators
+    float m[G], l[G], zacc[G][4], wsb[G][4];
+    floatx4 dpv[8];                  // INT4 PV: D[16mb + 4(lane/16) + r][head lane%16]
+    float acc[G][8];                 // 16-bit PV: channel-phase layout
     int E = -1000;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         m[h] = -INFINITY;
         l[h] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zacc[h][i] = wsum[h][i] = 0.f;
+        for (int i = 0; i < 4; ++i) zacc[h][i] = wsb[h][i] = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
     }
-    const int u = lane >> 4, c8 = lane & 15, gk = c8 >> 2;
-    uint32_t* pw_w = lds_pw[wave];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) dpv[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int u = lane >> 4, c8 = lane & 15;
     float* p_w = lds_p[wave];
-    const uint32_t ONES = 0x3C003C00u;  // fp16 (1, 1)
-    // extraction constants kept in VGPRs (opaque to constant folding)
-    uint32_t kM = F16 ? 0x00F000F0u : 0x00780078u, kC = F16 ? 0x64006400u : 0x43004300u;
-    uint32_t vMlo = 0x000F000Fu, vMhi = 0x00F000F0u, vClo = 0x64006400u, vChi = 0x54005400u;
-    asm("" : "+v"(kM), "+v"(kC), "+v"(vMlo), "+v"(vMhi), "+v"(vClo), "+v"(vChi));
+    float4* y_w = lds_y[wave];
+    uint16_t* w_w = lds_w[wave];
     float s_thr = 0.f;  // 2^(E+7): a V scale at or above it needs a larger E
+    const float ebias = elem_bias(lane & 7);  // magic bias of this lane's slot in the PV operand
+    const CodeConsts cc = code_consts();
 
-    for (int v = v0 + wave; v < v1; v += kWaves) {
+    if constexpr (MODE == 0) {
+        // Two tiles per wave per iteration: both tiles' loads are issued
+        // before either is used, doubling the bytes each wave keeps in flight.
+        struct TileRegs {
+            uint4 kd[4], kmv, vmv, vd[4];
+        };
+        const int wq = qt_cap * kTileBytesQ;  // bytes of one (b, g)'s INT4 codes / metadata
+        const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(reinterpret_cast<const uint8_t*>(p.c.k_codes) + (size_t)bg * wq), (short)0, wq, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(reinterpret_cast<const uint8_t*>(p.c.v_codes) + (size_t)bg * wq), (short)0, wq, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rkm = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(reinterpret_cast<const uint8_t*>(p.c.k_meta) + (size_t)bg * qt_cap * 1024), (short)0, qt_cap * 1024,
+            0x00020000);
+        const __amdgpu_buffer_rsrc_t rvm = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(reinterpret_cast<const uint8_t*>(p.c.v_meta) + (size_t)bg * qt_cap * 1024), (short)0, qt_cap * 1024,
+            0x00020000);
+        const int voff = lane * 16;
+        auto ld = [&](const __amdgpu_buffer_rsrc_t& r, int soff) {
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+        };
+        auto load_tile = [&](int v, TileRegs& r) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) r.kd[nb] = ld(rkc, v * kTileBytesQ + nb * 1024);
+            r.kmv = ld(rkm, v * 1024);
+            r.vmv = ld(rvm, v * 1024);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r.vd[i] = ld(rvc, v * kTileBytesQ + i * 1024);
+        };
+        auto step = [&](int v, const TileRegs& tr) {
         float lg[G];
-        const bool int4_tile = v < nqt;
         int count, tile;
         float vs[4], vz[4];
-        uint4 vw[4];
-        if (int4_tile) {
-            // ----------------------------- token phase, INT4 tile
+            // ----------------------------- QK on the matrix cores, INT4 tile
             tile = v;
             count = n_q;
             const bool valid = tile * kTile + lane < n_q;
-            const uint8_t* kc = reinterpret_cast<const uint8_t*>(p.c.k_codes) +
-                                ((size_t)bg * qt_cap + tile) * kTileBytesQ;
-            const size_t slot_g = (size_t)bg * p.c.cap_q + tile * kTile + lane;
-            uint4 kw[4];
+            const uint4* kd = tr.kd;
+            const uint4 kmv = tr.kmv;
+            uint4 vmv = tr.vmv;
+            const uint4* vd = tr.vd;
+            if (!valid) vmv = make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp)
-                kw[grp] = *reinterpret_cast<const uint4*>(kc + kcode_off(lane, grp));
-            uint4 km = reinterpret_cast<const uint4*>(p.c.k_meta)[slot_g];
-            uint4 vm = reinterpret_cast<const uint4*>(p.c.v_meta)[slot_g];
-            {   // V codes requested before QK so their latency overlaps the QK work
-                const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.c.v_codes) +
-                                    ((size_t)bg * qt_cap + tile) * kTileBytesQ;
+            for (int nb = 0; nb < 4; ++nb) {
+                halfx8 kb[4];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) vw[kk] = *reinterpret_cast<const uint4*>(vc + kk * 1024 + lane * 16);
+                for (int ks = 0; ks < 4; ++ks) kb[ks] = codes_to_f16(u4w(kd[nb], ks), cc);
+                const uint32_t md = u4w(kmv, nb);
+                const float sk = f16_to_f32(md & 0xFFFFu), zk = f16_to_f32(md >> 16);
+#pragma unroll
+                for (int hb = 0; hb < NHB; ++hb) {
+                    floatx4 dq = qb0[hb];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(halfx8, lds_qa[(hb * 4 + ks) * 64 + lane]), kb[ks], dq, 0, 0, 0);
+                    float4 y;
+                    y.x = fmaf(sk, dq[0], zk * qsj[hb][0]);
+                    y.y = fmaf(sk, dq[1], zk * qsj[hb][1]);
+                    y.z = fmaf(sk, dq[2], zk * qsj[hb][2]);
+                    y.w = fmaf(sk, dq[3], zk * qsj[hb][3]);
+                    y_w[(nb * NHB + hb) * 64 + lane] = y;
+                }
             }
-            if (!valid) {
-                km = make_uint4(0, 0, 0, 0);
-                vm = km;
-            }
+            lds_fence();
+            // lane = token: sum the four group partials
+            {
+                const int nb = lane >> 4, tl = lane & 15;
 #pragma unroll
-            for (int h = 0; h < G; ++h) lg[h] = 0.f;
+                for (int hb = 0; hb < NHB; ++hb) {
+                    float4 a = y_w[(nb * NHB + hb) * 64 + tl];
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const uint32_t mk = u4w(km, grp), mv = u4w(vm, grp);
-                const float sk = f16_to_f32(mk & 0xFFFFu), zk = f16_to_f32(mk >> 16);
-                vs[grp] = f16_to_f32(mv & 0xFFFFu);
-                vz[grp] = f16_to_f32(mv >> 16);
-                const float zz = zk - kBias<F16> * sk;
-                uint32_t pr[16];
+                    for (int j = 1; j < 4; ++j) {
+                        const float4 bq = y_w[(nb * NHB + hb) * 64 + tl + 16 * j];
+                        a.x += bq.x;
+                        a.y += bq.y;
+                        a.z += bq.z;
+                        a.w += bq.w;
+                    }
+                    const float av[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) extract_pairs<F16>(u4w(kw[grp], i), pr + 4 * i, kM, kC);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const uint32_t* qh = qp + (grp * G + h) * 16;
-                    float a = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) a = dot2<F16>(pr[e], qh[e], a);
-                    lg[h] = fmaf(sk, a, fmaf(zz, qs[h * 4 + grp], lg[h]));
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * hb + r < G) lg[4 * hb + r] = valid ? av[r] * (qsc[4 * hb + r] * p.scale2) : -INFINITY;
                 }
             }
 #pragma unroll
-            for (int h = 0; h < G; ++h) lg[h] = valid ? lg[h] * p.scale2 : -INFINITY;
-        } else {
+            for (int grp = 0; grp < 4; ++grp) {
+                const uint32_t mv = u4w(vmv, grp);
+                vs[grp] = f16_to_f32(mv & 0xFFFFu);
+                vz[grp] = f16_to_f32(mv >> 16);
+            }
+        // ----------------------------- online softmax (wave-uniform update)
+        float pr_h[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            if (__any(lg[h] > m[h] + kLazy)) {
+                const float tmax = wave_max_fast(lg[h]);
+                const float alpha = __builtin_amdgcn_exp2f(m[h] - tmax);
+                m[h] = tmax;
+                l[h] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    zacc[h][i] *= alpha;
+                    wsb[h][i] *= alpha;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dpv[mb][r] = (lane & 15) == h ? dpv[mb][r] * alpha : dpv[mb][r];
+            }
+            pr_h[h] = __builtin_amdgcn_exp2f(lg[h] - m[h]);
+            l[h] += pr_h[h];
+        }
+
+        {
+            // running power-of-two scale 2^E with p*s*2^-E < 2^15 (p <= 2^8 by the lazy
+            // rescale, s < 2^(e_s+1)): fp16 weights stay finite and mostly normal
+            const float s4 = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3]));
+            if (__any(s4 >= s_thr && s4 > 0.f)) {
+                const float smax = wave_max_fast(s4);
+                const int e_need = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127 - 6;
+                const float r = E <= -1000 ? 0.f : (e_need > E ? __builtin_ldexpf(1.0f, E - e_need) : 1.0f);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[h][i] *= r;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) wsb[h][i] *= r;
+                }
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb) dpv[mb] *= r;
+                E = e_need > E ? e_need : E;
+                s_thr = __builtin_ldexpf(1.0f, E + 7);
+            }
+            const float f = E <= -1000 ? 1.0f : __builtin_ldexpf(1.0f, -E);
+            // fp16 weights of this token into the B-operand layout
+            // w[grp][t/32][(t%32)/8][h][t%8]
+            const int wbase = ((lane >> 5) * 4 + ((lane >> 3) & 3)) * G * 8 + (lane & 7);
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const float sf = vs[grp] * f;
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    zacc[h][grp] = fmaf(pr_h[h], vz[grp], zacc[h][grp]);
+                    const _Float16 w16 = (_Float16)(pr_h[h] * sf);
+                    wsb[h][grp] = fmaf(ebias, (float)w16, wsb[h][grp]);
+                    w_w[grp * 2 * 4 * G * 8 + wbase + h * 8] = __builtin_bit_cast(uint16_t, w16);
+                }
+            }
+            lds_fence();
+            // ----------------------------- PV on the matrix cores
+            const int hs = (lane & 15) < G ? (lane & 15) : 0;
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const halfx8 wb = __builtin_bit_cast(
+                        halfx8, *reinterpret_cast<const uint4*>(w_w + ((grp * 2 + ks) * 4 + (lane >> 4)) * G * 8 + hs * 8));
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int mb = 2 * grp + half;
+                        const halfx8 va = codes_to_f16(u4w(vd[grp], half * 2 + ks), cc);
+                        dpv[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, wb, dpv[mb], 0, 0, 0);
+                    }
+                }
+            }
+            lds_fence();
+        }
+        };
+        for (int v = v0 + wave; v < v1; v += 2 * kWaves) {
+            TileRegs ta, tb;
+            load_tile(v, ta);
+            const bool two = v + kWaves < v1;
+            if (two) load_tile(v + kWaves, tb);
+            step(v, ta);
+            if (two) step(v + kWaves, tb);
+        }
+    } else {
+    for (int v = v0 + wave; v < v1; v += kWaves) {
+        float lg[G];
+        int count, tile;
+        {
             // ----------------------------- token phase, 16-bit tile
             const bool keep = v < nqt + nkt;
             tile = keep ? v - nqt : v - nqt - nkt;
             count = keep ? n_keep : nring;
             const bool valid = tile * kTile + lane < count;
-            const uint8_t* kt = keep ? reinterpret_cast<const uint8_t*>(p.c.k_keep) +
-                                           ((size_t)bg * kt_cap + tile) * kTileBytes16
-                                     : reinterpret_cast<const uint8_t*>(p.c.k_win) +
-                                           ((size_t)bg * wt_cap + tile) * kTileBytes16;
+            const uint8_t* kt = keep ? reinterpret_cast<const uint8_t*>(p.c.k_keep) + ((size_t)bg * kt_cap + tile) * kTileBytes16
+                                     : reinterpret_cast<const uint8_t*>(p.c.k_win) + ((size_t)bg * wt_cap + tile) * kTileBytes16;
 #pragma unroll
             for (int h = 0; h < G; ++h) lg[h] = 0.f;
 #pragma unroll
@@ -302,7 +465,6 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         float pr_h[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            // lazy max: the full reduction only runs when some logit exceeds m + 2^8
             if (__any(lg[h] > m[h] + kLazy)) {
                 const float tmax = wave_max_fast(lg[h]);
                 const float alpha = __builtin_amdgcn_exp2f(m[h] - tmax);
@@ -311,78 +473,20 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     zacc[h][i] *= alpha;
-                    wsum[h][i] *= alpha;
+                    wsb[h][i] *= alpha;
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dpv[mb][r] = (lane & 15) == h ? dpv[mb][r] * alpha : dpv[mb][r];
             }
             pr_h[h] = __builtin_amdgcn_exp2f(lg[h] - m[h]);
             l[h] += pr_h[h];
         }
 
-        if (int4_tile) {
-            // running power-of-two scale 2^E with p*s*2^-E < 2^15 (p <= 2^8 by the lazy
-            // rescale, s < 2^(e_s+1)): fp16 weights stay finite and mostly normal
-            const float s4 = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3]));
-            if (__any(s4 >= s_thr && s4 > 0.f)) {
-                const float smax = wave_max_fast(s4);
-                const int e_need = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127 - 6;
-                const float r = E <= -1000 ? 0.f : (e_need > E ? __builtin_ldexpf(1.0f, E - e_need) : 1.0f);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[h][i] *= r;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) wsum[h][i] *= r;
-                }
-                E = e_need > E ? e_need : E;
-                s_thr = __builtin_ldexpf(1.0f, E + 7);
-            }
-            const float f = E <= -1000 ? 1.0f : __builtin_ldexpf(1.0f, -E);
-            // fp16 weight pairs (slot lane, slot lane + 32), built by lanes 0..31
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const float sf = vs[grp] * f;
-                uint32_t words[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    zacc[h][grp] = fmaf(pr_h[h], vz[grp], zacc[h][grp]);
-                    const float w = pr_h[h] * sf;
-                    const float w2 = upper_half(w);
-                    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-                    h2_t pk = {(_Float16)w, (_Float16)w2};
-                    words[h] = __builtin_bit_cast(uint32_t, pk);
-                    wsum[h][grp] = dot2h(words[h], ONES, wsum[h][grp]);
-                }
-                if (lane < 32) {
-                    const int P = lane;
-                    uint32_t* dst = pw_w + P * 4 * G + ((grp ^ ((P >> 3) & 3)) * G);
-#pragma unroll
-                    for (int h = 0; h < G; ++h) dst[h] = words[h];
-                }
-            }
-            lds_fence();
-            // ----------------------------- channel phase, INT4 V
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int P = 8 * u + j;
-                uint32_t pw[G];
-                const uint32_t* src = pw_w + P * 4 * G + ((gk ^ u) * G);
-#pragma unroll
-                for (int h = 0; h < G; ++h) pw[h] = src[h];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const uint32_t d = u4w(vw[j >> 1], (j & 1) * 2 + e);
-                    uint32_t cp[4];
-                    extract_vpairs(d, cp, vMlo, vMhi, vClo, vChi);
-#pragma unroll
-                    for (int n = 0; n < 4; ++n)
-#pragma unroll
-                        for (int h = 0; h < G; ++h) acc[h][4 * e + n] = dot2h(cp[n], pw[h], acc[h][4 * e + n]);
-                }
-            }
-            lds_fence();
-        } else {
+        {
             if (E <= -1000) E = 0;  // no INT4 tile yet: fix the accumulator unit
             const float k16 = __builtin_ldexpf(1.0f, -E);
 #pragma unroll
@@ -390,10 +494,8 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
             lds_fence();
             // ----------------------------- channel phase, 16-bit V
             const bool keep = v < nqt + nkt;
-            const uint8_t* vt = keep ? reinterpret_cast<const uint8_t*>(p.c.v_keep) +
-                                           ((size_t)bg * kt_cap + tile) * kTileBytes16
-                                     : reinterpret_cast<const uint8_t*>(p.c.v_win) +
-                                           ((size_t)bg * wt_cap + tile) * kTileBytes16;
+            const uint8_t* vt = keep ? reinterpret_cast<const uint8_t*>(p.c.v_keep) + ((size_t)bg * kt_cap + tile) * kTileBytes16
+                                     : reinterpret_cast<const uint8_t*>(p.c.v_win) + ((size_t)bg * wt_cap + tile) * kTileBytes16;
 #pragma unroll 4
             for (int i = 0; i < 16; ++i) {
                 const int slot = 16 * u + i;
@@ -417,33 +519,54 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
         }
     }
 
+    }
     // ----------------------------- wave epilogue
-    // acc units: o = 2^E * (acc - bias * wsum) + sum(p z), bias 1024 on even
-    // and 64 on odd channels (the fp16 magic values); 16-bit tiles added
-    // p*v*2^-E directly.
+    // o = 2^E * (D - sum(bias * w)) + sum(p z) on INT4 tiles, 2^E * acc on
+    // 16-bit tiles.
     const float unit = E <= -1000 ? 0.f : __builtin_ldexpf(1.0f, E);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        l[h] = wave_sum_fast(l[h]);
+    for (int h = 0; h < G; ++h) l[h] = wave_sum_fast(l[h]);
+    if constexpr (MODE == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            zacc[h][i] = wave_sum_fast(zacc[h][i]);
-            wsum[h][i] = unit * wave_sum_fast(lane < 32 ? wsum[h][i] : 0.f);
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                zacc[h][i] = wave_sum_fast(zacc[h][i]);
+                wsb[h][i] = wave_sum_fast(wsb[h][i]);
+            }
+        const int hl = lane & 15;
+        if (hl < G) {
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                float zs[G], ws_[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    zs[h] = zacc[h][grp];
+                    ws_[h] = wsb[h][grp];
+                }
+                const float z = pick(zs, hl), wb = pick(ws_, hl);
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int mb = 2 * grp + half;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        lds_o[wave][hl][16 * mb + 4 * (lane >> 4) + r] = fmaf(unit, dpv[mb][r] - wb, z);
+                }
+            }
         }
+    } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            acc[h][i] += __shfl_xor(acc[h][i], 16);
-            acc[h][i] += __shfl_xor(acc[h][i], 32);
-        }
-    }
-    if (lane < 16) {
-        const int gq = lane >> 2;
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float z_even = fmaf(-1024.0f, wsum[h][gq], zacc[h][gq]);
-            const float z_odd = fmaf(-64.0f, wsum[h][gq], zacc[h][gq]);
+            for (int i = 0; i < 8; ++i) {
+                acc[h][i] += __shfl_xor(acc[h][i], 16);
+                acc[h][i] += __shfl_xor(acc[h][i], 32);
+            }
+        if (lane < 16) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) lds_o[wave][h][8 * lane + i] = fmaf(unit, acc[h][i], (i & 1) ? z_odd : z_even);
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) lds_o[wave][h][8 * lane + i] = unit * acc[h][i];
         }
     }
     if (lane == 0) {
@@ -455,7 +578,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
     }
     __syncthreads();
     // ----------------------------- merge the waves, write the split partial
-    const size_t pbase = ((size_t)bg * p.nsplit + s) * G;
+    const size_t pbase = ((size_t)bg * p.nsplit + split_out) * G;
     for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
         const int h = idx / kD, d = idx % kD;
         float M = lds_m[0][h];
@@ -477,39 +600,81 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p) {
     }
 }
 
-// Rearranges the query for the split kernel: INT4-path pairs (prescaled by
-// 1/8 for bf16, 1/16 for fp16, exact), natural pairs and group sums.
+// One launch covers both kinds of split: workgroups x < nsq take INT4 tiles,
+// the rest take 16-bit tiles, so the two kinds run side by side.
+template <int G, bool F16>
+__global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void k_decode_split(DecodeParams p) {
+    __shared__ SplitSmem<G> sm;
+    const int x = blockIdx.x;
+    if (x < p.nsq)
+        split_body<G, F16, 0>(p, sm, x);
+    else
+        split_body<G, F16, 1>(p, sm, x - p.nsq);
+}
+
+// Rearranges the query for the split kernel: per head a power-of-two scale
+// 2^k into fp16 range (q' = q 2^k, exact for every value above 2^-24 of the
+// head's maximum), the QK A operands (row 4j + h of K-step ks holds q'_h on
+// group ks when j == ks, zero otherwise), the per-group sums of q' and of
+// q' * bias, and the natural 16-bit pairs for the 16-bit tiles.
 template <bool F16>
-__global__ __launch_bounds__(1024) void k_decode_prep(const uint16_t* q, int Hq, int G, uint32_t* qp,
-                                                      uint32_t* qn, float* qsum) {
+__global__ __launch_bounds__(256) void k_decode_prep(const uint16_t* q, int Hq, int G, uint32_t* qa, float* qc,
+                                                     float* qsc, uint32_t* qn) {
+    __shared__ float qf[8][kD];
+    __shared__ uint16_t q16[8][kD];
+    __shared__ int kq[8];
     const int g = blockIdx.x, b = blockIdx.y, Hkv = gridDim.x;
     const int bg = b * Hkv + g;
-    const int h = threadIdx.x >> 7, t = threadIdx.x & 127;   // one thread per (head, channel)
-    const float sc = F16 ? 0.0625f : 0.125f;
-    const uint16_t* qh = q + ((size_t)b * Hq + g * G + h) * kD;
-    if (t < 64) {
-        qn[((size_t)bg * G + h) * 64 + t] = (uint32_t)qh[2 * t] | ((uint32_t)qh[2 * t + 1] << 16);
-        // INT4 arrangement: entry (grp, 4i + n) = (q[32grp+8i+n], q[32grp+8i+n+4]) * 2^-3 / 2^-4
-        const int grp = t >> 4, e = t & 15, i = e >> 2, n = e & 3;
-        const int d0 = 32 * grp + 8 * i + n;
-        const float a = h16_to_f32<F16>(qh[d0]) * sc, c = h16_to_f32<F16>(qh[d0 + 4]) * sc;
-        uint32_t wa, wc;
-        if constexpr (F16) {
-            wa = f32_to_f16_bits(a);
-            wc = f32_to_f16_bits(c);
-        } else {
-            wa = __float_as_uint(a) >> 16;  // exact: power-of-two scaling of a bf16 value
-            wc = __float_as_uint(c) >> 16;
+    const int tid = threadIdx.x;
+    const int NHB = (G + 3) / 4;
+    for (int i = tid; i < G * kD; i += 256) {
+        const int h = i / kD, c = i % kD;
+        const uint16_t bits = q[((size_t)b * Hq + g * G + h) * kD + c];
+        qf[h][c] = h16_to_f32<F16>(bits);
+        if (c < 64) {
+            const uint16_t* qh = q + ((size_t)b * Hq + g * G + h) * kD;
+            qn[((size_t)bg * G + h) * 64 + c] = (uint32_t)qh[2 * c] | ((uint32_t)qh[2 * c + 1] << 16);
         }
-        qp[(((size_t)bg * 4 + grp) * G + h) * 16 + e] = wa | (wc << 16);
     }
-    // group sums of exactly the values the pairs carry (rescaled), in double
-    float a = h16_to_f32<F16>(qh[t]) * sc;
-    if constexpr (F16) a = f16_to_f32(f32_to_f16_bits(a));
-    double acc = (double)a;
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) acc += __shfl_xor(acc, o);
-    if ((t & 31) == 0) qsum[((size_t)bg * G + h) * 4 + (t >> 5)] = (float)(acc / sc);
+    __syncthreads();
+    if (tid < G) {
+        float mx = 0.f;
+        for (int c = 0; c < kD; ++c) mx = fmaxf(mx, fabsf(qf[tid][c]));
+        const int e = mx > 0.f ? (int)((__float_as_uint(mx) >> 23) & 0xFF) - 127 : 0;
+        const int k = mx > 0.f ? min(max(14 - e, -100), 100) : 0;
+        kq[tid] = k;
+        qsc[(size_t)bg * 8 + tid] = __builtin_ldexpf(1.0f, -k);
+    }
+    __syncthreads();
+    for (int i = tid; i < G * kD; i += 256) {
+        const int h = i / kD, c = i % kD;
+        q16[h][c] = (uint16_t)f32_to_f16_bits(__builtin_ldexpf(qf[h][c], kq[h]));
+    }
+    __syncthreads();
+    for (int w = tid; w < NHB * 1024; w += 256) {
+        const int hb = w >> 10, ks = (w >> 8) & 3, ln = (w >> 2) & 63, reg = w & 3;
+        const int mrow = ln & 15, j = mrow >> 2, h = 4 * hb + (mrow & 3);
+        uint32_t val = 0;
+        if (j == ks && h < G) {
+            const int c0 = 32 * ks + 8 * (ln >> 4) + 2 * reg;
+            val = (uint32_t)q16[h][c0] | ((uint32_t)q16[h][c0 + 1] << 16);
+        }
+        qa[((size_t)bg * NHB + hb) * 1024 + w - hb * 1024] = val;
+    }
+    if (tid < NHB * 16) {
+        const int hb = tid >> 4, j = (tid >> 2) & 3, r = tid & 3, h = 4 * hb + r;
+        double sb = 0.0, sq = 0.0;
+        if (h < G) {
+            for (int c = 32 * j; c < 32 * j + 32; ++c) {
+                const double x = (double)f16_to_f32(q16[h][c]);
+                sq += x;
+                sb += x * (double)elem_bias(c & 7);
+            }
+        }
+        float* dst = qc + (((size_t)bg * NHB + hb) * 4 + j) * 8 + 2 * r;
+        dst[0] = (float)sb;
+        dst[1] = (float)sq;
+    }
 }
 
 __global__ __launch_bounds__(128) void k_decode_reduce(const hq_cache c, const float* part_m, const float* part_l,
@@ -519,11 +684,8 @@ __global__ __launch_bounds__(128) void k_decode_reduce(const hq_cache c, const f
     const int gh = blockIdx.x, b = blockIdx.y;
     const int g = gh / G, h = gh % G, d = threadIdx.x;
     const int bg = b * c.Hkv + g;
-    const int4 cnt = *reinterpret_cast<const int4*>(c.counts + 4 * bg);
-    const int T = cnt.x, n_q = cnt.y, n_keep = cnt.z;
-    const int nring = T < c.window ? T : c.window;
-    const int total = (n_q + kTile - 1) / kTile + (n_keep + kTile - 1) / kTile + (nring + kTile - 1) / kTile;
-    const int active = min((total + tps - 1) / tps, nsplit);
+    (void)tps;
+    const int active = nsplit;  // every split writes a partial (empty ones have m = -inf)
     const size_t base = (size_t)bg * nsplit * G + h;
     float* wsp = sh;
     __shared__ float red[2];
@@ -567,17 +729,19 @@ __global__ __launch_bounds__(128) void k_decode_reduce(const hq_cache c, const f
 }
 
 struct WsLayout {
-    size_t qp, qn, qsum, pm, pl, po, total;
+    size_t qa, qc, qsc, qn, pm, pl, po, total;
 };
 inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 WsLayout ws_layout(const hq_cache& c, int32_t Hq, int32_t nsplit) {
     const size_t BG = (size_t)c.B * c.Hkv;
     const int G = Hq / c.Hkv;
+    const int NHB = (G + 3) / 4;
     WsLayout w;
-    w.qp = 0;
-    w.qn = w.qp + al(BG * 4 * G * 16 * 4);
-    w.qsum = w.qn + al(BG * G * 64 * 4);
-    w.pm = w.qsum + al(BG * G * 4 * 4);
+    w.qa = 0;
+    w.qc = w.qa + al(BG * NHB * 1024 * 4);
+    w.qsc = w.qc + al(BG * NHB * 32 * 4);
+    w.qn = w.qsc + al(BG * 8 * 4);
+    w.pm = w.qn + al(BG * G * 64 * 4);
     w.pl = w.pm + al(BG * nsplit * G * 4);
     w.po = w.pl + al(BG * nsplit * G * 4);
     w.total = w.po + al(BG * nsplit * G * kD * 4);
@@ -585,15 +749,24 @@ WsLayout ws_layout(const hq_cache& c, int32_t Hq, int32_t nsplit) {
 }
 
 template <int G, bool F16>
-void launch_split(const DecodeParams& p, dim3 grid, hipStream_t s) {
-    k_decode_split<G, F16><<<grid, 256, 0, s>>>(p);
+void launch_split(const DecodeParams& p, int Hkv, int B, hipStream_t s) {
+    // INT4 splits (x < nsq) come first in dispatch order; the 16-bit ones
+    // fill in as slots free up.
+    k_decode_split<G, F16><<<dim3(p.nsplit, Hkv, B), 256, 0, s>>>(p);
 }
+
+constexpr int kTps16 = 8;  // 16-bit tiles per split
 
 }  // namespace
 
-int32_t decode_max_tiles(const hq_cache& c) {
-    return c.cap_q / kTile + c.cap_keep / kTile + c.window / kTile;
+int32_t decode_nsq(const hq_cache& c, int32_t tps) { return (c.cap_q / kTile + tps - 1) / tps; }
+int32_t decode_nsplit(const hq_cache& c, int32_t tps) {
+    return decode_nsq(c, tps) + (c.cap_keep / kTile + c.window / kTile + kTps16 - 1) / kTps16;
 }
+
+namespace {
+
+}  // namespace
 
 size_t decode_ws_bytes(const hq_cache& c, int32_t Hq, int32_t nsplit) {
     return ws_layout(c, Hq, nsplit).total;
@@ -605,38 +778,40 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     char* ws = static_cast<char*>(d.ws);
     DecodeParams p;
     p.c = c;
-    p.qp = reinterpret_cast<uint32_t*>(ws + w.qp);
+    p.qa = reinterpret_cast<uint32_t*>(ws + w.qa);
+    p.qc = reinterpret_cast<float*>(ws + w.qc);
+    p.qsc = reinterpret_cast<float*>(ws + w.qsc);
     p.qn = reinterpret_cast<uint32_t*>(ws + w.qn);
-    p.qsum = reinterpret_cast<float*>(ws + w.qsum);
     p.part_m = reinterpret_cast<float*>(ws + w.pm);
     p.part_l = reinterpret_cast<float*>(ws + w.pl);
     p.part_o = reinterpret_cast<float*>(ws + w.po);
     p.nsplit = d.nsplit;
     p.tps = d.tiles_per_split;
+    p.nsq = decode_nsq(c, d.tiles_per_split);
+    p.tps16 = kTps16;
     p.G = d.G;
     p.scale2 = d.sm_scale_log2;
     const bool f16 = c.dt == HQ_F16;
     dim3 pg(c.Hkv, c.B);
     if (f16)
-        k_decode_prep<true><<<pg, 128 * d.G, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
-                                               const_cast<uint32_t*>(p.qp), const_cast<uint32_t*>(p.qn),
-                                               const_cast<float*>(p.qsum));
+        k_decode_prep<true><<<pg, 256, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G, const_cast<uint32_t*>(p.qa),
+                                               const_cast<float*>(p.qc), const_cast<float*>(p.qsc),
+                                               const_cast<uint32_t*>(p.qn));
     else
-        k_decode_prep<false><<<pg, 128 * d.G, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G,
-                                                const_cast<uint32_t*>(p.qp), const_cast<uint32_t*>(p.qn),
-                                                const_cast<float*>(p.qsum));
+        k_decode_prep<false><<<pg, 256, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G, const_cast<uint32_t*>(p.qa),
+                                                const_cast<float*>(p.qc), const_cast<float*>(p.qsc),
+                                                const_cast<uint32_t*>(p.qn));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid(d.nsplit, c.Hkv, c.B);
     switch (d.G * 2 + (f16 ? 1 : 0)) {
-        case 2: launch_split<1, false>(p, grid, s); break;
-        case 3: launch_split<1, true>(p, grid, s); break;
-        case 4: launch_split<2, false>(p, grid, s); break;
-        case 5: launch_split<2, true>(p, grid, s); break;
-        case 8: launch_split<4, false>(p, grid, s); break;
-        case 9: launch_split<4, true>(p, grid, s); break;
-        case 16: launch_split<8, false>(p, grid, s); break;
-        case 17: launch_split<8, true>(p, grid, s); break;
+        case 2: launch_split<1, false>(p, c.Hkv, c.B, s); break;
+        case 3: launch_split<1, true>(p, c.Hkv, c.B, s); break;
+        case 4: launch_split<2, false>(p, c.Hkv, c.B, s); break;
+        case 5: launch_split<2, true>(p, c.Hkv, c.B, s); break;
+        case 8: launch_split<4, false>(p, c.Hkv, c.B, s); break;
+        case 9: launch_split<4, true>(p, c.Hkv, c.B, s); break;
+        case 16: launch_split<8, false>(p, c.Hkv, c.B, s); break;
+        case 17: launch_split<8, true>(p, c.Hkv, c.B, s); break;
         default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();

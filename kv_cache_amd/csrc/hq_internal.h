@@ -16,22 +16,45 @@ constexpr int kTileBytes16 = kTile * kD * 2;  // one tile of 16-bit rows
 constexpr int kInt8Block = 64;   // prefill INT8 block (tokens)
 
 // ---------------------------------------------------------------------------
-// INT4 tile layouts (per (b, g), tile of 64 slots; see hq.h for the format).
-//
-// K codes (read by the token phase, lane = slot): the 16 bytes of group k of
-// slot t are the canonical packed bytes of channels 32k..32k+31
-// (byte i = code[2i] | code[2i+1] << 4) at  k*1024 + t*16.
-__host__ __device__ inline int kcode_off(int slot, int group) { return group * 1024 + slot * 16; }
+// INT4 tile layouts (per (b, g), tile of 64 slots). The decode kernel feeds
+// the codes straight into 16x16x32 fp16 MFMA operands, so every 32-bit word
+// holds the 8 codes of one operand lane: element e (0..7) of the lane's
+// 8-element k-slice sits in the nibble at bit mf_nib(e) = 16*(e%2) + 4*(e/2),
+// so that register k of the operand (elements 2k, 2k+1 in its low / high
+// 16 bits) is the word's nibbles at bits (4(k/2)+..., 16+...) after at most
+// one shift, and a single and-or turns them into fp16 "1024 + c" (nibble at
+// bits 0..3 of a half) or "64 + c" (nibble at bits 4..7) values.
+__host__ __device__ constexpr int mf_nib(int e) { return 16 * (e & 1) + 4 * (e >> 1); }
 
-// V codes (read by the channel phase, lane l = 16u + c8 owns channels
-// 8c8..8c8+7 of pairs P = 8u..8u+7). Dword (pair P, quad Q), P in [0, 32),
-// holds in its low 16 bits the canonical nibbles of slot P, channels
-// 4Q..4Q+3, and in its high 16 bits the same channels of slot P+32. It lives at
-//   u = P/8, j = P%8, c8 = Q/2, e = Q%2, l = 16u + c8,
-//   byte offset = (j/2)*1024 + l*16 + ((j%2)*2 + e)*4.
-__host__ __device__ inline int vcode_off(int pair, int quad) {
-    int u = pair >> 3, j = pair & 7, c8 = quad >> 1, e = quad & 1;
-    return (j >> 1) * 1024 + (16 * u + c8) * 16 + ((j & 1) * 2 + e) * 4;
+// K codes: slot t, channel c. Operand lane l = t%16 + 16*((c%32)/8) (token
+// t%16 of 16-token block t/16, channel octet (c%32)/8), element c%8; the word
+// of (block nb = t/16, group c/32) is at byte nb*1024 + l*16 + (c/32)*4.
+__host__ __device__ inline int kq_word(int slot, int ch) {
+    return (slot >> 4) * 1024 + ((slot & 15) + 16 * ((ch >> 3) & 3)) * 16 + (ch >> 5) * 4;
+}
+// V codes: slot t, channel c. Operand lane l = c%16 + 16*((t%32)/8) (channel
+// c%16 of 16-channel block c/16, token octet (t%32)/8 of token half t/32),
+// element t%8; the word of (channel block mb = c/16, token half ks = t/32) is
+// at byte (mb/2)*1024 + l*16 + ((mb%2)*2 + ks)*4.
+__host__ __device__ inline int vq_word(int slot, int ch) {
+    return (ch >> 5) * 1024 + ((ch & 15) + 16 * ((slot >> 3) & 3)) * 16 + ((((ch >> 4) & 1) << 1) | (slot >> 5)) * 4;
+}
+// K scale/zero (fp16 pair, one dword) of slot t, group j inside the tile's
+// 1024-byte metadata block: byte (t%16 + 16*j)*16 + (t/16)*4, so lane
+// l = t%16 + 16j reads the four 16-token blocks with one 16-byte load.
+__host__ __device__ inline int kmeta_word(int slot, int group) {
+    return ((slot & 15) + 16 * group) * 16 + (slot >> 4) * 4;
+}
+// V scale/zero: slot t, group j at byte t*16 + j*4 (one 16-byte record per slot).
+__host__ __device__ inline int vmeta_word(int slot, int group) { return slot * 16 + group * 4; }
+
+// Canonical packed word (nibble n = channel/slot 8w+n at bits 4n) -> the
+// operand nibble order above.
+__host__ __device__ inline uint32_t to_mf_order(uint32_t w) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) r |= ((w >> (4 * n)) & 0xFu) << mf_nib(n);
+    return r;
 }
 
 // 16-bit tiles. K (token phase): 16-byte chunk c (channels 8c..8c+7) of slot
@@ -115,7 +138,7 @@ struct DecodeLaunch {
 hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype out_dt,
                          const DecodeLaunch& d, hipStream_t s);
 size_t decode_ws_bytes(const hq_cache& c, int32_t Hq, int32_t nsplit);
-int32_t decode_max_tiles(const hq_cache& c);
+int32_t decode_nsplit(const hq_cache& c, int32_t tps);
 
 hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_lens, int32_t B,
                         int32_t Hq, int32_t Hkv, int32_t Tmax, bool f16, const hq_policy& pol,

@@ -95,35 +95,36 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
             for (int i = 0; i < 4; ++i) unpack8<F16>(src[i], x + 8 * i);
             int4_quant_group(x, vp, vs, vz);
         }
-        // V pairs are slots (P, P + 32): stage the packed words in LDS
+        // V words gather 8 slots of one channel: stage the canonical words in LDS
         __shared__ uint32_t vstage[kTile][4][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vstage[t][grp][i] = vp[i];
+        for (int i = 0; i < 4; ++i) vstage[t][grp][i] = valid ? vp[i] : 0u;
         const size_t tile_base = ((size_t)bg * qt + tile) * kTileBytesQ;
+        const size_t meta_base = ((size_t)bg * qt + tile) * (kTile * 16);
         uint8_t* kc = reinterpret_cast<uint8_t*>(p.c.k_codes) + tile_base;
         uint8_t* vc = reinterpret_cast<uint8_t*>(p.c.v_codes) + tile_base;
-        const size_t slot_g = (size_t)bg * p.c.cap_q + n;
         if (valid) {
-            *reinterpret_cast<uint4*>(kc + kcode_off(t, grp)) = make_uint4(kp[0], kp[1], kp[2], kp[3]);
-            reinterpret_cast<uint32_t*>(p.c.k_meta)[slot_g * 4 + grp] = ks | (kz << 16);
-            reinterpret_cast<uint32_t*>(p.c.v_meta)[slot_g * 4 + grp] = vs | (vz << 16);
-            if (grp == 0) p.c.q_pos[slot_g] = pos;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                *reinterpret_cast<uint32_t*>(kc + kq_word(t, kGroup * grp + 8 * w)) = to_mf_order(kp[w]);
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.c.k_meta) + meta_base + kmeta_word(t, grp)) =
+                ks | (kz << 16);
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.c.v_meta) + meta_base + vmeta_word(t, grp)) =
+                vs | (vz << 16);
+            if (grp == 0) p.c.q_pos[(size_t)bg * p.c.cap_q + n] = pos;
         }
         __syncthreads();
-        {
-            const int P = tid >> 3, Q0 = (tid & 7) * 4;
-            if (tile * kTile + P < n_q) {
-                uint32_t pw[4];
+        // 1024 V words per tile: word (channel ch, slot octet o) holds slots 8o..8o+7
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int Q = Q0 + i, g8 = Q >> 3, q = Q & 7, w = q >> 1, h = 16 * (q & 1);
-                    const uint32_t lo = (vstage[P][g8][w] >> h) & 0xFFFFu;
-                    const uint32_t hi = (vstage[P + 32][g8][w] >> h) & 0xFFFFu;
-                    pw[i] = lo | (hi << 16);
-                }
-                *reinterpret_cast<uint2*>(vc + vcode_off(P, Q0)) = make_uint2(pw[0], pw[1]);
-                *reinterpret_cast<uint2*>(vc + vcode_off(P, Q0 + 2)) = make_uint2(pw[2], pw[3]);
+        for (int i = 0; i < 4; ++i) {
+            const int wi = tid + 256 * i, ch = wi >> 3, o = wi & 7;
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t code = (vstage[8 * o + e][ch >> 5][(ch >> 3) & 3] >> (4 * (ch & 7))) & 0xFu;
+                w |= code << mf_nib(e);
             }
+            *reinterpret_cast<uint32_t*>(vc + vq_word(8 * o, ch)) = w;
         }
         return;
     }

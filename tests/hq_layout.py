@@ -6,41 +6,54 @@ import numpy as np
 TILE = 64
 
 
-def _vcode_word_index():
-    """word index (uint32) inside a 4096-byte V-code tile for (pair P, quad Q)."""
-    P = np.arange(32)[:, None]
-    Q = np.arange(32)[None, :]
-    u, j, c8, e = P // 8, P % 8, Q // 2, Q % 2
-    off = (j // 2) * 1024 + (16 * u + c8) * 16 + ((j % 2) * 2 + e) * 4
-    return off // 4
+def _mf_nib(e):
+    return 16 * (e & 1) + 4 * (e >> 1)
 
 
-_VIDX = _vcode_word_index()
+def _int4_maps():
+    """(word index, nibble shift) of every (slot, channel) of a 4096-byte
+    K-code and V-code tile, and the dword index of every (slot, group) of the
+    K / V metadata blocks (the layouts documented in include/hq.h)."""
+    t = np.arange(TILE)[:, None]
+    c = np.arange(128)[None, :]
+    kw = ((t >> 4) * 1024 + ((t & 15) + 16 * ((c >> 3) & 3)) * 16 + (c >> 5) * 4) // 4
+    ks = _mf_nib(c & 7) + 0 * t
+    vw = ((c >> 5) * 1024 + ((c & 15) + 16 * ((t >> 3) & 3)) * 16 + ((((c >> 4) & 1) << 1) | (t >> 5)) * 4) // 4
+    vs = _mf_nib(t & 7) + 0 * c
+    j = np.arange(4)[None, :]
+    km = ((t & 15) + 16 * j) * 4 + (t >> 4)
+    vm = t * 4 + j
+    return kw, ks, vw, vs, km, vm
+
+
+_KW, _KS, _VW, _VS, _KM, _VM = _int4_maps()
+
+
+def _unpack_codes(buf, BG, cap_q, widx, shift):
+    nt = cap_q // TILE
+    w = buf.view(np.uint32).reshape(BG, nt, 1024)[:, :, widx]          # [BG][nt][64][128]
+    return ((w >> shift.astype(np.uint32)) & 0xF).astype(np.uint8).reshape(BG, cap_q, 128)
 
 
 def unpack_k_codes(kc: np.ndarray, BG: int, cap_q: int) -> np.ndarray:
     """[BG*cap_q/64*4096] bytes -> canonical codes [BG][cap_q][128] uint8."""
-    nt = cap_q // TILE
-    b = kc.reshape(BG, nt, 4, TILE, 16).transpose(0, 1, 3, 2, 4).reshape(BG, cap_q, 64)
-    out = np.empty((BG, cap_q, 128), dtype=np.uint8)
-    out[..., 0::2] = b & 0x0F
-    out[..., 1::2] = b >> 4
-    return out
+    return _unpack_codes(kc, BG, cap_q, _KW, _KS)
 
 
 def unpack_v_codes(vc: np.ndarray, BG: int, cap_q: int) -> np.ndarray:
+    return _unpack_codes(vc, BG, cap_q, _VW, _VS)
+
+
+def _unpack_meta(meta, BG, cap_q, idx):
     nt = cap_q // TILE
-    w = vc.view(np.uint32).reshape(BG, nt, 1024)[:, :, _VIDX]          # [BG][nt][P][Q]
-    halves = np.stack([w & 0xFFFF, w >> 16], axis=2)                  # [BG][nt][half][P][Q]
-    nib = np.stack([(halves >> (4 * n)) & 0xF for n in range(4)], axis=-1)  # [..][Q][4]
-    # slot = P + 32 * half
-    return nib.reshape(BG, nt, 2, 32, 128).reshape(BG, cap_q, 128).astype(np.uint8)
+    m = meta.view(np.uint32).reshape(BG, nt, 256)[:, :, idx].reshape(BG, cap_q, 4)
+    h = m.view(np.uint16).reshape(BG, cap_q, 4, 2).view(np.float16)
+    return h[..., 0], h[..., 1]
 
 
-def unpack_meta(meta: np.ndarray, BG: int, cap_q: int):
-    """-> (s, z) float16 [BG][cap_q][4]."""
-    m = meta.view(np.float16).reshape(BG, cap_q, 4, 2)
-    return m[..., 0], m[..., 1]
+def unpack_meta(meta: np.ndarray, BG: int, cap_q: int, which: str = "k"):
+    """-> (s, z) float16 [BG][cap_q][4] of the K ('k') or V ('v') metadata."""
+    return _unpack_meta(meta, BG, cap_q, _KM if which == "k" else _VM)
 
 
 def unpack_k16(buf: np.ndarray, BG: int, cap: int) -> np.ndarray:
@@ -74,8 +87,8 @@ def read_cache(cache) -> dict:
         "thresh": host["thresh"][: BG * 8].view(np.int32).reshape(BG, 2),
         "col_scores": host["col_scores"][: BG * c.cap_probe * 4].view(np.float32).reshape(BG, c.cap_probe),
     }
-    d["k_s"], d["k_z"] = unpack_meta(host["k_meta"][: BG * c.cap_q * 16], BG, c.cap_q)
-    d["v_s"], d["v_z"] = unpack_meta(host["v_meta"][: BG * c.cap_q * 16], BG, c.cap_q)
+    d["k_s"], d["k_z"] = unpack_meta(host["k_meta"][: BG * c.cap_q * 16], BG, c.cap_q, "k")
+    d["v_s"], d["v_z"] = unpack_meta(host["v_meta"][: BG * c.cap_q * 16], BG, c.cap_q, "v")
     if c.window > 0:
         d["k_win"] = unpack_k16(host["k_win"][: BG * c.window * 256], BG, c.window)
         d["v_win"] = unpack_v16(host["v_win"][: BG * c.window * 256], BG, c.window)
