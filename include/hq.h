@@ -131,14 +131,18 @@ size_t hq_probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32
  *   kept store : the selected positions (and departures flagged by the append
  *                rule), 16-bit, in insertion order.
  *   ring       : the last `window` positions, 16-bit, slot = position % window.
- * Storage is tiled in 64-token tiles laid out so that every 128-bit load of
- * the decode kernel is contiguous across the wavefront:
- *   K codes, tile byte  group*1024 + slot*16 + i : packed byte i of the
- *       32-channel group (byte i = code[2i] | code[2i+1] << 4);
- *   V codes, pre-paired: the 32-bit word for slots (P, P+32), P < 32, and
- *       channels 4Q..4Q+3 holds slot P's four nibbles in its low half and
- *       slot P+32's in its high half; it sits at (j/2)*1024 + (16u + Q/2)*16
- *       + ((j%2)*2 + Q%2)*4 with u = P/8, j = P%8;
+ * Storage is tiled in 64-token tiles. The INT4 tiles are laid out as the
+ * operands of the decode kernel's 16x16x32 fp16 matrix instructions: every
+ * 32-bit word holds 8 codes, element e (0..7) in the nibble at bit
+ * n(e) = 16*(e%2) + 4*(e/2), and every 128-bit load is contiguous across the
+ * wavefront. For slot t and channel c of a tile (4096 bytes each for K, V):
+ *   K code: element c%8 of the word at byte
+ *       (t/16)*1024 + ((t%16) + 16*((c%32)/8))*16 + (c/32)*4;
+ *   V code: element t%8 of the word at byte
+ *       (c/32)*1024 + ((c%16) + 16*((t%32)/8))*16 + (2*((c/16)%2) + t/32)*4;
+ *   K scale/zero of group j (one fp16 pair): byte ((t%16) + 16j)*16 + (t/16)*4
+ *       of the tile's 1024-byte metadata block;
+ *   V scale/zero of group j: byte t*16 + j*4 of the tile's metadata block;
  *   16-bit K rows, chunk c (channels 8c..8c+7) of slot t at c*1024 + t*16;
  *   16-bit V rows, chunk c of slot t at (t%16)*1024 + (16*(t/16) + c)*16.
  * Position tags give the canonical order. The struct is filled by the caller
@@ -152,8 +156,8 @@ typedef struct {
     int32_t dt;         /* hq_dtype of the 16-bit stores (HQ_BF16 or HQ_F16)  */
     void* k_codes;      /* [B][Hkv][cap_q/64][4096] bytes                     */
     void* v_codes;      /* [B][Hkv][cap_q/64][4096] bytes                     */
-    void* k_meta;       /* [B][Hkv][cap_q][8] fp16: (s,z) x 4 groups          */
-    void* v_meta;       /* [B][Hkv][cap_q][8] fp16                            */
+    void* k_meta;       /* [B][Hkv][cap_q/64][1024] bytes: (s,z) fp16 pairs    */
+    void* v_meta;       /* [B][Hkv][cap_q/64][1024] bytes                      */
     void* k_keep;       /* [B][Hkv][cap_keep/64][64*D] 16-bit                 */
     void* v_keep;
     void* k_win;        /* [B][Hkv][window/64][64*D] 16-bit                   */
