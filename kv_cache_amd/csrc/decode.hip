@@ -127,8 +127,12 @@ __device__ inline float wave_sum_fast(float v) {
     return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
+// Orders this wave's LDS writes before its later LDS reads (other lanes'
+// data). LDS operations of one wave execute in order, so this only has to
+// stop the compiler from reordering; it must not wait for global loads.
 __device__ inline void lds_fence() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
 }
 
@@ -218,10 +222,17 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
     for (int i = threadIdx.x; i < NHB * 4 * 64; i += 256)
         lds_qa[i] = reinterpret_cast<const uint4*>(p.qa)[(size_t)bg * NHB * 256 + i];
     __syncthreads();
+    // per-head logit scale 2^-k * sm_scale * log2(e), read once
+    float qscale[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) qscale[h] = qsc[h] * p.scale2;
     floatx4 qb0[NHB];
     float qsj[NHB][4];
+    halfx8 qreg[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qreg[hb][ks] = __builtin_bit_cast(halfx8, lds_qa[(hb * 4 + ks) * 64 + lane]);
         const float* qcj = p.qc + (((size_t)bg * NHB + hb) * 4 + (lane >> 4)) * 8;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -296,25 +307,37 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
             uint4 vmv = tr.vmv;
             const uint4* vd = tr.vd;
             if (!valid) vmv = make_uint4(0, 0, 0, 0);
+            // four independent accumulators (one per 16-token block), K-step
+            // outer, so consecutive MFMAs do not wait on each other
+            floatx4 dq[4][NHB];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int hb = 0; hb < NHB; ++hb) dq[nb][hb] = qb0[hb];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                halfx8 qk[NHB];
+#pragma unroll
+                for (int hb = 0; hb < NHB; ++hb) qk[hb] = qreg[hb][ks];
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const halfx8 kb = codes_to_f16(u4w(kd[nb], ks), cc);
+#pragma unroll
+                    for (int hb = 0; hb < NHB; ++hb)
+                        dq[nb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qk[hb], kb, dq[nb][hb], 0, 0, 0);
+                }
+            }
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                halfx8 kb[4];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kb[ks] = codes_to_f16(u4w(kd[nb], ks), cc);
                 const uint32_t md = u4w(kmv, nb);
                 const float sk = f16_to_f32(md & 0xFFFFu), zk = f16_to_f32(md >> 16);
 #pragma unroll
                 for (int hb = 0; hb < NHB; ++hb) {
-                    floatx4 dq = qb0[hb];
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(halfx8, lds_qa[(hb * 4 + ks) * 64 + lane]), kb[ks], dq, 0, 0, 0);
                     float4 y;
-                    y.x = fmaf(sk, dq[0], zk * qsj[hb][0]);
-                    y.y = fmaf(sk, dq[1], zk * qsj[hb][1]);
-                    y.z = fmaf(sk, dq[2], zk * qsj[hb][2]);
-                    y.w = fmaf(sk, dq[3], zk * qsj[hb][3]);
+                    y.x = fmaf(sk, dq[nb][hb][0], zk * qsj[hb][0]);
+                    y.y = fmaf(sk, dq[nb][hb][1], zk * qsj[hb][1]);
+                    y.z = fmaf(sk, dq[nb][hb][2], zk * qsj[hb][2]);
+                    y.w = fmaf(sk, dq[nb][hb][3], zk * qsj[hb][3]);
                     y_w[(nb * NHB + hb) * 64 + lane] = y;
                 }
             }
@@ -336,7 +359,7 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
                     const float av[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (4 * hb + r < G) lg[4 * hb + r] = valid ? av[r] * (qsc[4 * hb + r] * p.scale2) : -INFINITY;
+                        if (4 * hb + r < G) lg[4 * hb + r] = valid ? av[r] * qscale[4 * hb + r] : -INFINITY;
                 }
             }
 #pragma unroll
@@ -428,8 +451,11 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
         for (int v = v0 + wave; v < v1; v += 2 * kWaves) {
             TileRegs ta, tb;
             load_tile(v, ta);
+            __builtin_amdgcn_sched_barrier(0);  // keep tile v's loads ahead of tile v + 4's
             const bool two = v + kWaves < v1;
-            if (two) load_tile(v + kWaves, tb);
+            // issued unconditionally (a valid tile either way) so that the
+            // waits for tile v do not also wait for tile v + 4's loads
+            load_tile(two ? v + kWaves : v, tb);
             step(v, ta);
             if (two) step(v + kWaves, tb);
         }
