@@ -34,6 +34,9 @@
 //    through LDS. E is a running power of two keeping every w below 2^15;
 //    the bias is removed exactly with the sum of the same fp16 weights and
 //    sum(p * z_v) is accumulated in fp32 per token.
+//  * The query operands (q', the per-group sums, the per-head scale) are
+//    built in LDS by each INT4 workgroup while its first two tiles are in
+//    flight; a separate launch for them costs more than the work itself.
 //  * 16-bit tiles (kept columns, window ring) use v_dot2 / fp32 FMAs on the
 //    16-bit rows (they are a few percent of the tiles).
 //  * Each workgroup writes one partial (m, l, o[128]) per head; a second
@@ -53,10 +56,8 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 struct DecodeParams {
     hq_cache c;
-    const uint32_t* qa;    // [B][Hkv][NHB][4 ks][64 lanes][4] QK A operands (fp16 pairs)
-    const float* qc;       // [B][Hkv][NHB][4 j][4 r][2] (sum q' * bias, sum q') per group
-    const float* qsc;      // [B][Hkv][8] per-head 2^-k (q' = q * 2^k)
-    const uint32_t* qn;    // [B][Hkv][G][64] natural pairs for the 16-bit path
+    const uint32_t* qw;    // [B][Hq][64] query words (channels 2c, 2c + 1 of word c); 16-byte aligned
+    int32_t Hq;
     float* part_m;         // [B][Hkv][nsplit][G]
     float* part_l;         // [B][Hkv][nsplit][G]
     float* part_o;         // [B][Hkv][nsplit][G][128]
@@ -171,6 +172,8 @@ struct SplitSmem {
     float m[kWaves][G], l[kWaves][G];
     float o[kWaves][G][kD];
     uint4 qa[NHB * 4 * 64];
+    float qc[NHB * 4 * 8];  // [hb][group j][head r][sum q' * bias, sum q']
+    float qsc[8];           // per head 2^-k
 };
 
 template <int G, bool F16, int MODE>
@@ -213,33 +216,8 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
     }
 
     const int qt_cap = p.c.cap_q / kTile, kt_cap = p.c.cap_keep / kTile, wt_cap = W / kTile;
-    const uint32_t* qn = p.qn + (size_t)bg * G * 64;
-    const float* qsc = p.qsc + (size_t)bg * 8;
-
-    // QK A operands and the per-group constants of this lane's group j = lane/16
-    // the QK A operands live in LDS (read per use): [hb][ks][lane] x 16 bytes
-    auto& lds_qa = sm.qa;
-    for (int i = threadIdx.x; i < NHB * 4 * 64; i += 256)
-        lds_qa[i] = reinterpret_cast<const uint4*>(p.qa)[(size_t)bg * NHB * 256 + i];
-    __syncthreads();
-    // per-head logit scale 2^-k * sm_scale * log2(e), read once
-    float qscale[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) qscale[h] = qsc[h] * p.scale2;
-    floatx4 qb0[NHB];
-    float qsj[NHB][4];
-    halfx8 qreg[NHB][4];
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qreg[hb][ks] = __builtin_bit_cast(halfx8, lds_qa[(hb * 4 + ks) * 64 + lane]);
-        const float* qcj = p.qc + (((size_t)bg * NHB + hb) * 4 + (lane >> 4)) * 8;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            qb0[hb][r] = -qcj[2 * r];
-            qsj[hb][r] = qcj[2 * r + 1];
-        }
-    }
+    // the 16-bit tiles take the query's own words: word h*64 + c holds channels 2c, 2c + 1 of head h
+    const uint32_t* qn = p.qw + (size_t)bg * G * (kD / 2);  // Hq = Hkv * G
 
     // softmax state (lane = token), channel accumulators
     float m[G], l[G], zacc[G][4], wsb[G][4];
@@ -266,8 +244,6 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
     const CodeConsts cc = code_consts();
 
     if constexpr (MODE == 0) {
-        // Two tiles per wave per iteration: both tiles' loads are issued
-        // before either is used, doubling the bytes each wave keeps in flight.
         struct TileRegs {
             uint4 kd[4], kmv, vmv, vd[4];
         };
@@ -294,6 +270,90 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
 #pragma unroll
             for (int i = 0; i < 4; ++i) r.vd[i] = ld(rvc, v * kTileBytesQ + i * 1024);
         };
+        // The query is loaded first, then the first two tiles, so the query's
+        // operands are built while the tiles are in flight (waiting for the
+        // query leaves the 20 tile loads outstanding).
+        uint32_t qword[(G + kWaves - 1) / kWaves];
+#pragma unroll
+        for (int i = 0; i * kWaves < G; ++i) {
+            const int h = wave + i * kWaves;
+            qword[i] = h < G ? qn[h * 64 + lane] : 0u;
+        }
+        const int t0 = v0 + wave < v1 ? v0 + wave : v0;
+        TileRegs ta, tb;
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(t0, ta);
+        __builtin_amdgcn_sched_barrier(0);  // keep tile t0's loads ahead of tile t0 + 4's
+        load_tile(t0 + kWaves < v1 ? t0 + kWaves : t0, tb);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- query operands in LDS. Per head a power-of-two scale 2^k into
+        // fp16 range (q' = q 2^k, exact for every value above 2^-24 of the
+        // head's maximum). Lane l of the wave of head h holds channels 2l,
+        // 2l + 1: one word of the QK A operand (K-step ks = l/16 = channel
+        // group j, lane 4ks + h%4 + 16((l%16)/4), register l%4); the words of
+        // rows that hold another group's head, or no head, are zero. Per group
+        // the sums of q' and of q' * bias (exact in fp64, rounded once).
+        auto& lds_qa = sm.qa;
+        uint32_t* qa32 = reinterpret_cast<uint32_t*>(lds_qa);
+        for (int w = threadIdx.x; w < NHB * 1024; w += 256) {
+            const int hb = w >> 10, ks = (w >> 8) & 3, mrow = (w >> 2) & 15;
+            if ((mrow >> 2) != ks || 4 * hb + (mrow & 3) >= G) qa32[w] = 0u;
+        }
+        if (threadIdx.x < NHB * 16 && 4 * (threadIdx.x >> 4) + (threadIdx.x & 3) >= G) {
+            sm.qc[(threadIdx.x >> 2) * 8 + 2 * (threadIdx.x & 3)] = 0.f;
+            sm.qc[(threadIdx.x >> 2) * 8 + 2 * (threadIdx.x & 3) + 1] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i * kWaves < G; ++i) {
+            const int h = wave + i * kWaves;
+            if (h < G) {
+                const uint32_t word = qword[i];
+                const float x0 = h16_to_f32<F16>(word & 0xFFFFu), x1 = h16_to_f32<F16>(word >> 16);
+                const float mx = wave_max_fast(fmaxf(fabsf(x0), fabsf(x1)));
+                const int e = mx > 0.f ? (int)((__float_as_uint(mx) >> 23) & 0xFF) - 127 : 0;
+                const int k = mx > 0.f ? min(max(14 - e, -100), 100) : 0;
+                if (lane == 0) sm.qsc[h] = __builtin_ldexpf(1.0f, -k);
+                const uint32_t h0 = f32_to_f16_bits(__builtin_ldexpf(x0, k));
+                const uint32_t h1 = f32_to_f16_bits(__builtin_ldexpf(x1, k));
+                const int hb = h >> 2, ks = lane >> 4;
+                qa32[hb * 1024 + ks * 256 + (4 * ks + (h & 3) + 16 * ((lane & 15) >> 2)) * 4 + (lane & 3)] =
+                    h0 | (h1 << 16);
+                const double y0 = (double)f16_to_f32(h0), y1 = (double)f16_to_f32(h1);
+                double sq = y0 + y1;
+                double sb = y0 * (double)elem_bias((2 * lane) & 7) + y1 * (double)elem_bias((2 * lane + 1) & 7);
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    sq += __shfl_xor(sq, o);
+                    sb += __shfl_xor(sb, o);
+                }
+                if ((lane & 15) == 0) {
+                    sm.qc[(hb * 4 + ks) * 8 + 2 * (h & 3)] = (float)sb;
+                    sm.qc[(hb * 4 + ks) * 8 + 2 * (h & 3) + 1] = (float)sq;
+                }
+            }
+        }
+        __syncthreads();
+        // per-head logit scale 2^-k * sm_scale * log2(e); the QK A operands and
+        // the per-group constants of this lane's group j = lane/16
+        float qscale[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) qscale[h] = sm.qsc[h] * p.scale2;
+        floatx4 qb0[NHB];
+        float qsj[NHB][4];
+        halfx8 qreg[NHB][4];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) qreg[hb][ks] = __builtin_bit_cast(halfx8, lds_qa[(hb * 4 + ks) * 64 + lane]);
+            const float* qcj = sm.qc + (hb * 4 + (lane >> 4)) * 8;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                qb0[hb][r] = -qcj[2 * r];
+                qsj[hb][r] = qcj[2 * r + 1];
+            }
+        }
+
         auto step = [&](int v, const TileRegs& tr) {
         float lg[G];
         int count, tile;
@@ -448,24 +508,36 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
             lds_fence();
         }
         };
+        // Two tiles per wave per iteration: both tiles' loads are issued
+        // before either is used. The next pair's loads are issued once both
+        // steps are done (unconditionally within the pair, so that the waits
+        // for tile v never cover tile v + 4's loads).
         for (int v = v0 + wave; v < v1; v += 2 * kWaves) {
-            TileRegs ta, tb;
-            load_tile(v, ta);
-            __builtin_amdgcn_sched_barrier(0);  // keep tile v's loads ahead of tile v + 4's
-            const bool two = v + kWaves < v1;
-            // issued unconditionally (a valid tile either way) so that the
-            // waits for tile v do not also wait for tile v + 4's loads
-            load_tile(two ? v + kWaves : v, tb);
             step(v, ta);
-            if (two) step(v + kWaves, tb);
+            if (v + kWaves < v1) step(v + kWaves, tb);
+            if (v + 2 * kWaves < v1) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_tile(v + 2 * kWaves, ta);
+                __builtin_amdgcn_sched_barrier(0);
+                load_tile(v + 3 * kWaves < v1 ? v + 3 * kWaves : v + 2 * kWaves, tb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     } else {
+    // The query's words are read per tile with wave-uniform (scalar) loads.
+    // This barrier keeps them ordinary loads that the compiler reloads per
+    // tile rather than hoisting all 64*G of them out of the loop, which would
+    // not fit in scalar registers.
+    __syncthreads();
     for (int v = v0 + wave; v < v1; v += kWaves) {
         float lg[G];
         int count, tile;
         {
             // ----------------------------- token phase, 16-bit tile
             const bool keep = v < nqt + nkt;
+            // an offset the compiler cannot see through keeps the query's
+            // LDS reads inside the loop (hoisted, the 64*G words would take
+            // 64*G registers)
             tile = keep ? v - nqt : v - nqt - nkt;
             count = keep ? n_keep : nring;
             const bool valid = tile * kTile + lane < count;
@@ -643,131 +715,61 @@ __global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void k_decode_split(DecodePara
 // head's maximum), the QK A operands (row 4j + h of K-step ks holds q'_h on
 // group ks when j == ks, zero otherwise), the per-group sums of q' and of
 // q' * bias, and the natural 16-bit pairs for the 16-bit tiles.
-template <bool F16>
-__global__ __launch_bounds__(256) void k_decode_prep(const uint16_t* q, int Hq, int G, uint32_t* qa, float* qc,
-                                                     float* qsc, uint32_t* qn) {
-    __shared__ float qf[8][kD];
-    __shared__ uint16_t q16[8][kD];
-    __shared__ int kq[8];
-    const int g = blockIdx.x, b = blockIdx.y, Hkv = gridDim.x;
-    const int bg = b * Hkv + g;
-    const int tid = threadIdx.x;
-    const int NHB = (G + 3) / 4;
-    for (int i = tid; i < G * kD; i += 256) {
-        const int h = i / kD, c = i % kD;
-        const uint16_t bits = q[((size_t)b * Hq + g * G + h) * kD + c];
-        qf[h][c] = h16_to_f32<F16>(bits);
-        if (c < 64) {
-            const uint16_t* qh = q + ((size_t)b * Hq + g * G + h) * kD;
-            qn[((size_t)bg * G + h) * 64 + c] = (uint32_t)qh[2 * c] | ((uint32_t)qh[2 * c + 1] << 16);
-        }
-    }
-    __syncthreads();
-    if (tid < G) {
-        float mx = 0.f;
-        for (int c = 0; c < kD; ++c) mx = fmaxf(mx, fabsf(qf[tid][c]));
-        const int e = mx > 0.f ? (int)((__float_as_uint(mx) >> 23) & 0xFF) - 127 : 0;
-        const int k = mx > 0.f ? min(max(14 - e, -100), 100) : 0;
-        kq[tid] = k;
-        qsc[(size_t)bg * 8 + tid] = __builtin_ldexpf(1.0f, -k);
-    }
-    __syncthreads();
-    for (int i = tid; i < G * kD; i += 256) {
-        const int h = i / kD, c = i % kD;
-        q16[h][c] = (uint16_t)f32_to_f16_bits(__builtin_ldexpf(qf[h][c], kq[h]));
-    }
-    __syncthreads();
-    for (int w = tid; w < NHB * 1024; w += 256) {
-        const int hb = w >> 10, ks = (w >> 8) & 3, ln = (w >> 2) & 63, reg = w & 3;
-        const int mrow = ln & 15, j = mrow >> 2, h = 4 * hb + (mrow & 3);
-        uint32_t val = 0;
-        if (j == ks && h < G) {
-            const int c0 = 32 * ks + 8 * (ln >> 4) + 2 * reg;
-            val = (uint32_t)q16[h][c0] | ((uint32_t)q16[h][c0 + 1] << 16);
-        }
-        qa[((size_t)bg * NHB + hb) * 1024 + w - hb * 1024] = val;
-    }
-    if (tid < NHB * 16) {
-        const int hb = tid >> 4, j = (tid >> 2) & 3, r = tid & 3, h = 4 * hb + r;
-        double sb = 0.0, sq = 0.0;
-        if (h < G) {
-            for (int c = 32 * j; c < 32 * j + 32; ++c) {
-                const double x = (double)f16_to_f32(q16[h][c]);
-                sq += x;
-                sb += x * (double)elem_bias(c & 7);
-            }
-        }
-        float* dst = qc + (((size_t)bg * NHB + hb) * 4 + j) * 8 + 2 * r;
-        dst[0] = (float)sb;
-        dst[1] = (float)sq;
-    }
-}
-
-__global__ __launch_bounds__(128) void k_decode_reduce(const hq_cache c, const float* part_m, const float* part_l,
-                                                       const float* part_o, int nsplit, int tps, int G, int Hq,
+__global__ __launch_bounds__(128) void k_decode_reduce(const hq_cache c, const float* __restrict__ part_m,
+                                                       const float* __restrict__ part_l,
+                                                       const float* __restrict__ part_o, int nsplit, int G, int Hq,
                                                        void* out, int out_dt) {
-    extern __shared__ float sh[];  // [nsplit] weights, then 1/L
+    // One thread per output channel. The partials are merged in chunks of R
+    // splits whose loads are all issued before any of them is used; a chunk
+    // whose maximum exceeds the running one rescales the running sums (every
+    // split writes a partial; empty ones have m = -inf and are skipped).
+    constexpr int R = 16;
     const int gh = blockIdx.x, b = blockIdx.y;
     const int g = gh / G, h = gh % G, d = threadIdx.x;
     const int bg = b * c.Hkv + g;
-    (void)tps;
-    const int active = nsplit;  // every split writes a partial (empty ones have m = -inf)
     const size_t base = (size_t)bg * nsplit * G + h;
-    float* wsp = sh;
-    __shared__ float red[2];
-    // split weights 2^(m_s - M) and 1/L, one split per thread
-    float ms = -INFINITY, ls = 0.f;
-    if (d < active) {
-        ms = part_m[base + (size_t)d * G];
-        ls = part_l[base + (size_t)d * G];
-    }
-    for (int i = d + 128; i < active; i += 128) {  // more than 128 splits: fold
-        const float m2 = part_m[base + (size_t)i * G];
-        if (m2 > ms) ms = m2;
-    }
-    float M = wave_max(ms);
-    if ((d & 63) == 0) red[d >> 6] = M;
-    __syncthreads();
-    M = fmaxf(red[0], red[1]);
-    __syncthreads();
-    float L = 0.f;
-    for (int i = d; i < active; i += 128) {
-        const float mi = part_m[base + (size_t)i * G];
-        const float f = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - M);
-        wsp[i] = f;
-        L = fmaf(f, part_l[base + (size_t)i * G], L);
-    }
-    (void)ls;
-    L = wave_sum(L);
-    if ((d & 63) == 0) red[d >> 6] = L;
-    __syncthreads();
-    const float invL = 1.0f / (red[0] + red[1]);
     const float* po = part_o + base * kD + d;
-    float O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int sp = 0;
-    for (; sp + 8 <= active; sp += 8) {
+    float run_m = -INFINITY, L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += R) {
+        float mv[R], lv[R], ov[R];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) O[j] = fmaf(wsp[sp + j], po[(size_t)(sp + j) * G * kD], O[j]);
+        for (int j = 0; j < R; ++j) {
+            const int i = min(s0 + j, nsplit - 1);
+            mv[j] = part_m[base + (size_t)i * G];
+            lv[j] = part_l[base + (size_t)i * G];
+            ov[j] = po[(size_t)i * G * kD];
+        }
+        float mc = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            if (s0 + j < nsplit) mc = fmaxf(mc, mv[j]);
+        const float nm = fmaxf(run_m, mc);
+        if (nm == -INFINITY) continue;
+        const float sc = run_m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(run_m - nm);
+        L *= sc;
+        O *= sc;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            if (s0 + j < nsplit && mv[j] != -INFINITY) {
+                const float f = __builtin_amdgcn_exp2f(mv[j] - nm);
+                L = fmaf(f, lv[j], L);
+                O = fmaf(f, ov[j], O);
+            }
+        }
+        run_m = nm;
     }
-    for (; sp < active; ++sp) O[0] = fmaf(wsp[sp], po[(size_t)sp * G * kD], O[0]);
-    const float r = (((O[0] + O[1]) + (O[2] + O[3])) + ((O[4] + O[5]) + (O[6] + O[7]))) * invL;
-    store_out(out, out_dt, ((size_t)b * Hq + g * G + h) * kD + d, r);
+    store_out(out, out_dt, ((size_t)b * Hq + g * G + h) * kD + d, O / L);
 }
 
 struct WsLayout {
-    size_t qa, qc, qsc, qn, pm, pl, po, total;
+    size_t pm, pl, po, total;
 };
 inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 WsLayout ws_layout(const hq_cache& c, int32_t Hq, int32_t nsplit) {
     const size_t BG = (size_t)c.B * c.Hkv;
     const int G = Hq / c.Hkv;
-    const int NHB = (G + 3) / 4;
     WsLayout w;
-    w.qa = 0;
-    w.qc = w.qa + al(BG * NHB * 1024 * 4);
-    w.qsc = w.qc + al(BG * NHB * 32 * 4);
-    w.qn = w.qsc + al(BG * 8 * 4);
-    w.pm = w.qn + al(BG * G * 64 * 4);
+    w.pm = 0;
     w.pl = w.pm + al(BG * nsplit * G * 4);
     w.po = w.pl + al(BG * nsplit * G * 4);
     w.total = w.po + al(BG * nsplit * G * kD * 4);
@@ -778,6 +780,8 @@ template <int G, bool F16>
 void launch_split(const DecodeParams& p, int Hkv, int B, hipStream_t s) {
     // INT4 splits (x < nsq) come first in dispatch order; the 16-bit ones
     // fill in as slots free up.
+    // the query goes in as a separate read-only, non-aliased argument so that
+    // its wave-uniform reads become scalar loads
     k_decode_split<G, F16><<<dim3(p.nsplit, Hkv, B), 256, 0, s>>>(p);
 }
 
@@ -804,10 +808,8 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     char* ws = static_cast<char*>(d.ws);
     DecodeParams p;
     p.c = c;
-    p.qa = reinterpret_cast<uint32_t*>(ws + w.qa);
-    p.qc = reinterpret_cast<float*>(ws + w.qc);
-    p.qsc = reinterpret_cast<float*>(ws + w.qsc);
-    p.qn = reinterpret_cast<uint32_t*>(ws + w.qn);
+    p.qw = static_cast<const uint32_t*>(q);
+    p.Hq = d.Hq;
     p.part_m = reinterpret_cast<float*>(ws + w.pm);
     p.part_l = reinterpret_cast<float*>(ws + w.pl);
     p.part_o = reinterpret_cast<float*>(ws + w.po);
@@ -818,17 +820,6 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     p.G = d.G;
     p.scale2 = d.sm_scale_log2;
     const bool f16 = c.dt == HQ_F16;
-    dim3 pg(c.Hkv, c.B);
-    if (f16)
-        k_decode_prep<true><<<pg, 256, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G, const_cast<uint32_t*>(p.qa),
-                                               const_cast<float*>(p.qc), const_cast<float*>(p.qsc),
-                                               const_cast<uint32_t*>(p.qn));
-    else
-        k_decode_prep<false><<<pg, 256, 0, s>>>(static_cast<const uint16_t*>(q), d.Hq, d.G, const_cast<uint32_t*>(p.qa),
-                                                const_cast<float*>(p.qc), const_cast<float*>(p.qsc),
-                                                const_cast<uint32_t*>(p.qn));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     switch (d.G * 2 + (f16 ? 1 : 0)) {
         case 2: launch_split<1, false>(p, c.Hkv, c.B, s); break;
         case 3: launch_split<1, true>(p, c.Hkv, c.B, s); break;
@@ -840,11 +831,10 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
         case 17: launch_split<8, true>(p, c.Hkv, c.B, s); break;
         default: return hipErrorInvalidValue;
     }
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t shb = (size_t)d.nsplit * sizeof(float);
-    k_decode_reduce<<<dim3(c.Hkv * d.G, c.B), 128, shb, s>>>(c, p.part_m, p.part_l, p.part_o, d.nsplit,
-                                                              d.tiles_per_split, d.G, d.Hq, out, (int)out_dt);
+    k_decode_reduce<<<dim3(c.Hkv * d.G, c.B), 128, 0, s>>>(c, p.part_m, p.part_l, p.part_o, d.nsplit, d.G, d.Hq,
+                                                          out, (int)out_dt);
     return hipGetLastError();
 }
 
