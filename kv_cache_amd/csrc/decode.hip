@@ -62,7 +62,7 @@ struct DecodeParams {
     float* part_l;         // [B][Hkv][nsplit][G]
     float* part_o;         // [B][Hkv][nsplit][G][128]
     int32_t nsplit, tps, G;
-    int32_t nsq, tps16;    // INT4 splits (first nsq partials), tiles per 16-bit split
+    int32_t nsq, tps16;    // INT4 splits (first nsq partials); 16-bit tiles per split at capacity
     float scale2;          // sm_scale * log2(e)
 };
 
@@ -159,10 +159,10 @@ __device__ inline void store_out(void* out, int dt, size_t i, float r) {
 }
 
 
-// MODE 0: the INT4 tiles of a (b, g), split s = blockIdx.x covers tiles
-// [s*tps, (s+1)*tps); MODE 1: its 16-bit tiles (kept, then ring), split s
-// covers [s*tps16, ...) of them and writes partial nsq + s. Every workgroup
-// writes its partial (empty ones carry m = -inf).
+// MODE 0: the n INT4 tiles of a (b, g); split s = blockIdx.x < nsq covers
+// tiles [s*n/nsq, (s+1)*n/nsq). MODE 1: its 16-bit tiles (kept, then ring),
+// divided the same way over the remaining splits; split s writes partial
+// nsq + s. Every workgroup writes its partial (empty ones carry m = -inf).
 template <int G>
 struct SplitSmem {
     static constexpr int NHB = (G + 3) / 4;
@@ -200,8 +200,11 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
     const int nqt = (n_q + kTile - 1) / kTile, nkt = (n_keep + kTile - 1) / kTile;
     const int nwt = (nring + kTile - 1) / kTile;
     const int total = nqt + nkt + nwt;
-    const int v0 = MODE == 0 ? s * p.tps : nqt + s * p.tps16;
-    const int v1 = MODE == 0 ? min(v0 + p.tps, nqt) : min(v0 + p.tps16, total);
+    // the splits of each kind divide that kind's tiles evenly (the launch
+    // sizes the split counts for the capacity, the counts give the tiles)
+    const int n16s = p.nsplit - p.nsq, n16t = total - nqt;
+    const int v0 = MODE == 0 ? s * nqt / p.nsq : nqt + s * n16t / n16s;
+    const int v1 = MODE == 0 ? (s + 1) * nqt / p.nsq : nqt + (s + 1) * n16t / n16s;
     const int split_out = MODE == 0 ? s : p.nsq + s;
     if (v0 >= v1) {  // nothing here: an empty partial
         const size_t pb = ((size_t)bg * p.nsplit + split_out) * G;
@@ -529,25 +532,31 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
     // tile rather than hoisting all 64*G of them out of the loop, which would
     // not fit in scalar registers.
     __syncthreads();
+    uint4 kk16[16], vv16[16];
     for (int v = v0 + wave; v < v1; v += kWaves) {
         float lg[G];
         int count, tile;
         {
             // ----------------------------- token phase, 16-bit tile
             const bool keep = v < nqt + nkt;
-            // an offset the compiler cannot see through keeps the query's
-            // LDS reads inside the loop (hoisted, the 64*G words would take
-            // 64*G registers)
             tile = keep ? v - nqt : v - nqt - nkt;
             count = keep ? n_keep : nring;
             const bool valid = tile * kTile + lane < count;
             const uint8_t* kt = keep ? reinterpret_cast<const uint8_t*>(p.c.k_keep) + ((size_t)bg * kt_cap + tile) * kTileBytes16
                                      : reinterpret_cast<const uint8_t*>(p.c.k_win) + ((size_t)bg * wt_cap + tile) * kTileBytes16;
+            const uint8_t* vt = keep ? reinterpret_cast<const uint8_t*>(p.c.v_keep) + ((size_t)bg * kt_cap + tile) * kTileBytes16
+                                     : reinterpret_cast<const uint8_t*>(p.c.v_win) + ((size_t)bg * wt_cap + tile) * kTileBytes16;
+            // every K and V load of the tile is issued up front: one memory
+            // latency per tile (V does not depend on the scores)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) kk16[c] = *reinterpret_cast<const uint4*>(kt + k16_off(lane, c));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) vv16[i] = *reinterpret_cast<const uint4*>(vt + i * 1024 + lane * 16);
 #pragma unroll
             for (int h = 0; h < G; ++h) lg[h] = 0.f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
-                const uint4 kk = *reinterpret_cast<const uint4*>(kt + k16_off(lane, c));
+                const uint4 kk = kk16[c];
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     const uint32_t* qh = qn + h * 64 + 4 * c;
@@ -591,13 +600,10 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
             for (int h = 0; h < G; ++h) p_w[lane * G + h] = pr_h[h] * k16;
             lds_fence();
             // ----------------------------- channel phase, 16-bit V
-            const bool keep = v < nqt + nkt;
-            const uint8_t* vt = keep ? reinterpret_cast<const uint8_t*>(p.c.v_keep) + ((size_t)bg * kt_cap + tile) * kTileBytes16
-                                     : reinterpret_cast<const uint8_t*>(p.c.v_win) + ((size_t)bg * wt_cap + tile) * kTileBytes16;
-#pragma unroll 4
+#pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int slot = 16 * u + i;
-                const uint4 vv = *reinterpret_cast<const uint4*>(vt + i * 1024 + lane * 16);
+                const uint4 vv = vv16[i];
                 if (tile * kTile + slot < count) {
                     float x[8];
 #pragma unroll
@@ -785,7 +791,7 @@ void launch_split(const DecodeParams& p, int Hkv, int B, hipStream_t s) {
     k_decode_split<G, F16><<<dim3(p.nsplit, Hkv, B), 256, 0, s>>>(p);
 }
 
-constexpr int kTps16 = 8;  // 16-bit tiles per split
+constexpr int kTps16 = 16;  // 16-bit tiles per split
 
 }  // namespace
 
