@@ -6,7 +6,7 @@ One step = one pass of every row of the hot path over one batch of seeded
 synthetic input:
   decode workload (8B GQA shape: B=16, 32 Q / 8 KV heads, D=128, T=32768):
     probe + top-k select -> quantize/pack -> append one token -> decode
-    (prep + split-K + cross-split reduce);
+    (split-K + cross-split reduce);
   prefill workload (32 Q / 8 KV heads, causal, T=16384):
     probe + select on the last 64 rows -> INT8 block quantization + hybrid
     attention (skipped if the prefill operator is not built).
@@ -381,7 +381,7 @@ def main():
     if not args.decode_only:
         res["probe_select_ms"] = round(tm.ms("probe_select"), 3)
         res["quantize_ms"] = round(tm.ms("quantize_kv"), 3)
-    res["roofline"] = {"bound": "hbm", "kernel": "hq_decode_attn (prep + split-K + reduce)",
+    res["roofline"] = {"bound": "hbm", "kernel": "hq_decode_attn (split-K + reduce)",
                        "achieved": round(dbytes / (dec_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                        "unit": "GB/s", "frac": round(dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                        "traffic": decode_traffic(dbytes)}
