@@ -127,19 +127,19 @@ def prefill_roofline(T, W, sel_idx, sel_cnt, G, ms):
     peak = total / floor_s / 1e12
     return {"bound": "mfma", "kernel": "hq_prefill_attn (INT8 stage + hybrid attention)",
             "achieved": round(achieved, 1), "peak": round(peak, 1), "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None,
+            "frac": round(achieved / peak, 4), "traffic": prefill_traffic(),
             "floor_us": round(floor_s * 1e6, 1), "int8_qk_pair_frac": round(low / (exact + low), 4)}
 
 
-def decode_traffic(launch_bytes_alg):
-    """HBM bytes per launch of the decode split kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, each scaled by the factor a
-    plain copy of known size gives for the same counter; None when the kernel
-    source changed after the counters were taken."""
+def committed_traffic(profile, source, key):
+    """HBM bytes per call from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary (each counter scaled by the factor a plain copy of known size
+    gives for it); None when the kernel source changed after the counters
+    were taken."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", "decode_8b_32k_split_traffic.md")
-    src = os.path.join(ROOT, "kv_cache_amd", "csrc", "decode.hip")
+    path = os.path.join(ROOT, "profiles", profile)
+    src = os.path.join(ROOT, "kv_cache_amd", "csrc", source)
     try:
         text = open(path).read()
         m = re.search(r"```json\n(.*?)\n```", text, re.S)
@@ -147,9 +147,17 @@ def decode_traffic(launch_bytes_alg):
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except (OSError, AttributeError, ValueError):
         return None
-    if rec.get("decode_hip_sha256") != sha:
+    if rec.get(key) != sha:
         return None
     return int(rec["hbm_bytes_per_launch"])
+
+
+def decode_traffic(launch_bytes_alg):
+    return committed_traffic("decode_8b_32k_split_traffic.md", "decode.hip", "decode_hip_sha256")
+
+
+def prefill_traffic():
+    return committed_traffic("prefill_8b_16k_traffic.md", "prefill.hip", "prefill_hip_sha256")
 
 
 def cpu_baseline(inp, sels_gpu, budget_s=20.0):
