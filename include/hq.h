@@ -248,8 +248,9 @@ size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq);
  *   o1 = A(B Hq Tp D)             sQ fp32 [B][Hq][nb]
  *   o2 = o1 + A(4 B Hq nb)        K8 int8 [B][Hkv][Tp][D]
  *   o3 = o2 + A(B Hkv Tp D)       sK fp32 [B][Hkv][nb]
- * the rest is staging (fp16 V^T blocks, selected-column masks and gathered
- * selected K / V tiles).
+ * the rest is staging (fp16 V^T blocks, with and without the selected
+ * columns, selected-column masks and row-sum weights, gathered selected K / V
+ * tiles).
  * Errors: HQ_ERR_UNSUPPORTED for D != 128, Hq % Hkv != 0, G = Hq / Hkv not
  * in {1, 2, 4, 8} or an unsupported dtype; HQ_ERR_CAPACITY if ws_bytes is
  * too small; HQ_ERR_INVALID_ARG for null pointers or T outside [1, 2^22]. */

@@ -48,7 +48,7 @@ constexpr int kBM = 128;  // query rows per workgroup
 constexpr int kBN = 64;   // keys per block
 
 struct PfLayout {
-    size_t q8, sq, k8, sk, vt, mask, ksel, vtsel, total;
+    size_t q8, sq, k8, sk, vt, mask, ksel, vtsel, vt0, wsel, total;
     int nblk, nsel_tiles;
 };
 inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -66,7 +66,9 @@ PfLayout pf_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, const hq_polic
     w.mask = w.vt + al((size_t)B * Hkv * Tp * kD * 2);
     w.ksel = w.mask + al((size_t)B * Hkv * w.nblk * 8);
     w.vtsel = w.ksel + al((size_t)B * Hkv * w.nsel_tiles * kBN * kD * 2);
-    w.total = w.vtsel + al((size_t)B * Hkv * w.nsel_tiles * kBN * kD * 2);
+    w.vt0 = w.vtsel + al((size_t)B * Hkv * w.nsel_tiles * kBN * kD * 2);
+    w.wsel = w.vt0 + al((size_t)B * Hkv * Tp * kD * 2);
+    w.total = w.wsel + al((size_t)B * Hkv * w.nblk * 32 * 4);
     return w;
 }
 
@@ -146,6 +148,9 @@ struct PfParams {
     uint64_t* mask;      // [B][Hkv][nblk] selected-column bits
     uint16_t* ksel;      // [B][Hkv][nsel_tiles][64][D] 16-bit K rows of selected columns
     uint16_t* vtsel;     // [B][Hkv][nsel_tiles][D][64] fp16 V^T of selected columns, vt_key order
+    uint16_t* vt0;       // as vt, with the columns of selected keys zero (the INT8 blocks' PV operand)
+    uint32_t* wsel;      // [B][Hkv][nblk][2][16] fp16 pairs: 1 for an unselected key, 0 for a selected
+                         // one, in the order of the P^T words of lane half 0 / 1
     float* out;
     int out_dt;
     int B, Hq, Hkv, G, T, nblk, nsel_tiles, sel_stride, W;
@@ -185,17 +190,8 @@ __global__ __launch_bounds__(256) void k_pf_quant_kv(PfParams p) {
             vs[r][c0 + 8 * i + 2 * j + 1] = (uint16_t)f32_to_f16_bits(h16_to_f32<F16>(w[j] >> 16));
         }
     }
-    __syncthreads();
-    uint16_t* vdst = p.vt + ((size_t)bg * p.nblk + blk) * kD * kBN;
-    for (int e = t; e < kD * 8; e += 256) {   // (channel, 8-key segment)
-        const int ch = e >> 3, k0 = (e & 7) * 8;
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            w[j] = (uint32_t)vs[vt_key(k0 + 2 * j)][ch] | ((uint32_t)vs[vt_key(k0 + 2 * j + 1)][ch] << 16);
-        *reinterpret_cast<uint4*>(vdst + (size_t)ch * kBN + k0) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
     // selected-column bits of this block
+    __shared__ uint64_t sbits;
     if (t == 0) {
         const int32_t* S = p.sel_idx + (size_t)bg * p.sel_stride;
         const int k = min(max(p.sel_count[bg], 0), p.sel_stride);
@@ -209,6 +205,34 @@ __global__ __launch_bounds__(256) void k_pf_quant_kv(PfParams p) {
         for (int i = lo; i < k && S[i] < blk * kBN + kBN; ++i)
             if (S[i] >= blk * kBN) bits |= 1ull << (S[i] - blk * kBN);
         p.mask[(size_t)bg * p.nblk + blk] = bits;
+        sbits = bits;
+    }
+    __syncthreads();
+    const uint64_t bits = sbits;
+    uint16_t* vdst = p.vt + ((size_t)bg * p.nblk + blk) * kD * kBN;
+    uint16_t* v0dst = p.vt0 + ((size_t)bg * p.nblk + blk) * kD * kBN;
+    for (int e = t; e < kD * 8; e += 256) {   // (channel, 8-key segment)
+        const int ch = e >> 3, k0 = (e & 7) * 8;
+        uint32_t w[4], w0[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ka = vt_key(k0 + 2 * j), kb = vt_key(k0 + 2 * j + 1);
+            w[j] = (uint32_t)vs[ka][ch] | ((uint32_t)vs[kb][ch] << 16);
+            w0[j] = w[j] & (((bits >> ka) & 1ull) ? 0xFFFF0000u : 0xFFFFFFFFu) &
+                    (((bits >> kb) & 1ull) ? 0x0000FFFFu : 0xFFFFFFFFu);
+        }
+        *reinterpret_cast<uint4*>(vdst + (size_t)ch * kBN + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(v0dst + (size_t)ch * kBN + k0) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+    }
+    // row-sum weights: word 4j + e of lane half hf pairs the keys of P^T
+    // operand j, elements 2e and 2e + 1 (S^T tile j/2, registers
+    // 8(j%2) + 2e and + 1, i.e. keys 32(j/2) + 8(2(j%2) + e/2) + 4hf + 2(e%2) and + 1)
+    if (t < 32) {
+        const int hf = t >> 4, j = (t >> 2) & 3, e = t & 3;
+        const int ka = 32 * (j >> 1) + 8 * (2 * (j & 1) + (e >> 1)) + 4 * hf + 2 * (e & 1);
+        const uint32_t one = 0x3C00u;  // fp16 1.0
+        p.wsel[((size_t)bg * p.nblk + blk) * 32 + t] =
+            (((bits >> ka) & 1ull) ? 0u : one) | (((bits >> (ka + 1)) & 1ull) ? 0u : (one << 16));
     }
 }
 
@@ -265,6 +289,7 @@ struct Smem {
     int8_t k8[2][kBN * kK8Stride];
     uint8_t vt[2][kD * kVtStride];
     uint8_t k16[kBN * kK16Stride];
+    uint4 wt[2][8];  // row-sum weights of the INT8 blocks (two slots, like vt)
 };
 
 // S^T register r of lane half hf in a 32-key MFMA tile holds key
@@ -389,12 +414,13 @@ __device__ inline floatx16 st_16_tile(const uint8_t* k16, const intx4 (&qb)[8], 
 // (0-3, 8-11, 4-7, 12-15) so lane half hf reads its 8 keys with one 128-bit load.
 __device__ inline void pv_block(const uint8_t* vt, const halfx8 (&pb)[4], floatx16 (&o)[4]) {
     const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
+    // key step outer, channel tile inner: consecutive MFMAs write different
+    // accumulators
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        const uint8_t* row = vt + (32 * ct + m) * kVtStride + 16 * hf;
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const intx4 a = *reinterpret_cast<const intx4*>(row + 32 * j);
+        for (int ct = 0; ct < 4; ++ct) {
+            const intx4 a = *reinterpret_cast<const intx4*>(vt + (32 * ct + m) * kVtStride + 16 * hf + 32 * j);
             o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a), pb[j], o[ct], 0, 0, 0);
         }
     }
@@ -441,6 +467,22 @@ __device__ inline void pack_p(const float (&p)[2][16], halfx8 (&pb)[4], float& l
         for (int e = 0; e < 4; ++e) {
             w[e] = pack_h2(p[j >> 1][8 * (j & 1) + 2 * e], p[j >> 1][8 * (j & 1) + 2 * e + 1]);
             l = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[e]), ones, l, false);
+        }
+        const intx4 v = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        pb[j] = __builtin_bit_cast(halfx8, v);
+    }
+}
+
+// As pack_p, with the row sum weighted per key (fp16 pairs: 0 drops a key).
+__device__ inline void pack_p_w(const float (&p)[2][16], halfx8 (&pb)[4], float& l, const uint4 (&wt)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t w[4];
+        const uint32_t ww[4] = {wt[j].x, wt[j].y, wt[j].z, wt[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            w[e] = pack_h2(p[j >> 1][8 * (j & 1) + 2 * e], p[j >> 1][8 * (j & 1) + 2 * e + 1]);
+            l = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w[e]), __builtin_bit_cast(half2_t, ww[e]), l, false);
         }
         const intx4 v = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
         pb[j] = __builtin_bit_cast(halfx8, v);
@@ -615,18 +657,32 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
     // kb in V slot kb%2; iteration kb loads K8[kb+2] and V^T[kb+1] into
     // registers (buffer loads with scalar offsets) and stores them into the
     // slots freed by the previous iteration; one barrier per iteration.
+    // Selected columns are dropped without per-element work: their V^T
+    // columns are zero (vt0) and their row-sum weights are zero (wsel), so
+    // p of a selected key is computed but contributes nothing. (Its p stays
+    // finite: phase B has seen the key's exact score, so the reference is at
+    // most 2^8 below it, and the INT8 score differs from it by far less than
+    // the 2^7 headroom left to fp16.)
     if (kb_band > 0) {
         const int t = threadIdx.x;
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(p.k8 + (size_t)bg * Tp * kD), (short)0, kb_band * kBN * kD, 0x00020000);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(p.vt + (size_t)bg * p.nblk * kD * kBN), (short)0, kb_band * kD * kBN * 2, 0x00020000);
+            (void*)(p.vt0 + (size_t)bg * p.nblk * kD * kBN), (short)0, kb_band * kD * kBN * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.wsel + (size_t)bg * p.nblk * 32), (short)0, kb_band * 128, 0x00020000);
         const int voff = 16 * t;  // chunk t of a block; rows of K8 and V^T are both 128 bytes
         auto ld = [&](const __amdgpu_buffer_rsrc_t& r, int soff) {
             return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
         };
+        // the 128-byte weight record of a block: every thread loads chunk t % 8
+        auto ldw = [&](int soff) {
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * (t & 7), soff, 0));
+        };
         __syncthreads();  // the band phases are done with LDS
         {
+            const uint4 w0 = ldw(0);
+            if (t < 8) sm.wt[0][t] = w0;
             stage_store(sm, 0, Stage{ld(rk, 0), ld(rk, 4096), ld(rv, 0), ld(rv, 4096), ld(rv, 8192), ld(rv, 12288)});
             if (kb_band > 1) {
                 st16(sm.k8[1], t, kK8Stride, ld(rk, 8192));
@@ -644,9 +700,14 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
             const uint4 k0 = ld(rk, kn2 * 8192), k1 = ld(rk, kn2 * 8192 + 4096);
             const uint4 v0 = ld(rv, kn1 * 16384), v1 = ld(rv, kn1 * 16384 + 4096);
             const uint4 v2 = ld(rv, kn1 * 16384 + 8192), v3 = ld(rv, kn1 * 16384 + 12288);
-            if (kb + 1 < kb_band) st_int8(sm.k8[cur ^ 1], q8b, sn);
+            const uint4 wn = ldw(kn1 * 128);
+            // QK of the next block (on the last block: of stale LDS data, unused),
+            // unconditional so that it shares the softmax's basic block
+            st_int8(sm.k8[cur ^ 1], q8b, sn);
             const float c8 = sq * p.sk[(size_t)bg * p.nblk + kb] * c16;
-            const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
+            uint4 wt[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wt[j] = sm.wt[cur][4 * hf + j];
             // No block maximum on the common path: p = 2^(s - m_ref) with the
             // reference from the earlier blocks (the band and the selected
             // columns come first, so it is normally the row maximum already).
@@ -660,10 +721,20 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) x[tt][r] = __builtin_amdgcn_exp2f(fmaf((float)sc[tt][r], c8, nmr));
-                mask_selected(selbits, x, 0.0f);
-                pack_p(x, pb, lb);
+                pack_p_w(x, pb, lb, wt);
+                // interleave: the loads first, then each of the next block's
+                // QK MFMAs followed by a share of this block's softmax VALU work
+                __builtin_amdgcn_sched_group_barrier(0x0020, 7, 0);  // buffer loads
+                __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);  // LDS reads
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x0002, 14, 0); // VALU
+                }
             }
             if (__builtin_amdgcn_ballot_w64(!(lb <= 32768.0f))) {
+                const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
                 mask_selected(selbits, sc, (int)INT_MIN);
                 int imax = INT_MIN;
 #pragma unroll
@@ -690,6 +761,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
             st16(sm.vt[cur ^ 1], t + 256, kVtStride, v1);
             st16(sm.vt[cur ^ 1], t + 512, kVtStride, v2);
             st16(sm.vt[cur ^ 1], t + 768, kVtStride, v3);
+            if (t < 8) sm.wt[cur ^ 1][t] = wn;
             __syncthreads();
         };
         for (int kb = 0; kb < kb_band; kb += 2) {
@@ -758,6 +830,8 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, int32_t B
     p.mask = reinterpret_cast<uint64_t*>(base + w.mask);
     p.ksel = reinterpret_cast<uint16_t*>(base + w.ksel);
     p.vtsel = reinterpret_cast<uint16_t*>(base + w.vtsel);
+    p.vt0 = reinterpret_cast<uint16_t*>(base + w.vt0);
+    p.wsel = reinterpret_cast<uint32_t*>(base + w.wsel);
     p.out = static_cast<float*>(out);
     p.out_dt = (int)out_dt;
     p.B = B;
