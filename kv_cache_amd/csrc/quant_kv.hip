@@ -18,6 +18,17 @@
 namespace hq {
 namespace {
 
+// The cache is written once here and read by later calls: streaming
+// (non-temporal) stores keep it from sitting dirty in the caches, where its
+// write-backs would compete with the next kernel's reads.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline void st_nt(void* ptr, uint32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(ptr)); }
+__device__ inline void st_nt(void* ptr, int32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<int32_t*>(ptr)); }
+__device__ inline void st_nt(void* ptr, const uint4& v) {
+    const u32x4_t x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(ptr));
+}
+
 struct QuantParams {
     const uint16_t* k;
     const uint16_t* v;
@@ -106,12 +117,10 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
         if (valid) {
 #pragma unroll
             for (int w = 0; w < 4; ++w)
-                *reinterpret_cast<uint32_t*>(kc + kq_word(t, kGroup * grp + 8 * w)) = to_mf_order(kp[w]);
-            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.c.k_meta) + meta_base + kmeta_word(t, grp)) =
-                ks | (kz << 16);
-            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.c.v_meta) + meta_base + vmeta_word(t, grp)) =
-                vs | (vz << 16);
-            if (grp == 0) p.c.q_pos[(size_t)bg * p.c.cap_q + n] = pos;
+                st_nt(kc + kq_word(t, kGroup * grp + 8 * w), to_mf_order(kp[w]));
+            st_nt(reinterpret_cast<uint8_t*>(p.c.k_meta) + meta_base + kmeta_word(t, grp), (uint32_t)(ks | (kz << 16)));
+            st_nt(reinterpret_cast<uint8_t*>(p.c.v_meta) + meta_base + vmeta_word(t, grp), (uint32_t)(vs | (vz << 16)));
+            if (grp == 0) st_nt(p.c.q_pos + (size_t)bg * p.c.cap_q + n, (int32_t)pos);
         }
         __syncthreads();
         // 1024 V words per tile: word (channel ch, slot octet o) holds slots 8o..8o+7
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
                 const uint32_t code = (vstage[8 * o + e][ch >> 5][(ch >> 3) & 3] >> (4 * (ch & 7))) & 0xFu;
                 w |= code << mf_nib(e);
             }
-            *reinterpret_cast<uint32_t*>(vc + vq_word(8 * o, ch)) = w;
+            st_nt(vc + vq_word(8 * o, ch), w);
         }
         return;
     }
@@ -148,8 +157,8 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
             const int c = part * 4 + c4;
-            *reinterpret_cast<uint4*>(kd + k16_off(t, c)) = ks[c];
-            *reinterpret_cast<uint4*>(vd + v16_off(t, c)) = vs[c];
+            st_nt(kd + k16_off(t, c), ks[c]);
+            st_nt(vd + v16_off(t, c), vs[c]);
         }
         if (part == 0) p.c.keep_pos[(size_t)bg * p.c.cap_keep + i] = pos;
         return;
@@ -169,8 +178,8 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
         for (int c4 = 0; c4 < 4; ++c4) {
             const int c = part * 4 + c4;
             const uint4 zero = make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(kd + k16_off(t, c)) = valid ? ks[c] : zero;
-            *reinterpret_cast<uint4*>(vd + v16_off(t, c)) = valid ? vs[c] : zero;
+            st_nt(kd + k16_off(t, c), valid ? ks[c] : zero);
+            st_nt(vd + v16_off(t, c), valid ? vs[c] : zero);
         }
     }
 }
