@@ -297,14 +297,28 @@ struct Smem {
 __device__ constexpr int st_key(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
 // Cooperative copies into LDS (256 threads).
-__device__ inline void copy_k16(uint8_t* dst, const uint16_t* src, int rows_valid) {  // [64][128] 16-bit
+// A [64][128] 16-bit K tile in two halves, so that a block's loads can all
+// be issued before any store: rows at or beyond rows_valid repeat the last
+// valid row (their scores are masked; the reads stay inside the tensor).
+struct K16Regs {
+    uint4 v[4];
+};
+__device__ inline K16Regs load_k16(const uint16_t* src, int rows_valid) {
+    const int t = threadIdx.x;
+    K16Regs k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = t + 256 * i, r = min(e >> 4, rows_valid - 1), c = (e & 15) * 16;
+        k.v[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(src) + (size_t)r * 2 * kD + c);
+    }
+    return k;
+}
+__device__ inline void store_k16(uint8_t* dst, const K16Regs& k) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = t + 256 * i, r = e >> 4, c = (e & 15) * 16;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < rows_valid) v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(src) + (size_t)r * 2 * kD + c);
-        *reinterpret_cast<uint4*>(dst + r * kK16Stride + c) = v;
+        *reinterpret_cast<uint4*>(dst + r * kK16Stride + c) = k.v[i];
     }
 }
 
@@ -601,9 +615,13 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
         }
         for (int kb = kb_band; kb < nkb; ++kb) {
             __syncthreads();
-            stage_store(sm, 0, stage_load(p.k8 + ((size_t)bg * Tp + (size_t)kb * kBN) * kD,
-                                          p.vt + ((size_t)bg * p.nblk + kb) * kD * kBN));
-            copy_k16(sm.k16, p.k + ((size_t)bg * p.T + (size_t)kb * kBN) * kD, min(kBN, p.T - kb * kBN));
+            {
+                const Stage st = stage_load(p.k8 + ((size_t)bg * Tp + (size_t)kb * kBN) * kD,
+                                            p.vt + ((size_t)bg * p.nblk + kb) * kD * kBN);
+                const K16Regs kr = load_k16(p.k + ((size_t)bg * p.T + (size_t)kb * kBN) * kD, min(kBN, p.T - kb * kBN));
+                stage_store(sm, 0, st);
+                store_k16(sm.k16, kr);
+            }
             __syncthreads();
             const float c8 = sq * p.sk[(size_t)bg * p.nblk + kb] * c16;
             const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
@@ -625,28 +643,53 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
             softmax_x(x, m_ref, l, o, pb);
             pv_block(sm.vt[0], pb, o);
         }
-        for (int tile = 0; tile * kBN < nsel; ++tile) {
-            __syncthreads();
-            copy_k16(sm.k16, p.ksel + ((size_t)bg * p.nsel_tiles + tile) * kBN * kD, kBN);
-            {
-                const int t = threadIdx.x;
+        // Gathered tiles, double-buffered: tile n+1's K and V^T loads are
+        // in flight while tile n is computed (K slots: sm.k16 and the INT8 K
+        // area, free until phase C; V^T slots: sm.vt[0..1]).
+        const int ntile = (nsel + kBN - 1) / kBN;
+        if (ntile > 0) {
+            const int t = threadIdx.x;
+            auto kbuf = [&](int slot) { return slot ? reinterpret_cast<uint8_t*>(&sm.k8[0][0]) : sm.k16; };
+            auto load_sel = [&](int tile, K16Regs& kr, uint4 (&vv)[4]) {
+                kr = load_k16(p.ksel + ((size_t)bg * p.nsel_tiles + tile) * kBN * kD, kBN);
                 const uint16_t* src = p.vtsel + ((size_t)bg * p.nsel_tiles + tile) * kD * kBN;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) st16(sm.vt[0], t + 256 * i, kVtStride, ld16(src, t + 256 * i, 2 * kBN));
+                for (int i = 0; i < 4; ++i) vv[i] = ld16(src, t + 256 * i, 2 * kBN);
+            };
+            auto store_sel = [&](int slot, const K16Regs& kr, const uint4 (&vv)[4]) {
+                store_k16(kbuf(slot), kr);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st16(sm.vt[slot], t + 256 * i, kVtStride, vv[i]);
+            };
+            __syncthreads();  // the band blocks are done with LDS
+            {
+                K16Regs kr;
+                uint4 vv[4];
+                load_sel(0, kr, vv);
+                store_sel(0, kr, vv);
             }
             __syncthreads();
-            floatx16 sb[2];
-            st_16<F16>(sm.k16, q16b, sb);
-            float x[2][16];
+            for (int tile = 0; tile < ntile; ++tile) {
+                const int slot = tile & 1;
+                const bool more = tile + 1 < ntile;
+                K16Regs kr;
+                uint4 vv[4];
+                load_sel(more ? tile + 1 : tile, kr, vv);
+                floatx16 sb[2];
+                st_16<F16>(kbuf(slot), q16b, sb);
+                float x[2][16];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int idx = tile * kBN + 32 * tt + st_key(r, hf);
-                    x[tt][r] = (idx < nsel && qvalid) ? sb[tt][r] * c16 : -INFINITY;
-                }
-            softmax_x(x, m_ref, l, o, pb);
-            pv_block(sm.vt[0], pb, o);
+                    for (int r = 0; r < 16; ++r) {
+                        const int idx = tile * kBN + 32 * tt + st_key(r, hf);
+                        x[tt][r] = (idx < nsel && qvalid) ? sb[tt][r] * c16 : -INFINITY;
+                    }
+                softmax_x(x, m_ref, l, o, pb);
+                pv_block(sm.vt[slot], pb, o);
+                if (more) store_sel(slot ^ 1, kr, vv);
+                __syncthreads();
+            }
         }
     }
 
