@@ -61,8 +61,8 @@ struct DecodeParams {
     float* part_m;         // [B][Hkv][nsplit][G]
     float* part_l;         // [B][Hkv][nsplit][G]
     float* part_o;         // [B][Hkv][nsplit][G][128]
-    int32_t nsplit, tps, G;
-    int32_t nsq, tps16;    // INT4 splits (first nsq partials); 16-bit tiles per split at capacity
+    int32_t nsplit, G;
+    int32_t nsq;           // INT4 splits (the first nsq partials of a (b, g))
     float scale2;          // sm_scale * log2(e)
 };
 
@@ -238,7 +238,7 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
     }
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) dpv[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int u = lane >> 4, c8 = lane & 15;
+    const int u = lane >> 4;
     float* p_w = lds_p[wave];
     float4* y_w = lds_y[wave];
     uint16_t* w_w = lds_w[wave];
@@ -358,13 +358,10 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
         }
 
         auto step = [&](int v, const TileRegs& tr) {
-        float lg[G];
-        int count, tile;
-        float vs[4], vz[4];
+            float lg[G];
+            float vs[4], vz[4];
             // ----------------------------- QK on the matrix cores, INT4 tile
-            tile = v;
-            count = n_q;
-            const bool valid = tile * kTile + lane < n_q;
+            const bool valid = v * kTile + lane < n_q;
             const uint4* kd = tr.kd;
             const uint4 kmv = tr.kmv;
             uint4 vmv = tr.vmv;
@@ -431,85 +428,85 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
                 vs[grp] = f16_to_f32(mv & 0xFFFFu);
                 vz[grp] = f16_to_f32(mv >> 16);
             }
-        // ----------------------------- online softmax (wave-uniform update)
-        float pr_h[G];
+            // ----------------------------- online softmax (wave-uniform update)
+            float pr_h[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if (__any(lg[h] > m[h] + kLazy)) {
-                const float tmax = wave_max_fast(lg[h]);
-                const float alpha = __builtin_amdgcn_exp2f(m[h] - tmax);
-                m[h] = tmax;
-                l[h] *= alpha;
+            for (int h = 0; h < G; ++h) {
+                if (__any(lg[h] > m[h] + kLazy)) {
+                    const float tmax = wave_max_fast(lg[h]);
+                    const float alpha = __builtin_amdgcn_exp2f(m[h] - tmax);
+                    m[h] = tmax;
+                    l[h] *= alpha;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    zacc[h][i] *= alpha;
-                    wsb[h][i] *= alpha;
+                    for (int i = 0; i < 4; ++i) {
+                        zacc[h][i] *= alpha;
+                        wsb[h][i] *= alpha;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
+#pragma unroll
+                    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) dpv[mb][r] = (lane & 15) == h ? dpv[mb][r] * alpha : dpv[mb][r];
                 }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
-#pragma unroll
-                for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) dpv[mb][r] = (lane & 15) == h ? dpv[mb][r] * alpha : dpv[mb][r];
+                pr_h[h] = __builtin_amdgcn_exp2f(lg[h] - m[h]);
+                l[h] += pr_h[h];
             }
-            pr_h[h] = __builtin_amdgcn_exp2f(lg[h] - m[h]);
-            l[h] += pr_h[h];
-        }
 
-        {
-            // running power-of-two scale 2^E with p*s*2^-E < 2^15 (p <= 2^8 by the lazy
-            // rescale, s < 2^(e_s+1)): fp16 weights stay finite and mostly normal
-            const float s4 = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3]));
-            if (__any(s4 >= s_thr && s4 > 0.f)) {
-                const float smax = wave_max_fast(s4);
-                const int e_need = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127 - 6;
-                const float r = E <= -1000 ? 0.f : (e_need > E ? __builtin_ldexpf(1.0f, E - e_need) : 1.0f);
+            {
+                // running power-of-two scale 2^E with p*s*2^-E < 2^15 (p <= 2^8 by the lazy
+                // rescale, s < 2^(e_s+1)): fp16 weights stay finite and mostly normal
+                const float s4 = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3]));
+                if (__any(s4 >= s_thr && s4 > 0.f)) {
+                    const float smax = wave_max_fast(s4);
+                    const int e_need = (int)((__float_as_uint(smax) >> 23) & 0xFF) - 127 - 6;
+                    const float r = E <= -1000 ? 0.f : (e_need > E ? __builtin_ldexpf(1.0f, E - e_need) : 1.0f);
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
+                    for (int h = 0; h < G; ++h) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[h][i] *= r;
+                        for (int i = 0; i < 8; ++i) acc[h][i] *= r;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) wsb[h][i] *= r;
+                        for (int i = 0; i < 4; ++i) wsb[h][i] *= r;
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < 8; ++mb) dpv[mb] *= r;
+                    E = e_need > E ? e_need : E;
+                    s_thr = __builtin_ldexpf(1.0f, E + 7);
                 }
+                const float f = E <= -1000 ? 1.0f : __builtin_ldexpf(1.0f, -E);
+                // fp16 weights of this token into the B-operand layout
+                // w[grp][t/32][(t%32)/8][h][t%8]
+                const int wbase = ((lane >> 5) * 4 + ((lane >> 3) & 3)) * G * 8 + (lane & 7);
 #pragma unroll
-                for (int mb = 0; mb < 8; ++mb) dpv[mb] *= r;
-                E = e_need > E ? e_need : E;
-                s_thr = __builtin_ldexpf(1.0f, E + 7);
-            }
-            const float f = E <= -1000 ? 1.0f : __builtin_ldexpf(1.0f, -E);
-            // fp16 weights of this token into the B-operand layout
-            // w[grp][t/32][(t%32)/8][h][t%8]
-            const int wbase = ((lane >> 5) * 4 + ((lane >> 3) & 3)) * G * 8 + (lane & 7);
+                for (int grp = 0; grp < 4; ++grp) {
+                    const float sf = vs[grp] * f;
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const float sf = vs[grp] * f;
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    zacc[h][grp] = fmaf(pr_h[h], vz[grp], zacc[h][grp]);
-                    const _Float16 w16 = (_Float16)(pr_h[h] * sf);
-                    wsb[h][grp] = fmaf(ebias, (float)w16, wsb[h][grp]);
-                    w_w[grp * 2 * 4 * G * 8 + wbase + h * 8] = __builtin_bit_cast(uint16_t, w16);
-                }
-            }
-            lds_fence();
-            // ----------------------------- PV on the matrix cores
-            const int hs = (lane & 15) < G ? (lane & 15) : 0;
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const halfx8 wb = __builtin_bit_cast(
-                        halfx8, *reinterpret_cast<const uint4*>(w_w + ((grp * 2 + ks) * 4 + (lane >> 4)) * G * 8 + hs * 8));
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const int mb = 2 * grp + half;
-                        const halfx8 va = codes_to_f16(u4w(vd[grp], half * 2 + ks), cc);
-                        dpv[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, wb, dpv[mb], 0, 0, 0);
+                    for (int h = 0; h < G; ++h) {
+                        zacc[h][grp] = fmaf(pr_h[h], vz[grp], zacc[h][grp]);
+                        const _Float16 w16 = (_Float16)(pr_h[h] * sf);
+                        wsb[h][grp] = fmaf(ebias, (float)w16, wsb[h][grp]);
+                        w_w[grp * 2 * 4 * G * 8 + wbase + h * 8] = __builtin_bit_cast(uint16_t, w16);
                     }
                 }
+                lds_fence();
+                // ----------------------------- PV on the matrix cores
+                const int hs = (lane & 15) < G ? (lane & 15) : 0;
+#pragma unroll
+                for (int grp = 0; grp < 4; ++grp) {
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const halfx8 wb = __builtin_bit_cast(
+                            halfx8, *reinterpret_cast<const uint4*>(w_w + ((grp * 2 + ks) * 4 + (lane >> 4)) * G * 8 + hs * 8));
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const int mb = 2 * grp + half;
+                            const halfx8 va = codes_to_f16(u4w(vd[grp], half * 2 + ks), cc);
+                            dpv[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, wb, dpv[mb], 0, 0, 0);
+                        }
+                    }
+                }
+                lds_fence();
             }
-            lds_fence();
-        }
         };
         // Two tiles per wave per iteration: both tiles' loads are issued
         // before either is used. The next pair's loads are issued once both
@@ -820,9 +817,7 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     p.part_l = reinterpret_cast<float*>(ws + w.pl);
     p.part_o = reinterpret_cast<float*>(ws + w.po);
     p.nsplit = d.nsplit;
-    p.tps = d.tiles_per_split;
     p.nsq = decode_nsq(c, d.tiles_per_split);
-    p.tps16 = kTps16;
     p.G = d.G;
     p.scale2 = d.sm_scale_log2;
     const bool f16 = c.dt == HQ_F16;
