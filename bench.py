@@ -80,6 +80,14 @@ class Timer:
         v = [s.elapsed_time(e) for s, e in self.ev.get(name, [])]
         return sum(v) / len(v) if v else float("nan")
 
+    def pct(self, name, scale=1.0):
+        """p10, median, p90 of the call times (ms x scale)."""
+        v = sorted(s.elapsed_time(e) * scale for s, e in self.ev.get(name, []))
+        if not v:
+            return None
+        q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+        return [round(q(0.1), 2), round(q(0.5), 2), round(q(0.9), 2)]
+
     def reset(self):
         self.ev = {}
 
@@ -383,6 +391,7 @@ def main():
         "decode_us": round(dec_ms * 1e3, 2),
         "decode_TBps": round(dbytes / (dec_ms * 1e-3) / 1e12, 3),
         "decode_bytes": dbytes,
+        "decode_us_p10_p50_p90": tm.pct("decode_attn", 1e3),
         "append_us": round(tm.ms("append_kv") * 1e3, 2),
         "wall_s": round(wall, 3),
     }
@@ -393,11 +402,28 @@ def main():
                        "achieved": round(dbytes / (dec_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                        "unit": "GB/s", "frac": round(dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                        "traffic": decode_traffic(dbytes)}
+    # The achievable rate of the decode's access pattern on this GPU: the INT4
+    # store streamed by hq_diag_read_int4 (same splits, tiles and loads, no
+    # compute), timed after the step loop.
+    int4_bytes = int((counts[..., 1] * 160).sum())
+    sink = hq.diag_read_int4(cache)
+    for _ in range(3):
+        hq.diag_read_int4(cache, sink)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        tm("diag_read_int4", hq.diag_read_int4, cache, sink)
+    torch.cuda.synchronize()
+    ach = int4_bytes / (tm.ms("diag_read_int4") * 1e-3) / 1e9
+    res["roofline"]["achievable"] = round(ach, 1)
+    res["roofline"]["frac_of_achievable"] = round(res["roofline"]["achieved"] / ach, 4)
+    res["int4_stream_read"] = {"bytes": int4_bytes, "us": round(tm.ms("diag_read_int4") * 1e3, 2),
+                               "GBps": round(ach, 1)}
     if prefill_ok:
         pms = tm.ms("prefill_attn")
         psp = pf["spec"]
         fl = prefill_flops(psp.T, psp.Hq)
         res["prefill_ms"] = round(pms, 3)
+        res["prefill_ms_p10_p50_p90"] = tm.pct("prefill_attn")
         res["prefill_TFLOPs"] = round(fl / (pms * 1e-3) / 1e12, 1)
         res["prefill_probe_select_ms"] = round(tm.ms("prefill_probe_select"), 3)
         psel = hq.probe_select(pf["qprobe"], pf["k"], pf["lens"], pol)

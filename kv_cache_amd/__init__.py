@@ -21,7 +21,7 @@ HQ_F16, HQ_BF16, HQ_F32 = 0, 1, 2
 EXPORTED = (
     "hq_probe_select", "hq_probe_ws_bytes", "hq_quantize_kv", "hq_append_kv", "hq_decode_attn",
     "hq_decode_ws_bytes", "hq_prefill_attn", "hq_prefill_ws_bytes", "hq_cache_layout", "hq_sel_stride",
-    "hq_last_error",
+    "hq_last_error", "hq_diag_read_int4", "hq_diag_read_int4_sink_bytes",
 )
 
 
@@ -72,6 +72,8 @@ def _load():
         "hq_cache_layout": (I, [I, I, I, I, I, I, pol, ctypes.POINTER(hq_cache_sizes)]),
         "hq_sel_stride": (I, [I, pol]),
         "hq_last_error": (ctypes.c_char_p, []),
+        "hq_diag_read_int4": (I, [ctypes.POINTER(hq_cache), P, S, V]),
+        "hq_diag_read_int4_sink_bytes": (S, [ctypes.POINTER(hq_cache)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -236,6 +238,17 @@ def decode_attn(cache: HybridCache, q, sm_scale: float | None = None, out=None, 
     _check(lib.hq_decode_attn(cache.ptr(), _ptr(q), Hq, sm, _ptr(out), _dt(out), _ptr(ws), ws.numel(),
                               _stream()))
     return out
+
+
+def diag_read_int4(cache: HybridCache, sink=None):
+    """hq_diag_read_int4 (measurement helper): streams the cache's INT4 store
+    in the decode kernel's access pattern; returns the sink tensor."""
+    torch = _torch()
+    n = lib.hq_diag_read_int4_sink_bytes(cache.ptr())
+    if sink is None or sink.numel() < n:
+        sink = torch.empty(max(n, 256), dtype=torch.uint8, device=cache.device)
+    _check(lib.hq_diag_read_int4(cache.ptr(), _ptr(sink), sink.numel(), _stream()))
+    return sink
 
 
 def prefill_attn(q, k, v, sel_idx, sel_count, policy: Policy = Policy(), sm_scale: float | None = None,

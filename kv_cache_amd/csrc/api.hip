@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "hq_internal.h"
+#include "../../include/hq_diag.h"
 
 namespace {
 
@@ -280,6 +281,23 @@ hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B
     hipError_t e = hq::launch_prefill(q, k, v, B, Hq, Hkv, T, dt == HQ_F16, *policy, sel_idx, sel_count,
                                       hq::sel_stride(T, *policy), sm_scale, out, out_dt, ws, (hipStream_t)stream);
     if (e == hipErrorNotSupported) return fail(HQ_ERR_UNSUPPORTED, "%s: not available in this build", fn);
+    return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
+}
+
+size_t hq_diag_read_int4_sink_bytes(const hq_cache* cache) {
+    if (!cache || cache->B < 1 || cache->Hkv < 1 || cache->cap_q < hq::kTile) return 0;
+    return hq::diag_sink_bytes(*cache, decode_tps());
+}
+
+hq_status hq_diag_read_int4(const hq_cache* cache, void* sink, size_t sink_bytes, void* stream) {
+    static const char* fn = "hq_diag_read_int4";
+    clear_err();
+    hq_status st;
+    if ((st = check_cache(fn, cache))) return st;
+    REQ_PTR(sink);
+    const size_t need = hq::diag_sink_bytes(*cache, decode_tps());
+    if (sink_bytes < need) return fail(HQ_ERR_CAPACITY, "%s: sink %zu bytes < required %zu", fn, sink_bytes, need);
+    hipError_t e = hq::launch_diag_read_int4(*cache, sink, decode_tps(), (hipStream_t)stream);
     return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
 }
 

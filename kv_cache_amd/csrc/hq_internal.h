@@ -139,6 +139,12 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
                          const DecodeLaunch& d, hipStream_t s);
 size_t decode_ws_bytes(const hq_cache& c, int32_t Hq, int32_t nsplit);
 int32_t decode_nsplit(const hq_cache& c, int32_t tps);
+int32_t decode_nsq(const hq_cache& c, int32_t tps);  // INT4 splits of a (b, g)
+
+// Streaming read of the INT4 store in the decode kernel's access pattern
+// (measurement helper, not a step of the method).
+size_t diag_sink_bytes(const hq_cache& c, int32_t tps);
+hipError_t launch_diag_read_int4(const hq_cache& c, void* sink, int32_t tps, hipStream_t s);
 
 hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_lens, int32_t B,
                         int32_t Hq, int32_t Hkv, int32_t Tmax, bool f16, const hq_policy& pol,

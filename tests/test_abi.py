@@ -20,10 +20,13 @@ def hq():
 
 
 def _declared():
-    with open(os.path.join(ROOT, "include", "hq.h")) as f:
-        src = f.read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(hq_[a-z_0-9]+)\s*\(", src)))
+    names = set()
+    for h in ("hq.h", "hq_diag.h"):
+        with open(os.path.join(ROOT, "include", h)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(hq_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(hq):

@@ -1,0 +1,36 @@
+"""The streaming-read helper hq_diag_read_int4 (measurement aid, not a step
+of the method) reads exactly the INT4 store it claims to: the XOR of every
+word it writes to its sink equals the XOR of every 32-bit word of the
+n_q/64 leading tiles of K codes, V codes, K scale/zero and V scale/zero of
+each (b, g), computed on the host from the same cache buffers."""
+import numpy as np
+import pytest
+
+from synth import small_decode_inputs
+
+from test_gpu_cache_decode import _run_quantize
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("kw", [dict(B=2, Hq=8, Hkv=2, T=700, ragged_min=389, seed=31),
+                                dict(B=1, Hq=4, Hkv=1, T=3000, seed=32)])
+def test_diag_read_int4_reads_the_int4_store(kw):
+    import torch
+    import kv_cache_amd as hq
+    inp = small_decode_inputs(**kw)
+    cache, _, _ = _run_quantize(inp, 128, (5, 100))
+    sink = hq.diag_read_int4(cache)
+    torch.cuda.synchronize()
+    n = hq.lib.hq_diag_read_int4_sink_bytes(cache.ptr())
+    got = np.bitwise_xor.reduce(sink[:n].cpu().numpy().view(np.uint32))
+    counts = cache.counts().cpu().numpy().reshape(-1, 4)
+    qt = cache.c.cap_q // 64
+    want = np.uint32(0)
+    for name, per_tile in (("k_codes", 4096), ("v_codes", 4096), ("k_meta", 1024), ("v_meta", 1024)):
+        buf = cache.bufs[name].cpu().numpy()[: counts.shape[0] * qt * per_tile].reshape(counts.shape[0], qt * per_tile)
+        for bg in range(counts.shape[0]):
+            nqt = (int(counts[bg, 1]) + 63) // 64
+            want ^= np.bitwise_xor.reduce(buf[bg, : nqt * per_tile].view(np.uint32))
+    assert got == want
+    assert cache.err_flag() == 0
