@@ -48,6 +48,8 @@ def _args():
                     help="time only append+decode per step (profiling aid)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill probe + attention per step and print its fields (profiling aid)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="decode on the 8B GQA shape (B=16, 32/8 heads) at T = 1K..32K; prints one JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain device copy of this size (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -247,6 +249,55 @@ def cpu_baseline_prefill(pin, sel_idx, sel_cnt, budget_s=8.0):
                       f"({t_rows:.1f} s) plus one head's INT8 stage, scaled to {sp.T} rows x {sp.Hq} heads"}
 
 
+def decode_sweep(args):
+    """Decode (append + decode per step, on one built cache) on the 8B GQA
+    shape at the context lengths of the pages' speed table: absolute time and
+    bandwidth per length, and the streaming-read rate of the same INT4 store."""
+    import dataclasses
+    import torch
+    import kv_cache_amd as hq
+    from synth.inputs import CONFIGS, make_append_tokens, make_decode_inputs
+    dev = "cuda:0"
+    pol = hq.Policy()
+    rows = []
+    for T in (1024, 2048, 4096, 8192, 16384, 32768):
+        spec = dataclasses.replace(CONFIGS["c2_decode_8b_32k"], name=f"decode_8b_gqa_b16_{T}", T=T)
+        inp = make_decode_inputs(spec)
+        kn, vn, qn = make_append_tokens(spec, inp.outlier_channels, 1)
+        k, v = _dev16(inp.k, "bf16", dev), _dev16(inp.v, "bf16", dev)
+        qp, q = _dev16(inp.q_probe, "bf16", dev), _dev16(qn[0], "bf16", dev)
+        knew, vnew = _dev16(kn[0], "bf16", dev), _dev16(vn[0], "bf16", dev)
+        lens = torch.from_numpy(inp.seq_lens).to(dev)
+        cache = hq.HybridCache(spec.B, spec.Hkv, T + 64, T, torch.bfloat16, dev, pol)
+        col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol)
+        hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
+        out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.float32, device=dev)
+        tm = Timer()
+        for i in range(args.warmup + args.steps):
+            if i == args.warmup:
+                torch.cuda.synchronize()
+                tm.reset()
+            tm("append_kv", hq.append_kv, cache, knew, vnew)
+            tm("decode_attn", hq.decode_attn, cache, q, None, out)
+        sink = hq.diag_read_int4(cache)
+        for _ in range(10):
+            tm("diag", hq.diag_read_int4, cache, sink)
+        torch.cuda.synchronize()
+        counts = cache.counts().cpu().numpy()
+        by = decode_bytes_per_step(counts)
+        dms = tm.ms("decode_attn")
+        i4 = int((counts[..., 1] * 160).sum())
+        rows.append({"T": T, "decode_us": round(dms * 1e3, 2), "decode_us_p10_p50_p90": tm.pct("decode_attn", 1e3),
+                     "bytes": by, "TBps": round(by / (dms * 1e-3) / 1e12, 3),
+                     "frac_of_peak": round(by / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "int4_stream_TBps": round(i4 / (tm.ms("diag") * 1e-3) / 1e12, 3)})
+        print(f"# sweep T={T}: {rows[-1]}", file=sys.stderr, flush=True)
+        del cache, k, v, inp
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "decode_8b_gqa_b16 (B=16, 32/8 heads, bf16, top-5% + 128 window, INT4 g32)",
+                      "steps": args.steps, "warmup": args.warmup, "rows": rows}), flush=True)
+
+
 def prefill_only(args):
     """Probe + hybrid prefill attention on the 16K workload only."""
     import torch
@@ -301,6 +352,8 @@ def main():
 
     if args.prefill_only:
         return prefill_only(args)
+    if args.sweep:
+        return decode_sweep(args)
     t_gen = time.perf_counter()
     spec = CONFIGS["c2_decode_8b_32k"]
     inp = make_decode_inputs(spec)
