@@ -38,7 +38,8 @@
 //    built in LDS by each INT4 workgroup while its first two tiles are in
 //    flight; a separate launch for them costs more than the work itself.
 //  * 16-bit tiles (kept columns, window ring) use v_dot2 / fp32 FMAs on the
-//    16-bit rows (they are a few percent of the tiles).
+//    16-bit rows (they are a few percent of the tiles), with every K and V
+//    load of a tile issued before its first use.
 //  * Each workgroup writes one partial (m, l, o[128]) per head; a second
 //    kernel merges the splits of each (b, g).
 #include "hq_internal.h"

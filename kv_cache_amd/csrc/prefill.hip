@@ -17,15 +17,17 @@
 //
 // Pre-pass (k_pf_quant_q, k_pf_quant_kv, k_pf_gather_sel): Q8/sQ, K8/sK, V
 // converted to fp16 and transposed per 64-key block (the PV operand
-// layout), a 64-bit selected-column mask per key block, and gathered tiles of
-// the selected columns (16-bit K rows and transposed fp16 V).
+// layout), a second copy of it with the selected columns zeroed and per-block
+// row-sum weights (0 for a selected key) for the INT8 blocks, a 64-bit
+// selected-column mask per key block, and gathered tiles of the selected
+// columns (16-bit K rows and transposed fp16 V).
 //
 // Attention (k_pf_attn): one workgroup = 4 waves = 128 query rows of one head;
 // each wave owns 32 queries. S^T = K Q^T is computed with 32x32 MFMA tiles so
 // a lane holds one query column (16 keys per tile); row maxima need one
 // cross-half exchange. Key blocks of 64:
 //   * blocks entirely below the window band: int8 MFMA, selected columns
-//     dropped (p = 0);
+//     dropped through the zeroed V^T copy and zero row-sum weights;
 //   * the 4 blocks that touch the band/diagonal: int8 and bf16 MFMA, the
 //     score picked per element (band or selected -> bf16), causal mask;
 //   * gathered selected columns below the band: bf16 MFMA, no mask needed.
