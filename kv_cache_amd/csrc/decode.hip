@@ -264,7 +264,7 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
             0x00020000);
         const int voff = lane * 16;
         auto ld = [&](const __amdgpu_buffer_rsrc_t& r, int soff) {
-            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kLoadNT));
         };
         auto load_tile = [&](int v, TileRegs& r) {
 #pragma unroll

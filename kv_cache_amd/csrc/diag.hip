@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256, 2) void k_diag_read_int4(const hq_cache c, uin
         0x00020000);
     const int voff = lane * 16;
     auto ld = [&](const __amdgpu_buffer_rsrc_t& r, int soff) {
-        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kLoadNT));
     };
     uint4 acc = make_uint4(0, 0, 0, 0);
     auto fold = [&](const uint4& x) {

@@ -13,6 +13,26 @@ constexpr int kTile = 64;        // tokens per cache tile == wavefront size
 constexpr int kGroup = 32;       // INT4 quantization group (channels)
 constexpr int kTileBytesQ = 4096;        // packed INT4 codes of one tile (K or V)
 constexpr int kTileBytes16 = kTile * kD * 2;  // one tile of 16-bit rows
+// Cache-policy operand of the buffer loads that stream the INT4 store: the
+// non-temporal hint (each byte is read once per call, so it is not kept in
+// the caches at the expense of other data; measured faster than the default).
+constexpr int kLoadNT = 2;
+
+// Streaming (non-temporal) stores, for results that this call does not read
+// back: they are not kept dirty in the caches, where their later write-back
+// would take bandwidth from the kernels that run next.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline void st_nt(void* ptr, uint32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(ptr)); }
+__device__ inline void st_nt(void* ptr, int32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<int32_t*>(ptr)); }
+__device__ inline void st_nt(void* ptr, uint32_t a, uint32_t b) {
+    const u32x2_t x = {a, b};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x2_t*>(ptr));
+}
+__device__ inline void st_nt(void* ptr, const uint4& v) {
+    const u32x4_t x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(ptr));
+}
 constexpr int kInt8Block = 64;   // prefill INT8 block (tokens)
 
 // ---------------------------------------------------------------------------

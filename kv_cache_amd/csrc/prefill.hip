@@ -34,6 +34,13 @@
 // P goes to fp16 straight from the S^T registers (same key order as the V^T
 // operand) for the fp16 PV MFMA; O^T accumulates in fp32. Online softmax in
 // log2 units.
+// The output and the fp16 V^T tensors, written in whole 128-byte lines, use
+// streaming (non-temporal) stores: the output is not read again here and the
+// V^T copies are larger than the caches, so keeping them there buys little,
+// while dirty lines left behind would be written back during the kernels
+// that run after this call (a decode step, in mixed serving). The output is
+// staged through LDS so that each store instruction writes whole rows:
+// partial lines written this way are not merged before they reach memory.
 #include "hq_internal.h"
 
 namespace hq {
@@ -223,8 +230,8 @@ __global__ __launch_bounds__(256) void k_pf_quant_kv(PfParams p) {
             w0[j] = w[j] & (((bits >> ka) & 1ull) ? 0xFFFF0000u : 0xFFFFFFFFu) &
                     (((bits >> kb) & 1ull) ? 0x0000FFFFu : 0xFFFFFFFFu);
         }
-        *reinterpret_cast<uint4*>(vdst + (size_t)ch * kBN + k0) = make_uint4(w[0], w[1], w[2], w[3]);
-        *reinterpret_cast<uint4*>(v0dst + (size_t)ch * kBN + k0) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+        st_nt(vdst + (size_t)ch * kBN + k0, make_uint4(w[0], w[1], w[2], w[3]));
+        st_nt(v0dst + (size_t)ch * kBN + k0, make_uint4(w0[0], w0[1], w0[2], w0[3]));
     }
     // row-sum weights: word 4j + e of lane half hf pairs the keys of P^T
     // operand j, elements 2e and 2e + 1 (S^T tile j/2, registers
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(256) void k_pf_gather_sel(PfParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             w[j] = (uint32_t)vs[vt_key(k0 + 2 * j)][ch] | ((uint32_t)vs[vt_key(k0 + 2 * j + 1)][ch] << 16);
-        *reinterpret_cast<uint4*>(vdst + (size_t)ch * kBN + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+        st_nt(vdst + (size_t)ch * kBN + k0, make_uint4(w[0], w[1], w[2], w[3]));
     }
 }
 
@@ -287,12 +294,18 @@ constexpr int kK16Stride = 2 * kD + 16;   // 16-bit K rows (256 B + pad)
 constexpr int kVtStride = 2 * kBN + 16;   // fp16 V^T rows (one channel, 64 keys)
 constexpr float kLazy = 8.0f;             // log2-domain growth that triggers a rescale
 
+// Output staging at the end of the kernel (the tiles are dead by then): per
+// wave 32 rows of 128 values, rows padded by 16 bytes.
+constexpr int kOutRowF32 = 4 * kD + 16;
+constexpr int kOutRow16 = 2 * kD + 16;
+
 struct Smem {
     int8_t k8[2][kBN * kK8Stride];
     uint8_t vt[2][kD * kVtStride];
     uint8_t k16[kBN * kK16Stride];
     uint4 wt[2][8];  // row-sum weights of the INT8 blocks (two slots, like vt)
 };
+static_assert(4 * 32 * kOutRowF32 <= sizeof(Smem), "output staging must fit in the tile LDS");
 
 // S^T register r of lane half hf in a 32-key MFMA tile holds key
 // 8*(r/4) + 4*hf + r%4 (the 32x32 MFMA output layout, M = keys).
@@ -816,14 +829,17 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
         }
     }
 
-    // combine the two lane halves of each query and write
+    // combine the two lane halves of each query and write. Each wave stages
+    // its 32 x 128 output tile in LDS (rows padded by 16 bytes), then writes
+    // it out with streaming stores, 1 KiB of whole rows per instruction.
     {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
         l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
-    if (!qvalid) return;
-    const float inv = 1.0f / l;
-    const size_t orow = (((size_t)b * p.Hq + h) * p.T + qi) * kD;
+    const float inv = 1.0f / l;  // rows beyond T: unused
+    const bool f32 = p.out_dt == HQ_F32;
+    uint8_t* stg = reinterpret_cast<uint8_t*>(&sm) + wave * (32 * kOutRowF32);
+    __syncthreads();  // every wave is done with the LDS tiles
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
@@ -831,20 +847,40 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
             const int ch = 32 * ct + 8 * r4 + 4 * hf;
             const float vv[4] = {o[ct][4 * r4] * inv, o[ct][4 * r4 + 1] * inv, o[ct][4 * r4 + 2] * inv,
                                  o[ct][4 * r4 + 3] * inv};
-            if (p.out_dt == HQ_F32) {
-                *reinterpret_cast<float4*>(p.out + orow + ch) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+            if (f32) {
+                *reinterpret_cast<float4*>(stg + m_ * kOutRowF32 + 4 * ch) = make_float4(vv[0], vv[1], vv[2], vv[3]);
             } else {
-                uint16_t* o16 = reinterpret_cast<uint16_t*>(p.out) + orow + ch;
+                uint32_t hb[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (p.out_dt == HQ_F16) o16[e] = (uint16_t)f32_to_f16_bits(vv[e]);
+                    if (p.out_dt == HQ_F16) hb[e] = f32_to_f16_bits(vv[e]);
                     else {
                         uint32_t xb = __float_as_uint(vv[e]);
                         xb += 0x7FFFu + ((xb >> 16) & 1u);
-                        o16[e] = (uint16_t)(xb >> 16);
+                        hb[e] = xb >> 16;
                     }
                 }
+                *reinterpret_cast<uint2*>(stg + m_ * kOutRow16 + 2 * ch) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
             }
+        }
+    }
+    __syncthreads();
+    // 1 KiB per instruction: 2 rows (fp32) or 4 rows (16-bit) of the wave's tile
+    if (f32) {
+        float* ob = p.out + (((size_t)b * p.Hq + h) * p.T + qrow0) * kD;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 2 * i + (lane >> 5), ck = lane & 31;
+            if (qrow0 + row < p.T)
+                st_nt(ob + (size_t)row * kD + 4 * ck, *reinterpret_cast<const uint4*>(stg + row * kOutRowF32 + 16 * ck));
+        }
+    } else {
+        uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + (((size_t)b * p.Hq + h) * p.T + qrow0) * kD;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 4 * i + (lane >> 4), ck = lane & 15;
+            if (qrow0 + row < p.T)
+                st_nt(ob + (size_t)row * kD + 8 * ck, *reinterpret_cast<const uint4*>(stg + row * kOutRow16 + 16 * ck));
         }
     }
 }

@@ -18,16 +18,8 @@
 namespace hq {
 namespace {
 
-// The cache is written once here and read by later calls: streaming
-// (non-temporal) stores keep it from sitting dirty in the caches, where its
-// write-backs would compete with the next kernel's reads.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ inline void st_nt(void* ptr, uint32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(ptr)); }
-__device__ inline void st_nt(void* ptr, int32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<int32_t*>(ptr)); }
-__device__ inline void st_nt(void* ptr, const uint4& v) {
-    const u32x4_t x = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(ptr));
-}
+// The cache is written once here and read by later calls: every write is a
+// streaming store (st_nt).
 
 struct QuantParams {
     const uint16_t* k;
