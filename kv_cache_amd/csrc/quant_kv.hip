@@ -110,68 +110,111 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
 #pragma unroll
             for (int w = 0; w < 4; ++w)
                 st_nt(kc + kq_word(t, kGroup * grp + 8 * w), to_mf_order(kp[w]));
-            st_nt(reinterpret_cast<uint8_t*>(p.c.k_meta) + meta_base + kmeta_word(t, grp), (uint32_t)(ks | (kz << 16)));
+            // (K metadata and positions: a quarter line per instruction, default policy)
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.c.k_meta) + meta_base + kmeta_word(t, grp)) =
+                ks | (kz << 16);
             st_nt(reinterpret_cast<uint8_t*>(p.c.v_meta) + meta_base + vmeta_word(t, grp), (uint32_t)(vs | (vz << 16)));
-            if (grp == 0) st_nt(p.c.q_pos + (size_t)bg * p.c.cap_q + n, (int32_t)pos);
+            if (grp == 0) p.c.q_pos[(size_t)bg * p.c.cap_q + n] = pos;
         }
         __syncthreads();
-        // 1024 V words per tile: word (channel ch, slot octet o) holds slots 8o..8o+7
+        // 1024 V words per tile: word (channel ch, slot octet o) holds slots
+        // 8o..8o+7. Thread tid assembles the four words of one 16-byte record
+        // (channels ch, ch + 16 x octets o, o + 4), so each wave stores 1 KiB
+        // of whole lines.
+        {
+            const int cb = tid >> 6, oq = (tid >> 4) & 3, c16 = tid & 15;
+            uint32_t wd[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int wi = tid + 256 * i, ch = wi >> 3, o = wi & 7;
-            uint32_t w = 0;
+            for (int j = 0; j < 4; ++j) {
+                const int ch = 32 * cb + 16 * (j >> 1) + c16, o = oq + 4 * (j & 1);
+                uint32_t w = 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t code = (vstage[8 * o + e][ch >> 5][(ch >> 3) & 3] >> (4 * (ch & 7))) & 0xFu;
-                w |= code << mf_nib(e);
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t code = (vstage[8 * o + e][ch >> 5][(ch >> 3) & 3] >> (4 * (ch & 7))) & 0xFu;
+                    w |= code << mf_nib(e);
+                }
+                wd[j] = w;
             }
-            st_nt(vc + vq_word(8 * o, ch), w);
+            st_nt(vc + vq_word(8 * oq, 32 * cb + c16), make_uint4(wd[0], wd[1], wd[2], wd[3]));
         }
         return;
     }
     tile -= qt;
-    const int t = tid >> 2, part = tid & 3;
+    // 16-bit tiles: item e = tid + 256 r (r < 4) is the 16 bytes at byte 16e
+    // of the K tile and of the V tile, so each wave stores 1 KiB of whole
+    // lines. K byte 16e holds slot e % 64, chunk e / 64 (k16_off); V byte 16e
+    // holds slot e / 64 + 16 ((e / 16) % 4), chunk e % 16 (v16_off).
+    auto k_slot = [](int e) { return e & 63; };
+    auto k_chunk = [](int e) { return e >> 6; };
+    auto v_slot = [](int e) { return (e >> 6) + 16 * ((e >> 4) & 3); };
+    auto v_chunk = [](int e) { return e & 15; };
     if (tile < kt) {
         // ---------------- kept tile
-        const int i = tile * kTile + t;
         if (tile * kTile >= k) return;
-        if (i >= k) return;
-        const int pos = S[i];
-        if (pos < 0 || pos >= T - nwin || (i > 0 && S[i - 1] >= pos)) {
-            atomicOr(p.c.err_flag, 4);  // selected positions must be ascending candidates
-            return;
+        // position of slot s, or -1 past the count or for an invalid entry
+        auto kept_pos = [&](int s) {
+            const int i = tile * kTile + s;
+            if (i >= k) return -1;
+            const int pos = S[i];
+            return (pos < 0 || pos >= T - nwin || (i > 0 && S[i - 1] >= pos)) ? -1 : pos;
+        };
+        if (tid < kTile) {
+            const int i = tile * kTile + tid;
+            if (i < k) {
+                const int pos = kept_pos(tid);
+                if (pos < 0) atomicOr(p.c.err_flag, 4);  // selected positions must be ascending candidates
+                else p.c.keep_pos[(size_t)bg * p.c.cap_keep + i] = pos;
+            }
         }
         const size_t tb = ((size_t)bg * kt + tile) * kTileBytes16;
         uint8_t* kd = reinterpret_cast<uint8_t*>(p.c.k_keep) + tb;
         uint8_t* vd = reinterpret_cast<uint8_t*>(p.c.v_keep) + tb;
-        const uint4* ks = reinterpret_cast<const uint4*>(krows + (size_t)pos * kD);
-        const uint4* vs = reinterpret_cast<const uint4*>(vrows + (size_t)pos * kD);
+        int kp[4], vp[4];
+        uint4 kv[4], vv[4];
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            const int c = part * 4 + c4;
-            st_nt(kd + k16_off(t, c), ks[c]);
-            st_nt(vd + v16_off(t, c), vs[c]);
+        for (int r = 0; r < 4; ++r) {
+            const int e = tid + 256 * r;
+            kp[r] = kept_pos(k_slot(e));
+            vp[r] = kept_pos(v_slot(e));
+            kv[r] = reinterpret_cast<const uint4*>(krows + (size_t)max(kp[r], 0) * kD)[k_chunk(e)];
+            vv[r] = reinterpret_cast<const uint4*>(vrows + (size_t)max(vp[r], 0) * kD)[v_chunk(e)];
         }
-        if (part == 0) p.c.keep_pos[(size_t)bg * p.c.cap_keep + i] = pos;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = tid + 256 * r;
+            if (kp[r] >= 0) st_nt(kd + 16 * e, kv[r]);
+            if (vp[r] >= 0) st_nt(vd + 16 * e, vv[r]);
+        }
         return;
     }
     tile -= kt;
     {
         // ---------------- ring tile (slot = position % W)
-        const int s = tile * kTile + t;
-        const bool valid = T >= W || s < T;
-        const int pos = T >= W ? T - 1 - ((T - 1 - s) % W) : s;
         const size_t tb = ((size_t)bg * (W / kTile) + tile) * kTileBytes16;
         uint8_t* kd = reinterpret_cast<uint8_t*>(p.c.k_win) + tb;
         uint8_t* vd = reinterpret_cast<uint8_t*>(p.c.v_win) + tb;
-        const uint4* ks = reinterpret_cast<const uint4*>(krows + (size_t)(valid ? pos : 0) * kD);
-        const uint4* vs = reinterpret_cast<const uint4*>(vrows + (size_t)(valid ? pos : 0) * kD);
+        // position of ring slot s, or -1 for a slot no token has reached
+        auto ring_pos = [&](int s) {
+            const int slot = tile * kTile + s;
+            if (T >= W) return T - 1 - ((T - 1 - slot) % W);
+            return slot < T ? slot : -1;
+        };
+        int kp[4], vp[4];
+        uint4 kv[4], vv[4];
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            const int c = part * 4 + c4;
-            const uint4 zero = make_uint4(0, 0, 0, 0);
-            st_nt(kd + k16_off(t, c), valid ? ks[c] : zero);
-            st_nt(vd + v16_off(t, c), valid ? vs[c] : zero);
+        for (int r = 0; r < 4; ++r) {
+            const int e = tid + 256 * r;
+            kp[r] = ring_pos(k_slot(e));
+            vp[r] = ring_pos(v_slot(e));
+            kv[r] = reinterpret_cast<const uint4*>(krows + (size_t)max(kp[r], 0) * kD)[k_chunk(e)];
+            vv[r] = reinterpret_cast<const uint4*>(vrows + (size_t)max(vp[r], 0) * kD)[v_chunk(e)];
+        }
+        const uint4 zero = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = tid + 256 * r;
+            st_nt(kd + 16 * e, kp[r] >= 0 ? kv[r] : zero);
+            st_nt(vd + 16 * e, vp[r] >= 0 ? vv[r] : zero);
         }
     }
 }
