@@ -535,6 +535,25 @@ __device__ inline void softmax_x(float (&x)[2][16], float& m_ref, float& l, floa
     pack_p(x, pb, l);
 }
 
+// As softmax_x for unscaled scores: x = raw * scale in log2 units (scale > 0,
+// so the block maximum is taken on the raw values), one FMA per element.
+__device__ inline void softmax_scaled(float (&x)[2][16], float scale, float& m_ref, float& l, floatx16 (&o)[4],
+                                      halfx8 (&pb)[4]) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bm = fmaxf(bm, x[tt][r]);
+    bm = swap_max(bm) * scale;
+    lazy_rescale(bm, m_ref, l, o);
+    const float nmr = m_ref == -INFINITY ? 0.0f : -m_ref;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[tt][r] = __builtin_amdgcn_exp2f(fmaf(x[tt][r], scale, nmr));
+    pack_p(x, pb, l);
+}
+
 // Wave64 lane mask of the lanes whose S^T element r = 4a + b (tile tt)
 // holds a selected key: lane half 0 holds key 32tt + 8a + b, half 1 key
 // 32tt + 8a + 4 + b; `byte` = the 8 selection bits of keys 32tt + 8a ... +7.
@@ -640,19 +659,29 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
             __syncthreads();
             const float c8 = sq * p.sk[(size_t)bg * p.nblk + kb] * c16;
             const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
+            // Key kl = 32tt + 8a + b4 + 4hf of element r = 4a + b4 (tile tt) is
+            // in the window band when kl > qi - 64kb - W and masked when
+            // kl > qi - 64kb (which also covers keys at or beyond T: qi < T).
+            // The compares are against per-lane bounds, with the lane half's
+            // 4hf folded in; the selection test is a scalar lane mask. Rows
+            // at or beyond T are computed with a zero query and not stored.
+            const int lc = qi - kb * kBN - 4 * hf, lw = lc - W;
             float x[2][16];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const intx16 si = st_int8_tile(sm.k8[0], q8b, tt);
                 const floatx16 sb = st_16_tile<F16>(sm.k16, q16b, tt);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kl = 32 * tt + st_key(r, hf);
-                    const int j = kb * kBN + kl;
-                    const bool hi = ((selbits >> kl) & 1ull) || (qi - j < W);
-                    float val = hi ? sb[r] * c16 : (float)si[r] * c8;
-                    if (j > qi || j >= p.T || !qvalid) val = -INFINITY;
-                    x[tt][r] = val;
+                for (int a = 0; a < 4; ++a) {
+                    const uint32_t byte = (uint32_t)(selbits >> (32 * tt + 8 * a)) & 0xFFu;
+#pragma unroll
+                    for (int b4 = 0; b4 < 4; ++b4) {
+                        const int r = 4 * a + b4, k0 = 32 * tt + 8 * a + b4;
+                        const bool sel = __builtin_amdgcn_inverse_ballot_w64(elem_lanes(byte, b4));
+                        float val = (sel || k0 > lw) ? sb[r] * c16 : (float)si[r] * c8;
+                        if (k0 > lc) val = -INFINITY;
+                        x[tt][r] = val;
+                    }
                 }
             }
             softmax_x(x, m_ref, l, o, pb);
@@ -696,11 +725,15 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int idx = tile * kBN + 32 * tt + st_key(r, hf);
-                        x[tt][r] = (idx < nsel && qvalid) ? sb[tt][r] * c16 : -INFINITY;
-                    }
-                softmax_x(x, m_ref, l, o, pb);
+                    for (int r = 0; r < 16; ++r) x[tt][r] = sb[tt][r];
+                if ((tile + 1) * kBN > nsel) {  // the last, partial tile: mask its unused columns
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (tile * kBN + 32 * tt + st_key(r, hf) >= nsel) x[tt][r] = -INFINITY;
+                }
+                softmax_scaled(x, c16, m_ref, l, o, pb);
                 pv_block(sm.vt[slot], pb, o);
                 if (more) store_sel(slot ^ 1, kr, vv);
                 __syncthreads();
