@@ -10,9 +10,9 @@
 //
 // Column score c[j] = sum over the G query heads and the last R probe rows of
 // the row-normalised causal softmax. The map is never stored: pass 1
-// computes each row's max and normaliser over key chunks, a combine kernel
-// merges the chunks, pass 2 recomputes the logits and sums the normalised
-// probabilities per column.
+// computes each row's normaliser over key chunks (relative to a reference
+// logit per chunk), a combine kernel merges the chunks, pass 2 recomputes the
+// logits and sums the normalised probabilities per column.
 //
 // Precision: the selection is a ranking of scores whose top-k gap is often
 // only ~1e-5..1e-4 relative on long contexts, so the logits are formed
@@ -57,19 +57,33 @@ __device__ inline double exp2_f64(double x) {
     return ldexp(e, (int)n);
 }
 
-template <bool F16>
-__device__ inline void load32_f64(const uint16_t* src, bool ok, double* out) {
+// 32 consecutive 16-bit values (one lane's share of a row), loaded raw so
+// that the next tile's loads can be in flight while this tile is computed.
+struct Raw32 {
+    uint4 u[4];
+};
+__device__ inline Raw32 load_raw32(const uint16_t* src, bool ok) {
     const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    Raw32 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.u[i] = ok ? s4[i] : make_uint4(0, 0, 0, 0);
+    return r;
+}
+template <bool F16>
+__device__ inline void cvt32_f64(const Raw32& r, double* out) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint4 u = ok ? s4[i] : make_uint4(0, 0, 0, 0);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        const uint32_t w[4] = {r.u[i].x, r.u[i].y, r.u[i].z, r.u[i].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             out[8 * i + 2 * j] = (double)h16_to_f32<F16>(w[j] & 0xFFFFu);
             out[8 * i + 2 * j + 1] = (double)h16_to_f32<F16>(w[j] >> 16);
         }
     }
+}
+template <bool F16>
+__device__ inline void load32_f64(const uint16_t* src, bool ok, double* out) {
+    cvt32_f64<F16>(load_raw32(src, ok), out);
 }
 
 // Exact 16 x 16 block of dot products over 128 channels. Lane l supplies row
@@ -83,6 +97,21 @@ __device__ inline double4_t mfma_dot128(const double* a, const double* b) {
     return acc;
 }
 
+// As mfma_dot128 with the B operand given as raw 16-bit values, each
+// converted to fp64 just before the MFMA that reads it.
+template <bool F16>
+__device__ inline double raw_elem(const Raw32& r, int s) {
+    const uint4& u = r.u[s >> 3];
+    const uint32_t w = ((s >> 1) & 3) == 0 ? u.x : ((s >> 1) & 3) == 1 ? u.y : ((s >> 1) & 3) == 2 ? u.z : u.w;
+    return (double)h16_to_f32<F16>((s & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+template <bool F16>
+__device__ inline double4_t mfma_dot128_rb(const double* a, const Raw32& br) {
+    double4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], raw_elem<F16>(br, s), acc, 0, 0, 0);
+    return acc;
+}
 struct ProbeParams {
     const uint16_t* q;     // [B][Hq][R][D]
     const uint16_t* k;     // [B][Hkv][Tmax][D]
@@ -100,9 +129,12 @@ __device__ inline const uint16_t* qrow(const ProbeParams& p, int b, int g, int r
 }
 __device__ inline int row_pos(const ProbeParams& p, int T, int row) { return T - p.R + (row % p.R); }
 
-// Pass 1: per (key chunk, g, b), online max / sum of 2^x per probe row.
+// Pass 1: per (key chunk, g, b), online reference / sum of 2^x per probe
+// row. Each wave keeps its row tile's queries in fp64 and streams the key
+// tiles, the next tile's raw 16-bit values loaded while this tile's 32 MFMAs
+// run; at most 168 VGPRs, so three waves share a SIMD.
 template <bool F16>
-__global__ __launch_bounds__(256) void k_probe_rowstats(ProbeParams p) {
+__global__ __launch_bounds__(256, 3) void k_probe_rowstats(ProbeParams p) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int T = p.seq_lens[b];
@@ -125,22 +157,32 @@ __global__ __launch_bounds__(256) void k_probe_rowstats(ProbeParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) pos[i] = row_pos(p, T, rt * 16 + 4 * i + kq);
             const int key_hi = min(key_lo + kKeyChunk, T);
+            // m is a reference, not the running maximum: l = sum of 2^(x - m)
+            // with m moved only when a logit exceeds it by more than 2^9
+            // (and on the first one), so the common path takes one exp per
+            // element and no divergent branch. Terms up to 2^512 are exact
+            // in fp64 range; the chunk merge and the normalisation accept
+            // any reference.
+            Raw32 kn = load_raw32(kbase + (size_t)(key_lo + li < T ? key_lo + li : 0) * kD + 32 * kq, key_lo + li < T);
             for (int k0 = key_lo; k0 < key_hi; k0 += 16) {
                 const int key = k0 + li;
                 const bool kok = key < T;
-                double bv[32];
-                load32_f64<F16>(kbase + (size_t)(kok ? key : 0) * kD + 32 * kq, kok, bv);
-                const double4_t acc = mfma_dot128(a, bv);
+                const Raw32 kc = kn;
+                {
+                    const int nk = key + 16;
+                    const bool nok = nk < key_hi;
+                    kn = load_raw32(kbase + (size_t)(nok ? nk : 0) * kD + 32 * kq, nok);
+                }
+                const double4_t acc = mfma_dot128_rb<F16>(a, kc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (kok && pos[i] >= 0 && key <= pos[i]) {
                         const double x = acc[i] * p.sc2;
-                        if (x > m[i]) {
-                            l[i] = l[i] * exp2_f64(m[i] - x) + 1.0;
+                        if (x > m[i] + 512.0) {
+                            l[i] = l[i] * exp2_f64(m[i] - x);
                             m[i] = x;
-                        } else {
-                            l[i] += exp2_f64(x - m[i]);
                         }
+                        l[i] += exp2_f64(x - m[i]);
                     }
                 }
             }
@@ -185,9 +227,10 @@ __global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
     }
 }
 
-// Pass 2: per (64-key block, g, b), column sums of the normalised softmax.
+// Pass 2: per (64-key block, g, b), column sums of the normalised softmax;
+// at most 128 VGPRs, so four waves share a SIMD.
 template <bool F16>
-__global__ __launch_bounds__(256) void k_probe_colsum(ProbeParams p) {
+__global__ __launch_bounds__(256, 4) void k_probe_colsum(ProbeParams p) {
     __shared__ double2 rs[512];
     __shared__ int rpos[512];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
