@@ -10,6 +10,7 @@ import pytest
 
 import oracle as O
 from synth import small_decode_inputs
+from synth.inputs import bf16_bits_from_f32
 
 from gpu_common import ints_to_dev, to_dev
 
@@ -40,7 +41,9 @@ def run_probe(inp, window, keep):
     return tuple(t.cpu().numpy() for t in (col, sel, cnt, thr))
 
 
-def check_probe(inp, window=128, keep=(5, 100), rel_tol=1e-6, sample=None):
+def check_probe(inp, window=128, keep=(5, 100), rel_tol=1e-6, sample=None, floor=0.0):
+    """floor > 0: oracle scores below it (under the fp32 range the scores are
+    returned in) are checked to be at most the floor instead of relatively."""
     sp = inp.spec
     col, sel, cnt, thr = run_probe(inp, window, keep)
     sm = 1 / math.sqrt(sp.D)
@@ -51,9 +54,11 @@ def check_probe(inp, window=128, keep=(5, 100), rel_tol=1e-6, sample=None):
         T = int(inp.seq_lens[b])
         c_or = O.probe_column_scores(qp[b, g * (sp.Hq // sp.Hkv):(g + 1) * (sp.Hq // sp.Hkv)],
                                      O.to_f64(inp.k[b, g:g + 1], sp.dtype), T, sm)[0]
-        rel = np.abs(col[b, g, :T].astype(np.float64) - c_or) / np.maximum(c_or, 1e-300)
+        big = c_or >= floor
+        rel = np.abs(col[b, g, :T].astype(np.float64) - c_or)[big] / np.maximum(c_or[big], 1e-300)
         worst = max(worst, float(rel.max()))
         assert rel.max() <= rel_tol, (b, g, float(rel.max()))
+        assert np.all(col[b, g, :T][~big] <= floor), (b, g)
         assert np.all(col[b, g, T:] == 0)
         flips += compare_selection(sel[b, g, : cnt[b, g]], int(cnt[b, g]), c_or, T, window, keep)
         # the top-k stage alone: the oracle's selection on the GPU's own fp32 scores
@@ -96,3 +101,23 @@ def test_probe_exact_ties_take_lower_index():
     chosen = sorted(set(sel[0, 0, : cnt[0, 0]].tolist()) & set(tied.tolist()))
     assert chosen == sorted(tied.tolist())[: len(chosen)]
     print(f"tied columns selected: {len(chosen)} of {len(tied)}")
+
+
+def test_probe_logit_range_beyond_reference():
+    """Logits spanning far more than 2^9 in log2 units inside one key chunk:
+    the probe's per-row reference has to move (the rare rescale path). All
+    probe rows share a direction u; keys 300..450 lie along u, giving logits
+    ~600 (log2 units) above the other keys, so nearly all of the softmax
+    mass, and every selected column, is on that plateau, while the other
+    columns' scores fall below the fp32 range."""
+    inp = small_decode_inputs(B=1, Hq=4, Hkv=1, T=1500, seed=49)
+    rng = np.random.default_rng(4949)
+    u = np.ones(128, dtype=np.float32)
+    qp = u + 0.3 * rng.standard_normal(inp.q_probe.shape, dtype=np.float32)
+    kp = 37.0 * u + rng.standard_normal((151, 128), dtype=np.float32)
+    inp.q_probe[...] = bf16_bits_from_f32(qp)
+    inp.k[0, 0, 300:451] = bf16_bits_from_f32(kp)
+    sm = 1 / math.sqrt(128)
+    logits = O.to_f64(inp.q_probe, "bf16")[0, 0] @ O.to_f64(inp.k, "bf16")[0, 0].T * sm / math.log(2)
+    assert logits[:, 300:451].min() - logits[:, :300].max() > 512
+    check_probe(inp, 128, (5, 100), floor=1e-30)
