@@ -21,9 +21,10 @@
 // column sums accumulate in fp64. The scores are rounded once to fp32.
 //
 // Top-k: one workgroup per (b, g); 4-pass 8-bit radix select on the fp32 bit
-// patterns (scores are >= 0, so bit order = value order) with LDS histograms,
-// then an index-ordered block-scan compaction that takes all scores above
-// the threshold and the lowest-index ties.
+// patterns (scores are >= 0, so bit order = value order) with LDS histograms
+// and a wave-parallel scan over the bins, then an index-ordered compaction
+// (each thread a contiguous run of candidates, two block scans) that takes
+// all scores above the threshold and the lowest-index ties.
 #include "hq_internal.h"
 
 namespace hq {
@@ -275,12 +276,17 @@ __global__ __launch_bounds__(256, 4) void k_probe_colsum(ProbeParams p) {
 
 // ---------------------------------------------------------------- top-k
 
-__device__ inline uint32_t block_excl_scan(uint32_t flag, uint32_t* wsum, uint32_t& total) {
-    // 1024 threads = 16 waves
+// Exclusive prefix sum of v over the 1024 threads of the block (16 waves);
+// total = the sum over all threads.
+__device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t bal = __ballot(flag);
-    const uint32_t within = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(bal);
+    uint32_t incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
@@ -291,7 +297,7 @@ __device__ inline uint32_t block_excl_scan(uint32_t flag, uint32_t* wsum, uint32
     }
     __syncthreads();
     total = tot;
-    return before + within;
+    return before + incl - v;
 }
 
 __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, const int32_t* seq_lens, int Hkv,
@@ -303,7 +309,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
     __shared__ int sh_jk;
     const int g = blockIdx.x, b = blockIdx.y;
     const int bg = b * Hkv + g;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int T = seq_lens[b];
     const int ncand = T > pol.window ? T - pol.window : 0;
     const int k = keep_count(T, pol);
@@ -323,6 +329,9 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
         sh_remaining = (uint32_t)k;
         sh_jk = -1;
     }
+    // Radix select, 8 bits per pass from the top: the threshold's bits are
+    // fixed one byte at a time; sh_remaining counts the candidates still to
+    // take among those matching the fixed bits.
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256; i += 1024) hist[i] = 0;
         __syncthreads();
@@ -332,35 +341,63 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
             if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
         }
         __syncthreads();
-        if (tid == 0) {
-            uint32_t cum = 0, rem = sh_remaining;
-            int bin = 255;
-            for (; bin > 0; --bin) {
-                if (cum + hist[bin] >= rem) break;
-                cum += hist[bin];
+        if (tid < 64) {
+            // the highest bin at which the count from the top reaches the
+            // remaining number: lane l holds bins 255 - 4l .. 252 - 4l
+            const uint32_t rem = sh_remaining;
+            uint32_t h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[i] = hist[255 - 4 * lane - i];
+            const uint32_t s4 = h[0] + h[1] + h[2] + h[3];
+            uint32_t incl = s4;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t t = __shfl_up(incl, off);
+                if (lane >= off) incl += t;
             }
-            sh_remaining = rem - cum;
-            sh_prefix = prefix | ((uint32_t)bin << shift);
-            sh_mask = mask | (255u << shift);
+            const uint32_t excl = incl - s4;
+            if (excl < rem && rem <= incl) {  // exactly one lane
+                uint32_t cum = excl;
+                int i = 0;
+                for (; i < 3; ++i) {
+                    if (cum + h[i] >= rem) break;
+                    cum += h[i];
+                }
+                const int bin = 255 - 4 * lane - i;
+                sh_remaining = rem - cum;
+                sh_prefix = prefix | ((uint32_t)bin << shift);
+                sh_mask = mask | (255u << shift);
+            }
         }
         __syncthreads();
     }
     const uint32_t tau = sh_prefix;
     const uint32_t remaining = sh_remaining;  // ties to take, lowest index first (>= 1)
-    uint32_t out = 0, ties = 0;
-    for (int base = 0; base < ncand; base += 1024) {
-        const int j = base + tid;
-        const uint32_t x = j < ncand ? xs[j] : 0u;
-        const bool gt = j < ncand && x > tau;
-        const bool eq = j < ncand && x == tau;
-        uint32_t eq_tot, take_tot;
-        const uint32_t eq_rank = ties + block_excl_scan(eq ? 1u : 0u, wsum, eq_tot);
-        const bool take = gt || (eq && eq_rank < remaining);
-        const uint32_t pos = out + block_excl_scan(take ? 1u : 0u, wsum, take_tot);
-        if (take) sel[pos] = j;
-        if (eq && eq_rank == remaining - 1) sh_jk = j;
-        out += take_tot;
-        ties += eq_tot;
+    // Compaction: thread t owns candidates [t*per, (t+1)*per); index order is
+    // thread order, so two block scans give every thread its output offset
+    // and its share of the ties.
+    const int per = (ncand + 1023) / 1024;
+    const int j0 = min(tid * per, ncand), j1 = min(j0 + per, ncand);
+    uint32_t ngt = 0, neq = 0;
+    for (int j = j0; j < j1; ++j) {
+        const uint32_t x = xs[j];
+        ngt += x > tau ? 1u : 0u;
+        neq += x == tau ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t eq_base = block_excl_scan(neq, wsum, tot);
+    const uint32_t take_eq = eq_base >= remaining ? 0u : min(neq, remaining - eq_base);
+    uint32_t pos = block_excl_scan(ngt + take_eq, wsum, tot);
+    uint32_t te = 0;
+    for (int j = j0; j < j1; ++j) {
+        const uint32_t x = xs[j];
+        if (x > tau) {
+            sel[pos++] = j;
+        } else if (x == tau && te < take_eq) {
+            sel[pos++] = j;
+            if (eq_base + te == remaining - 1) sh_jk = j;
+            ++te;
+        }
     }
     __syncthreads();
     if (tid == 0) {
