@@ -219,10 +219,13 @@ hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_n
  * split-K partial softmax states are merged by a second kernel.
  *   q   [B][Hq][D] cache->dt;  out [B][Hq][D] out_dt (HQ_F32 for parity)
  *   ws  workspace of hq_decode_ws_bytes(cache, Hq) bytes
- * Tuning: each INT4 split covers 43 cache tiles of 64 tokens; a positive
- * integer in the environment variable HQ_DECODE_TPS overrides that count
- * (the workspace query and the call read it alike, so it must not change
- * between them). The result does not depend on it beyond fp32 rounding. */
+ * Split size: the INT4 tiles (64 tokens) of a (b, g) are divided over
+ * ceil(tiles / 54) splits, raised until the grid fills whole rounds of the
+ * current device's workgroup slots (2 per CU for Hq/Hkv <= 4, else 1), with
+ * at least 8 tiles per split. A positive integer in the environment variable
+ * HQ_DECODE_TPS fixes the tiles per split instead. The workspace query and
+ * the call compute it alike (same device, same environment). The result does
+ * not depend on it beyond fp32 rounding. */
 hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,
                          void* out, hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
 size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq);

@@ -1,5 +1,6 @@
 // Host side of libhyquant: argument validation, sizing and launches.
 // Every check runs before anything is enqueued; on error nothing is launched.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -91,10 +92,38 @@ hq_status hip_fail(const char* fn, hipError_t e) {
     return fail(HQ_ERR_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
 }
 
-int32_t decode_tps() {
+// Compute units of the current device (cached per device; 0 if unknown).
+int32_t device_cus() {
+    static int32_t cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    if (dev < 64) cached[dev] = n;
+    return n;
+}
+
+// INT4 cache tiles per decode split. Start from 54 tiles per split and add
+// splits until the grid fills whole rounds of the device's workgroup slots
+// (two per CU for up to four query heads per KV head, else one): a partial
+// last round leaves CUs idle at the end of the kernel. At least 8 tiles (two
+// per wave) per split.
+int32_t decode_tps(const hq_cache& c, int32_t G) {
     const char* s = std::getenv("HQ_DECODE_TPS");
-    int v = s ? std::atoi(s) : 0;
-    return v > 0 ? v : 43;
+    const int v = s ? std::atoi(s) : 0;
+    if (v > 0) return v;
+    const int32_t tiles = c.cap_q / hq::kTile;
+    if (tiles < 1) return 54;
+    const int32_t base = (tiles + 53) / 54;
+    const int32_t n16 = hq::decode_nsplit(c, 54) - base;
+    const int64_t bg = (int64_t)c.B * c.Hkv;
+    const int64_t slots = (int64_t)(G <= 4 ? 2 : 1) * device_cus();
+    if (slots <= 0 || bg <= 0) return 54;
+    const int64_t total = (base + n16) * bg;
+    const int64_t rounds = (total + slots - 1) / slots;
+    const int64_t nsq = std::max<int64_t>(base, rounds * slots / bg - n16);
+    return std::max<int32_t>(8, (int32_t)((tiles + nsq - 1) / nsq));  // at least two tiles per wave
 }
 
 }  // namespace
@@ -217,7 +246,7 @@ hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_n
 
 size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq) {
     if (!cache || cache->Hkv < 1 || Hq < 1 || Hq % cache->Hkv) return 0;
-    const int32_t tps = decode_tps();
+    const int32_t tps = decode_tps(*cache, Hq / cache->Hkv);
     const int32_t nsplit = hq::decode_nsplit(*cache, tps);
     return hq::decode_ws_bytes(*cache, Hq, nsplit);
 }
@@ -238,7 +267,7 @@ hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float
     hq::DecodeLaunch d;
     d.Hq = Hq;
     d.G = Hq / cache->Hkv;
-    d.tiles_per_split = decode_tps();
+    d.tiles_per_split = decode_tps(*cache, d.G);
     d.nsplit = hq::decode_nsplit(*cache, d.tiles_per_split);
     d.sm_scale_log2 = sm_scale * 1.4426950408889634f;
     d.ws = ws;
@@ -286,7 +315,7 @@ hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B
 
 size_t hq_diag_read_int4_sink_bytes(const hq_cache* cache) {
     if (!cache || cache->B < 1 || cache->Hkv < 1 || cache->cap_q < hq::kTile) return 0;
-    return hq::diag_sink_bytes(*cache, decode_tps());
+    return hq::diag_sink_bytes(*cache, decode_tps(*cache, 4));
 }
 
 hq_status hq_diag_read_int4(const hq_cache* cache, void* sink, size_t sink_bytes, void* stream) {
@@ -295,9 +324,9 @@ hq_status hq_diag_read_int4(const hq_cache* cache, void* sink, size_t sink_bytes
     hq_status st;
     if ((st = check_cache(fn, cache))) return st;
     REQ_PTR(sink);
-    const size_t need = hq::diag_sink_bytes(*cache, decode_tps());
+    const size_t need = hq::diag_sink_bytes(*cache, decode_tps(*cache, 4));
     if (sink_bytes < need) return fail(HQ_ERR_CAPACITY, "%s: sink %zu bytes < required %zu", fn, sink_bytes, need);
-    hipError_t e = hq::launch_diag_read_int4(*cache, sink, decode_tps(), (hipStream_t)stream);
+    hipError_t e = hq::launch_diag_read_int4(*cache, sink, decode_tps(*cache, 4), (hipStream_t)stream);
     return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
 }
 
