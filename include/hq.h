@@ -35,8 +35,9 @@
  *     On error nothing is enqueued, no output is written, the call returns a
  *     negative status and hq_last_error() describes the problem. A failed
  *     kernel launch returns HQ_ERR_HIP with the HIP error string.
- *   - The library holds no global state and is safe to call from several
- *     threads (each thread has its own hq_last_error buffer).
+ *   - The library's only global state is a per-device cache of the compute
+ *     unit count (read once with hipDeviceGetAttribute). It is safe to call
+ *     from several threads (each thread has its own hq_last_error buffer).
  */
 #ifndef HQ_H_
 #define HQ_H_

@@ -1,6 +1,7 @@
 // Host side of libhyquant: argument validation, sizing and launches.
 // Every check runs before anything is enqueued; on error nothing is launched.
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -94,13 +95,16 @@ hq_status hip_fail(const char* fn, hipError_t e) {
 
 // Compute units of the current device (cached per device; 0 if unknown).
 int32_t device_cus() {
-    static int32_t cached[64] = {};
+    static std::atomic<int32_t> cached[64];  // zero-initialised (static storage)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    if (dev < 64) {
+        const int32_t c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-    if (dev < 64) cached[dev] = n;
+    if (dev < 64 && n > 0) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
