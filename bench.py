@@ -249,16 +249,35 @@ def cpu_baseline_prefill(pin, sel_idx, sel_cnt, budget_s=8.0):
                       f"({t_rows:.1f} s) plus one head's INT8 stage, scaled to {sp.T} rows x {sp.Hq} heads"}
 
 
+def _time_decode(hq, cache, knew, vnew, q, out, steps, warmup):
+    """Append + decode per step on one built cache; the Timer of the calls."""
+    import torch
+    tm = Timer()
+    for i in range(warmup + steps):
+        if i == warmup:
+            torch.cuda.synchronize()
+            tm.reset()
+        tm("append_kv", hq.append_kv, cache, knew, vnew)
+        tm("decode_attn", hq.decode_attn, cache, q, None, out)
+    torch.cuda.synchronize()
+    return tm
+
+
 def decode_sweep(args):
     """Decode (append + decode per step, on one built cache) on the 8B GQA
     shape at the context lengths of the pages' speed table: absolute time and
-    bandwidth per length, and the streaming-read rate of the same INT4 store."""
+    bandwidth per length, the streaming-read rate of the same INT4 store, and
+    the same decode kernel on a cache that keeps every position in bf16 (ratio
+    100%: the full-precision decode), for the hybrid / bf16 speed ratio. Then
+    the 16K prefill, hybrid against every column selected (bf16 scores
+    everywhere)."""
     import dataclasses
     import torch
     import kv_cache_amd as hq
-    from synth.inputs import CONFIGS, make_append_tokens, make_decode_inputs
+    from synth.inputs import CONFIGS, make_append_tokens, make_decode_inputs, make_prefill_inputs
     dev = "cuda:0"
     pol = hq.Policy()
+    pol_bf16 = hq.Policy(100, 100, pol.window, pol.probe_rows)
     rows = []
     for T in (1024, 2048, 4096, 8192, 16384, 32768):
         spec = dataclasses.replace(CONFIGS["c2_decode_8b_32k"], name=f"decode_8b_gqa_b16_{T}", T=T)
@@ -272,13 +291,7 @@ def decode_sweep(args):
         col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol)
         hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
         out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.float32, device=dev)
-        tm = Timer()
-        for i in range(args.warmup + args.steps):
-            if i == args.warmup:
-                torch.cuda.synchronize()
-                tm.reset()
-            tm("append_kv", hq.append_kv, cache, knew, vnew)
-            tm("decode_attn", hq.decode_attn, cache, q, None, out)
+        tm = _time_decode(hq, cache, knew, vnew, q, out, args.steps, args.warmup)
         sink = hq.diag_read_int4(cache)
         for _ in range(10):
             tm("diag", hq.diag_read_int4, cache, sink)
@@ -291,11 +304,49 @@ def decode_sweep(args):
                      "bytes": by, "TBps": round(by / (dms * 1e-3) / 1e12, 3),
                      "frac_of_peak": round(by / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "int4_stream_TBps": round(i4 / (tm.ms("diag") * 1e-3) / 1e12, 3)})
+        del cache
+        torch.cuda.empty_cache()
+        # the same kernel with every position kept in bf16
+        cache = hq.HybridCache(spec.B, spec.Hkv, T + 64, T, torch.bfloat16, dev, pol_bf16)
+        col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol_bf16)
+        hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
+        tmb = _time_decode(hq, cache, knew, vnew, q, out, args.steps, args.warmup)
+        cb = cache.counts().cpu().numpy()
+        byb = decode_bytes_per_step(cb)
+        bms = tmb.ms("decode_attn")
+        rows[-1].update({"bf16_decode_us": round(bms * 1e3, 2), "bf16_decode_us_p10_p50_p90": tmb.pct("decode_attn", 1e3),
+                         "bf16_bytes": byb, "bf16_TBps": round(byb / (bms * 1e-3) / 1e12, 3),
+                         # ratio of the medians (robust to a slow call at short lengths)
+                         "bf16_over_hybrid": round(tmb.pct("decode_attn", 1e3)[1] / tm.pct("decode_attn", 1e3)[1], 3),
+                         # tokens that left the window during the timed appends
+                         # and ranked below the selection threshold
+                         "bf16_cache_int4_tokens": int(cb[..., 1].sum())})
         print(f"# sweep T={T}: {rows[-1]}", file=sys.stderr, flush=True)
         del cache, k, v, inp
         torch.cuda.empty_cache()
+    # prefill at 16K: hybrid against every column selected
+    pspec = CONFIGS["c4_prefill_8b_16k"]
+    pin = make_prefill_inputs(pspec)
+    pq, pk, pv = _dev16(pin.q, "bf16", dev), _dev16(pin.k, "bf16", dev), _dev16(pin.v, "bf16", dev)
+    plens = torch.full((1,), pspec.T, dtype=torch.int32, device=dev)
+    pqp = pq[:, :, pspec.T - 64:].contiguous()
+    pout = torch.empty((1, pspec.Hq, pspec.T, 128), dtype=torch.float32, device=dev)
+    prefill = {"T": pspec.T}
+    for name, pl in (("hybrid", pol), ("bf16", pol_bf16)):
+        psel = hq.probe_select(pqp, pk, plens, pl)
+        tmp = Timer()
+        for i in range(3 + max(5, args.steps // 2)):
+            if i == 3:
+                torch.cuda.synchronize()
+                tmp.reset()
+            tmp("prefill_attn", hq.prefill_attn, pq, pk, pv, psel[1], psel[2], pl, None, pout)
+        torch.cuda.synchronize()
+        prefill[f"{name}_ms"] = round(tmp.ms("prefill_attn"), 3)
+        prefill[f"{name}_ms_p10_p50_p90"] = tmp.pct("prefill_attn", 1.0)
+    prefill["bf16_over_hybrid"] = round(prefill["bf16_ms_p10_p50_p90"][1] / prefill["hybrid_ms_p10_p50_p90"][1], 3)
+    print(f"# sweep prefill: {prefill}", file=sys.stderr, flush=True)
     print(json.dumps({"sweep": "decode_8b_gqa_b16 (B=16, 32/8 heads, bf16, top-5% + 128 window, INT4 g32)",
-                      "steps": args.steps, "warmup": args.warmup, "rows": rows}), flush=True)
+                      "steps": args.steps, "warmup": args.warmup, "rows": rows, "prefill_16k": prefill}), flush=True)
 
 
 def prefill_only(args):

@@ -26,6 +26,8 @@ CASES = {
     "bf16_g2": (dict(B=3, Hq=4, Hkv=2, T=640, seed=14), 128, (5, 100)),
     "bf16_short_T_lt_W": (dict(B=2, Hq=4, Hkv=1, T=100, probe_rows=64, seed=15), 128, (5, 100)),
     "bf16_ratio100": (dict(B=1, Hq=4, Hkv=1, T=500, seed=16), 128, (100, 100)),
+    # every position 16-bit over several 16-tile splits: the full-precision decode
+    "bf16_ratio100_multisplit": (dict(B=2, Hq=8, Hkv=2, T=2900, ragged_min=2100, seed=22), 128, (100, 100)),
     "bf16_window_covers": (dict(B=1, Hq=4, Hkv=1, T=900, seed=17), 1024, (5, 100)),
     "bf16_all_int4": (dict(B=1, Hq=4, Hkv=1, T=777, seed=18), 0, (0, 100)),
     # V magnitudes spanning 2^16 across the sequence: the PV weight scale grows

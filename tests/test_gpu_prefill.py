@@ -140,6 +140,8 @@ CASES = [
     ("T64", 1, 2, 1, 64, "f16", 128, (5, 100), "seeded"),
     ("T129", 1, 2, 2, 129, "bf16", 64, (5, 100), "seeded"),
     ("T1000_w64", 1, 4, 1, 1000, "bf16", 64, (10, 100), "oracle"),
+    # every candidate selected: all scores 16-bit, i.e. exact causal attention
+    ("all_selected", 1, 4, 2, 900, "bf16", 128, (100, 100), "oracle"),
 ]
 
 
@@ -161,6 +163,16 @@ def test_prefill_parity(case):
     check_int8_stage(inp, ws)
     ref = oracle_prefill_all(inp, sels, W)
     assert_attn_close(out.cpu().numpy(), ref, name)
+    if keep == (100, 100):
+        # every candidate selected: exact causal softmax attention
+        o = out.cpu().numpy()
+        G, sm = Hq // Hkv, 1 / math.sqrt(spec.D)
+        qf, kf, vf = (O.to_f64(x, dtype) for x in (inp.q, inp.k, inp.v))
+        ex = np.zeros_like(o, dtype=np.float64)
+        for h in range(Hq):
+            for i in range(T):
+                ex[0, h, i] = O.softmax_attention(qf[0, h, i:i + 1], kf[0, h // G, :i + 1], vf[0, h // G, :i + 1], sm)[0]
+        assert_attn_close(o, ex, f"{name} exact causal attention")
 
 
 def test_prefill_zero_block_and_out_dtypes():
