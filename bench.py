@@ -50,6 +50,9 @@ def _args():
                     help="time only the prefill probe + attention per step and print its fields (profiling aid)")
     ap.add_argument("--sweep", action="store_true",
                     help="decode on the 8B GQA shape (B=16, 32/8 heads) at T = 1K..32K; prints one JSON line")
+    ap.add_argument("--ablation", action="store_true",
+                    help="decode output error of the cache policies (uniform INT4, hybrid 1%%/5%%) against the "
+                         "all-bf16 cache on the 8B GQA shape at T = 1K..32K; prints one JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain device copy of this size (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -263,6 +266,49 @@ def _time_decode(hq, cache, knew, vnew, q, out, steps, warmup):
     return tm
 
 
+def decode_ablation(args):
+    """Decode output error of each cache policy against the same decode on a
+    cache that keeps every position in bf16 (ratio 100%), on the seeded 8B GQA
+    inputs (outlier K channels, planted vertical lines) at T = 1K..32K. Every
+    output comes from hq_decode_attn; the error is of the fp32 outputs."""
+    import dataclasses
+    import torch
+    import kv_cache_amd as hq
+    from synth.inputs import CONFIGS, make_append_tokens, make_decode_inputs
+    dev = "cuda:0"
+    policies = [("int4_all", hq.Policy(0, 100, 0, 64)), ("int4_window128", hq.Policy(0, 100, 128, 64)),
+                ("hybrid_1pct", hq.Policy(1, 100, 128, 64)), ("hybrid_5pct", hq.Policy(5, 100, 128, 64)),
+                ("bf16_all", hq.Policy(100, 100, 128, 64))]
+    rows = []
+    for T in (1024, 4096, 16384, 32768):
+        spec = dataclasses.replace(CONFIGS["c2_decode_8b_32k"], name=f"decode_8b_gqa_b16_{T}", T=T)
+        inp = make_decode_inputs(spec)
+        _, _, qn = make_append_tokens(spec, inp.outlier_channels, 1)
+        k, v = _dev16(inp.k, "bf16", dev), _dev16(inp.v, "bf16", dev)
+        qp, q = _dev16(inp.q_probe, "bf16", dev), _dev16(qn[0], "bf16", dev)
+        lens = torch.from_numpy(inp.seq_lens).to(dev)
+        outs = {}
+        for name, pol in policies:
+            cache = hq.HybridCache(spec.B, spec.Hkv, T, T, torch.bfloat16, dev, pol)
+            col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol)
+            hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
+            outs[name] = hq.decode_attn(cache, q).double().cpu()
+            del cache
+            torch.cuda.empty_cache()
+        ref = outs["bf16_all"]
+        row = {"T": T}
+        for name, _ in policies[:-1]:
+            d = outs[name] - ref
+            row[name] = {"mse": float((d * d).mean()), "rel_l2": float(d.norm() / ref.norm()),
+                         "max_abs": float(d.abs().max())}
+        rows.append(row)
+        print(f"# ablation T={T}: {row}", file=sys.stderr, flush=True)
+        del k, v, inp
+        torch.cuda.empty_cache()
+    print(json.dumps({"ablation": "decode_8b_gqa_b16 (B=16, 32/8 heads, bf16 inputs); error of the fp32 decode "
+                                  "output against the all-bf16 cache", "rows": rows}), flush=True)
+
+
 def decode_sweep(args):
     """Decode (append + decode per step, on one built cache) on the 8B GQA
     shape at the context lengths of the pages' speed table: absolute time and
@@ -405,6 +451,8 @@ def main():
         return prefill_only(args)
     if args.sweep:
         return decode_sweep(args)
+    if args.ablation:
+        return decode_ablation(args)
     t_gen = time.perf_counter()
     spec = CONFIGS["c2_decode_8b_32k"]
     inp = make_decode_inputs(spec)
