@@ -117,8 +117,8 @@ struct ProbeParams {
     const uint16_t* q;     // [B][Hq][R][D]
     const uint16_t* k;     // [B][Hkv][Tmax][D]
     const int32_t* seq_lens;
-    double2* part;         // [B][Hkv][nchunk][NR] (m, l) per key chunk
-    double2* rows;         // [B][Hkv][NR] (m, 1/l)
+    double2* part;         // [B][Hkv][nchunk][NR] (m, l) per key chunk: l = sum of 2^(x - m), m a reference
+    double2* rows;         // [B][Hkv][NR] (M, 1/L) over all chunks, M = the largest chunk reference
     float* col_scores;     // [B][Hkv][Tmax]
     int32_t B, Hq, Hkv, Tmax, R, G, NR, nchunk;
     double sc2;            // sm_scale * log2(e)
@@ -210,7 +210,8 @@ __global__ __launch_bounds__(256, 3) void k_probe_rowstats(ProbeParams p) {
     }
 }
 
-// Merge the chunk statistics of every probe row: (m, 1/l).
+// Merge the chunk statistics of every probe row: (M, 1/L), with M the
+// largest chunk reference and L = sum of l * 2^(m - M).
 __global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
     const int g = blockIdx.x, b = blockIdx.y;
     const int bg = b * p.Hkv + g;
