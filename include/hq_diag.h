@@ -18,8 +18,10 @@ extern "C" {
 
 /* hq_diag_read_int4 -- read the INT4 store of `cache` (K and V codes, K and V
  * scale/zero of the n_q quantized tokens of every (b, g)) exactly as
- * hq_decode_attn's INT4 workgroups read it: the same splits, 64-token tiles,
- * 128-bit loads and two tiles in flight per wave; nothing is computed but an
+ * hq_decode_attn's INT4 workgroups read it: the same splits (those of a
+ * decode with up to four query heads per KV head), 64-token tiles, 128-bit
+ * loads with the non-temporal hint and two tiles in flight per wave; nothing is
+ * computed but an
  * XOR of the loaded words, written to `sink` (one word per thread, so the
  * loads cannot be dropped). The bytes read are 160 per quantized
  * token-head; the call's time gives the achievable streaming-read rate of
