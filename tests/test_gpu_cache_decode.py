@@ -136,6 +136,35 @@ def test_quantize_and_decode(name):
                 assert_attn_close(out[b, h * G:(h + 1) * G], ex, f"{name} exact-attention special case")
 
 
+def test_quantize_flags_invalid_selection():
+    """A selected-position list that is not strictly ascending is reported in
+    the cache's error flag (bit 2); the entries before the bad one are still
+    stored in the kept store."""
+    import torch
+    import kv_cache_amd as hq
+    inp = small_decode_inputs(B=1, Hq=4, Hkv=1, T=700, seed=23)
+    sp = inp.spec
+    pol = hq.Policy(5, 100, 128, sp.probe_rows)
+    scores, sels = oracle_selection(inp, 128, (5, 100))
+    Tmax = inp.k.shape[2]
+    stride = hq.sel_stride(Tmax, pol)
+    sel, cnt, col, thr = selection_tensors(scores, sels, sp.B, sp.Hkv, Tmax, stride)
+    k = int(cnt[0, 0].item())
+    assert k >= 8
+    bad = sel.clone()
+    bad[0, 0, 5] = bad[0, 0, 4]  # a repeated position
+    cache = hq.HybridCache(sp.B, sp.Hkv, Tmax + 256, Tmax, torch_dt(sp.dtype), "cuda", pol)
+    hq.quantize_kv(cache, to_dev(inp.k, sp.dtype), to_dev(inp.v, sp.dtype), ints_to_dev(inp.seq_lens), bad, cnt, col,
+                   thr)
+    torch.cuda.synchronize()
+    g = read_cache(cache)
+    assert g["err_flag"] & 4, g["err_flag"]
+    good = sel[0, 0, :5].cpu().numpy()
+    assert np.array_equal(g["keep_pos"][0, :5], good)
+    assert np.array_equal(g["k_keep"][0, :5], inp.k[0, 0][good])
+    assert np.array_equal(g["v_keep"][0, :5], inp.v[0, 0][good])
+
+
 def test_decode_output_dtypes_and_determinism():
     import torch
     import kv_cache_amd as hq
