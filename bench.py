@@ -53,6 +53,9 @@ def _args():
     ap.add_argument("--ablation", action="store_true",
                     help="decode output error of the cache policies (uniform INT4, hybrid 1%%/5%%) against the "
                          "all-bf16 cache on the 8B GQA shape at T = 1K..32K; prints one JSON line")
+    ap.add_argument("--configs", action="store_true",
+                    help="append + decode timed on every decode workload (4K 1 head, 32K 8B, 128K 8B, ragged 64K "
+                         "70B-like); prints one JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain device copy of this size (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -266,6 +269,43 @@ def _time_decode(hq, cache, knew, vnew, q, out, steps, warmup):
     return tm
 
 
+def decode_configs(args):
+    """Append + decode on each decode workload's full shape (one built cache
+    per workload, the steps timed as in the main loop), with the achieved HBM
+    rate of the algorithmic bytes."""
+    import torch
+    import kv_cache_amd as hq
+    from synth.inputs import CONFIGS, make_append_tokens, make_decode_inputs
+    dev = "cuda:0"
+    pol = hq.Policy()
+    rows = []
+    for name in ("c1_decode_4k_1head", "c2_decode_8b_32k", "c3_decode_8b_128k_append", "c5_decode_70b_ragged_64k"):
+        spec = CONFIGS[name]
+        inp = make_decode_inputs(spec)
+        kn, vn, qn = make_append_tokens(spec, inp.outlier_channels, 1)
+        dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float16
+        k, v = _dev16(inp.k, spec.dtype, dev), _dev16(inp.v, spec.dtype, dev)
+        qp, q = _dev16(inp.q_probe, spec.dtype, dev), _dev16(qn[0], spec.dtype, dev)
+        knew, vnew = _dev16(kn[0], spec.dtype, dev), _dev16(vn[0], spec.dtype, dev)
+        lens = torch.from_numpy(inp.seq_lens).to(dev)
+        cache = hq.HybridCache(spec.B, spec.Hkv, spec.T + 64, spec.T, dt, dev, pol)
+        col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol)
+        hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
+        out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.float32, device=dev)
+        tm = _time_decode(hq, cache, knew, vnew, q, out, args.steps, args.warmup)
+        counts = cache.counts().cpu().numpy()
+        by = decode_bytes_per_step(counts)
+        dms = tm.pct("decode_attn", 1e3)[1] * 1e-3  # the median call, ms
+        rows.append({"workload": name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "T": spec.T,
+                     "decode_us_p10_p50_p90": tm.pct("decode_attn", 1e3), "append_us": round(tm.ms("append_kv") * 1e3, 2),
+                     "bytes": by, "TBps_p50": round(by / (dms * 1e-3) / 1e12, 3),
+                     "frac_of_peak_p50": round(by / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
+        print(f"# configs {name}: {rows[-1]}", file=sys.stderr, flush=True)
+        del cache, k, v, inp
+        torch.cuda.empty_cache()
+    print(json.dumps({"configs": rows, "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def decode_ablation(args):
     """Decode output error of each cache policy against the same decode on a
     cache that keeps every position in bf16 (ratio 100%), on the seeded 8B GQA
@@ -453,6 +493,8 @@ def main():
         return decode_sweep(args)
     if args.ablation:
         return decode_ablation(args)
+    if args.configs:
+        return decode_configs(args)
     t_gen = time.perf_counter()
     spec = CONFIGS["c2_decode_8b_32k"]
     inp = make_decode_inputs(spec)

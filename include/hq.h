@@ -222,7 +222,8 @@ hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_n
  *   ws  workspace of hq_decode_ws_bytes(cache, Hq) bytes
  * Split size: the INT4 tiles (64 tokens) of a (b, g) are divided over
  * ceil(tiles / 54) splits, raised until the grid fills whole rounds of the
- * current device's workgroup slots (2 per CU for Hq/Hkv <= 4, else 1), with
+ * current device's workgroup slots (2 per CU; eight heads per KV head run
+ * as two four-head workgroups per split), with
  * at least 8 tiles per split. A positive integer in the environment variable
  * HQ_DECODE_TPS fixes the tiles per split instead. The workspace query and
  * the call compute it alike (same device, same environment). The result does

@@ -110,9 +110,8 @@ int32_t device_cus() {
 
 // INT4 cache tiles per decode split. Start from 54 tiles per split and add
 // splits until the grid fills whole rounds of the device's workgroup slots
-// (two per CU for up to four query heads per KV head, else one): a partial
-// last round leaves CUs idle at the end of the kernel. At least 8 tiles (two
-// per wave) per split.
+// (two per CU): a partial last round leaves CUs idle at the end of the
+// kernel. At least 8 tiles (two per wave) per split.
 int32_t decode_tps(const hq_cache& c, int32_t G) {
     const char* s = std::getenv("HQ_DECODE_TPS");
     const int v = s ? std::atoi(s) : 0;
@@ -121,8 +120,9 @@ int32_t decode_tps(const hq_cache& c, int32_t G) {
     if (tiles < 1) return 54;
     const int32_t base = (tiles + 53) / 54;
     const int32_t n16 = hq::decode_nsplit(c, 54) - base;
-    const int64_t bg = (int64_t)c.B * c.Hkv;
-    const int64_t slots = (int64_t)(G <= 4 ? 2 : 1) * device_cus();
+    // eight heads per KV head run as two four-head workgroups per split
+    const int64_t bg = (int64_t)c.B * c.Hkv * (G > 4 ? 2 : 1);
+    const int64_t slots = 2 * (int64_t)device_cus();
     if (slots <= 0 || bg <= 0) return 54;
     const int64_t total = (base + n16) * bg;
     const int64_t rounds = (total + slots - 1) / slots;

@@ -55,6 +55,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
+constexpr int kTps16 = 16;  // 16-bit tiles per split
+
 struct DecodeParams {
     hq_cache c;
     const uint32_t* qw;    // [B][Hq][64] query words (channels 2c, 2c + 1 of word c); 16-byte aligned
@@ -62,8 +64,9 @@ struct DecodeParams {
     float* part_m;         // [B][Hkv][nsplit][G]
     float* part_l;         // [B][Hkv][nsplit][G]
     float* part_o;         // [B][Hkv][nsplit][G][128]
-    int32_t nsplit, G;
+    int32_t nsplit, G;     // G: query heads per KV head (the partials' and the query's head count)
     int32_t nsq;           // INT4 splits (the first nsq partials of a (b, g))
+    int32_t halves;        // 2: the kernel's heads are half of G, the two halves run as separate workgroups
     float scale2;          // sm_scale * log2(e)
 };
 
@@ -178,7 +181,8 @@ struct SplitSmem {
 };
 
 template <int G, bool F16, int MODE>
-__device__ __attribute__((always_inline)) inline void split_body(const DecodeParams& p, SplitSmem<G>& sm, int s) {
+__device__ __attribute__((always_inline)) inline void split_body(const DecodeParams& p, SplitSmem<G>& sm, int s,
+                                                                 int half) {
     constexpr int NHB = (G + 3) / 4;  // 4-head blocks of the QK product
     // per wave: QK partials y[block nb][head block][lane] (float4), the PV
     // weights w[group][token half][token octet][head][8 slots] (fp16), the
@@ -208,7 +212,7 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
     const int v1 = MODE == 0 ? (s + 1) * nqt / p.nsq : nqt + (s + 1) * n16t / n16s;
     const int split_out = MODE == 0 ? s : p.nsq + s;
     if (v0 >= v1) {  // nothing here: an empty partial
-        const size_t pb = ((size_t)bg * p.nsplit + split_out) * G;
+        const size_t pb = ((size_t)bg * p.nsplit + split_out) * p.G + half * G;
         for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
             p.part_o[pb * kD + idx] = 0.f;
             if (idx < G) {
@@ -221,7 +225,7 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
 
     const int qt_cap = p.c.cap_q / kTile, kt_cap = p.c.cap_keep / kTile, wt_cap = W / kTile;
     // the 16-bit tiles take the query's own words: word h*64 + c holds channels 2c, 2c + 1 of head h
-    const uint32_t* qn = p.qw + (size_t)bg * G * (kD / 2);  // Hq = Hkv * G
+    const uint32_t* qn = p.qw + ((size_t)bg * p.G + half * G) * (kD / 2);  // Hq = Hkv * p.G
 
     // softmax state (lane = token), channel accumulators
     float m[G], l[G], zacc[G][4], wsb[G][4];
@@ -680,7 +684,7 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
     }
     __syncthreads();
     // ----------------------------- merge the waves, write the split partial
-    const size_t pbase = ((size_t)bg * p.nsplit + split_out) * G;
+    const size_t pbase = ((size_t)bg * p.nsplit + split_out) * p.G + half * G;
     for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
         const int h = idx / kD, d = idx % kD;
         float M = lds_m[0][h];
@@ -707,11 +711,18 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
 template <int G, bool F16>
 __global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void k_decode_split(DecodeParams p) {
     __shared__ SplitSmem<G> sm;
-    const int x = blockIdx.x;
+    int x = blockIdx.x, half = 0;
+    if (p.halves == 2) {
+        // the two head halves of split x are 8 workgroups apart in dispatch
+        // order, so they land on the same XCD and share its L2
+        half = (x >> 3) & 1;
+        x = (x >> 4) * 8 + (x & 7);
+        if (x >= p.nsplit) return;
+    }
     if (x < p.nsq)
-        split_body<G, F16, 0>(p, sm, x);
+        split_body<G, F16, 0>(p, sm, x, half);
     else
-        split_body<G, F16, 1>(p, sm, x - p.nsq);
+        split_body<G, F16, 1>(p, sm, x - p.nsq, half);
 }
 
 // Rearranges the query for the split kernel: per head a power-of-two scale
@@ -786,10 +797,10 @@ void launch_split(const DecodeParams& p, int Hkv, int B, hipStream_t s) {
     // fill in as slots free up.
     // the query goes in as a separate read-only, non-aliased argument so that
     // its wave-uniform reads become scalar loads
-    k_decode_split<G, F16><<<dim3(p.nsplit, Hkv, B), 256, 0, s>>>(p);
+    const int gx = p.halves == 2 ? (p.nsplit + 7) / 8 * 16 : p.nsplit;
+    k_decode_split<G, F16><<<dim3(gx, Hkv, B), 256, 0, s>>>(p);
 }
 
-constexpr int kTps16 = 16;  // 16-bit tiles per split
 
 }  // namespace
 
@@ -820,6 +831,7 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
     p.nsplit = d.nsplit;
     p.nsq = decode_nsq(c, d.tiles_per_split);
     p.G = d.G;
+    p.halves = d.G == 8 ? 2 : 1;  // eight heads run as two workgroups of four
     p.scale2 = d.sm_scale_log2;
     const bool f16 = c.dt == HQ_F16;
     switch (d.G * 2 + (f16 ? 1 : 0)) {
@@ -829,8 +841,8 @@ hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype o
         case 5: launch_split<2, true>(p, c.Hkv, c.B, s); break;
         case 8: launch_split<4, false>(p, c.Hkv, c.B, s); break;
         case 9: launch_split<4, true>(p, c.Hkv, c.B, s); break;
-        case 16: launch_split<8, false>(p, c.Hkv, c.B, s); break;
-        case 17: launch_split<8, true>(p, c.Hkv, c.B, s); break;
+        case 16: launch_split<4, false>(p, c.Hkv, c.B, s); break;
+        case 17: launch_split<4, true>(p, c.Hkv, c.B, s); break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
