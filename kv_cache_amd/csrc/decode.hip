@@ -180,7 +180,7 @@ struct SplitSmem {
     float qsc[8];           // per head 2^-k
 };
 
-template <int G, bool F16, int MODE>
+template <int G, bool F16, int MODE, bool NT = true>
 __device__ __attribute__((always_inline)) inline void split_body(const DecodeParams& p, SplitSmem<G>& sm, int s,
                                                                  int half) {
     constexpr int NHB = (G + 3) / 4;  // 4-head blocks of the QK product
@@ -268,7 +268,7 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
             0x00020000);
         const int voff = lane * 16;
         auto ld = [&](const __amdgpu_buffer_rsrc_t& r, int soff) {
-            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kLoadNT));
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? kLoadNT : 0));
         };
         auto load_tile = [&](int v, TileRegs& r) {
 #pragma unroll
@@ -708,7 +708,7 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
 
 // One launch covers both kinds of split: workgroups x < nsq take INT4 tiles,
 // the rest take 16-bit tiles, so the two kinds run side by side.
-template <int G, bool F16>
+template <int G, bool F16, bool NT = true>
 __global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void k_decode_split(DecodeParams p) {
     __shared__ SplitSmem<G> sm;
     int x = blockIdx.x, half = 0;
@@ -720,9 +720,9 @@ __global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void k_decode_split(DecodePara
         if (x >= p.nsplit) return;
     }
     if (x < p.nsq)
-        split_body<G, F16, 0>(p, sm, x, half);
+        split_body<G, F16, 0, NT>(p, sm, x, half);
     else
-        split_body<G, F16, 1>(p, sm, x - p.nsq, half);
+        split_body<G, F16, 1, NT>(p, sm, x - p.nsq, half);
 }
 
 // Rearranges the query for the split kernel: per head a power-of-two scale
@@ -798,7 +798,13 @@ void launch_split(const DecodeParams& p, int Hkv, int B, hipStream_t s) {
     // the query goes in as a separate read-only, non-aliased argument so that
     // its wave-uniform reads become scalar loads
     const int gx = p.halves == 2 ? (p.nsplit + 7) / 8 * 16 : p.nsplit;
-    k_decode_split<G, F16><<<dim3(gx, Hkv, B), 256, 0, s>>>(p);
+    // the two-halves launch reads with the default cache policy: the L2 then
+    // keeps the lines for the sibling workgroup (measured faster than the
+    // non-temporal hint there)
+    if (p.halves == 2)
+        k_decode_split<G, F16, false><<<dim3(gx, Hkv, B), 256, 0, s>>>(p);
+    else
+        k_decode_split<G, F16><<<dim3(gx, Hkv, B), 256, 0, s>>>(p);
 }
 
 
