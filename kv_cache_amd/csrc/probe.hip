@@ -131,12 +131,29 @@ __device__ inline const uint16_t* qrow(const ProbeParams& p, int b, int g, int r
 __device__ inline int row_pos(const ProbeParams& p, int T, int row) { return T - p.R + (row % p.R); }
 
 // Pass 1: per (key chunk, g, b), online reference / sum of 2^x per probe
-// row. Each wave keeps its row tile's queries in fp64 and streams the key
-// tiles, the next tile's raw 16-bit values loaded while this tile's 32 MFMAs
-// run; at most 168 VGPRs, so three waves share a SIMD.
+// row. A workgroup of 16 waves, one 16-row tile of probe rows per wave (its
+// queries held in fp64), streams the chunk's keys 16 at a time: each key tile
+// is converted to fp64 once into LDS (double-buffered; the next tile's raw
+// values are loaded while this one is computed) and read by every wave.
+constexpr int kPW = 16;          // waves per pass-1 workgroup
+constexpr int kKRow = kD + 2;    // LDS row stride in doubles (16-byte pad: no bank conflicts across rows)
 template <bool F16>
-__global__ __launch_bounds__(256, 3) void k_probe_rowstats(ProbeParams p) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ inline double4_t mfma_dot128_lds(const double* a, const double* brow) {
+    double4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < 32; s += 2) {
+        const double2 bb = *reinterpret_cast<const double2*>(brow + s);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], bb.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s + 1], bb.y, acc, 0, 0, 0);
+        if ((s & 7) == 6) asm volatile("" ::: "memory");  // bound the LDS reads in flight
+    }
+    return acc;
+}
+template <bool F16>
+__global__ __launch_bounds__(1024) void k_probe_rowstats(ProbeParams p) {
+    __shared__ __align__(16) double kt[2][16][kKRow];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int T = p.seq_lens[b];
     const int key_lo = chunk * kKeyChunk;
@@ -144,37 +161,61 @@ __global__ __launch_bounds__(256, 3) void k_probe_rowstats(ProbeParams p) {
     const int li = lane & 15, kq = lane >> 4;
     const uint16_t* kbase = p.k + (size_t)bg * p.Tmax * kD;
     const int nrt = p.NR / 16;
-    for (int rt = wave; rt < nrt; rt += 4) {
+    double2* part = p.part + ((size_t)bg * p.nchunk + chunk) * p.NR;
+    if (key_lo >= T) {  // no key of this chunk exists: empty statistics
+        for (int r = tid; r < p.NR; r += 1024) part[r] = make_double2(-INFINITY, 0.0);
+        return;
+    }
+    const int key_hi = min(key_lo + kKeyChunk, T);
+    const int ntile = (key_hi - key_lo + 15) / 16;
+    // staging: thread t < 256 moves 8 channels (16 bytes) of key t / 16 of a tile
+    const int srow = (tid >> 4) & 15, sc0 = (tid & 15) * 8;
+    auto stage_load = [&](int t) {
+        const int key = key_lo + 16 * t + srow;
+        const bool ok = tid < 256 && key < key_hi;
+        return ok ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * kD + sc0) : make_uint4(0, 0, 0, 0);
+    };
+    auto stage_store = [&](int buf, const uint4& raw) {
+        if (tid < 256) {
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+            double* dst = &kt[buf][srow][sc0];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<double2*>(dst + 2 * j) =
+                    make_double2((double)h16_to_f32<F16>(w[j] & 0xFFFFu), (double)h16_to_f32<F16>(w[j] >> 16));
+        }
+    };
+    for (int rt0 = 0; rt0 < nrt; rt0 += kPW) {
+        const int rt = rt0 + wave;
+        const bool active = rt < nrt;  // wave-uniform
+        stage_store(0, stage_load(0));
+        __syncthreads();
         double m[4], l[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             m[i] = -INFINITY;
             l[i] = 0.0;
         }
-        if (key_lo < T) {
-            double a[32];
+        double a[32];
+        int pos[4];
+        if (active) {
             load32_f64<F16>(qrow(p, b, g, rt * 16 + li) + 32 * kq, true, a);
-            int pos[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) pos[i] = row_pos(p, T, rt * 16 + 4 * i + kq);
-            const int key_hi = min(key_lo + kKeyChunk, T);
-            // m is a reference, not the running maximum: l = sum of 2^(x - m)
-            // with m moved only when a logit exceeds it by more than 2^9
-            // (and on the first one), so the common path takes one exp per
-            // element and no divergent branch. Terms up to 2^512 are exact
-            // in fp64 range; the chunk merge and the normalisation accept
-            // any reference.
-            Raw32 kn = load_raw32(kbase + (size_t)(key_lo + li < T ? key_lo + li : 0) * kD + 32 * kq, key_lo + li < T);
-            for (int k0 = key_lo; k0 < key_hi; k0 += 16) {
-                const int key = k0 + li;
-                const bool kok = key < T;
-                const Raw32 kc = kn;
-                {
-                    const int nk = key + 16;
-                    const bool nok = nk < key_hi;
-                    kn = load_raw32(kbase + (size_t)(nok ? nk : 0) * kD + 32 * kq, nok);
-                }
-                const double4_t acc = mfma_dot128_rb<F16>(a, kc);
+        }
+        // m is a reference, not the running maximum: l = sum of 2^(x - m)
+        // with m moved only when a logit exceeds it by more than 2^9 (and on
+        // the first one), so the common path takes one exp per element and
+        // no divergent branch. Terms up to 2^512 are exact in fp64 range; the
+        // chunk merge and the normalisation accept any reference.
+        for (int t = 0; t < ntile; ++t) {
+            const int cur = t & 1;
+            const bool more = t + 1 < ntile;
+            const uint4 nraw = more ? stage_load(t + 1) : make_uint4(0, 0, 0, 0);
+            if (active) {
+                const int key = key_lo + 16 * t + li;
+                const bool kok = key < key_hi;
+                const double4_t acc = mfma_dot128_lds<F16>(a, &kt[cur][li][32 * kq]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (kok && pos[i] >= 0 && key <= pos[i]) {
@@ -187,25 +228,28 @@ __global__ __launch_bounds__(256, 3) void k_probe_rowstats(ProbeParams p) {
                     }
                 }
             }
+            if (more) stage_store(cur ^ 1, nraw);
+            __syncthreads();
         }
-        // merge the 16 lanes that hold the same rows (different keys)
+        if (active) {
+            // merge the 16 lanes that hold the same rows (different keys)
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
+            for (int off = 1; off < 16; off <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const double m2 = __shfl_xor(m[i], off), l2 = __shfl_xor(l[i], off);
-                const double M = fmax(m[i], m2);
-                double L = 0.0;
-                if (m[i] != -INFINITY) L += l[i] * exp2_f64(m[i] - M);
-                if (m2 != -INFINITY) L += l2 * exp2_f64(m2 - M);
-                m[i] = M;
-                l[i] = L;
+                for (int i = 0; i < 4; ++i) {
+                    const double m2 = __shfl_xor(m[i], off), l2 = __shfl_xor(l[i], off);
+                    const double M = fmax(m[i], m2);
+                    double L = 0.0;
+                    if (m[i] != -INFINITY) L += l[i] * exp2_f64(m[i] - M);
+                    if (m2 != -INFINITY) L += l2 * exp2_f64(m2 - M);
+                    m[i] = M;
+                    l[i] = L;
+                }
             }
-        }
-        if (li == 0) {
-            double2* dst = p.part + ((size_t)bg * p.nchunk + chunk) * p.NR + rt * 16 + kq;
+            if (li == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[4 * i] = make_double2(m[i], l[i]);
+                for (int i = 0; i < 4; ++i) part[rt * 16 + kq + 4 * i] = make_double2(m[i], l[i]);
+            }
         }
     }
 }
@@ -229,27 +273,59 @@ __global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
     }
 }
 
-// Pass 2: per (64-key block, g, b), column sums of the normalised softmax;
-// at most 128 VGPRs, so four waves share a SIMD.
+// Pass 2: per (256-key block, g, b), column sums of the normalised softmax.
+// Each of the 16 waves holds 16 keys in fp64; the probe rows stream through
+// LDS 16 at a time, converted to fp64 once per workgroup (double-buffered,
+// the next tile's raw values loaded while this one is computed).
+__device__ inline double4_t mfma_dot128_lda(const double* arow, const double* b) {
+    double4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < 32; s += 2) {
+        const double2 aa = *reinterpret_cast<const double2*>(arow + s);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(aa.x, b[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(aa.y, b[s + 1], acc, 0, 0, 0);
+        if ((s & 7) == 6) asm volatile("" ::: "memory");  // bound the LDS reads in flight
+    }
+    return acc;
+}
+constexpr int kColKeys = 16 * kPW;  // keys per pass-2 workgroup
 template <bool F16>
-__global__ __launch_bounds__(256, 4) void k_probe_colsum(ProbeParams p) {
+__global__ __launch_bounds__(1024) void k_probe_colsum(ProbeParams p) {
+    __shared__ __align__(16) double qt[2][16][kKRow];
     __shared__ double2 rs[512];
     __shared__ int rpos[512];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int T = p.seq_lens[b];
     const int bg = b * p.Hkv + g;
     const int li = lane & 15, kq = lane >> 4;
-    const int key = blk * 64 + wave * 16 + li;
-    if (blk * 64 >= T) {
-        if (threadIdx.x < 64 && blk * 64 + threadIdx.x < p.Tmax)
-            p.col_scores[(size_t)bg * p.Tmax + blk * 64 + threadIdx.x] = 0.0f;
+    const int key = blk * kColKeys + wave * 16 + li;
+    if (blk * kColKeys >= T) {
+        if (tid < kColKeys && blk * kColKeys + tid < p.Tmax)
+            p.col_scores[(size_t)bg * p.Tmax + blk * kColKeys + tid] = 0.0f;
         return;
     }
-    for (int row = threadIdx.x; row < p.NR; row += 256) {
+    // staging: thread t < 256 moves 8 channels (16 bytes) of probe row t / 16 of a tile
+    const int srow = (tid >> 4) & 15, sc0 = (tid & 15) * 8;
+    auto stage_load = [&](int rt) {
+        return tid < 256 ? *reinterpret_cast<const uint4*>(qrow(p, b, g, rt * 16 + srow) + sc0) : make_uint4(0, 0, 0, 0);
+    };
+    auto stage_store = [&](int buf, const uint4& raw) {
+        if (tid < 256) {
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+            double* dst = &qt[buf][srow][sc0];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<double2*>(dst + 2 * j) =
+                    make_double2((double)h16_to_f32<F16>(w[j] & 0xFFFFu), (double)h16_to_f32<F16>(w[j] >> 16));
+        }
+    };
+    for (int row = tid; row < p.NR; row += 1024) {
         rs[row] = p.rows[(size_t)bg * p.NR + row];
         rpos[row] = row_pos(p, T, row);
     }
+    stage_store(0, stage_load(0));
     __syncthreads();
     const bool kok = key < T;
     double bv[32];
@@ -257,9 +333,10 @@ __global__ __launch_bounds__(256, 4) void k_probe_colsum(ProbeParams p) {
     double colacc = 0.0;
     const int nrt = p.NR / 16;
     for (int rt = 0; rt < nrt; ++rt) {
-        double a[32];
-        load32_f64<F16>(qrow(p, b, g, rt * 16 + li) + 32 * kq, true, a);
-        const double4_t acc = mfma_dot128(a, bv);
+        const int cur = rt & 1;
+        const bool more = rt + 1 < nrt;
+        const uint4 nraw = more ? stage_load(rt + 1) : make_uint4(0, 0, 0, 0);
+        const double4_t acc = mfma_dot128_lda(&qt[cur][li][32 * kq], bv);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = rt * 16 + 4 * i + kq;
@@ -269,6 +346,8 @@ __global__ __launch_bounds__(256, 4) void k_probe_colsum(ProbeParams p) {
                 colacc += exp2_f64(acc[i] * p.sc2 - st.x) * st.y;
             }
         }
+        if (more) stage_store(cur ^ 1, nraw);
+        __syncthreads();
     }
     colacc += __shfl_xor(colacc, 16);
     colacc += __shfl_xor(colacc, 32);
@@ -453,15 +532,15 @@ hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_l
     p.nchunk = (Tmax + kKeyChunk - 1) / kKeyChunk;
     p.sc2 = (double)sm_scale * 1.4426950408889634074;
     dim3 g1(p.nchunk, Hkv, B);
-    if (f16) k_probe_rowstats<true><<<g1, 256, 0, s>>>(p);
-    else k_probe_rowstats<false><<<g1, 256, 0, s>>>(p);
+    if (f16) k_probe_rowstats<true><<<g1, 1024, 0, s>>>(p);
+    else k_probe_rowstats<false><<<g1, 1024, 0, s>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_probe_rowfinal<<<dim3(Hkv, B), 256, 0, s>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dim3 g2((Tmax + 63) / 64, Hkv, B);
-    if (f16) k_probe_colsum<true><<<g2, 256, 0, s>>>(p);
-    else k_probe_colsum<false><<<g2, 256, 0, s>>>(p);
+    dim3 g2((Tmax + kColKeys - 1) / kColKeys, Hkv, B);
+    if (f16) k_probe_colsum<true><<<g2, 1024, 0, s>>>(p);
+    else k_probe_colsum<false><<<g2, 1024, 0, s>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     k_topk_select<<<dim3(Hkv, B), 1024, 0, s>>>(col_scores, seq_lens, Hkv, Tmax, pol, sel_stride(Tmax, pol),
                                                   sel_idx, sel_count, thresh);
