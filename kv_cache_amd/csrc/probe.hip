@@ -32,7 +32,13 @@ namespace {
 
 typedef double double4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kKeyChunk = 1024;  // keys per pass-1 workgroup
+// Keys per pass-1 workgroup: 1,024, or 512 when 1,024-key chunks would give
+// fewer than 1,024 workgroups (four per CU of the chip), so that short or
+// small-batch calls still spread over every CU. A multiple of 16.
+inline int probe_key_chunk(int32_t B, int32_t Hkv, int32_t Tmax) {
+    const int64_t wg = (int64_t)((Tmax + 1023) / 1024) * Hkv * B;
+    return wg >= 1024 ? 1024 : 512;
+}
 
 // 2^x in fp64 (x finite or very negative): 2^n * e^(f ln2), |f| <= 1/2,
 // Taylor series to degree 14 (truncation < 1e-17 relative).
@@ -120,7 +126,7 @@ struct ProbeParams {
     double2* part;         // [B][Hkv][nchunk][NR] (m, l) per key chunk: l = sum of 2^(x - m), m a reference
     double2* rows;         // [B][Hkv][NR] (M, 1/L) over all chunks, M = the largest chunk reference
     float* col_scores;     // [B][Hkv][Tmax]
-    int32_t B, Hq, Hkv, Tmax, R, G, NR, nchunk;
+    int32_t B, Hq, Hkv, Tmax, R, G, NR, nchunk, chunk;  // chunk: keys per pass-1 workgroup
     double sc2;            // sm_scale * log2(e)
 };
 
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(1024) void k_probe_rowstats(ProbeParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int T = p.seq_lens[b];
-    const int key_lo = chunk * kKeyChunk;
+    const int key_lo = chunk * p.chunk;
     const int bg = b * p.Hkv + g;
     const int li = lane & 15, kq = lane >> 4;
     const uint16_t* kbase = p.k + (size_t)bg * p.Tmax * kD;
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(1024) void k_probe_rowstats(ProbeParams p) {
         for (int r = tid; r < p.NR; r += 1024) part[r] = make_double2(-INFINITY, 0.0);
         return;
     }
-    const int key_hi = min(key_lo + kKeyChunk, T);
+    const int key_hi = min(key_lo + p.chunk, T);
     const int ntile = (key_hi - key_lo + 15) / 16;
     // staging: thread t < 256 moves 8 channels (16 bytes) of key t / 16 of a tile
     const int srow = (tid >> 4) & 15, sc0 = (tid & 15) * 8;
@@ -260,7 +266,7 @@ __global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
     const int g = blockIdx.x, b = blockIdx.y;
     const int bg = b * p.Hkv + g;
     const int T = p.seq_lens[b];
-    const int nch = (T + kKeyChunk - 1) / kKeyChunk;
+    const int nch = (T + p.chunk - 1) / p.chunk;
     for (int row = threadIdx.x; row < p.NR; row += 256) {
         double M = -INFINITY;
         for (int c = 0; c < nch; ++c) M = fmax(M, p.part[((size_t)bg * p.nchunk + c) * p.NR + row].x);
@@ -493,7 +499,8 @@ inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 ProbeWs probe_ws(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_policy& pol) {
     const int G = Hq / Hkv;
     const size_t NR = (size_t)G * pol.probe_rows;
-    const size_t nchunk = (Tmax + kKeyChunk - 1) / kKeyChunk;
+    const int kc = probe_key_chunk(B, Hkv, Tmax);
+    const size_t nchunk = (Tmax + kc - 1) / kc;
     ProbeWs w;
     w.part = 0;
     w.rows = al((size_t)B * Hkv * nchunk * NR * 16);
@@ -529,7 +536,8 @@ hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_l
     p.R = pol.probe_rows;
     p.G = G;
     p.NR = NR;
-    p.nchunk = (Tmax + kKeyChunk - 1) / kKeyChunk;
+    p.chunk = probe_key_chunk(B, Hkv, Tmax);
+    p.nchunk = (Tmax + p.chunk - 1) / p.chunk;
     p.sc2 = (double)sm_scale * 1.4426950408889634074;
     dim3 g1(p.nchunk, Hkv, B);
     if (f16) k_probe_rowstats<true><<<g1, 1024, 0, s>>>(p);
