@@ -41,24 +41,18 @@ inline int probe_key_chunk(int32_t B, int32_t Hkv, int32_t Tmax) {
 }
 
 // 2^x in fp64 (x finite or very negative): 2^n * e^(f ln2), |f| <= 1/2,
-// Taylor series to degree 14 (truncation < 1e-17 relative).
-__device__ inline double exp2_f64(double x) {
+// Taylor series to degree 14 (truncation < 1e-17 relative). The coefficients
+// 1/14! .. 1/2! come in the kernel arguments (c): uniform values in scalar
+// registers that the FMAs read directly (as literals the compiler keeps them
+// in vector registers and copies one into place before every FMA).
+constexpr int kExpCoefs = 13;
+__device__ inline double exp2_f64(double x, const double (&c)[kExpCoefs]) {
     if (x < -1000.0) return 0.0;
     const double n = rint(x);
     const double y = (x - n) * 0.69314718055994530942;
-    double e = 1.0 / 87178291200.0;  // 1/14!
-    e = fma(e, y, 1.0 / 6227020800.0);
-    e = fma(e, y, 1.0 / 479001600.0);
-    e = fma(e, y, 1.0 / 39916800.0);
-    e = fma(e, y, 1.0 / 3628800.0);
-    e = fma(e, y, 1.0 / 362880.0);
-    e = fma(e, y, 1.0 / 40320.0);
-    e = fma(e, y, 1.0 / 5040.0);
-    e = fma(e, y, 1.0 / 720.0);
-    e = fma(e, y, 1.0 / 120.0);
-    e = fma(e, y, 1.0 / 24.0);
-    e = fma(e, y, 1.0 / 6.0);
-    e = fma(e, y, 0.5);
+    double e = c[0];
+#pragma unroll
+    for (int i = 1; i < kExpCoefs; ++i) e = fma(e, y, c[i]);
     e = fma(e, y, 1.0);
     e = fma(e, y, 1.0);
     return ldexp(e, (int)n);
@@ -128,6 +122,7 @@ struct ProbeParams {
     float* col_scores;     // [B][Hkv][Tmax]
     int32_t B, Hq, Hkv, Tmax, R, G, NR, nchunk, chunk;  // chunk: keys per pass-1 workgroup
     double sc2;            // sm_scale * log2(e)
+    double ec[kExpCoefs];  // 1/14!, 1/13!, ..., 1/2!: the exp2_f64 series
 };
 
 __device__ inline const uint16_t* qrow(const ProbeParams& p, int b, int g, int row) {
@@ -227,10 +222,10 @@ __global__ __launch_bounds__(1024) void k_probe_rowstats(ProbeParams p) {
                     if (kok && pos[i] >= 0 && key <= pos[i]) {
                         const double x = acc[i] * p.sc2;
                         if (x > m[i] + 512.0) {
-                            l[i] = l[i] * exp2_f64(m[i] - x);
+                            l[i] = l[i] * exp2_f64(m[i] - x, p.ec);
                             m[i] = x;
                         }
-                        l[i] += exp2_f64(x - m[i]);
+                        l[i] += exp2_f64(x - m[i], p.ec);
                     }
                 }
             }
@@ -246,8 +241,8 @@ __global__ __launch_bounds__(1024) void k_probe_rowstats(ProbeParams p) {
                     const double m2 = __shfl_xor(m[i], off), l2 = __shfl_xor(l[i], off);
                     const double M = fmax(m[i], m2);
                     double L = 0.0;
-                    if (m[i] != -INFINITY) L += l[i] * exp2_f64(m[i] - M);
-                    if (m2 != -INFINITY) L += l2 * exp2_f64(m2 - M);
+                    if (m[i] != -INFINITY) L += l[i] * exp2_f64(m[i] - M, p.ec);
+                    if (m2 != -INFINITY) L += l2 * exp2_f64(m2 - M, p.ec);
                     m[i] = M;
                     l[i] = L;
                 }
@@ -273,7 +268,7 @@ __global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
         double L = 0.0;
         for (int c = 0; c < nch; ++c) {
             const double2 v = p.part[((size_t)bg * p.nchunk + c) * p.NR + row];
-            if (v.x != -INFINITY) L += v.y * exp2_f64(v.x - M);
+            if (v.x != -INFINITY) L += v.y * exp2_f64(v.x - M, p.ec);
         }
         p.rows[(size_t)bg * p.NR + row] = make_double2(M, L > 0.0 ? 1.0 / L : 0.0);
     }
@@ -349,7 +344,7 @@ __global__ __launch_bounds__(1024) void k_probe_colsum(ProbeParams p) {
             const int pr = rpos[row];
             if (kok && pr >= 0 && key <= pr) {
                 const double2 st = rs[row];
-                colacc += exp2_f64(acc[i] * p.sc2 - st.x) * st.y;
+                colacc += exp2_f64(acc[i] * p.sc2 - st.x, p.ec) * st.y;
             }
         }
         if (more) stage_store(cur ^ 1, nraw);
@@ -539,6 +534,14 @@ hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_l
     p.chunk = probe_key_chunk(B, Hkv, Tmax);
     p.nchunk = (Tmax + p.chunk - 1) / p.chunk;
     p.sc2 = (double)sm_scale * 1.4426950408889634074;
+    {
+        double f = 1.0;  // 14! .. 2!
+        for (int k = 2; k <= 14; ++k) f *= k;
+        for (int i = 0; i < kExpCoefs; ++i) {
+            p.ec[i] = 1.0 / f;
+            f /= 14 - i;
+        }
+    }
     dim3 g1(p.nchunk, Hkv, B);
     if (f16) k_probe_rowstats<true><<<g1, 1024, 0, s>>>(p);
     else k_probe_rowstats<false><<<g1, 1024, 0, s>>>(p);
