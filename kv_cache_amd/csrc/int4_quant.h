@@ -7,7 +7,8 @@
 //   mn, mx over the group; d = mx - mn (exact in fp32 for 16-bit inputs);
 //   s = fp16_rne(fp32 d / 15)   (IEEE correctly rounded fp32 divide);
 //   z = fp16_rne(mn);
-//   code = clamp(rint_even(fp32(x - z) / s), 0, 15), or 0 when s == 0.
+//   code = clamp(rint_even(fp32(x - z) / s), 0, 15), or 0 when s == 0
+//   (the quotient correctly rounded, as an IEEE fp32 divide gives it).
 // Packed canonically: byte i = code[2i] | code[2i+1] << 4.
 #pragma once
 
@@ -35,13 +36,25 @@ __device__ inline void int4_quant_group(const float (&x)[kGroup], uint32_t (&pac
     const float z = (float)z16;
     s_bits = (uint32_t)__builtin_bit_cast(uint16_t, s16);
     z_bits = (uint32_t)__builtin_bit_cast(uint16_t, z16);
+    // diff / s, correctly rounded, without a full divide per element: y is
+    // the correctly rounded reciprocal (one IEEE divide per group), q0 = diff * y
+    // is within a few ulps, one FMA residual step makes it faithful, and by
+    // Markstein's theorem (faithful quotient, reciprocal within half an ulp,
+    // exact FMA residual) a second step gives the correctly rounded quotient.
+    // An infinite diff (z rounded to -inf in fp16) keeps diff * y, whose sign
+    // and infinity are those of the quotient; s = 0, inf or NaN end as code 0
+    // on both forms.
+    const float y = 1.0f / s;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         uint32_t word = 0;
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
             const float diff = x[8 * w + n] - z;
-            const float qv = diff / s;
+            const float q0 = diff * y;
+            const float q1 = fmaf(fmaf(-q0, s, diff), y, q0);
+            const float q2 = fmaf(fmaf(-q1, s, diff), y, q1);
+            const float qv = __builtin_isfinite(q0) ? q2 : q0;
             float c = rintf(qv);
             c = fminf(fmaxf(c, 0.0f), 15.0f);
             const uint32_t code = (s > 0.0f) ? (uint32_t)c : 0u;

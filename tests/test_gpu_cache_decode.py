@@ -136,6 +136,67 @@ def test_quantize_and_decode(name):
                 assert_attn_close(out[b, h * G:(h + 1) * G], ex, f"{name} exact-attention special case")
 
 
+def _tie_groups(inp, seed):
+    """Overwrite K and V with 32-channel groups whose INT4 quotients
+    (x - z) / s land exactly on half-integers k + 0.5 (round half to even
+    decides the code) or next to them. Each group has minimum 0 or -c (c a
+    multiple of the step) and maximum 15 * u, u = m * 2^e exact in fp16; the
+    other 30 values are (k + 1/2) * u (exact ties where the 16-bit type holds
+    them) or one 16-bit step away from it. About one group in eight takes u
+    scaled by 1.1, so s is d / 15 rounded to fp16, the quotients land near the
+    ties but not on them, and the fp32 quotient rounding decides."""
+    from synth import bf16_bits_from_f32, f16_bits_from_f32
+    sp = inp.spec
+    rng = np.random.default_rng(seed)
+    conv = bf16_bits_from_f32 if sp.dtype == "bf16" else f16_bits_from_f32
+    for arr in (inp.k, inp.v):
+        shape = arr.shape[:-1] + (arr.shape[-1] // 32, 32)
+        n = int(np.prod(shape[:-1]))
+        m = rng.choice([1, 3, 5, 7, 9, 11, 13, 17], size=n).astype(np.float64)
+        e = rng.integers(-12, 3, size=n).astype(np.float64)
+        u = m * 2.0 ** e
+        u = np.where(rng.random(n) < 0.125, u * 1.1, u)
+        k = rng.integers(0, 15, size=(n, 30)).astype(np.float64)
+        vals = (k + 0.5) * u[:, None]
+        g = np.concatenate([np.zeros((n, 1)), 15.0 * u[:, None], vals], axis=1)
+        off = np.where(rng.random(n) < 0.25, -rng.integers(1, 4, size=n) * u, 0.0)
+        g = g + off[:, None]
+        for row in g:
+            rng.shuffle(row)
+        bits = conv(g.astype(np.float32)).reshape(shape)
+        # one group value in four moved one 16-bit step up or down
+        step = rng.integers(-1, 2, size=bits.shape) * (rng.random(bits.shape) < 0.25)
+        moved = (bits.astype(np.int32) + step).astype(np.uint16)
+        # (zeros stay: a subnormal next to a large maximum would make the
+        # group range inexact in fp32, outside the quantizer's domain)
+        ok = (np.isfinite(O.to_f64(moved.reshape(arr.shape), sp.dtype)).reshape(bits.shape)
+              & (O.to_f64(bits.reshape(arr.shape), sp.dtype).reshape(bits.shape) != 0))
+        bits = np.where(ok, moved, bits)
+        arr[...] = bits.reshape(arr.shape)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_quantize_half_integer_quotients(dtype):
+    """INT4 codes bit-exact with the oracle where the quotient (x - z) / s is
+    at or next to a half-integer: the kernel's quotient has to be the
+    correctly rounded fp32 one (a quotient one ulp off flips such a code)."""
+    inp = small_decode_inputs(B=2, Hq=4, Hkv=2, T=900, dtype=dtype, seed=24)
+    _tie_groups(inp, 2424)
+    print(f"case half-integer quotients {dtype}", flush=True)
+    cache, scores, sels = _run_quantize(inp, 0, (0, 100))
+    ocaches = oracle_caches(inp, sels, scores, 0)
+    _check_cache(cache, inp, ocaches)
+    # the inputs do put many quotients exactly on a tie
+    oc = ocaches[0][0]
+    x = O.to_f64(inp.k[0, 0, :oc.T], dtype).reshape(oc.T, -1, 32)
+    s = oc.k_s.astype(np.float32)[..., None]
+    z = oc.k_z.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        qq = (x.astype(np.float32) - z) / s
+    ties = np.count_nonzero((s > 0) & (qq - np.floor(qq) == 0.5))
+    assert ties > 1000, ties
+
+
 def test_quantize_flags_invalid_selection():
     """A selected-position list that is not strictly ascending is reported in
     the cache's error flag (bit 2); the entries before the bad one are still
