@@ -93,9 +93,11 @@ __device__ inline float block_max256(float v, float* red) {
 
 #pragma clang fp contract(off)
 // Symmetric INT8 of one 64 x 128 block (rows beyond T are zero); 256 threads,
-// thread t owns row t/4, channels 32*(t%4) .. +31.
-template <bool F16>
-__device__ inline void quant_block_i8(const uint16_t* src, int rows_valid, int8_t* dst, float* scale) {
+// thread t owns row t/4, channels 32*(t%4) .. +31. RECIP: quotients from the
+// reciprocal and FMA residual steps (fewer instructions, more registers: the
+// Q kernel gains, the K/V kernel, which also writes V^T, runs slower with it).
+template <bool F16, bool RECIP>
+__device__ __attribute__((always_inline)) inline void quant_block_i8(const uint16_t* src, int rows_valid, int8_t* dst, float* scale) {
     __shared__ float red[4];
     const int t = threadIdx.x, r = t >> 2, c0 = (t & 3) * 32;
     float x[32];
@@ -121,16 +123,34 @@ __device__ inline void quant_block_i8(const uint16_t* src, int rows_valid, int8_
     am = block_max256(am, red);
     const float s = am / 127.0f;
     uint32_t packed[8];
+    auto pack = [&](auto quot) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t w = 0;
+        for (int i = 0; i < 8; ++i) {
+            uint32_t w = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float c = 0.f;
-            if (s > 0.f) c = fminf(fmaxf(rintf(x[4 * i + j] / s), -127.f), 127.f);
-            w |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * j);
+            for (int j = 0; j < 4; ++j) {
+                float c = 0.f;
+                if (s > 0.f) c = fminf(fmaxf(rintf(quot(x[4 * i + j])), -127.f), 127.f);
+                w |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * j);
+            }
+            packed[i] = w;
         }
-        packed[i] = w;
+    };
+    // x / s correctly rounded without a divide per element: y = RN(1/s), then
+    // q0 = x * y and two FMA residual steps; by Markstein's theorem the second
+    // step gives RN(x / s) once the first has made the quotient faithful. The
+    // scale is uniform over the block; tiny, huge or non-finite scales (where
+    // a residual could underflow or the reciprocal overflow) take the IEEE
+    // divide.
+    if (RECIP && s >= 0x1p-100f && s < 0x1p100f) {
+        const float y = 1.0f / s;
+        pack([&](float v) {
+            const float q0 = v * y;
+            const float q1 = fmaf(fmaf(-q0, s, v), y, q0);
+            return fmaf(fmaf(-q1, s, v), y, q1);
+        });
+    } else {
+        pack([&](float v) { return v / s; });
     }
     uint4* d4 = reinterpret_cast<uint4*>(dst + (size_t)r * kD + c0);
     d4[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
@@ -172,7 +192,7 @@ __global__ __launch_bounds__(256) void k_pf_quant_q(PfParams p) {
     const size_t Tp = (size_t)p.nblk * kBN;
     const uint16_t* src = p.q + (((size_t)b * p.Hq + h) * p.T + (size_t)blk * kBN) * kD;
     int8_t* dst = p.q8 + (((size_t)b * p.Hq + h) * Tp + (size_t)blk * kBN) * kD;
-    quant_block_i8<F16>(src, min(kBN, p.T - blk * kBN), dst, p.sq + ((size_t)b * p.Hq + h) * p.nblk + blk);
+    quant_block_i8<F16, true>(src, min(kBN, p.T - blk * kBN), dst, p.sq + ((size_t)b * p.Hq + h) * p.nblk + blk);
 }
 
 // K8 + sK, V^T in fp16, and the selected-column mask of one key block.
@@ -184,7 +204,7 @@ __global__ __launch_bounds__(256) void k_pf_quant_kv(PfParams p) {
     const size_t Tp = (size_t)p.nblk * kBN;
     const int rows = min(kBN, p.T - blk * kBN);
     const uint16_t* ksrc = p.k + ((size_t)bg * p.T + (size_t)blk * kBN) * kD;
-    quant_block_i8<F16>(ksrc, rows, p.k8 + ((size_t)bg * Tp + (size_t)blk * kBN) * kD, p.sk + (size_t)bg * p.nblk + blk);
+    quant_block_i8<F16, false>(ksrc, rows, p.k8 + ((size_t)bg * Tp + (size_t)blk * kBN) * kD, p.sk + (size_t)bg * p.nblk + blk);
     // V -> fp16 -> transposed
     const int t = threadIdx.x, r = t >> 2, c0 = (t & 3) * 32;
     const uint16_t* vsrc = p.v + ((size_t)bg * p.T + (size_t)blk * kBN) * kD;
