@@ -32,9 +32,12 @@
  *   - All device pointers must be 16-byte aligned. Outputs must not alias
  *     inputs.
  *   - Every argument is validated on the host before anything is launched.
- *     On error nothing is enqueued, no output is written, the call returns a
- *     negative status and hq_last_error() describes the problem. A failed
- *     kernel launch returns HQ_ERR_HIP with the HIP error string.
+ *     On a validation error nothing is enqueued, no output is written, the
+ *     call returns a negative status and hq_last_error() describes the
+ *     problem. A failed kernel launch returns HQ_ERR_HIP with the HIP error
+ *     string; calls that launch several kernels in sequence (probe, decode,
+ *     prefill) may then leave the kernels launched before the failing one
+ *     enqueued, so their outputs are undefined after HQ_ERR_HIP.
  *   - The library's only global state is a per-device cache of the compute
  *     unit count (read once with hipDeviceGetAttribute). It is safe to call
  *     from several threads (each thread has its own hq_last_error buffer).
@@ -101,6 +104,8 @@ int32_t hq_sel_stride(int32_t T, const hq_policy* policy);
  * Logits are formed exactly (fp64 accumulation of the exact products);
  * softmax normalisers and column sums accumulate in fp64; scores are
  * returned as fp32.
+ * Supported shapes: (Hq/Hkv) * probe_rows must be a multiple of 16 and at
+ * most 512; other shapes return HQ_ERR_UNSUPPORTED before any launch.
  *   q_probe   [B][Hq][probe_rows][D] dt  row r is position T_b - probe_rows + r
  *   k         [B][Hkv][Tmax][D]      dt
  *   seq_lens  [B] int32, 1 <= T_b <= Tmax
@@ -168,7 +173,12 @@ typedef struct {
     int32_t* counts;    /* [B][Hkv][4]: seq_len, n_q, n_keep, probe_len       */
     float* col_scores;  /* [B][Hkv][cap_probe] probe scores kept for append   */
     hq_thresh* thresh;  /* [B][Hkv]                                           */
-    int32_t* err_flag;  /* [1]: set nonzero by a kernel on capacity overflow  */
+    int32_t* err_flag;  /* [1]: bits set by kernels, never cleared by them:
+                           1 quantize: a count or length out of range (that
+                             (b, g) is left unwritten); 2 append: a store full
+                             (nothing stored); 4 quantize: selected positions
+                             not ascending candidates (the entries before the
+                             first bad one are stored)                      */
 } hq_cache;
 
 typedef struct {
@@ -178,7 +188,16 @@ typedef struct {
 } hq_cache_sizes;
 
 /* Byte sizes of every cache buffer for contexts of up to cap_tokens tokens
- * (prompt plus appends) whose probe covered at most cap_probe positions.   */
+ * (prompt plus appends) whose probe covered at most cap_probe positions.
+ *   cap_q    = round64(cap_tokens - min(window, cap_tokens)), at least 64:
+ *              every position outside the window may be quantized (a short
+ *              sequence of a ragged batch keeps few columns and may be
+ *              appended up to cap_tokens, so the top-k is not subtracted);
+ *   cap_keep = round64(k(cap_probe) + min(window, cap_probe)): the selected
+ *              columns plus the departures the append rule may keep, which
+ *              were window positions when the probe ran.
+ * cap_tokens above 2^24 returns HQ_ERR_CAPACITY (one (b, g)'s INT4 store is
+ * addressed with 32-bit byte offsets).                                     */
 hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens,
                           int32_t cap_probe, hq_dtype dt, const hq_policy* policy,
                           hq_cache_sizes* out);
@@ -199,12 +218,20 @@ hq_status hq_quantize_kv(const void* k, const void* v, const int32_t* seq_lens, 
 
 /* ------------------------------------------------------------------------
  * hq_append_kv -- append one token per (b, g) at position T = seq_len.
+ * Pages: "HyQuant: ...", flowchart (the recent local sliding window stays in
+ * high precision next to the vertical-line columns; the rest is low-bit);
+ * "How HyQuant uses ...", "What hybrid-precision attention changes" (during
+ * decode the cache keeps the selected positions in high precision and the
+ * rest in low bit width). The pages do not say what happens to a token that
+ * slides out of the window. Reading: it is treated as the selection would
+ * have treated it.
  * The new token enters the ring. The token leaving the window, d = T - W
  * (when T >= W), goes to the kept store if it was probed (d < probe_len) and
  * its probe score ranks above the k-th selected candidate (it would have been
- * selected had it been a candidate), and is INT4-quantized otherwise.
- * Reading of "tokens leaving the window are quantized unless selected".
- *   k_new, v_new [B][Hkv][D] cache->dt                                      */
+ * selected had it been a candidate), and is INT4-quantized otherwise; tokens
+ * generated after the probe are always quantized when they leave.
+ *   k_new, v_new [B][Hkv][D] cache->dt
+ * A capacity overflow sets bit 1 of cache->err_flag and stores nothing.    */
 hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_new, void* stream);
 
 /* ------------------------------------------------------------------------
@@ -224,10 +251,9 @@ hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_n
  * ceil(tiles / 54) splits, raised until the grid fills whole rounds of the
  * current device's workgroup slots (2 per CU; eight heads per KV head run
  * as two four-head workgroups per split), with
- * at least 8 tiles per split. A positive integer in the environment variable
- * HQ_DECODE_TPS fixes the tiles per split instead. The workspace query and
- * the call compute it alike (same device, same environment). The result does
- * not depend on it beyond fp32 rounding. */
+ * at least 8 tiles per split. The workspace query and the call compute it
+ * alike for the current device. The result does not depend on it beyond
+ * fp32 rounding. */
 hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,
                          void* out, hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
 size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq);

@@ -56,7 +56,7 @@ class hq_cache_sizes(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing; build it with `python -m kv_cache_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing; build it with `python kv_cache_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F, S, V = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
     pol = ctypes.POINTER(hq_policy)

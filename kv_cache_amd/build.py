@@ -1,6 +1,7 @@
 """Build libhyquant.so (HIP for gfx950) in-tree.
 
-    python -m kv_cache_amd.build          # compile every csrc/*.hip and link
+    python kv_cache_amd/build.py          # compile every csrc/*.hip and link (run as a
+                                          # script: importing the package needs the library)
 
 Objects go to kv_cache_amd/_build/, the library to kv_cache_amd/libhyquant.so.
 Every HIP source is compiled with packed-fp32 instructions disabled

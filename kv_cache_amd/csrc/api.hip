@@ -68,8 +68,11 @@ hq_status check_cache(const char* fn, const hq_cache* c) {
         return fail(HQ_ERR_INVALID_ARG, "%s: cache window %d must be a multiple of 64", fn, c->window);
     if (c->cap_q < hq::kTile || c->cap_q % hq::kTile || c->cap_keep < hq::kTile || c->cap_keep % hq::kTile)
         return fail(HQ_ERR_INVALID_ARG, "%s: cache capacities must be positive multiples of 64", fn);
-    if (c->cap_probe < 1 || c->cap_probe > c->cap_q)
-        return fail(HQ_ERR_INVALID_ARG, "%s: cap_probe %d must be in [1, cap_q]", fn, c->cap_probe);
+    if (c->cap_q > hq::kMaxCapTokens || c->cap_keep > hq::kMaxCapTokens)
+        return fail(HQ_ERR_CAPACITY, "%s: cache capacities %d / %d exceed %d slots (32-bit byte offsets)", fn,
+                    c->cap_q, c->cap_keep, hq::kMaxCapTokens);
+    if (c->cap_probe < 1 || c->cap_probe > c->cap_q + c->window)
+        return fail(HQ_ERR_INVALID_ARG, "%s: cap_probe %d must be in [1, cap_q + window]", fn, c->cap_probe);
     REQ_PTR(c->k_codes);
     REQ_PTR(c->v_codes);
     REQ_PTR(c->k_meta);
@@ -113,9 +116,6 @@ int32_t device_cus() {
 // (two per CU): a partial last round leaves CUs idle at the end of the
 // kernel. At least 8 tiles (two per wave) per split.
 int32_t decode_tps(const hq_cache& c, int32_t G) {
-    const char* s = std::getenv("HQ_DECODE_TPS");
-    const int v = s ? std::atoi(s) : 0;
-    if (v > 0) return v;
     const int32_t tiles = c.cap_q / hq::kTile;
     if (tiles < 1) return 54;
     const int32_t base = (tiles + 53) / 54;
@@ -151,13 +151,22 @@ hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens,
     if (B < 1 || Hkv < 1) return fail(HQ_ERR_INVALID_ARG, "%s: B and Hkv must be >= 1", fn);
     if (D != hq::kD) return fail(HQ_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (only 128)", fn, D);
     if ((st = check_dt(fn, dt))) return st;
-    if (cap_tokens < 1 || cap_tokens > (1 << 26))
-        return fail(HQ_ERR_INVALID_ARG, "%s: cap_tokens %d out of range", fn, cap_tokens);
+    if (cap_tokens < 1) return fail(HQ_ERR_INVALID_ARG, "%s: cap_tokens %d out of range", fn, cap_tokens);
+    if (cap_tokens > hq::kMaxCapTokens)
+        return fail(HQ_ERR_CAPACITY, "%s: cap_tokens %d exceeds %d (32-bit byte offsets of the INT4 store)", fn,
+                    cap_tokens, hq::kMaxCapTokens);
     if (cap_probe < 1 || cap_probe > cap_tokens)
         return fail(HQ_ERR_INVALID_ARG, "%s: cap_probe %d must be in [1, cap_tokens]", fn, cap_probe);
     const int32_t kmax = hq::keep_count(cap_probe, *policy);
     const int32_t w = policy->window < cap_probe ? policy->window : cap_probe;
-    out->cap_q = hq::round_up(cap_tokens, hq::kTile);
+    // INT4 store: every token outside the window can land there. The top-k
+    // count is not subtracted: a shorter sequence of a ragged batch keeps
+    // fewer columns and may be appended up to cap_tokens.
+    const int32_t wq = policy->window < cap_tokens ? policy->window : cap_tokens;
+    out->cap_q = std::max(hq::kTile, hq::round_up(cap_tokens - wq, hq::kTile));
+    // kept store: the k selected columns plus, during appends, departures
+    // flagged by the probe scores; those were window positions at probe
+    // time, so at most w of them.
     int32_t ck = hq::round_up(kmax + w, hq::kTile);
     out->cap_keep = ck < hq::kTile ? hq::kTile : ck;
     out->cap_probe = cap_probe;
@@ -177,6 +186,7 @@ hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens,
 
 size_t hq_probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32_t D, const hq_policy* policy) {
     if (!policy || B < 1 || Hq < 1 || Hkv < 1 || Tmax < 1 || D != hq::kD || Hq % Hkv) return 0;
+    if (!hq::probe_shape_supported(Hq / Hkv, policy->probe_rows)) return 0;
     return hq::probe_ws_bytes(B, Hq, Hkv, Tmax, *policy);
 }
 
@@ -192,6 +202,9 @@ hq_status hq_probe_select(const void* q_probe, const void* k, const int32_t* seq
     if ((st = check_dt(fn, dt))) return st;
     if (Tmax < 1 || Tmax > (1 << 24)) return fail(HQ_ERR_INVALID_ARG, "%s: Tmax %d out of range", fn, Tmax);
     if (!(sm_scale > 0.0f) || sm_scale > 1e6f) return fail(HQ_ERR_INVALID_ARG, "%s: sm_scale must be positive", fn);
+    if (!hq::probe_shape_supported(Hq / Hkv, policy->probe_rows))
+        return fail(HQ_ERR_UNSUPPORTED, "%s: %s (query heads per KV head %d, probe_rows %d)", fn,
+                    hq::probe_shape_rule(), Hq / Hkv, policy->probe_rows);
     REQ_PTR(q_probe);
     REQ_PTR(k);
     REQ_PTR(seq_lens);
@@ -205,7 +218,6 @@ hq_status hq_probe_select(const void* q_probe, const void* k, const int32_t* seq
         return fail(HQ_ERR_CAPACITY, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
     hipError_t e = hq::launch_probe(q_probe, k, seq_lens, B, Hq, Hkv, Tmax, dt == HQ_F16, *policy, sm_scale,
                                     col_scores, sel_idx, sel_count, thresh, ws, (hipStream_t)stream);
-    if (e == hipErrorNotSupported) return fail(HQ_ERR_UNSUPPORTED, "%s: not available in this build", fn);
     return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
 }
 
@@ -219,7 +231,7 @@ hq_status hq_quantize_kv(const void* k, const void* v, const int32_t* seq_lens, 
     if ((st = check_cache(fn, cache))) return st;
     if (policy->window != cache->window)
         return fail(HQ_ERR_INVALID_ARG, "%s: policy window %d != cache window %d", fn, policy->window, cache->window);
-    if (Tmax < 1 || Tmax > cache->cap_probe || Tmax > cache->cap_q)
+    if (Tmax < 1 || Tmax > cache->cap_probe)
         return fail(HQ_ERR_CAPACITY, "%s: Tmax %d exceeds the cache capacity (cap_probe %d)", fn, Tmax,
                     cache->cap_probe);
     if (hq::keep_count(Tmax, *policy) > cache->cap_keep)
@@ -313,7 +325,6 @@ hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B
         return fail(HQ_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
     hipError_t e = hq::launch_prefill(q, k, v, B, Hq, Hkv, T, dt == HQ_F16, *policy, sel_idx, sel_count,
                                       hq::sel_stride(T, *policy), sm_scale, out, out_dt, ws, (hipStream_t)stream);
-    if (e == hipErrorNotSupported) return fail(HQ_ERR_UNSUPPORTED, "%s: not available in this build", fn);
     return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
 }
 

@@ -725,11 +725,8 @@ __global__ __launch_bounds__(256, G <= 4 ? 2 : 1) void k_decode_split(DecodePara
         split_body<G, F16, 1, NT>(p, sm, x - p.nsq, half);
 }
 
-// Rearranges the query for the split kernel: per head a power-of-two scale
-// 2^k into fp16 range (q' = q 2^k, exact for every value above 2^-24 of the
-// head's maximum), the QK A operands (row 4j + h of K-step ks holds q'_h on
-// group ks when j == ks, zero otherwise), the per-group sums of q' and of
-// q' * bias, and the natural 16-bit pairs for the 16-bit tiles.
+// Cross-split merge: out[b][h] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
+// with M = max_s m_s, over the partials of every split of the (b, g).
 __global__ __launch_bounds__(128) void k_decode_reduce(const hq_cache c, const float* __restrict__ part_m,
                                                        const float* __restrict__ part_l,
                                                        const float* __restrict__ part_o, int nsplit, int G, int Hq,
@@ -814,10 +811,6 @@ int32_t decode_nsq(const hq_cache& c, int32_t tps) { return (c.cap_q / kTile + t
 int32_t decode_nsplit(const hq_cache& c, int32_t tps) {
     return decode_nsq(c, tps) + (c.cap_keep / kTile + c.window / kTile + kTps16 - 1) / kTps16;
 }
-
-namespace {
-
-}  // namespace
 
 size_t decode_ws_bytes(const hq_cache& c, int32_t Hq, int32_t nsplit) {
     return ws_layout(c, Hq, nsplit).total;

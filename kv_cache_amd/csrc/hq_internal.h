@@ -34,6 +34,9 @@ __device__ inline void st_nt(void* ptr, const uint4& v) {
     __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(ptr));
 }
 constexpr int kInt8Block = 64;   // prefill INT8 block (tokens)
+// Largest cache capacity in slots: the decode kernel addresses one (b, g)'s
+// INT4 codes (64 bytes per slot) with 32-bit buffer offsets.
+constexpr int32_t kMaxCapTokens = 1 << 24;
 
 // ---------------------------------------------------------------------------
 // INT4 tile layouts (per (b, g), tile of 64 slots). The decode kernel feeds
@@ -166,6 +169,10 @@ int32_t decode_nsq(const hq_cache& c, int32_t tps);  // INT4 splits of a (b, g)
 size_t diag_sink_bytes(const hq_cache& c, int32_t tps);
 hipError_t launch_diag_read_int4(const hq_cache& c, void* sink, int32_t tps, hipStream_t s);
 
+// Shapes the probe kernels support: G query heads per KV head times
+// probe_rows rows. probe_shape_rule() states the rule for error messages.
+bool probe_shape_supported(int32_t G, int32_t probe_rows);
+const char* probe_shape_rule();
 hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_lens, int32_t B,
                         int32_t Hq, int32_t Hkv, int32_t Tmax, bool f16, const hq_policy& pol,
                         float sm_scale, float* col_scores, int32_t* sel_idx, int32_t* sel_count,

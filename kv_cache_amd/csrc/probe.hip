@@ -505,6 +505,14 @@ ProbeWs probe_ws(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_poli
 
 }  // namespace
 
+bool probe_shape_supported(int32_t G, int32_t probe_rows) {
+    const int64_t NR = (int64_t)G * probe_rows;
+    return NR % 16 == 0 && NR <= 512;
+}
+const char* probe_shape_rule() {
+    return "query heads per KV head x probe_rows must be a multiple of 16 and at most 512";
+}
+
 size_t probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_policy& pol) {
     return probe_ws(B, Hq, Hkv, Tmax, pol).total;
 }
@@ -514,8 +522,7 @@ hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_l
                         float* col_scores, int32_t* sel_idx, int32_t* sel_count, hq_thresh* thresh, void* ws,
                         hipStream_t s) {
     const int G = Hq / Hkv;
-    const int NR = G * pol.probe_rows;
-    if (NR % 16 != 0 || NR > 512) return hipErrorNotSupported;
+    const int NR = G * pol.probe_rows;  // probe_shape_supported(G, probe_rows) holds (host check)
     const ProbeWs w = probe_ws(B, Hq, Hkv, Tmax, pol);
     ProbeParams p;
     p.q = static_cast<const uint16_t*>(q_probe);

@@ -73,11 +73,11 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
 
     if (tile < qt) {
         // ---------------- INT4 tile
+        // the probe scores of positions tile*64 + 64*qt*r + lane (cap_probe
+        // may exceed cap_q by up to the window)
         if (tid < kTile) {
-            const int j = tile * kTile + tid;
-            if (j < p.c.cap_probe)
-                p.c.col_scores[(size_t)bg * p.c.cap_probe + j] =
-                    j < T ? p.col_scores[(size_t)bg * p.Tmax + j] : 0.0f;
+            for (int j = tile * kTile + tid; j < p.c.cap_probe; j += qt * kTile)
+                p.c.col_scores[(size_t)bg * p.c.cap_probe + j] = j < T ? p.col_scores[(size_t)bg * p.Tmax + j] : 0.0f;
         }
         const int t = tid >> 2, grp = tid & 3;
         const int n = tile * kTile + t;

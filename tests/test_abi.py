@@ -53,14 +53,21 @@ def test_cache_layout_closed_form(hq):
     sz = hq.hq_cache_sizes()
     assert hq.lib.hq_cache_layout(16, 8, 128, 32768, 32768, hq.HQ_BF16, ctypes.byref(pol.c()), ctypes.byref(sz)) == 0
     BG = 16 * 8
-    assert sz.cap_q == 32768
-    assert sz.cap_keep == 1792                     # round64(1638 + 128)
-    assert sz.k_codes == BG * 32768 * 64           # 64 B of K codes per token
-    assert sz.k_meta == BG * 32768 * 16            # 4 groups x (fp16 s, fp16 z)
+    assert sz.cap_q == 32768 - 128                 # every position outside the window
+    assert sz.cap_keep == 1792                     # round64(1638 + 128): selected + flagged departures
+    assert sz.k_codes == BG * sz.cap_q * 64        # 64 B of K codes per token
+    assert sz.k_meta == BG * sz.cap_q * 16         # 4 groups x (fp16 s, fp16 z)
     assert sz.k_win == BG * 128 * 256
     # per-token traffic of the decode kernel: 160 B quantized, 512 B 16-bit
-    assert (sz.k_codes + sz.v_codes + sz.k_meta + sz.v_meta) // (BG * 32768) == 160
+    assert (sz.k_codes + sz.v_codes + sz.k_meta + sz.v_meta) // (BG * sz.cap_q) == 160
     assert (sz.k_keep + sz.v_keep) // (BG * 1792) == 512
+    # a context shorter than the window: the INT4 store keeps its minimum tile
+    assert hq.lib.hq_cache_layout(1, 1, 128, 100, 100, hq.HQ_BF16, ctypes.byref(pol.c()), ctypes.byref(sz)) == 0
+    assert sz.cap_q == 64 and sz.cap_keep == 128
+    # capacities are bounded by the 32-bit byte offsets of the INT4 store
+    assert hq.lib.hq_cache_layout(1, 1, 128, (1 << 24) + 1, 1000, hq.HQ_BF16, ctypes.byref(pol.c()),
+                                  ctypes.byref(sz)) == hq.HQ_ERR_CAPACITY
+    assert "2^24" in hq.lib.hq_last_error().decode() or "16777216" in hq.lib.hq_last_error().decode()
 
 
 def test_sel_stride(hq):
@@ -102,6 +109,13 @@ def test_probe_validation(hq):
     assert _probe(hq, Tmax=0) == hq.HQ_ERR_INVALID_ARG
     assert _probe(hq, wsb=16) == hq.HQ_ERR_CAPACITY                      # workspace too small
     assert "workspace" in hq.lib.hq_last_error().decode()
+    # probe shapes: G x probe_rows a multiple of 16, at most 512
+    assert _probe(hq, pol=hq.hq_policy(5, 100, 128, 10)) == hq.HQ_ERR_UNSUPPORTED   # 4 x 10 = 40
+    assert "multiple of 16" in hq.lib.hq_last_error().decode()
+    assert _probe(hq, Hq=8, pol=hq.hq_policy(5, 100, 128, 128)) == hq.HQ_ERR_UNSUPPORTED   # 8 x 128 = 1024
+    assert "at most 512" in hq.lib.hq_last_error().decode()
+    assert hq.lib.hq_probe_ws_bytes(1, 4, 1, 256, 128, ctypes.byref(hq.hq_policy(5, 100, 128, 10))) == 0
+    assert _probe(hq, pol=hq.hq_policy(5, 100, 128, 4), wsb=16) == hq.HQ_ERR_CAPACITY  # 4 x 4 = 16 is accepted
 
 
 def _cache(hq, **kw):
@@ -123,7 +137,8 @@ def test_cache_validation(hq):
     for bad, code in [(dict(D=64), hq.HQ_ERR_UNSUPPORTED), (dict(k_codes=0), hq.HQ_ERR_INVALID_ARG),
                       (dict(v_meta=0x100008), hq.HQ_ERR_INVALID_ARG), (dict(cap_q=100), hq.HQ_ERR_INVALID_ARG),
                       (dict(window=100), hq.HQ_ERR_INVALID_ARG), (dict(dt=hq.HQ_F32), hq.HQ_ERR_UNSUPPORTED),
-                      (dict(cap_probe=5000), hq.HQ_ERR_INVALID_ARG)]:
+                      (dict(cap_probe=5000), hq.HQ_ERR_INVALID_ARG),
+                      (dict(cap_q=1 << 25), hq.HQ_ERR_CAPACITY), (dict(cap_keep=1 << 25), hq.HQ_ERR_CAPACITY)]:
         c = _cache(hq, **bad)
         assert hq.lib.hq_decode_attn(ctypes.byref(c), q, 4, 0.088, FAKE, hq.HQ_F32, ws, 1 << 30, None) == code, bad
         assert hq.lib.hq_append_kv(ctypes.byref(c), FAKE, FAKE, None) == code, bad
