@@ -313,6 +313,39 @@ def append_token(cache: HybridCache, k_new: np.ndarray, v_new: np.ndarray) -> Hy
                        cache.tau, cache.j_k)
 
 
+def append_tokens(cache: HybridCache, k_rows: np.ndarray, v_rows: np.ndarray) -> HybridCache:
+    """s consecutive appends (O6) in one pass: the same cache as s calls of
+    append_token with the rows in order.
+
+    Every position that has left the window after the s steps (d < T + s - W)
+    and was still in it is decided by the same rule as in append_token; the
+    rule depends only on d's probe score and the threshold, never on the
+    order in which departures happen, so deciding them together is the same.
+    k_rows, v_rows: [s][D].
+    """
+    T, W = cache.T, cache.window
+    D = cache.k.shape[-1]
+    s = k_rows.shape[0]
+    k = np.vstack([cache.k, k_rows.reshape(s, D)])
+    v = np.vstack([cache.v, v_rows.reshape(s, D)])
+    mode = np.concatenate([cache.mode, np.full(s, MODE_WINDOW)]).astype(np.int8)
+    grow = lambda a: np.concatenate([a, np.zeros((s,) + a.shape[1:], dtype=a.dtype)])
+    kc, vc = grow(cache.k_codes), grow(cache.v_codes)
+    ks, kz, vs, vz = (grow(a) for a in (cache.k_s, cache.k_z, cache.v_s, cache.v_z))
+    T1 = T + s
+    left = np.nonzero((mode == MODE_WINDOW) & (np.arange(T1) < T1 - W))[0]
+    keep = np.array([d < cache.T0 and ranks_above(float(cache.col_scores[d]), int(d), cache.tau, cache.j_k)
+                     for d in left], dtype=bool)
+    mode[left[keep]] = MODE_KEPT
+    q = left[~keep]
+    mode[q] = MODE_INT4
+    if len(q):
+        kc[q], ks[q], kz[q] = int4_quantize(k[q])
+        vc[q], vs[q], vz[q] = int4_quantize(v[q])
+    return HybridCache(k, v, mode, kc, vc, ks, kz, vs, vz, W, cache.T0, cache.col_scores,
+                       cache.tau, cache.j_k)
+
+
 def storage_ratio_vs_int4(T: int, window: int, k: int) -> float:
     """Non-window bits per element relative to strict 4-bit storage.
 

@@ -237,3 +237,95 @@ def test_prefill_int8_score_error_bound():
     s_q, s_k = float(sq[0]), float(sk[0])
     bound = (s_k / 2) * np.abs(q).sum(1)[:, None] + (s_q / 2) * np.abs(k).sum(1)[None, :] + 3 * D * s_q * s_k / 4
     assert np.all(np.abs(exact - low) <= bound + 1e-12)
+
+
+# ---------------------------------------------------------------- batched appends and batch drivers
+
+
+def test_append_tokens_equals_one_at_a_time():
+    """append_tokens(s rows) is the same cache as s calls of append_token,
+    field by field, including departures that are kept (score above tau),
+    ties with tau and tokens that were never probed."""
+    T, D, W = 300, 128, 64
+    k, v = _kv(31, T + 90)
+    cache, sel, c = _cache(k[:T], v[:T], T, W, 5, 100, seed=3)
+    c = c.copy()
+    c[T - W + 2] = 2.0                       # ranks above every candidate: kept
+    c[T - W + 9] = sel.tau                   # a tie with tau: kept iff its index < j_k
+    cache = O.build_cache(k[:T], v[:T], T, sel, W, c)
+    one = cache
+    for i in range(90):
+        one = O.append_token(one, k[T + i], v[T + i])
+    many = O.append_tokens(cache, k[T:T + 90], v[T:T + 90])
+    for f in ("k", "v", "mode", "k_codes", "v_codes"):
+        assert np.array_equal(getattr(one, f), getattr(many, f)), f
+    for f in ("k_s", "k_z", "v_s", "v_z"):
+        assert np.array_equal(getattr(one, f).view(np.uint16), getattr(many, f).view(np.uint16)), f
+    assert one.mode[T - W + 2] == O.MODE_KEPT
+    assert one.mode[T + 5] == O.MODE_INT4    # generated after the probe, left the window: quantized
+    # two batches in a row equal one batch
+    two = O.append_tokens(O.append_tokens(cache, k[T:T + 40], v[T:T + 40]), k[T + 40:T + 90], v[T + 40:T + 90])
+    assert np.array_equal(two.mode, many.mode) and np.array_equal(two.k_codes, many.k_codes)
+
+
+def test_decode_batch_gqa_map_closed_form():
+    """decode_batch maps query head h to KV head h // G. With every V row of
+    (b, g) equal to the constant 2 + g + 4b (exact in fp16, so its INT4
+    group has scale 0 and dequantizes exactly), the softmax-weighted average
+    is that constant whatever the logits: out[b][h] = 2 + h // G + 4b (up to
+    the rounding of the fp64 weighted sum). The
+    other map, h % Hkv, gives a different value for every h with
+    h // G != h % Hkv."""
+    B, Hkv, G, D, W = 2, 3, 2, 64, 64
+    lens = [150, 97]
+    rng = np.random.default_rng(9)
+    q = _bf16(rng.standard_normal((B, Hkv * G, D)))
+    caches = []
+    for b in range(B):
+        row = []
+        for g in range(Hkv):
+            T = lens[b]
+            k = _bf16(rng.standard_normal((T, D)))
+            v = np.full((T, D), 2.0 + g + 4 * b)
+            c = rng.random(T)
+            row.append(O.build_cache(k, v, T, O.select_topk(c, T, W, 5, 100), W, c))
+        caches.append(row)
+    out = O.decode_batch(q, caches, 0.125)
+    for b in range(B):
+        for h in range(Hkv * G):
+            assert np.allclose(out[b, h], 2.0 + h // G + 4 * b, rtol=1e-13, atol=0), (b, h)
+    assert any(h // G != h % Hkv for h in range(Hkv * G))
+
+
+def test_probe_select_batch_gqa_map_and_ragged_lengths():
+    """probe_select_batch: (i) per (b, g) the scores have length T_b and sum
+    to G * min(R, T_b) (each of the G heads' rows is a distribution over the
+    keys before it); (ii) keys at positions >= T_b do not matter; (iii) the
+    query heads of group g are heads gG..gG+G-1: heads of group g point along
+    a direction u_g, and KV head g holds a strong key along u_{g'} at
+    position 20 + 7g' for every g', so group g's top column is 20 + 7g."""
+    B, Hkv, G, R, D, W = 2, 3, 2, 16, 64, 64
+    lens = np.array([300, 211])
+    Tmax = 320
+    rng = np.random.default_rng(17)
+    u = np.linalg.qr(rng.standard_normal((D, Hkv)))[0].T * 8.0     # orthogonal directions, |u| = 8
+    qp = np.empty((B, Hkv * G, R, D))
+    k = _bf16(rng.standard_normal((B, Hkv, Tmax, D)) * 0.5)
+    for h in range(Hkv * G):
+        qp[:, h] = _bf16(u[h // G] + 0.1 * rng.standard_normal((B, R, D)))
+    for g in range(Hkv):
+        for g2 in range(Hkv):
+            k[:, g, 20 + 7 * g2] = _bf16(u[g2] * 2.0)
+    scores, sels = O.probe_select_batch(qp, k, lens, 0.125, W, 5, 100)
+    k2 = k.copy()
+    for b in range(B):
+        k2[b, :, lens[b]:] = 1e3                          # beyond T_b: must be ignored
+    scores2, sels2 = O.probe_select_batch(qp, k2, lens, 0.125, W, 5, 100)
+    for b in range(B):
+        assert scores[b].shape == (Hkv, lens[b])
+        for g in range(Hkv):
+            assert abs(scores[b][g].sum() - G * min(R, lens[b])) < 1e-9
+            assert np.array_equal(scores[b][g], scores2[b][g])
+            assert int(np.argmax(scores[b][g])) == 20 + 7 * g, (b, g)
+            assert sels[b][g].k == lens[b] * 5 // 100
+            assert 20 + 7 * g in set(sels[b][g].idx.tolist())
