@@ -78,8 +78,25 @@ def attn_errors(gpu: np.ndarray, ref: np.ndarray):
     return float(np.abs(diff).max()), float(np.linalg.norm(diff) / np.linalg.norm(ref))
 
 
-def assert_attn_close(gpu, ref, what=""):
+def v_scale(caches):
+    """sigma_V = max(1, RMS of the dequantized V values seen by attention)
+    over a list of oracle caches: the unit in which the max-abs bar is read
+    (R20: the kernels' arithmetic errors are proportional to the magnitude of
+    V, so the 2e-3 bar, stated for unit-scale values, scales with it)."""
+    ss, n = 0.0, 0
+    for c in caches:
+        _, vh = O.cache_kv_hat(c)
+        ss += float((vh * vh).sum())
+        n += vh.size
+    return max(1.0, math.sqrt(ss / max(n, 1)))
+
+
+def assert_attn_close(gpu, ref, what="", vscale=1.0):
+    """max-abs <= ATOL * vscale and rel-L2 <= RTOL_L2; vscale = 1 for
+    unit-scale V (every workload), sigma_V of v_scale() otherwise. Prints the
+    unscaled errors."""
     mx, rl2 = attn_errors(gpu, ref)
-    print(f"{what}: max-abs {mx:.3e} rel-L2 {rl2:.3e}", flush=True)
-    assert mx <= ATOL and rl2 <= RTOL_L2, (what, mx, rl2)
+    print(f"{what}: max-abs {mx:.3e} (bar {ATOL * vscale:.3e}, sigma_V {vscale:.2f}, max|o| "
+          f"{float(np.abs(ref).max()):.2f}) rel-L2 {rl2:.3e}", flush=True)
+    assert mx <= ATOL * vscale and rl2 <= RTOL_L2, (what, mx, rl2, vscale)
     return mx, rl2

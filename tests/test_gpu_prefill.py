@@ -208,11 +208,14 @@ def test_prefill_deterministic():
     assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.slow
-def test_prefill_16k_sampled():
+def test_prefill_16k_full_size():
     """The 16K causal prefill workload (B=1, 32 query / 8 KV heads), launched
-    as the benchmark launches it: the INT8 stage bit-exact for the sampled
-    heads and every K head, sampled output rows against the oracle."""
+    as the benchmark launches it: the INT8 stage bit-exact for every Q and K
+    head, and 1,024 rows of every head against the oracle: the last 64 rows,
+    runs of 64 rows across the first window / block boundaries and the
+    middle block boundary, and 13 runs at seeded random offsets (not aligned
+    to the 64-row blocks)."""
+    import time
     import torch
     import kv_cache_amd as hq
     spec = CONFIGS["c4_prefill_8b_16k"]
@@ -228,17 +231,76 @@ def test_prefill_16k_sampled():
     del q, k, col, sel, cnt, thr
     print("prefill 16k: attention", flush=True)
     out, ws = run_prefill(inp, sels, pol)
-    heads = [0, 5, 13, 31]
-    check_int8_stage(inp, ws, heads=heads)
+    check_int8_stage(inp, ws)
+    print("prefill 16k: INT8 stage bit-exact on all heads", flush=True)
     out = out.cpu().numpy()
     rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 129, 255, 4095, 8191, T - 129, T - 128, T - 1],
-                                     rng.integers(0, T, size=12)]))
+    starts = [T - 64, 96, 8160] + sorted(int(x) for x in rng.integers(0, T - 64, size=13))
     qf, kf, vf = (O.to_f64(x, spec.dtype) for x in (inp.q, inp.k, inp.v))
     sm = 1 / math.sqrt(D)
-    for h in heads:
+    t0 = time.time()
+    k8s = [O.int8_block_quantize(kf[0, g]) for g in range(spec.Hkv)]
+    refs = np.zeros((spec.Hq, len(starts) * 64, D))
+    rows = np.concatenate([np.arange(r0, r0 + 64) for r0 in starts])
+    for h in range(spec.Hq):
         g = h // G
-        k8, sk = O.int8_block_quantize(kf[0, g])
+        k8, sk = k8s[g]
         q8, sq = O.int8_block_quantize(qf[0, h])
-        ref = O.prefill_attention_rows(qf[0, h], kf[0, g], vf[0, g], sels[0][g], 128, sm, q8, sq, k8, sk, rows)
-        assert_attn_close(out[0, h, rows], ref, f"16k head {h}")
+        for n, r0 in enumerate(starts):
+            refs[h, 64 * n:64 * (n + 1)] = O.prefill_attention_block(qf[0, h], kf[0, g], vf[0, g], sels[0][g], 128,
+                                                                     sm, q8, sq, k8, sk, r0, r0 + 64)
+        if h % 8 == 7:
+            print(f"  heads 0..{h} computed ({time.time() - t0:.0f} s)", flush=True)
+    assert_attn_close(out[0][:, rows], refs, f"16k prefill, {len(rows)} rows x {spec.Hq} heads")
+
+
+def _q_tie_blocks(inp):
+    """Q blocks whose INT8 quotients x / s land exactly on half-integers or
+    one bf16 step beside them, with block scales on both sides of the bounds
+    [2^-100, 2^100) at which the Q quantizer switches from the reciprocal and
+    FMA residual quotient to the IEEE divide. A block's maximum is 127 * u
+    (s = u exactly) and its other values (k + 1/2) * u, k in 0..126."""
+    from synth import bf16_bits_from_f32
+    rng = np.random.default_rng(2024)
+    q = inp.q
+    B, Hq, T, _ = q.shape
+    us = [2.0 ** -100, 2.0 ** -101, 2.0 ** 99, 2.0 ** 100, 1.1 * 2.0 ** -100, 1.1 * 2.0 ** 99, 2.0 ** -3, 1.0]
+    for h in range(Hq):
+        for blk in range(T // 64):
+            u = us[(blk + h) % len(us)]
+            k = rng.integers(0, 127, size=(64, D)).astype(np.float64)
+            x = (k + 0.5) * u * np.where(rng.random((64, D)) < 0.5, -1.0, 1.0)
+            x[rng.integers(0, 64), rng.integers(0, D)] = 127.0 * u
+            bits = bf16_bits_from_f32(x.astype(np.float32))
+            step = rng.integers(-1, 2, size=bits.shape) * (rng.random(bits.shape) < 0.25)
+            bits = np.where(np.abs(x) == 127.0 * u, bits, (bits.astype(np.int32) + step).astype(np.uint16))
+            q[0, h, 64 * blk:64 * (blk + 1)] = bits
+
+
+def test_prefill_int8_q_half_integer_quotients():
+    """The INT8 Q stage where x / s sits on or next to k + 1/2, with scales
+    just inside and just outside [2^-100, 2^100): Q8 and sQ bit-exact with
+    the oracle (the codes round half to even on the correctly rounded fp32
+    quotient). The softmax scale 2^-120 keeps the attention finite for the
+    2^100-scale rows; only the INT8 stage is compared."""
+    import kv_cache_amd as hq
+    spec = PrefillSpec(name="qties", B=1, Hq=4, Hkv=1, T=512, seed=321)
+    inp = make_prefill_inputs(spec)
+    _q_tie_blocks(inp)
+    qf = O.to_f64(inp.q, "bf16")
+    q8, sq = O.int8_block_quantize(qf[0, 0])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quo = qf[0, 0].astype(np.float32) / np.repeat(sq, 64)[:, None]
+    assert np.count_nonzero(np.abs(quo - np.trunc(quo)) == 0.5) > 10000
+    pol = hq.Policy()
+    sels = oracle_sel(inp, 128, (5, 100))
+    import torch
+    stride = hq.sel_stride(spec.T, pol)
+    idx, cnt = sel_device(sels, 1, 1, stride)
+    q, k, v = (to_dev(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    n = hq.lib.hq_prefill_ws_bytes(1, 4, 1, spec.T, D, __import__("ctypes").byref(pol.c()))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    out = hq.prefill_attn(q, k, v, idx, cnt, pol, sm_scale=2.0 ** -120, ws=ws)
+    torch.cuda.synchronize()
+    assert np.isfinite(out.cpu().numpy()).all()
+    check_int8_stage(inp, ws)
