@@ -3,35 +3,49 @@
 MI355X.
 
 One step = one pass of every row of the hot path over one batch of seeded
-synthetic input:
+synthetic input, in the order a server runs them:
   decode workload (8B GQA shape: B=16, 32 Q / 8 KV heads, D=128, T=32768):
-    probe + top-k select -> quantize/pack -> append one token -> decode
-    (split-K + cross-split reduce);
+    the prompt once (probe + top-k select -> quantize/pack), then 16 decode
+    tokens on that cache, each one append + one decode (split-K + cross-split
+    reduce) with its own query;
   prefill workload (32 Q / 8 KV heads, causal, T=16384):
     probe + select on the last 64 rows -> INT8 block quantization + hybrid
-    attention (skipped if the prefill operator is not built).
+    attention.
 Inputs are resident in HBM before timing starts. Every kernel call is
 bracketed by HIP events on the stream it is launched on (torch's current
-stream); `value` is the decode attention time per step (hq_decode_attn) in
-microseconds; the other rows are reported beside it.
+stream). `value` is the steady-state decode attention time (hq_decode_attn,
+the 2nd..16th decode of each step) in microseconds; the first decode after
+the cache build is reported as decode_us_full_step; the once-per-prompt rows
+(probe, quantize, prefill) are reported beside it. After the timed steps the
+other decode workloads (1-head 4K warm and cold, 128K with 64 appends, the
+ragged 70B-like shape) and the 1K..32K context sweep are timed the same way
+and reported under "workloads" and "sweep".
 
 Prints ONE JSON line: the decode time and bandwidth, the prefill time and
-TFLOP/s, a roofline object for each, and the oracle's CPU timings.
+TFLOP/s, a roofline object for each, the other decode workloads and the
+context-length sweep, and the oracle's CPU timings.
 """
 from __future__ import annotations
 
-import argparse
-import json
-import math
 import os
-import platform
-import sys
-import time
+
+# The oracle's CPU baseline: BLAS / OpenMP threads are fixed before numpy is
+# first imported (a value already set in the environment is kept).
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(os.cpu_count() or 1))
+
+import argparse  # noqa: E402
+import json  # noqa: E402
+import math  # noqa: E402
+import platform  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+N_DECODE = 16  # decode tokens per step on the cache the step's prompt built
 MFMA_BF16_TFLOPS = 2500.0
 MFMA_I8_TOPS = 5000.0
 MFMA_F64_TFLOPS = 78.6
@@ -44,8 +58,10 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other decode workloads and the context sweep after the timed steps")
     ap.add_argument("--decode-only", action="store_true",
-                    help="time only append+decode per step (profiling aid)")
+                    help="time only the decode tokens (append + decode) on one built cache (profiling aid)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill probe + attention per step and print its fields (profiling aid)")
     ap.add_argument("--sweep", action="store_true",
@@ -176,18 +192,37 @@ def prefill_traffic():
     return committed_traffic("prefill_8b_16k_traffic.md", "prefill.hip", "prefill_hip_sha256")
 
 
-def cpu_baseline(inp, sels_gpu, budget_s=20.0):
-    """The oracle (numpy fp64) timed on this host on a bounded sample of the
-    decode workload: whole (b, g) units of one decode step, scaled to the
-    full step."""
+def _host_info():
+    """CPU model and memory of this host (for the CPU baseline's record)."""
+    model, mem = platform.processor() or platform.machine(), None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+        for ln in open("/proc/meminfo"):
+            if ln.startswith("MemTotal"):
+                mem = f"{int(ln.split()[1]) / 2**20:.0f} GiB"
+                break
+    except OSError:
+        pass
+    return {"cpu": model, "logical_cpus": os.cpu_count(), "memory": mem}
+
+
+def cpu_baseline(inp, sels_gpu, q, budget_s=15.0):
+    """The oracle (numpy fp64) timed on this host for the unit the GPU's
+    `value` times: one decode step's attention over an already built hybrid
+    cache (all (b, g) of the 32K decode workload). Caches are built for
+    whole (b, g) units until the time budget is spent (the build is timed as
+    its own field, the once-per-prompt cost); the decode of those units is
+    timed and scaled to all units."""
     import numpy as np
     import oracle as O
     sp = inp.spec
     sm = 1 / math.sqrt(sp.D)
     G = sp.Hq // sp.Hkv
     col, sel, cnt, thr = sels_gpu
-    t_units = []
-    n = 0
+    t_build, t_dec = [], []
     start = time.perf_counter()
     for b in range(sp.B):
         for g in range(sp.Hkv):
@@ -200,16 +235,20 @@ def cpu_baseline(inp, sels_gpu, budget_s=20.0):
             idx = sel[b, g, : cnt[b, g]].astype(np.int64)
             c = O.build_cache(k, v, T, O.Selection(idx, len(idx), float(thr[b, g, 0:1].view(np.float32)[0]),
                                                    int(thr[b, g, 1])), 128, col[b, g, :T].astype(np.float64))
-            O.decode_attention(O.to_f64(inp.q[b, g * G:(g + 1) * G], sp.dtype), c, sm)
-            t_units.append(time.perf_counter() - t0)
-            n += 1
-    per_unit = sum(t_units) / len(t_units)
-    full_us = per_unit * sp.B * sp.Hkv * 1e6
-    return {"value": round(full_us, 1), "unit": "us/step", "cores": _cpu_threads(), "kind": "oracle",
-            "sample": f"{n} of {sp.B * sp.Hkv} (batch, KV head) units of one 32K decode step "
-                      f"(cache build + fp64 attention), {sum(t_units):.1f} s, scaled x{sp.B * sp.Hkv / n:.1f}",
-            "cpu": platform.processor() or platform.machine()}
-
+            t1 = time.perf_counter()
+            qg = O.to_f64(q[b, g * G:(g + 1) * G], sp.dtype)
+            O.decode_attention(qg, c, sm)
+            t2 = time.perf_counter()
+            t_build.append(t1 - t0)
+            t_dec.append(t2 - t1)
+    n, units = len(t_dec), sp.B * sp.Hkv
+    rec = {"value": round(sum(t_dec) / n * units * 1e6, 1), "unit": "us/step", "cores": _cpu_threads(),
+           "kind": "oracle",
+           "sample": f"decode attention (fp64) over the built hybrid cache of {n} of {units} (batch, KV head) "
+                     f"units of one 32K decode step ({sum(t_dec):.1f} s), scaled x{units / n:.1f}",
+           "cache_build_us_per_prompt": round(sum(t_build) / n * units * 1e6, 1)}
+    rec.update(_host_info())
+    return rec
 
 def _cpu_threads():
     """Threads the oracle's numpy BLAS actually runs with."""
@@ -269,42 +308,82 @@ def _time_decode(hq, cache, knew, vnew, q, out, steps, warmup):
     return tm
 
 
-def decode_configs(args):
-    """Append + decode on each decode workload's full shape (one built cache
-    per workload, the steps timed as in the main loop), with the achieved HBM
-    rate of the algorithmic bytes."""
+def _decode_workload(hq, name, steps, warmup, cold_mib=0):
+    """One decode workload at its full shape: probe, quantize, then `steps`
+    timed append + decode calls (after `warmup`), each decode with its own
+    query. cold_mib > 0: also time decodes that each follow a write of that
+    many MiB (the caches no longer hold the cache's bytes)."""
+    import numpy as np
     import torch
-    import kv_cache_amd as hq
     from synth.inputs import CONFIGS, make_append_tokens, make_decode_inputs
     dev = "cuda:0"
     pol = hq.Policy()
-    rows = []
-    for name in ("c1_decode_4k_1head", "c2_decode_8b_32k", "c3_decode_8b_128k_append", "c5_decode_70b_ragged_64k"):
-        spec = CONFIGS[name]
-        inp = make_decode_inputs(spec)
-        kn, vn, qn = make_append_tokens(spec, inp.outlier_channels, 1)
-        dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float16
-        k, v = _dev16(inp.k, spec.dtype, dev), _dev16(inp.v, spec.dtype, dev)
-        qp, q = _dev16(inp.q_probe, spec.dtype, dev), _dev16(qn[0], spec.dtype, dev)
-        knew, vnew = _dev16(kn[0], spec.dtype, dev), _dev16(vn[0], spec.dtype, dev)
-        lens = torch.from_numpy(inp.seq_lens).to(dev)
-        cache = hq.HybridCache(spec.B, spec.Hkv, spec.T + 64, spec.T, dt, dev, pol)
-        col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol)
-        hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
-        out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.float32, device=dev)
-        tm = _time_decode(hq, cache, knew, vnew, q, out, args.steps, args.warmup)
-        counts = cache.counts().cpu().numpy()
-        by = decode_bytes_per_step(counts)
-        dms = tm.pct("decode_attn", 1e3)[1] * 1e-3  # the median call, ms
-        rows.append({"workload": name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "T": spec.T,
-                     "decode_us_p10_p50_p90": tm.pct("decode_attn", 1e3), "append_us": round(tm.ms("append_kv") * 1e3, 2),
-                     "bytes": by, "TBps_p50": round(by / (dms * 1e-3) / 1e12, 3),
-                     "frac_of_peak_p50": round(by / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
-        print(f"# configs {name}: {rows[-1]}", file=sys.stderr, flush=True)
-        del cache, k, v, inp
-        torch.cuda.empty_cache()
-    print(json.dumps({"configs": rows, "steps": args.steps, "warmup": args.warmup}), flush=True)
+    spec = CONFIGS[name]
+    t0 = time.perf_counter()
+    inp = make_decode_inputs(spec)
+    n = steps + warmup
+    kn, vn, qn = make_append_tokens(spec, inp.outlier_channels, n)
+    k, v = _dev16(inp.k, spec.dtype, dev), _dev16(inp.v, spec.dtype, dev)
+    qp = _dev16(inp.q_probe, spec.dtype, dev)
+    knew, vnew, qd = _dev16(kn, spec.dtype, dev), _dev16(vn, spec.dtype, dev), _dev16(qn, spec.dtype, dev)
+    lens = torch.from_numpy(inp.seq_lens).to(dev)
+    dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float16
+    cache = hq.HybridCache(spec.B, spec.Hkv, spec.T + n, spec.T, dt, dev, pol)
+    col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol)
+    hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
+    keep0 = cache.counts()[..., 2].clone()
+    out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.float32, device=dev)
+    tm = Timer()
+    for i in range(n):
+        if i == warmup:
+            torch.cuda.synchronize()
+            tm.reset()
+        tm("append_kv", hq.append_kv, cache, knew[i], vnew[i])
+        tm("decode_attn", hq.decode_attn, cache, qd[i], None, out)
+    torch.cuda.synchronize()
+    counts = cache.counts().cpu().numpy()
+    by = decode_bytes_per_step(counts)
+    p = tm.pct("decode_attn", 1e3)
+    dus = p[1]  # the median call: robust to a rare slow call in a long loop of short ones
+    rec = {"B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv, "T": spec.T, "dtype": spec.dtype,
+           "decode_us": round(dus, 2), "decode_us_p10_p50_p90": p, "decode_us_mean": round(tm.ms("decode_attn") * 1e3, 2),
+           "append_us": round(tm.pct("append_kv", 1e3)[1], 2),
+           "steps": steps, "bytes": by, "TBps": round(by / (dus * 1e-6) / 1e12, 3),
+           "frac_of_peak": round(by / (dus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "kept_by_append_rule": int((cache.counts()[..., 2] - keep0).sum().item())}
+    if spec.ragged_min is not None:
+        rec["seq_lens"] = [int(x) for x in inp.seq_lens]
+    if cold_mib:
+        scrub = torch.empty(cold_mib << 20, dtype=torch.uint8, device=dev)
+        tc = Timer()
+        for i in range(steps):
+            scrub.fill_(i & 255)
+            tc("decode_attn", hq.decode_attn, cache, qd[i % n], None, out)
+        torch.cuda.synchronize()
+        rec["cold_decode_us"] = tc.pct("decode_attn", 1e3)[1]
+        rec["cold_decode_us_p10_p50_p90"] = tc.pct("decode_attn", 1e3)
+        rec["cold"] = f"each decode after a {cold_mib} MiB device write"
+        del scrub
+    print(f"# workload {name}: {rec} ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+    del cache, k, v, inp, knew, vnew, qd
+    torch.cuda.empty_cache()
+    return rec
 
+
+def decode_workloads(args):
+    """The decode workloads other than the 32K headline, each at its full
+    shape: 1-head 4K (warm, and cold after a 512 MiB write), 8B 128K with 64
+    consecutive appends, the ragged 70B-like 64K."""
+    import kv_cache_amd as hq
+    return {
+        "c1_decode_4k_1head": _decode_workload(hq, "c1_decode_4k_1head", 200, 20, cold_mib=512),
+        "c3_decode_8b_128k_append": _decode_workload(hq, "c3_decode_8b_128k_append", 64, 0),
+        "c5_decode_70b_ragged_64k": _decode_workload(hq, "c5_decode_70b_ragged_64k", max(20, args.steps), 5),
+    }
+
+
+def decode_configs(args):
+    print(json.dumps({"workloads": decode_workloads(args), "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 def decode_ablation(args):
     """Decode output error of each cache policy against the same decode on a
@@ -349,7 +428,7 @@ def decode_ablation(args):
                                   "output against the all-bf16 cache", "rows": rows}), flush=True)
 
 
-def decode_sweep(args):
+def sweep(args):
     """Decode (append + decode per step, on one built cache) on the 8B GQA
     shape at the context lengths of the pages' speed table: absolute time and
     bandwidth per length, the streaming-read rate of the same INT4 store, and
@@ -373,7 +452,7 @@ def decode_sweep(args):
         qp, q = _dev16(inp.q_probe, "bf16", dev), _dev16(qn[0], "bf16", dev)
         knew, vnew = _dev16(kn[0], "bf16", dev), _dev16(vn[0], "bf16", dev)
         lens = torch.from_numpy(inp.seq_lens).to(dev)
-        cache = hq.HybridCache(spec.B, spec.Hkv, T + 64, T, torch.bfloat16, dev, pol)
+        cache = hq.HybridCache(spec.B, spec.Hkv, T + 64 + args.steps + args.warmup, T, torch.bfloat16, dev, pol)
         col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol)
         hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
         out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.float32, device=dev)
@@ -393,7 +472,7 @@ def decode_sweep(args):
         del cache
         torch.cuda.empty_cache()
         # the same kernel with every position kept in bf16
-        cache = hq.HybridCache(spec.B, spec.Hkv, T + 64, T, torch.bfloat16, dev, pol_bf16)
+        cache = hq.HybridCache(spec.B, spec.Hkv, T + 64 + args.steps + args.warmup, T, torch.bfloat16, dev, pol_bf16)
         col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol_bf16)
         hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
         tmb = _time_decode(hq, cache, knew, vnew, q, out, args.steps, args.warmup)
@@ -431,8 +510,14 @@ def decode_sweep(args):
         prefill[f"{name}_ms_p10_p50_p90"] = tmp.pct("prefill_attn", 1.0)
     prefill["bf16_over_hybrid"] = round(prefill["bf16_ms_p10_p50_p90"][1] / prefill["hybrid_ms_p10_p50_p90"][1], 3)
     print(f"# sweep prefill: {prefill}", file=sys.stderr, flush=True)
-    print(json.dumps({"sweep": "decode_8b_gqa_b16 (B=16, 32/8 heads, bf16, top-5% + 128 window, INT4 g32)",
-                      "steps": args.steps, "warmup": args.warmup, "rows": rows, "prefill_16k": prefill}), flush=True)
+    return {"workload": "decode_8b_gqa_b16 (B=16, 32/8 heads, bf16, top-5% + 128 window, INT4 g32)",
+            "steps": args.steps, "warmup": args.warmup, "rows": rows, "prefill_16k": prefill}
+
+
+def decode_sweep(args):
+    print(json.dumps({"sweep": sweep(args)}), flush=True)
+
+
 
 
 def prefill_only(args):
@@ -498,17 +583,16 @@ def main():
     t_gen = time.perf_counter()
     spec = CONFIGS["c2_decode_8b_32k"]
     inp = make_decode_inputs(spec)
-    kn, vn, qn = make_append_tokens(spec, inp.outlier_channels, 1)
+    kn, vn, qn = make_append_tokens(spec, inp.outlier_channels, N_DECODE)
     print(f"# generated decode inputs in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     pol = hq.Policy()
     B, Hq, Hkv, T, D = spec.B, spec.Hq, spec.Hkv, spec.T, spec.D
     k = _dev16(inp.k, "bf16", dev)
     v = _dev16(inp.v, "bf16", dev)
     qp = _dev16(inp.q_probe, "bf16", dev)
-    q = _dev16(qn[0], "bf16", dev)
-    knew, vnew = _dev16(kn[0], "bf16", dev), _dev16(vn[0], "bf16", dev)
+    qd, knew, vnew = _dev16(qn, "bf16", dev), _dev16(kn, "bf16", dev), _dev16(vn, "bf16", dev)
     lens = torch.from_numpy(inp.seq_lens).to(dev)
-    cache = hq.HybridCache(B, Hkv, T + 64, T, torch.bfloat16, dev, pol)
+    cache = hq.HybridCache(B, Hkv, T + N_DECODE, T, torch.bfloat16, dev, pol)
 
     pf = None
     if not args.no_prefill and not args.decode_only:
@@ -522,32 +606,26 @@ def main():
             del pin
         else:
             pf["pin"] = pin
-        print(f"# generated prefill inputs", file=sys.stderr, flush=True)
+        print("# generated prefill inputs", file=sys.stderr, flush=True)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     tm = Timer()
-    prefill_ok = pf is not None
 
     def step():
-        nonlocal prefill_ok
         if not args.decode_only:
             col, sel, cnt, thr = tm("probe_select", hq.probe_select, qp, k, lens, pol)
             tm("quantize_kv", hq.quantize_kv, cache, k, v, lens, sel, cnt, col, thr)
-            sel4 = (col, sel, cnt, thr)
-        else:
-            sel4 = None
-        tm("append_kv", hq.append_kv, cache, knew, vnew)
-        tm("decode_attn", hq.decode_attn, cache, q, None, out)
-        if prefill_ok:
+        for i in range(N_DECODE):
+            tm("append_kv", hq.append_kv, cache, knew[i], vnew[i])
+            first = i == 0 and not args.decode_only
+            tm("decode_first" if first else "decode_attn", hq.decode_attn, cache, qd[i], None, out)
+        if pf is not None:
             psel = tm("prefill_probe_select", hq.probe_select, pf["qprobe"], pf["k"], pf["lens"], pol)
-            try:
-                tm("prefill_attn", hq.prefill_attn, pf["q"], pf["k"], pf["v"], psel[1], psel[2], pol, None, pf["out"])
-            except hq.HQError as e:
-                if e.status != hq.HQ_ERR_UNSUPPORTED:
-                    raise
-                prefill_ok = False
-        return sel4
+            tm("prefill_attn", hq.prefill_attn, pf["q"], pf["k"], pf["v"], psel[1], psel[2], pol, None, pf["out"])
 
     if args.decode_only:
+        # one built cache; the step is append + decode only (the cache grows by
+        # N_DECODE tokens per step)
+        cache = hq.HybridCache(B, Hkv, T + N_DECODE * (args.steps + args.warmup), T, torch.bfloat16, dev, pol)
         col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol)
         hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
     for _ in range(args.warmup):
@@ -560,11 +638,12 @@ def main():
     w0 = time.perf_counter()
     s0.record()
     for _ in range(args.steps):
-        sel4 = step()
+        step()
     s1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = s0.elapsed_time(s1) / args.steps
+    print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     counts = cache.counts().cpu().numpy()
     dec_ms = tm.ms("decode_attn")
@@ -581,7 +660,8 @@ def main():
         "dtype": "int4+bf16 cache, fp32 accumulate",
         "data": "synthetic (seeded; Llama-3.1-8B attention shapes, outlier K channels, planted vertical lines)",
         "config": {"workload": "decode_8b_gqa_b16_32k (+ prefill_8b_gqa_16k causal)", "B": B, "Hq": Hq,
-                   "Hkv": Hkv, "T": T, "head_dim": D, "keep": "top-5% + 128 window", "int4_group": 32},
+                   "Hkv": Hkv, "T": T, "head_dim": D, "keep": "top-5% + 128 window", "int4_group": 32,
+                   "decode_tokens_per_step": N_DECODE},
         "decode_us": round(dec_ms * 1e3, 2),
         "decode_TBps": round(dbytes / (dec_ms * 1e-3) / 1e12, 3),
         "decode_bytes": dbytes,
@@ -590,6 +670,7 @@ def main():
         "wall_s": round(wall, 3),
     }
     if not args.decode_only:
+        res["decode_us_full_step"] = round(tm.ms("decode_first") * 1e3, 2)
         res["probe_select_ms"] = round(tm.ms("probe_select"), 3)
         res["quantize_ms"] = round(tm.ms("quantize_kv"), 3)
     res["roofline"] = {"bound": "hbm", "kernel": "hq_decode_attn (split-K + reduce)",
@@ -612,7 +693,7 @@ def main():
     res["roofline"]["frac_of_achievable"] = round(res["roofline"]["achieved"] / ach, 4)
     res["int4_stream_read"] = {"bytes": int4_bytes, "us": round(tm.ms("diag_read_int4") * 1e3, 2),
                                "GBps": round(ach, 1)}
-    if prefill_ok:
+    if pf is not None:
         pms = tm.ms("prefill_attn")
         psp = pf["spec"]
         fl = prefill_flops(psp.T, psp.Hq)
@@ -623,10 +704,18 @@ def main():
         psel = hq.probe_select(pf["qprobe"], pf["k"], pf["lens"], pol)
         psel_idx, psel_cnt = psel[1].cpu().numpy(), psel[2].cpu().numpy()
         res["prefill_roofline"] = prefill_roofline(psp.T, pol.window, psel_idx, psel_cnt, psp.Hq // psp.Hkv, pms)
+    sels = tuple(t.cpu().numpy() for t in (hq.probe_select(qp, k, lens, pol)))
+    del cache, k, v, knew, vnew
+    if pf is not None:
+        for key in ("q", "k", "v", "out", "qprobe"):
+            pf.pop(key)
+    torch.cuda.empty_cache()
+    if not args.decode_only and not args.no_workloads:
+        res["workloads"] = decode_workloads(args)
+        res["sweep"] = sweep(args)
     if not args.no_cpu_baseline:
-        sels = tuple(t.cpu().numpy() for t in (hq.probe_select(qp, k, lens, pol)))
-        res["cpu_baseline"] = cpu_baseline(inp, sels)
-        if prefill_ok and "pin" in pf:
+        res["cpu_baseline"] = cpu_baseline(inp, sels, qn[1])
+        if pf is not None and "pin" in pf:
             res["cpu_baseline_prefill"] = cpu_baseline_prefill(pf["pin"], psel_idx, psel_cnt)
     print(json.dumps(res), flush=True)
 
