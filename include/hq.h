@@ -39,8 +39,9 @@
  *     prefill) may then leave the kernels launched before the failing one
  *     enqueued, so their outputs are undefined after HQ_ERR_HIP.
  *   - The library's only global state is a per-device cache of the compute
- *     unit count (read once with hipDeviceGetAttribute). It is safe to call
- *     from several threads (each thread has its own hq_last_error buffer).
+ *     unit count (read once with hipDeviceGetAttribute) and the per-device
+ *     scratch array of hq_decode_attn_noalloc. It is safe to call from
+ *     several threads (each thread has its own hq_last_error buffer).
  */
 #ifndef HQ_H_
 #define HQ_H_
@@ -257,6 +258,26 @@ hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_n
 hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,
                          void* out, hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
 size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq);
+
+/* ------------------------------------------------------------------------
+ * hq_decode_attn_noalloc -- hq_decode_attn without a workspace argument, for
+ * callers that cannot allocate device memory around the call (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, kernels and results as hq_decode_attn; the split partials
+ * go to a fixed array inside the library (HQ_DECODE_NOALLOC_SCRATCH_BYTES
+ * per device, held until the process ends) instead of `ws`. The call
+ * allocates nothing: the first call on a device looks up that device's copy
+ * of the array once (hipGetSymbolAddress).
+ * Errors as hq_decode_attn, plus HQ_ERR_CAPACITY when the cache needs more
+ * partials than the array holds (hq_decode_ws_bytes(cache, Hq) bytes must be
+ * at most HQ_DECODE_NOALLOC_SCRATCH_BYTES), checked before any launch.
+ * Every call on one device uses the same array: calls that overlap on one
+ * device (concurrent streams, or host threads without ordering) race and
+ * give undefined results. Calls on one stream are ordered and safe; nothing
+ * in the array needs to be cleared between calls. */
+#define HQ_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+hq_status hq_decode_attn_noalloc(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,
+                                 void* out, hq_dtype out_dt, void* stream);
 
 /* ------------------------------------------------------------------------
  * hq_prefill_attn -- causal hybrid-precision prefill attention.

@@ -20,7 +20,7 @@ HQ_F16, HQ_BF16, HQ_F32 = 0, 1, 2
 
 EXPORTED = (
     "hq_probe_select", "hq_probe_ws_bytes", "hq_quantize_kv", "hq_append_kv", "hq_decode_attn",
-    "hq_decode_ws_bytes", "hq_prefill_attn", "hq_prefill_ws_bytes", "hq_cache_layout", "hq_sel_stride",
+    "hq_decode_ws_bytes", "hq_decode_attn_noalloc", "hq_prefill_attn", "hq_prefill_ws_bytes", "hq_cache_layout", "hq_sel_stride",
     "hq_last_error", "hq_diag_read_int4", "hq_diag_read_int4_sink_bytes",
 )
 
@@ -67,6 +67,7 @@ def _load():
         "hq_append_kv": (I, [ctypes.POINTER(hq_cache), P, P, V]),
         "hq_decode_attn": (I, [ctypes.POINTER(hq_cache), P, I, F, P, I, P, S, V]),
         "hq_decode_ws_bytes": (S, [ctypes.POINTER(hq_cache), I]),
+        "hq_decode_attn_noalloc": (I, [ctypes.POINTER(hq_cache), P, I, F, P, I, V]),
         "hq_prefill_attn": (I, [P, P, P, I, I, I, I, I, I, pol, P, P, F, P, I, P, S, V]),
         "hq_prefill_ws_bytes": (S, [I, I, I, I, I, pol]),
         "hq_cache_layout": (I, [I, I, I, I, I, I, pol, ctypes.POINTER(hq_cache_sizes)]),
@@ -237,6 +238,19 @@ def decode_attn(cache: HybridCache, q, sm_scale: float | None = None, out=None, 
     ws = decode_ws(cache, Hq)
     _check(lib.hq_decode_attn(cache.ptr(), _ptr(q), Hq, sm, _ptr(out), _dt(out), _ptr(ws), ws.numel(),
                               _stream()))
+    return out
+
+
+def decode_attn_noalloc(cache: HybridCache, q, sm_scale: float | None = None, out=None, out_dtype=None):
+    """hq_decode_attn_noalloc: as decode_attn, with the split partials in the
+    library's static scratch array (no workspace). q [B][Hq][D]; returns out."""
+    torch = _torch()
+    _need_contig(q)
+    B, Hq, D = q.shape
+    sm = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or torch.float32, device=q.device)
+    _check(lib.hq_decode_attn_noalloc(cache.ptr(), _ptr(q), Hq, sm, _ptr(out), _dt(out), _stream()))
     return out
 
 

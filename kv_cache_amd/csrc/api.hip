@@ -267,9 +267,14 @@ size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq) {
     return hq::decode_ws_bytes(*cache, Hq, nsplit);
 }
 
-hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale, void* out,
-                         hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
-    static const char* fn = "hq_decode_attn";
+}  // extern "C"
+
+namespace {
+
+// Shared by hq_decode_attn (caller's workspace) and hq_decode_attn_noalloc
+// (ws == nullptr: the library's static scratch array).
+hq_status decode_call(const char* fn, const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,
+                      void* out, hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
     clear_err();
     hq_status st;
     if ((st = check_cache(fn, cache))) return st;
@@ -279,18 +284,48 @@ hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float
     if (!(sm_scale > 0.0f) || sm_scale > 1e6f) return fail(HQ_ERR_INVALID_ARG, "%s: sm_scale must be positive", fn);
     REQ_PTR(q);
     REQ_PTR(out);
-    REQ_PTR(ws);
+    const bool own_ws = ws != nullptr || ws_bytes != (size_t)-1;
+    if (own_ws) REQ_PTR(ws);
     hq::DecodeLaunch d;
     d.Hq = Hq;
     d.G = Hq / cache->Hkv;
     d.tiles_per_split = decode_tps(*cache, d.G);
     d.nsplit = hq::decode_nsplit(*cache, d.tiles_per_split);
     d.sm_scale_log2 = sm_scale * 1.4426950408889634f;
-    d.ws = ws;
     const size_t need = hq::decode_ws_bytes(*cache, Hq, d.nsplit);
-    if (ws_bytes < need) return fail(HQ_ERR_CAPACITY, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    if (own_ws) {
+        if (ws_bytes < need)
+            return fail(HQ_ERR_CAPACITY, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+        d.ws = ws;
+    } else {
+        if (need > hq::kDecodeScratchBytes)
+            return fail(HQ_ERR_CAPACITY, "%s: this cache needs %zu bytes of split partials, more than the %zu-byte "
+                        "static scratch holds (use hq_decode_attn with a workspace)", fn, need,
+                        hq::kDecodeScratchBytes);
+        hipError_t e = hq::decode_scratch(&d.ws);
+        if (e != hipSuccess) return fail(HQ_ERR_HIP, "%s: scratch lookup failed: %s", fn, hipGetErrorString(e));
+    }
     hipError_t e = hq::launch_decode(*cache, q, out, out_dt, d, (hipStream_t)stream);
     return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
+}
+
+}  // namespace
+
+extern "C" {
+
+hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale, void* out,
+                         hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
+    if (ws == nullptr) {
+        clear_err();
+        return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: ws is null");
+    }
+    return decode_call("hq_decode_attn", cache, q, Hq, sm_scale, out, out_dt, ws, ws_bytes, stream);
+}
+
+hq_status hq_decode_attn_noalloc(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale, void* out,
+                                 hq_dtype out_dt, void* stream) {
+    return decode_call("hq_decode_attn_noalloc", cache, q, Hq, sm_scale, out, out_dt, nullptr, (size_t)-1,
+                       stream);
 }
 
 size_t hq_prefill_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t D, const hq_policy* policy) {

@@ -42,6 +42,8 @@
 //    load of a tile issued before its first use.
 //  * Each workgroup writes one partial (m, l, o[128]) per head; a second
 //    kernel merges the splits of each (b, g).
+#include <atomic>
+
 #include "hq_internal.h"
 
 namespace hq {
@@ -810,6 +812,29 @@ void launch_split(const DecodeParams& p, int Hkv, int B, hipStream_t s) {
 int32_t decode_nsq(const hq_cache& c, int32_t tps) { return (c.cap_q / kTile + tps - 1) / tps; }
 int32_t decode_nsplit(const hq_cache& c, int32_t tps) {
     return decode_nsq(c, tps) + (c.cap_keep / kTile + c.window / kTile + kTps16 - 1) / kTps16;
+}
+
+// The fixed scratch of hq_decode_attn_noalloc (the split partials), one copy
+// per device for the life of the process. Host code never uses this name as
+// an address: each device's copy is looked up once with hipGetSymbolAddress
+// and that pointer is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** out) {
+    static std::atomic<void*> cached[64];  // per device, zero-initialised
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* p = cached[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        cached[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
 }
 
 size_t decode_ws_bytes(const hq_cache& c, int32_t Hq, int32_t nsplit) {

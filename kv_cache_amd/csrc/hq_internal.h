@@ -161,6 +161,11 @@ struct DecodeLaunch {
 hipError_t launch_decode(const hq_cache& c, const void* q, void* out, hq_dtype out_dt,
                          const DecodeLaunch& d, hipStream_t s);
 size_t decode_ws_bytes(const hq_cache& c, int32_t Hq, int32_t nsplit);
+// hq_decode_attn_noalloc: the static scratch array (HQ_DECODE_NOALLOC_SCRATCH_BYTES)
+// that replaces the workspace; *out = its address on the current device
+// (looked up once per device, never allocated).
+constexpr size_t kDecodeScratchBytes = HQ_DECODE_NOALLOC_SCRATCH_BYTES;
+hipError_t decode_scratch(void** out);
 int32_t decode_nsplit(const hq_cache& c, int32_t tps);
 int32_t decode_nsq(const hq_cache& c, int32_t tps);  // INT4 splits of a (b, g)
 

@@ -180,3 +180,34 @@ def test_layout_rejects_bad_sizes(hq):
     assert hq.lib.hq_cache_layout(1, 1, 128, 100, 200, hq.HQ_BF16, ctypes.byref(pol), ctypes.byref(sz)) == hq.HQ_ERR_INVALID_ARG
     assert hq.lib.hq_cache_layout(1, 1, 96, 100, 100, hq.HQ_BF16, ctypes.byref(pol), ctypes.byref(sz)) == hq.HQ_ERR_UNSUPPORTED
     assert hq.lib.hq_cache_layout(1, 1, 128, 100, 100, hq.HQ_BF16, ctypes.byref(pol), None) == hq.HQ_ERR_INVALID_ARG
+
+
+def test_decode_noalloc_validation(hq):
+    """hq_decode_attn_noalloc validates like hq_decode_attn on the host, and
+    rejects a cache whose split partials exceed the static scratch."""
+    c = _cache(hq)
+    q = FAKE
+    assert hq.lib.hq_decode_attn_noalloc(ctypes.byref(c), _null(), 4, 0.088, FAKE, hq.HQ_F32, None) == \
+        hq.HQ_ERR_INVALID_ARG
+    assert hq.lib.hq_decode_attn_noalloc(ctypes.byref(c), q, 6, 0.088, FAKE, hq.HQ_F32, None) == hq.HQ_ERR_UNSUPPORTED
+    assert hq.lib.hq_decode_attn_noalloc(None, q, 4, 0.088, FAKE, hq.HQ_F32, None) == hq.HQ_ERR_INVALID_ARG
+    bad = _cache(hq, k_codes=0)
+    assert hq.lib.hq_decode_attn_noalloc(ctypes.byref(bad), q, 4, 0.088, FAKE, hq.HQ_F32, None) == \
+        hq.HQ_ERR_INVALID_ARG
+    # a cache far beyond the scratch: 64 x 64 (b, g) of 1M tokens, 8 query heads each
+    sz = hq.hq_cache_sizes()
+    pol = hq.Policy()
+    assert hq.lib.hq_cache_layout(64, 64, 128, 1 << 20, 1 << 20, hq.HQ_BF16, ctypes.byref(pol.c()),
+                                  ctypes.byref(sz)) == 0
+    big = hq.hq_cache(B=64, Hkv=64, D=128, window=128, cap_q=sz.cap_q, cap_keep=sz.cap_keep, cap_probe=sz.cap_probe,
+                      dt=hq.HQ_BF16)
+    for n in hq._CACHE_PTRS:
+        setattr(big, n, 0x100000)
+    need = hq.lib.hq_decode_ws_bytes(ctypes.byref(big), 512)
+    assert need > (16 << 20)
+    assert hq.lib.hq_decode_attn_noalloc(ctypes.byref(big), q, 512, 0.088, FAKE, hq.HQ_F32, None) == \
+        hq.HQ_ERR_CAPACITY
+    assert "static scratch" in hq.lib.hq_last_error().decode()
+    # the workspace entry point still requires its workspace
+    assert hq.lib.hq_decode_attn(ctypes.byref(c), q, 4, 0.088, FAKE, hq.HQ_F32, None, 1 << 30, None) == \
+        hq.HQ_ERR_INVALID_ARG
