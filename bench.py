@@ -219,7 +219,7 @@ def cpu_baseline(inp, sels_gpu, q, budget_s=15.0):
     import numpy as np
     import oracle as O
     sp = inp.spec
-    sm = 1 / math.sqrt(sp.D)
+    sm = float(np.float32(1 / math.sqrt(sp.D)))  # the fp32 scale the library receives
     G = sp.Hq // sp.Hkv
     col, sel, cnt, thr = sels_gpu
     t_build, t_dec = [], []
@@ -270,7 +270,7 @@ def cpu_baseline_prefill(pin, sel_idx, sel_cnt, budget_s=8.0):
     import oracle as O
     sp = pin.spec
     G = sp.Hq // sp.Hkv
-    sm = 1 / math.sqrt(sp.D)
+    sm = float(np.float32(1 / math.sqrt(sp.D)))  # the fp32 scale the library receives
     rng = np.random.default_rng(0)
     t0 = time.perf_counter()
     q = O.to_f64(pin.q[0, 0], sp.dtype)

@@ -102,9 +102,13 @@ int32_t hq_sel_stride(int32_t T, const hq_policy* policy);
  *   sel_idx[b][g][0..k)  = the k candidates j in [0, T - window) with the
  *     largest score (ties: lower j first), in ascending order; k as in
  *     hq_policy. sel_count[b][g] = k; thresh[b][g] = the k-th one.
- * Logits are formed exactly (fp64 accumulation of the exact products);
- * softmax normalisers and column sums accumulate in fp64; scores are
- * returned as fp32.
+ * sm_scale is used as the fp32 value passed. Logits come from exact integer
+ * products on the int8 matrix cores (each 16-bit value written as base-256
+ * digits of a scaled integer); a per-tile a-posteriori bound on the digits
+ * left out is checked and any tile above 1.5e-7 (log2 units) is recomputed
+ * in fp64. Softmax normalisers and column sums accumulate in fp64; scores
+ * are rounded once to fp32. Each score's relative error is below 2.7e-7
+ * (with the observed bounds, ~1e-8 logit error, it is the fp32 rounding).
  * Supported shapes: (Hq/Hkv) * probe_rows must be a multiple of 16 and at
  * most 512; other shapes return HQ_ERR_UNSUPPORTED before any launch.
  *   q_probe   [B][Hq][probe_rows][D] dt  row r is position T_b - probe_rows + r

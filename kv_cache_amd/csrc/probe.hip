@@ -6,19 +6,40 @@
 // signal finds them without calibration), "Gaps" (the probe must not
 // materialise the attention map); "How HyQuant uses hybrid-precision
 // attention to cut decode compute", "Why preserve selected positions?" (keep
-// the top 5% high-score positions).
+// the top 5% high-score positions) and "Memory and runtime costs" (finding
+// the columns costs a few percent of the runtime).
 //
 // Column score c[j] = sum over the G query heads and the last R probe rows of
 // the row-normalised causal softmax. The map is never stored: pass 1
-// computes each row's normaliser over key chunks (relative to a reference
-// logit per chunk), a combine kernel merges the chunks, pass 2 recomputes the
-// logits and sums the normalised probabilities per column.
+// computes each row's normaliser over key chunks, a combine kernel merges
+// the chunks into one reference per row, pass 2 recomputes the logits and
+// sums the normalised probabilities per column.
 //
-// Precision: the selection is a ranking of scores whose top-k gap is often
-// only ~1e-5..1e-4 relative on long contexts, so the logits are formed
-// exactly (bf16/fp16 inputs converted to fp64, v_mfma_f64_16x16x4 with fp64
-// accumulation), exponentials use an fp64 polynomial, and normalisers and
-// column sums accumulate in fp64. The scores are rounded once to fp32.
+// Logits, exactly, on the int8 matrix cores. Every 16-bit value x of a set
+// (a 32-row tile of probe queries, or one key) becomes the integer
+// X = rint(x * 2^sh), |X| <= 2^30, with one power-of-two shift sh per set,
+// and X is split into four signed base-256 digits X = sum_a d_a 256^(3 - a)
+// (d_0 in [-65, 65], the others in [-128, 127]). A dot product of a query
+// row and a key is then 2^(48 - shq - shk) * sum_d 256^-d A_d with
+// A_d = sum_{a + b = d} sum_c dq_a[c] dk_b[c], every A_d an exact int32 sum
+// from v_mfma_i32_32x32x32_i8. The 13 digit pairs with a + b <= 4 are
+// computed; the rest of the product is bounded, not dropped silently: per
+// (query tile, key tile) the kernel evaluates, from the digits and the
+// rounding residuals x - X 2^-sh themselves, a bound on the logit error
+// (rounding residuals times the other operand's magnitude, plus the three
+// omitted pairs bounded through the digit planes' l1 norms and maxima).
+// On the workloads this bound is ~1e-8 in log2 units; a tile whose bound
+// exceeds kLogitBudget has its logits recomputed from the 16-bit inputs in
+// fp64 (exact products, fp64 sums), so every logit carries at most the
+// budget's error. Exponentials are fp64 (a degree-8 series on [-1/2, 1/2]
+// after an exact power-of-two split, relative error < 1e-10); every
+// normaliser and column sum accumulates in fp64 relative to integer
+// references, so rescaling by a power of two is exact. Scores are rounded
+// once to fp32. Resulting bound on each returned score, for the softmax with
+// the fp32 scale the caller passes: relative error < 2 ln2 kLogitBudget +
+// 2^-24 + 1e-9 < 2.7e-7, so two columns can change order only where their
+// exact scores differ by less than 5.4e-7 relative. (With the certificate at
+// ~1e-8 the scores come out within a few 1e-8: the fp32 rounding dominates.)
 //
 // Top-k: one workgroup per (b, g); 4-pass 8-bit radix select on the fp32 bit
 // patterns (scores are >= 0, so bit order = value order) with LDS histograms
@@ -30,329 +51,580 @@
 namespace hq {
 namespace {
 
-typedef double double4_t __attribute__((ext_vector_type(4)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx16 __attribute__((ext_vector_type(16)));
 
-// Keys per pass-1 workgroup: 1,024, or 512 when 1,024-key chunks would give
-// fewer than 1,024 workgroups (four per CU of the chip), so that short or
-// small-batch calls still spread over every CU. A multiple of 16.
-inline int probe_key_chunk(int32_t B, int32_t Hkv, int32_t Tmax) {
-    const int64_t wg = (int64_t)((Tmax + 1023) / 1024) * Hkv * B;
-    return wg >= 1024 ? 1024 : 512;
-}
+constexpr int kRT = 32;            // probe rows per row tile (one wave)
+constexpr int kKT = 32;            // keys per key tile
+constexpr int kTilesPerWg = 8;     // row tiles (waves) per workgroup at most
+constexpr int kPlanes = 4;         // base-256 digits per value
+constexpr int kDS = kD + 16;       // LDS bytes per key in a digit plane (pad: no bank conflicts)
+constexpr int kColBlk = 256;       // keys per pass-2 workgroup
+constexpr double kLogitBudget = 1.5e-7;  // largest logit error accepted from the digit path (log2 units)
+constexpr int kExpTerms = 8;       // 2^f = sum_{n <= 8} (f ln2)^n / n!, |f| <= 1/2: relative error < 1e-10
 
-// 2^x in fp64 (x finite or very negative): 2^n * e^(f ln2), |f| <= 1/2,
-// Taylor series to degree 14 (truncation < 1e-17 relative). The coefficients
-// 1/14! .. 1/2! come in the kernel arguments (c): uniform values in scalar
-// registers that the FMAs read directly (as literals the compiler keeps them
-// in vector registers and copies one into place before every FMA).
-constexpr int kExpCoefs = 13;
-__device__ inline double exp2_f64(double x, const double (&c)[kExpCoefs]) {
-    if (x < -1000.0) return 0.0;
-    const double n = rint(x);
-    const double y = (x - n) * 0.69314718055994530942;
-    double e = c[0];
-#pragma unroll
-    for (int i = 1; i < kExpCoefs; ++i) e = fma(e, y, c[i]);
-    e = fma(e, y, 1.0);
-    e = fma(e, y, 1.0);
-    return ldexp(e, (int)n);
-}
-
-// 32 consecutive 16-bit values (one lane's share of a row), loaded raw so
-// that the next tile's loads can be in flight while this tile is computed.
-struct Raw32 {
-    uint4 u[4];
-};
-__device__ inline Raw32 load_raw32(const uint16_t* src, bool ok) {
-    const uint4* s4 = reinterpret_cast<const uint4*>(src);
-    Raw32 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.u[i] = ok ? s4[i] : make_uint4(0, 0, 0, 0);
-    return r;
-}
-template <bool F16>
-__device__ inline void cvt32_f64(const Raw32& r, double* out) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t w[4] = {r.u[i].x, r.u[i].y, r.u[i].z, r.u[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            out[8 * i + 2 * j] = (double)h16_to_f32<F16>(w[j] & 0xFFFFu);
-            out[8 * i + 2 * j + 1] = (double)h16_to_f32<F16>(w[j] >> 16);
-        }
-    }
-}
-template <bool F16>
-__device__ inline void load32_f64(const uint16_t* src, bool ok, double* out) {
-    cvt32_f64<F16>(load_raw32(src, ok), out);
-}
-
-// Exact 16 x 16 block of dot products over 128 channels. Lane l supplies row
-// (l % 16) of A and column (l % 16) of B for channels 32*(l/16) .. +31; the
-// result element i of lane l is D[4*i + l/16][l % 16] (rows interleave across
-// the four 16-lane groups).
-__device__ inline double4_t mfma_dot128(const double* a, const double* b) {
-    double4_t acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int s = 0; s < 32; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc, 0, 0, 0);
-    return acc;
-}
-
-// As mfma_dot128 with the B operand given as raw 16-bit values, each
-// converted to fp64 just before the MFMA that reads it.
-template <bool F16>
-__device__ inline double raw_elem(const Raw32& r, int s) {
-    const uint4& u = r.u[s >> 3];
-    const uint32_t w = ((s >> 1) & 3) == 0 ? u.x : ((s >> 1) & 3) == 1 ? u.y : ((s >> 1) & 3) == 2 ? u.z : u.w;
-    return (double)h16_to_f32<F16>((s & 1) ? (w >> 16) : (w & 0xFFFFu));
-}
-template <bool F16>
-__device__ inline double4_t mfma_dot128_rb(const double* a, const Raw32& br) {
-    double4_t acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int s = 0; s < 32; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], raw_elem<F16>(br, s), acc, 0, 0, 0);
-    return acc;
-}
 struct ProbeParams {
     const uint16_t* q;     // [B][Hq][R][D]
     const uint16_t* k;     // [B][Hkv][Tmax][D]
     const int32_t* seq_lens;
-    double2* part;         // [B][Hkv][nchunk][NR] (m, l) per key chunk: l = sum of 2^(x - m), m a reference
-    double2* rows;         // [B][Hkv][NR] (M, 1/L) over all chunks, M = the largest chunk reference
+    double2* part;         // [B][Hkv][nchunk][NRp] (m, l) per key chunk: l = sum 2^(z - m), m an integer
+    double* rowref;        // [B][Hkv][NRp] m' = M + log2(L) per row: p = 2^(z - m')
+    double* colpart;       // [B][Hkv][ngroups][Tmax] column sums per row group (ngroups > 1)
     float* col_scores;     // [B][Hkv][Tmax]
-    int32_t B, Hq, Hkv, Tmax, R, G, NR, nchunk, chunk;  // chunk: keys per pass-1 workgroup
+    int32_t B, Hq, Hkv, Tmax, R, G, NR, NRp, ngroups, nchunk, chunk;
     double sc2;            // sm_scale * log2(e)
-    double ec[kExpCoefs];  // 1/14!, 1/13!, ..., 1/2!: the exp2_f64 series
+    double ec[kExpTerms + 1];  // (ln2)^n / n!, n = 0..8
 };
 
+// Row `row` of the (b, g) probe rows: head g*G + row / R, probe row row % R,
+// at position T - R + row % R (negative positions are not rows of the map).
 __device__ inline const uint16_t* qrow(const ProbeParams& p, int b, int g, int row) {
     const int h = row / p.R, r = row % p.R;
     return p.q + (((size_t)b * p.Hq + g * p.G + h) * p.R + r) * kD;
 }
-__device__ inline int row_pos(const ProbeParams& p, int T, int row) { return T - p.R + (row % p.R); }
 
-// Pass 1: per (key chunk, g, b), online reference / sum of 2^x per probe
-// row. A workgroup of 16 waves, one 16-row tile of probe rows per wave (its
-// queries held in fp64), streams the chunk's keys 16 at a time: each key tile
-// is converted to fp64 once into LDS (double-buffered; the next tile's raw
-// values are loaded while this one is computed) and read by every wave.
-constexpr int kPW = 16;          // waves per pass-1 workgroup
-constexpr int kKRow = kD + 2;    // LDS row stride in doubles (16-byte pad: no bank conflicts across rows)
 template <bool F16>
-__device__ inline double4_t mfma_dot128_lds(const double* a, const double* brow) {
-    double4_t acc = {0.0, 0.0, 0.0, 0.0};
+__device__ inline void unpack8(const uint4& u, float* x) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int s = 0; s < 32; s += 2) {
-        const double2 bb = *reinterpret_cast<const double2*>(brow + s);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], bb.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s + 1], bb.y, acc, 0, 0, 0);
-        if ((s & 7) == 6) asm volatile("" ::: "memory");  // bound the LDS reads in flight
+    for (int j = 0; j < 4; ++j) {
+        x[2 * j] = h16_to_f32<F16>(w[j] & 0xFFFFu);
+        x[2 * j + 1] = h16_to_f32<F16>(w[j] >> 16);
     }
-    return acc;
+}
+
+// Shift of a set whose largest magnitude is mx: |x| * 2^sh < 2^30.
+__device__ inline int set_shift(float mx) { return mx > 0.f ? 30 - __builtin_amdgcn_frexp_expf(mx) : 0; }
+
+// x -> X = rint(x 2^sh) (exact int32) and the residual |x 2^sh - X| (<= 1/2).
+__device__ inline int to_fixed(float x, int sh, float& res) {
+    const float t = __builtin_ldexpf(x, sh);  // exact: a power-of-two scaling
+    const float tr = __builtin_rintf(t);
+    res = fabsf(t - tr);                       // exact
+    return (int)tr;
+}
+// The four balanced base-256 digits of X (|X| <= 2^30) are the bytes of
+// (X + 0x808080) ^ 0x808080: byte 3 = d_0 (top), byte 0 = d_3.
+__device__ inline uint32_t digit_bytes(int X) { return (uint32_t)(X + 0x808080) ^ 0x808080u; }
+// Byte `by` of four words, packed into one word (element order z0..z3).
+__device__ inline uint32_t gather_byte(uint32_t z0, uint32_t z1, uint32_t z2, uint32_t z3, int by) {
+    const uint32_t sel = (uint32_t)by | ((uint32_t)(by + 4) << 8) | 0x0C0C0000u;
+    const uint32_t lo = __builtin_amdgcn_perm(z1, z0, sel);  // z0[by], z1[by], 0, 0
+    const uint32_t hi = __builtin_amdgcn_perm(z3, z2, sel);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+__device__ inline int sbyte(uint32_t w, int i) { return (int)(int8_t)(w >> (8 * i)); }
+
+// Reductions over 16- and 32-lane groups without LDS traffic: DPP moves
+// within rows of 16 lanes, then v_permlane16_swap across the two rows of a
+// 32-lane half.
+template <int CTRL>
+__device__ inline uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) { return __uint_as_float(dpp_u<CTRL>(__float_as_uint(v))); }
+__device__ inline float max16(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+    return fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+}
+__device__ inline float sum16(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    return v + dpp_f<0x140>(v);
+}
+__device__ inline int min16(int v) {
+    v = min(v, (int)dpp_u<0xB1>((uint32_t)v));
+    v = min(v, (int)dpp_u<0x4E>((uint32_t)v));
+    v = min(v, (int)dpp_u<0x141>((uint32_t)v));
+    return min(v, (int)dpp_u<0x140>((uint32_t)v));
+}
+__device__ inline float max32(float v) {
+    v = max16(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline int min32(int v) {
+    v = min16(v);
+    const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    return min((int)r[0], (int)r[1]);
+}
+
+// 2^y in fp64 for y <= 1023: 2^n * 2^f, n = rint(y), |f| <= 1/2, series with
+// the coefficients (ln2)^k / k! passed in (uniform values in scalar registers).
+__device__ inline double exp2_d(double y, const double (&c)[kExpTerms + 1]) {
+    const double n = __builtin_rint(y);
+    const double f = y - n;  // exact
+    double e = c[kExpTerms];
+#pragma unroll
+    for (int i = kExpTerms - 1; i >= 0; --i) e = __builtin_fma(e, f, c[i]);
+    return __builtin_ldexp(e, (int)n);  // underflows to 0 for very negative y
+}
+
+// Per-key data of the key tile in LDS.
+struct KeyTile {
+    int8_t d[kPlanes][kKT][kDS];  // digit planes, key-major, the MFMA B operand
+    int sh[kKT];                   // shift of the key
+    float rho[kKT];                // sum over channels of |residual| * 2^-sh (an upper bound, real units)
+    float kmax[kKT];               // max |k|
+};
+
+// Digit planes 2 and 3 of one wave's query tile (row-major like the key
+// planes; the MFMA A operand of the pairs (2, b) and (3, b)).
+struct QPlanes {
+    int8_t d[2][kRT][kDS];
+};
+
+struct ProbeSmem {
+    KeyTile kt[2];
+    QPlanes q23[kTilesPerWg];
+    double col[kTilesPerWg][kColBlk];  // pass 2: per-wave column partial sums of the block
+};
+
+// Key tile [key0, key0 + 32) of one (b, g): thread t (of the workgroup's
+// 512) moves channels 8 (t % 16) .. + 7 of key key0 + t / 16. The load is
+// issued a tile ahead; the conversion to digit planes and statistics writes
+// the LDS tile (keys >= key_end are zero).
+__device__ inline uint4 load_keys(const uint16_t* kbase, int key0, int key_end) {
+    const int t = threadIdx.x, key = key0 + (t >> 4), c0 = (t & 15) * 8;
+    return key < key_end ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * kD + c0) : make_uint4(0, 0, 0, 0);
 }
 template <bool F16>
-__global__ __launch_bounds__(1024) void k_probe_rowstats(ProbeParams p) {
-    __shared__ __align__(16) double kt[2][16][kKRow];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__device__ inline void store_keys(const uint4& u, KeyTile& kt) {
+    const int t = threadIdx.x, kk = t >> 4, c0 = (t & 15) * 8;
+    float x[8];
+    unpack8<F16>(u, x);
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(x[j]));
+    mx = max16(mx);  // the 16 threads of a key are one 16-lane row of a wave
+    const int sh = set_shift(mx);
+    uint32_t z[8];
+    float rsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float r;
+        z[j] = digit_bytes(to_fixed(x[j], sh, r));
+        rsum += r;
+    }
+#pragma unroll
+    for (int a = 0; a < kPlanes; ++a) {
+        const int by = 3 - a;
+        uint2 w;
+        w.x = gather_byte(z[0], z[1], z[2], z[3], by);
+        w.y = gather_byte(z[4], z[5], z[6], z[7], by);
+        *reinterpret_cast<uint2*>(&kt.d[a][kk][c0]) = w;
+    }
+    rsum = sum16(rsum);
+    if ((t & 15) == 0) {
+        kt.sh[kk] = sh;
+        kt.rho[kk] = __builtin_ldexpf(rsum * (1.0f + 0x1p-16f), -sh);
+        kt.kmax[kk] = mx;
+    }
+}
+
+// One wave's probe rows (a 32-row tile): digit planes as MFMA A operands
+// (lane l holds row l % 32, channels 32 ks + 16 (l / 32) .. + 15 of K-step
+// ks), and the tile's statistics.
+struct QTile {
+    intx4 d[2][4];     // planes 0 and 1 (planes 2 and 3 are in LDS)
+    int sh;
+    float qmax, rho;   // max |q|; max over rows of sum |residual| (real units)
+    int n2, n3;        // max over rows of sum |d_2|, sum |d_3|
+};
+template <bool F16>
+__device__ inline QTile convert_queries(const ProbeParams& p, int b, int g, int T, int rt, QPlanes& q23) {
+    const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
+    const int row = rt * kRT + m;
+    const bool ok = row < p.NR && T - p.R + row % p.R >= 0;
+    const uint16_t* src = ok ? qrow(p, b, g, row) : nullptr;
+    float x[4][16];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const uint4 u0 = ok ? *reinterpret_cast<const uint4*>(src + 32 * ks + 16 * hf) : make_uint4(0, 0, 0, 0);
+        const uint4 u1 = ok ? *reinterpret_cast<const uint4*>(src + 32 * ks + 16 * hf + 8) : make_uint4(0, 0, 0, 0);
+        unpack8<F16>(u0, x[ks]);
+        unpack8<F16>(u1, x[ks] + 8);
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(x[ks][j]));
+    mx = wave_max(mx);
+    QTile t;
+    t.sh = set_shift(mx);
+    t.qmax = mx;
+    float rsum = 0.f;
+    int n2 = 0, n3 = 0;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        uint32_t z[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            float r;
+            z[j] = digit_bytes(to_fixed(x[ks][j], t.sh, r));
+            rsum += r;
+            n2 += abs(sbyte(z[j], 1));
+            n3 += abs(sbyte(z[j], 0));
+        }
+#pragma unroll
+        for (int a = 0; a < kPlanes; ++a) {
+            const int by = 3 - a;
+            const intx4 w{(int)gather_byte(z[0], z[1], z[2], z[3], by), (int)gather_byte(z[4], z[5], z[6], z[7], by),
+                          (int)gather_byte(z[8], z[9], z[10], z[11], by), (int)gather_byte(z[12], z[13], z[14], z[15], by)};
+            if (a < 2) t.d[a][ks] = w;
+            else *reinterpret_cast<intx4*>(&q23.d[a - 2][lane & 31][32 * ks + 16 * (lane >> 5)]) = w;
+        }
+    }
+    // per row: both halves of the row (lanes l, l ^ 32); then the tile maximum
+    rsum += __shfl_xor(rsum, 32);
+    n2 += __shfl_xor(n2, 32);
+    n3 += __shfl_xor(n3, 32);
+    t.rho = __builtin_ldexpf(wave_max(rsum * (1.0f + 0x1p-16f)), -t.sh);
+    t.n2 = (int)wave_max((float)n2);
+    t.n3 = (int)wave_max((float)n3);
+    return t;
+}
+
+// Exact digit sums of a 32-row x 32-key tile: D[row][key] with lane l holding
+// key l % 32 and rows 8 (i / 4) + 4 (l / 32) + i % 4 in element i. hi =
+// 256 A_0 + A_1, mid = 256 A_2 + A_3, lo = A_4 (all within int32).
+struct DigitSums {
+    intx16 hi, mid, lo;
+};
+__device__ inline DigitSums tile_digit_sums(const QTile& q, const QPlanes& q23, const KeyTile& kt) {
+    const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+    DigitSums s;
+    // A_0 first, then hi = 256 A_0 accumulates A_1 (one accumulator fewer
+    // live during the main loop; key plane 0 is read twice)
+    intx16 hi = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        hi = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[0][ks], *reinterpret_cast<const intx4*>(&kt.d[0][n][32 * ks + 16 * hf]),
+                                                  hi, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) hi[i] <<= 8;
+    intx16 a2 = {}, a3 = {}, a4 = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        intx4 kb[kPlanes];
+#pragma unroll
+        for (int a = 0; a < kPlanes; ++a) kb[a] = *reinterpret_cast<const intx4*>(&kt.d[a][n][32 * ks + 16 * hf]);
+        const intx4 q2 = *reinterpret_cast<const intx4*>(&q23.d[0][n][32 * ks + 16 * hf]);
+        const intx4 q3 = *reinterpret_cast<const intx4*>(&q23.d[1][n][32 * ks + 16 * hf]);
+        hi = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[0][ks], kb[1], hi, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[0][ks], kb[2], a2, 0, 0, 0);
+        a3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[0][ks], kb[3], a3, 0, 0, 0);
+        hi = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[1][ks], kb[0], hi, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[1][ks], kb[1], a2, 0, 0, 0);
+        a3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[1][ks], kb[2], a3, 0, 0, 0);
+        a4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[1][ks], kb[3], a4, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q2, kb[0], a2, 0, 0, 0);
+        a3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q2, kb[1], a3, 0, 0, 0);
+        a4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q2, kb[2], a4, 0, 0, 0);
+        a3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q3, kb[0], a3, 0, 0, 0);
+        a4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q3, kb[1], a4, 0, 0, 0);
+    }
+    s.hi = hi;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s.mid[i] = (a2[i] << 8) + a3[i];
+    s.lo = a4;
+    return s;
+}
+
+// Bound (log2 units) on the error of the digit path's logits for this tile
+// pair: rounding residuals times the other operand, and the omitted pairs
+// (2,3), (3,2), (3,3) through the query digit planes' l1 norms.
+__device__ inline double tile_error_bound(const QTile& q, const KeyTile& kt, double asc2) {
+    const int n = threadIdx.x & 31;
+    const float kmax = max32(kt.kmax[n]), krho = max32(kt.rho[n]);
+    const int shmin = min32(kt.sh[n]);
+    const double res = (double)q.rho * kmax + ((double)q.qmax + q.rho) * krho;
+    // |D_23| <= n2 * 128, |D_32| <= n3 * 128, |D_33| <= n3 * 128 (|d| <= 128),
+    // weights 2^(8 - sh), 2^(8 - sh), 2^(-sh)
+    const double om = __builtin_ldexp(128.0 * ((double)q.n2 + (double)q.n3 * (1.0 + 0x1p-8)), 8 - q.sh - shmin);
+    return (res + om) * asc2 * (1.0 + 0x1p-20);
+}
+
+// The tile's logits in log2 units (z = q . k * sm_scale * log2 e), one
+// element at a time: from the digit sums, or, when the tile's error bound
+// exceeds the budget (a wave-uniform decision), recomputed in fp64 from the
+// 16-bit inputs (exact products, fp64 sums).
+struct TileLogits {
+    DigitSums s;
+    double F;       // 2^(16 - shq - shk) * sm_scale * log2 e of this lane's key
+    bool exact_fallback;
+};
+__device__ inline TileLogits tile_begin(const ProbeParams& p, const QTile& q, const QPlanes& q23, const KeyTile& kt) {
+    TileLogits t;
+    t.s = tile_digit_sums(q, q23, kt);
+    // the same value in every lane; made a scalar so the branches on it are uniform
+    t.exact_fallback = __builtin_amdgcn_readfirstlane((int)!(tile_error_bound(q, kt, fabs(p.sc2)) <= kLogitBudget)) != 0;
+    t.F = __builtin_ldexp(p.sc2, 16 - q.sh - kt.sh[threadIdx.x & 31]);
+    return t;
+}
+// Element i's logit: from the digit sums, or (exact_fallback) the fp64 value
+// whose bits fill_exact() left in hi (low word) and mid (high word).
+__device__ inline double tile_logit(const TileLogits& t, int i) {
+    if (t.exact_fallback)
+        return __builtin_bit_cast(double, ((uint64_t)(uint32_t)t.s.mid[i] << 32) | (uint32_t)t.s.hi[i]);
+    const double u = __builtin_fma((double)t.s.hi[i], 65536.0, (double)t.s.mid[i]);  // exact
+    return __builtin_fma(u, 256.0 * t.F, (double)t.s.lo[i] * t.F);
+}
+template <bool F16>
+__device__ inline double exact_logit(const ProbeParams& p, int b, int g, const uint16_t* kbase, int key,
+                                                       int row) {
+    // (rare: a few registers, no unrolling, so the common path keeps its occupancy)
+    double acc = 0.0;
+    const uint32_t* qr = reinterpret_cast<const uint32_t*>(qrow(p, b, g, row));
+    const uint32_t* kr = reinterpret_cast<const uint32_t*>(kbase + (size_t)key * kD);
+#pragma unroll 1
+    for (int c = 0; c < kD / 2; ++c) {
+        const uint32_t wq = qr[c], wk = kr[c];
+        acc = __builtin_fma((double)h16_to_f32<F16>(wq & 0xFFFFu), (double)h16_to_f32<F16>(wk & 0xFFFFu), acc);
+        acc = __builtin_fma((double)h16_to_f32<F16>(wq >> 16), (double)h16_to_f32<F16>(wk >> 16), acc);
+    }
+    return acc * p.sc2;
+}
+
+// The probe row held in element i of this lane, its position, and whether
+// it is a row of the map.
+__device__ inline int elem_row(int rt, int i) { return rt * kRT + 8 * (i >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (i & 3); }
+
+// Pass 1: per (key chunk, row group, g, b): for every probe row of the group,
+// (m, l) over the chunk's keys with m an integer reference and
+// l = sum 2^(z - m). One wave per 32-row tile; the key tiles are converted to
+// digits once per workgroup into LDS (double-buffered) and read by every wave.
+// The tile's exact logits (rare): every element of this lane, stored as fp64
+// bits in the digit-sum registers.
+template <bool F16>
+__device__ inline void fill_exact(const ProbeParams& p, TileLogits& t, int b, int g, const uint16_t* kbase, int key,
+                                  int key_end, int rt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int row = elem_row(rt, i);
+        const double z = (key < key_end && row < p.NR) ? exact_logit<F16>(p, b, g, kbase, key, row) : 0.0;
+        const uint64_t u = __builtin_bit_cast(uint64_t, z);
+        t.s.hi[i] = (int)(uint32_t)u;
+        t.s.mid[i] = (int)(uint32_t)(u >> 32);
+    }
+}
+
+// Whether element i's probe row is a row of the map (row < NR, position
+// >= 0) and the key (< key_end) is at or before its position. Rows' positions
+// are T - R + row % R, so keys below T - R pass for every real row.
+__device__ inline bool elem_valid(const ProbeParams& p, int T, int row, int key, int key_end) {
+    if (key >= key_end || row >= p.NR) return false;
+    return key <= T - p.R + row % p.R;
+}
+// Bit i: element i's row is a row of the map (row < NR, position >= 0).
+__device__ inline uint32_t row_mask(const ProbeParams& p, int T, int rt) {
+    uint32_t mk = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int row = elem_row(rt, i);
+        mk |= (row < p.NR && T - p.R + row % p.R >= 0) ? 1u << i : 0u;
+    }
+    return mk;
+}
+// Mask of the elements of a key tile [key0, key0 + 32): keys below T - R are
+// before every row's position, so only the last tiles need the causal test.
+__device__ inline uint32_t tile_mask(const ProbeParams& p, int T, int rt, uint32_t rowmk, int key0, int key_end) {
+    const int key = key0 + (threadIdx.x & 31);
+    if (key >= key_end) return 0u;
+    if (key0 + kKT - 1 <= T - p.R) return rowmk;
+    uint32_t mk = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mk |= elem_valid(p, T, elem_row(rt, i), key, key_end) ? 1u << i : 0u;
+    return mk;
+}
+
+template <bool F16>
+__global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
+    __shared__ ProbeSmem sm;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int chunk = blockIdx.x, grp = blockIdx.y % p.ngroups, g = blockIdx.y / p.ngroups, b = blockIdx.z;
     const int T = p.seq_lens[b];
-    const int key_lo = chunk * p.chunk;
     const int bg = b * p.Hkv + g;
-    const int li = lane & 15, kq = lane >> 4;
-    const uint16_t* kbase = p.k + (size_t)bg * p.Tmax * kD;
-    const int nrt = p.NR / 16;
-    double2* part = p.part + ((size_t)bg * p.nchunk + chunk) * p.NR;
+    const int rt = grp * kTilesPerWg + wave;
+    const int key_lo = chunk * p.chunk;
+    double2* part = p.part + ((size_t)bg * p.nchunk + chunk) * p.NRp;
+    const bool active = rt * kRT < p.NRp;  // wave-uniform: the last group may have fewer tiles
     if (key_lo >= T) {  // no key of this chunk exists: empty statistics
-        for (int r = tid; r < p.NR; r += 1024) part[r] = make_double2(-INFINITY, 0.0);
+        if (lane < 32 && active) part[rt * kRT + lane] = make_double2(-INFINITY, 0.0);
         return;
     }
     const int key_hi = min(key_lo + p.chunk, T);
-    const int ntile = (key_hi - key_lo + 15) / 16;
-    // staging: thread t < 256 moves 8 channels (16 bytes) of key t / 16 of a tile
-    const int srow = (tid >> 4) & 15, sc0 = (tid & 15) * 8;
-    auto stage_load = [&](int t) {
-        const int key = key_lo + 16 * t + srow;
-        const bool ok = tid < 256 && key < key_hi;
-        return ok ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * kD + sc0) : make_uint4(0, 0, 0, 0);
-    };
-    auto stage_store = [&](int buf, const uint4& raw) {
-        if (tid < 256) {
-            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-            double* dst = &kt[buf][srow][sc0];
+    const int ntile = (key_hi - key_lo + kKT - 1) / kKT;
+    const uint16_t* kbase = p.k + (size_t)bg * p.Tmax * kD;
+    const QTile q = convert_queries<F16>(p, b, g, T, rt, sm.q23[wave]);
+    const uint32_t rowmk = row_mask(p, T, rt);
+    int m[16];  // integer references (INT_MIN: none yet)
+    double l[16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<double2*>(dst + 2 * j) =
-                    make_double2((double)h16_to_f32<F16>(w[j] & 0xFFFFu), (double)h16_to_f32<F16>(w[j] >> 16));
+    for (int i = 0; i < 16; ++i) {
+        m[i] = INT_MIN;
+        l[i] = 0.0;
+    }
+    store_keys<F16>(load_keys(kbase, key_lo, key_hi), sm.kt[0]);
+    __syncthreads();
+    for (int t = 0; t < ntile; ++t) {
+        const int cur = t & 1;
+        const int key0 = key_lo + kKT * t;
+        const uint4 nxt = load_keys(kbase, key0 + kKT, t + 1 < ntile ? key_hi : 0);  // next tile, in flight
+        if (active) {
+            TileLogits tl = tile_begin(p, q, sm.q23[wave], sm.kt[cur]);
+            const int key = key0 + (lane & 31);
+            if (tl.exact_fallback) fill_exact<F16>(p, tl, b, g, kbase, key, key_hi, rt);
+            const uint32_t mk = tile_mask(p, T, rt, rowmk, key0, key_hi);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const bool v = (mk >> i) & 1u;
+                const double z = tile_logit(tl, i);
+                if (v && z > (double)m[i] + 256.0) {
+                    // move the reference up to ceil(z) (rare; the first valid
+                    // logit of the row always): an exact power-of-two rescale
+                    const int mn = (int)__builtin_ceil(fmax(fmin(z, 2.0e9), -2.0e9));
+                    l[i] = m[i] == INT_MIN ? 0.0 : __builtin_ldexp(l[i], m[i] - mn);
+                    m[i] = mn;
+                }
+                const double e = exp2_d(z - (double)m[i], p.ec);
+                l[i] += v ? e : 0.0;
+            }
         }
-    };
-    for (int rt0 = 0; rt0 < nrt; rt0 += kPW) {
-        const int rt = rt0 + wave;
-        const bool active = rt < nrt;  // wave-uniform
-        stage_store(0, stage_load(0));
+        if (t + 1 < ntile) store_keys<F16>(nxt, sm.kt[cur ^ 1]);
         __syncthreads();
-        double m[4], l[4];
+    }
+    if (!active) return;
+    // merge the 32 lanes of each half (same rows, different keys): exact
+    // power-of-two rescales to the larger reference
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m[i] = -INFINITY;
-            l[i] = 0.0;
+    for (int o = 1; o < 32; o <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m2 = __shfl_xor(m[i], o);
+            const double l2 = __shfl_xor(l[i], o);
+            const int M = max(m[i], m2);
+            double L = 0.0;
+            if (m[i] != INT_MIN) L += __builtin_ldexp(l[i], m[i] - M);
+            if (m2 != INT_MIN) L += __builtin_ldexp(l2, m2 - M);
+            m[i] = M;
+            l[i] = L;
         }
-        double a[32];
-        int pos[4];
-        if (active) {
-            load32_f64<F16>(qrow(p, b, g, rt * 16 + li) + 32 * kq, true, a);
+    }
+    if ((lane & 31) == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pos[i] = row_pos(p, T, rt * 16 + 4 * i + kq);
-        }
-        // m is a reference, not the running maximum: l = sum of 2^(x - m)
-        // with m moved only when a logit exceeds it by more than 2^9 (and on
-        // the first one), so the common path takes one exp per element and
-        // no divergent branch. Terms up to 2^512 are exact in fp64 range; the
-        // chunk merge and the normalisation accept any reference.
-        for (int t = 0; t < ntile; ++t) {
-            const int cur = t & 1;
-            const bool more = t + 1 < ntile;
-            const uint4 nraw = more ? stage_load(t + 1) : make_uint4(0, 0, 0, 0);
-            if (active) {
-                const int key = key_lo + 16 * t + li;
-                const bool kok = key < key_hi;
-                const double4_t acc = mfma_dot128_lds<F16>(a, &kt[cur][li][32 * kq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (kok && pos[i] >= 0 && key <= pos[i]) {
-                        const double x = acc[i] * p.sc2;
-                        if (x > m[i] + 512.0) {
-                            l[i] = l[i] * exp2_f64(m[i] - x, p.ec);
-                            m[i] = x;
-                        }
-                        l[i] += exp2_f64(x - m[i], p.ec);
-                    }
-                }
-            }
-            if (more) stage_store(cur ^ 1, nraw);
-            __syncthreads();
-        }
-        if (active) {
-            // merge the 16 lanes that hold the same rows (different keys)
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const double m2 = __shfl_xor(m[i], off), l2 = __shfl_xor(l[i], off);
-                    const double M = fmax(m[i], m2);
-                    double L = 0.0;
-                    if (m[i] != -INFINITY) L += l[i] * exp2_f64(m[i] - M, p.ec);
-                    if (m2 != -INFINITY) L += l2 * exp2_f64(m2 - M, p.ec);
-                    m[i] = M;
-                    l[i] = L;
-                }
-            }
-            if (li == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) part[rt * 16 + kq + 4 * i] = make_double2(m[i], l[i]);
-            }
-        }
+        for (int i = 0; i < 16; ++i)
+            part[elem_row(rt, i)] = make_double2(m[i] == INT_MIN ? -INFINITY : (double)m[i], l[i]);
     }
 }
 
-// Merge the chunk statistics of every probe row: (M, 1/L), with M the
-// largest chunk reference and L = sum of l * 2^(m - M).
+// Merge the chunk statistics of every probe row: M = the largest chunk
+// reference, L = sum l 2^(m - M) (exact rescales), m' = M + log2(L).
 __global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
     const int g = blockIdx.x, b = blockIdx.y;
     const int bg = b * p.Hkv + g;
     const int T = p.seq_lens[b];
     const int nch = (T + p.chunk - 1) / p.chunk;
-    for (int row = threadIdx.x; row < p.NR; row += 256) {
+    for (int row = threadIdx.x; row < p.NRp; row += 256) {
         double M = -INFINITY;
-        for (int c = 0; c < nch; ++c) M = fmax(M, p.part[((size_t)bg * p.nchunk + c) * p.NR + row].x);
+        for (int c = 0; c < nch; ++c) M = fmax(M, p.part[((size_t)bg * p.nchunk + c) * p.NRp + row].x);
         double L = 0.0;
-        for (int c = 0; c < nch; ++c) {
-            const double2 v = p.part[((size_t)bg * p.nchunk + c) * p.NR + row];
-            if (v.x != -INFINITY) L += v.y * exp2_f64(v.x - M, p.ec);
+        if (M != -INFINITY) {
+            for (int c = 0; c < nch; ++c) {
+                const double2 v = p.part[((size_t)bg * p.nchunk + c) * p.NRp + row];
+                if (v.x != -INFINITY) L += __builtin_ldexp(v.y, (int)(v.x - M));
+            }
         }
-        p.rows[(size_t)bg * p.NR + row] = make_double2(M, L > 0.0 ? 1.0 / L : 0.0);
+        p.rowref[(size_t)bg * p.NRp + row] = L > 0.0 ? M + log2(L) : INFINITY;
     }
 }
 
-// Pass 2: per (256-key block, g, b), column sums of the normalised softmax.
-// Each of the 16 waves holds 16 keys in fp64; the probe rows stream through
-// LDS 16 at a time, converted to fp64 once per workgroup (double-buffered,
-// the next tile's raw values loaded while this one is computed).
-__device__ inline double4_t mfma_dot128_lda(const double* arow, const double* b) {
-    double4_t acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int s = 0; s < 32; s += 2) {
-        const double2 aa = *reinterpret_cast<const double2*>(arow + s);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(aa.x, b[s], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(aa.y, b[s + 1], acc, 0, 0, 0);
-        if ((s & 7) == 6) asm volatile("" ::: "memory");  // bound the LDS reads in flight
-    }
-    return acc;
-}
-constexpr int kColKeys = 16 * kPW;  // keys per pass-2 workgroup
+// Pass 2: per (256-key block, row group, g, b): column sums of
+// 2^(z - m'_row) over the group's probe rows. The same tiling as pass 1;
+// per lane the 16 rows of its elements, per wave a 32-row tile; the waves'
+// partial sums meet in LDS and are added in a fixed order.
 template <bool F16>
-__global__ __launch_bounds__(1024) void k_probe_colsum(ProbeParams p) {
-    __shared__ __align__(16) double qt[2][16][kKRow];
-    __shared__ double2 rs[512];
-    __shared__ int rpos[512];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(512) void k_probe_colsum(ProbeParams p) {
+    __shared__ ProbeSmem sm;
+    const int lane = threadIdx.x & 63, hf = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int blk = blockIdx.x, grp = blockIdx.y % p.ngroups, g = blockIdx.y / p.ngroups, b = blockIdx.z;
     const int T = p.seq_lens[b];
     const int bg = b * p.Hkv + g;
-    const int li = lane & 15, kq = lane >> 4;
-    const int key = blk * kColKeys + wave * 16 + li;
-    if (blk * kColKeys >= T) {
-        if (tid < kColKeys && blk * kColKeys + tid < p.Tmax)
-            p.col_scores[(size_t)bg * p.Tmax + blk * kColKeys + tid] = 0.0f;
+    const int rt = grp * kTilesPerWg + wave;
+    const int key_lo = blk * kColBlk;
+    float* out = p.col_scores + (size_t)bg * p.Tmax;
+    double* outp = p.colpart + ((size_t)bg * p.ngroups + grp) * p.Tmax;
+    if (key_lo >= T) {
+        for (int j = threadIdx.x; j < kColBlk && key_lo + j < p.Tmax; j += blockDim.x) {
+            if (p.ngroups == 1) out[key_lo + j] = 0.0f;
+            else outp[key_lo + j] = 0.0;
+        }
         return;
     }
-    // staging: thread t < 256 moves 8 channels (16 bytes) of probe row t / 16 of a tile
-    const int srow = (tid >> 4) & 15, sc0 = (tid & 15) * 8;
-    auto stage_load = [&](int rt) {
-        return tid < 256 ? *reinterpret_cast<const uint4*>(qrow(p, b, g, rt * 16 + srow) + sc0) : make_uint4(0, 0, 0, 0);
-    };
-    auto stage_store = [&](int buf, const uint4& raw) {
-        if (tid < 256) {
-            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-            double* dst = &qt[buf][srow][sc0];
+    const int key_hi = min(key_lo + kColBlk, T);
+    const int ntile = (key_hi - key_lo + kKT - 1) / kKT;
+    const uint16_t* kbase = p.k + (size_t)bg * p.Tmax * kD;
+    const bool active = rt * kRT < p.NRp;
+    const QTile q = convert_queries<F16>(p, b, g, T, rt, sm.q23[wave]);
+    const uint32_t rowmk = row_mask(p, T, rt);
+    double ref[16];  // m' of each element's row (rows beyond NR are never used)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<double2*>(dst + 2 * j) =
-                    make_double2((double)h16_to_f32<F16>(w[j] & 0xFFFFu), (double)h16_to_f32<F16>(w[j] >> 16));
-        }
-    };
-    for (int row = tid; row < p.NR; row += 1024) {
-        rs[row] = p.rows[(size_t)bg * p.NR + row];
-        rpos[row] = row_pos(p, T, row);
+    for (int i = 0; i < 16; ++i) {
+        const int row = elem_row(rt, i);
+        ref[i] = row < p.NR ? p.rowref[(size_t)bg * p.NRp + row] : 0.0;
     }
-    stage_store(0, stage_load(0));
+    store_keys<F16>(load_keys(kbase, key_lo, key_hi), sm.kt[0]);
     __syncthreads();
-    const bool kok = key < T;
-    double bv[32];
-    load32_f64<F16>(p.k + ((size_t)bg * p.Tmax + (kok ? key : 0)) * kD + 32 * kq, kok, bv);
-    double colacc = 0.0;
-    const int nrt = p.NR / 16;
-    for (int rt = 0; rt < nrt; ++rt) {
-        const int cur = rt & 1;
-        const bool more = rt + 1 < nrt;
-        const uint4 nraw = more ? stage_load(rt + 1) : make_uint4(0, 0, 0, 0);
-        const double4_t acc = mfma_dot128_lda(&qt[cur][li][32 * kq], bv);
+    for (int t = 0; t < ntile; ++t) {
+        const int cur = t & 1;
+        const int key0 = key_lo + kKT * t;
+        const uint4 nxt = load_keys(kbase, key0 + kKT, t + 1 < ntile ? key_hi : 0);  // next tile, in flight
+        double acc = 0.0;
+        if (active) {
+            TileLogits tl = tile_begin(p, q, sm.q23[wave], sm.kt[cur]);
+            const int key = key0 + (lane & 31);
+            if (tl.exact_fallback) fill_exact<F16>(p, tl, b, g, kbase, key, key_hi, rt);
+            const uint32_t mk = tile_mask(p, T, rt, rowmk, key0, key_hi);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = rt * 16 + 4 * i + kq;
-            const int pr = rpos[row];
-            if (kok && pr >= 0 && key <= pr) {
-                const double2 st = rs[row];
-                colacc += exp2_f64(acc[i] * p.sc2 - st.x, p.ec) * st.y;
+            for (int i = 0; i < 16; ++i) {
+                const double e = exp2_d(tile_logit(tl, i) - ref[i], p.ec);
+                acc += ((mk >> i) & 1u) ? e : 0.0;
             }
+            acc += __shfl_xor(acc, 32);
         }
-        if (more) stage_store(cur ^ 1, nraw);
+        if (hf == 0) sm.col[wave][kKT * t + (lane & 31)] = acc;
+        if (t + 1 < ntile) store_keys<F16>(nxt, sm.kt[cur ^ 1]);
         __syncthreads();
     }
-    colacc += __shfl_xor(colacc, 16);
-    colacc += __shfl_xor(colacc, 32);
-    if (kq == 0 && key < p.Tmax) p.col_scores[(size_t)bg * p.Tmax + key] = kok ? (float)colacc : 0.0f;
+    // sum over the waves (row tiles) in order
+    for (int j = threadIdx.x; j < kColBlk; j += blockDim.x) {
+        const int key = key_lo + j;
+        if (key >= p.Tmax) break;
+        double sum = 0.0;
+        if (key < key_hi)
+            for (int w = 0; w < nw; ++w) sum += sm.col[w][j];
+        if (p.ngroups == 1) out[key] = key < key_hi ? (float)sum : 0.0f;
+        else outp[key] = sum;
+    }
+}
+
+// More than 8 row tiles: the row groups' column sums, added in group order.
+__global__ __launch_bounds__(256) void k_probe_colfinal(ProbeParams p) {
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int bg = b * p.Hkv + g;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= p.Tmax) return;
+    double s = 0.0;
+    for (int grp = 0; grp < p.ngroups; ++grp) s += p.colpart[((size_t)bg * p.ngroups + grp) * p.Tmax + j];
+    p.col_scores[(size_t)bg * p.Tmax + j] = (float)s;
 }
 
 // ---------------------------------------------------------------- top-k
@@ -487,19 +759,37 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
     }
 }
 
+
 struct ProbeWs {
-    size_t part, rows, total;
+    size_t part, rowref, colpart, total;
 };
 inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct ProbeShape {
+    int NR, NRp, nrt, ngroups, waves, chunk, nchunk;
+};
+// Keys per pass-1 workgroup: 1,024, halved (down to 256) while the grid
+// would have fewer than 1,024 workgroups (four per CU of the chip).
+ProbeShape probe_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_policy& pol) {
+    ProbeShape s;
+    s.NR = (Hq / Hkv) * pol.probe_rows;
+    s.NRp = (s.NR + kRT - 1) / kRT * kRT;
+    s.nrt = s.NRp / kRT;
+    s.ngroups = (s.nrt + kTilesPerWg - 1) / kTilesPerWg;
+    s.waves = s.nrt < kTilesPerWg ? s.nrt : kTilesPerWg;
+    s.chunk = 1024;
+    while (s.chunk > 256 && (int64_t)((Tmax + s.chunk - 1) / s.chunk) * Hkv * s.ngroups * B < 1024) s.chunk /= 2;
+    s.nchunk = (Tmax + s.chunk - 1) / s.chunk;
+    return s;
+}
 ProbeWs probe_ws(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_policy& pol) {
-    const int G = Hq / Hkv;
-    const size_t NR = (size_t)G * pol.probe_rows;
-    const int kc = probe_key_chunk(B, Hkv, Tmax);
-    const size_t nchunk = (Tmax + kc - 1) / kc;
+    const ProbeShape s = probe_shape(B, Hq, Hkv, Tmax, pol);
+    const size_t BG = (size_t)B * Hkv;
     ProbeWs w;
     w.part = 0;
-    w.rows = al((size_t)B * Hkv * nchunk * NR * 16);
-    w.total = w.rows + al((size_t)B * Hkv * NR * 16);
+    w.rowref = al(BG * s.nchunk * s.NRp * 16);
+    w.colpart = w.rowref + al(BG * s.NRp * 8);
+    w.total = w.colpart + (s.ngroups > 1 ? al(BG * s.ngroups * (size_t)Tmax * 8) : 0);
     return w;
 }
 
@@ -521,45 +811,54 @@ hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_l
                         int32_t Hkv, int32_t Tmax, bool f16, const hq_policy& pol, float sm_scale,
                         float* col_scores, int32_t* sel_idx, int32_t* sel_count, hq_thresh* thresh, void* ws,
                         hipStream_t s) {
-    const int G = Hq / Hkv;
-    const int NR = G * pol.probe_rows;  // probe_shape_supported(G, probe_rows) holds (host check)
+    // probe_shape_supported(G, probe_rows) holds (host check)
+    const ProbeShape sh = probe_shape(B, Hq, Hkv, Tmax, pol);
     const ProbeWs w = probe_ws(B, Hq, Hkv, Tmax, pol);
     ProbeParams p;
     p.q = static_cast<const uint16_t*>(q_probe);
     p.k = static_cast<const uint16_t*>(k);
     p.seq_lens = seq_lens;
     p.part = reinterpret_cast<double2*>(static_cast<char*>(ws) + w.part);
-    p.rows = reinterpret_cast<double2*>(static_cast<char*>(ws) + w.rows);
+    p.rowref = reinterpret_cast<double*>(static_cast<char*>(ws) + w.rowref);
+    p.colpart = reinterpret_cast<double*>(static_cast<char*>(ws) + w.colpart);
     p.col_scores = col_scores;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.Tmax = Tmax;
     p.R = pol.probe_rows;
-    p.G = G;
-    p.NR = NR;
-    p.chunk = probe_key_chunk(B, Hkv, Tmax);
-    p.nchunk = (Tmax + p.chunk - 1) / p.chunk;
+    p.G = Hq / Hkv;
+    p.NR = sh.NR;
+    p.NRp = sh.NRp;
+    p.ngroups = sh.ngroups;
+    p.nchunk = sh.nchunk;
+    p.chunk = sh.chunk;
     p.sc2 = (double)sm_scale * 1.4426950408889634074;
     {
-        double f = 1.0;  // 14! .. 2!
-        for (int k = 2; k <= 14; ++k) f *= k;
-        for (int i = 0; i < kExpCoefs; ++i) {
-            p.ec[i] = 1.0 / f;
-            f /= 14 - i;
+        // (ln 2)^n / n!
+        const double ln2 = 0.69314718055994530942;
+        double c = 1.0;
+        for (int n = 0; n <= kExpTerms; ++n) {
+            p.ec[n] = c;
+            c = c * ln2 / (n + 1);
         }
     }
-    dim3 g1(p.nchunk, Hkv, B);
-    if (f16) k_probe_rowstats<true><<<g1, 1024, 0, s>>>(p);
-    else k_probe_rowstats<false><<<g1, 1024, 0, s>>>(p);
+    const int threads = 64 * kTilesPerWg;  // 8 waves; waves past the last row tile only move key tiles
+    dim3 g1(sh.nchunk, Hkv * sh.ngroups, B);
+    if (f16) k_probe_rowstats<true><<<g1, threads, 0, s>>>(p);
+    else k_probe_rowstats<false><<<g1, threads, 0, s>>>(p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_probe_rowfinal<<<dim3(Hkv, B), 256, 0, s>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dim3 g2((Tmax + kColKeys - 1) / kColKeys, Hkv, B);
-    if (f16) k_probe_colsum<true><<<g2, 1024, 0, s>>>(p);
-    else k_probe_colsum<false><<<g2, 1024, 0, s>>>(p);
+    dim3 g2((Tmax + kColBlk - 1) / kColBlk, Hkv * sh.ngroups, B);
+    if (f16) k_probe_colsum<true><<<g2, threads, 0, s>>>(p);
+    else k_probe_colsum<false><<<g2, threads, 0, s>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (sh.ngroups > 1) {
+        k_probe_colfinal<<<dim3((Tmax + 255) / 256, Hkv, B), 256, 0, s>>>(p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     k_topk_select<<<dim3(Hkv, B), 1024, 0, s>>>(col_scores, seq_lens, Hkv, Tmax, pol, sel_stride(Tmax, pol),
                                                   sel_idx, sel_count, thresh);
     return hipGetLastError();

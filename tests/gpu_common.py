@@ -8,6 +8,18 @@ import oracle as O
 
 ATOL = 2e-3      # max-abs bar for attention outputs
 RTOL_L2 = 1e-3   # relative-L2 bar for attention outputs
+# Column-score bar: the probe's stated bound, 2 ln2 (logit budget 1.5e-7) +
+# 2^-24 (the final fp32 rounding) ~ 2.7e-7 relative.
+SCORE_RTOL = 3e-7
+
+
+def fp32_scale(D):
+    """The softmax scale 1/sqrt(D) as the library receives it: an fp32 value
+    (its `float sm_scale` argument). The oracle is given this same number, so
+    both sides compute the same softmax; 1/sqrt(128) rounded to fp32 differs
+    from the real number by ~3e-8 relative, which on logits of ~20 (log2
+    units) would alone move column scores by ~3e-7."""
+    return float(np.float32(1 / math.sqrt(D)))
 
 
 def torch_dtype(dtype):
@@ -29,7 +41,7 @@ def ints_to_dev(a):
 def oracle_selection(inp, window=128, keep=(5, 100)):
     """Oracle probe + selection for every (b, g) of a DecodeInputs."""
     sp = inp.spec
-    sm = 1 / math.sqrt(sp.D)
+    sm = fp32_scale(sp.D)
     qp = O.to_f64(inp.q_probe, sp.dtype)
     k = O.to_f64(inp.k, sp.dtype)
     return O.probe_select_batch(qp, k, inp.seq_lens, sm, window, keep[0], keep[1])

@@ -2,7 +2,6 @@
 16-bit rows), hq_decode_attn (attention within max-abs 2e-3, rel-L2 1e-3 of
 the fp64 oracle) and hq_append_kv (bit-exact cache evolution), all through
 the C ABI."""
-import math
 
 import numpy as np
 import pytest
@@ -11,7 +10,7 @@ import oracle as O
 from synth import small_decode_inputs
 from synth.inputs import CONFIGS, make_decode_inputs
 
-from gpu_common import (assert_attn_close, ints_to_dev, oracle_caches, oracle_selection, selection_tensors,
+from gpu_common import (assert_attn_close, fp32_scale, ints_to_dev, oracle_caches, oracle_selection, selection_tensors,
                         to_dev, v_scale)
 from hq_layout import read_cache
 
@@ -117,7 +116,7 @@ def test_quantize_and_decode(name):
     q = to_dev(inp.q, sp.dtype)
     out = hq.decode_attn(cache, q).cpu().numpy()
     torch.cuda.synchronize()
-    ref = O.decode_batch(O.to_f64(inp.q, sp.dtype), ocaches, 1 / math.sqrt(sp.D))
+    ref = O.decode_batch(O.to_f64(inp.q, sp.dtype), ocaches, fp32_scale(sp.D))
     # R20: the max-abs bar is read in units of sigma_V (1 for unit-scale V;
     # about 1e2 for the vscale cases, whose V spans 2^-8 .. 2^8)
     sv = v_scale([c for row in ocaches for c in row])
@@ -131,7 +130,7 @@ def test_quantize_and_decode(name):
             for h in range(sp.Hkv):
                 qg = O.to_f64(inp.q[b, h * G:(h + 1) * G], sp.dtype)
                 ex = O.softmax_attention(qg, O.to_f64(inp.k[b, h, :T], sp.dtype),
-                                         O.to_f64(inp.v[b, h, :T], sp.dtype), 1 / math.sqrt(sp.D))
+                                         O.to_f64(inp.v[b, h, :T], sp.dtype), fp32_scale(sp.D))
                 assert_attn_close(out[b, h * G:(h + 1) * G], ex, f"{name} exact-attention special case")
 
 
@@ -251,7 +250,7 @@ def test_decode_c1_full_size():
     assert int(cache.counts()[0, 0, 2]) == 204 and int(cache.counts()[0, 0, 1]) == 4096 - 204 - 128
     out = hq.decode_attn(cache, to_dev(inp.q, "f16")).cpu().numpy()
     torch.cuda.synchronize()
-    ref = O.decode_batch(O.to_f64(inp.q, "f16"), ocaches, 1 / math.sqrt(128))
+    ref = O.decode_batch(O.to_f64(inp.q, "f16"), ocaches, fp32_scale(128))
     assert_attn_close(out, ref, "decode c1")
 
 
@@ -300,5 +299,5 @@ def test_append_matches_oracle(dtype, W, steps):
     ext.spec, ext.k, ext.v = sp, k_all, v_all
     _check_cache(cache, ext, ocaches)
     out = hq.decode_attn(cache, to_dev(qn[-1], dtype)).cpu().numpy()
-    ref = O.decode_batch(O.to_f64(qn[-1], dtype), ocaches, 1 / math.sqrt(sp.D))
+    ref = O.decode_batch(O.to_f64(qn[-1], dtype), ocaches, fp32_scale(sp.D))
     assert_attn_close(out, ref, f"decode after {steps} appends")

@@ -6,7 +6,6 @@ pair: column scores (relative error) and the selected set (near-tie flips
 counted), INT4 codes / scales / zeros / positions bit-exact, attention within
 the bars. The oracle recomputes each pair completely, from the raw inputs,
 with the GPU's selection (a counted near-tie flip may legitimately differ)."""
-import math
 import time
 
 import numpy as np
@@ -15,7 +14,7 @@ import pytest
 import oracle as O
 from synth.inputs import CONFIGS, make_append_tokens, make_decode_inputs
 
-from gpu_common import assert_attn_close, ints_to_dev, to_dev
+from gpu_common import SCORE_RTOL, assert_attn_close, fp32_scale, ints_to_dev, to_dev
 from hq_layout import read_cache
 from test_gpu_probe import compare_selection
 
@@ -44,11 +43,11 @@ def _oracle_pair(spec, inp, b, g, gsel):
     col, sel, cnt, thr = gsel
     T = int(inp.seq_lens[b])
     G = spec.Hq // spec.Hkv
-    sm = 1 / math.sqrt(spec.D)
+    sm = fp32_scale(spec.D)
     qp = O.to_f64(inp.q_probe[b, g * G:(g + 1) * G], spec.dtype)
     c_or = O.probe_column_scores(qp, O.to_f64(inp.k[b, g:g + 1, :T], spec.dtype), T, sm)[0]
     rel = float((np.abs(col[b, g, :T].astype(np.float64) - c_or) / c_or).max())
-    assert rel < 1e-6, (b, g, rel)
+    assert rel < SCORE_RTOL, (b, g, rel)
     flips = compare_selection(sel[b, g, : cnt[b, g]], int(cnt[b, g]), c_or, T, spec.window, (5, 100))
     idx = sel[b, g, : cnt[b, g]].astype(np.int64)
     assert len(idx) == T * 5 // 100                      # kept = top-5% (+ the 128 window)
@@ -88,7 +87,7 @@ def test_decode_path_full_size(name):
     gc = read_cache(cache)
     del cache
     G = spec.Hq // spec.Hkv
-    sm = 1 / math.sqrt(spec.D)
+    sm = fp32_scale(spec.D)
     flips, worst_rel, recalls, errs = 0, 0.0, [], []
     ref = np.zeros(out.shape)
     t0 = time.time()
@@ -121,7 +120,7 @@ def test_decode_with_appends_128k():
     steps = 64
     kn, vn, qn = make_append_tokens(spec, inp.outlier_channels, steps)
     G = spec.Hq // spec.Hkv
-    sm = 1 / math.sqrt(spec.D)
+    sm = fp32_scale(spec.D)
     kd, vd, qd = to_dev(kn, "bf16"), to_dev(vn, "bf16"), to_dev(qn, "bf16")
     outs = []
     for s in range(steps):

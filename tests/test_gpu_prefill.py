@@ -10,7 +10,6 @@ max-abs 2e-3 and relative L2 1e-3.
 The selected set S is an input of the operator: small cases take the oracle's
 probe selection, edge cases take seeded sets, and the full-size case takes
 what hq_probe_select returned on the device (the same S is fed to both)."""
-import math
 
 import numpy as np
 import pytest
@@ -18,7 +17,7 @@ import pytest
 import oracle as O
 from synth.inputs import CONFIGS, PrefillSpec, make_prefill_inputs
 
-from gpu_common import assert_attn_close, to_dev
+from gpu_common import assert_attn_close, fp32_scale, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +48,7 @@ def oracle_sel(inp, window, keep):
     R = min(sp.probe_rows, sp.T)
     qp = O.to_f64(inp.q[:, :, sp.T - R:], sp.dtype)
     k = O.to_f64(inp.k, sp.dtype)
-    _, sels = O.probe_select_batch(qp, k, np.full(sp.B, sp.T), 1 / math.sqrt(D), window, keep[0], keep[1])
+    _, sels = O.probe_select_batch(qp, k, np.full(sp.B, sp.T), fp32_scale(D), window, keep[0], keep[1])
     return [[s.idx.astype(np.int64) for s in row] for row in sels]
 
 
@@ -114,7 +113,7 @@ def check_int8_stage(inp, ws, heads=None):
 def oracle_prefill_all(inp, sels, window):
     sp = inp.spec
     G = sp.Hq // sp.Hkv
-    sm = 1 / math.sqrt(D)
+    sm = fp32_scale(D)
     qf, kf, vf = (O.to_f64(x, sp.dtype) for x in (inp.q, inp.k, inp.v))
     ref = np.empty((sp.B, sp.Hq, sp.T, D))
     for b in range(sp.B):
@@ -166,7 +165,7 @@ def test_prefill_parity(case):
     if keep == (100, 100):
         # every candidate selected: exact causal softmax attention
         o = out.cpu().numpy()
-        G, sm = Hq // Hkv, 1 / math.sqrt(spec.D)
+        G, sm = Hq // Hkv, fp32_scale(spec.D)
         qf, kf, vf = (O.to_f64(x, dtype) for x in (inp.q, inp.k, inp.v))
         ex = np.zeros_like(o, dtype=np.float64)
         for h in range(Hq):
@@ -237,7 +236,7 @@ def test_prefill_16k_full_size():
     rng = np.random.default_rng(4)
     starts = [T - 64, 96, 8160] + sorted(int(x) for x in rng.integers(0, T - 64, size=13))
     qf, kf, vf = (O.to_f64(x, spec.dtype) for x in (inp.q, inp.k, inp.v))
-    sm = 1 / math.sqrt(D)
+    sm = fp32_scale(D)
     t0 = time.time()
     k8s = [O.int8_block_quantize(kf[0, g]) for g in range(spec.Hkv)]
     refs = np.zeros((spec.Hq, len(starts) * 64, D))

@@ -12,7 +12,7 @@ import oracle as O
 from synth import small_decode_inputs
 from synth.inputs import bf16_bits_from_f32
 
-from gpu_common import ints_to_dev, to_dev
+from gpu_common import SCORE_RTOL, fp32_scale, ints_to_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -41,12 +41,12 @@ def run_probe(inp, window, keep):
     return tuple(t.cpu().numpy() for t in (col, sel, cnt, thr))
 
 
-def check_probe(inp, window=128, keep=(5, 100), rel_tol=1e-6, sample=None, floor=0.0):
+def check_probe(inp, window=128, keep=(5, 100), rel_tol=SCORE_RTOL, sample=None, floor=0.0):
     """floor > 0: oracle scores below it (under the fp32 range the scores are
     returned in) are checked to be at most the floor instead of relatively."""
     sp = inp.spec
     col, sel, cnt, thr = run_probe(inp, window, keep)
-    sm = 1 / math.sqrt(sp.D)
+    sm = fp32_scale(sp.D)
     qp = O.to_f64(inp.q_probe, sp.dtype)
     flips, worst = 0, 0.0
     pairs = sample or [(b, g) for b in range(sp.B) for g in range(sp.Hkv)]
@@ -117,7 +117,7 @@ def test_probe_logit_range_beyond_reference():
     kp = 37.0 * u + rng.standard_normal((151, 128), dtype=np.float32)
     inp.q_probe[...] = bf16_bits_from_f32(qp)
     inp.k[0, 0, 300:451] = bf16_bits_from_f32(kp)
-    sm = 1 / math.sqrt(128)
+    sm = fp32_scale(128)
     logits = O.to_f64(inp.q_probe, "bf16")[0, 0] @ O.to_f64(inp.k, "bf16")[0, 0].T * sm / math.log(2)
     assert logits[:, 300:451].min() - logits[:, :300].max() > 512
     check_probe(inp, 128, (5, 100), floor=1e-30)

@@ -3,7 +3,6 @@ hq_decode_attn with a caller workspace (bit for bit: same kernels, same
 split count) and within the attention bars of the oracle, on two calls in a
 row, the second on a smaller cache (the static scratch keeps the first
 call's partials; nothing of them may leak into the second)."""
-import math
 
 import numpy as np
 import pytest
@@ -11,7 +10,7 @@ import pytest
 import oracle as O
 from synth import small_decode_inputs
 
-from gpu_common import assert_attn_close, ints_to_dev, oracle_caches, oracle_selection, selection_tensors, to_dev
+from gpu_common import assert_attn_close, fp32_scale, ints_to_dev, oracle_caches, oracle_selection, selection_tensors, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +47,7 @@ def test_noalloc_matches_workspace_entry_point():
         torch.cuda.synchronize()
         print(f"call {n + 1}: B={sp.B} Hq={sp.Hq} Hkv={sp.Hkv} T={sp.T}, partials {need} bytes", flush=True)
         assert torch.equal(out, ref_ws), "noalloc output differs from the workspace entry point"
-        ref = O.decode_batch(O.to_f64(inp.q, sp.dtype), ocaches, 1 / math.sqrt(sp.D))
+        ref = O.decode_batch(O.to_f64(inp.q, sp.dtype), ocaches, fp32_scale(sp.D))
         assert_attn_close(out.cpu().numpy(), ref, f"noalloc call {n + 1}")
         # 16-bit output from the same entry point equals the fp32 one rounded once
         o16 = hq.decode_attn_noalloc(cache, q, out_dtype=torch.bfloat16)
