@@ -107,7 +107,7 @@ int32_t hq_sel_stride(int32_t T, const hq_policy* policy);
  * digits of a scaled integer); a per-tile a-posteriori bound on the digits
  * left out is checked and any tile above 1.5e-7 (log2 units) is recomputed
  * in fp64. Softmax normalisers and column sums accumulate in fp64; scores
- * are rounded once to fp32. Each score's relative error is below 2.7e-7
+ * are rounded once to fp32. Each score's relative error is below 2.9e-7
  * (with the observed bounds, ~1e-8 logit error, it is the fp32 rounding).
  * Supported shapes: (Hq/Hkv) * probe_rows must be a multiple of 16 and at
  * most 512; other shapes return HQ_ERR_UNSUPPORTED before any launch.

@@ -31,15 +31,16 @@
 // On the workloads this bound is ~1e-8 in log2 units; a tile whose bound
 // exceeds kLogitBudget has its logits recomputed from the 16-bit inputs in
 // fp64 (exact products, fp64 sums), so every logit carries at most the
-// budget's error. Exponentials are fp64 (a degree-8 series on [-1/2, 1/2]
-// after an exact power-of-two split, relative error < 1e-10); every
+// budget's error. Exponentials are fp64 (a degree-7 series on [-1/2, 1/2]
+// after an exact power-of-two split, relative error < 1.1e-8); every
 // normaliser and column sum accumulates in fp64 relative to integer
 // references, so rescaling by a power of two is exact. Scores are rounded
 // once to fp32. Resulting bound on each returned score, for the softmax with
 // the fp32 scale the caller passes: relative error < 2 ln2 kLogitBudget +
-// 2^-24 + 1e-9 < 2.7e-7, so two columns can change order only where their
-// exact scores differ by less than 5.4e-7 relative. (With the certificate at
-// ~1e-8 the scores come out within a few 1e-8: the fp32 rounding dominates.)
+// 2 x 1.1e-8 (the series in both passes) + 2^-24 < 2.9e-7, so two columns can
+// change order only where their exact scores differ by less than 5.8e-7
+// relative. (With the certificate at ~1e-8 the scores come out within a few
+// 1e-8: the fp32 rounding dominates.)
 //
 // Top-k: one workgroup per (b, g); 4-pass 8-bit radix select on the fp32 bit
 // patterns (scores are >= 0, so bit order = value order) with LDS histograms
@@ -61,7 +62,7 @@ constexpr int kPlanes = 4;         // base-256 digits per value
 constexpr int kDS = kD + 16;       // LDS bytes per key in a digit plane (pad: no bank conflicts)
 constexpr int kColBlk = 256;       // keys per pass-2 workgroup
 constexpr double kLogitBudget = 1.5e-7;  // largest logit error accepted from the digit path (log2 units)
-constexpr int kExpTerms = 8;       // 2^f = sum_{n <= 8} (f ln2)^n / n!, |f| <= 1/2: relative error < 1e-10
+constexpr int kExpTerms = 7;       // 2^f = sum_{n <= 7} (f ln2)^n / n!, |f| <= 1/2: relative error < 1.1e-8
 
 struct ProbeParams {
     const uint16_t* q;     // [B][Hq][R][D]
@@ -73,7 +74,7 @@ struct ProbeParams {
     float* col_scores;     // [B][Hkv][Tmax]
     int32_t B, Hq, Hkv, Tmax, R, G, NR, NRp, ngroups, nchunk, chunk;
     double sc2;            // sm_scale * log2(e)
-    double ec[kExpTerms + 1];  // (ln2)^n / n!, n = 0..8
+    double ec[kExpTerms + 1];  // (ln2)^n / n!, n = 0..7
 };
 
 // Row `row` of the (b, g) probe rows: head g*G + row / R, probe row row % R,
@@ -350,35 +351,10 @@ __device__ inline double tile_error_bound(const QTile& q, const KeyTile& kt, dou
     return (res + om) * asc2 * (1.0 + 0x1p-20);
 }
 
-// The tile's logits in log2 units (z = q . k * sm_scale * log2 e), one
-// element at a time: from the digit sums, or, when the tile's error bound
-// exceeds the budget (a wave-uniform decision), recomputed in fp64 from the
-// 16-bit inputs (exact products, fp64 sums).
-struct TileLogits {
-    DigitSums s;
-    double F;       // 2^(16 - shq - shk) * sm_scale * log2 e of this lane's key
-    bool exact_fallback;
-};
-__device__ inline TileLogits tile_begin(const ProbeParams& p, const QTile& q, const QPlanes& q23, const KeyTile& kt) {
-    TileLogits t;
-    t.s = tile_digit_sums(q, q23, kt);
-    // the same value in every lane; made a scalar so the branches on it are uniform
-    t.exact_fallback = __builtin_amdgcn_readfirstlane((int)!(tile_error_bound(q, kt, fabs(p.sc2)) <= kLogitBudget)) != 0;
-    t.F = __builtin_ldexp(p.sc2, 16 - q.sh - kt.sh[threadIdx.x & 31]);
-    return t;
-}
-// Element i's logit: from the digit sums, or (exact_fallback) the fp64 value
-// whose bits fill_exact() left in hi (low word) and mid (high word).
-__device__ inline double tile_logit(const TileLogits& t, int i) {
-    if (t.exact_fallback)
-        return __builtin_bit_cast(double, ((uint64_t)(uint32_t)t.s.mid[i] << 32) | (uint32_t)t.s.hi[i]);
-    const double u = __builtin_fma((double)t.s.hi[i], 65536.0, (double)t.s.mid[i]);  // exact
-    return __builtin_fma(u, 256.0 * t.F, (double)t.s.lo[i] * t.F);
-}
+// One logit from the 16-bit inputs: exact products, fp64 sum (the fallback;
+// rare, so a few registers and no unrolling keep the common path's occupancy).
 template <bool F16>
-__device__ inline double exact_logit(const ProbeParams& p, int b, int g, const uint16_t* kbase, int key,
-                                                       int row) {
-    // (rare: a few registers, no unrolling, so the common path keeps its occupancy)
+__device__ inline double exact_logit(const ProbeParams& p, int b, int g, const uint16_t* kbase, int key, int row) {
     double acc = 0.0;
     const uint32_t* qr = reinterpret_cast<const uint32_t*>(qrow(p, b, g, row));
     const uint32_t* kr = reinterpret_cast<const uint32_t*>(kbase + (size_t)key * kD);
@@ -391,26 +367,38 @@ __device__ inline double exact_logit(const ProbeParams& p, int b, int g, const u
     return acc * p.sc2;
 }
 
-// The probe row held in element i of this lane, its position, and whether
-// it is a row of the map.
+// The probe row held in element i of this lane (MFMA D layout).
 __device__ inline int elem_row(int rt, int i) { return rt * kRT + 8 * (i >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (i & 3); }
 
-// Pass 1: per (key chunk, row group, g, b): for every probe row of the group,
-// (m, l) over the chunk's keys with m an integer reference and
-// l = sum 2^(z - m). One wave per 32-row tile; the key tiles are converted to
-// digits once per workgroup into LDS (double-buffered) and read by every wave.
-// The tile's exact logits (rare): every element of this lane, stored as fp64
-// bits in the digit-sum registers.
+// The tile's logits in log2 units (z = q . k * sm_scale * log2 e) less a
+// per-element offset, for the 16 elements of this lane: from the digit sums
+// (the offset enters the last fma, one rounding), or, when the tile's error bound
+// exceeds the budget (a wave-uniform decision, so the common path is one
+// straight run over the 16 independent elements), recomputed in fp64 from
+// the 16-bit inputs (exact products, fp64 sums). Elements outside the map
+// (key >= key_end, row >= NR) get 0.
 template <bool F16>
-__device__ inline void fill_exact(const ProbeParams& p, TileLogits& t, int b, int g, const uint16_t* kbase, int key,
-                                  int key_end, int rt) {
+__device__ inline void tile_logits(const ProbeParams& p, const QTile& q, const QPlanes& q23, const KeyTile& kt,
+                                   int b, int g, const uint16_t* kbase, int key, int key_end, int rt,
+                                   const double (&off)[16], double (&z)[16]) {
+    const DigitSums s = tile_digit_sums(q, q23, kt);
+    const bool fallback =
+        __builtin_amdgcn_readfirstlane((int)!(tile_error_bound(q, kt, fabs(p.sc2)) <= kLogitBudget)) != 0;
+    if (!fallback) {
+        // z - off = F (65536 hi + mid) 256 + (F lo - off), F = 2^(16 - shq - shk) sm_scale log2 e
+        const double F = __builtin_ldexp(p.sc2, 16 - q.sh - kt.sh[threadIdx.x & 31]);
+        const double F256 = 256.0 * F;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int row = elem_row(rt, i);
-        const double z = (key < key_end && row < p.NR) ? exact_logit<F16>(p, b, g, kbase, key, row) : 0.0;
-        const uint64_t u = __builtin_bit_cast(uint64_t, z);
-        t.s.hi[i] = (int)(uint32_t)u;
-        t.s.mid[i] = (int)(uint32_t)(u >> 32);
+        for (int i = 0; i < 16; ++i) {
+            const double u = __builtin_fma((double)s.hi[i], 65536.0, (double)s.mid[i]);  // exact
+            z[i] = __builtin_fma(u, F256, __builtin_fma((double)s.lo[i], F, -off[i]));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = elem_row(rt, i);
+            z[i] = (key < key_end && row < p.NR) ? exact_logit<F16>(p, b, g, kbase, key, row) - off[i] : 0.0;
+        }
     }
 }
 
@@ -443,6 +431,16 @@ __device__ inline uint32_t tile_mask(const ProbeParams& p, int T, int rt, uint32
     return mk;
 }
 
+constexpr double kZeros[16] = {};
+
+// Whether every element of the wave's tile is in the map (wave-uniform): then
+// the element loops need no mask.
+__device__ inline bool tile_full(uint32_t mk) { return __builtin_amdgcn_ballot_w64(mk != 0xFFFFu) == 0; }
+
+// Pass 1: per (key chunk, row group, g, b): for every probe row of the group,
+// (m, l) over the chunk's keys with m an integer reference and
+// l = sum 2^(z - m). One wave per 32-row tile; the key tiles are converted to
+// digits once per workgroup into LDS (double-buffered) and read by every wave.
 template <bool F16>
 __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
     __shared__ ProbeSmem sm;
@@ -478,23 +476,35 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
         const int key0 = key_lo + kKT * t;
         const uint4 nxt = load_keys(kbase, key0 + kKT, t + 1 < ntile ? key_hi : 0);  // next tile, in flight
         if (active) {
-            TileLogits tl = tile_begin(p, q, sm.q23[wave], sm.kt[cur]);
             const int key = key0 + (lane & 31);
-            if (tl.exact_fallback) fill_exact<F16>(p, tl, b, g, kbase, key, key_hi, rt);
+            double z[16];
+            tile_logits<F16>(p, q, sm.q23[wave], sm.kt[cur], b, g, kbase, key, key_hi, rt, kZeros, z);
             const uint32_t mk = tile_mask(p, T, rt, rowmk, key0, key_hi);
+            // move a reference up to ceil(z) where a valid logit exceeds it by
+            // more than 256 (rare; always at a row's first valid logit): an
+            // exact power-of-two rescale of l
+            bool move = false;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const bool v = (mk >> i) & 1u;
-                const double z = tile_logit(tl, i);
-                if (v && z > (double)m[i] + 256.0) {
-                    // move the reference up to ceil(z) (rare; the first valid
-                    // logit of the row always): an exact power-of-two rescale
-                    const int mn = (int)__builtin_ceil(fmax(fmin(z, 2.0e9), -2.0e9));
-                    l[i] = m[i] == INT_MIN ? 0.0 : __builtin_ldexp(l[i], m[i] - mn);
-                    m[i] = mn;
+            for (int i = 0; i < 16; ++i) move |= ((mk >> i) & 1u) && z[i] > (double)m[i] + 256.0;
+            if (__builtin_amdgcn_ballot_w64(move) != 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (((mk >> i) & 1u) && z[i] > (double)m[i] + 256.0) {
+                        const int mn = (int)__builtin_ceil(fmax(fmin(z[i], 2.0e9), -2.0e9));
+                        l[i] = m[i] == INT_MIN ? 0.0 : __builtin_ldexp(l[i], m[i] - mn);
+                        m[i] = mn;
+                    }
                 }
-                const double e = exp2_d(z - (double)m[i], p.ec);
-                l[i] += v ? e : 0.0;
+            }
+            if (tile_full(mk)) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) l[i] += exp2_d(z[i] - (double)m[i], p.ec);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const double e = exp2_d(z[i] - (double)m[i], p.ec);
+                    l[i] += ((mk >> i) & 1u) ? e : 0.0;
+                }
             }
         }
         if (t + 1 < ntile) store_keys<F16>(nxt, sm.kt[cur ^ 1]);
@@ -589,14 +599,19 @@ __global__ __launch_bounds__(512) void k_probe_colsum(ProbeParams p) {
         const uint4 nxt = load_keys(kbase, key0 + kKT, t + 1 < ntile ? key_hi : 0);  // next tile, in flight
         double acc = 0.0;
         if (active) {
-            TileLogits tl = tile_begin(p, q, sm.q23[wave], sm.kt[cur]);
             const int key = key0 + (lane & 31);
-            if (tl.exact_fallback) fill_exact<F16>(p, tl, b, g, kbase, key, key_hi, rt);
+            double d[16];  // z - m'
+            tile_logits<F16>(p, q, sm.q23[wave], sm.kt[cur], b, g, kbase, key, key_hi, rt, ref, d);
             const uint32_t mk = tile_mask(p, T, rt, rowmk, key0, key_hi);
+            if (tile_full(mk)) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const double e = exp2_d(tile_logit(tl, i) - ref[i], p.ec);
-                acc += ((mk >> i) & 1u) ? e : 0.0;
+                for (int i = 0; i < 16; ++i) acc += exp2_d(d[i], p.ec);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const double e = exp2_d(d[i], p.ec);
+                    acc += ((mk >> i) & 1u) ? e : 0.0;
+                }
             }
             acc += __shfl_xor(acc, 32);
         }
