@@ -134,6 +134,15 @@ __device__ inline float wave_sum_fast(float v) {
     return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
+// Sum over the four 16-lane rows: lane l gets v(l) + v(l^32) + v(l^16) +
+// v(l^48) (two swaps between halves / rows, no LDS traffic).
+__device__ inline float rows_sum4(float v) {
+    auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+    auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+}
+
 // Orders this wave's LDS writes before its later LDS reads (other lanes'
 // data). LDS operations of one wave execute in order, so this only has to
 // stop the compiler from reordering; it must not wait for global loads.
@@ -632,16 +641,46 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
     // o = 2^E * (D - sum(bias * w)) + sum(p z) on INT4 tiles, 2^E * acc on
     // 16-bit tiles.
     const float unit = E <= -1000 ? 0.f : __builtin_ldexpf(1.0f, E);
-#pragma unroll
-    for (int h = 0; h < G; ++h) l[h] = wave_sum_fast(l[h]);
     if constexpr (MODE == 0) {
+        // The 9G per-lane sums (l[h], zacc[h][grp], wsb[h][grp]) over the
+        // wave: two swaps leave 16 partials of each in lanes 0..15, which go
+        // through this wave's QK transpose area (free after the last tile);
+        // lane k < 9G then adds the 16 partials of sum k (fewer cross-lane
+        // steps than a 64-lane reduction per sum).
+        constexpr int NV = 9 * G, RS = 17;
+        static_assert(NV * RS + NV <= 4 * NHB * 64 * 4, "reduction area exceeds the wave's QK transpose area");
+        float* red = reinterpret_cast<float*>(y_w);
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h) {
+            const float vl = rows_sum4(l[h]);
+            if (lane < 16) red[h * RS + lane] = vl;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                zacc[h][i] = wave_sum_fast(zacc[h][i]);
-                wsb[h][i] = wave_sum_fast(wsb[h][i]);
+                const float vz = rows_sum4(zacc[h][i]), vw = rows_sum4(wsb[h][i]);
+                if (lane < 16) {
+                    red[(G + 4 * h + i) * RS + lane] = vz;
+                    red[(5 * G + 4 * h + i) * RS + lane] = vw;
+                }
             }
+        }
+        lds_fence();
+        if (lane < NV) {
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s += red[lane * RS + j];
+            red[NV * RS + lane] = s;
+        }
+        lds_fence();
+        const float* sums = red + NV * RS;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            l[h] = sums[h];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                zacc[h][i] = sums[G + 4 * h + i];
+                wsb[h][i] = sums[5 * G + 4 * h + i];
+            }
+        }
         const int hl = lane & 15;
         if (hl < G) {
 #pragma unroll
@@ -664,12 +703,11 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
         }
     } else {
 #pragma unroll
+        for (int h = 0; h < G; ++h) l[h] = wave_sum_fast(l[h]);
+#pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                acc[h][i] += __shfl_xor(acc[h][i], 16);
-                acc[h][i] += __shfl_xor(acc[h][i], 32);
-            }
+            for (int i = 0; i < 8; ++i) acc[h][i] = rows_sum4(acc[h][i]);
         if (lane < 16) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
