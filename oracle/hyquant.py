@@ -30,8 +30,9 @@ head h // G.
 Parity status: every function below is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (closed forms, invariants, special cases that
 reduce to textbook/library attention, brute force on tiny inputs), except the
-diagnostics at the end, which are "parity unpinned" (they measure, they do not
-define).
+diagnostics at the end (kept-mass coverage, the uniform INT8 reference line's
+attention), which are "parity unpinned" as measurements: they measure, they
+do not define the method. The INT8 quantizer itself is pinned.
 """
 from __future__ import annotations
 
@@ -525,3 +526,34 @@ def kept_mass_coverage(q_group: np.ndarray, K: np.ndarray, mode: np.ndarray, sm_
     p = np.exp(logits - logits.max(axis=-1, keepdims=True))
     p /= p.sum(axis=-1, keepdims=True)
     return float(p[:, mode != MODE_INT4].sum(axis=-1).mean())
+
+
+def int8_token_quantize(x: np.ndarray):
+    """Uniform per-token INT8 of a [T][D] block (O9 reference line).
+
+    [HQ-news] "Why preserve selected positions?": the authors compare the
+    hybrid cache's operator-level error with a uniform 8-bit cache. The pages
+    do not give that cache's format; reading (the plainest symmetric one):
+    per token, s = fp32_rne(max_c |x[t][c]| / 127); code = clamp(rint_even(
+    fp32 x / s), -127, 127); 0 when s == 0. Decisions in fp32, like the other
+    quantizers here.
+
+    x: [T][D] float64 exact values. Returns (codes int8 [T][D], s float32 [T]).
+    """
+    xf = x.astype(np.float32)
+    s = (np.abs(xf).max(axis=1) / np.float32(127.0)).astype(np.float32)
+    codes = np.zeros(x.shape, dtype=np.int8)
+    nz = s > 0
+    codes[nz] = np.clip(np.rint(xf[nz] / s[nz, None]), -127, 127).astype(np.int8)
+    return codes, s
+
+
+def uniform_int8_attention(q_group: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float) -> np.ndarray:
+    """Decode attention over a cache that holds every token of K and V in
+    uniform per-token INT8 (the dequantized values code * s), fp64 softmax.
+    A diagnostic reference line (O9), not a path of the method."""
+    kc, ks = int8_token_quantize(K)
+    vc, vs = int8_token_quantize(V)
+    Kh = kc.astype(np.float64) * ks.astype(np.float64)[:, None]
+    Vh = vc.astype(np.float64) * vs.astype(np.float64)[:, None]
+    return softmax_attention(q_group, Kh, Vh, sm_scale)

@@ -154,3 +154,66 @@ def test_int8_zero_block():
     codes, s = O.int8_block_quantize(x)
     assert s[0] == 0 and np.all(codes[:64] == 0)
     assert codes[64, 0] == 127 and float(s[1]) == float(np.float32(1) / np.float32(127))
+
+
+# ---- O9 reference line: uniform per-token INT8 ----
+
+def test_int8_token_closed_form_and_exact_dequant():
+    """A token whose values are m * 2^e with max |m| = 127 has s = 2^e
+    exactly and codes m: the dequantized token equals the input."""
+    rng = np.random.default_rng(91)
+    m = rng.integers(-127, 128, size=(5, 128))
+    m[:, 7] = 127 * np.array([1, -1, 1, -1, 1])  # the maximum magnitude of each token
+    e = np.array([-3, 0, 2, -10, 5])
+    x = m * np.ldexp(1.0, e)[:, None]
+    codes, s = O.int8_token_quantize(x)
+    assert np.array_equal(s.astype(np.float64), np.ldexp(1.0, e))
+    assert np.array_equal(codes.astype(np.int64), m)
+    assert np.array_equal(codes.astype(np.float64) * s.astype(np.float64)[:, None], x)
+
+
+def test_int8_token_half_integer_quotients_round_to_even():
+    """s = 1 (max |x| = 127): quotients k + 0.5 go to the even neighbour."""
+    x = np.zeros((1, 128))
+    x[0, 0] = 127.0
+    x[0, 1:7] = [2.5, 3.5, -2.5, -3.5, 0.5, 126.5]
+    codes, s = O.int8_token_quantize(x)
+    assert s[0] == 1.0
+    assert codes[0, :7].tolist() == [127, 2, 4, -2, -4, 0, 126]
+
+
+def test_int8_token_error_bound_and_zero_token():
+    """|x - code * s| <= s / 2 + 2^-23 |x| for 16-bit inputs (exact in
+    fp32), per token: the fp32 quotient x / s can move a value that sits on a
+    half-integer by 2^-24 relative (x = max / 2 lands there exactly); an
+    all-zero token has s = 0 and codes 0."""
+    rng = np.random.default_rng(92)
+    x = O.to_f64(bf16_bits_from_f32(rng.standard_normal((64, 128)).astype(np.float32) * 3.0), "bf16")
+    x[5] = 0.0
+    codes, s = O.int8_token_quantize(x)
+    err = np.abs(x - codes.astype(np.float64) * s.astype(np.float64)[:, None])
+    assert np.all(err <= s.astype(np.float64)[:, None] / 2 + np.ldexp(np.abs(x), -23))
+    assert s[5] == 0 and not codes[5].any()
+    # brute force: each code is a nearest of the 255 levels to the fp32
+    # quotient (ties: the even one)
+    lv = np.arange(-127, 128, dtype=np.float64)
+    for t in (0, 17, 63):
+        qt = (x[t].astype(np.float32) / s[t]).astype(np.float64)
+        d = np.abs(qt[:, None] - lv[None, :])
+        best = d.min(axis=1)
+        ok = np.abs(qt - codes[t].astype(np.float64)) == best
+        assert ok.all()
+
+
+def test_uniform_int8_attention_reduces_to_softmax_attention():
+    """When every token is exactly representable the INT8 reference line is
+    plain softmax attention; otherwise it is within a small error of it."""
+    rng = np.random.default_rng(93)
+    m = rng.integers(-127, 128, size=(300, 128)).astype(np.float64)
+    m[:, 0] = 127
+    K = m * 0.03125
+    V = np.roll(m, 3, axis=1) * 0.0625
+    q = rng.standard_normal((4, 128))
+    a = O.uniform_int8_attention(q, K, V, 0.088)
+    b = O.softmax_attention(q, K, V, 0.088)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
