@@ -386,18 +386,34 @@ def decode_configs(args):
     print(json.dumps({"workloads": decode_workloads(args), "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 def decode_ablation(args):
-    """Decode output error of each cache policy against the same decode on a
-    cache that keeps every position in bf16 (ratio 100%), on the seeded 8B GQA
-    inputs (outlier K channels, planted vertical lines) at T = 1K..32K. Every
-    output comes from hq_decode_attn; the error is of the fp32 outputs."""
+    """Decode output error of each cache policy on the seeded 8B GQA inputs
+    (outlier K channels, planted vertical lines) at T = 1K..32K: all-INT4,
+    INT4 + bf16 window, the retained-ratio sweep (1, 2, 5, 10, 20% + 128
+    window), the window sweep (64, 128, 256, 512 at 5%), every position in
+    bf16. Each policy's output comes from hq_decode_attn on its own cache
+    (probe, select, quantize, decode: all kernels). The errors are taken
+    against exact softmax attention over the bf16 K/V in fp64, and two
+    measurements ride along, computed with a few lines of plain torch on the
+    device (diagnostics, not paths of the method): a uniform per-token INT8
+    cache's output (s = max|x| / 127 per token, round half to even, K and V)
+    and each kept set's share of the decode query's exact attention mass."""
     import dataclasses
     import torch
     import kv_cache_amd as hq
     from synth.inputs import CONFIGS, make_append_tokens, make_decode_inputs
     dev = "cuda:0"
-    policies = [("int4_all", hq.Policy(0, 100, 0, 64)), ("int4_window128", hq.Policy(0, 100, 128, 64)),
-                ("hybrid_1pct", hq.Policy(1, 100, 128, 64)), ("hybrid_5pct", hq.Policy(5, 100, 128, 64)),
-                ("bf16_all", hq.Policy(100, 100, 128, 64))]
+    policies = [("int4_all", hq.Policy(0, 100, 0, 64)), ("int4_window128", hq.Policy(0, 100, 128, 64))]
+    policies += [(f"hybrid_{r}pct", hq.Policy(r, 100, 128, 64)) for r in (1, 2, 5, 10, 20)]
+    policies += [(f"hybrid_5pct_w{w}", hq.Policy(5, 100, w, 64)) for w in (64, 256, 512)]
+    policies += [("bf16_all", hq.Policy(100, 100, 128, 64))]
+
+    def int8_token(x):  # [..., T, D] fp64 exact -> dequantized uniform per-token INT8 (fp32 decisions)
+        xf = x.float()
+        s = xf.abs().amax(dim=-1, keepdim=True) / 127.0
+        c = torch.where(s > 0, torch.round(xf / torch.where(s > 0, s, torch.ones_like(s))).clamp(-127, 127),
+                        torch.zeros_like(xf))
+        return c.double() * s.double()
+
     rows = []
     for T in (1024, 4096, 16384, 32768):
         spec = dataclasses.replace(CONFIGS["c2_decode_8b_32k"], name=f"decode_8b_gqa_b16_{T}", T=T)
@@ -406,26 +422,57 @@ def decode_ablation(args):
         k, v = _dev16(inp.k, "bf16", dev), _dev16(inp.v, "bf16", dev)
         qp, q = _dev16(inp.q_probe, "bf16", dev), _dev16(qn[0], "bf16", dev)
         lens = torch.from_numpy(inp.seq_lens).to(dev)
-        outs = {}
+        B, Hkv, G, D = spec.B, spec.Hkv, spec.Hq // spec.Hkv, spec.D
+        sm = 1.0 / math.sqrt(D)
+        # exact attention, the INT8 line and the attention probabilities, per batch row
+        exact = torch.empty((B, spec.Hq, D), dtype=torch.float64, device=dev)
+        int8 = torch.empty_like(exact)
+        probs = []
+        for b in range(B):
+            qb = q[b].double().view(Hkv, G, D)
+            Kb, Vb = k[b].double(), v[b].double()
+            p = torch.softmax(qb @ Kb.transpose(1, 2) * sm, dim=-1)      # [Hkv][G][T]
+            exact[b] = (p @ Vb).view(spec.Hq, D)
+            p8 = torch.softmax(qb @ int8_token(Kb).transpose(1, 2) * sm, dim=-1)
+            int8[b] = (p8 @ int8_token(Vb)).view(spec.Hq, D)
+            probs.append(p.sum(dim=1) / G)                                # [Hkv][T] mean over the G heads
+        row = {"T": T}
+
+        def err(o):
+            d = o - exact
+            return {"mse": float((d * d).mean()), "rel_l2": float(d.norm() / exact.norm()),
+                    "max_abs": float(d.abs().max())}
+
         for name, pol in policies:
-            cache = hq.HybridCache(spec.B, spec.Hkv, T, T, torch.bfloat16, dev, pol)
+            cache = hq.HybridCache(B, Hkv, T, T, torch.bfloat16, dev, pol)
             col, sel, cnt, thr = hq.probe_select(qp, k, lens, pol)
             hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
-            outs[name] = hq.decode_attn(cache, q).double().cpu()
+            out = hq.decode_attn(cache, q).double()
+            e = err(out)
+            # kept set = the selection + the last W positions
+            cov = []
+            for b in range(B):
+                m = torch.zeros((Hkv, T), dtype=torch.bool, device=dev)
+                for g in range(Hkv):
+                    n = int(cnt[b, g])
+                    m[g, sel[b, g, :n].long()] = True
+                m[:, max(0, T - pol.window):] = True
+                cov.append((probs[b] * m).sum(dim=-1))
+            e["kept_mass"] = float(torch.stack(cov).mean())
+            row[name] = e
             del cache
             torch.cuda.empty_cache()
-        ref = outs["bf16_all"]
-        row = {"T": T}
-        for name, _ in policies[:-1]:
-            d = outs[name] - ref
-            row[name] = {"mse": float((d * d).mean()), "rel_l2": float(d.norm() / ref.norm()),
-                         "max_abs": float(d.abs().max())}
+        row["uniform_int8"] = err(int8)
         rows.append(row)
-        print(f"# ablation T={T}: {row}", file=sys.stderr, flush=True)
-        del k, v, inp
+        print(f"# ablation T={T}: " + ", ".join(f"{n} {row[n]['rel_l2']:.3g}" for n in row if n != "T"),
+              file=sys.stderr, flush=True)
+        del k, v, inp, probs, exact, int8
         torch.cuda.empty_cache()
-    print(json.dumps({"ablation": "decode_8b_gqa_b16 (B=16, 32/8 heads, bf16 inputs); error of the fp32 decode "
-                                  "output against the all-bf16 cache", "rows": rows}), flush=True)
+    print(json.dumps({"ablation": "decode_8b_gqa_b16 (B=16, 32/8 heads, bf16 inputs); error of each policy's fp32 "
+                                  "decode output (hq_decode_attn on its own cache) and of a uniform per-token INT8 "
+                                  "cache (plain torch) against exact fp64 attention over the bf16 K/V; kept_mass: "
+                                  "share of the decode query's exact attention mass on the kept set (selection + "
+                                  "window), mean over (b, KV head) of the G heads' mean", "rows": rows}), flush=True)
 
 
 def sweep(args):
