@@ -56,6 +56,8 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTps16 = 16;  // 16-bit tiles per split
 
@@ -150,15 +152,6 @@ __device__ inline void lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
-}
-
-// v[idx] for a lane-dependent idx < N without dynamic register indexing.
-template <int N>
-__device__ inline float pick(const float (&v)[N], int idx) {
-    float r = v[0];
-#pragma unroll
-    for (int i = 1; i < N; ++i) r = idx == i ? v[i] : r;
-    return r;
 }
 
 __device__ inline void store_out(void* out, int dt, size_t i, float r) {
@@ -540,11 +533,22 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
             }
         }
     } else {
-    // The query's words are read per tile with wave-uniform (scalar) loads.
-    // This barrier keeps them ordinary loads that the compiler reloads per
-    // tile rather than hoisting all 64*G of them out of the loop, which would
-    // not fit in scalar registers.
-    __syncthreads();
+    // QK of a 16-bit tile on the matrix cores: D[h][t] = sum_c q_h[c] k_t[c]
+    // with v_mfma_f32_16x16x32 on the 16-bit inputs (exact products, fp32
+    // accumulation): A = the query, lane l holding head l % 16 (zero rows for
+    // heads >= G) and channels 32 ks + 8 (l / 16) .. + 7 of K-step ks, loaded
+    // once; B = the tile's K rows, lane l holding those channels of token
+    // 16 nb + l % 16 (one 16-byte load each). D of token block nb: lane l
+    // (l < 16) holds heads 0..3 of token 16 nb + l; three lane swaps per head
+    // gather the four blocks into the lane = token layout of the softmax.
+    intx4 qa16[4];
+    {
+        const int hrow = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qa16[ks] = hrow < G ? *reinterpret_cast<const intx4*>(qn + hrow * 64 + 16 * ks + 4 * (lane >> 4))
+                                : intx4{0, 0, 0, 0};
+    }
     uint4 kk16[16], vv16[16];
     for (int v = v0 + wave; v < v1; v += kWaves) {
         float lg[G];
@@ -562,23 +566,38 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
             // every K and V load of the tile is issued up front: one memory
             // latency per tile (V does not depend on the scores)
 #pragma unroll
-            for (int c = 0; c < 16; ++c) kk16[c] = *reinterpret_cast<const uint4*>(kt + k16_off(lane, c));
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    kk16[4 * nb + ks] =
+                        *reinterpret_cast<const uint4*>(kt + k16_off(16 * nb + (lane & 15), 4 * ks + (lane >> 4)));
 #pragma unroll
             for (int i = 0; i < 16; ++i) vv16[i] = *reinterpret_cast<const uint4*>(vt + i * 1024 + lane * 16);
+            floatx4 d[4];
 #pragma unroll
-            for (int h = 0; h < G; ++h) lg[h] = 0.f;
+            for (int nb = 0; nb < 4; ++nb) {
+                d[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const uint4 kk = kk16[c];
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const uint32_t* qh = qn + h * 64 + 4 * c;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) lg[h] = dot2<F16>(u4w(kk, i), qh[i], lg[h]);
+                for (int ks = 0; ks < 4; ++ks) {
+                    if constexpr (F16)
+                        d[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, qa16[ks]),
+                                                                      __builtin_bit_cast(halfx8, kk16[4 * nb + ks]),
+                                                                      d[nb], 0, 0, 0);
+                    else
+                        d[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa16[ks]),
+                                                                       __builtin_bit_cast(bf16x8, kk16[4 * nb + ks]),
+                                                                       d[nb], 0, 0, 0);
                 }
             }
 #pragma unroll
-            for (int h = 0; h < G; ++h) lg[h] = valid ? lg[h] * p.scale2 : -INFINITY;
+            for (int h = 0; h < G; ++h) {
+                // rows 1 of blocks 0 / 2 <- rows 0 of blocks 1 / 3, then the
+                // upper half of the first <- the lower half of the second
+                const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[0][h]), __float_as_uint(d[1][h]), false, false);
+                const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[2][h]), __float_as_uint(d[3][h]), false, false);
+                const auto s = __builtin_amdgcn_permlane32_swap(s01[0], s23[0], false, false);
+                lg[h] = valid ? __uint_as_float(s[0]) * p.scale2 : -INFINITY;
+            }
         }
 
         // ----------------------------- online softmax (wave-uniform update)
@@ -673,25 +692,16 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
         lds_fence();
         const float* sums = red + NV * RS;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            l[h] = sums[h];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                zacc[h][i] = sums[G + 4 * h + i];
-                wsb[h][i] = sums[5 * G + 4 * h + i];
-            }
-        }
+        for (int h = 0; h < G; ++h) l[h] = sums[h];
+        // the lane's head hl reads its group sums straight from LDS (a
+        // lane-indexed pick from registers is promoted to a per-thread LDS
+        // array, whose address needs the workgroup size from the dispatch
+        // packet: a long scalar-load stall per wave)
         const int hl = lane & 15;
         if (hl < G) {
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
-                float zs[G], ws_[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    zs[h] = zacc[h][grp];
-                    ws_[h] = wsb[h][grp];
-                }
-                const float z = pick(zs, hl), wb = pick(ws_, hl);
+                const float z = sums[G + 4 * hl + grp], wb = sums[5 * G + 4 * hl + grp];
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int mb = 2 * grp + half;
