@@ -19,7 +19,10 @@ the cache build is reported as decode_us_full_step; the once-per-prompt rows
 (probe, quantize, prefill) are reported beside it. After the timed steps the
 other decode workloads (1-head 4K warm and cold, 128K with 64 appends, the
 ragged 70B-like shape) and the 1K..32K context sweep are timed the same way
-and reported under "workloads" and "sweep".
+and reported under "workloads" and "sweep"; each of them also reports
+decode_us_graph, the device time of one decode with no host work between
+calls (20 calls captured in a HIP graph and replayed), which at short contexts
+is well below the per-call time (the host's enqueue of a call takes ~12 us).
 
 Prints ONE JSON line: the decode time and bandwidth, the prefill time and
 TFLOP/s, a roofline object for each, the other decode workloads and the
@@ -294,6 +297,38 @@ def cpu_baseline_prefill(pin, sel_idx, sel_cnt, budget_s=8.0):
                       f"({t_rows:.1f} s) plus one head's INT8 stage, scaled to {sp.T} rows x {sp.Hq} heads"}
 
 
+def _graph_decode_us(hq, cache, q, out, n=20, reps=10):
+    """Device time of one decode with no host work between calls: n calls of
+    hq_decode_attn_noalloc captured in a HIP graph, replayed `reps` times
+    (microseconds per call). The first replay is checked bit for bit against
+    the eager call's output."""
+    import torch
+    hq.decode_attn_noalloc(cache, q, None, out)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(n):
+                hq.decode_attn_noalloc(cache, q, None, out)
+    torch.cuda.synchronize()
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref):
+        raise RuntimeError("graph-replayed decode differs from the eager call")
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    del g
+    return s.elapsed_time(e) * 1e3 / (n * reps)
+
+
 def _time_decode(hq, cache, knew, vnew, q, out, steps, warmup):
     """Append + decode per step on one built cache; the Timer of the calls."""
     import torch
@@ -351,6 +386,9 @@ def _decode_workload(hq, name, steps, warmup, cold_mib=0):
            "steps": steps, "bytes": by, "TBps": round(by / (dus * 1e-6) / 1e12, 3),
            "frac_of_peak": round(by / (dus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
            "kept_by_append_rule": int((cache.counts()[..., 2] - keep0).sum().item())}
+    gus = _graph_decode_us(hq, cache, qd[n - 1], out)
+    rec["decode_us_graph"] = round(gus, 2)
+    rec["frac_of_peak_graph"] = round(by / (gus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
     if spec.ragged_min is not None:
         rec["seq_lens"] = [int(x) for x in inp.seq_lens]
     if cold_mib:
@@ -504,6 +542,7 @@ def sweep(args):
         hq.quantize_kv(cache, k, v, lens, sel, cnt, col, thr)
         out = torch.empty((spec.B, spec.Hq, spec.D), dtype=torch.float32, device=dev)
         tm = _time_decode(hq, cache, knew, vnew, q, out, args.steps, args.warmup)
+        gus = _graph_decode_us(hq, cache, q, out)
         sink = hq.diag_read_int4(cache)
         for _ in range(10):
             tm("diag", hq.diag_read_int4, cache, sink)
@@ -513,6 +552,8 @@ def sweep(args):
         dms = tm.ms("decode_attn")
         i4 = int((counts[..., 1] * 160).sum())
         rows.append({"T": T, "decode_us": round(dms * 1e3, 2), "decode_us_p10_p50_p90": tm.pct("decode_attn", 1e3),
+                     "decode_us_graph": round(gus, 2),
+                     "frac_of_peak_graph": round(by / (gus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                      "bytes": by, "TBps": round(by / (dms * 1e-3) / 1e12, 3),
                      "frac_of_peak": round(by / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "int4_stream_TBps": round(i4 / (tm.ms("diag") * 1e-3) / 1e12, 3)})
