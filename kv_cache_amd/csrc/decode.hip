@@ -136,6 +136,25 @@ __device__ inline float wave_sum_fast(float v) {
     return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
+// fp64 sum over each 16-lane row, every lane gets its row's sum: DPP moves
+// on both words of the double (quad swaps, then the half-row and row
+// mirrors), no LDS round trips.
+template <int CTRL>
+__device__ inline double dpp_d(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)u, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(u >> 32), (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ inline double row16_sum_d(double v) {
+    v += dpp_d<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_d<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_d<0x141>(v);  // row_half_mirror
+    v += dpp_d<0x140>(v);  // row_mirror
+    return v;
+}
+
 // Sum over the four 16-lane rows: lane l gets v(l) + v(l^32) + v(l^16) +
 // v(l^48) (two swaps between halves / rows, no LDS traffic).
 __device__ inline float rows_sum4(float v) {
@@ -332,13 +351,9 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
                 qa32[hb * 1024 + ks * 256 + (4 * ks + (h & 3) + 16 * ((lane & 15) >> 2)) * 4 + (lane & 3)] =
                     h0 | (h1 << 16);
                 const double y0 = (double)f16_to_f32(h0), y1 = (double)f16_to_f32(h1);
-                double sq = y0 + y1;
-                double sb = y0 * (double)elem_bias((2 * lane) & 7) + y1 * (double)elem_bias((2 * lane + 1) & 7);
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    sq += __shfl_xor(sq, o);
-                    sb += __shfl_xor(sb, o);
-                }
+                const double sq = row16_sum_d(y0 + y1);
+                const double sb = row16_sum_d(y0 * (double)elem_bias((2 * lane) & 7) +
+                                              y1 * (double)elem_bias((2 * lane + 1) & 7));
                 if ((lane & 15) == 0) {
                     sm.qc[(hb * 4 + ks) * 8 + 2 * (h & 3)] = (float)sb;
                     sm.qc[(hb * 4 + ks) * 8 + 2 * (h & 3) + 1] = (float)sq;
