@@ -557,3 +557,53 @@ def uniform_int8_attention(q_group: np.ndarray, K: np.ndarray, V: np.ndarray, sm
     Kh = kc.astype(np.float64) * ks.astype(np.float64)[:, None]
     Vh = vc.astype(np.float64) * vs.astype(np.float64)[:, None]
     return softmax_attention(q_group, Kh, Vh, sm_scale)
+
+
+# ---------------------------------------------------------------------------
+# O10: re-probing the hybrid cache from decode-time queries (a "next" step)
+# ---------------------------------------------------------------------------
+
+
+def bf16_rne(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 with round-half-to-even, returned as float64 (finite inputs)."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def reprobe_keys(cache: HybridCache, dtype: str) -> np.ndarray:
+    """The keys as a re-probe over the hybrid cache sees them (O10).
+
+    [HQ-wiki] "Gaps": whether the vertical lines found on the prompt persist
+    through decoding is left open; re-probing from decode-time attention
+    tracks it. The probe takes 16-bit keys; reading: kept and window rows are
+    the stored 16-bit values, INT4 rows are dequantized in fp32,
+    x = code * s + z with one rounding (code * s is exact: 4 bits times an
+    fp16), then rounded to the cache's 16-bit type with round half to even.
+
+    Returns [T][D] float64 (exact 16-bit values)."""
+    D = cache.k.shape[-1]
+    s32 = np.repeat(cache.k_s.astype(np.float32), INT4_GROUP, axis=-1).reshape(cache.k_codes.shape)
+    z32 = np.repeat(cache.k_z.astype(np.float32), INT4_GROUP, axis=-1).reshape(cache.k_codes.shape)
+    x32 = (cache.k_codes.astype(np.float32) * s32 + z32).astype(np.float32)
+    kq = bf16_rne(x32) if dtype == "bf16" else x32.astype(np.float16).astype(np.float64)
+    hi = (cache.mode != MODE_INT4)[:, None]
+    return np.where(hi, cache.k[:, :D], kq)
+
+
+def reprobe(cache: HybridCache, q_recent: np.ndarray, sm_scale: float, keep_num: int, keep_den: int,
+            dtype: str = "bf16"):
+    """Re-probe one (batch, KV head) from its last R decode queries (O10).
+
+    q_recent: [G][R][D] float64, row r the query issued when the cache held
+    T - R + r + 1 tokens, i.e. at position T - R + r with the causal structure
+    of the prompt probe's rows (O1). Scores the cached keys as reprobe_keys
+    gives them, selects as O2 over the candidates [0, T - W), and counts how
+    many of the new selection are already in the kept store (persistence).
+    Returns (col_scores [T], Selection, n_persist)."""
+    T = len(cache.mode)
+    K = reprobe_keys(cache, dtype)
+    c = probe_column_scores(q_recent, K[None], T, sm_scale)[0]
+    sel = select_topk(c, T, cache.window, keep_num, keep_den)
+    n_persist = int((cache.mode[sel.idx] == MODE_KEPT).sum())
+    return c, sel, n_persist
