@@ -18,6 +18,7 @@
  *   hq_append_kv     -- one decode-time token append (the window slides)
  *   hq_decode_attn   -- decode attention with fused INT4 dequantization
  *   hq_prefill_attn  -- the causal prefill hybrid-precision operator
+ * and hq_reprobe runs the probe again over the cache during decoding.
  *
  * Conventions shared by every call
  *   - Device pointers unless stated otherwise. All work is enqueued on
@@ -262,6 +263,43 @@ hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_n
 hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,
                          void* out, hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
 size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq);
+
+/* ------------------------------------------------------------------------
+ * hq_reprobe -- run the probe again over the hybrid cache, from the last
+ * decode queries, to see whether the kept columns are still the heavy ones.
+ * Pages: "HyQuant: ...", "Gaps" (whether the vertical-line columns found on
+ * the prompt persist through decoding, notably under heavy batching, is left
+ * open) and TL;DR (the columns are found with a lightweight signal of the
+ * attention pattern).
+ * Computes what hq_probe_select computes, with T = the cache's seq_len, over
+ * the keys the cache now holds:
+ *   k~_j = the stored 16-bit row for kept and window positions; for INT4
+ *          positions code*s + z evaluated in fp32 with one rounding, then
+ *          rounded to cache->dt (half to even),
+ * and the last R = policy->probe_rows decode queries (row r at position
+ * T - R + r: the query issued when the cache held T - R + r + 1 tokens);
+ * and in addition
+ *   n_persist[b][g] = how many of the newly selected columns are in the kept
+ *                     store, i.e. already held in 16 bits.
+ * The cache is only read; moving tokens between stores is left to the
+ * caller. Tcap = cache->cap_q + cache->cap_keep + cache->window bounds every
+ * seq_len and is the position stride of the outputs:
+ *   q_recent   [B][Hq][probe_rows][D] cache->dt
+ *   col_scores [B][Hkv][Tcap] fp32 out (entries >= seq_len are 0)
+ *   sel_idx    [B][Hkv][hq_sel_stride(Tcap)] int32 out (unused tail = -1)
+ *   sel_count, n_persist [B][Hkv] int32 out;  thresh [B][Hkv] out
+ *   ws         hq_reprobe_ws_bytes(cache, Hq, policy) bytes, 256-byte aligned.
+ *              After the call its first B*Hkv*Tcap*D*2 bytes hold the expanded
+ *              keys k~ as [B][Hkv][Tcap][D] cache->dt (rows >= seq_len are
+ *              not written).
+ * policy->window must equal cache->window. The shape rule, error bound and
+ * errors of hq_probe_select apply; Tcap above 2^24 returns HQ_ERR_CAPACITY.
+ * All KV heads of one batch row hold the same seq_len (hq_quantize_kv and
+ * hq_append_kv keep it so); the one of KV head 0 is used. */
+hq_status hq_reprobe(const hq_cache* cache, const void* q_recent, int32_t Hq, const hq_policy* policy,
+                     float sm_scale, float* col_scores, int32_t* sel_idx, int32_t* sel_count,
+                     hq_thresh* thresh, int32_t* n_persist, void* ws, size_t ws_bytes, void* stream);
+size_t hq_reprobe_ws_bytes(const hq_cache* cache, int32_t Hq, const hq_policy* policy);
 
 /* ------------------------------------------------------------------------
  * hq_decode_attn_noalloc -- hq_decode_attn without a workspace argument, for

@@ -21,7 +21,7 @@ HQ_F16, HQ_BF16, HQ_F32 = 0, 1, 2
 EXPORTED = (
     "hq_probe_select", "hq_probe_ws_bytes", "hq_quantize_kv", "hq_append_kv", "hq_decode_attn",
     "hq_decode_ws_bytes", "hq_decode_attn_noalloc", "hq_prefill_attn", "hq_prefill_ws_bytes", "hq_cache_layout", "hq_sel_stride",
-    "hq_last_error", "hq_diag_read_int4", "hq_diag_read_int4_sink_bytes",
+    "hq_last_error", "hq_diag_read_int4", "hq_diag_read_int4_sink_bytes", "hq_reprobe", "hq_reprobe_ws_bytes",
 )
 
 
@@ -75,6 +75,8 @@ def _load():
         "hq_last_error": (ctypes.c_char_p, []),
         "hq_diag_read_int4": (I, [ctypes.POINTER(hq_cache), P, S, V]),
         "hq_diag_read_int4_sink_bytes": (S, [ctypes.POINTER(hq_cache)]),
+        "hq_reprobe": (I, [ctypes.POINTER(hq_cache), P, I, pol, F, P, P, P, P, P, P, S, V]),
+        "hq_reprobe_ws_bytes": (S, [ctypes.POINTER(hq_cache), I, pol]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -252,6 +254,40 @@ def decode_attn_noalloc(cache: HybridCache, q, sm_scale: float | None = None, ou
         out = torch.empty((B, Hq, D), dtype=out_dtype or torch.float32, device=q.device)
     _check(lib.hq_decode_attn_noalloc(cache.ptr(), _ptr(q), Hq, sm, _ptr(out), _dt(out), _stream()))
     return out
+
+
+def reprobe_tcap(cache: HybridCache) -> int:
+    """Position stride of hq_reprobe's outputs: cap_q + cap_keep + window."""
+    return int(cache.c.cap_q + cache.c.cap_keep + cache.c.window)
+
+
+def reprobe(cache: HybridCache, q_recent, sm_scale: float | None = None, policy: Policy | None = None, ws=None):
+    """hq_reprobe. q_recent [B][Hq][R][D] in the cache dtype (R = policy.probe_rows).
+    Returns (col_scores f32 [B][Hkv][Tcap], sel_idx int32 [B][Hkv][stride],
+    sel_count int32 [B][Hkv], thresh int32 [B][Hkv][2], n_persist int32 [B][Hkv],
+    ws uint8; its first B*Hkv*Tcap*D*2 bytes are the expanded keys)."""
+    torch = _torch()
+    _need_contig(q_recent)
+    B, Hq, R, D = q_recent.shape
+    policy = policy or cache.policy
+    if R != policy.probe_rows:
+        raise ValueError("q_recent rows must equal policy.probe_rows")
+    sm = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    dev = q_recent.device
+    tcap = reprobe_tcap(cache)
+    stride = sel_stride(tcap, policy)
+    col = torch.empty((B, cache.Hkv, tcap), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, cache.Hkv, stride), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, cache.Hkv), dtype=torch.int32, device=dev)
+    thr = torch.empty((B, cache.Hkv, 2), dtype=torch.int32, device=dev)
+    npers = torch.empty((B, cache.Hkv), dtype=torch.int32, device=dev)
+    pc = policy.c()
+    n = lib.hq_reprobe_ws_bytes(cache.ptr(), Hq, ctypes.byref(pc))
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    _check(lib.hq_reprobe(cache.ptr(), _ptr(q_recent), Hq, ctypes.byref(pc), sm, _ptr(col), _ptr(sel), _ptr(cnt),
+                          _ptr(thr), _ptr(npers), _ptr(ws), ws.numel(), _stream()))
+    return col, sel, cnt, thr, npers, ws
 
 
 def diag_read_int4(cache: HybridCache, sink=None):

@@ -328,6 +328,47 @@ hq_status hq_decode_attn_noalloc(const hq_cache* cache, const void* q, int32_t H
                        stream);
 }
 
+size_t hq_reprobe_ws_bytes(const hq_cache* cache, int32_t Hq, const hq_policy* policy) {
+    if (!cache || !policy || cache->B < 1 || cache->Hkv < 1 || Hq < 1 || Hq % cache->Hkv) return 0;
+    if (cache->cap_q < hq::kTile || cache->cap_keep < hq::kTile || cache->window < 0) return 0;
+    if ((int64_t)cache->cap_q + cache->cap_keep + cache->window > (1 << 24)) return 0;
+    if (!hq::probe_shape_supported(Hq / cache->Hkv, policy->probe_rows)) return 0;
+    return hq::reprobe_ws_bytes(*cache, Hq, *policy);
+}
+
+hq_status hq_reprobe(const hq_cache* cache, const void* q_recent, int32_t Hq, const hq_policy* policy,
+                     float sm_scale, float* col_scores, int32_t* sel_idx, int32_t* sel_count, hq_thresh* thresh,
+                     int32_t* n_persist, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "hq_reprobe";
+    clear_err();
+    hq_status st;
+    if ((st = check_policy(fn, policy))) return st;
+    if ((st = check_cache(fn, cache))) return st;
+    if ((st = check_heads(fn, cache->B, Hq, cache->Hkv, cache->D))) return st;
+    if (policy->window != cache->window)
+        return fail(HQ_ERR_INVALID_ARG, "%s: policy window %d != cache window %d", fn, policy->window, cache->window);
+    if (!hq::probe_shape_supported(Hq / cache->Hkv, policy->probe_rows))
+        return fail(HQ_ERR_UNSUPPORTED, "%s: %s (query heads per KV head %d, probe_rows %d)", fn,
+                    hq::probe_shape_rule(), Hq / cache->Hkv, policy->probe_rows);
+    if ((int64_t)cache->cap_q + cache->cap_keep + cache->window > (1 << 24))
+        return fail(HQ_ERR_CAPACITY, "%s: cap_q + cap_keep + window exceeds 2^24 positions", fn);
+    if (!(sm_scale > 0.0f) || sm_scale > 1e6f) return fail(HQ_ERR_INVALID_ARG, "%s: sm_scale must be positive", fn);
+    REQ_PTR(q_recent);
+    REQ_PTR(col_scores);
+    REQ_PTR(sel_idx);
+    REQ_PTR(sel_count);
+    REQ_PTR(thresh);
+    REQ_PTR(n_persist);
+    REQ_PTR(ws);
+    if (reinterpret_cast<uintptr_t>(ws) % 256)
+        return fail(HQ_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+    const size_t need = hq::reprobe_ws_bytes(*cache, Hq, *policy);
+    if (ws_bytes < need) return fail(HQ_ERR_CAPACITY, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+    hipError_t e = hq::launch_reprobe(*cache, q_recent, Hq, *policy, sm_scale, col_scores, sel_idx, sel_count, thresh,
+                                      n_persist, ws, (hipStream_t)stream);
+    return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
+}
+
 size_t hq_prefill_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t D, const hq_policy* policy) {
     if (!policy || B < 1 || Hq < 1 || Hkv < 1 || T < 1 || D != hq::kD || Hq % Hkv) return 0;
     return hq::prefill_ws_bytes(B, Hq, Hkv, T, *policy);

@@ -184,6 +184,14 @@ hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_l
                         hq_thresh* thresh, void* ws, hipStream_t s);
 size_t probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_policy& pol);
 
+// Re-probe of a hybrid cache: positions the probe covers (every slot of the
+// three stores), workspace bytes, and the launch (expand, probe, persistence).
+int32_t reprobe_tcap(const hq_cache& c);
+size_t reprobe_ws_bytes(const hq_cache& c, int32_t Hq, const hq_policy& pol);
+hipError_t launch_reprobe(const hq_cache& c, const void* q_recent, int32_t Hq, const hq_policy& pol,
+                          float sm_scale, float* col_scores, int32_t* sel_idx, int32_t* sel_count,
+                          hq_thresh* thresh, int32_t* n_persist, void* ws, hipStream_t s);
+
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,
                           int32_t Hkv, int32_t T, bool f16, const hq_policy& pol,
                           const int32_t* sel_idx, const int32_t* sel_count, int32_t sel_stride,

@@ -14,6 +14,27 @@ RTOL_L2 = 1e-3   # relative-L2 bar for attention outputs
 SCORE_RTOL = 3e-7
 
 
+# Selection flips are allowed only between near-ties: columns whose oracle
+# scores differ by less than this, relative (the score bar is 3e-7).
+NEAR_TIE = 1e-6
+
+
+def compare_selection(gpu_idx, gpu_cnt, c_or, T, W, keep):
+    """The GPU's selected set against the oracle's selection on its fp64
+    scores c_or. Returns the number of near-tie flips (a column swapped with
+    one whose oracle score is within NEAR_TIE); fails on any other
+    difference."""
+    s = O.select_topk(c_or, T, W, keep[0], keep[1])
+    assert gpu_cnt == s.k
+    a, b = set(gpu_idx.tolist()), set(s.idx.tolist())
+    only_gpu, only_or = sorted(a - b), sorted(b - a)
+    assert len(only_gpu) == len(only_or)
+    for x, y in zip(sorted(only_gpu, key=lambda j: -c_or[j]), sorted(only_or, key=lambda j: c_or[j])):
+        gap = abs(c_or[x] - c_or[y]) / max(c_or[x], c_or[y])
+        assert gap < NEAR_TIE, f"selection flip with gap {gap:.3e} (positions {x}, {y})"
+    return len(only_gpu)
+
+
 def fp32_scale(D):
     """The softmax scale 1/sqrt(D) as the library receives it: an fp32 value
     (its `float sm_scale` argument). The oracle is given this same number, so

@@ -211,3 +211,33 @@ def test_decode_noalloc_validation(hq):
     # the workspace entry point still requires its workspace
     assert hq.lib.hq_decode_attn(ctypes.byref(c), q, 4, 0.088, FAKE, hq.HQ_F32, None, 1 << 30, None) == \
         hq.HQ_ERR_INVALID_ARG
+
+
+def test_reprobe_validation(hq):
+    """hq_reprobe checks the cache, the policy against it, the probe's shape
+    rule, the workspace and its alignment before anything is launched."""
+    c = _cache(hq)
+    pol = hq.Policy().c()
+    need = hq.lib.hq_reprobe_ws_bytes(ctypes.byref(c), 4, ctypes.byref(pol))
+    tcap = c.cap_q + c.cap_keep + c.window
+    assert need >= tcap * 128 * 2 + tcap
+
+    def call(cache=c, Hq=4, p=pol, sm=0.088, ws=FAKE, wsb=None, **ptrs):
+        a = dict(q=FAKE, col=FAKE, sel=FAKE, cnt=FAKE, thr=FAKE, npers=FAKE)
+        a.update(ptrs)
+        return hq.lib.hq_reprobe(ctypes.byref(cache) if cache is not None else None, a["q"], Hq, ctypes.byref(p), sm,
+                                 a["col"], a["sel"], a["cnt"], a["thr"], a["npers"], ws,
+                                 need if wsb is None else wsb, None)
+    assert call(cache=None) == hq.HQ_ERR_INVALID_ARG
+    assert call(cache=_cache(hq, k_codes=0)) == hq.HQ_ERR_INVALID_ARG
+    assert call(Hq=6) == hq.HQ_ERR_UNSUPPORTED
+    assert call(p=hq.hq_policy(5, 100, 64, 64)) == hq.HQ_ERR_INVALID_ARG          # window != cache window
+    assert call(p=hq.hq_policy(5, 100, 128, 10)) == hq.HQ_ERR_UNSUPPORTED         # 4 x 10 rows
+    assert call(sm=0.0) == hq.HQ_ERR_INVALID_ARG
+    assert call(npers=_null()) == hq.HQ_ERR_INVALID_ARG
+    assert call(q=_null()) == hq.HQ_ERR_INVALID_ARG
+    assert call(ws=ctypes.c_void_p(0x100010)) == hq.HQ_ERR_INVALID_ARG            # not 256-byte aligned
+    assert call(wsb=need - 1) == hq.HQ_ERR_CAPACITY
+    big = _cache(hq, cap_q=(1 << 24) - 64, cap_keep=128)
+    assert call(cache=big) == hq.HQ_ERR_CAPACITY
+    assert hq.lib.hq_reprobe_ws_bytes(ctypes.byref(big), 4, ctypes.byref(pol)) == 0

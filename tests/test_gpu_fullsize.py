@@ -14,9 +14,8 @@ import pytest
 import oracle as O
 from synth.inputs import CONFIGS, make_append_tokens, make_decode_inputs
 
-from gpu_common import SCORE_RTOL, assert_attn_close, fp32_scale, ints_to_dev, to_dev
+from gpu_common import SCORE_RTOL, assert_attn_close, compare_selection, fp32_scale, ints_to_dev, to_dev
 from hq_layout import read_cache
-from test_gpu_probe import compare_selection
 
 pytestmark = pytest.mark.gpu
 

@@ -12,24 +12,9 @@ import oracle as O
 from synth import small_decode_inputs
 from synth.inputs import bf16_bits_from_f32
 
-from gpu_common import SCORE_RTOL, fp32_scale, ints_to_dev, to_dev
+from gpu_common import SCORE_RTOL, compare_selection, fp32_scale, ints_to_dev, to_dev
 
 pytestmark = pytest.mark.gpu
-
-NEAR_TIE = 1e-6
-
-
-def compare_selection(gpu_idx, gpu_cnt, c_or, T, W, keep):
-    """Returns the number of near-tie flips; fails on any other difference."""
-    s = O.select_topk(c_or, T, W, keep[0], keep[1])
-    assert gpu_cnt == s.k
-    a, b = set(gpu_idx.tolist()), set(s.idx.tolist())
-    only_gpu, only_or = sorted(a - b), sorted(b - a)
-    assert len(only_gpu) == len(only_or)
-    for x, y in zip(sorted(only_gpu, key=lambda j: -c_or[j]), sorted(only_or, key=lambda j: c_or[j])):
-        gap = abs(c_or[x] - c_or[y]) / max(c_or[x], c_or[y])
-        assert gap < NEAR_TIE, f"selection flip with gap {gap:.3e} (positions {x}, {y})"
-    return len(only_gpu)
 
 
 def run_probe(inp, window, keep):
