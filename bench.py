@@ -16,7 +16,9 @@ bracketed by HIP events on the stream it is launched on (torch's current
 stream). `value` is the steady-state decode attention time (hq_decode_attn,
 the 2nd..16th decode of each step) in microseconds; the first decode after
 the cache build is reported as decode_us_full_step; the once-per-prompt rows
-(probe, quantize, prefill) are reported beside it. After the timed steps the
+(probe, quantize, prefill) are reported beside it, and so is a re-probe of
+the step's cache from its last 64 query rows ("reprobe": time and the share
+of the new selection already kept). After the timed steps the
 other decode workloads (1-head 4K warm and cold, 128K with 64 appends, the
 ragged 70B-like shape) and the 1K..32K context sweep are timed the same way
 and reported under "workloads" and "sweep"; each of them also reports
@@ -781,6 +783,23 @@ def main():
     res["roofline"]["frac_of_achievable"] = round(res["roofline"]["achieved"] / ach, 4)
     res["int4_stream_read"] = {"bytes": int4_bytes, "us": round(tm.ms("diag_read_int4") * 1e3, 2),
                                "GBps": round(ach, 1)}
+    # Re-probe of the step's cache (prompt + N_DECODE decode tokens) from its
+    # last 64 query rows (the prompt's last 64 - N_DECODE probe rows, then the
+    # decode queries), timed after the step loop: a periodic call, not a step.
+    qr = torch.cat([qp[:, :, N_DECODE:], qd.permute(1, 2, 0, 3)], dim=2).contiguous()
+    rp = hq.reprobe(cache, qr)
+    for _ in range(2):
+        rp = hq.reprobe(cache, qr, None, None, rp[5])
+    torch.cuda.synchronize()
+    for _ in range(5):
+        rp = tm("reprobe", hq.reprobe, cache, qr, None, None, rp[5])
+    torch.cuda.synchronize()
+    npers, rcnt = rp[4].cpu().numpy(), rp[2].cpu().numpy()
+    frac = npers / np.maximum(rcnt, 1)
+    res["reprobe"] = {"ms": round(tm.ms("reprobe"), 3), "T": int(counts[0, 0, 0]),
+                      "persistence_mean": round(float(frac.mean()), 4),
+                      "persistence_min": round(float(frac.min()), 4)}
+    del rp
     if pf is not None:
         pms = tm.ms("prefill_attn")
         psp = pf["spec"]

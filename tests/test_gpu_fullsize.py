@@ -109,7 +109,10 @@ def test_decode_path_full_size(name):
 def test_decode_with_appends_128k():
     """8B shape at 128K, batch 4, 64 consecutive appends, each followed by a
     decode with its own query. Every (b, g) at steps 1, 2, 32 and 64 (and its
-    codes after the 64 appends); two pairs at every step."""
+    codes after the 64 appends); two pairs at every step. Then a re-probe from
+    the 64 decode queries: every pair's expanded keys (bit-exact) and
+    persistence count (exact on the GPU's selection), and the two pairs'
+    scores and selection against the oracle's re-probe."""
     import torch
     import kv_cache_amd as hq
     spec = CONFIGS["c3_decode_8b_128k_append"]
@@ -127,13 +130,20 @@ def test_decode_with_appends_128k():
         outs.append(hq.decode_attn(cache, qd[s]).cpu().numpy())
     torch.cuda.synchronize()
     assert cache.err_flag() == 0
+    # re-probe from the 64 decode queries (positions T0 .. T0 + 63 = the last 64)
+    q_recent = np.ascontiguousarray(qn.transpose(1, 2, 0, 3))
+    rp = hq.reprobe(cache, to_dev(q_recent, "bf16"), sm)
+    torch.cuda.synchronize()
+    tcap = hq.reprobe_tcap(cache)
+    rcol, rsel, rcnt, rthr, rpers = (t.cpu().numpy() for t in rp[:5])
+    kx = rp[5][: spec.B * spec.Hkv * tcap * spec.D * 2].view(torch.int16).view(spec.B, spec.Hkv, tcap, spec.D)
     gc = read_cache(cache)
     del cache
     every_step = {(0, 1), (3, 6)}
     check_steps = (1, 2, 32, 64)
     flips = 0
     t0 = time.time()
-    kept_added = []
+    kept_added, persist = [], []
     for b in range(spec.B):
         for g in range(spec.Hkv):
             oc, f, _, _ = _oracle_pair(spec, inp, b, g, gsel)
@@ -154,6 +164,23 @@ def test_decode_with_appends_128k():
             assert cnts[0] == oc.T and cnts[1] == int((oc.mode == O.MODE_INT4).sum())
             assert cnts[2] == int((oc.mode == O.MODE_KEPT).sum())
             kept_added.append(int(cnts[2]) - n_keep0)
+            # re-probe: expanded keys of every pair bit-exact; persistence exact on the GPU's selection
+            kxb = kx[b, g, : oc.T].cpu().numpy().view(np.uint16)
+            assert np.array_equal(O.to_f64(kxb, "bf16"), O.reprobe_keys(oc, "bf16")), (b, g)
+            k = int(rcnt[b, g])
+            assert k == oc.T * 5 // 100
+            kept = oc.mode == O.MODE_KEPT
+            assert int(rpers[b, g]) == int(kept[rsel[b, g, :k]].sum()), (b, g)
+            persist.append(int(rpers[b, g]) / k)
+            if (b, g) in every_step:   # scores and selection against the oracle's re-probe
+                c_or, _, n_or = O.reprobe(oc, O.to_f64(q_recent[b, qsl], "bf16"), sm, 5, 100)
+                rel = float((np.abs(rcol[b, g, : oc.T].astype(np.float64) - c_or) / c_or).max())
+                assert rel < SCORE_RTOL, (b, g, rel)
+                if compare_selection(rsel[b, g, :k], k, c_or, oc.T, spec.window, (5, 100)) == 0:
+                    assert int(rpers[b, g]) == n_or
+                print(f"  re-probe (b={b}, g={g}): score rel err {rel:.2e}, persistence {rpers[b, g]}/{k}",
+                      flush=True)
         print(f"  b={b}: {spec.Hkv} pairs checked ({time.time() - t0:.0f} s)", flush=True)
     print(f"c3: near-tie selection flips {flips}; departures kept by the append rule per (b, g): "
-          f"min {min(kept_added)} max {max(kept_added)}", flush=True)
+          f"min {min(kept_added)} max {max(kept_added)}; re-probe persistence min {min(persist):.3f} "
+          f"mean {np.mean(persist):.3f}", flush=True)
