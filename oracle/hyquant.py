@@ -416,6 +416,78 @@ def int8_block_quantize(x: np.ndarray):
 
 
 # ---------------------------------------------------------------------------
+# O11: OCP FP8 (E4M3) block quantization, the prefill's other low-bit format
+# ---------------------------------------------------------------------------
+
+FP8_MAX = 448.0  # largest finite E4M3 magnitude: 2^8 x 1.75
+
+
+def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """E4M3 bit patterns -> float64 (O11).
+
+    The OCP 8-bit floating point format E4M3: sign, 4 exponent bits (bias
+    7), 3 mantissa bits; exponent field 0 holds the subnormals m/8 x 2^-6;
+    exponent 15 with mantissa 7 is NaN (no infinities), so the largest
+    finite value is 1.75 x 2^8 = 448. Written from that definition."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_e4m3_encode(x32: np.ndarray) -> np.ndarray:
+    """float32 -> E4M3 bit patterns, round to nearest, ties to even (O11).
+
+    The spacing of E4M3 values is 2^(e - 3) in the binade [2^e, 2^(e+1)) for
+    e >= -6 and 2^-9 below 2^-6 (subnormals), so |x| rounds to an integer
+    multiple of that spacing (ties to the even multiple, i.e. to the even
+    mantissa). Magnitudes that round above 448 saturate to 448 (reading: the
+    kernels never produce them, |x / s| <= 448 (1 + 2^-23) by construction).
+    The sign of zero is kept. x32: finite float32 values."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)  # exact
+    a = np.abs(x)
+    _, ex = np.frexp(a)                        # a = f 2^ex, f in [1/2, 1)
+    e = np.maximum(ex - 1, -6)                 # binade exponent, subnormals share e = -6
+    q = np.ldexp(1.0, e - 3)                   # spacing
+    r = np.rint(a / q) * q                     # a / q exact (power of two); rint: ties to even
+    r = np.minimum(r, FP8_MAX)
+    # bits of r: exponent field and mantissa
+    _, er = np.frexp(r)
+    normal = r >= 2.0 ** -6
+    efield = np.where(normal, er - 1 + 7, 0)
+    mant = np.where(normal, np.rint(np.ldexp(r, -(er - 1)) * 8.0) - 8.0, np.rint(np.ldexp(r, 9)))
+    bits = (efield.astype(np.int64) << 3) | mant.astype(np.int64)
+    bits = bits | np.where(np.signbit(x), 0x80, 0)
+    return bits.astype(np.uint8)
+
+
+def fp8_block_quantize(x: np.ndarray):
+    """Symmetric OCP FP8 (E4M3) per 64-token block over all channels (O11).
+
+    [HQ-wiki] "Gaps": FP8 as a third precision point is left open; the
+    reading taken here mirrors O7 with the E4M3 grid: per block of 64 rows of
+    one head, s = fp32_rne(max|x| / 448), code = E4M3_rne(fp32_rne(x / s)),
+    all codes +0 when s == 0. The value of a code is decode(code) * s.
+
+    x: [T][D] float64 exact values. Returns (codes uint8 [T][D], s float32 [ceil(T/64)])."""
+    T, D = x.shape
+    nb = (T + INT8_BLOCK - 1) // INT8_BLOCK
+    codes = np.zeros((T, D), dtype=np.uint8)
+    scales = np.zeros(nb, dtype=np.float32)
+    for b in range(nb):
+        blk = x[b * INT8_BLOCK:(b + 1) * INT8_BLOCK].astype(np.float32)
+        amax = np.float32(np.abs(blk).max()) if blk.size else np.float32(0)
+        s = np.float32(amax / np.float32(FP8_MAX))
+        scales[b] = s
+        if s > 0:
+            codes[b * INT8_BLOCK:(b + 1) * INT8_BLOCK] = fp8_e4m3_encode((blk / s).astype(np.float32))
+    return codes, scales
+
+
+# ---------------------------------------------------------------------------
 # O8: prefill hybrid-precision attention
 # ---------------------------------------------------------------------------
 
@@ -437,6 +509,8 @@ def prefill_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_idx:
 
     q: [T][D], k, v: [T][D] (this head's KV head), q8/sq: this query head's
     INT8 codes/scales, k8/sk: the KV head's; rows: query positions to compute.
+    With the FP8 low path (O11), q8 and k8 are the decoded E4M3 values
+    (fp8_e4m3_decode of the codes) and sq, sk the FP8 block scales.
     Returns [len(rows)][D].
     """
     T, D = k.shape

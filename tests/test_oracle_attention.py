@@ -329,3 +329,32 @@ def test_probe_select_batch_gqa_map_and_ragged_lengths():
             assert int(np.argmax(scores[b][g])) == 20 + 7 * g, (b, g)
             assert sels[b][g].k == lens[b] * 5 // 100
             assert 20 + 7 * g in set(sels[b][g].idx.tolist())
+
+
+def test_prefill_fp8_on_representable_inputs_is_exact():
+    """Q and K whose 64-row blocks lie on the E4M3 grid times a power of two
+    (block maximum 448 x 2^e): the FP8 path reproduces every value, so the
+    hybrid prefill with any selection equals exact causal attention."""
+    T, D, W = 300, 128, 64
+    rng = np.random.default_rng(60)
+    table = O.fp8_e4m3_decode(np.arange(256, dtype=np.uint8))
+    fin = table[~np.isnan(table)]
+
+    def grid(seed):
+        r = np.random.default_rng(seed)
+        x = r.choice(fin, size=(T, D))
+        for b in range(0, T, 64):
+            x[b, 0] = 448.0
+            x[b:b + 64] *= 2.0 ** (r.integers(-9, -6))
+        return x
+    q, k = grid(61), grid(62)
+    v = _bf16(rng.standard_normal((T, D)))
+    assert np.array_equal(O.bf16_to_f64(bf16_bits_from_f32(q.astype(np.float32))), q)   # exact in bf16
+    q8, sq = O.fp8_block_quantize(q)
+    k8, sk = O.fp8_block_quantize(k)
+    qd, kd = O.fp8_e4m3_decode(q8), O.fp8_e4m3_decode(k8)
+    assert np.array_equal(qd * sq.astype(np.float64)[np.arange(T) // 64][:, None], q)
+    sel = np.sort(rng.choice(T - W, 9, replace=False))
+    sm = 1 / math.sqrt(D)
+    out = O.prefill_attention_block(q, k, v, sel, W, sm, qd, sq, kd, sk, 0, T)
+    assert np.allclose(out, _sdpa(q, k, v, sm, causal=True), rtol=1e-11, atol=1e-12)

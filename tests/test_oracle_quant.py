@@ -217,3 +217,92 @@ def test_uniform_int8_attention_reduces_to_softmax_attention():
     a = O.uniform_int8_attention(q, K, V, 0.088)
     b = O.softmax_attention(q, K, V, 0.088)
     assert np.allclose(a, b, rtol=0, atol=1e-12)
+
+
+# ---- O11: OCP FP8 (E4M3) prefill blocks ----
+
+def test_fp8_decode_closed_forms():
+    """Values the E4M3 definition fixes: 1.0, 1.5, -1, the largest finite
+    (448), the smallest normal (2^-6), the smallest and largest subnormals
+    (2^-9, 7 x 2^-9), signed zero, and the two NaN patterns; the 127
+    non-negative finite patterns increase with the code."""
+    d = O.fp8_e4m3_decode(np.arange(256, dtype=np.uint8))
+    fixed = {0x38: 1.0, 0x3C: 1.5, 0xB8: -1.0, 0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6,
+             0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x00: 0.0, 0x40: 2.0, 0x77: 240.0}
+    for c, val in fixed.items():
+        assert d[c] == val, hex(c)
+    assert np.signbit(d[0x80]) and d[0x80] == 0.0
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF])
+    assert np.sum(np.isnan(d)) == 2
+    assert np.all(np.diff(d[:0x7F]) > 0)
+    assert np.array_equal(d[0x80:0xFF], -d[:0x7F])
+
+
+def test_fp8_encode_round_trip_ties_and_nearest():
+    d = O.fp8_e4m3_decode(np.arange(256, dtype=np.uint8))
+    finite = np.nonzero(~np.isnan(d))[0].astype(np.uint8)
+    assert np.array_equal(O.fp8_e4m3_encode(d[finite].astype(np.float32)), finite)
+    pos = d[:0x7F]
+    mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)     # exact in fp32
+    enc = O.fp8_e4m3_encode(mid)
+    assert np.all((enc & 1) == 0)                             # ties go to the even mantissa
+    assert np.all((enc == np.arange(0x00, 0x7E)) | (enc == np.arange(0x01, 0x7F)))
+    # just off the midpoints: the nearer neighbour
+    up = np.nextafter(mid, np.float32(np.inf))
+    dn = np.nextafter(mid, np.float32(-np.inf))
+    assert np.array_equal(O.fp8_e4m3_encode(up), np.arange(0x01, 0x7F))
+    assert np.array_equal(O.fp8_e4m3_encode(dn[1:]), np.arange(0x01, 0x7E))
+    assert O.fp8_e4m3_encode(np.float32(463.9)) == 0x7E and O.fp8_e4m3_encode(np.float32(-1e-4)) == 0x80
+
+
+def test_fp8_encode_matches_torch_cast():
+    """A library routine that implements the same format: torch's fp32 ->
+    float8_e4m3fn cast (round to nearest even) on the CPU."""
+    import torch
+    rng = np.random.default_rng(11)
+    mags = rng.choice([1e-4, 1e-3, 1e-2, 0.1, 1.0, 10.0, 100.0], 60000)
+    x = np.concatenate([rng.standard_normal(60000) * mags, rng.uniform(-448, 448, 20000),
+                        np.ldexp(rng.uniform(-1, 1, 20000), -7)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.fp8_e4m3_encode(x), ref)
+
+
+def test_fp8_block_brute_force_and_bound():
+    """Per block: the scale's definition, the block maximum on +-448, each
+    code the nearest E4M3 value to fp32(x / s) by exhaustive search (ties,
+    which do not occur here, aside), and |x - decode(code) s| <= 2^-4 |x| +
+    2^-10 s (half a spacing, relative in the normal range, absolute in the
+    subnormal one)."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((150, 128), dtype=np.float32)
+    x[:, 9] *= 30
+    x[3, :] *= 1e-4
+    xv = O.bf16_to_f64(bf16_bits_from_f32(x))
+    codes, s = O.fp8_block_quantize(xv)
+    assert codes.shape == (150, 128) and s.shape == (3,)
+    table = O.fp8_e4m3_decode(np.arange(256, dtype=np.uint8))
+    fin = np.nonzero(~np.isnan(table))[0]
+    for b in range(3):
+        blk = xv[b * 64:(b + 1) * 64]
+        sb = np.float32(s[b])
+        assert sb == np.float32(np.float32(np.abs(blk).max()) / np.float32(448))
+        c = codes[b * 64:(b + 1) * 64]
+        assert np.abs(O.fp8_e4m3_decode(c)).max() == 448.0
+        qv = (blk.astype(np.float32) / sb).astype(np.float64)
+        dist = np.abs(qv[..., None] - table[fin])
+        best = dist.min(-1, keepdims=True)
+        ok = dist == best
+        chosen = (fin[None, None, :] == c[..., None].astype(np.int64))
+        assert np.all((ok & chosen).any(-1)), b
+        recon = O.fp8_e4m3_decode(c) * float(sb)
+        assert np.all(np.abs(blk - recon) <= 2.0 ** -4 * np.abs(blk) + 2.0 ** -10 * float(sb) + 1e-300)
+
+
+def test_fp8_zero_block_and_signed_zero():
+    x = np.zeros((70, 128))
+    x[64:, 0] = -2.0
+    x[64:, 1] = -0.0
+    codes, s = O.fp8_block_quantize(x)
+    assert s[0] == 0 and np.all(codes[:64] == 0)
+    assert codes[64, 0] == 0xFE and codes[64, 1] == 0x80 and codes[64, 2] == 0x00
+    assert float(s[1]) == float(np.float32(2) / np.float32(448))
