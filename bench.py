@@ -811,6 +811,20 @@ def main():
         psel = hq.probe_select(pf["qprobe"], pf["k"], pf["lens"], pol)
         psel_idx, psel_cnt = psel[1].cpu().numpy(), psel[2].cpu().numpy()
         res["prefill_roofline"] = prefill_roofline(psp.T, pol.window, psel_idx, psel_cnt, psp.Hq // psp.Hkv, pms)
+        # the same prefill with the OCP FP8 (E4M3) low-precision path, timed
+        # after the step loop (an option of the operator, not a step)
+        polf = hq.Policy(low_fmt=hq.HQ_LOW_FP8)
+        for _ in range(2):
+            hq.prefill_attn(pf["q"], pf["k"], pf["v"], psel[1], psel[2], polf, None, pf["out"])
+        torch.cuda.synchronize()
+        for _ in range(5):
+            tm("prefill_attn_fp8", hq.prefill_attn, pf["q"], pf["k"], pf["v"], psel[1], psel[2], polf, None,
+               pf["out"])
+        torch.cuda.synchronize()
+        fms = tm.ms("prefill_attn_fp8")
+        fr = prefill_roofline(psp.T, pol.window, psel_idx, psel_cnt, psp.Hq // psp.Hkv, fms)
+        res["prefill_fp8"] = {"ms": round(fms, 3), "TFLOPs": round(fl / (fms * 1e-3) / 1e12, 1),
+                              "frac": fr["frac"], "low_fmt": "OCP FP8 E4M3, per-64-token block scale"}
     sels = tuple(t.cpu().numpy() for t in (hq.probe_select(qp, k, lens, pol)))
     del cache, k, v, knew, vnew
     if pf is not None:

@@ -76,7 +76,10 @@ typedef struct {
     int32_t keep_den;
     int32_t window;
     int32_t probe_rows;
+    int32_t low_fmt;   /* low-precision path of hq_prefill_attn: HQ_LOW_INT8
+                          (0, the default) or HQ_LOW_FP8; ignored elsewhere */
 } hq_policy;
+typedef enum { HQ_LOW_INT8 = 0, HQ_LOW_FP8 = 1 } hq_low_fmt;
 
 /* Score and position of the k-th selected candidate (k > 0), or
  * {+inf, -1} when nothing was selected. */
@@ -329,10 +332,13 @@ hq_status hq_decode_attn_noalloc(const hq_cache* cache, const void* q, int32_t H
  * paths updating one online-softmax state).
  * For query row i of head h (KV head g) and key j <= i:
  *   j in S_g or i - j < window : score = (q_i . k_j) * sm_scale   (bf16 MFMA)
- *   otherwise : score = (Q8_i . K8_j) * sQ * sK * sm_scale          (INT8 MFMA)
- * with symmetric INT8 per 64-token block over all channels (s = max|x|/127
- * in fp32, code = rint(x/s)); out_i = sum_j softmax(score)_j v_j. P and V
- * enter the PV product as fp16.
+ *   otherwise : score = (Q8_i . K8_j) * sQ * sK * sm_scale  (INT8 or FP8 MFMA)
+ * with symmetric codes per 64-token block over all channels, by
+ * policy->low_fmt: HQ_LOW_INT8, s = max|x|/127 in fp32, code = rint(x/s)
+ * (exact int32 products); or HQ_LOW_FP8 (HyQuant page "Gaps": FP8 as a third
+ * precision point), s = max|x|/448 in fp32, code = OCP E4M3 of fp32(x/s),
+ * round to nearest even (fp32 sums of exact products). out_i = sum_j
+ * softmax(score)_j v_j. P and V enter the PV product as fp16.
  *   q [B][Hq][T][D], k, v [B][Hkv][T][D] dt (values within fp16 range for
  *   V); sel_idx [B][Hkv][hq_sel_stride(T)] int32, the first sel_count[b][g]
  *   entries ascending, distinct and in [0, T) (as hq_probe_select returns
@@ -340,7 +346,8 @@ hq_status hq_decode_attn_noalloc(const hq_cache* cache, const void* q, int32_t H
  *   out [B][Hq][T][D] out_dt; ws of hq_prefill_ws_bytes() bytes, 256-byte
  *   aligned. Entries outside the documented range are ignored, never read
  *   out of bounds.
- * Workspace after the call (the INT8 stage, readable for inspection), with
+ * Workspace after the call (the low-precision stage, readable for
+ * inspection; one code byte per element, INT8 or E4M3 bits), with
  * nb = ceil(T / 64), Tp = 64 nb and A(x) = x rounded up to a multiple of 256:
  *   offset 0                      Q8 int8 [B][Hq][Tp][D] (rows >= T are 0)
  *   o1 = A(B Hq Tp D)             sQ fp32 [B][Hq][nb]

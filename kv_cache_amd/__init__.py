@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libhyquant.so")
 
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_CAPACITY, HQ_ERR_HIP = 0, -1, -2, -3, -4
 HQ_F16, HQ_BF16, HQ_F32 = 0, 1, 2
+HQ_LOW_INT8, HQ_LOW_FP8 = 0, 1
 
 EXPORTED = (
     "hq_probe_select", "hq_probe_ws_bytes", "hq_quantize_kv", "hq_append_kv", "hq_decode_attn",
@@ -33,7 +34,7 @@ class HQError(RuntimeError):
 
 class hq_policy(ctypes.Structure):
     _fields_ = [("keep_num", ctypes.c_int32), ("keep_den", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("probe_rows", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("probe_rows", ctypes.c_int32), ("low_fmt", ctypes.c_int32)]
 
 
 class hq_thresh(ctypes.Structure):
@@ -57,6 +58,10 @@ class hq_cache_sizes(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing; build it with `python kv_cache_amd/build.py`")
+    # torch first: the library then binds to the HIP runtime torch has
+    # loaded, so both see the same devices, memory and streams (loaded the
+    # other way round, the library's calls find no device).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F, S, V = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
     pol = ctypes.POINTER(hq_policy)
@@ -103,9 +108,10 @@ class Policy:
     keep_den: int = 100
     window: int = 128
     probe_rows: int = 64
+    low_fmt: int = HQ_LOW_INT8   # prefill's low-precision path (HQ_LOW_INT8 / HQ_LOW_FP8)
 
     def c(self) -> hq_policy:
-        return hq_policy(self.keep_num, self.keep_den, self.window, self.probe_rows)
+        return hq_policy(self.keep_num, self.keep_den, self.window, self.probe_rows, self.low_fmt)
 
 
 def _torch():

@@ -40,6 +40,8 @@ hq_status check_policy(const char* fn, const hq_policy* p) {
         return fail(HQ_ERR_INVALID_ARG, "%s: window %d must be a non-negative multiple of 64", fn, p->window);
     if (p->probe_rows < 1 || p->probe_rows > 256)
         return fail(HQ_ERR_INVALID_ARG, "%s: probe_rows %d must be in [1, 256]", fn, p->probe_rows);
+    if (p->low_fmt != HQ_LOW_INT8 && p->low_fmt != HQ_LOW_FP8)
+        return fail(HQ_ERR_UNSUPPORTED, "%s: low_fmt %d unsupported (HQ_LOW_INT8, HQ_LOW_FP8)", fn, p->low_fmt);
     return HQ_OK;
 }
 

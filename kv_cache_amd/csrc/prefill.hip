@@ -11,9 +11,16 @@
 //
 // Score of query row i and key j <= i (window W, selected set S of the KV head):
 //   j in S or i - j < W : (q_i . k_j) * sm_scale                 bf16 MFMA
-//   otherwise           : (Q8_i . K8_j) * sQ * sK * sm_scale      int8 MFMA
-// INT8 is symmetric per 64-token block over all 128 channels:
-// s = fp32(max|x| / 127), code = clamp(rint(x / s), -127, 127).
+//   otherwise           : (Q8_i . K8_j) * sQ * sK * sm_scale      int8 or fp8 MFMA
+// The low-precision codes are symmetric per 64-token block over all 128
+// channels, INT8: s = fp32(max|x| / 127), code = clamp(rint(x / s), -127, 127);
+// or OCP FP8 E4M3 (the policy's choice; the pages leave FP8 as an open third
+// precision point): s = fp32(max|x| / 448), code = E4M3 of fp32(x / s),
+// rounded to nearest even. Both are one byte per element, so the two
+// formats share the layout and the kernels differ only in the conversion and
+// the matrix instruction (v_mfma_i32_32x32x32_i8, or gfx950's
+// v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands: the same throughput, and
+// float scores that need no integer conversion).
 //
 // Pre-pass (k_pf_quant_q, k_pf_quant_kv, k_pf_gather_sel): Q8/sQ, K8/sK, V
 // converted to fp16 and transposed per 64-key block (the PV operand
@@ -48,6 +55,7 @@ namespace {
 
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef int intx16 __attribute__((ext_vector_type(16)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
@@ -96,7 +104,7 @@ __device__ inline float block_max256(float v, float* red) {
 // thread t owns row t/4, channels 32*(t%4) .. +31. RECIP: quotients from the
 // reciprocal and FMA residual steps (fewer instructions, more registers: the
 // Q kernel gains, the K/V kernel, which also writes V^T, runs slower with it).
-template <bool F16, bool RECIP>
+template <bool F16, bool RECIP, bool FP8>
 __device__ __attribute__((always_inline)) inline void quant_block_i8(const uint16_t* src, int rows_valid, int8_t* dst, float* scale) {
     __shared__ float red[4];
     const int t = threadIdx.x, r = t >> 2, c0 = (t & 3) * 32;
@@ -121,17 +129,31 @@ __device__ __attribute__((always_inline)) inline void quant_block_i8(const uint1
 #pragma unroll
     for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
     am = block_max256(am, red);
-    const float s = am / 127.0f;
+    const float s = am / (FP8 ? 448.0f : 127.0f);
     uint32_t packed[8];
     auto pack = [&](auto quot) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             uint32_t w = 0;
+            if constexpr (FP8) {
+                // E4M3, round to nearest even; |x / s| <= 448 (1 + 2^-23), so
+                // nothing reaches the overflow range; element j in byte j.
+                // E4M3 keeps the sign of zero, which the residual steps of the
+                // reciprocal route lose (-0 - (+0) = +0): the quotient takes
+                // the dividend's sign, as the IEEE divide gives it (s > 0).
+                auto qs = [&](float v) { return __builtin_copysignf(quot(v), v); };
+                if (s > 0.f) {
+                    int v = __builtin_amdgcn_cvt_pk_fp8_f32(qs(x[4 * i]), qs(x[4 * i + 1]), 0, false);
+                    v = __builtin_amdgcn_cvt_pk_fp8_f32(qs(x[4 * i + 2]), qs(x[4 * i + 3]), v, true);
+                    w = (uint32_t)v;
+                }
+            } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float c = 0.f;
-                if (s > 0.f) c = fminf(fmaxf(rintf(quot(x[4 * i + j])), -127.f), 127.f);
-                w |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * j);
+                for (int j = 0; j < 4; ++j) {
+                    float c = 0.f;
+                    if (s > 0.f) c = fminf(fmaxf(rintf(quot(x[4 * i + j])), -127.f), 127.f);
+                    w |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * j);
+                }
             }
             packed[i] = w;
         }
@@ -186,17 +208,17 @@ struct PfParams {
     float c16;           // sm_scale * log2(e)
 };
 
-template <bool F16>
+template <bool F16, bool FP8>
 __global__ __launch_bounds__(256) void k_pf_quant_q(PfParams p) {
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const size_t Tp = (size_t)p.nblk * kBN;
     const uint16_t* src = p.q + (((size_t)b * p.Hq + h) * p.T + (size_t)blk * kBN) * kD;
     int8_t* dst = p.q8 + (((size_t)b * p.Hq + h) * Tp + (size_t)blk * kBN) * kD;
-    quant_block_i8<F16, true>(src, min(kBN, p.T - blk * kBN), dst, p.sq + ((size_t)b * p.Hq + h) * p.nblk + blk);
+    quant_block_i8<F16, true, FP8>(src, min(kBN, p.T - blk * kBN), dst, p.sq + ((size_t)b * p.Hq + h) * p.nblk + blk);
 }
 
 // K8 + sK, V^T in fp16, and the selected-column mask of one key block.
-template <bool F16>
+template <bool F16, bool FP8>
 __global__ __launch_bounds__(256) void k_pf_quant_kv(PfParams p) {
     __shared__ uint16_t vs[kBN][kD + 8];
     const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -204,7 +226,7 @@ __global__ __launch_bounds__(256) void k_pf_quant_kv(PfParams p) {
     const size_t Tp = (size_t)p.nblk * kBN;
     const int rows = min(kBN, p.T - blk * kBN);
     const uint16_t* ksrc = p.k + ((size_t)bg * p.T + (size_t)blk * kBN) * kD;
-    quant_block_i8<F16, false>(ksrc, rows, p.k8 + ((size_t)bg * Tp + (size_t)blk * kBN) * kD, p.sk + (size_t)bg * p.nblk + blk);
+    quant_block_i8<F16, false, FP8>(ksrc, rows, p.k8 + ((size_t)bg * Tp + (size_t)blk * kBN) * kD, p.sk + (size_t)bg * p.nblk + blk);
     // V -> fp16 -> transposed
     const int t = threadIdx.x, r = t >> 2, c0 = (t & 3) * 32;
     const uint16_t* vsrc = p.v + ((size_t)bg * p.T + (size_t)blk * kBN) * kD;
@@ -394,19 +416,47 @@ __device__ inline void stage_store(Smem& sm, int buf, const Stage& s) {
     st16(sm.vt[buf], t + 768, kVtStride, s.v3);
 }
 
-// S^T (64 keys x 32 queries) in int8: two 32x32 tiles, K = 128 in 4 steps.
-__device__ inline void st_int8(const int8_t* k8, const intx4 (&qb)[4], intx16 (&s)[2]) {
+// Accumulators of the low-precision scores: exact int32 sums for INT8,
+// fp32 for FP8 (E4M3 products are exact in fp32; the sums round).
+template <bool FP8> struct LowAcc { typedef intx16 type; };
+template <> struct LowAcc<true> { typedef floatx16 type; };
+
+// One 32-key S^T tile (keys 32tt..32tt+31) of the low-precision products.
+// INT8: K = 128 in 4 steps of 32; lane l supplies row l % 32, bytes
+// 32 ks + 16 (l / 32) .. + 15 of each operand. FP8: 2 steps of 64; the lane
+// supplies the two 16-byte pieces of the INT8 steps 2 k2 and 2 k2 + 1 as one
+// 32-byte operand. Both operands are assembled the same way, so every
+// channel meets its partner once whatever order the instruction sums in.
+template <bool FP8>
+__device__ inline typename LowAcc<FP8>::type st_low_tile(const int8_t* k8, const intx4 (&qb)[4], int tt) {
     const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
+    typename LowAcc<FP8>::type acc = {};
+    const int8_t* row = k8 + (32 * tt + m) * kK8Stride + 16 * hf;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        intx16 acc = {};
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const intx4 a0 = *reinterpret_cast<const intx4*>(row + 64 * k2);
+            const intx4 a1 = *reinterpret_cast<const intx4*>(row + 64 * k2 + 32);
+            const intx8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            const intx4 b0 = qb[2 * k2], b1 = qb[2 * k2 + 1];
+            const intx8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            // format 0 (E4M3) for both operands, no block scaling
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bq, acc, 0, 0, 0, 0, 0, 0);
+        }
+    } else {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const intx4 a = *reinterpret_cast<const intx4*>(k8 + (32 * tt + m) * kK8Stride + 32 * ks + 16 * hf);
+            const intx4 a = *reinterpret_cast<const intx4*>(row + 32 * ks);
             acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qb[ks], acc, 0, 0, 0);
         }
-        s[tt] = acc;
     }
+    return acc;
+}
+// S^T (64 keys x 32 queries) of the low-precision products: two 32x32 tiles.
+template <bool FP8>
+__device__ inline void st_low(const int8_t* k8, const intx4 (&qb)[4], typename LowAcc<FP8>::type (&s)[2]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) s[tt] = st_low_tile<FP8>(k8, qb, tt);
 }
 // S^T in 16-bit (bf16 or fp16 inputs), K = 128 in 8 steps.
 template <bool F16>
@@ -429,17 +479,7 @@ __device__ inline void st_16(const uint8_t* k16, const intx4 (&qb)[8], floatx16 
     }
 }
 
-// One 32-key S^T tile (keys 32tt..32tt+31) of the int8 / 16-bit products.
-__device__ inline intx16 st_int8_tile(const int8_t* k8, const intx4 (&qb)[4], int tt) {
-    const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
-    intx16 acc = {};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const intx4 a = *reinterpret_cast<const intx4*>(k8 + (32 * tt + m) * kK8Stride + 32 * ks + 16 * hf);
-        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qb[ks], acc, 0, 0, 0);
-    }
-    return acc;
-}
+// One 32-key S^T tile (keys 32tt..32tt+31) of the 16-bit products.
 template <bool F16>
 __device__ inline floatx16 st_16_tile(const uint8_t* k16, const intx4 (&qb)[8], int tt) {
     const int lane = threadIdx.x & 63, m = lane & 31, hf = lane >> 5;
@@ -600,7 +640,7 @@ __device__ inline void mask_selected(uint64_t selbits, A (&v)[2], V sentinel) {
         }
 }
 
-template <bool F16>
+template <bool F16, bool FP8>
 __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
     __shared__ Smem sm;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -689,7 +729,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
             float x[2][16];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                const intx16 si = st_int8_tile(sm.k8[0], q8b, tt);
+                const auto si = st_low_tile<FP8>(sm.k8[0], q8b, tt);
                 const floatx16 sb = st_16_tile<F16>(sm.k16, q16b, tt);
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
@@ -801,11 +841,11 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
             }
         }
         __syncthreads();
-        intx16 sA[2], sB[2];
-        st_int8(sm.k8[0], q8b, sA);
+        typename LowAcc<FP8>::type sA[2], sB[2];
+        st_low<FP8>(sm.k8[0], q8b, sA);
         __syncthreads();  // every wave has read K slot 0 before iteration 0 refills it
 
-        auto step = [&](auto P, intx16 (&sc)[2], intx16 (&sn)[2], int kb) {
+        auto step = [&](auto P, typename LowAcc<FP8>::type (&sc)[2], typename LowAcc<FP8>::type (&sn)[2], int kb) {
             constexpr int cur = decltype(P)::value;
             const int kn2 = min(kb + 2, kb_band - 1), kn1 = min(kb + 1, kb_band - 1);
             const uint4 k0 = ld(rk, kn2 * 8192), k1 = ld(rk, kn2 * 8192 + 4096);
@@ -814,7 +854,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
             const uint4 wn = ldw(kn1 * 128);
             // QK of the next block (on the last block: of stale LDS data, unused),
             // unconditional so that it shares the softmax's basic block
-            st_int8(sm.k8[cur ^ 1], q8b, sn);
+            st_low<FP8>(sm.k8[cur ^ 1], q8b, sn);
             const float c8 = sq * p.sk[(size_t)bg * p.nblk + kb] * c16;
             uint4 wt[4];
 #pragma unroll
@@ -846,21 +886,37 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
             }
             if (__builtin_amdgcn_ballot_w64(!(lb <= 32768.0f))) {
                 const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
-                mask_selected(selbits, sc, (int)INT_MIN);
-                int imax = INT_MIN;
+                float bm;
+                if constexpr (FP8) {
+                    mask_selected(selbits, sc, -INFINITY);
+                    float fmx = -INFINITY;
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
+                    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) imax = max(imax, sc[tt][r]);
-                imax = swap_max_i(imax);
-                const float bm = imax == INT_MIN ? -INFINITY : (float)imax * c8;
+                        for (int r = 0; r < 16; ++r) fmx = fmaxf(fmx, sc[tt][r]);
+                    fmx = swap_max(fmx);
+                    bm = fmx == -INFINITY ? -INFINITY : fmx * c8;
+                } else {
+                    mask_selected(selbits, sc, (int)INT_MIN);
+                    int imax = INT_MIN;
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) imax = max(imax, sc[tt][r]);
+                    imax = swap_max_i(imax);
+                    bm = imax == INT_MIN ? -INFINITY : (float)imax * c8;
+                }
                 lazy_rescale(bm, m_ref, l, o);
                 const float nmr = m_ref == -INFINITY ? 0.0f : -m_ref;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        x[tt][r] = sc[tt][r] == INT_MIN ? 0.0f : __builtin_amdgcn_exp2f(fmaf((float)sc[tt][r], c8, nmr));
+                    for (int r = 0; r < 16; ++r) {
+                        bool masked;
+                        if constexpr (FP8) masked = sc[tt][r] == -INFINITY;
+                        else masked = sc[tt][r] == INT_MIN;
+                        x[tt][r] = masked ? 0.0f : __builtin_amdgcn_exp2f(fmaf((float)sc[tt][r], c8, nmr));
+                    }
                 lb = 0.0f;
                 pack_p(x, pb, lb);
             }
@@ -938,6 +994,14 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
     }
 }
 
+template <bool F16, bool FP8>
+void launch_pf(const PfParams& p, const PfLayout& w, int32_t B, int32_t Hq, int32_t Hkv, int32_t T, hipStream_t s) {
+    k_pf_quant_q<F16, FP8><<<dim3(w.nblk, Hq, B), 256, 0, s>>>(p);
+    k_pf_quant_kv<F16, FP8><<<dim3(w.nblk, Hkv, B), 256, 0, s>>>(p);
+    k_pf_gather_sel<F16><<<dim3(w.nsel_tiles, Hkv, B), 256, 0, s>>>(p);
+    k_pf_attn<F16, FP8><<<dim3(((T + kBM - 1) / kBM) * Hq * B), 256, 0, s>>>(p);
+}
+
 }  // namespace
 
 size_t prefill_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, const hq_policy& pol) {
@@ -978,16 +1042,13 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, int32_t B
     p.sel_stride = sel_stride_;
     p.W = pol.window;
     p.c16 = sm_scale * 1.4426950408889634f;
+    const bool fp8 = pol.low_fmt == HQ_LOW_FP8;
     if (f16) {
-        k_pf_quant_q<true><<<dim3(w.nblk, Hq, B), 256, 0, s>>>(p);
-        k_pf_quant_kv<true><<<dim3(w.nblk, Hkv, B), 256, 0, s>>>(p);
-        k_pf_gather_sel<true><<<dim3(w.nsel_tiles, Hkv, B), 256, 0, s>>>(p);
-        k_pf_attn<true><<<dim3(((T + kBM - 1) / kBM) * Hq * B), 256, 0, s>>>(p);
+        if (fp8) launch_pf<true, true>(p, w, B, Hq, Hkv, T, s);
+        else launch_pf<true, false>(p, w, B, Hq, Hkv, T, s);
     } else {
-        k_pf_quant_q<false><<<dim3(w.nblk, Hq, B), 256, 0, s>>>(p);
-        k_pf_quant_kv<false><<<dim3(w.nblk, Hkv, B), 256, 0, s>>>(p);
-        k_pf_gather_sel<false><<<dim3(w.nsel_tiles, Hkv, B), 256, 0, s>>>(p);
-        k_pf_attn<false><<<dim3(((T + kBM - 1) / kBM) * Hq * B), 256, 0, s>>>(p);
+        if (fp8) launch_pf<false, true>(p, w, B, Hq, Hkv, T, s);
+        else launch_pf<false, false>(p, w, B, Hq, Hkv, T, s);
     }
     return hipGetLastError();
 }

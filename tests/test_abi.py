@@ -105,6 +105,7 @@ def test_probe_validation(hq):
     assert _probe(hq, pol=hq.hq_policy(5, 0, 128, 64)) == hq.HQ_ERR_INVALID_ARG
     assert _probe(hq, pol=hq.hq_policy(5, 100, 100, 64)) == hq.HQ_ERR_INVALID_ARG   # window % 64
     assert _probe(hq, pol=hq.hq_policy(101, 100, 128, 64)) == hq.HQ_ERR_INVALID_ARG
+    assert _probe(hq, pol=hq.hq_policy(5, 100, 128, 64, 2)) == hq.HQ_ERR_UNSUPPORTED     # low_fmt
     assert _probe(hq, sm=-1.0) == hq.HQ_ERR_INVALID_ARG
     assert _probe(hq, Tmax=0) == hq.HQ_ERR_INVALID_ARG
     assert _probe(hq, wsb=16) == hq.HQ_ERR_CAPACITY                      # workspace too small

@@ -1,8 +1,9 @@
 """GPU parity of hq_prefill_attn against the oracle's hybrid prefill.
 
-INT8 stage: the Q8/K8 codes and the per-64-block fp32 scales read back from
-the documented workspace prefix are compared bit-exactly with
-oracle.int8_block_quantize. Attention: the fp32 output is compared with
+Low-precision stage (INT8, or FP8 E4M3 with policy.low_fmt): the Q8/K8 code
+bytes and the per-64-block fp32 scales read back from the documented
+workspace prefix are compared bit-exactly with oracle.int8_block_quantize or
+oracle.fp8_block_quantize. Attention: the fp32 output is compared with
 oracle.prefill_attention_block (all rows, small sizes) or
 oracle.prefill_attention_rows (sampled rows, the 16K prefill workload) within
 max-abs 2e-3 and relative L2 1e-3.
@@ -91,7 +92,17 @@ def run_prefill(inp, sels, pol, out_dtype=None):
     return out, ws
 
 
-def check_int8_stage(inp, ws, heads=None):
+def low_quant(x, fp8):
+    """Oracle codes (as stored bytes), block scales and the code values the
+    attention uses (INT8 integers, or decoded E4M3)."""
+    if fp8:
+        c, s = O.fp8_block_quantize(x)
+        return c.view(np.int8), s, O.fp8_e4m3_decode(c)
+    c, s = O.int8_block_quantize(x)
+    return c, s, c
+
+
+def check_int8_stage(inp, ws, heads=None, fp8=False):
     sp = inp.spec
     q8, sq, k8, sk = ws_int8_stage(ws, sp.B, sp.Hq, sp.Hkv, sp.T)
     T = sp.T
@@ -99,18 +110,65 @@ def check_int8_stage(inp, ws, heads=None):
     kf = O.to_f64(inp.k, sp.dtype)
     for b in range(sp.B):
         for g in range(sp.Hkv):
-            c, s = O.int8_block_quantize(kf[b, g])
+            c, s, _ = low_quant(kf[b, g], fp8)
             assert np.array_equal(k8[b, g, :T], c), (b, g)
             assert np.all(k8[b, g, T:] == 0)
             assert np.array_equal(sk[b, g].view(np.uint32), s.view(np.uint32)), (b, g)
         for h in (heads if heads is not None else range(sp.Hq)):
-            c, s = O.int8_block_quantize(qf[b, h])
+            c, s, _ = low_quant(qf[b, h], fp8)
             assert np.array_equal(q8[b, h, :T], c), (b, h)
             assert np.all(q8[b, h, T:] == 0)
             assert np.array_equal(sq[b, h].view(np.uint32), s.view(np.uint32)), (b, h)
 
 
-def oracle_prefill_all(inp, sels, window):
+# The E4M3 matrix instruction (v_mfma_f32_32x32x64_f8f6f4) sums its 64 exact
+# products in a block-aligned format: its error, measured against exact sums
+# on random E4M3 operands spanning the whole format, reaches 2^-12.5 of the
+# sum of |products| (the 16-bit instructions stay within 3 fp32 ulps of it).
+# The FP8 path's bar adds what score errors |delta_j| <= d_j can do to a row,
+# d_j = 2^-11 (a factor 2 of margin) sum_c |Q8_c K8_jc| sQ sK sm_scale on the
+# low-precision keys and 0 on the exact ones. With w the exact softmax
+# weights, the perturbed weights are w'_j = w_j e^delta_j / Z' where
+# e^(-sum w d) <= Z' <= sum w e^d (Jensen), so |w'_j - w_j| <= w_j (e^(d_j + L) - 1),
+# L = ln sum_k w_k e^(d_k), and since sum (w' - w) = 0,
+#   |o'_c - o_c| <= sum_j w_j (e^(d_j + L) - 1) (|v_jc| + |o_c|).
+FP8_SUM_EPS = 2.0 ** -11
+
+
+def fp8_bars(qf, kf, qd, sq, kd, sk, vf, ref, rows, sel, W, sm):
+    """Per-element max-abs bars [len(rows)][D] of the FP8 path: the 2e-3 of
+    the INT8 path plus the bound above (qf, kf: exact 16-bit values of the
+    query head and its KV head; qd, kd: decoded E4M3 codes; ref: the
+    oracle's output rows)."""
+    T = kd.shape[0]
+    cols = np.arange(T)
+    in_sel = np.zeros(T, dtype=bool)
+    in_sel[sel] = True
+    causal = cols[None, :] <= rows[:, None]
+    exact = in_sel[None, :] | (rows[:, None] - cols[None, :] < W)
+    scl = sq.astype(np.float64)[rows // 64][:, None] * sk.astype(np.float64)[cols // 64][None, :]
+    logits = np.where(exact, qf[rows] @ kf.T, (qd[rows] @ kd.T) * scl) * sm
+    logits[~causal] = -np.inf
+    w = np.exp(logits - logits.max(1, keepdims=True))
+    w /= w.sum(1, keepdims=True)
+    d = FP8_SUM_EPS * (np.abs(qd[rows]) @ np.abs(kd).T) * scl * sm
+    d[exact | ~causal] = 0.0
+    L = np.log((w * np.exp(d)).sum(1, keepdims=True))
+    a = w * np.expm1(d + L)
+    return 2e-3 + a @ np.abs(vf) + np.abs(ref) * a.sum(1, keepdims=True)
+
+
+def assert_fp8_rows(out, ref, bars, what):
+    err = np.abs(out - ref)
+    worst = float((err / bars).max())
+    rl2 = float(np.linalg.norm(out - ref) / np.linalg.norm(ref))
+    print(f"{what}: FP8 max-abs {err.max():.3e}, worst error / its bar {worst:.3f} (bars "
+          f"{bars.min():.2e}..{bars.max():.2e}), rel-L2 {rl2:.3e}", flush=True)
+    assert worst <= 1.0, (what, worst)
+    assert rl2 <= 1e-3, (what, rl2)
+
+
+def oracle_prefill_all(inp, sels, window, fp8=False):
     sp = inp.spec
     G = sp.Hq // sp.Hkv
     sm = fp32_scale(D)
@@ -118,9 +176,9 @@ def oracle_prefill_all(inp, sels, window):
     ref = np.empty((sp.B, sp.Hq, sp.T, D))
     for b in range(sp.B):
         for g in range(sp.Hkv):
-            k8, sk = O.int8_block_quantize(kf[b, g])
+            _, sk, k8 = low_quant(kf[b, g], fp8)
             for h in range(g * G, (g + 1) * G):
-                q8, sq = O.int8_block_quantize(qf[b, h])
+                _, sq, q8 = low_quant(qf[b, h], fp8)
                 ref[b, h] = O.prefill_attention_block(qf[b, h], kf[b, g], vf[b, g], sels[b][g], window, sm,
                                                       q8, sq, k8, sk, 0, sp.T)
     return ref
@@ -144,24 +202,42 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_prefill_parity(case):
+FP8_CASES = ["bf16_ragged", "f16_g2", "g8", "no_window", "many_selected", "T1", "T129", "T1000_w64",
+             "all_selected"]
+
+
+@pytest.mark.parametrize("case,fp8", [(c, False) for c in CASES] + [(c, True) for c in CASES if c[0] in FP8_CASES],
+                         ids=[c[0] for c in CASES] + [c[0] + "-fp8" for c in CASES if c[0] in FP8_CASES])
+def test_prefill_parity(case, fp8):
     import kv_cache_amd as hq
     name, B, Hq, Hkv, T, dtype, W, keep, src = case
     spec = PrefillSpec(name=name, B=B, Hq=Hq, Hkv=Hkv, T=T, dtype=dtype, window=W, plant_frac=0.01, seed=77 + T)
     inp = make_prefill_inputs(spec)
-    pol = hq.Policy(keep[0], keep[1], W, 64)
+    pol = hq.Policy(keep[0], keep[1], W, 64, hq.HQ_LOW_FP8 if fp8 else hq.HQ_LOW_INT8)
     if src == "oracle":
         sels = oracle_sel(inp, W, keep)
     else:
         frac = keep[0] / keep[1]
         sels = seeded_sel(B, Hkv, T, frac, seed=T)
-    print(f"prefill case {name}: B={B} Hq={Hq} Hkv={Hkv} T={T} {dtype} W={W} |S|={[len(s) for s in sels[0]]}",
-          flush=True)
+    print(f"prefill case {name}: B={B} Hq={Hq} Hkv={Hkv} T={T} {dtype} W={W} |S|={[len(s) for s in sels[0]]} "
+          f"low={'fp8' if fp8 else 'int8'}", flush=True)
     out, ws = run_prefill(inp, sels, pol)
-    check_int8_stage(inp, ws)
-    ref = oracle_prefill_all(inp, sels, W)
-    assert_attn_close(out.cpu().numpy(), ref, name)
+    check_int8_stage(inp, ws, fp8=fp8)
+    ref = oracle_prefill_all(inp, sels, W, fp8)
+    if fp8:
+        o = out.cpu().numpy()
+        G = Hq // Hkv
+        qf, kf, vf = (O.to_f64(x, dtype) for x in (inp.q, inp.k, inp.v))
+        for b in range(B):
+            for h in range(Hq):
+                _, sq, qd = low_quant(qf[b, h], True)
+                _, sk, kd = low_quant(kf[b, h // G], True)
+                rows = np.arange(T)
+                bars = fp8_bars(qf[b, h], kf[b, h // G], qd, sq, kd, sk, vf[b, h // G], ref[b, h], rows,
+                                sels[b][h // G], W, fp32_scale(D))
+                assert_fp8_rows(o[b, h], ref[b, h], bars, f"{name} b={b} h={h}")
+    else:
+        assert_attn_close(out.cpu().numpy(), ref, name)
     if keep == (100, 100):
         # every candidate selected: exact causal softmax attention
         o = out.cpu().numpy()
@@ -207,9 +283,11 @@ def test_prefill_deterministic():
     assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
 
 
-def test_prefill_16k_full_size():
+@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
+def test_prefill_16k_full_size(fp8):
     """The 16K causal prefill workload (B=1, 32 query / 8 KV heads), launched
-    as the benchmark launches it: the INT8 stage bit-exact for every Q and K
+    as the benchmark launches it (INT8, and the FP8 low path): the
+    low-precision stage bit-exact for every Q and K
     head, and 1,024 rows of every head against the oracle: the last 64 rows,
     runs of 64 rows across the first window / block boundaries and the
     middle block boundary, and 13 runs at seeded random offsets (not aligned
@@ -220,8 +298,8 @@ def test_prefill_16k_full_size():
     spec = CONFIGS["c4_prefill_8b_16k"]
     inp = make_prefill_inputs(spec)
     T, G = spec.T, spec.Hq // spec.Hkv
-    pol = hq.Policy()
-    print("prefill 16k: probe", flush=True)
+    pol = hq.Policy(low_fmt=hq.HQ_LOW_FP8 if fp8 else hq.HQ_LOW_INT8)
+    print(f"prefill 16k ({'fp8' if fp8 else 'int8'}): probe", flush=True)
     q, k = to_dev(inp.q, spec.dtype), to_dev(inp.k, spec.dtype)
     lens = torch.full((1,), T, dtype=torch.int32, device="cuda")
     col, sel, cnt, thr = hq.probe_select(q[:, :, T - 64:].contiguous(), k, lens, pol)
@@ -230,27 +308,31 @@ def test_prefill_16k_full_size():
     del q, k, col, sel, cnt, thr
     print("prefill 16k: attention", flush=True)
     out, ws = run_prefill(inp, sels, pol)
-    check_int8_stage(inp, ws)
-    print("prefill 16k: INT8 stage bit-exact on all heads", flush=True)
+    check_int8_stage(inp, ws, fp8=fp8)
+    print("prefill 16k: low-precision stage bit-exact on all heads", flush=True)
     out = out.cpu().numpy()
     rng = np.random.default_rng(4)
     starts = [T - 64, 96, 8160] + sorted(int(x) for x in rng.integers(0, T - 64, size=13))
     qf, kf, vf = (O.to_f64(x, spec.dtype) for x in (inp.q, inp.k, inp.v))
     sm = fp32_scale(D)
     t0 = time.time()
-    k8s = [O.int8_block_quantize(kf[0, g]) for g in range(spec.Hkv)]
+    k8s = [low_quant(kf[0, g], fp8) for g in range(spec.Hkv)]
     refs = np.zeros((spec.Hq, len(starts) * 64, D))
     rows = np.concatenate([np.arange(r0, r0 + 64) for r0 in starts])
     for h in range(spec.Hq):
         g = h // G
-        k8, sk = k8s[g]
-        q8, sq = O.int8_block_quantize(qf[0, h])
+        _, sk, k8 = k8s[g]
+        _, sq, q8 = low_quant(qf[0, h], fp8)
         for n, r0 in enumerate(starts):
             refs[h, 64 * n:64 * (n + 1)] = O.prefill_attention_block(qf[0, h], kf[0, g], vf[0, g], sels[0][g], 128,
                                                                      sm, q8, sq, k8, sk, r0, r0 + 64)
+        if fp8:
+            bars = fp8_bars(qf[0, h], kf[0, g], q8, sq, k8, sk, vf[0, g], refs[h], rows, sels[0][g], 128, sm)
+            assert_fp8_rows(out[0][h, rows], refs[h], bars, f"16k prefill head {h}")
         if h % 8 == 7:
             print(f"  heads 0..{h} computed ({time.time() - t0:.0f} s)", flush=True)
-    assert_attn_close(out[0][:, rows], refs, f"16k prefill, {len(rows)} rows x {spec.Hq} heads")
+    if not fp8:
+        assert_attn_close(out[0][:, rows], refs, f"16k prefill, {len(rows)} rows x {spec.Hq} heads")
 
 
 def _q_tie_blocks(inp):
@@ -303,3 +385,48 @@ def test_prefill_int8_q_half_integer_quotients():
     torch.cuda.synchronize()
     assert np.isfinite(out.cpu().numpy()).all()
     check_int8_stage(inp, ws)
+
+
+def test_prefill_fp8_q_ties_subnormals_and_signed_zero():
+    """The FP8 Q stage on quotients x / s that sit exactly on the midpoints
+    between E4M3 values (ties to the even mantissa), one bf16 step beside
+    them, in the E4M3 subnormal range, and on signed zeros: Q8 bytes and sQ
+    bit-exact with the oracle's encoder (itself pinned against the format and
+    torch's cast). Block maximum 448 u with u a power of two, so s = u."""
+    import torch
+    import kv_cache_amd as hq
+    from synth import bf16_bits_from_f32
+    spec = PrefillSpec(name="fp8ties", B=1, Hq=2, Hkv=1, T=384, seed=322)
+    inp = make_prefill_inputs(spec)
+    table = O.fp8_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (table[:-1] + table[1:]) / 2                    # exact, and exact in bf16 (<= 5 significant bits)
+    rng = np.random.default_rng(77)
+    for h in range(2):
+        for blk in range(spec.T // 64):
+            u = 2.0 ** int(rng.integers(-12, 4))
+            x = rng.choice(mids, size=(64, D)) * np.where(rng.random((64, D)) < 0.5, -1.0, 1.0)
+            x[:8] = rng.choice(table[:8], size=(8, D)) / 3.0     # subnormal quotients (rounded in bf16 first)
+            x[8, :] = 0.0
+            x[9, :] = -0.0
+            x[rng.integers(10, 64), rng.integers(0, D)] = 448.0
+            bits = bf16_bits_from_f32((x * u).astype(np.float32))
+            step = rng.integers(-1, 2, size=bits.shape) * (rng.random(bits.shape) < 0.2)
+            keep = (np.abs(x) == 448.0) | (np.abs(x) == 0.0)
+            bits = np.where(keep, bits, (bits.astype(np.int32) + step).astype(np.uint16))
+            inp.q[0, h, 64 * blk:64 * (blk + 1)] = bits
+    qf = O.to_f64(inp.q, "bf16")
+    c, s = O.fp8_block_quantize(qf[0, 0])
+    quo = qf[0, 0].astype(np.float32) / np.repeat(s, 64)[:, None]
+    on_mid = np.isin(np.abs(quo.astype(np.float64)), mids)
+    assert np.count_nonzero(on_mid) > 3000 and np.any((c & 0x78) == 0) and np.any(c == 0x80)
+    pol = hq.Policy(low_fmt=hq.HQ_LOW_FP8)
+    sels = oracle_sel(inp, 128, (5, 100))
+    stride = hq.sel_stride(spec.T, pol)
+    idx, cnt = sel_device(sels, 1, 1, stride)
+    q, k, v = (to_dev(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    n = hq.lib.hq_prefill_ws_bytes(1, 2, 1, spec.T, D, __import__("ctypes").byref(pol.c()))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    out = hq.prefill_attn(q, k, v, idx, cnt, pol, sm_scale=2.0 ** -8, ws=ws)
+    torch.cuda.synchronize()
+    assert np.isfinite(out.cpu().numpy()).all()
+    check_int8_stage(inp, ws, fp8=True)
