@@ -168,6 +168,34 @@ def prefill_roofline(T, W, sel_idx, sel_cnt, G, ms):
             "floor_us": round(floor_s * 1e6, 1), "int8_qk_pair_frac": round(low / (exact + low), 4)}
 
 
+def prefill_low_error(hq, pf, psel, pol, polf, heads=4, nrows=512):
+    """Output error of the INT8 and the FP8 low-precision paths against exact
+    causal attention (fp64, plain torch on the device) on the last `nrows`
+    rows of the first `heads` query heads: the pages' open question of FP8 as
+    another precision point, measured on the seeded inputs."""
+    import torch
+    T = pf["spec"].T
+    outs = {}
+    for name, p in (("int8", pol), ("fp8", polf)):
+        o = hq.prefill_attn(pf["q"], pf["k"], pf["v"], psel[1], psel[2], p)
+        outs[name] = o[0, :heads, T - nrows:].double()
+    G = pf["spec"].Hq // pf["spec"].Hkv
+    q = pf["q"][0, :heads, T - nrows:].double()
+    k = pf["k"][0, [h // G for h in range(heads)]].double()
+    v = pf["v"][0, [h // G for h in range(heads)]].double()
+    s = torch.matmul(q, k.transpose(1, 2).contiguous()) / math.sqrt(q.shape[-1])
+    i = torch.arange(T - nrows, T, device=s.device)[:, None]
+    s = s.masked_fill(torch.arange(T, device=s.device)[None, :] > i, float("-inf"))
+    ref = torch.matmul(torch.softmax(s, -1), v)
+    err = {}
+    for name, o in outs.items():
+        d = o - ref
+        err[f"{name}_rel_l2_vs_exact"] = float(d.norm() / ref.norm())
+        err[f"{name}_max_abs_vs_exact"] = float(d.abs().max())
+    err["error_sample"] = f"last {nrows} rows of query heads 0..{heads - 1}"
+    return {k2: (round(v2, 7) if isinstance(v2, float) else v2) for k2, v2 in err.items()}
+
+
 def committed_traffic(profile, source, key):
     """HBM bytes per call from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary (each counter scaled by the factor a plain copy of known size
@@ -825,6 +853,7 @@ def main():
         fr = prefill_roofline(psp.T, pol.window, psel_idx, psel_cnt, psp.Hq // psp.Hkv, fms)
         res["prefill_fp8"] = {"ms": round(fms, 3), "TFLOPs": round(fl / (fms * 1e-3) / 1e12, 1),
                               "frac": fr["frac"], "low_fmt": "OCP FP8 E4M3, per-64-token block scale"}
+        res["prefill_fp8"].update(prefill_low_error(hq, pf, psel, pol, polf))
     sels = tuple(t.cpu().numpy() for t in (hq.probe_select(qp, k, lens, pol)))
     del cache, k, v, knew, vnew
     if pf is not None:
