@@ -421,6 +421,21 @@ def _decode_workload(hq, name, steps, warmup, cold_mib=0):
     rec["frac_of_peak_graph"] = round(by / (gus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
     if spec.ragged_min is not None:
         rec["seq_lens"] = [int(x) for x in inp.seq_lens]
+        # the same batch in the ragged INT4 layout (hq_cache_layout_ragged):
+        # each sequence sized for its own prompt plus the decode tokens
+        caps = [int(x) + n for x in inp.seq_lens]
+        rcache = hq.HybridCache(spec.B, spec.Hkv, caps, spec.T, dt, dev, pol)
+        hq.quantize_kv(rcache, k, v, lens, sel, cnt, col, thr)
+        tr = Timer()
+        for i in range(n):
+            hq.append_kv(rcache, knew[i], vnew[i])
+            tr("decode_attn", hq.decode_attn, rcache, qd[i], None, out)
+        torch.cuda.synchronize()
+        pool = lambda sz: int(sz.k_codes + sz.v_codes + sz.k_meta + sz.v_meta + sz.q_pos)
+        rec["ragged_layout"] = {"int4_store_bytes": pool(rcache.sizes), "uniform_int4_store_bytes": pool(cache.sizes),
+                                "decode_us": tr.pct("decode_attn", 1e3)[1],
+                                "same_counts": bool(torch.equal(rcache.counts(), cache.counts()))}
+        del rcache
     if cold_mib:
         scrub = torch.empty(cold_mib << 20, dtype=torch.uint8, device=dev)
         tc = Timer()

@@ -188,6 +188,16 @@ typedef struct {
                              (nothing stored); 4 quantize: selected positions
                              not ascending candidates (the entries before the
                              first bad one are stored)                      */
+    /* Ragged INT4 layout (hq_cache_layout_ragged); NULL / 0 for the uniform
+     * one above. q_tile_off: device [B*Hkv + 1] int64, ascending: the INT4
+     * store of (b, g) is tiles [q_tile_off[bg], q_tile_off[bg+1]) of
+     * k_codes / v_codes / k_meta / v_meta (4096 / 4096 / 1024 / 1024 bytes
+     * per tile) and slots [64 q_tile_off[bg], ...) of q_pos; cap_q is the
+     * largest per-(b, g) capacity. q_tiles_total: tiles in each of those
+     * buffers. A span that is not ascending or leaves [0, q_tiles_total) is
+     * treated as empty (nothing read or written there).                    */
+    const int64_t* q_tile_off;
+    int64_t q_tiles_total;
 } hq_cache;
 
 typedef struct {
@@ -210,6 +220,26 @@ typedef struct {
 hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens,
                           int32_t cap_probe, hq_dtype dt, const hq_policy* policy,
                           hq_cache_sizes* out);
+
+/* The ragged INT4 layout: a host-side allocator for batches whose sequences
+ * have different capacities (serving: each sequence sized for its own prompt
+ * plus its own decode budget, instead of every (b, g) sized for the longest).
+ * Pages: "How HyQuant uses ...", "Reported speedups: kernel gains are not
+ * end-to-end gains" (the serving system around the kernel decides the end to
+ * end gain) and "Memory and runtime costs" (the memory the cache takes).
+ * Sequence b gets round64(cap_tokens[b] - min(window, cap_tokens[b])) INT4
+ * slots (at least 64), for each of its Hkv heads, packed back to back in
+ * (b, g) order: q_tile_off (host [B*Hkv + 1], written) holds the tile
+ * offsets, to be copied to the device for hq_cache.q_tile_off. The kept
+ * store, ring and per-(b, g) arrays keep the uniform layout of
+ * max(max cap_tokens, cap_probe) (cap_probe may exceed every capacity when
+ * the prompts were probed padded to a common length). out receives every
+ * buffer's bytes (the INT4 pools sized by the total) and out->cap_q = that
+ * uniform layout's INT4 capacity, at least every sequence's.
+ * Errors as hq_cache_layout, checked for every cap_tokens[b].            */
+hq_status hq_cache_layout_ragged(int32_t B, int32_t Hkv, int32_t D, const int32_t* cap_tokens,
+                                 int32_t cap_probe, hq_dtype dt, const hq_policy* policy,
+                                 int64_t* q_tile_off, hq_cache_sizes* out);
 
 /* ------------------------------------------------------------------------
  * hq_quantize_kv -- build the hybrid cache from a prompt's K and V.

@@ -23,6 +23,7 @@ EXPORTED = (
     "hq_probe_select", "hq_probe_ws_bytes", "hq_quantize_kv", "hq_append_kv", "hq_decode_attn",
     "hq_decode_ws_bytes", "hq_decode_attn_noalloc", "hq_prefill_attn", "hq_prefill_ws_bytes", "hq_cache_layout", "hq_sel_stride",
     "hq_last_error", "hq_diag_read_int4", "hq_diag_read_int4_sink_bytes", "hq_reprobe", "hq_reprobe_ws_bytes",
+    "hq_cache_layout_ragged",
 )
 
 
@@ -47,7 +48,8 @@ _CACHE_PTRS = ("k_codes", "v_codes", "k_meta", "v_meta", "k_keep", "v_keep", "k_
 
 class hq_cache(ctypes.Structure):
     _fields_ = ([(n, ctypes.c_int32) for n in ("B", "Hkv", "D", "window", "cap_q", "cap_keep", "cap_probe", "dt")]
-                + [(n, ctypes.c_void_p) for n in _CACHE_PTRS])
+                + [(n, ctypes.c_void_p) for n in _CACHE_PTRS]
+                + [("q_tile_off", ctypes.c_void_p), ("q_tiles_total", ctypes.c_int64)])
 
 
 class hq_cache_sizes(ctypes.Structure):
@@ -76,6 +78,8 @@ def _load():
         "hq_prefill_attn": (I, [P, P, P, I, I, I, I, I, I, pol, P, P, F, P, I, P, S, V]),
         "hq_prefill_ws_bytes": (S, [I, I, I, I, I, pol]),
         "hq_cache_layout": (I, [I, I, I, I, I, I, pol, ctypes.POINTER(hq_cache_sizes)]),
+        "hq_cache_layout_ragged": (I, [I, I, I, ctypes.POINTER(ctypes.c_int32), I, I, pol,
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(hq_cache_sizes)]),
         "hq_sel_stride": (I, [I, pol]),
         "hq_last_error": (ctypes.c_char_p, []),
         "hq_diag_read_int4": (I, [ctypes.POINTER(hq_cache), P, S, V]),
@@ -176,9 +180,11 @@ def probe_select(q_probe, k, seq_lens, policy: Policy = Policy(), sm_scale: floa
 
 
 class HybridCache:
-    """Caller-owned buffers of the hybrid KV cache (hq_cache)."""
+    """Caller-owned buffers of the hybrid KV cache (hq_cache). cap_tokens is
+    one capacity for every sequence (the uniform layout) or a list of B
+    capacities (the ragged INT4 layout of hq_cache_layout_ragged)."""
 
-    def __init__(self, B: int, Hkv: int, cap_tokens: int, cap_probe: int, dtype, device,
+    def __init__(self, B: int, Hkv: int, cap_tokens, cap_probe: int, dtype, device,
                  policy: Policy = Policy(), D: int = 128):
         torch = _torch()
         self.policy = policy
@@ -186,8 +192,17 @@ class HybridCache:
         if dt is None:
             raise TypeError("cache dtype must be bf16 or fp16")
         sz = hq_cache_sizes()
-        _check(lib.hq_cache_layout(B, Hkv, D, cap_tokens, cap_probe, dt, ctypes.byref(policy.c()),
-                                   ctypes.byref(sz)))
+        ragged = not isinstance(cap_tokens, int)
+        if ragged:
+            caps = (ctypes.c_int32 * B)(*[int(x) for x in cap_tokens])
+            offs = (ctypes.c_int64 * (B * Hkv + 1))()
+            _check(lib.hq_cache_layout_ragged(B, Hkv, D, caps, cap_probe, dt, ctypes.byref(policy.c()), offs,
+                                              ctypes.byref(sz)))
+            self.q_tile_off = list(offs)
+        else:
+            _check(lib.hq_cache_layout(B, Hkv, D, cap_tokens, cap_probe, dt, ctypes.byref(policy.c()),
+                                       ctypes.byref(sz)))
+            self.q_tile_off = None
         self.sizes = sz
         self.bufs = {}
         c = hq_cache(B=B, Hkv=Hkv, D=D, window=policy.window, cap_q=sz.cap_q, cap_keep=sz.cap_keep,
@@ -197,6 +212,11 @@ class HybridCache:
             t = torch.zeros(nbytes, dtype=torch.uint8, device=device)
             self.bufs[name] = t
             setattr(c, name, t.data_ptr())
+        if ragged:
+            t = torch.tensor(self.q_tile_off, dtype=torch.int64, device=device)
+            self.bufs["q_tile_off"] = t
+            c.q_tile_off = t.data_ptr()
+            c.q_tiles_total = self.q_tile_off[-1]
         self.c = c
         self.B, self.Hkv, self.D, self.dtype, self.device = B, Hkv, D, dtype, device
         self._ws = None

@@ -91,6 +91,11 @@ hq_status check_cache(const char* fn, const hq_cache* c) {
     REQ_PTR(c->col_scores);
     REQ_PTR(c->thresh);
     if (c->err_flag == nullptr) return fail(HQ_ERR_INVALID_ARG, "%s: cache err_flag is null", fn);
+    if (c->q_tile_off != nullptr) {
+        REQ_PTR(c->q_tile_off);
+        if (c->q_tiles_total < 1)
+            return fail(HQ_ERR_INVALID_ARG, "%s: ragged layout needs q_tiles_total >= 1", fn);
+    }
     return HQ_OK;
 }
 
@@ -183,6 +188,42 @@ hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens,
     out->col_scores = BG * (size_t)cap_probe * 4;
     out->thresh = BG * sizeof(hq_thresh);
     out->err_flag = 4;
+    return HQ_OK;
+}
+
+hq_status hq_cache_layout_ragged(int32_t B, int32_t Hkv, int32_t D, const int32_t* cap_tokens, int32_t cap_probe,
+                                 hq_dtype dt, const hq_policy* policy, int64_t* q_tile_off, hq_cache_sizes* out) {
+    static const char* fn = "hq_cache_layout_ragged";
+    clear_err();
+    hq_status st = check_policy(fn, policy);
+    if (st) return st;
+    if (!out || !cap_tokens || !q_tile_off) return fail(HQ_ERR_INVALID_ARG, "%s: null argument", fn);
+    if (B < 1 || Hkv < 1) return fail(HQ_ERR_INVALID_ARG, "%s: B and Hkv must be >= 1", fn);
+    int32_t cmax = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        if (cap_tokens[b] < 1) return fail(HQ_ERR_INVALID_ARG, "%s: cap_tokens[%d] = %d out of range", fn, b, cap_tokens[b]);
+        if (cap_tokens[b] > hq::kMaxCapTokens)
+            return fail(HQ_ERR_CAPACITY, "%s: cap_tokens[%d] = %d exceeds %d", fn, b, cap_tokens[b], hq::kMaxCapTokens);
+        cmax = std::max(cmax, cap_tokens[b]);
+    }
+    // every buffer but the INT4 pools as for the uniform layout of the longest
+    // sequence (or of the probe's positions, when the prompts were probed
+    // padded to a longer length than any sequence's capacity)
+    if (cap_probe < 1) return fail(HQ_ERR_INVALID_ARG, "%s: cap_probe %d out of range", fn, cap_probe);
+    if ((st = hq_cache_layout(B, Hkv, D, std::max(cmax, cap_probe), cap_probe, dt, policy, out))) return st;
+    int64_t off = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t wq = std::min(policy->window, cap_tokens[b]);
+        const int64_t tiles = std::max(hq::kTile, hq::round_up(cap_tokens[b] - wq, hq::kTile)) / hq::kTile;
+        for (int32_t g = 0; g < Hkv; ++g) {
+            q_tile_off[(size_t)b * Hkv + g] = off;
+            off += tiles;
+        }
+    }
+    q_tile_off[(size_t)B * Hkv] = off;
+    out->k_codes = out->v_codes = (size_t)off * hq::kTileBytesQ;
+    out->k_meta = out->v_meta = (size_t)off * 1024;
+    out->q_pos = (size_t)off * hq::kTile * 4;
     return HQ_OK;
 }
 

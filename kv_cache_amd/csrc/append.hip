@@ -72,11 +72,12 @@ __global__ __launch_bounds__(64) void k_append(hq_cache c, const uint16_t* k_new
                 n_keep += 1;
             }
         } else {
-            overflow = n_q >= c.cap_q;
+            const QSpan qs = q_span(c, bg);
+            overflow = n_q >= qs.tiles * kTile;
             if (!overflow) {
                 const int n = n_q, tile = n / kTile, ts = n % kTile;
-                const size_t tb = ((size_t)bg * (c.cap_q / kTile) + tile) * kTileBytesQ;
-                const size_t mb = ((size_t)bg * (c.cap_q / kTile) + tile) * (kTile * 16);
+                const size_t tb = ((size_t)qs.tile0 + tile) * kTileBytesQ;
+                const size_t mb = ((size_t)qs.tile0 + tile) * (kTile * 16);
                 __shared__ uint32_t vwords[4][4];  // canonical V words of the departing token
                 if (lane < 8) {
                     const bool isv = lane >= 4;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(64) void k_append(hq_cache c, const uint16_t* k_new
                     uint32_t* wp = reinterpret_cast<uint32_t*>(vc + vq_word(ts, ch));
                     *wp = (*wp & ~(0xFu << sh)) | (code << sh);
                 }
-                if (lane == 0) c.q_pos[(size_t)bg * c.cap_q + n] = d;
+                if (lane == 0) c.q_pos[(size_t)qs.tile0 * kTile + n] = d;
                 n_q += 1;
             }
         }

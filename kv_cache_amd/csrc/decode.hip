@@ -246,7 +246,7 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
         return;
     }
 
-    const int qt_cap = p.c.cap_q / kTile, kt_cap = p.c.cap_keep / kTile, wt_cap = W / kTile;
+    const int kt_cap = p.c.cap_keep / kTile, wt_cap = W / kTile;
     // the 16-bit tiles take the query's own words: word h*64 + c holds channels 2c, 2c + 1 of head h
     const uint32_t* qn = p.qw + ((size_t)bg * p.G + half * G) * (kD / 2);  // Hq = Hkv * p.G
 
@@ -278,16 +278,21 @@ __device__ __attribute__((always_inline)) inline void split_body(const DecodePar
         struct TileRegs {
             uint4 kd[4], kmv, vmv, vd[4];
         };
-        const int wq = qt_cap * kTileBytesQ;  // bytes of one (b, g)'s INT4 codes / metadata
+        // one (b, g)'s INT4 codes / metadata: its span of the pools, as buffer
+        // resources whose range check keeps every load inside the span
+        const QSpan qs = q_span(p.c, bg);
+        const int wq = qs.tiles * kTileBytesQ;
         const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(reinterpret_cast<const uint8_t*>(p.c.k_codes) + (size_t)bg * wq), (short)0, wq, 0x00020000);
+            (void*)(reinterpret_cast<const uint8_t*>(p.c.k_codes) + (size_t)qs.tile0 * kTileBytesQ), (short)0, wq,
+            0x00020000);
         const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(reinterpret_cast<const uint8_t*>(p.c.v_codes) + (size_t)bg * wq), (short)0, wq, 0x00020000);
+            (void*)(reinterpret_cast<const uint8_t*>(p.c.v_codes) + (size_t)qs.tile0 * kTileBytesQ), (short)0, wq,
+            0x00020000);
         const __amdgpu_buffer_rsrc_t rkm = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(reinterpret_cast<const uint8_t*>(p.c.k_meta) + (size_t)bg * qt_cap * 1024), (short)0, qt_cap * 1024,
+            (void*)(reinterpret_cast<const uint8_t*>(p.c.k_meta) + (size_t)qs.tile0 * 1024), (short)0, qs.tiles * 1024,
             0x00020000);
         const __amdgpu_buffer_rsrc_t rvm = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(reinterpret_cast<const uint8_t*>(p.c.v_meta) + (size_t)bg * qt_cap * 1024), (short)0, qt_cap * 1024,
+            (void*)(reinterpret_cast<const uint8_t*>(p.c.v_meta) + (size_t)qs.tile0 * 1024), (short)0, qs.tiles * 1024,
             0x00020000);
         const int voff = lane * 16;
         auto ld = [&](const __amdgpu_buffer_rsrc_t& r, int soff) {

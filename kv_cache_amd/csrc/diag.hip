@@ -21,17 +21,17 @@ __global__ __launch_bounds__(256, 2) void k_diag_read_int4(const hq_cache c, uin
     const int n_q = c.counts[4 * bg + 1];
     const int nqt = (n_q + kTile - 1) / kTile;
     const int v0 = s * nqt / nsq, v1 = (s + 1) * nqt / nsq;
-    const int qt_cap = c.cap_q / kTile;
-    const int wq = qt_cap * kTileBytesQ;
+    const QSpan qs = q_span(c, bg);
+    const int wq = qs.tiles * kTileBytesQ;
     const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(reinterpret_cast<const uint8_t*>(c.k_codes) + (size_t)bg * wq), (short)0, wq, 0x00020000);
+        (void*)(reinterpret_cast<const uint8_t*>(c.k_codes) + (size_t)qs.tile0 * kTileBytesQ), (short)0, wq, 0x00020000);
     const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(reinterpret_cast<const uint8_t*>(c.v_codes) + (size_t)bg * wq), (short)0, wq, 0x00020000);
+        (void*)(reinterpret_cast<const uint8_t*>(c.v_codes) + (size_t)qs.tile0 * kTileBytesQ), (short)0, wq, 0x00020000);
     const __amdgpu_buffer_rsrc_t rkm = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(reinterpret_cast<const uint8_t*>(c.k_meta) + (size_t)bg * qt_cap * 1024), (short)0, qt_cap * 1024,
+        (void*)(reinterpret_cast<const uint8_t*>(c.k_meta) + (size_t)qs.tile0 * 1024), (short)0, qs.tiles * 1024,
         0x00020000);
     const __amdgpu_buffer_rsrc_t rvm = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(reinterpret_cast<const uint8_t*>(c.v_meta) + (size_t)bg * qt_cap * 1024), (short)0, qt_cap * 1024,
+        (void*)(reinterpret_cast<const uint8_t*>(c.v_meta) + (size_t)qs.tile0 * 1024), (short)0, qs.tiles * 1024,
         0x00020000);
     const int voff = lane * 16;
     auto ld = [&](const __amdgpu_buffer_rsrc_t& r, int soff) {

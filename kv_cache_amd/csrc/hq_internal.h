@@ -88,6 +88,22 @@ __host__ __device__ inline int v16_off(int slot, int chunk) {
     return (slot & 15) * 1024 + (16 * (slot >> 4) + chunk) * 16;
 }
 
+// INT4 store of one (b, g): its first tile in the pools and its capacity in
+// tiles. Uniform layout: tiles [bg cap_q/64, (bg + 1) cap_q/64). Ragged
+// layout: the span q_tile_off[bg] .. q_tile_off[bg + 1], empty if it is not
+// ascending, leaves [0, q_tiles_total) or exceeds cap_q/64 tiles.
+struct QSpan {
+    int64_t tile0;
+    int32_t tiles;
+};
+__host__ __device__ inline QSpan q_span(const hq_cache& c, int bg) {
+    const int32_t qt = c.cap_q / kTile;
+    if (c.q_tile_off == nullptr) return {(int64_t)bg * qt, qt};
+    const int64_t a = c.q_tile_off[bg], b = c.q_tile_off[bg + 1];
+    if (a < 0 || b < a || b > c.q_tiles_total || b - a > qt) return {0, 0};
+    return {a, (int32_t)(b - a)};
+}
+
 // Device-side counters of one (b, g).
 struct Counts {
     int32_t seq_len, n_q, n_keep, probe_len;

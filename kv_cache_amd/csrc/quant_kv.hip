@@ -60,6 +60,11 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
         return;
     }
     const int n_q = T - k - nwin;
+    const QSpan qs = q_span(p.c, bg);
+    if (n_q > qs.tiles * kTile) {  // the (b, g)'s INT4 capacity (ragged layout)
+        if (tid == 0) atomicOr(p.c.err_flag, 1);
+        return;
+    }
     const int qt = p.c.cap_q / kTile, kt = p.c.cap_keep / kTile;
     int tile = blockIdx.x;
     const uint16_t* krows = p.k + (size_t)bg * p.Tmax * kD;
@@ -102,8 +107,8 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
         __shared__ uint32_t vstage[kTile][4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) vstage[t][grp][i] = valid ? vp[i] : 0u;
-        const size_t tile_base = ((size_t)bg * qt + tile) * kTileBytesQ;
-        const size_t meta_base = ((size_t)bg * qt + tile) * (kTile * 16);
+        const size_t tile_base = ((size_t)qs.tile0 + tile) * kTileBytesQ;
+        const size_t meta_base = ((size_t)qs.tile0 + tile) * (kTile * 16);
         uint8_t* kc = reinterpret_cast<uint8_t*>(p.c.k_codes) + tile_base;
         uint8_t* vc = reinterpret_cast<uint8_t*>(p.c.v_codes) + tile_base;
         if (valid) {
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantParams p) {
             *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.c.k_meta) + meta_base + kmeta_word(t, grp)) =
                 ks | (kz << 16);
             st_nt(reinterpret_cast<uint8_t*>(p.c.v_meta) + meta_base + vmeta_word(t, grp), (uint32_t)(vs | (vz << 16)));
-            if (grp == 0) p.c.q_pos[(size_t)bg * p.c.cap_q + n] = pos;
+            if (grp == 0) p.c.q_pos[(size_t)qs.tile0 * kTile + n] = pos;
         }
         __syncthreads();
         // 1024 V words per tile: word (channel ch, slot octet o) holds slots

@@ -59,9 +59,10 @@ __global__ __launch_bounds__(256) void k_reprobe_expand(ExpandParams p) {
         uint4 val;
         uint8_t flag = 0;
         if (kind == 0) {
-            if (i >= min(cn.n_q, p.c.cap_q)) continue;
-            pos = p.c.q_pos[(size_t)bg * p.c.cap_q + i];
-            const size_t tb = (size_t)bg * (p.c.cap_q / kTile) + lt;
+            const QSpan qs = q_span(p.c, bg);
+            if (i >= min(cn.n_q, qs.tiles * kTile)) continue;
+            pos = p.c.q_pos[(size_t)qs.tile0 * kTile + i];
+            const size_t tb = (size_t)qs.tile0 + lt;
             const uint32_t w =
                 *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.c.k_codes) + tb * kTileBytesQ +
                                                    kq_word(s, 8 * ch));

@@ -75,6 +75,17 @@ def read_cache(cache) -> dict:
     c = cache.c
     BG = c.B * c.Hkv
     host = {k: v.cpu().numpy() for k, v in cache.bufs.items()}
+    if getattr(cache, "q_tile_off", None) is not None:
+        # ragged INT4 pools: each (b, g)'s span copied into the uniform
+        # [BG][cap_q] arrangement (zero past its capacity)
+        off, qt = cache.q_tile_off, c.cap_q // 64
+        for name, per_tile in (("k_codes", 4096), ("v_codes", 4096), ("k_meta", 1024), ("v_meta", 1024),
+                               ("q_pos", 256)):
+            dense = np.zeros(BG * qt * per_tile, dtype=np.uint8)
+            for bg in range(BG):
+                a, b = off[bg], off[bg + 1]
+                dense[bg * qt * per_tile:(bg * qt + b - a) * per_tile] = host[name][a * per_tile:b * per_tile]
+            host[name] = dense
     d = {
         "counts": host["counts"][: BG * 16].view(np.int32).reshape(c.B, c.Hkv, 4),
         "k_codes": unpack_k_codes(host["k_codes"][: BG * c.cap_q * 64], BG, c.cap_q),

@@ -242,3 +242,42 @@ def test_reprobe_validation(hq):
     big = _cache(hq, cap_q=(1 << 24) - 64, cap_keep=128)
     assert call(cache=big) == hq.HQ_ERR_CAPACITY
     assert hq.lib.hq_reprobe_ws_bytes(ctypes.byref(big), 4, ctypes.byref(pol)) == 0
+
+
+def test_cache_layout_ragged_closed_form(hq):
+    """Per-sequence INT4 capacities round64(cap - min(W, cap)) (at least 64),
+    packed back to back in (b, g) order; every other buffer as the uniform
+    layout of the longest sequence; equal capacities give the uniform sizes."""
+    pol = hq.Policy()
+    caps = [700, 3000, 129, 64]
+    B, Hkv = len(caps), 3
+    c_caps = (ctypes.c_int32 * B)(*caps)
+    offs = (ctypes.c_int64 * (B * Hkv + 1))()
+    rg, un = hq.hq_cache_sizes(), hq.hq_cache_sizes()
+    assert hq.lib.hq_cache_layout_ragged(B, Hkv, 128, c_caps, 2000, hq.HQ_BF16, ctypes.byref(pol.c()), offs,
+                                         ctypes.byref(rg)) == 0
+    assert hq.lib.hq_cache_layout(B, Hkv, 128, 3000, 2000, hq.HQ_BF16, ctypes.byref(pol.c()), ctypes.byref(un)) == 0
+    tiles = [max(64, -(-(cap - min(128, cap)) // 64) * 64) // 64 for cap in caps]
+    assert tiles == [9, 45, 1, 1]
+    expect = [0]
+    for b in range(B):
+        for _ in range(Hkv):
+            expect.append(expect[-1] + tiles[b])
+    assert list(offs) == expect
+    total = expect[-1]
+    assert rg.k_codes == rg.v_codes == total * 4096 and rg.k_meta == rg.v_meta == total * 1024
+    assert rg.q_pos == total * 64 * 4
+    assert rg.cap_q == un.cap_q == 45 * 64
+    for n in ("k_keep", "v_keep", "k_win", "v_win", "keep_pos", "counts", "col_scores", "thresh", "err_flag"):
+        assert getattr(rg, n) == getattr(un, n), n
+    assert rg.k_codes < un.k_codes
+    same = (ctypes.c_int32 * B)(*([3000] * B))
+    assert hq.lib.hq_cache_layout_ragged(B, Hkv, 128, same, 2000, hq.HQ_BF16, ctypes.byref(pol.c()), offs,
+                                         ctypes.byref(rg)) == 0
+    for n in hq._CACHE_PTRS:
+        assert getattr(rg, n) == getattr(un, n), n
+    bad = (ctypes.c_int32 * B)(700, 0, 129, 64)
+    assert hq.lib.hq_cache_layout_ragged(B, Hkv, 128, bad, 2000, hq.HQ_BF16, ctypes.byref(pol.c()), offs,
+                                         ctypes.byref(rg)) == hq.HQ_ERR_INVALID_ARG
+    c = _cache(hq, q_tile_off=0x100000, q_tiles_total=0)
+    assert hq.lib.hq_append_kv(ctypes.byref(c), FAKE, FAKE, None) == hq.HQ_ERR_INVALID_ARG
