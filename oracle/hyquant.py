@@ -494,7 +494,8 @@ def fp8_block_quantize(x: np.ndarray):
 
 def prefill_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_idx: np.ndarray,
                            window: int, sm_scale: float, q8: np.ndarray, sq: np.ndarray,
-                           k8: np.ndarray, sk: np.ndarray, rows: np.ndarray) -> np.ndarray:
+                           k8: np.ndarray, sk: np.ndarray, rows: np.ndarray,
+                           route: np.ndarray | None = None) -> np.ndarray:
     """Causal hybrid-precision attention for one query head, selected rows (O8).
 
     [HQ-abs] (Prefill stage) and [HQ-news] "What hybrid-precision attention
@@ -510,7 +511,9 @@ def prefill_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_idx:
     q: [T][D], k, v: [T][D] (this head's KV head), q8/sq: this query head's
     INT8 codes/scales, k8/sk: the KV head's; rows: query positions to compute.
     With the FP8 low path (O11), q8 and k8 are the decoded E4M3 values
-    (fp8_e4m3_decode of the codes) and sq, sk the FP8 block scales.
+    (fp8_e4m3_decode of the codes) and sq, sk the FP8 block scales. route
+    (O12, optional): bool [ceil(T/128)][ceil(T/64)]; a routed tile's
+    scores are exact as well.
     Returns [len(rows)][D].
     """
     T, D = k.shape
@@ -525,6 +528,8 @@ def prefill_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_idx:
         exact = k[:i + 1] @ q[i]
         low = (k8f[:i + 1] @ q8[i].astype(np.float64)) * float(sq[i // INT8_BLOCK]) * skf[:i + 1]
         use_exact = in_sel[:i + 1] | (i - j < window)
+        if route is not None:
+            use_exact = use_exact | route[i // TILE_ROWS][j // INT8_BLOCK]
         logits = np.where(use_exact, exact, low) * sm_scale
         m = logits.max()
         e = np.exp(logits - m)
@@ -534,7 +539,8 @@ def prefill_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_idx:
 
 def prefill_attention_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_idx: np.ndarray,
                             window: int, sm_scale: float, q8: np.ndarray, sq: np.ndarray,
-                            k8: np.ndarray, sk: np.ndarray, r0: int, r1: int) -> np.ndarray:
+                            k8: np.ndarray, sk: np.ndarray, r0: int, r1: int,
+                            route: np.ndarray | None = None) -> np.ndarray:
     """Same definition as prefill_attention_rows for the contiguous rows
     [r0, r1), written with matrix products (one fp64 GEMM per precision)."""
     T, D = k.shape
@@ -548,11 +554,61 @@ def prefill_attention_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_idx
     low *= sk.astype(np.float64)[cols // INT8_BLOCK][None, :]
     diff = rows[:, None] - cols[None, :]
     use_exact = in_sel[None, :] | (diff < window)
+    if route is not None:
+        use_exact = use_exact | route[rows // TILE_ROWS][:, cols // INT8_BLOCK]
     logits = np.where(use_exact, exact, low) * sm_scale
     logits[diff < 0] = -np.inf
     m = logits.max(axis=1, keepdims=True)
     e = np.exp(logits - m)
     return (e @ v[:r1]) / e.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# O12: tile-level precision routing composed with the token routing
+# ---------------------------------------------------------------------------
+
+TILE_ROWS = 128  # query rows of a routed tile (the key side is one 64-token INT8 block)
+
+
+def tile_route(q8: np.ndarray, k8: np.ndarray, sk: np.ndarray, T: int, window: int,
+               num: int, den: int) -> np.ndarray:
+    """Which (128-row query block, 64-key block) tiles take the 16-bit path (O12).
+
+    [HQ-wiki] "How this relates to prior wiki pages" and "Gaps": TileMix
+    routes tiles of the score matrix between an FP16 and an INT8 path, and
+    whether that composes with HyQuant's token routing is the open
+    experiment. The tile criterion is not given; reading: rank a query
+    block's candidate key blocks by the INT8 score error bound of O8 (whose
+    pinned form gives |q.k - Q8.K8 sQ sK| <= sQ sK ((|Q8|_1 + |K8|_1) / 2 +
+    5 D / 4)), i.e. by E(kb) = fp32(sK(kb) * (A + B(kb) + 5 D / 2)) with
+    A = max over the block's rows (< T) of sum|Q8_i|, B(kb) = max over the
+    key block of sum|K8_j| (integers; one fp32 rounding), and route the
+    floor(num * n / den) largest (ties: lower kb) of the n = kb_band
+    candidate blocks, the blocks every row of the query block sees only
+    below its window band: kb_band = min(nkb, max(0, (i0 - W + 1) // 64)),
+    i0 = 128 qb, nkb = the blocks holding keys <= the block's last row.
+
+    q8: [T][D] int8 codes of one query head; k8: [T][D] of its KV head; sk:
+    [ceil(T/64)] fp32. Returns bool [ceil(T/128)][ceil(T/64)]."""
+    D = k8.shape[1]
+    nblk = (T + INT8_BLOCK - 1) // INT8_BLOCK
+    nqb = (T + TILE_ROWS - 1) // TILE_ROWS
+    l1q = np.abs(q8[:T].astype(np.int64)).sum(1)
+    l1k = np.abs(k8[:T].astype(np.int64)).sum(1)
+    Bk = np.array([l1k[j * INT8_BLOCK:(j + 1) * INT8_BLOCK].max() for j in range(nblk)])
+    route = np.zeros((nqb, nblk), dtype=bool)
+    for qb in range(nqb):
+        i0 = qb * TILE_ROWS
+        A = int(l1q[i0:min(T, i0 + TILE_ROWS)].max())
+        nkb = min(nblk, (i0 + TILE_ROWS + INT8_BLOCK - 1) // INT8_BLOCK)
+        kb_band = min(nkb, max(0, (i0 - window + 1) // INT8_BLOCK))
+        n = num * kb_band // den
+        if n == 0:
+            continue
+        E = (sk[:kb_band].astype(np.float32) * (A + Bk[:kb_band] + 5 * D // 2).astype(np.float32)).astype(np.float32)
+        order = sorted(range(kb_band), key=lambda kb: (-float(E[kb]), kb))
+        route[qb, order[:n]] = True
+    return route
 
 
 # ---------------------------------------------------------------------------

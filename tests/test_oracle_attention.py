@@ -358,3 +358,97 @@ def test_prefill_fp8_on_representable_inputs_is_exact():
     sm = 1 / math.sqrt(D)
     out = O.prefill_attention_block(q, k, v, sel, W, sm, qd, sq, kd, sk, 0, T)
     assert np.allclose(out, _sdpa(q, k, v, sm, causal=True), rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------- O12: tile routing composed with token routing
+
+
+def _route_brute(q8, k8, sk, T, W, num, den):
+    """tile_route restated with explicit loops over rows, keys and blocks."""
+    D = k8.shape[1]
+    nblk, nqb = (T + 63) // 64, (T + 127) // 128
+    out = np.zeros((nqb, nblk), dtype=bool)
+    for qb in range(nqb):
+        i0 = 128 * qb
+        A = max(sum(abs(int(x)) for x in q8[i]) for i in range(i0, min(T, i0 + 128)))
+        nkb = min(nblk, (i0 + 128 + 63) // 64)
+        band = min(nkb, max(0, (i0 - W + 1) // 64))
+        E = []
+        for kb in range(band):
+            B = max(sum(abs(int(x)) for x in k8[j]) for j in range(64 * kb, min(T, 64 * kb + 64)))
+            E.append((float(np.float32(np.float32(sk[kb]) * np.float32(A + B + 5 * D // 2))), kb))
+        E.sort(key=lambda e: (-e[0], e[1]))
+        for _, kb in E[: num * band // den]:
+            out[qb, kb] = True
+    return out
+
+
+def test_tile_route_brute_force_and_counts():
+    T, D, W = 700, 32, 128
+    q, k, v, q8, sq, k8, sk = _prefill_inputs(T, D, seed=70)
+    for num, den in [(0, 100), (5, 100), (30, 100), (100, 100)]:
+        r = O.tile_route(q8, k8, sk, T, W, num, den)
+        assert np.array_equal(r, _route_brute(q8, k8, sk, T, W, num, den)), (num, den)
+        for qb in range(r.shape[0]):
+            band = min(min(11, (128 * qb + 128 + 63) // 64), max(0, (128 * qb - W + 1) // 64))
+            assert r[qb].sum() == num * band // den
+            assert not r[qb, band:].any()          # never a block that touches the band
+
+
+def test_tile_route_picks_the_coarse_block_and_breaks_ties_low():
+    """A key block holding one element of 5000 has a far larger INT8 scale and is
+    routed first; an identical copy of it ties exactly and loses to the
+    lower block index."""
+    T, D, W = 1024, 64, 128
+    q, k, v, q8, sq, k8, sk = _prefill_inputs(T, D, seed=71)
+    k = k.copy()
+    k[64 * 5 + 9, 2] = 5000.0
+    k[64 * 6:64 * 7] = k[64 * 5:64 * 6]
+    k = _bf16(k)
+    k8, sk = O.int8_block_quantize(k)
+    assert sk[5] == sk[6] and sk[5] > 10 * np.delete(sk, [5, 6]).max()
+    last = (T + 127) // 128 - 1                 # its band: blocks 0..13
+    r = O.tile_route(q8, k8, sk, T, W, 1, 100)  # floor(14 / 100) = 0 blocks
+    assert not r.any()
+    r = O.tile_route(q8, k8, sk, T, W, 10, 100)  # floor(1.4) = 1
+    assert r[last].sum() == 1 and r[last, 5]
+    r = O.tile_route(q8, k8, sk, T, W, 20, 100)  # 2
+    assert r[last].sum() == 2 and r[last, 5] and r[last, 6]
+
+
+def test_prefill_with_route_brute_force_and_identities():
+    """The routed prefill by explicit loops (a routed tile's scores are
+    exact); a route that is all False is the token-routed prefill; routing
+    a tile whose keys are all selected changes nothing."""
+    T, D, W = 300, 32, 64
+    q, k, v, q8, sq, k8, sk = _prefill_inputs(T, D, seed=72)
+    sel = np.sort(np.random.default_rng(73).choice(T - W, 9, replace=False))
+    sm = 0.2
+    route = O.tile_route(q8, k8, sk, T, W, 40, 100)
+    assert route.any()
+    blk = O.prefill_attention_block(q, k, v, sel, W, sm, q8, sq, k8, sk, 0, T, route)
+    rows = np.array([0, 70, 127, 128, 200, 255, 256, 299])
+    out = O.prefill_attention_rows(q, k, v, sel, W, sm, q8, sq, k8, sk, rows, route)
+    sset = set(sel.tolist())
+    for n, i in enumerate(rows):
+        logit = []
+        for j in range(i + 1):
+            if j in sset or i - j < W or route[i // 128][j // 64]:
+                s = sum(q[i, d] * k[j, d] for d in range(D))
+            else:
+                s = sum(int(q8[i, d]) * int(k8[j, d]) for d in range(D)) * float(sq[i // 64]) * float(sk[j // 64])
+            logit.append(s * sm)
+        mx = max(logit)
+        w = [math.exp(x - mx) for x in logit]
+        ref = [sum(w[j] * v[j, d] for j in range(i + 1)) / sum(w) for d in range(D)]
+        assert np.allclose(out[n], ref, rtol=1e-11, atol=1e-12)
+        assert np.allclose(blk[i], ref, rtol=1e-11, atol=1e-12)
+    none = np.zeros_like(route)
+    assert np.array_equal(O.prefill_attention_block(q, k, v, sel, W, sm, q8, sq, k8, sk, 0, T, none),
+                          O.prefill_attention_block(q, k, v, sel, W, sm, q8, sq, k8, sk, 0, T))
+    allsel = np.arange(64)                     # block 0 entirely selected
+    extra = np.zeros_like(route)
+    extra[:, 0] = True
+    a = O.prefill_attention_block(q, k, v, allsel, W, sm, q8, sq, k8, sk, 0, T)
+    b = O.prefill_attention_block(q, k, v, allsel, W, sm, q8, sq, k8, sk, 0, T, extra)
+    assert np.array_equal(a, b)
