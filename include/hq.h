@@ -78,6 +78,11 @@ typedef struct {
     int32_t probe_rows;
     int32_t low_fmt;   /* low-precision path of hq_prefill_attn: HQ_LOW_INT8
                           (0, the default) or HQ_LOW_FP8; ignored elsewhere */
+    int32_t tile_num;  /* tile routing of hq_prefill_attn (INT8 path only):  */
+    int32_t tile_den;  /* the fraction tile_num / tile_den of each 128-row
+                          query block's key blocks below its window band is
+                          also computed in 16 bits; tile_num = 0 (the
+                          default) turns it off                            */
 } hq_policy;
 typedef enum { HQ_LOW_INT8 = 0, HQ_LOW_FP8 = 1 } hq_low_fmt;
 
@@ -369,6 +374,16 @@ hq_status hq_decode_attn_noalloc(const hq_cache* cache, const void* q, int32_t H
  * precision point), s = max|x|/448 in fp32, code = OCP E4M3 of fp32(x/s),
  * round to nearest even (fp32 sums of exact products). out_i = sum_j
  * softmax(score)_j v_j. P and V enter the PV product as fp16.
+ * Tile routing (policy->tile_num > 0, INT8 only; HyQuant page "How this
+ * relates to prior wiki pages" and "Gaps": TileMix's tile-level FP16/INT8
+ * dispatch, and whether it composes with the token routing): for every
+ * 128-row query block (rows i0 .. i0+127, i0 = 128 qb) the candidate key
+ * blocks kb < kb_band = min(nkb, max(0, (i0 - window + 1) / 64)) are ranked
+ * by E(kb) = fp32(sK(kb) * (A + B(kb) + 5D/2)), A = max over the block's rows
+ * of sum_c |Q8_ic|, B(kb) = max over the key block of sum_c |K8_jc| (the
+ * INT8 score error bound's shape), and the floor(tile_num * kb_band /
+ * tile_den) largest (ties: lower kb) are scored in 16 bits for every row of
+ * the query block. T must then be at most 262,144.
  *   q [B][Hq][T][D], k, v [B][Hkv][T][D] dt (values within fp16 range for
  *   V); sel_idx [B][Hkv][hq_sel_stride(T)] int32, the first sel_count[b][g]
  *   entries ascending, distinct and in [0, T) (as hq_probe_select returns
@@ -385,7 +400,10 @@ hq_status hq_decode_attn_noalloc(const hq_cache* cache, const void* q, int32_t H
  *   o3 = o2 + A(B Hkv Tp D)       sK fp32 [B][Hkv][nb]
  * the rest is staging (fp16 V^T blocks, with and without the selected
  * columns, selected-column masks and row-sum weights, gathered selected K / V
- * tiles).
+ * tiles) and, with tile routing, the per-block code norms; the workspace
+ * ends with the routed tiles' masks: its last A(8 B Hq nqb nw) bytes,
+ * nqb = ceil(T / 128), nw = ceil(nb / 64), hold uint64 [B][Hq][nqb][nw]
+ * with bit kb % 64 of word kb / 64 set for a routed key block kb.
  * Errors: HQ_ERR_UNSUPPORTED for D != 128, Hq % Hkv != 0, G = Hq / Hkv not
  * in {1, 2, 4, 8} or an unsupported dtype; HQ_ERR_CAPACITY if ws_bytes is
  * too small; HQ_ERR_INVALID_ARG for null pointers or T outside [1, 2^22]. */

@@ -35,7 +35,8 @@ class HQError(RuntimeError):
 
 class hq_policy(ctypes.Structure):
     _fields_ = [("keep_num", ctypes.c_int32), ("keep_den", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("probe_rows", ctypes.c_int32), ("low_fmt", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("probe_rows", ctypes.c_int32), ("low_fmt", ctypes.c_int32),
+                ("tile_num", ctypes.c_int32), ("tile_den", ctypes.c_int32)]
 
 
 class hq_thresh(ctypes.Structure):
@@ -113,9 +114,12 @@ class Policy:
     window: int = 128
     probe_rows: int = 64
     low_fmt: int = HQ_LOW_INT8   # prefill's low-precision path (HQ_LOW_INT8 / HQ_LOW_FP8)
+    tile_num: int = 0            # prefill tile routing fraction (0 = off)
+    tile_den: int = 100
 
     def c(self) -> hq_policy:
-        return hq_policy(self.keep_num, self.keep_den, self.window, self.probe_rows, self.low_fmt)
+        return hq_policy(self.keep_num, self.keep_den, self.window, self.probe_rows, self.low_fmt,
+                         self.tile_num, self.tile_den)
 
 
 def _torch():

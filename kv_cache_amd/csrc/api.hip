@@ -42,6 +42,11 @@ hq_status check_policy(const char* fn, const hq_policy* p) {
         return fail(HQ_ERR_INVALID_ARG, "%s: probe_rows %d must be in [1, 256]", fn, p->probe_rows);
     if (p->low_fmt != HQ_LOW_INT8 && p->low_fmt != HQ_LOW_FP8)
         return fail(HQ_ERR_UNSUPPORTED, "%s: low_fmt %d unsupported (HQ_LOW_INT8, HQ_LOW_FP8)", fn, p->low_fmt);
+    if (p->tile_num < 0 || (p->tile_num > 0 && (p->tile_den <= 0 || p->tile_num > p->tile_den)))
+        return fail(HQ_ERR_INVALID_ARG, "%s: tile fraction %d/%d must satisfy 0 <= num <= den, den > 0", fn,
+                    p->tile_num, p->tile_den);
+    if (p->tile_num > 0 && p->low_fmt != HQ_LOW_INT8)
+        return fail(HQ_ERR_UNSUPPORTED, "%s: tile routing needs the INT8 low-precision path", fn);
     return HQ_OK;
 }
 
@@ -428,6 +433,8 @@ hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B
     if ((st = check_heads(fn, B, Hq, Hkv, D))) return st;
     if ((st = check_dt(fn, dt))) return st;
     if (T < 1 || T > (1 << 22)) return fail(HQ_ERR_INVALID_ARG, "%s: T %d out of range", fn, T);
+    if (policy->tile_num > 0 && T > hq::kRouteMaxT)
+        return fail(HQ_ERR_UNSUPPORTED, "%s: tile routing supports T <= %d (T = %d)", fn, hq::kRouteMaxT, T);
     if (out_dt != HQ_F32 && out_dt != HQ_BF16 && out_dt != HQ_F16)
         return fail(HQ_ERR_UNSUPPORTED, "%s: out dtype %d unsupported", fn, out_dt);
     if (!(sm_scale > 0.0f) || sm_scale > 1e6f) return fail(HQ_ERR_INVALID_ARG, "%s: sm_scale must be positive", fn);

@@ -34,6 +34,7 @@ __device__ inline void st_nt(void* ptr, const uint4& v) {
     __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(ptr));
 }
 constexpr int kInt8Block = 64;   // prefill INT8 block (tokens)
+constexpr int kRouteMaxT = 1 << 18;  // longest prefill with tile routing (4,096 key blocks sorted in LDS)
 // Largest cache capacity in slots: the decode kernel addresses one (b, g)'s
 // INT4 codes (64 bytes per slot) with 32-bit buffer offsets.
 constexpr int32_t kMaxCapTokens = 1 << 24;

@@ -65,8 +65,8 @@ constexpr int kBM = 128;  // query rows per workgroup
 constexpr int kBN = 64;   // keys per block
 
 struct PfLayout {
-    size_t q8, sq, k8, sk, vt, mask, ksel, vtsel, vt0, wsel, total;
-    int nblk, nsel_tiles;
+    size_t q8, sq, k8, sk, vt, mask, ksel, vtsel, vt0, wsel, l1q, l1k, route, total;
+    int nblk, nsel_tiles, nqb, nw;
 };
 inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 PfLayout pf_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, const hq_policy& pol) {
@@ -85,7 +85,14 @@ PfLayout pf_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, const hq_polic
     w.vtsel = w.ksel + al((size_t)B * Hkv * w.nsel_tiles * kBN * kD * 2);
     w.vt0 = w.vtsel + al((size_t)B * Hkv * w.nsel_tiles * kBN * kD * 2);
     w.wsel = w.vt0 + al((size_t)B * Hkv * Tp * kD * 2);
-    w.total = w.wsel + al((size_t)B * Hkv * w.nblk * 32 * 4);
+    // tile routing: per-block maxima of the rows' code L1 norms, and per
+    // (b, h, 128-row query block) a bit per key block
+    w.nqb = (T + kBM - 1) / kBM;
+    w.nw = (w.nblk + 63) / 64;
+    w.l1q = w.wsel + al((size_t)B * Hkv * w.nblk * 32 * 4);
+    w.l1k = w.l1q + al((size_t)B * Hq * w.nblk * 4);
+    w.route = w.l1k + al((size_t)B * Hkv * w.nblk * 4);
+    w.total = w.route + al((size_t)B * Hq * w.nqb * w.nw * 8);
     return w;
 }
 
@@ -105,7 +112,8 @@ __device__ inline float block_max256(float v, float* red) {
 // reciprocal and FMA residual steps (fewer instructions, more registers: the
 // Q kernel gains, the K/V kernel, which also writes V^T, runs slower with it).
 template <bool F16, bool RECIP, bool FP8>
-__device__ __attribute__((always_inline)) inline void quant_block_i8(const uint16_t* src, int rows_valid, int8_t* dst, float* scale) {
+__device__ __attribute__((always_inline)) inline void quant_block_i8(const uint16_t* src, int rows_valid, int8_t* dst,
+                                                                    float* scale, int32_t* l1max) {
     __shared__ float red[4];
     const int t = threadIdx.x, r = t >> 2, c0 = (t & 3) * 32;
     float x[32];
@@ -178,6 +186,19 @@ __device__ __attribute__((always_inline)) inline void quant_block_i8(const uint1
     d4[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     d4[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
     if (t == 0) *scale = s;
+    if constexpr (!FP8) {
+        if (l1max != nullptr) {  // tile routing: the block's largest row sum of |code| (uniform branch)
+            int a = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a += abs((int)(int8_t)(packed[i] >> (8 * j)));
+            a += __shfl_xor(a, 1);  // the four threads of row r
+            a += __shfl_xor(a, 2);
+            const float mx = block_max256((float)a, red);  // exact: a <= 128 * 127
+            if (t == 0) *l1max = (int32_t)mx;
+        }
+    }
 }
 #pragma clang fp contract(on)
 
@@ -204,7 +225,10 @@ struct PfParams {
                          // one, in the order of the P^T words of lane half 0 / 1
     float* out;
     int out_dt;
-    int B, Hq, Hkv, G, T, nblk, nsel_tiles, sel_stride, W;
+    int32_t* l1q;        // [B][Hq][nblk] max row sum |Q8| per 64-row block (tile routing; else null)
+    int32_t* l1k;        // [B][Hkv][nblk]
+    uint64_t* route;     // [B][Hq][nqb][nw] routed key blocks of each 128-row query block (or null)
+    int B, Hq, Hkv, G, T, nblk, nsel_tiles, sel_stride, W, nqb, nw, tile_num, tile_den;
     float c16;           // sm_scale * log2(e)
 };
 
@@ -214,7 +238,8 @@ __global__ __launch_bounds__(256) void k_pf_quant_q(PfParams p) {
     const size_t Tp = (size_t)p.nblk * kBN;
     const uint16_t* src = p.q + (((size_t)b * p.Hq + h) * p.T + (size_t)blk * kBN) * kD;
     int8_t* dst = p.q8 + (((size_t)b * p.Hq + h) * Tp + (size_t)blk * kBN) * kD;
-    quant_block_i8<F16, true, FP8>(src, min(kBN, p.T - blk * kBN), dst, p.sq + ((size_t)b * p.Hq + h) * p.nblk + blk);
+    quant_block_i8<F16, true, FP8>(src, min(kBN, p.T - blk * kBN), dst, p.sq + ((size_t)b * p.Hq + h) * p.nblk + blk,
+                                   p.l1q ? p.l1q + ((size_t)b * p.Hq + h) * p.nblk + blk : nullptr);
 }
 
 // K8 + sK, V^T in fp16, and the selected-column mask of one key block.
@@ -226,7 +251,8 @@ __global__ __launch_bounds__(256) void k_pf_quant_kv(PfParams p) {
     const size_t Tp = (size_t)p.nblk * kBN;
     const int rows = min(kBN, p.T - blk * kBN);
     const uint16_t* ksrc = p.k + ((size_t)bg * p.T + (size_t)blk * kBN) * kD;
-    quant_block_i8<F16, false, FP8>(ksrc, rows, p.k8 + ((size_t)bg * Tp + (size_t)blk * kBN) * kD, p.sk + (size_t)bg * p.nblk + blk);
+    quant_block_i8<F16, false, FP8>(ksrc, rows, p.k8 + ((size_t)bg * Tp + (size_t)blk * kBN) * kD, p.sk + (size_t)bg * p.nblk + blk,
+                                    p.l1k ? p.l1k + (size_t)bg * p.nblk + blk : nullptr);
     // V -> fp16 -> transposed
     const int t = threadIdx.x, r = t >> 2, c0 = (t & 3) * 32;
     const uint16_t* vsrc = p.v + ((size_t)bg * p.T + (size_t)blk * kBN) * kD;
@@ -285,6 +311,63 @@ __global__ __launch_bounds__(256) void k_pf_quant_kv(PfParams p) {
         p.wsel[((size_t)bg * p.nblk + blk) * 32 + t] =
             (((bits >> ka) & 1ull) ? 0u : one) | (((bits >> (ka + 1)) & 1ull) ? 0u : (one << 16));
     }
+}
+
+// Tile routing: for one (b, h, 128-row query block), rank its candidate key
+// blocks (below the window band for every row of the block) by the INT8
+// score error bound's shape E = sK (A + B + 5D/2) and set the bits of the
+// floor(tile_num * n / tile_den) largest, ties to the lower block. The keys
+// (E bits, ~kb) are sorted in LDS (bitonic, ascending; E >= 0 so its bit
+// pattern orders like its value, and every real key is above the zero
+// padding).
+__global__ __launch_bounds__(256) void k_pf_route(PfParams p) {
+    __shared__ uint64_t key[kRouteMaxT / kBN];
+    __shared__ unsigned long long bits[kRouteMaxT / kBN / 64];
+    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+    const int bg = b * p.Hkv + h / p.G;
+    const int i0 = qb * kBM;
+    const int nkb = min(p.nblk, (i0 + kBM + kBN - 1) / kBN);
+    const int kb_band = min(nkb, max(0, (i0 - p.W + 1) / kBN));
+    const int n = (int)((int64_t)p.tile_num * kb_band / p.tile_den);
+    for (int w = t; w < p.nw; w += 256) bits[w] = 0ull;
+    if (n > 0) {
+        const int32_t* lq = p.l1q + ((size_t)b * p.Hq + h) * p.nblk;
+        const int A = max(lq[2 * qb], 2 * qb + 1 < p.nblk ? lq[2 * qb + 1] : 0);
+        const int32_t* lk = p.l1k + (size_t)bg * p.nblk;
+        const float* sk = p.sk + (size_t)bg * p.nblk;
+        int P = 1;
+        while (P < kb_band) P <<= 1;
+        for (int i = t; i < P; i += 256) {
+            uint64_t kv = 0;
+            if (i < kb_band) {
+                const float e = sk[i] * (float)(A + lk[i] + 5 * kD / 2);
+                kv = ((uint64_t)__float_as_uint(e) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+            }
+            key[i] = kv;
+        }
+        __syncthreads();
+        for (int k = 2; k <= P; k <<= 1)
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int i = t; i < P; i += 256) {
+                    const int ixj = i ^ j;
+                    if (ixj > i) {
+                        const uint64_t a = key[i], c = key[ixj];
+                        if (((i & k) == 0) ? (a > c) : (a < c)) {
+                            key[i] = c;
+                            key[ixj] = a;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        for (int i = t; i < n; i += 256) {
+            const uint32_t kb = 0xFFFFFFFFu - (uint32_t)key[P - 1 - i];
+            atomicOr(&bits[kb >> 6], 1ull << (kb & 63));
+        }
+    }
+    __syncthreads();
+    uint64_t* out = p.route + (((size_t)b * p.Hq + h) * p.nqb + qb) * p.nw;
+    for (int w = t; w < p.nw; w += 256) out[w] = bits[w];
 }
 
 // Gathered tiles of selected columns: 16-bit K rows and fp16 V^T.
@@ -707,6 +790,50 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
                 q16b[ks] = qvalid ? *reinterpret_cast<const intx4*>(q16 + 16 * ks + 8 * hf) : z;
             }
         }
+        // routed tiles (below the band, chosen by k_pf_route): 16-bit scores
+        // for every key of the block except the selected ones, which phase B
+        // covers (their p is 0 here)
+        if (p.route != nullptr) {
+            const uint64_t* rw = p.route + (((size_t)b * p.Hq + h) * p.nqb + qb) * p.nw;
+            for (int w = 0; w < (kb_band + 63) / 64; ++w) {
+                uint64_t mw = rw[w];
+                while (mw) {
+                    const int kb = 64 * w + __builtin_ctzll(mw);
+                    mw &= mw - 1;
+                    __syncthreads();
+                    {
+                        const int t = threadIdx.x;
+                        const uint16_t* vsrc = p.vt + ((size_t)bg * p.nblk + kb) * kD * kBN;
+                        const uint4 v0 = ld16(vsrc, t, 2 * kBN), v1 = ld16(vsrc, t + 256, 2 * kBN);
+                        const uint4 v2 = ld16(vsrc, t + 512, 2 * kBN), v3 = ld16(vsrc, t + 768, 2 * kBN);
+                        const K16Regs kr = load_k16(p.k + ((size_t)bg * p.T + (size_t)kb * kBN) * kD, kBN);
+                        st16(sm.vt[0], t, kVtStride, v0);
+                        st16(sm.vt[0], t + 256, kVtStride, v1);
+                        st16(sm.vt[0], t + 512, kVtStride, v2);
+                        st16(sm.vt[0], t + 768, kVtStride, v3);
+                        store_k16(sm.k16, kr);
+                    }
+                    __syncthreads();
+                    const uint64_t selbits = p.mask[(size_t)bg * p.nblk + kb];
+                    float x[2][16];
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const floatx16 sb = st_16_tile<F16>(sm.k16, q16b, tt);
+#pragma unroll
+                        for (int a = 0; a < 4; ++a) {
+                            const uint32_t byte = (uint32_t)(selbits >> (32 * tt + 8 * a)) & 0xFFu;
+#pragma unroll
+                            for (int b4 = 0; b4 < 4; ++b4) {
+                                const bool sel = __builtin_amdgcn_inverse_ballot_w64(elem_lanes(byte, b4));
+                                x[tt][4 * a + b4] = sel ? -INFINITY : sb[4 * a + b4] * c16;
+                            }
+                        }
+                    }
+                    softmax_x(x, m_ref, l, o, pb);
+                    pv_block(sm.vt[0], pb, o);
+                }
+            }
+        }
         for (int kb = kb_band; kb < nkb; ++kb) {
             __syncthreads();
             {
@@ -843,6 +970,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
         __syncthreads();
         typename LowAcc<FP8>::type sA[2], sB[2];
         st_low<FP8>(sm.k8[0], q8b, sA);
+        const uint64_t* rwc = p.route ? p.route + (((size_t)b * p.Hq + h) * p.nqb + qb) * p.nw : nullptr;
         __syncthreads();  // every wave has read K slot 0 before iteration 0 refills it
 
         auto step = [&](auto P, typename LowAcc<FP8>::type (&sc)[2], typename LowAcc<FP8>::type (&sn)[2], int kb) {
@@ -867,7 +995,9 @@ __global__ __launch_bounds__(256, 2) void k_pf_attn(PfParams p) {
             float x[2][16];
             float lb = 0.0f;
             {
-                const float nmr = m_ref == -INFINITY ? 0.0f : -m_ref;
+                // a routed block was scored in 16 bits in phase A: p = 2^-inf = 0 here
+                const bool routed = rwc != nullptr && ((rwc[kb >> 6] >> (kb & 63)) & 1ull);
+                const float nmr = routed ? -INFINITY : (m_ref == -INFINITY ? 0.0f : -m_ref);
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -999,6 +1129,7 @@ void launch_pf(const PfParams& p, const PfLayout& w, int32_t B, int32_t Hq, int3
     k_pf_quant_q<F16, FP8><<<dim3(w.nblk, Hq, B), 256, 0, s>>>(p);
     k_pf_quant_kv<F16, FP8><<<dim3(w.nblk, Hkv, B), 256, 0, s>>>(p);
     k_pf_gather_sel<F16><<<dim3(w.nsel_tiles, Hkv, B), 256, 0, s>>>(p);
+    if (p.route != nullptr) k_pf_route<<<dim3(w.nqb, Hq, B), 256, 0, s>>>(p);
     k_pf_attn<F16, FP8><<<dim3(((T + kBM - 1) / kBM) * Hq * B), 256, 0, s>>>(p);
 }
 
@@ -1030,6 +1161,14 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, int32_t B
     p.vtsel = reinterpret_cast<uint16_t*>(base + w.vtsel);
     p.vt0 = reinterpret_cast<uint16_t*>(base + w.vt0);
     p.wsel = reinterpret_cast<uint32_t*>(base + w.wsel);
+    const bool route = pol.tile_num > 0;
+    p.l1q = route ? reinterpret_cast<int32_t*>(base + w.l1q) : nullptr;
+    p.l1k = route ? reinterpret_cast<int32_t*>(base + w.l1k) : nullptr;
+    p.route = route ? reinterpret_cast<uint64_t*>(base + w.route) : nullptr;
+    p.nqb = w.nqb;
+    p.nw = w.nw;
+    p.tile_num = pol.tile_num;
+    p.tile_den = pol.tile_den > 0 ? pol.tile_den : 1;
     p.out = static_cast<float*>(out);
     p.out_dt = (int)out_dt;
     p.B = B;

@@ -173,6 +173,15 @@ def test_prefill_validation(hq):
     assert call(odt=7) == hq.HQ_ERR_UNSUPPORTED
     assert call(T=0) == hq.HQ_ERR_INVALID_ARG
     assert call(wsb=1) == hq.HQ_ERR_CAPACITY
+    # tile routing: a valid fraction, the INT8 path, T <= 2^18
+    for bad, code in [(hq.hq_policy(5, 100, 128, 64, 0, 5, 0), hq.HQ_ERR_INVALID_ARG),
+                      (hq.hq_policy(5, 100, 128, 64, 0, 7, 5), hq.HQ_ERR_INVALID_ARG),
+                      (hq.hq_policy(5, 100, 128, 64, 1, 5, 100), hq.HQ_ERR_UNSUPPORTED)]:
+        assert hq.lib.hq_prefill_attn(FAKE, FAKE, FAKE, 1, 32, 8, 1024, 128, hq.HQ_BF16, ctypes.byref(bad), FAKE,
+                                      FAKE, 0.088, FAKE, hq.HQ_F32, FAKE, 1 << 40, None) == code
+    tp = hq.hq_policy(5, 100, 128, 64, 0, 5, 100)
+    assert hq.lib.hq_prefill_attn(FAKE, FAKE, FAKE, 1, 32, 8, (1 << 18) + 1, 128, hq.HQ_BF16, ctypes.byref(tp), FAKE,
+                                  FAKE, 0.088, FAKE, hq.HQ_F32, FAKE, 1 << 40, None) == hq.HQ_ERR_UNSUPPORTED
 
 
 def test_layout_rejects_bad_sizes(hq):

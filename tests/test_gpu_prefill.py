@@ -283,8 +283,8 @@ def test_prefill_deterministic():
     assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
-def test_prefill_16k_full_size(fp8):
+@pytest.mark.parametrize("fp8,tile", [(False, 0), (True, 0), (False, 5)], ids=["int8", "fp8", "int8_tile5"])
+def test_prefill_16k_full_size(fp8, tile):
     """The 16K causal prefill workload (B=1, 32 query / 8 KV heads), launched
     as the benchmark launches it (INT8, and the FP8 low path): the
     low-precision stage bit-exact for every Q and K
@@ -298,8 +298,8 @@ def test_prefill_16k_full_size(fp8):
     spec = CONFIGS["c4_prefill_8b_16k"]
     inp = make_prefill_inputs(spec)
     T, G = spec.T, spec.Hq // spec.Hkv
-    pol = hq.Policy(low_fmt=hq.HQ_LOW_FP8 if fp8 else hq.HQ_LOW_INT8)
-    print(f"prefill 16k ({'fp8' if fp8 else 'int8'}): probe", flush=True)
+    pol = hq.Policy(low_fmt=hq.HQ_LOW_FP8 if fp8 else hq.HQ_LOW_INT8, tile_num=tile)
+    print(f"prefill 16k ({'fp8' if fp8 else 'int8'}, tile routing {tile}%): probe", flush=True)
     q, k = to_dev(inp.q, spec.dtype), to_dev(inp.k, spec.dtype)
     lens = torch.full((1,), T, dtype=torch.int32, device="cuda")
     col, sel, cnt, thr = hq.probe_select(q[:, :, T - 64:].contiguous(), k, lens, pol)
@@ -310,6 +310,7 @@ def test_prefill_16k_full_size(fp8):
     out, ws = run_prefill(inp, sels, pol)
     check_int8_stage(inp, ws, fp8=fp8)
     print("prefill 16k: low-precision stage bit-exact on all heads", flush=True)
+    bits = ws_route_bits(ws, 1, spec.Hq, T) if tile else None
     out = out.cpu().numpy()
     rng = np.random.default_rng(4)
     starts = [T - 64, 96, 8160] + sorted(int(x) for x in rng.integers(0, T - 64, size=13))
@@ -323,9 +324,13 @@ def test_prefill_16k_full_size(fp8):
         g = h // G
         _, sk, k8 = k8s[g]
         _, sq, q8 = low_quant(qf[0, h], fp8)
+        route = None
+        if tile:
+            route = O.tile_route(q8, k8, sk, T, 128, tile, 100)
+            assert np.array_equal(bits[0, h], route), h
         for n, r0 in enumerate(starts):
             refs[h, 64 * n:64 * (n + 1)] = O.prefill_attention_block(qf[0, h], kf[0, g], vf[0, g], sels[0][g], 128,
-                                                                     sm, q8, sq, k8, sk, r0, r0 + 64)
+                                                                     sm, q8, sq, k8, sk, r0, r0 + 64, route)
         if fp8:
             bars = fp8_bars(qf[0, h], kf[0, g], q8, sq, k8, sk, vf[0, g], refs[h], rows, sels[0][g], 128, sm)
             assert_fp8_rows(out[0][h, rows], refs[h], bars, f"16k prefill head {h}")
@@ -430,3 +435,60 @@ def test_prefill_fp8_q_ties_subnormals_and_signed_zero():
     torch.cuda.synchronize()
     assert np.isfinite(out.cpu().numpy()).all()
     check_int8_stage(inp, ws, fp8=True)
+
+
+def ws_route_bits(ws, B, Hq, T):
+    """The routed tiles' masks from the end of the workspace (include/hq.h)."""
+    nb, nqb = (T + 63) // 64, (T + 127) // 128
+    nw = (nb + 63) // 64
+    n = B * Hq * nqb * nw * 8
+    h = ws.cpu().numpy()
+    words = h[len(h) - _al(n): len(h) - _al(n) + n].view(np.uint64).reshape(B, Hq, nqb, nw)
+    bits = np.zeros((B, Hq, nqb, nb), dtype=bool)
+    for kb in range(nb):
+        bits[..., kb] = (words[..., kb // 64] >> np.uint64(kb % 64)) & np.uint64(1)
+    return bits
+
+
+TILE_CASES = [
+    # name, B, Hq, Hkv, T, dtype, window, keep, tile fraction
+    ("token5_tile10", 1, 4, 2, 1000, "bf16", 128, (5, 100), (10, 100)),
+    ("tile30_only_f16", 2, 4, 2, 700, "f16", 64, (0, 100), (30, 100)),
+    ("token5_tile100", 1, 2, 1, 2000, "bf16", 128, (5, 100), (100, 100)),
+    ("g8_tile20", 1, 8, 1, 900, "bf16", 128, (5, 100), (20, 100)),
+    ("T129_tile50", 1, 2, 1, 129, "bf16", 64, (5, 100), (50, 100)),
+]
+
+
+@pytest.mark.parametrize("case", TILE_CASES, ids=[c[0] for c in TILE_CASES])
+def test_prefill_tile_routing_parity(case):
+    """Tile routing composed with the token routing: the routed key blocks
+    of every (head, 128-row query block) bit-exact with oracle.tile_route on
+    the oracle's INT8 codes, and the attention against the oracle's prefill
+    with that routing."""
+    import torch
+    import kv_cache_amd as hq
+    name, B, Hq, Hkv, T, dtype, W, keep, tile = case
+    spec = PrefillSpec(name=name, B=B, Hq=Hq, Hkv=Hkv, T=T, dtype=dtype, window=W, plant_frac=0.01, seed=91 + T)
+    inp = make_prefill_inputs(spec)
+    pol = hq.Policy(keep[0], keep[1], W, 64, hq.HQ_LOW_INT8, tile[0], tile[1])
+    sels = oracle_sel(inp, W, keep)
+    out, ws = run_prefill(inp, sels, pol)
+    check_int8_stage(inp, ws)
+    bits = ws_route_bits(ws, B, Hq, T)
+    G, sm = Hq // Hkv, fp32_scale(D)
+    qf, kf, vf = (O.to_f64(x, dtype) for x in (inp.q, inp.k, inp.v))
+    ref = np.empty((B, Hq, T, D))
+    routed = 0
+    for b in range(B):
+        for g in range(Hkv):
+            k8, sk = O.int8_block_quantize(kf[b, g])
+            for h in range(g * G, (g + 1) * G):
+                q8, sq = O.int8_block_quantize(qf[b, h])
+                r = O.tile_route(q8, k8, sk, T, W, tile[0], tile[1])
+                assert np.array_equal(bits[b, h], r), (b, h)
+                routed += int(r.sum())
+                ref[b, h] = O.prefill_attention_block(qf[b, h], kf[b, g], vf[b, g], sels[b][g], W, sm, q8, sq, k8, sk,
+                                                      0, T, r)
+    print(f"tile routing {name}: {routed} routed tiles", flush=True)
+    assert_attn_close(out.cpu().numpy(), ref, name)
