@@ -196,6 +196,61 @@ def prefill_low_error(hq, pf, psel, pol, polf, heads=4, nrows=512):
     return {k2: (round(v2, 7) if isinstance(v2, float) else v2) for k2, v2 in err.items()}
 
 
+def prefill_routing_study(hq, pf, psel, heads=4, nrows=512, fracs=(5, 20)):
+    """The pages' additivity experiment at the 16K prefill shape: output
+    error against exact causal attention (fp64, plain torch on the device;
+    last `nrows` rows of the first `heads` query heads) and time of the INT8
+    prefill with no routing (window only), token routing (the probe's top 5%),
+    tile routing (a fraction of each query block's key blocks by the INT8
+    error bound) and both. recovered = error(none) - error(config); the
+    ratio recovered(both) / (recovered(token) + recovered(tile)) is 1 when
+    the two are additive and near max/sum when they cash the same slack."""
+    import torch
+    T = pf["spec"].T
+    G = pf["spec"].Hq // pf["spec"].Hkv
+    q = pf["q"][0, :heads, T - nrows:].double()
+    k = pf["k"][0, [h // G for h in range(heads)]].double()
+    v = pf["v"][0, [h // G for h in range(heads)]].double()
+    s = torch.matmul(q, k.transpose(1, 2).contiguous()) / math.sqrt(q.shape[-1])
+    i = torch.arange(T - nrows, T, device=s.device)[:, None]
+    s = s.masked_fill(torch.arange(T, device=s.device)[None, :] > i, float("-inf"))
+    ref = torch.matmul(torch.softmax(s, -1), v)
+    empty_cnt = torch.zeros_like(psel[2])
+
+    def run(keep, tile):
+        pol = hq.Policy(tile_num=tile)
+        cnt = psel[2] if keep else empty_cnt
+        for _ in range(2):
+            o = hq.prefill_attn(pf["q"], pf["k"], pf["v"], psel[1], cnt, pol, None, pf["out"])
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            o = hq.prefill_attn(pf["q"], pf["k"], pf["v"], psel[1], cnt, pol, None, pf["out"])
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        d = o[0, :heads, T - nrows:].double() - ref
+        return {"rel_l2": round(float(d.norm() / ref.norm()), 6), "max_abs": round(float(d.abs().max()), 5),
+                "ms": round(sorted(x.elapsed_time(y) for x, y in ev)[1], 3)}
+
+    res = {"none": run(False, 0), "token_5pct": run(True, 0)}
+    base = res["none"]["rel_l2"]
+    for f in fracs:
+        res[f"tile_{f}pct"] = run(False, f)
+        res[f"token_5pct+tile_{f}pct"] = both = run(True, f)
+        rt = base - res["token_5pct"]["rel_l2"]
+        rl = base - res[f"tile_{f}pct"]["rel_l2"]
+        rb = base - both["rel_l2"]
+        res[f"additivity_tile_{f}pct"] = {"recovered_token": round(rt, 6), "recovered_tile": round(rl, 6),
+                                          "recovered_both": round(rb, 6),
+                                          "both_over_sum": round(rb / (rt + rl), 4) if rt + rl > 0 else None,
+                                          "max_over_sum": round(max(rt, rl) / (rt + rl), 4) if rt + rl > 0 else None}
+    res["error_sample"] = f"last {nrows} rows of query heads 0..{heads - 1} against exact fp64 attention"
+    return res
+
+
 def committed_traffic(profile, source, key):
     """HBM bytes per call from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary (each counter scaled by the factor a plain copy of known size
@@ -869,6 +924,7 @@ def main():
         res["prefill_fp8"] = {"ms": round(fms, 3), "TFLOPs": round(fl / (fms * 1e-3) / 1e12, 1),
                               "frac": fr["frac"], "low_fmt": "OCP FP8 E4M3, per-64-token block scale"}
         res["prefill_fp8"].update(prefill_low_error(hq, pf, psel, pol, polf))
+        res["prefill_routing"] = prefill_routing_study(hq, pf, psel)
     sels = tuple(t.cpu().numpy() for t in (hq.probe_select(qp, k, lens, pol)))
     del cache, k, v, knew, vnew
     if pf is not None:
