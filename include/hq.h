@@ -295,7 +295,7 @@ hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_n
  * ceil(tiles / 54) splits, raised until the grid fills whole rounds of the
  * current device's workgroup slots (2 per CU; eight heads per KV head run
  * as two four-head workgroups per split), with
- * at least 8 tiles per split. The workspace query and the call compute it
+ * at least 4 tiles per split. The workspace query and the call compute it
  * alike for the current device. The result does not depend on it beyond
  * fp32 rounding. */
 hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,

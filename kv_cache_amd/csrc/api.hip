@@ -126,7 +126,7 @@ int32_t device_cus() {
 // INT4 cache tiles per decode split. Start from 54 tiles per split and add
 // splits until the grid fills whole rounds of the device's workgroup slots
 // (two per CU): a partial last round leaves CUs idle at the end of the
-// kernel. At least 8 tiles (two per wave) per split.
+// kernel. At least 4 tiles (one per wave) per split.
 int32_t decode_tps(const hq_cache& c, int32_t G) {
     const int32_t tiles = c.cap_q / hq::kTile;
     if (tiles < 1) return 54;
@@ -139,7 +139,7 @@ int32_t decode_tps(const hq_cache& c, int32_t G) {
     const int64_t total = (base + n16) * bg;
     const int64_t rounds = (total + slots - 1) / slots;
     const int64_t nsq = std::max<int64_t>(base, rounds * slots / bg - n16);
-    return std::max<int32_t>(8, (int32_t)((tiles + nsq - 1) / nsq));  // at least two tiles per wave
+    return std::max<int32_t>(4, (int32_t)((tiles + nsq - 1) / nsq));  // at least one tile per wave
 }
 
 }  // namespace

@@ -60,7 +60,7 @@ constexpr int kKT = 32;            // keys per key tile
 constexpr int kTilesPerWg = 8;     // row tiles (waves) per workgroup at most
 constexpr int kPlanes = 4;         // base-256 digits per value
 constexpr int kDS = kD + 16;       // LDS bytes per key in a digit plane (pad: no bank conflicts)
-constexpr int kColBlk = 256;       // keys per pass-2 workgroup
+constexpr int kColBlk = 512;       // largest keys per pass-2 workgroup (the launch picks 512 or 256)
 constexpr double kLogitBudget = 1.5e-7;  // largest logit error accepted from the digit path (log2 units)
 constexpr int kExpTerms = 7;       // 2^f = sum_{n <= 7} (f ln2)^n / n!, |f| <= 1/2: relative error < 1.1e-8
 
@@ -72,7 +72,7 @@ struct ProbeParams {
     double* rowref;        // [B][Hkv][NRp] m' = M + log2(L) per row: p = 2^(z - m')
     double* colpart;       // [B][Hkv][ngroups][Tmax] column sums per row group (ngroups > 1)
     float* col_scores;     // [B][Hkv][Tmax]
-    int32_t B, Hq, Hkv, Tmax, R, G, NR, NRp, ngroups, nchunk, chunk;
+    int32_t B, Hq, Hkv, Tmax, R, G, NR, NRp, ngroups, nchunk, chunk, colblk;
     double sc2;            // sm_scale * log2(e)
     double ec[kExpTerms + 1];  // (ln2)^n / n!, n = 0..7
 };
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
     }
 }
 
-// Pass 2: per (256-key block, row group, g, b): column sums of
+// Pass 2: per (512- or 256-key block, row group, g, b): column sums of
 // 2^(z - m'_row) over the group's probe rows. The same tiling as pass 1;
 // per lane the 16 rows of its elements, per wave a 32-row tile; the waves'
 // partial sums meet in LDS and are added in a fixed order.
@@ -569,17 +569,17 @@ __global__ __launch_bounds__(512) void k_probe_colsum(ProbeParams p) {
     const int T = p.seq_lens[b];
     const int bg = b * p.Hkv + g;
     const int rt = grp * kTilesPerWg + wave;
-    const int key_lo = blk * kColBlk;
+    const int key_lo = blk * p.colblk;
     float* out = p.col_scores + (size_t)bg * p.Tmax;
     double* outp = p.colpart + ((size_t)bg * p.ngroups + grp) * p.Tmax;
     if (key_lo >= T) {
-        for (int j = threadIdx.x; j < kColBlk && key_lo + j < p.Tmax; j += blockDim.x) {
+        for (int j = threadIdx.x; j < p.colblk && key_lo + j < p.Tmax; j += blockDim.x) {
             if (p.ngroups == 1) out[key_lo + j] = 0.0f;
             else outp[key_lo + j] = 0.0;
         }
         return;
     }
-    const int key_hi = min(key_lo + kColBlk, T);
+    const int key_hi = min(key_lo + p.colblk, T);
     const int ntile = (key_hi - key_lo + kKT - 1) / kKT;
     const uint16_t* kbase = p.k + (size_t)bg * p.Tmax * kD;
     const bool active = rt * kRT < p.NRp;
@@ -620,7 +620,7 @@ __global__ __launch_bounds__(512) void k_probe_colsum(ProbeParams p) {
         __syncthreads();
     }
     // sum over the waves (row tiles) in order
-    for (int j = threadIdx.x; j < kColBlk; j += blockDim.x) {
+    for (int j = threadIdx.x; j < p.colblk; j += blockDim.x) {
         const int key = key_lo + j;
         if (key >= p.Tmax) break;
         double sum = 0.0;
@@ -866,7 +866,10 @@ hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_l
     if (e != hipSuccess) return e;
     k_probe_rowfinal<<<dim3(Hkv, B), 256, 0, s>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dim3 g2((Tmax + kColBlk - 1) / kColBlk, Hkv * sh.ngroups, B);
+    // 512-key blocks (the query tiles' digit conversion amortised over twice
+    // the keys) while the grid keeps at least 1,024 workgroups
+    p.colblk = (int64_t)((Tmax + 511) / 512) * Hkv * sh.ngroups * B >= 1024 ? 512 : 256;
+    dim3 g2((Tmax + p.colblk - 1) / p.colblk, Hkv * sh.ngroups, B);
     if (f16) k_probe_colsum<true><<<g2, threads, 0, s>>>(p);
     else k_probe_colsum<false><<<g2, threads, 0, s>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
