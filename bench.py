@@ -297,20 +297,30 @@ def _host_info():
     return {"cpu": model, "logical_cpus": os.cpu_count(), "memory": mem}
 
 
-def cpu_baseline(inp, sels_gpu, q, budget_s=15.0):
+def _parity(gpu, ref, n, what):
+    """Parity summary of the units the oracle computed: max-abs and
+    relative L2 of the GPU's output against it, beside the bars."""
+    import numpy as np
+    d = gpu.astype(np.float64) - ref
+    return {"what": what, "units": n, "max_abs": float(f"{np.abs(d).max():.3e}"),
+            "rel_l2": float(f"{np.linalg.norm(d) / np.linalg.norm(ref):.3e}"), "bar_max_abs": 2e-3, "bar_rel_l2": 1e-3}
+
+
+def cpu_baseline(inp, sels_gpu, q, budget_s=15.0, gpu_out=None):
     """The oracle (numpy fp64) timed on this host for the unit the GPU's
     `value` times: one decode step's attention over an already built hybrid
     cache (all (b, g) of the 32K decode workload). Caches are built for
     whole (b, g) units until the time budget is spent (the build is timed as
     its own field, the once-per-prompt cost); the decode of those units is
-    timed and scaled to all units."""
+    timed and scaled to all units. gpu_out: the library's decode of q over
+    the same caches, compared with the oracle's on those units."""
     import numpy as np
     import oracle as O
     sp = inp.spec
     sm = float(np.float32(1 / math.sqrt(sp.D)))  # the fp32 scale the library receives
     G = sp.Hq // sp.Hkv
     col, sel, cnt, thr = sels_gpu
-    t_build, t_dec = [], []
+    t_build, t_dec, refs, gots = [], [], [], []
     start = time.perf_counter()
     for b in range(sp.B):
         for g in range(sp.Hkv):
@@ -325,10 +335,12 @@ def cpu_baseline(inp, sels_gpu, q, budget_s=15.0):
                                                    int(thr[b, g, 1])), 128, col[b, g, :T].astype(np.float64))
             t1 = time.perf_counter()
             qg = O.to_f64(q[b, g * G:(g + 1) * G], sp.dtype)
-            O.decode_attention(qg, c, sm)
+            o = O.decode_attention(qg, c, sm)
             t2 = time.perf_counter()
             t_build.append(t1 - t0)
             t_dec.append(t2 - t1)
+            refs.append(o)
+            gots.append(gpu_out[b, g * G:(g + 1) * G] if gpu_out is not None else o)
     n, units = len(t_dec), sp.B * sp.Hkv
     rec = {"value": round(sum(t_dec) / n * units * 1e6, 1), "unit": "us/step", "cores": _cpu_threads(),
            "kind": "oracle",
@@ -336,6 +348,9 @@ def cpu_baseline(inp, sels_gpu, q, budget_s=15.0):
                      f"units of one 32K decode step ({sum(t_dec):.1f} s), scaled x{units / n:.1f}",
            "cache_build_us_per_prompt": round(sum(t_build) / n * units * 1e6, 1)}
     rec.update(_host_info())
+    if gpu_out is not None:
+        rec["parity"] = _parity(np.stack(gots), np.stack(refs), n,
+                                "hq_decode_attn over the prompt's hybrid cache vs the oracle, (batch, KV head) units")
     return rec
 
 def _cpu_threads():
@@ -350,10 +365,11 @@ def _cpu_threads():
     return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
 
 
-def cpu_baseline_prefill(pin, sel_idx, sel_cnt, budget_s=8.0):
+def cpu_baseline_prefill(pin, sel_idx, sel_cnt, budget_s=8.0, gpu_head0=None):
     """The oracle's hybrid prefill timed on this host on sampled query rows of
     the 16K workload (INT8 stage of the head + per-row fp64 attention),
-    scaled to all rows of all heads, in ms."""
+    scaled to all rows of all heads, in ms. gpu_head0: the library's output
+    of head 0 [T][D], compared with the oracle's on the sampled rows."""
     import numpy as np
     import oracle as O
     sp = pin.spec
@@ -368,18 +384,25 @@ def cpu_baseline_prefill(pin, sel_idx, sel_cnt, budget_s=8.0):
     k8, sk = O.int8_block_quantize(k)
     t_quant = time.perf_counter() - t0
     S = sel_idx[0, 0, : sel_cnt[0, 0]].astype(np.int64)
-    done, t_rows = 0, 0.0
+    done, t_rows, refs, gots = 0, 0.0, [], []
     while t_rows < budget_s:
         rows = rng.integers(0, sp.T, size=16)
         t1 = time.perf_counter()
-        O.prefill_attention_rows(q, k, v, S, 128, sm, q8, sq, k8, sk, rows)
+        o = O.prefill_attention_rows(q, k, v, S, 128, sm, q8, sq, k8, sk, rows)
         t_rows += time.perf_counter() - t1
         done += len(rows)
+        if gpu_head0 is not None:
+            refs.append(o)
+            gots.append(gpu_head0[rows])
     # rows are uniform over [0, T), so the mean row cost scales to all rows
     full_s = t_rows / done * sp.T * sp.Hq + t_quant * (sp.Hq + sp.Hkv) / 2
-    return {"value": round(full_s * 1e3, 1), "unit": "ms/prefill", "cores": _cpu_threads(), "kind": "oracle",
-            "sample": f"{done} uniformly drawn query rows of head 0 of the 16K prefill "
-                      f"({t_rows:.1f} s) plus one head's INT8 stage, scaled to {sp.T} rows x {sp.Hq} heads"}
+    rec = {"value": round(full_s * 1e3, 1), "unit": "ms/prefill", "cores": _cpu_threads(), "kind": "oracle",
+           "sample": f"{done} uniformly drawn query rows of head 0 of the 16K prefill "
+                     f"({t_rows:.1f} s) plus one head's INT8 stage, scaled to {sp.T} rows x {sp.Hq} heads"}
+    if gpu_head0 is not None:
+        rec["parity"] = _parity(np.concatenate(gots), np.concatenate(refs), done,
+                                "hq_prefill_attn head 0 vs the oracle, query rows")
+    return rec
 
 
 def _graph_decode_us(hq, cache, q, out, n=20, reps=10):
@@ -926,6 +949,18 @@ def main():
         res["prefill_fp8"].update(prefill_low_error(hq, pf, psel, pol, polf))
         res["prefill_routing"] = prefill_routing_study(hq, pf, psel)
     sels = tuple(t.cpu().numpy() for t in (hq.probe_select(qp, k, lens, pol)))
+    par_dec = par_pf = None
+    if not args.no_cpu_baseline:
+        # the library's outputs on the units the oracle legs compute: decode of
+        # the second decode query over the prompt's cache (the oracle builds the
+        # same cache from the same selection), and the plain INT8 prefill
+        pc = hq.HybridCache(B, Hkv, T + N_DECODE, T, torch.bfloat16, dev, pol)
+        pcol, psl, pcnt, pthr = hq.probe_select(qp, k, lens, pol)
+        hq.quantize_kv(pc, k, v, lens, psl, pcnt, pcol, pthr)
+        par_dec = hq.decode_attn(pc, qd[1]).cpu().numpy()
+        del pc
+        if pf is not None:
+            par_pf = hq.prefill_attn(pf["q"], pf["k"], pf["v"], psel[1], psel[2], pol)[0, 0].cpu().numpy()
     del cache, k, v, knew, vnew
     if pf is not None:
         for key in ("q", "k", "v", "out", "qprobe"):
@@ -935,9 +970,9 @@ def main():
         res["workloads"] = decode_workloads(args)
         res["sweep"] = sweep(args)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, sels, qn[1])
+        res["cpu_baseline"] = cpu_baseline(inp, sels, qn[1], gpu_out=par_dec)
         if pf is not None and "pin" in pf:
-            res["cpu_baseline_prefill"] = cpu_baseline_prefill(pf["pin"], psel_idx, psel_cnt)
+            res["cpu_baseline_prefill"] = cpu_baseline_prefill(pf["pin"], psel_idx, psel_cnt, gpu_head0=par_pf)
     print(json.dumps(res), flush=True)
 
 

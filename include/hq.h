@@ -27,7 +27,10 @@
  *     changes the current device. Buffers are owned by the caller; the *_bytes
  *     and hq_cache_layout queries give their sizes.
  *   - Tensors are contiguous, row-major, in the shapes written next to each
- *     argument. 16-bit tensors use `dt` (HQ_BF16 or HQ_F16); head_dim D must
+ *     argument. Element types (`dt`, `out_dt`) are hq_dtype values passed as
+ *     int32_t, so that any integer a caller passes is validated rather than
+ *     being an out-of-range enum. 16-bit tensors use `dt` (HQ_BF16 or
+ *     HQ_F16); head_dim D must
  *     be 128; Hq must be a multiple of Hkv (grouped-query attention: query
  *     head h reads KV head h / (Hq/Hkv)); Hq/Hkv must be 1, 2, 4 or 8.
  *   - All device pointers must be 16-byte aligned. Outputs must not alias
@@ -129,7 +132,7 @@ int32_t hq_sel_stride(int32_t T, const hq_policy* policy);
  *   ws        workspace of hq_probe_ws_bytes(...) bytes                    */
 hq_status hq_probe_select(const void* q_probe, const void* k, const int32_t* seq_lens,
                           int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32_t D,
-                          hq_dtype dt, const hq_policy* policy, float sm_scale,
+                          int32_t dt, const hq_policy* policy, float sm_scale,
                           float* col_scores, int32_t* sel_idx, int32_t* sel_count,
                           hq_thresh* thresh, void* ws, size_t ws_bytes, void* stream);
 size_t hq_probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32_t D,
@@ -223,7 +226,7 @@ typedef struct {
  * cap_tokens above 2^24 returns HQ_ERR_CAPACITY (one (b, g)'s INT4 store is
  * addressed with 32-bit byte offsets).                                     */
 hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens,
-                          int32_t cap_probe, hq_dtype dt, const hq_policy* policy,
+                          int32_t cap_probe, int32_t dt, const hq_policy* policy,
                           hq_cache_sizes* out);
 
 /* The ragged INT4 layout: a host-side allocator for batches whose sequences
@@ -243,7 +246,7 @@ hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens,
  * uniform layout's INT4 capacity, at least every sequence's.
  * Errors as hq_cache_layout, checked for every cap_tokens[b].            */
 hq_status hq_cache_layout_ragged(int32_t B, int32_t Hkv, int32_t D, const int32_t* cap_tokens,
-                                 int32_t cap_probe, hq_dtype dt, const hq_policy* policy,
+                                 int32_t cap_probe, int32_t dt, const hq_policy* policy,
                                  int64_t* q_tile_off, hq_cache_sizes* out);
 
 /* ------------------------------------------------------------------------
@@ -299,7 +302,7 @@ hq_status hq_append_kv(const hq_cache* cache, const void* k_new, const void* v_n
  * alike for the current device. The result does not depend on it beyond
  * fp32 rounding. */
 hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,
-                         void* out, hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
+                         void* out, int32_t out_dt, void* ws, size_t ws_bytes, void* stream);
 size_t hq_decode_ws_bytes(const hq_cache* cache, int32_t Hq);
 
 /* ------------------------------------------------------------------------
@@ -357,7 +360,7 @@ size_t hq_reprobe_ws_bytes(const hq_cache* cache, int32_t Hq, const hq_policy* p
  * in the array needs to be cleared between calls. */
 #define HQ_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 hq_status hq_decode_attn_noalloc(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,
-                                 void* out, hq_dtype out_dt, void* stream);
+                                 void* out, int32_t out_dt, void* stream);
 
 /* ------------------------------------------------------------------------
  * hq_prefill_attn -- causal hybrid-precision prefill attention.
@@ -408,10 +411,10 @@ hq_status hq_decode_attn_noalloc(const hq_cache* cache, const void* q, int32_t H
  * in {1, 2, 4, 8} or an unsupported dtype; HQ_ERR_CAPACITY if ws_bytes is
  * too small; HQ_ERR_INVALID_ARG for null pointers or T outside [1, 2^22]. */
 hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B, int32_t Hq,
-                          int32_t Hkv, int32_t T, int32_t D, hq_dtype dt,
+                          int32_t Hkv, int32_t T, int32_t D, int32_t dt,
                           const hq_policy* policy, const int32_t* sel_idx,
                           const int32_t* sel_count, float sm_scale, void* out,
-                          hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream);
+                          int32_t out_dt, void* ws, size_t ws_bytes, void* stream);
 size_t hq_prefill_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t D,
                            const hq_policy* policy);
 

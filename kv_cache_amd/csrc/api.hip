@@ -153,7 +153,7 @@ int32_t hq_sel_stride(int32_t T, const hq_policy* policy) {
     return hq::sel_stride(T, *policy);
 }
 
-hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens, int32_t cap_probe, hq_dtype dt,
+hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens, int32_t cap_probe, int32_t dt,
                           const hq_policy* policy, hq_cache_sizes* out) {
     static const char* fn = "hq_cache_layout";
     clear_err();
@@ -197,7 +197,7 @@ hq_status hq_cache_layout(int32_t B, int32_t Hkv, int32_t D, int32_t cap_tokens,
 }
 
 hq_status hq_cache_layout_ragged(int32_t B, int32_t Hkv, int32_t D, const int32_t* cap_tokens, int32_t cap_probe,
-                                 hq_dtype dt, const hq_policy* policy, int64_t* q_tile_off, hq_cache_sizes* out) {
+                                 int32_t dt, const hq_policy* policy, int64_t* q_tile_off, hq_cache_sizes* out) {
     static const char* fn = "hq_cache_layout_ragged";
     clear_err();
     hq_status st = check_policy(fn, policy);
@@ -239,7 +239,7 @@ size_t hq_probe_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32
 }
 
 hq_status hq_probe_select(const void* q_probe, const void* k, const int32_t* seq_lens, int32_t B, int32_t Hq,
-                          int32_t Hkv, int32_t Tmax, int32_t D, hq_dtype dt, const hq_policy* policy,
+                          int32_t Hkv, int32_t Tmax, int32_t D, int32_t dt, const hq_policy* policy,
                           float sm_scale, float* col_scores, int32_t* sel_idx, int32_t* sel_count,
                           hq_thresh* thresh, void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "hq_probe_select";
@@ -322,7 +322,7 @@ namespace {
 // Shared by hq_decode_attn (caller's workspace) and hq_decode_attn_noalloc
 // (ws == nullptr: the library's static scratch array).
 hq_status decode_call(const char* fn, const hq_cache* cache, const void* q, int32_t Hq, float sm_scale,
-                      void* out, hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
+                      void* out, int32_t out_dt, void* ws, size_t ws_bytes, void* stream) {
     clear_err();
     hq_status st;
     if ((st = check_cache(fn, cache))) return st;
@@ -353,7 +353,7 @@ hq_status decode_call(const char* fn, const hq_cache* cache, const void* q, int3
         hipError_t e = hq::decode_scratch(&d.ws);
         if (e != hipSuccess) return fail(HQ_ERR_HIP, "%s: scratch lookup failed: %s", fn, hipGetErrorString(e));
     }
-    hipError_t e = hq::launch_decode(*cache, q, out, out_dt, d, (hipStream_t)stream);
+    hipError_t e = hq::launch_decode(*cache, q, out, (hq_dtype)out_dt, d, (hipStream_t)stream);  // validated above
     return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
 }
 
@@ -362,7 +362,7 @@ hq_status decode_call(const char* fn, const hq_cache* cache, const void* q, int3
 extern "C" {
 
 hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale, void* out,
-                         hq_dtype out_dt, void* ws, size_t ws_bytes, void* stream) {
+                         int32_t out_dt, void* ws, size_t ws_bytes, void* stream) {
     if (ws == nullptr) {
         clear_err();
         return fail(HQ_ERR_INVALID_ARG, "hq_decode_attn: ws is null");
@@ -371,7 +371,7 @@ hq_status hq_decode_attn(const hq_cache* cache, const void* q, int32_t Hq, float
 }
 
 hq_status hq_decode_attn_noalloc(const hq_cache* cache, const void* q, int32_t Hq, float sm_scale, void* out,
-                                 hq_dtype out_dt, void* stream) {
+                                 int32_t out_dt, void* stream) {
     return decode_call("hq_decode_attn_noalloc", cache, q, Hq, sm_scale, out, out_dt, nullptr, (size_t)-1,
                        stream);
 }
@@ -423,8 +423,8 @@ size_t hq_prefill_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_
 }
 
 hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
-                          int32_t D, hq_dtype dt, const hq_policy* policy, const int32_t* sel_idx,
-                          const int32_t* sel_count, float sm_scale, void* out, hq_dtype out_dt, void* ws,
+                          int32_t D, int32_t dt, const hq_policy* policy, const int32_t* sel_idx,
+                          const int32_t* sel_count, float sm_scale, void* out, int32_t out_dt, void* ws,
                           size_t ws_bytes, void* stream) {
     static const char* fn = "hq_prefill_attn";
     clear_err();
@@ -450,7 +450,7 @@ hq_status hq_prefill_attn(const void* q, const void* k, const void* v, int32_t B
     if (reinterpret_cast<uintptr_t>(ws) % 256)
         return fail(HQ_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
     hipError_t e = hq::launch_prefill(q, k, v, B, Hq, Hkv, T, dt == HQ_F16, *policy, sel_idx, sel_count,
-                                      hq::sel_stride(T, *policy), sm_scale, out, out_dt, ws, (hipStream_t)stream);
+                                      hq::sel_stride(T, *policy), sm_scale, out, (hq_dtype)out_dt, ws, (hipStream_t)stream);
     return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
 }
 

@@ -290,3 +290,39 @@ def test_cache_layout_ragged_closed_form(hq):
                                          ctypes.byref(rg)) == hq.HQ_ERR_INVALID_ARG
     c = _cache(hq, q_tile_off=0x100000, q_tiles_total=0)
     assert hq.lib.hq_append_kv(ctypes.byref(c), FAKE, FAKE, None) == hq.HQ_ERR_INVALID_ARG
+
+
+def test_host_layer_under_address_and_undefined_sanitizers(tmp_path):
+    """The library's sources and tests/abi_host_check.cpp built with
+    AddressSanitizer and UndefinedBehaviorSanitizer on the host side (device
+    code is compiled as usual and never run), then run with every device
+    hidden: size and layout queries and every validation path, on bad and
+    edge arguments, must finish with no sanitizer report."""
+    import glob
+    import shutil
+    import subprocess
+    from concurrent.futures import ThreadPoolExecutor
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+    base = [hipcc, "--offload-arch=gfx950", "-std=c++17", "-O1", "-fno-omit-frame-pointer",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"] + san
+    srcs = sorted(glob.glob(os.path.join(ROOT, "kv_cache_amd", "csrc", "*.hip")))
+    srcs.append(os.path.join(ROOT, "tests", "abi_host_check.cpp"))
+
+    def compile_one(src):
+        obj = str(tmp_path / (os.path.basename(src) + ".o"))
+        r = subprocess.run(base + ["-c", src, "-o", obj], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return obj
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    exe = str(tmp_path / "abi_host_check")
+    r = subprocess.run([hipcc, "--offload-arch=gfx950"] + san + objs + ["-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="",
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1", UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0 and "host checks passed" in r.stdout, (r.stdout[-2000:], r.stderr[-2000:])
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-2000:]
