@@ -117,10 +117,14 @@ int32_t hq_sel_stride(int32_t T, const hq_policy* policy);
  * sm_scale is used as the fp32 value passed. Logits come from exact integer
  * products on the int8 matrix cores (each 16-bit value written as base-256
  * digits of a scaled integer); a per-tile a-posteriori bound on the digits
- * left out is checked and any tile above 1.5e-7 (log2 units) is recomputed
- * in fp64. Softmax normalisers and column sums accumulate in fp64; scores
- * are rounded once to fp32. Each score's relative error is below 2.9e-7
- * (with the observed bounds, ~1e-8 logit error, it is the fp32 rounding).
+ * left out is checked and any tile above 1.0e-7 (log2 units) is recomputed
+ * in fp64. Each logit is computed once: its softmax term (against a
+ * per-row, per-key-chunk power-of-two reference) is stored in fp32 in the
+ * workspace, the row normalisers and the column sums of the stored terms
+ * accumulate in fp64, and the scores are rounded to fp32. Each score above
+ * 1e-30 has a relative error below 2.9e-7 (with the observed bounds, ~1e-8
+ * logit error, it is the two fp32 roundings); smaller scores are within
+ * 1e-42 absolute.
  * Supported shapes: (Hq/Hkv) * probe_rows must be a multiple of 16 and at
  * most 512; other shapes return HQ_ERR_UNSUPPORTED before any launch.
  *   q_probe   [B][Hq][probe_rows][D] dt  row r is position T_b - probe_rows + r
@@ -129,7 +133,10 @@ int32_t hq_sel_stride(int32_t T, const hq_policy* policy);
  *   col_scores[B][Hkv][Tmax] fp32 out (entries >= T_b are set to 0)
  *   sel_idx   [B][Hkv][hq_sel_stride(Tmax)] int32 out (unused tail = -1)
  *   sel_count [B][Hkv] int32 out;  thresh [B][Hkv] out
- *   ws        workspace of hq_probe_ws_bytes(...) bytes                    */
+ *   ws        workspace of hq_probe_ws_bytes(...) bytes: mostly the probe
+ *             rows' stored terms, 4 * (Hq/Hkv) * probe_rows * Tmax bytes
+ *             (Tmax rounded up to 32) per (b, KV head); 4.3 GB for B = 16,
+ *             8 KV heads, 4 heads each, 64 rows, Tmax = 32768             */
 hq_status hq_probe_select(const void* q_probe, const void* k, const int32_t* seq_lens,
                           int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32_t D,
                           int32_t dt, const hq_policy* policy, float sm_scale,

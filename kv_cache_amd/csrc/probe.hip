@@ -3,17 +3,21 @@
 // HyQuant pages: "HyQuant: Hybrid-Precision Quantization for LLM
 // Attention", TL;DR and "What problem it solves" (a small number of key
 // columns are attended to by almost every query row; a lightweight pattern
-// signal finds them without calibration), "Gaps" (the probe must not
-// materialise the attention map); "How HyQuant uses hybrid-precision
-// attention to cut decode compute", "Why preserve selected positions?" (keep
-// the top 5% high-score positions) and "Memory and runtime costs" (finding
-// the columns costs a few percent of the runtime).
+// signal finds them without calibration), "Gaps" (the probe works on the
+// attention map, the tensor the method otherwise avoids forming); "How HyQuant
+// uses hybrid-precision attention to cut decode compute", "Why preserve
+// selected positions?" (keep the top 5% high-score positions) and "Memory and
+// runtime costs" (finding the columns costs a few percent of the runtime).
 //
 // Column score c[j] = sum over the G query heads and the last R probe rows of
-// the row-normalised causal softmax. The map is never stored: pass 1
-// computes each row's normaliser over key chunks, a combine kernel merges
-// the chunks into one reference per row, pass 2 recomputes the logits and
-// sums the normalised probabilities per column.
+// the row-normalised causal softmax. Only the probe rows' slice of the map
+// (G R rows x T keys per (b, g); at 32K and G R = 256, 0.8% of the T x T map)
+// is ever formed, and each of its logits is computed once: pass 1 computes
+// the logits, each term 2^(z - m) against an integer reference m per (row,
+// key chunk), the rows' normalisers per chunk, and stores the terms (fp32)
+// in the workspace; a combine kernel merges the chunks into (M, 1/L) per
+// row; pass 2 streams the stored terms and adds them per column with the
+// weights 2^(m - M) / L in fp64.
 //
 // Logits, exactly, on the int8 matrix cores. Every 16-bit value x of a set
 // (a 32-row tile of probe queries, or one key) becomes the integer
@@ -54,14 +58,17 @@ namespace {
 
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef int intx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRT = 32;            // probe rows per row tile (one wave)
 constexpr int kKT = 32;            // keys per key tile
 constexpr int kTilesPerWg = 8;     // row tiles (waves) per workgroup at most
 constexpr int kPlanes = 4;         // base-256 digits per value
 constexpr int kDS = kD + 16;       // LDS bytes per key in a digit plane (pad: no bank conflicts)
-constexpr int kColBlk = 512;       // largest keys per pass-2 workgroup (the launch picks 512 or 256)
-constexpr double kLogitBudget = 1.5e-7;  // largest logit error accepted from the digit path (log2 units)
+constexpr int kColCols = 1024;     // columns per pass-2 workgroup (256 threads x 4)
+constexpr int kMoveGap = 100;      // a row's reference moves when a logit exceeds it by more than this (log2
+                                   // units), so every stored term 2^(z - ref) is at most 2^100 (fp32 range)
+constexpr double kLogitBudget = 1.0e-7;  // largest logit error accepted from the digit path (log2 units)
 constexpr int kExpTerms = 7;       // 2^f = sum_{n <= 7} (f ln2)^n / n!, |f| <= 1/2: relative error < 1.1e-8
 
 struct ProbeParams {
@@ -69,10 +76,11 @@ struct ProbeParams {
     const uint16_t* k;     // [B][Hkv][Tmax][D]
     const int32_t* seq_lens;
     double2* part;         // [B][Hkv][nchunk][NRp] (m, l) per key chunk: l = sum 2^(z - m), m an integer
-    double* rowref;        // [B][Hkv][NRp] m' = M + log2(L) per row: p = 2^(z - m')
-    double* colpart;       // [B][Hkv][ngroups][Tmax] column sums per row group (ngroups > 1)
+    double2* rownorm;      // [B][Hkv][NRp] (M, 1/L) per row: p = 2^(z - M) / L
+    float* emap;           // [B][Hkv][NRp][Tp] the probe rows' terms 2^(z - m) of pass 1, m the row's
+                           // reference in the key's chunk (0 outside the causal map)
     float* col_scores;     // [B][Hkv][Tmax]
-    int32_t B, Hq, Hkv, Tmax, R, G, NR, NRp, ngroups, nchunk, chunk, colblk;
+    int32_t B, Hq, Hkv, Tmax, Tp, R, G, NR, NRp, ngroups, nchunk, chunk;
     double sc2;            // sm_scale * log2(e)
     double ec[kExpTerms + 1];  // (ln2)^n / n!, n = 0..7
 };
@@ -179,10 +187,9 @@ struct QPlanes {
     int8_t d[2][kRT][kDS];
 };
 
-struct ProbeSmem {
+struct __align__(16) ProbeSmem {  // 16-byte rows: the MFMA operands are read as 128-bit LDS loads
     KeyTile kt[2];
     QPlanes q23[kTilesPerWg];
-    double col[kTilesPerWg][kColBlk];  // pass 2: per-wave column partial sums of the block
 };
 
 // Key tile [key0, key0 + 32) of one (b, g): thread t (of the workgroup's
@@ -437,10 +444,21 @@ constexpr double kZeros[16] = {};
 // the element loops need no mask.
 __device__ inline bool tile_full(uint32_t mk) { return __builtin_amdgcn_ballot_w64(mk != 0xFFFFu) == 0; }
 
+// One stored term of pass 1 (fp32, rounded to nearest), streamed past the caches.
+__device__ inline void store_term(const __amdgpu_buffer_rsrc_t& r, int voff, int soff, double e) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((float)e), r, voff, soff, kLoadNT);
+}
+
 // Pass 1: per (key chunk, row group, g, b): for every probe row of the group,
 // (m, l) over the chunk's keys with m an integer reference and
-// l = sum 2^(z - m). One wave per 32-row tile; the key tiles are converted to
-// digits once per workgroup into LDS (double-buffered) and read by every wave.
+// l = sum 2^(z - m), and every term 2^(z - m) stored (fp32) for pass 2. One
+// wave per 32-row tile; the key tiles are converted to digits once per
+// workgroup into LDS (double-buffered) and read by every wave. A row's
+// reference is the same in the 32 lanes of a half-wave (the lanes are the
+// tile's keys): it is set from the first tile with a valid logit of the row
+// and moves up only when a logit exceeds it by more than kMoveGap; a move
+// rescales the lane's sum and the terms the lane already stored for the row
+// by the same power of two, exactly (down to fp32 underflow).
 template <bool F16>
 __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
     __shared__ ProbeSmem sm;
@@ -462,7 +480,14 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
     const uint16_t* kbase = p.k + (size_t)bg * p.Tmax * kD;
     const QTile q = convert_queries<F16>(p, b, g, T, rt, sm.q23[wave]);
     const uint32_t rowmk = row_mask(p, T, rt);
-    int m[16];  // integer references (INT_MIN: none yet)
+    // this lane's stored terms: element i is row rt*32 + 8(i/4) + 4(lane/32) + i%4,
+    // key key0 + lane % 32; a buffer resource over the tile's rows from key_lo
+    // (32-bit offsets: at most 32 rows x Tp keys)
+    const int hoff = 4 * (lane >> 5);
+    const __amdgpu_buffer_rsrc_t emr = __builtin_amdgcn_make_buffer_rsrc(
+        p.emap + ((size_t)bg * p.NRp + rt * kRT) * p.Tp + key_lo, (short)0, kRT * p.Tp * 4 - key_lo * 4, 0x00020000);
+    const int evoff = ((lane & 31) + hoff * p.Tp) * 4;
+    int m[16];  // integer references, uniform over the half-wave (INT_MIN: none yet)
     double l[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -480,30 +505,50 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
             double z[16];
             tile_logits<F16>(p, q, sm.q23[wave], sm.kt[cur], b, g, kbase, key, key_hi, rt, kZeros, z);
             const uint32_t mk = tile_mask(p, T, rt, rowmk, key0, key_hi);
-            // move a reference up to ceil(z) where a valid logit exceeds it by
-            // more than 256 (rare; always at a row's first valid logit): an
-            // exact power-of-two rescale of l
             bool move = false;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) move |= ((mk >> i) & 1u) && z[i] > (double)m[i] + 256.0;
+            for (int i = 0; i < 16; ++i) move |= ((mk >> i) & 1u) && z[i] > (double)m[i] + kMoveGap;
             if (__builtin_amdgcn_ballot_w64(move) != 0) {
+                // rare (once per row and chunk, at its first valid logits):
+                // the half-wave's largest valid logit of each element's row
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    if (((mk >> i) & 1u) && z[i] > (double)m[i] + 256.0) {
-                        const int mn = (int)__builtin_ceil(fmax(fmin(z[i], 2.0e9), -2.0e9));
-                        l[i] = m[i] == INT_MIN ? 0.0 : __builtin_ldexp(l[i], m[i] - mn);
+                    double v = ((mk >> i) & 1u) ? z[i] : -INFINITY;
+#pragma unroll
+                    for (int o = 1; o < 32; o <<= 1) v = fmax(v, __shfl_xor(v, o));
+                    if (v > (double)m[i] + kMoveGap) {  // the same decision in all 32 lanes of the half
+                        const int mn = (int)__builtin_ceil(fmax(fmin(v, 2.0e9), -2.0e9));
+                        if (m[i] != INT_MIN) {
+                            const int sh = m[i] - mn;
+                            l[i] = __builtin_ldexp(l[i], sh);
+                            const int so = (8 * (i >> 2) + (i & 3)) * p.Tp * 4;
+                            for (int u = 0; u < t; ++u) {
+                                const float x = __uint_as_float(
+                                    __builtin_amdgcn_raw_buffer_load_b32(emr, evoff, so + kKT * u * 4, 0));
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_ldexpf(x, sh)), emr,
+                                                                      evoff, so + kKT * u * 4, 0);
+                            }
+                        }
                         m[i] = mn;
                     }
                 }
             }
+            // straight-line code over the 16 independent elements in both
+            // forms (a masked element's exponential is computed, then dropped)
             if (tile_full(mk)) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) l[i] += exp2_d(z[i] - (double)m[i], p.ec);
+                for (int i = 0; i < 16; ++i) {
+                    const double e = exp2_d(z[i] - (double)m[i], p.ec);
+                    l[i] += e;
+                    store_term(emr, evoff, ((8 * (i >> 2) + (i & 3)) * p.Tp + key0 - key_lo) * 4, e);
+                }
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const double e = exp2_d(z[i] - (double)m[i], p.ec);
-                    l[i] += ((mk >> i) & 1u) ? e : 0.0;
+                    const double ev = ((mk >> i) & 1u) ? e : 0.0;
+                    l[i] += ev;
+                    store_term(emr, evoff, ((8 * (i >> 2) + (i & 3)) * p.Tp + key0 - key_lo) * 4, ev);
                 }
             }
         }
@@ -511,21 +556,12 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
         __syncthreads();
     }
     if (!active) return;
-    // merge the 32 lanes of each half (same rows, different keys): exact
-    // power-of-two rescales to the larger reference
+    // the 32 lanes of each half hold the same rows (different keys) with the
+    // same references: their sums add
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m2 = __shfl_xor(m[i], o);
-            const double l2 = __shfl_xor(l[i], o);
-            const int M = max(m[i], m2);
-            double L = 0.0;
-            if (m[i] != INT_MIN) L += __builtin_ldexp(l[i], m[i] - M);
-            if (m2 != INT_MIN) L += __builtin_ldexp(l2, m2 - M);
-            m[i] = M;
-            l[i] = L;
-        }
+        for (int i = 0; i < 16; ++i) l[i] += __shfl_xor(l[i], o);
     }
     if ((lane & 31) == 0) {
 #pragma unroll
@@ -535,7 +571,7 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
 }
 
 // Merge the chunk statistics of every probe row: M = the largest chunk
-// reference, L = sum l 2^(m - M) (exact rescales), m' = M + log2(L).
+// reference, L = sum l 2^(m - M) (exact rescales); stores (M, 1/L).
 __global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
     const int g = blockIdx.x, b = blockIdx.y;
     const int bg = b * p.Hkv + g;
@@ -551,95 +587,52 @@ __global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
                 if (v.x != -INFINITY) L += __builtin_ldexp(v.y, (int)(v.x - M));
             }
         }
-        p.rowref[(size_t)bg * p.NRp + row] = L > 0.0 ? M + log2(L) : INFINITY;
+        p.rownorm[(size_t)bg * p.NRp + row] = L > 0.0 ? make_double2(M, 1.0 / L) : make_double2(-INFINITY, 0.0);
     }
 }
 
-// Pass 2: per (512- or 256-key block, row group, g, b): column sums of
-// 2^(z - m'_row) over the group's probe rows. The same tiling as pass 1;
-// per lane the 16 rows of its elements, per wave a 32-row tile; the waves'
-// partial sums meet in LDS and are added in a fixed order.
-template <bool F16>
-__global__ __launch_bounds__(512) void k_probe_colsum(ProbeParams p) {
-    __shared__ ProbeSmem sm;
-    const int lane = threadIdx.x & 63, hf = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nw = blockDim.x >> 6;
-    const int blk = blockIdx.x, grp = blockIdx.y % p.ngroups, g = blockIdx.y / p.ngroups, b = blockIdx.z;
-    const int T = p.seq_lens[b];
-    const int bg = b * p.Hkv + g;
-    const int rt = grp * kTilesPerWg + wave;
-    const int key_lo = blk * p.colblk;
-    float* out = p.col_scores + (size_t)bg * p.Tmax;
-    double* outp = p.colpart + ((size_t)bg * p.ngroups + grp) * p.Tmax;
-    if (key_lo >= T) {
-        for (int j = threadIdx.x; j < p.colblk && key_lo + j < p.Tmax; j += blockDim.x) {
-            if (p.ngroups == 1) out[key_lo + j] = 0.0f;
-            else outp[key_lo + j] = 0.0;
-        }
-        return;
-    }
-    const int key_hi = min(key_lo + p.colblk, T);
-    const int ntile = (key_hi - key_lo + kKT - 1) / kKT;
-    const uint16_t* kbase = p.k + (size_t)bg * p.Tmax * kD;
-    const bool active = rt * kRT < p.NRp;
-    const QTile q = convert_queries<F16>(p, b, g, T, rt, sm.q23[wave]);
-    const uint32_t rowmk = row_mask(p, T, rt);
-    double ref[16];  // m' of each element's row (rows beyond NR are never used)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int row = elem_row(rt, i);
-        ref[i] = row < p.NR ? p.rowref[(size_t)bg * p.NRp + row] : 0.0;
-    }
-    store_keys<F16>(load_keys(kbase, key_lo, key_hi), sm.kt[0]);
-    __syncthreads();
-    for (int t = 0; t < ntile; ++t) {
-        const int cur = t & 1;
-        const int key0 = key_lo + kKT * t;
-        const uint4 nxt = load_keys(kbase, key0 + kKT, t + 1 < ntile ? key_hi : 0);  // next tile, in flight
-        double acc = 0.0;
-        if (active) {
-            const int key = key0 + (lane & 31);
-            double d[16];  // z - m'
-            tile_logits<F16>(p, q, sm.q23[wave], sm.kt[cur], b, g, kbase, key, key_hi, rt, ref, d);
-            const uint32_t mk = tile_mask(p, T, rt, rowmk, key0, key_hi);
-            if (tile_full(mk)) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc += exp2_d(d[i], p.ec);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const double e = exp2_d(d[i], p.ec);
-                    acc += ((mk >> i) & 1u) ? e : 0.0;
-                }
-            }
-            acc += __shfl_xor(acc, 32);
-        }
-        if (hf == 0) sm.col[wave][kKT * t + (lane & 31)] = acc;
-        if (t + 1 < ntile) store_keys<F16>(nxt, sm.kt[cur ^ 1]);
-        __syncthreads();
-    }
-    // sum over the waves (row tiles) in order
-    for (int j = threadIdx.x; j < p.colblk; j += blockDim.x) {
-        const int key = key_lo + j;
-        if (key >= p.Tmax) break;
-        double sum = 0.0;
-        if (key < key_hi)
-            for (int w = 0; w < nw; ++w) sum += sm.col[w][j];
-        if (p.ngroups == 1) out[key] = key < key_hi ? (float)sum : 0.0f;
-        else outp[key] = sum;
-    }
-}
-
-// More than 8 row tiles: the row groups' column sums, added in group order.
-__global__ __launch_bounds__(256) void k_probe_colfinal(ProbeParams p) {
+// Pass 2: per (1,024-column block, g, b): c[j] = sum over the probe rows r of
+// E[r][j] * w[r][chunk(j)], E the terms pass 1 stored and
+// w = 2^(m_chunk - M) / L the row's weight for that chunk (fp64). Thread t
+// takes columns j0 + 4t .. + 3 and adds the rows in order, in fp64.
+__global__ __launch_bounds__(256) void k_probe_colsum(ProbeParams p) {
+    __shared__ double wt[kColCols / 256][2 * kTilesPerWg * kRT];  // [chunk in the block][row], NR <= 512
     const int g = blockIdx.y, b = blockIdx.z;
     const int bg = b * p.Hkv + g;
-    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int T = p.seq_lens[b];
+    const int j0 = blockIdx.x * kColCols;
+    const int c0 = j0 / p.chunk;  // chunks are 256, 512 or 1,024 keys
+    const int ncb = min(kColCols / p.chunk, p.nchunk - c0);
+    for (int idx = threadIdx.x; idx < ncb * p.NR; idx += 256) {
+        const int cc = idx / p.NR, row = idx - cc * p.NR;
+        const double2 pr = p.part[((size_t)bg * p.nchunk + c0 + cc) * p.NRp + row];
+        const double2 rn = p.rownorm[(size_t)bg * p.NRp + row];
+        wt[cc][row] = (pr.x == -INFINITY || rn.y == 0.0)
+                          ? 0.0
+                          : __builtin_ldexp(rn.y, (int)fmax(pr.x - rn.x, -2000.0));  // pr.x <= rn.x
+    }
+    __syncthreads();
+    const int j = j0 + 4 * (int)threadIdx.x;
     if (j >= p.Tmax) return;
-    double s = 0.0;
-    for (int grp = 0; grp < p.ngroups; ++grp) s += p.colpart[((size_t)bg * p.ngroups + grp) * p.Tmax + j];
-    p.col_scores[(size_t)bg * p.Tmax + j] = (float)s;
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    if (j < T) {
+        const double* w = wt[j / p.chunk - c0];
+        const float* e = p.emap + (size_t)bg * p.NRp * p.Tp + j;
+#pragma unroll 8
+        for (int r = 0; r < p.NR; ++r) {
+            const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(e + (size_t)r * p.Tp));
+            const double wr = w[r];
+            a0 = __builtin_fma(wr, (double)v[0], a0);
+            a1 = __builtin_fma(wr, (double)v[1], a1);
+            a2 = __builtin_fma(wr, (double)v[2], a2);
+            a3 = __builtin_fma(wr, (double)v[3], a3);
+        }
+    }
+    float* out = p.col_scores + (size_t)bg * p.Tmax;
+    const double a[4] = {a0, a1, a2, a3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (j + i < p.Tmax) out[j + i] = j + i < T ? (float)a[i] : 0.0f;
 }
 
 // ---------------------------------------------------------------- top-k
@@ -776,7 +769,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
 
 
 struct ProbeWs {
-    size_t part, rowref, colpart, total;
+    size_t part, rownorm, emap, total;
 };
 inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -797,14 +790,15 @@ ProbeShape probe_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const h
     s.nchunk = (Tmax + s.chunk - 1) / s.chunk;
     return s;
 }
+inline int probe_tp(int32_t Tmax) { return (Tmax + kKT - 1) / kKT * kKT; }
 ProbeWs probe_ws(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_policy& pol) {
     const ProbeShape s = probe_shape(B, Hq, Hkv, Tmax, pol);
     const size_t BG = (size_t)B * Hkv;
     ProbeWs w;
     w.part = 0;
-    w.rowref = al(BG * s.nchunk * s.NRp * 16);
-    w.colpart = w.rowref + al(BG * s.NRp * 8);
-    w.total = w.colpart + (s.ngroups > 1 ? al(BG * s.ngroups * (size_t)Tmax * 8) : 0);
+    w.rownorm = al(BG * s.nchunk * s.NRp * 16);
+    w.emap = w.rownorm + al(BG * s.NRp * 16);
+    w.total = w.emap + al(BG * s.NRp * (size_t)probe_tp(Tmax) * 4);
     return w;
 }
 
@@ -834,13 +828,14 @@ hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_l
     p.k = static_cast<const uint16_t*>(k);
     p.seq_lens = seq_lens;
     p.part = reinterpret_cast<double2*>(static_cast<char*>(ws) + w.part);
-    p.rowref = reinterpret_cast<double*>(static_cast<char*>(ws) + w.rowref);
-    p.colpart = reinterpret_cast<double*>(static_cast<char*>(ws) + w.colpart);
+    p.rownorm = reinterpret_cast<double2*>(static_cast<char*>(ws) + w.rownorm);
+    p.emap = reinterpret_cast<float*>(static_cast<char*>(ws) + w.emap);
     p.col_scores = col_scores;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.Tmax = Tmax;
+    p.Tp = probe_tp(Tmax);
     p.R = pol.probe_rows;
     p.G = Hq / Hkv;
     p.NR = sh.NR;
@@ -866,17 +861,8 @@ hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_l
     if (e != hipSuccess) return e;
     k_probe_rowfinal<<<dim3(Hkv, B), 256, 0, s>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // 512-key blocks (the query tiles' digit conversion amortised over twice
-    // the keys) while the grid keeps at least 1,024 workgroups
-    p.colblk = (int64_t)((Tmax + 511) / 512) * Hkv * sh.ngroups * B >= 1024 ? 512 : 256;
-    dim3 g2((Tmax + p.colblk - 1) / p.colblk, Hkv * sh.ngroups, B);
-    if (f16) k_probe_colsum<true><<<g2, threads, 0, s>>>(p);
-    else k_probe_colsum<false><<<g2, threads, 0, s>>>(p);
+    k_probe_colsum<<<dim3((Tmax + kColCols - 1) / kColCols, Hkv, B), 256, 0, s>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (sh.ngroups > 1) {
-        k_probe_colfinal<<<dim3((Tmax + 255) / 256, Hkv, B), 256, 0, s>>>(p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     k_topk_select<<<dim3(Hkv, B), 1024, 0, s>>>(col_scores, seq_lens, Hkv, Tmax, pol, sel_stride(Tmax, pol),
                                                   sel_idx, sel_count, thresh);
     return hipGetLastError();
