@@ -571,20 +571,30 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
 }
 
 // Merge the chunk statistics of every probe row: M = the largest chunk
-// reference, L = sum l 2^(m - M) (exact rescales); stores (M, 1/L).
+// reference, L = sum l 2^(m - M); stores (M, 1/L). One pass over the chunks
+// in order with a running maximum: every rescale is by a power of two, so L
+// is the same exact-rescale sum in any order of maxima; the loads of 8
+// chunks are issued before they are used.
 __global__ __launch_bounds__(256) void k_probe_rowfinal(ProbeParams p) {
     const int g = blockIdx.x, b = blockIdx.y;
     const int bg = b * p.Hkv + g;
     const int T = p.seq_lens[b];
     const int nch = (T + p.chunk - 1) / p.chunk;
     for (int row = threadIdx.x; row < p.NRp; row += 256) {
-        double M = -INFINITY;
-        for (int c = 0; c < nch; ++c) M = fmax(M, p.part[((size_t)bg * p.nchunk + c) * p.NRp + row].x);
-        double L = 0.0;
-        if (M != -INFINITY) {
-            for (int c = 0; c < nch; ++c) {
-                const double2 v = p.part[((size_t)bg * p.nchunk + c) * p.NRp + row];
-                if (v.x != -INFINITY) L += __builtin_ldexp(v.y, (int)(v.x - M));
+        const double2* pc = p.part + (size_t)bg * p.nchunk * p.NRp + row;
+        double M = -INFINITY, L = 0.0;
+        for (int c0 = 0; c0 < nch; c0 += 8) {
+            double2 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = c0 + j < nch ? pc[(size_t)(c0 + j) * p.NRp] : make_double2(-INFINITY, 0.0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (v[j].x == -INFINITY) continue;
+                if (v[j].x > M) {
+                    L = M == -INFINITY ? 0.0 : __builtin_ldexp(L, (int)fmax(M - v[j].x, -2000.0));
+                    M = v[j].x;
+                }
+                L += __builtin_ldexp(v[j].y, (int)fmax(v[j].x - M, -2000.0));
             }
         }
         p.rownorm[(size_t)bg * p.NRp + row] = L > 0.0 ? make_double2(M, 1.0 / L) : make_double2(-INFINITY, 0.0);
