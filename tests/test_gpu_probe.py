@@ -106,3 +106,36 @@ def test_probe_logit_range_beyond_reference():
     logits = O.to_f64(inp.q_probe, "bf16")[0, 0] @ O.to_f64(inp.k, "bf16")[0, 0].T * sm / math.log(2)
     assert logits[:, 300:451].min() - logits[:, :300].max() > 512
     check_probe(inp, 128, (5, 100), floor=1e-30)
+
+
+def _reference_move_inputs():
+    """All probe rows along one direction u; every key near zero except 8
+    keys (300..307) along u whose logits sit ~103 log2 units higher. The
+    probe's key chunks are 256 keys here, so in the chunk of keys 256..511
+    every row's reference is set by the tile of keys 256..287 and then has to
+    move (by more than 100) at the tile holding the 8 keys; the terms already
+    stored for keys 256..287 are rescaled by that power of two and stay
+    normal fp32 numbers, so every score keeps the relative bound (the scores
+    of the near-zero keys are 1e-32 .. 1e-30: a key is seen by fewer probe
+    rows the later it is)."""
+    inp = small_decode_inputs(B=1, Hq=4, Hkv=1, T=1500, seed=51)
+    rng = np.random.default_rng(5151)
+    u = np.ones(128, dtype=np.float32)
+    inp.q_probe[...] = bf16_bits_from_f32(u + 0.05 * rng.standard_normal(inp.q_probe.shape, dtype=np.float32))
+    k = 0.05 * rng.standard_normal((1500, 128), dtype=np.float32)
+    k[300:308] += 6.35 * u
+    inp.k[0, 0] = bf16_bits_from_f32(k)
+    return inp
+
+
+def test_probe_reference_move_rescales_stored_terms():
+    inp = _reference_move_inputs()
+    sm = fp32_scale(128)
+    z = O.to_f64(inp.q_probe, "bf16")[0].reshape(-1, 128) @ O.to_f64(inp.k, "bf16")[0, 0].T * sm / math.log(2)
+    ref0 = np.ceil(z[:, 256:288].max(axis=1))                     # each row's reference after keys 256..287
+    assert np.all(z[:, 300:308].max(axis=1) - ref0 > 100)         # every row's reference moves
+    assert np.all(z[:, 256:288].min(axis=1) - np.ceil(z[:, 300:308].max(axis=1)) > -126)  # rescaled terms stay normal
+    assert np.all(z.max(axis=1) - z.min(axis=1) < 120)           # no term below fp32's normal range anywhere
+    c_or = O.probe_column_scores(O.to_f64(inp.q_probe, "bf16")[0], O.to_f64(inp.k[0, 0:1], "bf16"), 1500, sm)[0]
+    assert c_or.min() > 1e-36                                     # normal fp32 scores, all checked relatively
+    check_probe(inp, 128, (5, 100))
