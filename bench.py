@@ -537,9 +537,9 @@ def decode_workloads(args):
     consecutive appends, the ragged 70B-like 64K."""
     import kv_cache_amd as hq
     return {
-        "c1_decode_4k_1head": _decode_workload(hq, "c1_decode_4k_1head", 200, 20, cold_mib=512),
-        "c3_decode_8b_128k_append": _decode_workload(hq, "c3_decode_8b_128k_append", 64, 0),
-        "c5_decode_70b_ragged_64k": _decode_workload(hq, "c5_decode_70b_ragged_64k", max(20, args.steps), 5),
+        "decode_4k_1head": _decode_workload(hq, "decode_4k_1head", 200, 20, cold_mib=512),
+        "decode_8b_128k_append": _decode_workload(hq, "decode_8b_128k_append", 64, 0),
+        "decode_70b_ragged_64k": _decode_workload(hq, "decode_70b_ragged_64k", max(20, args.steps), 5),
     }
 
 
@@ -577,7 +577,7 @@ def decode_ablation(args):
 
     rows = []
     for T in (1024, 4096, 16384, 32768):
-        spec = dataclasses.replace(CONFIGS["c2_decode_8b_32k"], name=f"decode_8b_gqa_b16_{T}", T=T)
+        spec = dataclasses.replace(CONFIGS["decode_8b_32k"], name=f"decode_8b_gqa_b16_{T}", T=T)
         inp = make_decode_inputs(spec)
         _, _, qn = make_append_tokens(spec, inp.outlier_channels, 1)
         k, v = _dev16(inp.k, "bf16", dev), _dev16(inp.v, "bf16", dev)
@@ -653,7 +653,7 @@ def sweep(args):
     pol_bf16 = hq.Policy(100, 100, pol.window, pol.probe_rows)
     rows = []
     for T in (1024, 2048, 4096, 8192, 16384, 32768):
-        spec = dataclasses.replace(CONFIGS["c2_decode_8b_32k"], name=f"decode_8b_gqa_b16_{T}", T=T)
+        spec = dataclasses.replace(CONFIGS["decode_8b_32k"], name=f"decode_8b_gqa_b16_{T}", T=T)
         inp = make_decode_inputs(spec)
         kn, vn, qn = make_append_tokens(spec, inp.outlier_channels, 1)
         k, v = _dev16(inp.k, "bf16", dev), _dev16(inp.v, "bf16", dev)
@@ -701,7 +701,7 @@ def sweep(args):
         del cache, k, v, inp
         torch.cuda.empty_cache()
     # prefill at 16K: hybrid against every column selected
-    pspec = CONFIGS["c4_prefill_8b_16k"]
+    pspec = CONFIGS["prefill_8b_16k"]
     pin = make_prefill_inputs(pspec)
     pq, pk, pv = _dev16(pin.q, "bf16", dev), _dev16(pin.k, "bf16", dev), _dev16(pin.v, "bf16", dev)
     plens = torch.full((1,), pspec.T, dtype=torch.int32, device=dev)
@@ -737,7 +737,7 @@ def prefill_only(args):
     import kv_cache_amd as hq
     from synth.inputs import CONFIGS, make_prefill_inputs
     dev = "cuda:0"
-    pspec = CONFIGS["c4_prefill_8b_16k"]
+    pspec = CONFIGS["prefill_8b_16k"]
     pin = make_prefill_inputs(pspec)
     q, k, v = (_dev16(x, "bf16", dev) for x in (pin.q, pin.k, pin.v))
     lens = torch.full((1,), pspec.T, dtype=torch.int32, device=dev)
@@ -792,7 +792,7 @@ def main():
     if args.configs:
         return decode_configs(args)
     t_gen = time.perf_counter()
-    spec = CONFIGS["c2_decode_8b_32k"]
+    spec = CONFIGS["decode_8b_32k"]
     inp = make_decode_inputs(spec)
     kn, vn, qn = make_append_tokens(spec, inp.outlier_channels, N_DECODE)
     print(f"# generated decode inputs in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
@@ -807,7 +807,7 @@ def main():
 
     pf = None
     if not args.no_prefill and not args.decode_only:
-        pspec = CONFIGS["c4_prefill_8b_16k"]
+        pspec = CONFIGS["prefill_8b_16k"]
         pin = make_prefill_inputs(pspec)
         pf = dict(spec=pspec, q=_dev16(pin.q, "bf16", dev), k=_dev16(pin.k, "bf16", dev),
                   v=_dev16(pin.v, "bf16", dev), lens=torch.full((1,), pspec.T, dtype=torch.int32, device=dev))

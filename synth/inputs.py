@@ -115,20 +115,20 @@ class PrefillSpec:
 # (headline), 8B GQA 128K decode with appends, the 16K causal prefill, and
 # the ragged 70B-like decode.
 CONFIGS = {
-    "c1_decode_4k_1head": DecodeSpec(
-        name="c1_decode_4k_1head", B=1, Hq=1, Hkv=1, T=4096, dtype="f16",
+    "decode_4k_1head": DecodeSpec(
+        name="decode_4k_1head", B=1, Hq=1, Hkv=1, T=4096, dtype="f16",
         plant_count=21, seed=20260911 + 1),
-    "c2_decode_8b_32k": DecodeSpec(
-        name="c2_decode_8b_32k", B=16, Hq=32, Hkv=8, T=32768,
+    "decode_8b_32k": DecodeSpec(
+        name="decode_8b_32k", B=16, Hq=32, Hkv=8, T=32768,
         plant_frac=0.005, seed=20260911 + 2),
-    "c3_decode_8b_128k_append": DecodeSpec(
-        name="c3_decode_8b_128k_append", B=4, Hq=32, Hkv=8, T=131072,
+    "decode_8b_128k_append": DecodeSpec(
+        name="decode_8b_128k_append", B=4, Hq=32, Hkv=8, T=131072,
         plant_frac=0.005, append_steps=64, seed=20260911 + 3),
-    "c4_prefill_8b_16k": PrefillSpec(
-        name="c4_prefill_8b_16k", B=1, Hq=32, Hkv=8, T=16384,
+    "prefill_8b_16k": PrefillSpec(
+        name="prefill_8b_16k", B=1, Hq=32, Hkv=8, T=16384,
         plant_frac=0.005, seed=20260911 + 4),
-    "c5_decode_70b_ragged_64k": DecodeSpec(
-        name="c5_decode_70b_ragged_64k", B=8, Hq=64, Hkv=8, T=65536,
+    "decode_70b_ragged_64k": DecodeSpec(
+        name="decode_70b_ragged_64k", B=8, Hq=64, Hkv=8, T=65536,
         n_outlier=8, outlier_scale=30.0, plant_frac=0.01, ragged_min=16384,
         seed=20260911 + 5),
 }

@@ -242,7 +242,7 @@ def test_decode_c1_full_size():
     """The 1-head 4K fp16 workload end to end (oracle selection)."""
     import torch
     import kv_cache_amd as hq
-    inp = make_decode_inputs(CONFIGS["c1_decode_4k_1head"])
+    inp = make_decode_inputs(CONFIGS["decode_4k_1head"])
     sp = inp.spec
     cache, scores, sels = _run_quantize(inp, 128, (5, 100))
     ocaches = oracle_caches(inp, sels, scores, 128)
@@ -251,7 +251,7 @@ def test_decode_c1_full_size():
     out = hq.decode_attn(cache, to_dev(inp.q, "f16")).cpu().numpy()
     torch.cuda.synchronize()
     ref = O.decode_batch(O.to_f64(inp.q, "f16"), ocaches, fp32_scale(128))
-    assert_attn_close(out, ref, "decode c1")
+    assert_attn_close(out, ref, "decode 4K one head")
 
 
 @pytest.mark.parametrize("dtype,W,steps", [("bf16", 128, 150), ("f16", 128, 70), ("bf16", 0, 40), ("bf16", 192, 90)])

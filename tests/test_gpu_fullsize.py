@@ -71,7 +71,7 @@ def _check_codes(gcache, oc, bg):
     assert np.array_equal(np.sort(gcache["keep_pos"][bg, :len(kpos)]), kpos)
 
 
-@pytest.mark.parametrize("name", ["c2_decode_8b_32k", "c5_decode_70b_ragged_64k"])
+@pytest.mark.parametrize("name", ["decode_8b_32k", "decode_70b_ragged_64k"])
 def test_decode_path_full_size(name):
     """Every (b, g) of the workload: scores, selection, codes, attention."""
     import torch
@@ -115,8 +115,8 @@ def test_decode_with_appends_128k():
     scores and selection against the oracle's re-probe."""
     import torch
     import kv_cache_amd as hq
-    spec = CONFIGS["c3_decode_8b_128k_append"]
-    print("generating c3", flush=True)
+    spec = CONFIGS["decode_8b_128k_append"]
+    print("generating the 128K workload", flush=True)
     inp = make_decode_inputs(spec)
     cache, gsel = _pipeline(spec, inp, cap_extra=64)
     steps = 64
@@ -157,7 +157,7 @@ def test_decode_with_appends_128k():
                 oc = O.append_tokens(oc, O.to_f64(kn[done:s, b, g], "bf16"), O.to_f64(vn[done:s, b, g], "bf16"))
                 done = s
                 ref = O.decode_attention(O.to_f64(qn[s - 1, b, qsl], "bf16"), oc, sm)
-                assert_attn_close(outs[s - 1][b, qsl], ref, f"c3 step {s} (b={b}, g={g})")
+                assert_attn_close(outs[s - 1][b, qsl], ref, f"128K step {s} (b={b}, g={g})")
             assert done == steps
             _check_codes(gc, oc, b * spec.Hkv + g)
             cnts = gc["counts"][b, g]
@@ -181,6 +181,6 @@ def test_decode_with_appends_128k():
                 print(f"  re-probe (b={b}, g={g}): score rel err {rel:.2e}, persistence {rpers[b, g]}/{k}",
                       flush=True)
         print(f"  b={b}: {spec.Hkv} pairs checked ({time.time() - t0:.0f} s)", flush=True)
-    print(f"c3: near-tie selection flips {flips}; departures kept by the append rule per (b, g): "
+    print(f"128K: near-tie selection flips {flips}; departures kept by the append rule per (b, g): "
           f"min {min(kept_added)} max {max(kept_added)}; re-probe persistence min {min(persist):.3f} "
           f"mean {np.mean(persist):.3f}", flush=True)

@@ -295,7 +295,7 @@ def test_prefill_16k_full_size(fp8, tile):
     import time
     import torch
     import kv_cache_amd as hq
-    spec = CONFIGS["c4_prefill_8b_16k"]
+    spec = CONFIGS["prefill_8b_16k"]
     inp = make_prefill_inputs(spec)
     T, G = spec.T, spec.Hq // spec.Hkv
     pol = hq.Policy(low_fmt=hq.HQ_LOW_FP8 if fp8 else hq.HQ_LOW_INT8, tile_num=tile)
