@@ -66,6 +66,7 @@ constexpr int kTilesPerWg = 8;     // row tiles (waves) per workgroup at most
 constexpr int kPlanes = 4;         // base-256 digits per value
 constexpr int kDS = kD + 16;       // LDS bytes per key in a digit plane (pad: no bank conflicts)
 constexpr int kColCols = 1024;     // columns per pass-2 workgroup (256 threads x 4)
+constexpr int kTopkLds = 34816;    // candidates the top-k stages in LDS (136 KiB + padding)
 constexpr int kMoveGap = 100;      // a row's reference moves when a logit exceeds it by more than this (log2
                                    // units), so every stored term 2^(z - ref) is at most 2^100 (fp32 range)
 constexpr double kLogitBudget = 1.0e-7;  // largest logit error accepted from the digit path (log2 units)
@@ -674,6 +675,10 @@ __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t&
 __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, const int32_t* seq_lens, int Hkv,
                                                      int Tmax, hq_policy pol, int stride, int32_t* sel_idx,
                                                      int32_t* sel_count, hq_thresh* thresh) {
+    // the candidates' score bits, staged once when they fit (one padding
+    // word per 32, so the compaction's per-thread runs fall in different
+    // banks); longer contexts read them from global memory in every pass
+    __shared__ uint32_t sx[kTopkLds + kTopkLds / 32];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t wsum[16];
     __shared__ uint32_t sh_prefix, sh_mask, sh_remaining;
@@ -694,6 +699,10 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
         }
         return;
     }
+    const bool staged = ncand <= kTopkLds;  // uniform
+    if (staged)
+        for (int j = tid; j < ncand; j += 1024) sx[j + (j >> 5)] = xs[j];
+    auto rd = [&](int j) { return staged ? sx[j + (j >> 5)] : xs[j]; };
     if (tid == 0) {
         sh_prefix = 0;
         sh_mask = 0;
@@ -707,9 +716,12 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
         for (int i = tid; i < 256; i += 1024) hist[i] = 0;
         __syncthreads();
         const uint32_t prefix = sh_prefix, mask = sh_mask;
-        for (int j = tid; j < ncand; j += 1024) {
-            const uint32_t x = xs[j];
-            if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+        for (int base = 0; base < ncand; base += 1024) {
+            const int j = base + tid;
+            const uint32_t x = j < ncand ? rd(j) : 0u;
+            // (a wave-level add of the lanes sharing a bin, against the
+            // contention of the top byte's few bins, measured slower)
+            if (j < ncand && (x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
         }
         __syncthreads();
         if (tid < 64) {
@@ -751,7 +763,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
     const int j0 = min(tid * per, ncand), j1 = min(j0 + per, ncand);
     uint32_t ngt = 0, neq = 0;
     for (int j = j0; j < j1; ++j) {
-        const uint32_t x = xs[j];
+        const uint32_t x = rd(j);
         ngt += x > tau ? 1u : 0u;
         neq += x == tau ? 1u : 0u;
     }
@@ -761,7 +773,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
     uint32_t pos = block_excl_scan(ngt + take_eq, wsum, tot);
     uint32_t te = 0;
     for (int j = j0; j < j1; ++j) {
-        const uint32_t x = xs[j];
+        const uint32_t x = rd(j);
         if (x > tau) {
             sel[pos++] = j;
         } else if (x == tau && te < take_eq) {
