@@ -139,3 +139,19 @@ def test_probe_reference_move_rescales_stored_terms():
     c_or = O.probe_column_scores(O.to_f64(inp.q_probe, "bf16")[0], O.to_f64(inp.k[0, 0:1], "bf16"), 1500, sm)[0]
     assert c_or.min() > 1e-36                                     # normal fp32 scores, all checked relatively
     check_probe(inp, 128, (5, 100))
+
+
+def test_probe_at_the_16k_prefill_shape():
+    """The 16K prefill's probe (B=1, 32 query / 8 KV heads, its last 64 rows):
+    the only workload whose pass 1 runs on 512-key chunks (two per pass-2
+    block). Every (b, g) against the oracle."""
+    import types
+    from synth.inputs import CONFIGS, make_prefill_inputs
+    pin = make_prefill_inputs(CONFIGS["prefill_8b_16k"])
+    sp = pin.spec
+    inp = types.SimpleNamespace(
+        spec=types.SimpleNamespace(B=sp.B, Hq=sp.Hq, Hkv=sp.Hkv, D=sp.D, dtype=sp.dtype, probe_rows=sp.probe_rows),
+        q_probe=np.ascontiguousarray(pin.q[:, :, sp.T - sp.probe_rows:]), k=pin.k,
+        seq_lens=np.full(sp.B, sp.T, dtype=np.int32))
+    flips = check_probe(inp, 128, (5, 100))
+    print(f"16K prefill probe: near-tie flips {flips}", flush=True)
