@@ -612,8 +612,8 @@ __global__ __launch_bounds__(256) void k_probe_colsum(ProbeParams p) {
     const int bg = b * p.Hkv + g;
     const int T = p.seq_lens[b];
     const int j0 = blockIdx.x * kColCols;
-    const int c0 = j0 / p.chunk;  // chunks are 256, 512 or 1,024 keys
-    const int ncb = min(kColCols / p.chunk, p.nchunk - c0);
+    const int c0 = j0 / p.chunk;  // chunks are 256 .. 4,096 keys: a block spans 1, 2 or 4 of them, or lies in one
+    const int ncb = min(max(kColCols / p.chunk, 1), p.nchunk - c0);
     for (int idx = threadIdx.x; idx < ncb * p.NR; idx += 256) {
         const int cc = idx / p.NR, row = idx - cc * p.NR;
         const double2 pr = p.part[((size_t)bg * p.nchunk + c0 + cc) * p.NRp + row];
@@ -798,11 +798,13 @@ inline size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 struct ProbeShape {
     int NR, NRp, nrt, ngroups, waves, chunk, nchunk;
 };
-// Keys per pass-1 workgroup: 1,024, halved (down to 256) while the grid
+// Keys per pass-1 workgroup: 4,096, halved (down to 256) while the grid
 // would have fewer than 256 workgroups. A pass-1 workgroup holds 109 KiB of
-// LDS, so one runs per CU: 256 is one round of the chip's 256 CUs, and
-// smaller chunks would only add rounds and per-workgroup query conversions
-// (16K prefill probe: 512-key chunks 102 us, 256-key chunks 123 us).
+// LDS, so one runs per CU: 256 is one round of the chip's 256 CUs. Longer
+// chunks convert each query tile to digits fewer times (32K decode shape,
+// pass 1: 2.83 / 2.69 / 2.65 ms with 1,024 / 2,048 / 4,096 keys), and
+// chunks that leave CUs idle or add rounds cost more (16K prefill probe:
+// 512-key chunks 102 us, 256 123 us, 1,024 164 us).
 ProbeShape probe_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const hq_policy& pol) {
     ProbeShape s;
     s.NR = (Hq / Hkv) * pol.probe_rows;
@@ -810,7 +812,7 @@ ProbeShape probe_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, const h
     s.nrt = s.NRp / kRT;
     s.ngroups = (s.nrt + kTilesPerWg - 1) / kTilesPerWg;
     s.waves = s.nrt < kTilesPerWg ? s.nrt : kTilesPerWg;
-    s.chunk = 1024;
+    s.chunk = 4096;
     while (s.chunk > 256 && (int64_t)((Tmax + s.chunk - 1) / s.chunk) * Hkv * s.ngroups * B < 256) s.chunk /= 2;
     s.nchunk = (Tmax + s.chunk - 1) / s.chunk;
     return s;
