@@ -32,6 +32,20 @@ extern "C" {
 hq_status hq_diag_read_int4(const hq_cache* cache, void* sink, size_t sink_bytes, void* stream);
 size_t hq_diag_read_int4_sink_bytes(const hq_cache* cache);
 
+/* hq_diag_exp2_error -- accuracy of the hardware base-2 exponential
+ * (v_exp_f32) that the probe's first pass takes 2^f with, |f| <= 1/2 (the
+ * probe's score bound in hq_probe_select's kernel source counts its largest
+ * relative error there). Evaluates it on every fp32 value x in [lo, hi] and
+ * compares with the fp64 exponential 2^x: out[i], i < out_count, receives the
+ * largest |v_exp_f32(x) - 2^x| / 2^x seen by workgroup i (the grid has
+ * out_count workgroups, which split the inputs between them); the answer is
+ * the largest of the out_count values.
+ *   lo, hi     finite, -64 <= lo <= hi <= 64 (results stay normal fp32);
+ *   out        device buffer of out_count doubles, out_count in [1, 65536].
+ * Errors: HQ_ERR_INVALID_ARG for a range or count outside these limits or a
+ * null out, with nothing enqueued. */
+hq_status hq_diag_exp2_error(float lo, float hi, double* out, size_t out_count, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ EXPORTED = (
     "hq_probe_select", "hq_probe_ws_bytes", "hq_quantize_kv", "hq_append_kv", "hq_decode_attn",
     "hq_decode_ws_bytes", "hq_decode_attn_noalloc", "hq_prefill_attn", "hq_prefill_ws_bytes", "hq_cache_layout", "hq_sel_stride",
     "hq_last_error", "hq_diag_read_int4", "hq_diag_read_int4_sink_bytes", "hq_reprobe", "hq_reprobe_ws_bytes",
-    "hq_cache_layout_ragged",
+    "hq_cache_layout_ragged", "hq_diag_exp2_error",
 )
 
 
@@ -85,6 +85,7 @@ def _load():
         "hq_last_error": (ctypes.c_char_p, []),
         "hq_diag_read_int4": (I, [ctypes.POINTER(hq_cache), P, S, V]),
         "hq_diag_read_int4_sink_bytes": (S, [ctypes.POINTER(hq_cache)]),
+        "hq_diag_exp2_error": (I, [F, F, P, S, V]),
         "hq_reprobe": (I, [ctypes.POINTER(hq_cache), P, I, pol, F, P, P, P, P, P, P, S, V]),
         "hq_reprobe_ws_bytes": (S, [ctypes.POINTER(hq_cache), I, pol]),
     }
@@ -329,6 +330,15 @@ def diag_read_int4(cache: HybridCache, sink=None):
         sink = torch.empty(max(n, 256), dtype=torch.uint8, device=cache.device)
     _check(lib.hq_diag_read_int4(cache.ptr(), _ptr(sink), sink.numel(), _stream()))
     return sink
+
+
+def diag_exp2_error(lo: float = -0.5, hi: float = 0.5, nblocks: int = 4096) -> float:
+    """hq_diag_exp2_error (measurement helper): the largest relative error of
+    the hardware base-2 exponential over every fp32 input in [lo, hi]."""
+    torch = _torch()
+    out = torch.zeros(nblocks, dtype=torch.float64, device="cuda")
+    _check(lib.hq_diag_exp2_error(lo, hi, _ptr(out), nblocks, _stream()))
+    return float(out.max().item())
 
 
 def prefill_attn(q, k, v, sel_idx, sel_count, policy: Policy = Policy(), sm_scale: float | None = None,

@@ -471,4 +471,22 @@ hq_status hq_diag_read_int4(const hq_cache* cache, void* sink, size_t sink_bytes
     return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
 }
 
+hq_status hq_diag_exp2_error(float lo, float hi, double* out, size_t out_count, void* stream) {
+    static const char* fn = "hq_diag_exp2_error";
+    clear_err();
+    if (!(lo >= -64.0f && hi <= 64.0f && lo <= hi))
+        return fail(HQ_ERR_INVALID_ARG, "%s: need -64 <= lo <= hi <= 64 (finite)", fn);
+    if (out_count < 1 || out_count > 65536)
+        return fail(HQ_ERR_INVALID_ARG, "%s: out_count must be in [1, 65536]", fn);
+    REQ_PTR(out);
+    auto key = [](float x) -> int64_t {
+        uint32_t b;
+        memcpy(&b, &x, 4);
+        return (b & 0x80000000u) ? -(int64_t)(b & 0x7FFFFFFFu) : (int64_t)b;
+    };
+    const int64_t k0 = key(lo), n = key(hi) - k0 + 1;
+    hipError_t e = hq::launch_diag_exp2_error((int32_t)k0, n, out, (int)out_count, (hipStream_t)stream);
+    return e == hipSuccess ? HQ_OK : hip_fail(fn, e);
+}
+
 }  // extern "C"

@@ -68,7 +68,35 @@ __global__ __launch_bounds__(256, 2) void k_diag_read_int4(const hq_cache c, uin
     sink[(((size_t)bg * nsq + s) * 4 + wave) * 64 + lane] = x;
 }
 
+// Largest relative error of the hardware base-2 exponential (v_exp_f32, the
+// instruction the probe's pass 1 takes 2^f with) against the fp64 exponential
+// over the fp32 inputs with order keys k0 .. k0 + n - 1 (the key of x is its
+// bit pattern for x >= 0, minus the pattern of |x| for x < 0, so consecutive
+// keys are consecutive fp32 values). One result per workgroup.
+__global__ __launch_bounds__(256) void k_diag_exp2_error(int32_t k0, int64_t n, double* out) {
+    __shared__ double red[4];
+    double mx = 0.0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int32_t key = k0 + (int32_t)i;
+        const uint32_t bits = key >= 0 ? (uint32_t)key : ((uint32_t)(-(int64_t)key) | 0x80000000u);
+        const float x = __uint_as_float(bits);
+        const double ref = exp2((double)x);
+        const double e = (double)__builtin_amdgcn_exp2f(x);
+        mx = fmax(mx, fabs(e - ref) / ref);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+}
+
 }  // namespace
+
+hipError_t launch_diag_exp2_error(int32_t k0, int64_t n, double* out, int nblocks, hipStream_t s) {
+    k_diag_exp2_error<<<nblocks, 256, 0, s>>>(k0, n, out);
+    return hipGetLastError();
+}
 
 size_t diag_sink_bytes(const hq_cache& c, int32_t tps) {
     return (size_t)c.B * c.Hkv * decode_nsq(c, tps) * 4 * 64 * sizeof(uint32_t);

@@ -190,6 +190,7 @@ int32_t decode_nsq(const hq_cache& c, int32_t tps);  // INT4 splits of a (b, g)
 // (measurement helper, not a step of the method).
 size_t diag_sink_bytes(const hq_cache& c, int32_t tps);
 hipError_t launch_diag_read_int4(const hq_cache& c, void* sink, int32_t tps, hipStream_t s);
+hipError_t launch_diag_exp2_error(int32_t k0, int64_t n, double* out, int nblocks, hipStream_t s);
 
 // Shapes the probe kernels support: G query heads per KV head times
 // probe_rows rows. probe_shape_rule() states the rule for error messages.

@@ -35,16 +35,22 @@
 // On the workloads this bound is ~1e-8 in log2 units; a tile whose bound
 // exceeds kLogitBudget has its logits recomputed from the 16-bit inputs in
 // fp64 (exact products, fp64 sums), so every logit carries at most the
-// budget's error. Exponentials are fp64 (a degree-7 series on [-1/2, 1/2]
-// after an exact power-of-two split, relative error < 1.1e-8); every
+// budget's error. Each term 2^(z - m) is split exactly in fp64 into 2^n 2^f
+// (n = rint(z - m), |f| <= 1/2); f is rounded to fp32 (error <= 2^-26) and
+// 2^f taken by the hardware base-2 exponential (v_exp_f32, relative error at
+// most 1.5 2^-24 on [-1/2, 1/2]: checked over every fp32 input there with
+// hq_diag_exp2_error, which finds 1.395 2^-24), then scaled by 2^n exactly; that fp32 value is
+// both the stored term and what the row's normaliser adds, in fp64. Every
 // normaliser and column sum accumulates in fp64 relative to integer
 // references, so rescaling by a power of two is exact. Scores are rounded
 // once to fp32. Resulting bound on each returned score, for the softmax with
-// the fp32 scale the caller passes: relative error < 2 ln2 kLogitBudget +
-// 2 x 1.1e-8 (the series in both passes) + 2^-24 < 2.9e-7, so two columns can
-// change order only where their exact scores differ by less than 5.8e-7
-// relative. (With the certificate at ~1e-8 the scores come out within a few
-// 1e-8: the fp32 rounding dominates.)
+// the fp32 scale the caller passes: a term is off by at most
+// d = ln2 (kLogitBudget + 2^-26) + 1.5 2^-24 relative, a row's normaliser by at
+// most d too (a sum of such terms), so a score (a sum of term / normaliser)
+// by at most 2 d + 2^-24 < 3.3e-7, and two columns can change order only
+// where their exact scores differ by less than 6.6e-7 relative. (The fp64
+// roundings of the logit and the split, < 1e-12 in log2 units, are far
+// below these terms.)
 //
 // Top-k: one workgroup per (b, g); 4-pass 8-bit radix select on the fp32 bit
 // patterns (scores are >= 0, so bit order = value order) with LDS histograms
@@ -69,8 +75,7 @@ constexpr int kColCols = 1024;     // columns per pass-2 workgroup (256 threads 
 constexpr int kTopkLds = 34816;    // candidates the top-k stages in LDS (136 KiB + padding)
 constexpr int kMoveGap = 100;      // a row's reference moves when a logit exceeds it by more than this (log2
                                    // units), so every stored term 2^(z - ref) is at most 2^100 (fp32 range)
-constexpr double kLogitBudget = 1.0e-7;  // largest logit error accepted from the digit path (log2 units)
-constexpr int kExpTerms = 7;       // 2^f = sum_{n <= 7} (f ln2)^n / n!, |f| <= 1/2: relative error < 1.1e-8
+constexpr double kLogitBudget = 0.5e-7;  // largest logit error accepted from the digit path (log2 units)
 
 struct ProbeParams {
     const uint16_t* q;     // [B][Hq][R][D]
@@ -83,7 +88,6 @@ struct ProbeParams {
     float* col_scores;     // [B][Hkv][Tmax]
     int32_t B, Hq, Hkv, Tmax, Tp, R, G, NR, NRp, ngroups, nchunk, chunk;
     double sc2;            // sm_scale * log2(e)
-    double ec[kExpTerms + 1];  // (ln2)^n / n!, n = 0..7
 };
 
 // Row `row` of the (b, g) probe rows: head g*G + row / R, probe row row % R,
@@ -163,15 +167,13 @@ __device__ inline int min32(int v) {
     return min((int)r[0], (int)r[1]);
 }
 
-// 2^y in fp64 for y <= 1023: 2^n * 2^f, n = rint(y), |f| <= 1/2, series with
-// the coefficients (ln2)^k / k! passed in (uniform values in scalar registers).
-__device__ inline double exp2_d(double y, const double (&c)[kExpTerms + 1]) {
+// One term 2^y (fp32): y = n + f split exactly in fp64 (n = rint(y),
+// |f| <= 1/2), f rounded to fp32, 2^f by the hardware exponential, then the
+// exact power-of-two scaling (0 below the fp32 range, inf above; such terms
+// occur only for elements outside the map, whose term is dropped).
+__device__ inline float exp2_term(double y) {
     const double n = __builtin_rint(y);
-    const double f = y - n;  // exact
-    double e = c[kExpTerms];
-#pragma unroll
-    for (int i = kExpTerms - 1; i >= 0; --i) e = __builtin_fma(e, f, c[i]);
-    return __builtin_ldexp(e, (int)n);  // underflows to 0 for very negative y
+    return __builtin_ldexpf(__builtin_amdgcn_exp2f((float)(y - n)), (int)n);
 }
 
 // Per-key data of the key tile in LDS.
@@ -445,9 +447,9 @@ constexpr double kZeros[16] = {};
 // the element loops need no mask.
 __device__ inline bool tile_full(uint32_t mk) { return __builtin_amdgcn_ballot_w64(mk != 0xFFFFu) == 0; }
 
-// One stored term of pass 1 (fp32, rounded to nearest), streamed past the caches.
-__device__ inline void store_term(const __amdgpu_buffer_rsrc_t& r, int voff, int soff, double e) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((float)e), r, voff, soff, kLoadNT);
+// One stored term of pass 1, streamed past the caches.
+__device__ inline void store_term(const __amdgpu_buffer_rsrc_t& r, int voff, int soff, float e) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), r, voff, soff, kLoadNT);
 }
 
 // Pass 1: per (key chunk, row group, g, b): for every probe row of the group,
@@ -539,16 +541,16 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
             if (tile_full(mk)) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const double e = exp2_d(z[i] - (double)m[i], p.ec);
-                    l[i] += e;
+                    const float e = exp2_term(z[i] - (double)m[i]);
+                    l[i] += (double)e;
                     store_term(emr, evoff, ((8 * (i >> 2) + (i & 3)) * p.Tp + key0 - key_lo) * 4, e);
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const double e = exp2_d(z[i] - (double)m[i], p.ec);
-                    const double ev = ((mk >> i) & 1u) ? e : 0.0;
-                    l[i] += ev;
+                    const float e = exp2_term(z[i] - (double)m[i]);
+                    const float ev = ((mk >> i) & 1u) ? e : 0.f;
+                    l[i] += (double)ev;
                     store_term(emr, evoff, ((8 * (i >> 2) + (i & 3)) * p.Tp + key0 - key_lo) * 4, ev);
                 }
             }
@@ -871,15 +873,6 @@ hipError_t launch_probe(const void* q_probe, const void* k, const int32_t* seq_l
     p.nchunk = sh.nchunk;
     p.chunk = sh.chunk;
     p.sc2 = (double)sm_scale * 1.4426950408889634074;
-    {
-        // (ln 2)^n / n!
-        const double ln2 = 0.69314718055994530942;
-        double c = 1.0;
-        for (int n = 0; n <= kExpTerms; ++n) {
-            p.ec[n] = c;
-            c = c * ln2 / (n + 1);
-        }
-    }
     const int threads = 64 * kTilesPerWg;  // 8 waves; waves past the last row tile only move key tiles
     dim3 g1(sh.nchunk, Hkv * sh.ngroups, B);
     if (f16) k_probe_rowstats<true><<<g1, threads, 0, s>>>(p);

@@ -141,6 +141,12 @@ int main() {
     // the measurement helper
     EXPECT(hq_diag_read_int4(nullptr, F, 1ull << 40, nullptr) == HQ_ERR_INVALID_ARG);
     EXPECT(hq_diag_read_int4_sink_bytes(nullptr) == 0);
+    double* const D = reinterpret_cast<double*>(0x100000);
+    EXPECT(hq_diag_exp2_error(0.5f, -0.5f, D, 16, nullptr) == HQ_ERR_INVALID_ARG);
+    EXPECT(hq_diag_exp2_error(-65.f, 0.f, D, 16, nullptr) == HQ_ERR_INVALID_ARG);
+    EXPECT(hq_diag_exp2_error(-0.5f, 0.5f, D, 0, nullptr) == HQ_ERR_INVALID_ARG);
+    EXPECT(hq_diag_exp2_error(-0.5f, 0.5f, D, 65537, nullptr) == HQ_ERR_INVALID_ARG);
+    EXPECT(hq_diag_exp2_error(-0.5f, 0.5f, nullptr, 16, nullptr) == HQ_ERR_INVALID_ARG);
 
     if (failures) return 1;
     std::printf("host checks passed\n");

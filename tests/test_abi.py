@@ -223,6 +223,21 @@ def test_decode_noalloc_validation(hq):
         hq.HQ_ERR_INVALID_ARG
 
 
+def test_diag_exp2_error_validation(hq):
+    """hq_diag_exp2_error rejects an empty or out-of-limit range, a NaN bound,
+    a bad workgroup count and a null output on the host."""
+    d = FAKE
+    f = hq.lib.hq_diag_exp2_error
+    assert f(0.5, -0.5, d, 16, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(-65.0, 0.0, d, 16, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(0.0, 64.5, d, 16, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(float("nan"), 0.5, d, 16, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(-0.5, 0.5, d, 0, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(-0.5, 0.5, d, 65537, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(-0.5, 0.5, None, 16, None) == hq.HQ_ERR_INVALID_ARG
+    assert "hq_diag_exp2_error" in hq.lib.hq_last_error().decode()
+
+
 def test_reprobe_validation(hq):
     """hq_reprobe checks the cache, the policy against it, the probe's shape
     rule, the workspace and its alignment before anything is launched."""

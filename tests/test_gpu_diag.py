@@ -34,3 +34,17 @@ def test_diag_read_int4_reads_the_int4_store(kw):
             want ^= np.bitwise_xor.reduce(buf[bg, : nqt * per_tile].view(np.uint32))
     assert got == want
     assert cache.err_flag() == 0
+
+
+def test_hw_exp2_error_within_the_probe_bound():
+    """The probe's first pass takes 2^f, |f| <= 1/2, with the hardware base-2
+    exponential; its score bound counts that instruction's relative error as
+    at most 1.5 2^-24 there. Checked over every fp32 input in [-1/2, 1/2]
+    (2.1e9 values) against the fp64 exponential."""
+    import kv_cache_amd as hq
+    from gpu_common import HW_EXP2_REL
+    err = hq.diag_exp2_error(-0.5, 0.5)
+    print(f"hardware exp2 on [-1/2, 1/2]: largest relative error {err:.4e} ({err / 2.0 ** -24:.3f} x 2^-24)")
+    assert 0.0 < err <= HW_EXP2_REL
+    # a one-point range still reports that point's error (2^0 is exact)
+    assert hq.diag_exp2_error(0.0, 0.0, nblocks=4) == 0.0
