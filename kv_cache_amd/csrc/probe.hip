@@ -49,8 +49,8 @@
 // most d too (a sum of such terms), so a score (a sum of term / normaliser)
 // by at most 2 d + 2^-24 < 3.3e-7, and two columns can change order only
 // where their exact scores differ by less than 6.6e-7 relative. (The fp64
-// roundings of the logit and the split, < 1e-12 in log2 units, are far
-// below these terms.)
+// roundings of the logit, of z - m and of the split, each below 2^-33 in log2
+// units for logits below 2^19 in magnitude, are far below these terms.)
 //
 // Top-k: one workgroup per (b, g); 4-pass 8-bit radix select on the fp32 bit
 // patterns (scores are >= 0, so bit order = value order) with LDS histograms
@@ -73,6 +73,8 @@ constexpr int kPlanes = 4;         // base-256 digits per value
 constexpr int kDS = kD + 16;       // LDS bytes per key in a digit plane (pad: no bank conflicts)
 constexpr int kColCols = 1024;     // columns per pass-2 workgroup (256 threads x 4)
 constexpr int kTopkLds = 34816;    // candidates the top-k stages in LDS (136 KiB + padding)
+constexpr int kUnset = -(1 << 20);  // reference of a row with no valid logit yet in the chunk: y = z + 2^20
+                                     // keeps z to 2^-33 and moves at the first valid logit above -2^20 + 100
 constexpr int kMoveGap = 100;      // a row's reference moves when a logit exceeds it by more than this (log2
                                    // units), so every stored term 2^(z - ref) is at most 2^100 (fp32 range)
 constexpr double kLogitBudget = 0.5e-7;  // largest logit error accepted from the digit path (log2 units)
@@ -129,9 +131,8 @@ __device__ inline uint32_t gather_byte(uint32_t z0, uint32_t z1, uint32_t z2, ui
 }
 __device__ inline int sbyte(uint32_t w, int i) { return (int)(int8_t)(w >> (8 * i)); }
 
-// Reductions over 16- and 32-lane groups without LDS traffic: DPP moves
-// within rows of 16 lanes, then v_permlane16_swap across the two rows of a
-// 32-lane half.
+// Reductions over 16-lane groups (one key's threads) without LDS traffic:
+// DPP moves within rows of 16 lanes.
 template <int CTRL>
 __device__ inline uint32_t dpp_u(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
@@ -150,23 +151,6 @@ __device__ inline float sum16(float v) {
     v += dpp_f<0x141>(v);
     return v + dpp_f<0x140>(v);
 }
-__device__ inline int min16(int v) {
-    v = min(v, (int)dpp_u<0xB1>((uint32_t)v));
-    v = min(v, (int)dpp_u<0x4E>((uint32_t)v));
-    v = min(v, (int)dpp_u<0x141>((uint32_t)v));
-    return min(v, (int)dpp_u<0x140>((uint32_t)v));
-}
-__device__ inline float max32(float v) {
-    v = max16(v);
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline int min32(int v) {
-    v = min16(v);
-    const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-    return min((int)r[0], (int)r[1]);
-}
-
 // One term 2^y (fp32): y = n + f split exactly in fp64 (n = rint(y),
 // |f| <= 1/2), f rounded to fp32, 2^f by the hardware exponential, then the
 // exact power-of-two scaling (0 below the fp32 range, inf above; such terms
@@ -326,7 +310,6 @@ __device__ inline DigitSums tile_digit_sums(const QTile& q, const QPlanes& q23, 
 #pragma unroll
         for (int a = 0; a < kPlanes; ++a) kb[a] = *reinterpret_cast<const intx4*>(&kt.d[a][n][32 * ks + 16 * hf]);
         const intx4 q2 = *reinterpret_cast<const intx4*>(&q23.d[0][n][32 * ks + 16 * hf]);
-        const intx4 q3 = *reinterpret_cast<const intx4*>(&q23.d[1][n][32 * ks + 16 * hf]);
         hi = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[0][ks], kb[1], hi, 0, 0, 0);
         a2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[0][ks], kb[2], a2, 0, 0, 0);
         a3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q.d[0][ks], kb[3], a3, 0, 0, 0);
@@ -337,8 +320,21 @@ __device__ inline DigitSums tile_digit_sums(const QTile& q, const QPlanes& q23, 
         a2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q2, kb[0], a2, 0, 0, 0);
         a3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q2, kb[1], a3, 0, 0, 0);
         a4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q2, kb[2], a4, 0, 0, 0);
-        a3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q3, kb[0], a3, 0, 0, 0);
-        a4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q3, kb[1], a4, 0, 0, 0);
+    }
+    // the pairs (3, 0) and (3, 1) only where the tile's query digit plane 3 is
+    // not all zero (a wave-uniform test; a zero plane contributes exactly 0,
+    // and the int32 sums are exact in any order). Plane 3 holds the bits of
+    // values below 2^-22 of the tile's largest magnitude, so most query
+    // tiles skip these 8 MFMAs.
+    if (__builtin_amdgcn_readfirstlane(q.n3) != 0) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const intx4 q3 = *reinterpret_cast<const intx4*>(&q23.d[1][n][32 * ks + 16 * hf]);
+            a3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q3, *reinterpret_cast<const intx4*>(&kt.d[0][n][32 * ks + 16 * hf]),
+                                                      a3, 0, 0, 0);
+            a4 = __builtin_amdgcn_mfma_i32_32x32x32_i8(q3, *reinterpret_cast<const intx4*>(&kt.d[1][n][32 * ks + 16 * hf]),
+                                                      a4, 0, 0, 0);
+        }
     }
     s.hi = hi;
 #pragma unroll
@@ -347,17 +343,17 @@ __device__ inline DigitSums tile_digit_sums(const QTile& q, const QPlanes& q23, 
     return s;
 }
 
-// Bound (log2 units) on the error of the digit path's logits for this tile
-// pair: rounding residuals times the other operand, and the omitted pairs
-// (2,3), (3,2), (3,3) through the query digit planes' l1 norms.
-__device__ inline double tile_error_bound(const QTile& q, const KeyTile& kt, double asc2) {
+// Bound (log2 units) on the error of the digit path's logits of this lane's
+// key (lane % 32) against every row of the tile: rounding residuals times the
+// other operand, and the omitted pairs (2,3), (3,2), (3,3) through the query
+// digit planes' l1 norms, weighted by the key's own shift.
+__device__ inline double key_error_bound(const QTile& q, const KeyTile& kt, double asc2) {
     const int n = threadIdx.x & 31;
-    const float kmax = max32(kt.kmax[n]), krho = max32(kt.rho[n]);
-    const int shmin = min32(kt.sh[n]);
+    const float kmax = kt.kmax[n], krho = kt.rho[n];
     const double res = (double)q.rho * kmax + ((double)q.qmax + q.rho) * krho;
     // |D_23| <= n2 * 128, |D_32| <= n3 * 128, |D_33| <= n3 * 128 (|d| <= 128),
     // weights 2^(8 - sh), 2^(8 - sh), 2^(-sh)
-    const double om = __builtin_ldexp(128.0 * ((double)q.n2 + (double)q.n3 * (1.0 + 0x1p-8)), 8 - q.sh - shmin);
+    const double om = __builtin_ldexp(128.0 * ((double)q.n2 + (double)q.n3 * (1.0 + 0x1p-8)), 8 - q.sh - kt.sh[n]);
     return (res + om) * asc2 * (1.0 + 0x1p-20);
 }
 
@@ -392,8 +388,9 @@ __device__ inline void tile_logits(const ProbeParams& p, const QTile& q, const Q
                                    int b, int g, const uint16_t* kbase, int key, int key_end, int rt,
                                    const double (&off)[16], double (&z)[16]) {
     const DigitSums s = tile_digit_sums(q, q23, kt);
-    const bool fallback =
-        __builtin_amdgcn_readfirstlane((int)!(tile_error_bound(q, kt, fabs(p.sc2)) <= kLogitBudget)) != 0;
+    // the whole tile takes the fallback when any of its keys' bounds exceeds
+    // the budget (wave-uniform)
+    const bool fallback = __builtin_amdgcn_ballot_w64(!(key_error_bound(q, kt, fabs(p.sc2)) <= kLogitBudget)) != 0;
     if (!fallback) {
         // z - off = F (65536 hi + mid) 256 + (F lo - off), F = 2^(16 - shq - shk) sm_scale log2 e
         const double F = __builtin_ldexp(p.sc2, 16 - q.sh - kt.sh[threadIdx.x & 31]);
@@ -490,13 +487,14 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
     const __amdgpu_buffer_rsrc_t emr = __builtin_amdgcn_make_buffer_rsrc(
         p.emap + ((size_t)bg * p.NRp + rt * kRT) * p.Tp + key_lo, (short)0, kRT * p.Tp * 4 - key_lo * 4, 0x00020000);
     const int evoff = ((lane & 31) + hoff * p.Tp) * 4;
-    int m[16];  // integer references, uniform over the half-wave (INT_MIN: none yet)
+    int m[16];  // integer references, uniform over the half-wave (kUnset: none yet)
     double l[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        m[i] = INT_MIN;
+        m[i] = kUnset;
         l[i] = 0.0;
     }
+
     store_keys<F16>(load_keys(kbase, key_lo, key_hi), sm.kt[0]);
     __syncthreads();
     for (int t = 0; t < ntile; ++t) {
@@ -508,21 +506,31 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
             double z[16];
             tile_logits<F16>(p, q, sm.q23[wave], sm.kt[cur], b, g, kbase, key, key_hi, rt, kZeros, z);
             const uint32_t mk = tile_mask(p, T, rt, rowmk, key0, key_hi);
+            // z becomes y = z - m, the exponent of the term against the row's
+            // reference (for a row without one, m = kUnset: y > kMoveGap)
+            const bool full = tile_full(mk);
             bool move = false;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) move |= ((mk >> i) & 1u) && z[i] > (double)m[i] + kMoveGap;
+            for (int i = 0; i < 16; ++i) z[i] -= (double)m[i];
+            if (full) {  // wave-uniform: every element is in the map
+#pragma unroll
+                for (int i = 0; i < 16; ++i) move |= z[i] > (double)kMoveGap;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) move |= ((mk >> i) & 1u) && z[i] > (double)kMoveGap;
+            }
             if (__builtin_amdgcn_ballot_w64(move) != 0) {
                 // rare (once per row and chunk, at its first valid logits):
-                // the half-wave's largest valid logit of each element's row
+                // the half-wave's largest valid y of each element's row
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     double v = ((mk >> i) & 1u) ? z[i] : -INFINITY;
 #pragma unroll
                     for (int o = 1; o < 32; o <<= 1) v = fmax(v, __shfl_xor(v, o));
-                    if (v > (double)m[i] + kMoveGap) {  // the same decision in all 32 lanes of the half
-                        const int mn = (int)__builtin_ceil(fmax(fmin(v, 2.0e9), -2.0e9));
-                        if (m[i] != INT_MIN) {
-                            const int sh = m[i] - mn;
+                    if (v > (double)kMoveGap) {  // the same decision in all 32 lanes of the half
+                        const int mn = (int)__builtin_ceil(fmax(fmin(v + (double)m[i], 2.0e9), -2.0e9));
+                        const int sh = m[i] - mn;
+                        if (l[i] != 0.0) {  // this lane has stored nonzero terms of the row: rescale them
                             l[i] = __builtin_ldexp(l[i], sh);
                             const int so = (8 * (i >> 2) + (i & 3)) * p.Tp * 4;
                             for (int u = 0; u < t; ++u) {
@@ -532,23 +540,24 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
                                                                       evoff, so + kKT * u * 4, 0);
                             }
                         }
+                        z[i] += (double)sh;  // exact: an integer shift of a value below 2^21
                         m[i] = mn;
                     }
                 }
             }
             // straight-line code over the 16 independent elements in both
             // forms (a masked element's exponential is computed, then dropped)
-            if (tile_full(mk)) {
+            if (full) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float e = exp2_term(z[i] - (double)m[i]);
+                    const float e = exp2_term(z[i]);
                     l[i] += (double)e;
                     store_term(emr, evoff, ((8 * (i >> 2) + (i & 3)) * p.Tp + key0 - key_lo) * 4, e);
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float e = exp2_term(z[i] - (double)m[i]);
+                    const float e = exp2_term(z[i]);
                     const float ev = ((mk >> i) & 1u) ? e : 0.f;
                     l[i] += (double)ev;
                     store_term(emr, evoff, ((8 * (i >> 2) + (i & 3)) * p.Tp + key0 - key_lo) * 4, ev);
@@ -569,7 +578,7 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
     if ((lane & 31) == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            part[elem_row(rt, i)] = make_double2(m[i] == INT_MIN ? -INFINITY : (double)m[i], l[i]);
+            part[elem_row(rt, i)] = make_double2(l[i] > 0.0 ? (double)m[i] : -INFINITY, l[i]);
     }
 }
 
