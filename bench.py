@@ -69,6 +69,8 @@ def _args():
                     help="time only the decode tokens (append + decode) on one built cache (profiling aid)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill probe + attention per step and print its fields (profiling aid)")
+    ap.add_argument("--probe-only", action="store_true",
+                    help="time only hq_probe_select at the 32K decode shape per step and print its time (profiling aid)")
     ap.add_argument("--sweep", action="store_true",
                     help="decode on the 8B GQA shape (B=16, 32/8 heads) at T = 1K..32K; prints one JSON line")
     ap.add_argument("--ablation", action="store_true",
@@ -760,6 +762,28 @@ def prefill_only(args):
     print(json.dumps(res), flush=True)
 
 
+def probe_only(args):
+    """hq_probe_select (probe + top-k) on the 32K decode workload only."""
+    import torch
+    import kv_cache_amd as hq
+    from synth.inputs import CONFIGS, make_decode_inputs
+    dev = "cuda:0"
+    spec = CONFIGS["decode_8b_32k"]
+    inp = make_decode_inputs(spec)
+    qp, k = _dev16(inp.q_probe, spec.dtype, dev), _dev16(inp.k, spec.dtype, dev)
+    lens = torch.from_numpy(inp.seq_lens).to(dev)
+    pol = hq.Policy()
+    tm = Timer()
+    for _ in range(args.warmup):
+        hq.probe_select(qp, k, lens, pol)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        tm("probe_select", hq.probe_select, qp, k, lens, pol)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe_select_ms": round(tm.ms("probe_select"), 3), "workload": "decode_8b_32k",
+                      "steps": args.steps}), flush=True)
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -785,6 +809,8 @@ def main():
 
     if args.prefill_only:
         return prefill_only(args)
+    if args.probe_only:
+        return probe_only(args)
     if args.sweep:
         return decode_sweep(args)
     if args.ablation:
