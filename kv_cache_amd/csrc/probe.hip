@@ -73,8 +73,8 @@ constexpr int kPlanes = 4;         // base-256 digits per value
 constexpr int kDS = kD + 16;       // LDS bytes per key in a digit plane (pad: no bank conflicts)
 constexpr int kColCols = 1024;     // columns per pass-2 workgroup (256 threads x 4)
 constexpr int kTopkLds = 34816;    // candidates the top-k stages in LDS (136 KiB + padding)
-constexpr int kUnset = -(1 << 20);  // reference of a row with no valid logit yet in the chunk: y = z + 2^20
-                                     // keeps z to 2^-33 and moves at the first valid logit above -2^20 + 100
+constexpr int kUnset = -(1 << 20);  // placeholder reference of a row with no valid logit yet in the chunk:
+                                     // y = z + 2^20 keeps z to 2^-33 until the row's first valid logit moves it
 constexpr int kMoveGap = 100;      // a row's reference moves when a logit exceeds it by more than this (log2
                                    // units), so every stored term 2^(z - ref) is at most 2^100 (fp32 range)
 constexpr double kLogitBudget = 0.5e-7;  // largest logit error accepted from the digit path (log2 units)
@@ -488,6 +488,7 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
         p.emap + ((size_t)bg * p.NRp + rt * kRT) * p.Tp + key_lo, (short)0, kRT * p.Tp * 4 - key_lo * 4, 0x00020000);
     const int evoff = ((lane & 31) + hoff * p.Tp) * 4;
     int m[16];  // integer references, uniform over the half-wave (kUnset: none yet)
+    uint32_t unset = 0xFFFFu;  // bit i: element i's row has no reference yet (uniform over the half-wave)
     double l[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -507,9 +508,10 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
             tile_logits<F16>(p, q, sm.q23[wave], sm.kt[cur], b, g, kbase, key, key_hi, rt, kZeros, z);
             const uint32_t mk = tile_mask(p, T, rt, rowmk, key0, key_hi);
             // z becomes y = z - m, the exponent of the term against the row's
-            // reference (for a row without one, m = kUnset: y > kMoveGap)
+            // reference (m = kUnset for a row without one yet: y = z + 2^20)
             const bool full = tile_full(mk);
-            bool move = false;
+            // a row without a reference moves at its first valid logit
+            bool move = (mk & unset) != 0u;
 #pragma unroll
             for (int i = 0; i < 16; ++i) z[i] -= (double)m[i];
             if (full) {  // wave-uniform: every element is in the map
@@ -527,7 +529,8 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
                     double v = ((mk >> i) & 1u) ? z[i] : -INFINITY;
 #pragma unroll
                     for (int o = 1; o < 32; o <<= 1) v = fmax(v, __shfl_xor(v, o));
-                    if (v > (double)kMoveGap) {  // the same decision in all 32 lanes of the half
+                    // the same decision in all 32 lanes of the half (same rows, same unset bits)
+                    if (v > (double)kMoveGap || (((unset >> i) & 1u) && v != -INFINITY)) {
                         const int mn = (int)__builtin_ceil(fmax(fmin(v + (double)m[i], 2.0e9), -2.0e9));
                         const int sh = m[i] - mn;
                         if (l[i] != 0.0) {  // this lane has stored nonzero terms of the row: rescale them
@@ -542,6 +545,7 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
                         }
                         z[i] += (double)sh;  // exact: an integer shift of a value below 2^21
                         m[i] = mn;
+                        unset &= ~(1u << i);
                     }
                 }
             }

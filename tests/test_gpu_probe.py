@@ -108,6 +108,27 @@ def test_probe_logit_range_beyond_reference():
     check_probe(inp, 128, (5, 100), floor=1e-30)
 
 
+def test_probe_logits_far_below_zero():
+    """Every logit near -1.5e6 in log2 units: channel 0 carries 29,952 in
+    every probe query and -392 in every key (a constant -1.498e6 added to
+    each logit; the other channels are the seeded N(0, 1) values, so the
+    softmax is that of an ordinary probe). Far below any fixed starting
+    reference, each row's reference has to be taken from its first valid
+    logit however negative (a row that kept a placeholder reference would
+    see all its terms underflow and drop out of the scores)."""
+    inp = small_decode_inputs(B=1, Hq=4, Hkv=1, T=900, seed=53)
+    q = O.to_f64(inp.q_probe, "bf16").astype(np.float32)
+    k = O.to_f64(inp.k, "bf16").astype(np.float32)
+    q[..., 0] = 29952.0
+    k[..., 0] = -392.0
+    inp.q_probe[...] = bf16_bits_from_f32(q)
+    inp.k[...] = bf16_bits_from_f32(k)
+    sm = fp32_scale(128)
+    z = O.to_f64(inp.q_probe, "bf16")[0].reshape(-1, 128) @ O.to_f64(inp.k, "bf16")[0, 0].T * sm / math.log(2)
+    assert z.max() < -2.0 ** 20 - 1000 and z.max() - z.min() < 200
+    check_probe(inp, 128, (5, 100), floor=1e-30)
+
+
 def _reference_move_inputs():
     """All probe rows along one direction u; every key near zero except 8
     keys (300..307) along u whose logits sit ~103 log2 units higher. The
