@@ -134,8 +134,9 @@ int32_t hq_sel_stride(int32_t T, const hq_policy* policy);
  *   sel_idx   [B][Hkv][hq_sel_stride(Tmax)] int32 out (unused tail = -1)
  *   sel_count [B][Hkv] int32 out;  thresh [B][Hkv] out
  *   ws        workspace of hq_probe_ws_bytes(...) bytes: mostly the probe
- *             rows' stored terms, 4 * (Hq/Hkv) * probe_rows * Tmax bytes
- *             (Tmax rounded up to 32) per (b, KV head); 4.3 GB for B = 16,
+ *             rows' stored terms, 4 * (Hq/Hkv) * probe_rows * Tp bytes
+ *             (Tp = Tmax rounded up to 32, plus 32) per (b, KV head), the
+ *             rows' count rounded up to 32; 4.3 GB for B = 16,
  *             8 KV heads, 4 heads each, 64 rows, Tmax = 32768             */
 hq_status hq_probe_select(const void* q_probe, const void* k, const int32_t* seq_lens,
                           int32_t B, int32_t Hq, int32_t Hkv, int32_t Tmax, int32_t D,
