@@ -73,6 +73,7 @@ constexpr int kPlanes = 4;         // base-256 digits per value
 constexpr int kDS = kD + 16;       // LDS bytes per key in a digit plane (pad: no bank conflicts)
 constexpr int kColCols = 1024;     // columns per pass-2 workgroup (256 threads x 4)
 constexpr int kTopkLds = 34816;    // candidates the top-k stages in LDS (136 KiB + padding)
+constexpr int kHistCopies = 8;     // copies of the top-k's radix histogram (8 KiB of LDS)
 constexpr int kUnset = -(1 << 20);  // placeholder reference of a row with no valid logit yet in the chunk:
                                      // y = z + 2^20 keeps z to 2^-33 until the row's first valid logit moves it
 constexpr int kMoveGap = 100;      // a row's reference moves when a logit exceeds it by more than this (log2
@@ -694,7 +695,10 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
     // word per 32, so the compaction's per-thread runs fall in different
     // banks); longer contexts read them from global memory in every pass
     __shared__ uint32_t sx[kTopkLds + kTopkLds / 32];
-    __shared__ uint32_t hist[256];
+    // kHistCopies copies of the 256-bin histogram, lane l adding to copy
+    // l % kHistCopies: the scores of a pass crowd into a few bins, and lanes
+    // of one wave adding to one LDS word are serialised
+    __shared__ uint32_t hist[kHistCopies * 256];
     __shared__ uint32_t wsum[16];
     __shared__ uint32_t sh_prefix, sh_mask, sh_remaining;
     __shared__ int sh_jk;
@@ -728,7 +732,7 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
     // fixed one byte at a time; sh_remaining counts the candidates still to
     // take among those matching the fixed bits.
     for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+        for (int i = tid; i < kHistCopies * 256; i += 1024) hist[i] = 0;
         __syncthreads();
         const uint32_t prefix = sh_prefix, mask = sh_mask;
         for (int base = 0; base < ncand; base += 1024) {
@@ -736,7 +740,8 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
             const uint32_t x = j < ncand ? rd(j) : 0u;
             // (a wave-level add of the lanes sharing a bin, against the
             // contention of the top byte's few bins, measured slower)
-            if (j < ncand && (x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+            if (j < ncand && (x & mask) == prefix)
+                atomicAdd(&hist[(lane & (kHistCopies - 1)) * 256 + ((x >> shift) & 255u)], 1u);
         }
         __syncthreads();
         if (tid < 64) {
@@ -745,7 +750,11 @@ __global__ __launch_bounds__(1024) void k_topk_select(const float* col_scores, c
             const uint32_t rem = sh_remaining;
             uint32_t h[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) h[i] = hist[255 - 4 * lane - i];
+            for (int i = 0; i < 4; ++i) {
+                h[i] = 0;
+#pragma unroll
+                for (int c = 0; c < kHistCopies; ++c) h[i] += hist[c * 256 + 255 - 4 * lane - i];
+            }
             const uint32_t s4 = h[0] + h[1] + h[2] + h[3];
             uint32_t incl = s4;
 #pragma unroll
