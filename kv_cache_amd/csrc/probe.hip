@@ -378,8 +378,9 @@ __device__ inline double exact_logit(const ProbeParams& p, int b, int g, const u
 __device__ inline int elem_row(int rt, int i) { return rt * kRT + 8 * (i >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (i & 3); }
 
 // The tile's logits in log2 units (z = q . k * sm_scale * log2 e) less a
-// per-element offset, for the 16 elements of this lane: from the digit sums
-// (the offset enters the last fma, one rounding), or, when the tile's error bound
+// per-element integer offset (the row's reference), for the 16 elements of
+// this lane: from the digit sums (the offset enters the inner fma, two
+// roundings in all), or, when the tile's error bound
 // exceeds the budget (a wave-uniform decision, so the common path is one
 // straight run over the 16 independent elements), recomputed in fp64 from
 // the 16-bit inputs (exact products, fp64 sums). Elements outside the map
@@ -387,7 +388,7 @@ __device__ inline int elem_row(int rt, int i) { return rt * kRT + 8 * (i >> 2) +
 template <bool F16>
 __device__ inline void tile_logits(const ProbeParams& p, const QTile& q, const QPlanes& q23, const KeyTile& kt,
                                    int b, int g, const uint16_t* kbase, int key, int key_end, int rt,
-                                   const double (&off)[16], double (&z)[16]) {
+                                   const int (&off)[16], double (&z)[16]) {
     const DigitSums s = tile_digit_sums(q, q23, kt);
     // the whole tile takes the fallback when any of its keys' bounds exceeds
     // the budget (wave-uniform)
@@ -399,13 +400,13 @@ __device__ inline void tile_logits(const ProbeParams& p, const QTile& q, const Q
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const double u = __builtin_fma((double)s.hi[i], 65536.0, (double)s.mid[i]);  // exact
-            z[i] = __builtin_fma(u, F256, __builtin_fma((double)s.lo[i], F, -off[i]));
+            z[i] = __builtin_fma(u, F256, __builtin_fma((double)s.lo[i], F, -(double)off[i]));
         }
     } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int row = elem_row(rt, i);
-            z[i] = (key < key_end && row < p.NR) ? exact_logit<F16>(p, b, g, kbase, key, row) - off[i] : 0.0;
+            z[i] = (key < key_end && row < p.NR) ? exact_logit<F16>(p, b, g, kbase, key, row) - (double)off[i] : 0.0;
         }
     }
 }
@@ -438,8 +439,6 @@ __device__ inline uint32_t tile_mask(const ProbeParams& p, int T, int rt, uint32
     for (int i = 0; i < 16; ++i) mk |= elem_valid(p, T, elem_row(rt, i), key, key_end) ? 1u << i : 0u;
     return mk;
 }
-
-constexpr double kZeros[16] = {};
 
 // Whether every element of the wave's tile is in the map (wave-uniform): then
 // the element loops need no mask.
@@ -506,15 +505,13 @@ __global__ __launch_bounds__(512) void k_probe_rowstats(ProbeParams p) {
         if (active) {
             const int key = key0 + (lane & 31);
             double z[16];
-            tile_logits<F16>(p, q, sm.q23[wave], sm.kt[cur], b, g, kbase, key, key_hi, rt, kZeros, z);
+            // z: y = z - m, the exponent of the term against the row's reference
+            // (m = kUnset for a row without one yet: y = z + 2^20)
+            tile_logits<F16>(p, q, sm.q23[wave], sm.kt[cur], b, g, kbase, key, key_hi, rt, m, z);
             const uint32_t mk = tile_mask(p, T, rt, rowmk, key0, key_hi);
-            // z becomes y = z - m, the exponent of the term against the row's
-            // reference (m = kUnset for a row without one yet: y = z + 2^20)
             const bool full = tile_full(mk);
             // a row without a reference moves at its first valid logit
             bool move = (mk & unset) != 0u;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) z[i] -= (double)m[i];
             if (full) {  // wave-uniform: every element is in the map
 #pragma unroll
                 for (int i = 0; i < 16; ++i) move |= z[i] > (double)kMoveGap;
