@@ -28,14 +28,14 @@
 // A_d = sum_{a + b = d} sum_c dq_a[c] dk_b[c], every A_d an exact int32 sum
 // from v_mfma_i32_32x32x32_i8. The 13 digit pairs with a + b <= 4 are
 // computed; the rest of the product is bounded, not dropped silently: per
-// (query tile, key tile) the kernel evaluates, from the digits and the
-// rounding residuals x - X 2^-sh themselves, a bound on the logit error
-// (rounding residuals times the other operand's magnitude, plus the three
-// omitted pairs bounded through the digit planes' l1 norms and maxima).
-// On the workloads this bound is ~1e-8 in log2 units; a tile whose bound
-// exceeds kLogitBudget has its logits recomputed from the 16-bit inputs in
-// fp64 (exact products, fp64 sums), so every logit carries at most the
-// budget's error. Each term 2^(z - m) is split exactly in fp64 into 2^n 2^f
+// (query tile, key) the kernel evaluates, from the digits and the rounding
+// residuals x - X 2^-sh themselves, a bound on the logit error (rounding
+// residuals times the other operand's magnitude, plus the three omitted
+// pairs bounded through the query digit planes' l1 norms and the key's
+// shift). On the workloads this bound is ~1e-8 in log2 units; a 32-key tile
+// where any key's bound exceeds kLogitBudget has its logits recomputed from
+// the 16-bit inputs in fp64 (exact products, fp64 sums), so every logit
+// carries at most the budget's error. Each term 2^(z - m) is split exactly in fp64 into 2^n 2^f
 // (n = rint(z - m), |f| <= 1/2); f is rounded to fp32 (error <= 2^-26) and
 // 2^f taken by the hardware base-2 exponential (v_exp_f32, relative error at
 // most 1.5 2^-24 on [-1/2, 1/2]: checked over every fp32 input there with
